@@ -1,0 +1,277 @@
+#!/usr/bin/env python
+"""Benchmark of the gated delta-rule hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step = one chunked prefill (both stages: per-chunk preparation and the
+sequential propagation with outputs) of the long-context workload: B=1, H=6,
+d_k = d_v = 256, T = 65,536 tokens, bf16 q/k/v, fp32 gates and state, chunk
+64, inputs resident in HBM.  ``value`` is prefill tokens/s.  The decode
+workload (256 sequences x 6 heads, d = 256, 128 consecutive single-token
+steps, fp32 state updated in place) is timed in the same run and reported
+under "decode" (state GB/s).
+
+Roofline: the dominant kernel of the step is the propagation (chain) kernel;
+its achieved rate is its algorithmic flops per launch (SURVEY-style count,
+not the dense tiles it issues) over its average duration, timed with HIP
+events on the stream it runs on.  Algorithmic work per token and head, with
+C = 64:  chain 6 d_k d_v + C d_v;  preparation C (3 d_k + d_v) + C^2 / 3.
+
+cpu_baseline: the fp64 oracle (plain sequential recurrence, one thread per
+(sequence, head) chain) run on the host on the same 64K-token inputs.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GDN prefill tokens/s (H=6,d=256,T=64K) + decode state GB/s; % of roofline"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+
+T, H, DK, DV, C = 65536, 6, 256, 256, 64
+DEC_N = 256
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def flops_chain_per_token():
+    return H * (6 * DK * DV + C * DV)
+
+
+def flops_prepare_per_token():
+    return H * (C * (3 * DK + DV) + C * C / 3.0)
+
+
+def decode_bytes_per_step(N=DEC_N):
+    # state read + write (fp32), q, k, v read and o written (bf16), g and beta (fp32)
+    return 2 * N * H * DK * DV * 4 + N * H * (2 * DK + 2 * DV) * 2 + 2 * N * H * 4
+
+
+def kernel_sources_digest():
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "hybrid_linear_attention_delta_amd", "csrc")
+    for fn in sorted(os.listdir(d)):
+        if fn.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(d, fn), "rb") as f:
+                h.update(fn.encode())
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel_key):
+    """HBM bytes per launch measured by rocprofv3 counters (FETCH_SIZE + WRITE_SIZE,
+    scaled by the copy-kernel calibration), valid only while the kernel sources
+    are unchanged since the counters were taken; else None."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        with open(p) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("sources_digest") != kernel_sources_digest():
+        return None
+    ent = d.get("kernels", {}).get(kernel_key)
+    return None if ent is None else ent.get("hbm_bytes_per_launch")
+
+
+def bench_prefill(torch, gdn, synth, steps, warmup):
+    dev = torch.device("cuda:0")
+    log(f"[bench] generating prefill inputs T={T} H={H} d={DK} bf16")
+    inp = synth.prefill_inputs(T, H, DK, DV, "bf16", seed=synth.seed_for("prefill64k"))
+    q = synth.to_torch(inp.q, dev, bf16=True)
+    k = synth.to_torch(inp.k, dev, bf16=True)
+    v = synth.to_torch(inp.v, dev, bf16=True)
+    g = synth.to_torch(inp.g, dev)
+    beta = synth.to_torch(inp.beta, dev)
+    o = torch.empty((T, H, DV), dtype=torch.bfloat16, device=dev)
+    fs = torch.empty((1, H, DV, DK), dtype=torch.float32, device=dev)
+    ws = torch.empty(gdn.prefill_workspace_size(T, 1, H, DK, DV, C), dtype=torch.uint8, device=dev)
+    log(f"[bench] workspace {ws.numel() / 2**20:.0f} MiB")
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record()
+        gdn.chunk_prefill(q, k, v, g, beta, chunk=C, out=o, final_state=fs, workspace=ws, stages=gdn.STAGE_PREPARE)
+        if evs is not None:
+            evs[1].record()
+        gdn.chunk_prefill(q, k, v, g, beta, chunk=C, out=o, final_state=fs, workspace=ws,
+                          stages=gdn.STAGE_PROPAGATE)
+        if evs is not None:
+            evs[2].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] prefill warmup done ({warmup} steps)")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    t_all0 = torch.cuda.Event(enable_timing=True)
+    t_all1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    t_all0.record()
+    for i in range(steps):
+        step(evs[i])
+    t_all1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    total_ms = t_all0.elapsed_time(t_all1)
+    prep = [e[0].elapsed_time(e[1]) for e in evs]
+    prop = [e[1].elapsed_time(e[2]) for e in evs]
+    log(f"[bench] prefill {steps} steps: {total_ms / steps:.3f} ms/step (prepare {sum(prep) / steps:.3f}, "
+        f"propagate {sum(prop) / steps:.3f}); wall {wall / steps * 1e3:.3f} ms/step")
+    return dict(ms_per_step=total_ms / steps, wall_ms_per_step=wall * 1e3 / steps,
+                prepare_ms=sum(prep) / steps, propagate_ms=sum(prop) / steps, inputs=inp)
+
+
+def bench_decode(torch, gdn, synth, n_steps, warmup=3):
+    dev = torch.device("cuda:0")
+    seed = synth.seed_for("decode")
+    log(f"[bench] generating decode inputs N={DEC_N} H={H} d={DK}, {n_steps} steps")
+    state = torch.from_numpy(synth.decode_state(DEC_N, H, DK, DV, seed)).to(dev)
+    per_step = []
+    for s in range(n_steps):
+        qn, kn, vn, gn, bn = synth.decode_step_inputs(DEC_N, H, DK, DV, "bf16", seed, s)
+        per_step.append((synth.to_torch(qn, dev, bf16=True), synth.to_torch(kn, dev, bf16=True),
+                         synth.to_torch(vn, dev, bf16=True), synth.to_torch(gn, dev), synth.to_torch(bn, dev)))
+    o = torch.empty((DEC_N, H, DV), dtype=torch.bfloat16, device=dev)
+    scratch = state.clone()
+    for s in range(warmup):
+        gdn.decode_step(*per_step[s % n_steps], scratch, out=o)
+    del scratch
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_steps + 1)]
+    evs[0].record()
+    for s in range(n_steps):
+        gdn.decode_step(*per_step[s], state, out=o)
+        evs[s + 1].record()
+    torch.cuda.synchronize()
+    times = [evs[i].elapsed_time(evs[i + 1]) for i in range(n_steps)]
+    total = evs[0].elapsed_time(evs[-1])
+    ms = total / n_steps
+    times.sort()
+    med = times[len(times) // 2]
+    log(f"[bench] decode {n_steps} steps: mean {ms * 1e3:.1f} us/step, median {med * 1e3:.1f} us/step")
+    return dict(ms_per_step=ms, median_ms=med)
+
+
+def cpu_baseline(inp, max_threads=16):
+    import oracle
+
+    chains = H
+    threads = max(1, min(chains, os.cpu_count() or 1, max_threads))
+    log(f"[bench] cpu baseline: fp64 oracle on {T} tokens x {H} heads, {threads} threads")
+    t0 = time.perf_counter()
+    oracle.prefill(inp.q, inp.k, inp.v, inp.g, inp.beta, bf16=True, n_threads=threads)
+    dt = time.perf_counter() - t0
+    log(f"[bench] cpu baseline {dt:.1f} s")
+    return dict(value=T / dt, unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"full prefill workload: {T} tokens x {H} heads, d={DK}, fp64 sequential recurrence, "
+                       f"{dt:.1f} s wall")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=128)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    a = ap.parse_args()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the mixer shards by head, state row or sequence without collectives; see DESIGN.md). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from hybrid_linear_attention_delta_amd import gdn, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (cuda:0)", file=sys.stderr)
+        sys.exit(2)
+    gdn.load_library()
+    pre = bench_prefill(torch, gdn, synth, a.steps, a.warmup)
+    dec = None if a.no_decode else bench_decode(torch, gdn, synth, a.decode_steps)
+
+    tok_s = T / (pre["ms_per_step"] / 1e3)
+    chain_tflops = flops_chain_per_token() * T / (pre["propagate_ms"] / 1e3) / 1e12
+    whole_tflops = (flops_chain_per_token() + flops_prepare_per_token()) * T / (pre["ms_per_step"] / 1e3) / 1e12
+    min_bytes = T * H * (2 * DK + 2 * DV) * 2 + T * H * 8  # q, k, v, o bf16 + g, beta fp32
+    out = {
+        "metric": METRIC,
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": pre["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"gdn_chunk_prefill B=1 H={H} d_k={DK} d_v={DV} T={T} chunk={C} bf16",
+                   "global_batch": 1, "seq_len": T, "heads": H, "d_k": DK, "d_v": DV, "chunk": C,
+                   "parallelism": "single-gpu"},
+        "roofline": {
+            "kernel": "chain_kernel (sequential state propagation + outputs)",
+            "bound": "mfma",
+            "achieved": chain_tflops,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": chain_tflops / PEAK_BF16_TFLOPS,
+            "traffic": traffic_from_profiles("chain_kernel"),
+            "avg_launch_ms": pre["propagate_ms"],
+            "algorithmic_flops_per_launch": flops_chain_per_token() * T,
+        },
+        "prefill": {
+            "tokens_per_s": tok_s,
+            "prepare_ms": pre["prepare_ms"],
+            "propagate_ms": pre["propagate_ms"],
+            "wall_ms_per_step": pre["wall_ms_per_step"],
+            "whole_path_tflops": whole_tflops,
+            "whole_path_mfma_frac": whole_tflops / PEAK_BF16_TFLOPS,
+            "min_traffic_GBps": min_bytes / (pre["ms_per_step"] / 1e3) / 1e9,
+            "algorithmic_flops_per_token": flops_chain_per_token() + flops_prepare_per_token(),
+        },
+    }
+    if dec is not None:
+        b = decode_bytes_per_step()
+        gbps = b / (dec["ms_per_step"] / 1e3) / 1e9
+        state_gbps = 2 * DEC_N * H * DK * DV * 4 / (dec["ms_per_step"] / 1e3) / 1e9
+        out["decode"] = {
+            "workload": f"gdn_decode_step N={DEC_N} H={H} d={DK} bf16 q/k/v, fp32 state, "
+                        f"{a.decode_steps} steps",
+            "ms_per_step": dec["ms_per_step"],
+            "median_ms_per_step": dec["median_ms"],
+            "tokens_per_s": DEC_N / (dec["ms_per_step"] / 1e3),
+            "state_GBps": state_gbps,
+            "roofline": {"kernel": "decode_kernel", "bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_GBPS,
+                         "unit": "GB/s", "frac": gbps / PEAK_HBM_GBPS,
+                         "traffic": traffic_from_profiles("decode_kernel"),
+                         "algorithmic_bytes_per_launch": b},
+        }
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(pre["inputs"])
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

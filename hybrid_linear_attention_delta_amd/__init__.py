@@ -1,1 +1,16 @@
+"""Gated delta-rule (Gated DeltaNet) sequence mixer for AMD Instinct MI355X.
 
+Chunked prefill and single-token recurrent decode, implemented as gfx950 HIP
+kernels behind the C ABI in include/gdn.h.  This package holds the thin
+ctypes binding (``gdn``), the seeded synthetic workload generators (``synth``)
+and the kernel sources (``csrc``).
+"""
+from .gdn import (  # noqa: F401
+    GdnError,
+    chunk_prefill,
+    decode_step,
+    load_library,
+    prefill_workspace_size,
+)
+
+__all__ = ["chunk_prefill", "decode_step", "prefill_workspace_size", "load_library", "GdnError"]

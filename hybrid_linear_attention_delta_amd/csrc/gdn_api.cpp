@@ -1,0 +1,207 @@
+// gdn_api.cpp -- C-ABI entry points: argument validation, workspace layout,
+// dispatch onto the caller's stream.  No device allocation, no global state.
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "../../include/gdn.h"
+#include "gdn_launch.h"
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+bool debug_sync()
+{
+    static int cached = -1;  // read once; a plain int written with the same value is benign
+    if (cached < 0) {
+        const char* s = getenv("GDN_DEBUG_SYNC");
+        cached = (s && s[0] == '1') ? 1 : 0;
+    }
+    return cached == 1;
+}
+
+bool in_list(int32_t x, const int32_t* xs, int n)
+{
+    for (int i = 0; i < n; ++i)
+        if (xs[i] == x) return true;
+    return false;
+}
+
+gdn_status finish(hipError_t e, hipStream_t stream)
+{
+    if (e != hipSuccess) return GDN_ERR_LAUNCH;
+    if (debug_sync()) {
+        if (hipStreamSynchronize(stream) != hipSuccess) return GDN_ERR_LAUNCH;
+        if (hipGetLastError() != hipSuccess) return GDN_ERR_LAUNCH;
+    }
+    return GDN_OK;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace
+
+namespace gdn {
+
+bool prefill_supported(bool bf16, int32_t dk, int32_t dv, int32_t chunk)
+{
+    static const int32_t f32_d[] = {16, 32, 64, 128, 256};
+    static const int32_t f32_c[] = {16, 32, 64};
+    static const int32_t bf_dk[] = {64, 128, 256};
+    static const int32_t bf_dv[] = {64, 128, 256, 512};
+    if (bf16) return in_list(dk, bf_dk, 3) && in_list(dv, bf_dv, 4) && chunk == 64;
+    return in_list(dk, f32_d, 5) && in_list(dv, f32_d, 5) && in_list(chunk, f32_c, 3);
+}
+
+PrefillLayout prefill_layout(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv, int32_t C, bool bf16)
+{
+    PrefillLayout L;
+    memset(&L, 0, sizeof L);
+    L.max_chunks = T / C + N;  // >= sum_n ceil(L_n / C)
+    const size_t el = bf16 ? 2 : 4;
+    // record: W fragments (C x dk, hi+lo for bf16), raw K^T fragments (dk x C),
+    // P fragments (C x C, hi+lo for bf16) in the operand element type; then U
+    // tiles (C x dv) and two per-row scale vectors (C each) in fp32.
+    const size_t split = bf16 ? 2 : 1;
+    const size_t oper = align_up(((size_t)C * dk * (split + 1) + (size_t)C * C * split) * el, 16);
+    L.record_bytes = align_up(oper + (size_t)C * dv * 4 + (size_t)C * 8, 256);
+    size_t off = 0;
+    L.off_header = off;
+    off = align_up(off + 64, 256);
+    L.off_chunk_tab = off;
+    off = align_up(off + (size_t)L.max_chunks * 16, 256);
+    L.off_seq_first = off;
+    off = align_up(off + ((size_t)N + 1) * 4, 256);
+    L.off_decay = off;
+    off = align_up(off + (size_t)L.max_chunks * H * 4, 256);
+    L.off_records = off;
+    off += (size_t)L.max_chunks * H * L.record_bytes;
+    L.total = off;
+    return L;
+}
+
+}  // namespace gdn
+
+extern "C" {
+
+const char* gdn_status_string(gdn_status s)
+{
+    switch (s) {
+        case GDN_OK: return "GDN_OK";
+        case GDN_ERR_NULL_ARG: return "GDN_ERR_NULL_ARG: a required pointer is NULL";
+        case GDN_ERR_BAD_SHAPE: return "GDN_ERR_BAD_SHAPE: invalid or inconsistent sizes";
+        case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED: dtype/d_k/d_v/chunk combination not built";
+        case GDN_ERR_BAD_SEQLENS: return "GDN_ERR_BAD_SEQLENS: cu_seqlens must rise from 0 to total_tokens";
+        case GDN_ERR_ALIGNMENT: return "GDN_ERR_ALIGNMENT: tensor pointers must be 16-byte aligned";
+        case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE: workspace missing or too small";
+        case GDN_ERR_LAUNCH: return "GDN_ERR_LAUNCH: kernel launch or execution failed";
+    }
+    return "GDN_ERR_UNKNOWN";
+}
+
+int32_t gdn_version(void) { return 100; }
+
+size_t gdn_prefill_workspace_size(int64_t total_tokens, int32_t num_seqs, int32_t H, int32_t dk, int32_t dv,
+                                  int32_t chunk, gdn_dtype dt)
+{
+    if (total_tokens < 0 || num_seqs < 1 || H < 1) return 0;
+    if (dt != GDN_F32 && dt != GDN_BF16) return 0;
+    if (!gdn::prefill_supported(dt == GDN_BF16, dk, dv, chunk)) return 0;
+    return gdn::prefill_layout(total_tokens, num_seqs, H, dk, dv, chunk, dt == GDN_BF16).total;
+}
+
+gdn_status gdn_chunk_prefill(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                             const float* init_state, const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                             int32_t num_seqs, int64_t total_tokens, int32_t H, int32_t dk, int32_t dv,
+                             int32_t chunk, gdn_dtype dt, float scale, int32_t qk_l2norm, void* o,
+                             float* final_state, void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    return gdn_chunk_prefill_staged(q, k, v, g, beta, init_state, cu_seqlens, cu_seqlens_host, num_seqs,
+                                    total_tokens, H, dk, dv, chunk, dt, scale, qk_l2norm, o, final_state, workspace,
+                                    workspace_bytes, GDN_STAGE_ALL, stream);
+}
+
+gdn_status gdn_chunk_prefill_staged(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                                    const float* init_state, const int32_t* cu_seqlens,
+                                    const int32_t* cu_seqlens_host, int32_t num_seqs, int64_t total_tokens,
+                                    int32_t H, int32_t dk, int32_t dv, int32_t chunk, gdn_dtype dt, float scale,
+                                    int32_t qk_l2norm, void* o, float* final_state, void* workspace,
+                                    size_t workspace_bytes, int32_t stages, hipStream_t stream)
+{
+    if (stages < 1 || stages > GDN_STAGE_ALL) return GDN_ERR_BAD_SHAPE;
+    if (dt != GDN_F32 && dt != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+    if (total_tokens < 0 || num_seqs < 1 || H < 1 || dk < 1 || dv < 1 || chunk < 1) return GDN_ERR_BAD_SHAPE;
+    if (total_tokens > ((int64_t)1 << 31) - 1) return GDN_ERR_BAD_SHAPE;  // int32 token indices on device
+    if (!cu_seqlens && num_seqs != 1) return GDN_ERR_BAD_SHAPE;
+    if (!gdn::prefill_supported(dt == GDN_BF16, dk, dv, chunk)) return GDN_ERR_UNSUPPORTED;
+    if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL_ARG;
+    if (!workspace) return GDN_ERR_WORKSPACE;
+    const bool bf16 = dt == GDN_BF16;
+    const void* ptrs[] = {q, k, v, init_state, o, final_state};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return GDN_ERR_ALIGNMENT;
+    if (!aligned4(g) || !aligned4(beta)) return GDN_ERR_ALIGNMENT;
+    if (((uintptr_t)workspace & 255u) != 0) return GDN_ERR_ALIGNMENT;
+    if (cu_seqlens_host) {
+        if (cu_seqlens_host[0] != 0 || cu_seqlens_host[num_seqs] != total_tokens) return GDN_ERR_BAD_SEQLENS;
+        for (int32_t n = 0; n < num_seqs; ++n)
+            if (cu_seqlens_host[n + 1] < cu_seqlens_host[n]) return GDN_ERR_BAD_SEQLENS;
+    }
+    gdn::PrefillLayout lay = gdn::prefill_layout(total_tokens, num_seqs, H, dk, dv, chunk, bf16);
+    if (workspace_bytes < lay.total) return GDN_ERR_WORKSPACE;
+    if (init_state && final_state && init_state != final_state) {
+        // partial overlap would make the in-place carry order-dependent
+        const char* a0 = (const char*)init_state;
+        const char* b0 = (const char*)final_state;
+        size_t bytes = (size_t)num_seqs * H * dv * dk * 4;
+        if (a0 < b0 + bytes && b0 < a0 + bytes) return GDN_ERR_BAD_SHAPE;
+    }
+
+    gdn::PrefillArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+    a.init_state = init_state;
+    a.cu_seqlens = cu_seqlens;
+    a.seq_order = nullptr;
+    a.N = num_seqs; a.T = total_tokens; a.H = H; a.dk = dk; a.dv = dv; a.chunk = chunk;
+    a.bf16 = bf16;
+    a.scale = scale > 0.f ? scale : 1.0f / sqrtf((float)dk);
+    a.l2norm = qk_l2norm ? 1 : 0;
+    a.o = o; a.final_state = final_state;
+    a.ws = (unsigned char*)workspace;
+    a.lay = lay;
+    a.stages = stages;
+    a.stream = stream;
+    return finish(gdn::launch_prefill(a), stream);
+}
+
+gdn_status gdn_decode_step(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                           float* state, int32_t N, int32_t H, int32_t dk, int32_t dv, gdn_dtype dt, float scale,
+                           int32_t qk_l2norm, void* o, hipStream_t stream)
+{
+    static const int32_t ds[] = {16, 32, 64, 128, 256};
+    static const int32_t dvs[] = {16, 32, 64, 128, 256, 512};
+    if (dt != GDN_F32 && dt != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+    if (N < 0 || H < 1 || dk < 1 || dv < 1) return GDN_ERR_BAD_SHAPE;
+    if (!in_list(dk, ds, 5) || !in_list(dv, dvs, 6)) return GDN_ERR_UNSUPPORTED;
+    if (N == 0) return GDN_OK;
+    if (!q || !k || !v || !g || !beta || !state || !o) return GDN_ERR_NULL_ARG;
+    const void* ptrs[] = {q, k, v, state, o};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return GDN_ERR_ALIGNMENT;
+    if (!aligned4(g) || !aligned4(beta)) return GDN_ERR_ALIGNMENT;
+    gdn::DecodeArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+    a.state = state; a.o = o;
+    a.N = N; a.H = H; a.dk = dk; a.dv = dv;
+    a.bf16 = dt == GDN_BF16;
+    a.scale = scale > 0.f ? scale : 1.0f / sqrtf((float)dk);
+    a.l2norm = qk_l2norm ? 1 : 0;
+    a.stream = stream;
+    return finish(gdn::launch_decode(a), stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,166 @@
+// gdn_decode.hip -- single-token recurrent decode of the gated delta rule (gfx950).
+//
+// Operation: "Long-Context Aware Upcycling: A New Frontier for Hybrid LLM
+// Scaling" (arXiv:2604.24715), App. A.3, Eqs. 16-19, one token per sequence.
+// For each (sequence n, head h) and each state row i (value index), with the
+// state stored [N][H][d_v][d_k] fp32 (row i = one contiguous d_k vector):
+//
+//     a   = s_i . k^        retrieval from the old row        (Eq. 17, before decay)
+//     b   = s_i . q^        read of the old row
+//     c   = beta (v_i - alpha a)                               (Eqs. 16-17, scaled by beta)
+//     s_i <- alpha s_i + c k^                                  (Eq. 18)
+//     o_i = scale (alpha b + c (k^ . q^))  == scale (s_i_new . q^)   (Eq. 19)
+//
+// so every state byte is read once and written once, and both dot products
+// come out of one pass over the row.
+//
+// Mapping: a row of d_k fp32 values is split over RL = d_k/16 lanes, each lane
+// owning 16 columns as four 16-byte vectors strided by RL*4 columns, so every
+// load instruction of a row group touches RL*16 contiguous bytes.  A wave holds
+// 64/RL rows per pass and runs ITERS passes with all loads issued up front
+// (16 rows of 1 KiB in flight per wave at d_k = 256).  The state is streamed
+// with non-temporal loads and stores: it is touched once per step and is
+// larger than the last-level cache in the workloads this serves.
+#include "gdn_common.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+
+template <int DK>
+struct DecodeShape {
+    static_assert(DK % 16 == 0 && DK >= 16 && DK <= 1024, "d_k");
+    static constexpr int RL = DK / 16;                         // lanes per row
+    static constexpr int ROWS_PER_PASS = kWave / RL;           // rows per wave per pass
+    static constexpr int ITERS = ROWS_PER_PASS >= 16 ? 1 : 16 / ROWS_PER_PASS;
+    static constexpr int ROWS_PER_WAVE = ROWS_PER_PASS * ITERS;
+    static constexpr int WAVES = 4;
+    static constexpr int ROWS_PER_BLOCK = ROWS_PER_WAVE * WAVES;
+};
+
+template <typename TIn, int DK>
+__global__ __launch_bounds__(256) void decode_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
+                                                     const TIn* __restrict__ v, const float* __restrict__ g,
+                                                     const float* __restrict__ beta, float* __restrict__ state,
+                                                     TIn* __restrict__ o, int32_t H, int32_t dv,
+                                                     int32_t blocks_per_head, float scale, int32_t l2norm)
+{
+    using S = DecodeShape<DK>;
+    constexpr int RL = S::RL;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int64_t nh = blockIdx.x / blocks_per_head;  // (n * H + h)
+    const int rb = blockIdx.x % blocks_per_head;
+    const int j = lane % RL;          // lane within its row group
+    const int rsub = lane / RL;       // row group within the wave
+
+    // Columns owned by this lane: 4 vectors, vector m covers 4*(j + RL*m) .. +3.
+    const int64_t qk_base = nh * DK;
+    f32x4 kv[4], qv[4];
+    float ss_k = 0.f, ss_q = 0.f, qk = 0.f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int col = 4 * (j + RL * m);
+        kv[m] = Elem<TIn>::load4(k, qk_base + col);
+        qv[m] = Elem<TIn>::load4(q, qk_base + col);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            ss_k += kv[m][e] * kv[m][e];
+            ss_q += qv[m][e] * qv[m][e];
+            qk += qv[m][e] * kv[m][e];
+        }
+    }
+    ss_k = group_sum<RL>(ss_k);
+    ss_q = group_sum<RL>(ss_q);
+    qk = group_sum<RL>(qk);
+    float rk = 1.f, rq = 1.f;
+    if (l2norm) {
+        rk = 1.0f / sqrtf(ss_k + kNormEps);
+        rq = 1.0f / sqrtf(ss_q + kNormEps);
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        kv[m] *= rk;
+        qv[m] *= rq;
+    }
+    const float kq = qk * rk * rq;  // k^ . q^
+
+    const float alpha = expf(g[nh]);
+    const float b = beta[nh];
+
+    const int row0 = rb * S::ROWS_PER_BLOCK + wave * S::ROWS_PER_WAVE;
+    float* srow_base = state + nh * (int64_t)dv * DK;
+
+    f32x4 s[S::ITERS][4];
+#pragma unroll
+    for (int it = 0; it < S::ITERS; ++it) {
+        const int row = row0 + it * S::ROWS_PER_PASS + rsub;
+        if (row < dv) {
+            const f32x4* p = reinterpret_cast<const f32x4*>(srow_base + (int64_t)row * DK);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) s[it][m] = __builtin_nontemporal_load(p + j + RL * m);
+        } else {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) s[it][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+
+#pragma unroll
+    for (int it = 0; it < S::ITERS; ++it) {
+        const int row = row0 + it * S::ROWS_PER_PASS + rsub;
+        float a = 0.f, bq = 0.f;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                a += s[it][m][e] * kv[m][e];
+                bq += s[it][m][e] * qv[m][e];
+            }
+        a = group_sum<RL>(a);
+        bq = group_sum<RL>(bq);
+        const float vi = row < dv ? Elem<TIn>::load(v, nh * dv + row) : 0.f;
+        const float c = b * (vi - alpha * a);
+        if (row < dv) {
+            f32x4* p = reinterpret_cast<f32x4*>(srow_base + (int64_t)row * DK);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                f32x4 nv = alpha * s[it][m] + c * kv[m];
+                __builtin_nontemporal_store(nv, p + j + RL * m);
+            }
+            if (j == 0) Elem<TIn>::store(o, nh * dv + row, scale * (alpha * bq + c * kq));
+        }
+    }
+}
+
+template <typename TIn, int DK>
+static hipError_t launch_decode_t(const DecodeArgs& a)
+{
+    using S = DecodeShape<DK>;
+    const int32_t bph = (a.dv + S::ROWS_PER_BLOCK - 1) / S::ROWS_PER_BLOCK;
+    const int64_t blocks = (int64_t)a.N * a.H * bph;
+    if (blocks == 0) return hipSuccess;
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((decode_kernel<TIn, DK>), dim3((uint32_t)blocks), dim3(256), 0, a.stream,
+                       (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, a.g, a.beta, a.state, (TIn*)a.o, a.H,
+                       a.dv, bph, a.scale, a.l2norm);
+    return hipGetLastError();
+}
+
+template <typename TIn>
+static hipError_t launch_decode_dt(const DecodeArgs& a)
+{
+    switch (a.dk) {
+        case 16: return launch_decode_t<TIn, 16>(a);
+        case 32: return launch_decode_t<TIn, 32>(a);
+        case 64: return launch_decode_t<TIn, 64>(a);
+        case 128: return launch_decode_t<TIn, 128>(a);
+        case 256: return launch_decode_t<TIn, 256>(a);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_decode(const DecodeArgs& a)
+{
+    return a.bf16 ? launch_decode_dt<uint16_t>(a) : launch_decode_dt<float>(a);
+}
+
+}  // namespace gdn

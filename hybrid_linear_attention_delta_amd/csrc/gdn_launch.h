@@ -1,0 +1,64 @@
+// gdn_launch.h -- internal launch interface between the C-ABI host code and
+// the kernel translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+struct DecodeArgs {
+    const void *q, *k, *v;
+    const float *g, *beta;
+    float* state;
+    void* o;
+    int32_t N, H, dk, dv;
+    bool bf16;
+    float scale;
+    int32_t l2norm;
+    hipStream_t stream;
+};
+
+hipError_t launch_decode(const DecodeArgs& a);
+
+// Chunked prefill.  The workspace is carved into the regions described by
+// PrefillLayout (computed on the host, identically for size queries and calls).
+struct PrefillLayout {
+    int64_t max_chunks;     // upper bound on sum_n ceil(L_n / C)
+    size_t off_header;      // int32[16]: [0] error flag, [1] number of chunks
+    size_t off_chunk_tab;   // int32[max_chunks][4]: tok0, len, seq, 0
+    size_t off_seq_first;   // int32[N + 1]: first chunk of each sequence
+    size_t off_decay;       // float[max_chunks][H]: e^{gamma_L} per chunk-head
+    size_t off_records;     // per chunk-head operand records
+    size_t record_bytes;    // bytes of one record
+    size_t total;
+};
+
+bool prefill_supported(bool bf16, int32_t dk, int32_t dv, int32_t chunk);
+PrefillLayout prefill_layout(int64_t total_tokens, int32_t num_seqs, int32_t H, int32_t dk, int32_t dv,
+                             int32_t chunk, bool bf16);
+
+struct PrefillArgs {
+    const void *q, *k, *v;
+    const float *g, *beta;
+    const float* init_state;
+    const int32_t* cu_seqlens;       // device, may be NULL (single sequence)
+    const int32_t* seq_order;        // unused for now (NULL)
+    int32_t N;
+    int64_t T;
+    int32_t H, dk, dv, chunk;
+    bool bf16;
+    float scale;
+    int32_t l2norm;
+    void* o;
+    float* final_state;
+    unsigned char* ws;
+    PrefillLayout lay;
+    int32_t stages;  // bit 0: prepare (chunk table + intra-chunk), bit 1: propagate (chain)
+    hipStream_t stream;
+};
+
+hipError_t launch_prefill(const PrefillArgs& a);
+
+}  // namespace gdn

@@ -1,0 +1,209 @@
+"""Thin Python binding over the C ABI in include/gdn.h (libgdn_mi355x.so).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI.  PyTorch supplies device memory and the current
+stream.  There is no CPU or PyTorch fallback: if the library is missing or the
+tensors are not on a GPU, the calls raise.
+
+The operation is the gated delta rule of "Long-Context Aware Upcycling: A New
+Frontier for Hybrid LLM Scaling" (arXiv:2604.24715), App. A.3, Eqs. 16-19,
+with the state stored [.., d_v, d_k] (row i = value index).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn_mi355x.so")
+
+GDN_F32, GDN_BF16 = 0, 1
+STAGE_PREPARE, STAGE_PROPAGATE, STAGE_ALL = 1, 2, 3
+STATUS = {
+    0: "GDN_OK", 1: "GDN_ERR_NULL_ARG", 2: "GDN_ERR_BAD_SHAPE", 3: "GDN_ERR_UNSUPPORTED",
+    4: "GDN_ERR_BAD_SEQLENS", 5: "GDN_ERR_ALIGNMENT", 6: "GDN_ERR_WORKSPACE", 7: "GDN_ERR_LAUNCH",
+}
+
+_lock = threading.Lock()
+_lib = None
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)}")
+
+
+def load_library(path: str | None = None):
+    """Load (once) and return the ctypes handle of the HIP library."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            p = path or LIB_PATH
+            if not os.path.exists(p):
+                raise RuntimeError(
+                    f"HIP library {p} is not built; run __graft_entry__.build() or "
+                    "python -m hybrid_linear_attention_delta_amd.csrc.build")
+            lib = ctypes.CDLL(p)
+            vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+            lib.gdn_prefill_workspace_size.argtypes = [i64, i32, i32, i32, i32, i32, ctypes.c_int]
+            lib.gdn_prefill_workspace_size.restype = sz
+            lib.gdn_chunk_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32,
+                                              ctypes.c_int, f32, i32, vp, vp, vp, sz, vp]
+            lib.gdn_chunk_prefill.restype = ctypes.c_int
+            lib.gdn_chunk_prefill_staged.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32,
+                                                     ctypes.c_int, f32, i32, vp, vp, vp, sz, i32, vp]
+            lib.gdn_chunk_prefill_staged.restype = ctypes.c_int
+            lib.gdn_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int, f32, i32,
+                                            vp, vp]
+            lib.gdn_decode_step.restype = ctypes.c_int
+            lib.gdn_status_string.argtypes = [ctypes.c_int]
+            lib.gdn_status_string.restype = ctypes.c_char_p
+            lib.gdn_version.argtypes = []
+            lib.gdn_version.restype = i32
+            _lib = lib
+    return _lib
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return GDN_BF16
+    if t.dtype == torch.float32:
+        return GDN_F32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _check(t, name, dtype=None, device=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device}); there is no CPU path")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def prefill_workspace_size(total_tokens: int, num_seqs: int, H: int, dk: int, dv: int, chunk: int = 64,
+                           dtype=None) -> int:
+    torch = _torch()
+    code = GDN_BF16 if (dtype is None or dtype == torch.bfloat16) else GDN_F32
+    return int(load_library().gdn_prefill_workspace_size(total_tokens, num_seqs, H, dk, dv, chunk, code))
+
+
+def chunk_prefill(q, k, v, g, beta, init_state=None, cu_seqlens=None, scale=None, qk_l2norm=True, chunk=64,
+                  out=None, final_state=None, workspace=None, return_final_state=True, stages=STAGE_ALL):
+    """Chunked gated delta-rule prefill over packed sequences.
+
+    q, k [T, H, dk]; v [T, H, dv] (bf16 or fp32, same dtype); g, beta [T, H] fp32;
+    init_state [N, H, dv, dk] fp32 or None; cu_seqlens int [N+1] (list, CPU or GPU
+    tensor) or None for one sequence.  Returns (o [T, H, dv], final_state [N, H, dv, dk]).
+    ``stages`` selects STAGE_PREPARE / STAGE_PROPAGATE / STAGE_ALL (see include/gdn.h);
+    a PROPAGATE-only call must get the workspace of a PREPARE on the same inputs.
+    """
+    torch = _torch()
+    lib = load_library()
+    dev = q.device
+    _check(q, "q", device=dev)
+    dt = q.dtype
+    for name, t in (("k", k), ("v", v)):
+        _check(t, name, dtype=dt, device=dev)
+    _check(g, "g", dtype=torch.float32, device=dev)
+    _check(beta, "beta", dtype=torch.float32, device=dev)
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    if k.shape != (T, H, dk) or v.shape[:2] != (T, H) or g.shape != (T, H) or beta.shape != (T, H):
+        raise ValueError("shape mismatch among q, k, v, g, beta")
+
+    cu_dev = None
+    cu_host = None
+    if cu_seqlens is None:
+        N = 1
+    else:
+        if isinstance(cu_seqlens, torch.Tensor) and cu_seqlens.device.type == "cuda":
+            cu_dev = cu_seqlens.to(torch.int32).contiguous()
+        else:
+            cu_host = torch.as_tensor(cu_seqlens, dtype=torch.int32).contiguous().cpu()
+            cu_dev = cu_host.to(dev)
+        N = cu_dev.shape[0] - 1
+        if N < 1:
+            raise ValueError("cu_seqlens needs at least two entries")
+    if init_state is not None:
+        _check(init_state, "init_state", dtype=torch.float32, device=dev)
+        if init_state.shape != (N, H, dv, dk):
+            raise ValueError(f"init_state must be [{N}, {H}, {dv}, {dk}]")
+    if out is None:
+        out = torch.empty((T, H, dv), dtype=dt, device=dev)
+    else:
+        _check(out, "out", dtype=dt, device=dev)
+    if final_state is None and return_final_state:
+        final_state = torch.empty((N, H, dv, dk), dtype=torch.float32, device=dev)
+    elif final_state is not None:
+        _check(final_state, "final_state", dtype=torch.float32, device=dev)
+    code = _dtype_code(q)
+    need = int(lib.gdn_prefill_workspace_size(T, N, H, dk, dv, chunk, code))
+    if need == 0:
+        raise GdnError(3, "gdn_prefill_workspace_size")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    s = -1.0 if scale is None else float(scale)
+    cu_host_ptr = None if cu_host is None else ctypes.c_void_p(cu_host.data_ptr())
+    st = lib.gdn_chunk_prefill_staged(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(init_state),
+                                      _ptr(cu_dev), cu_host_ptr, N, T, H, dk, dv, chunk, code, s,
+                                      int(bool(qk_l2norm)), _ptr(out), _ptr(final_state), _ptr(workspace),
+                                      workspace.numel(), int(stages), _stream(dev))
+    if st != 0:
+        raise GdnError(st, "gdn_chunk_prefill")
+    return out, final_state
+
+
+def decode_step(q, k, v, g, beta, state, scale=None, qk_l2norm=True, out=None):
+    """One recurrent decode step: q, k [N, H, dk]; v [N, H, dv]; g, beta [N, H] fp32;
+    state [N, H, dv, dk] fp32 updated in place.  Returns o [N, H, dv]."""
+    torch = _torch()
+    lib = load_library()
+    dev = q.device
+    _check(q, "q", device=dev)
+    dt = q.dtype
+    for name, t in (("k", k), ("v", v)):
+        _check(t, name, dtype=dt, device=dev)
+    _check(g, "g", dtype=torch.float32, device=dev)
+    _check(beta, "beta", dtype=torch.float32, device=dev)
+    _check(state, "state", dtype=torch.float32, device=dev)
+    N, H, dk = q.shape
+    dv = v.shape[2]
+    if state.shape != (N, H, dv, dk):
+        raise ValueError("state must be [N, H, dv, dk]")
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=dt, device=dev)
+    s = -1.0 if scale is None else float(scale)
+    st = lib.gdn_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), N, H, dk, dv,
+                             _dtype_code(q), s, int(bool(qk_l2norm)), _ptr(out), _stream(dev))
+    if st != 0:
+        raise GdnError(st, "gdn_decode_step")
+    return out
+
+
+def default_scale(dk: int) -> float:
+    return 1.0 / math.sqrt(dk)

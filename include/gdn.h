@@ -1,0 +1,164 @@
+/*
+ * gdn.h -- C ABI of the gated delta-rule (Gated DeltaNet) sequence mixer for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the gated delta rule of "Long-Context Aware Upcycling: A
+ * New Frontier for Hybrid LLM Scaling" (arXiv:2604.24715), App. A.3 "GDN Layer
+ * Architecture", Eqs. 16-19.  Per sequence n and head h a fixed-size fp32
+ * state S (d_v x d_k) replaces the KV cache; each token t does
+ *
+ *     S_t = e^{g_t} S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ *     o_t = scale * S_t q_t
+ *
+ * which is Eqs. 16-18 (decay, delta correction, write) with the decay and the
+ * correction multiplied out, and Eq. 19 (read of the updated state).  The
+ * paper's state is d_k x d_v with o = S^T q; this library stores its
+ * transpose, row i = value index, so every state row is one contiguous d_k
+ * vector.  g_t <= 0 is the log forget gate (alpha_t = e^{g_t}) and
+ * beta_t in (0, 1) the write strength, as stated under Eq. 21.
+ *
+ * Optional q/k L2 normalisation (qk_l2norm != 0) replaces x by
+ * x / sqrt(sum(x^2) + 1e-6) per (token, head) before use.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers unless the name ends in _host.
+ *   - The caller owns and allocates every buffer (including the workspace);
+ *     the library never allocates device memory and keeps no global state.
+ *   - Work is enqueued on `stream` and runs asynchronously; no call
+ *     synchronises the device (unless GDN_DEBUG_SYNC=1 is set, which makes
+ *     each call wait for its kernels and report launch/device errors).
+ *   - Argument errors are detected on the host before anything is launched
+ *     and returned as a gdn_status; nothing is written in that case.
+ *   - Results are deterministic: no atomics, fixed reduction order.
+ *   - Calls on different streams with disjoint buffers may run concurrently.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_NULL_ARG = 1,     /* a required pointer is NULL                                  */
+    GDN_ERR_BAD_SHAPE = 2,    /* negative / zero sizes, or sizes that disagree              */
+    GDN_ERR_UNSUPPORTED = 3,  /* (dtype, d_k, d_v, chunk) combination not built             */
+    GDN_ERR_BAD_SEQLENS = 4,  /* cu_seqlens not 0 = c_0 <= c_1 <= ... <= c_N = total_tokens  */
+    GDN_ERR_ALIGNMENT = 5,    /* q/k/v/o/state not 16-byte, g/beta not 4-byte aligned       */
+    GDN_ERR_WORKSPACE = 6,    /* workspace NULL or smaller than gdn_prefill_workspace_size */
+    GDN_ERR_LAUNCH = 7        /* a kernel launch failed (or, under GDN_DEBUG_SYNC, faulted) */
+} gdn_status;
+
+/* Element type of q, k, v and o.  Gates, beta and states are always fp32. */
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+/*
+ * Supported combinations (anything else returns GDN_ERR_UNSUPPORTED):
+ *   GDN_F32 : d_k, d_v in {16, 32, 64, 128, 256}, chunk in {16, 32, 64}
+ *   GDN_BF16: d_k in {64, 128, 256}, d_v in {64, 128, 256, 512}, chunk = 64
+ * gdn_decode_step has no chunk and accepts any d_k, d_v in the lists above.
+ */
+
+/*
+ * Bytes of device workspace gdn_chunk_prefill needs for these sizes.
+ * Returns 0 for an unsupported or invalid combination.  The workspace holds
+ * per-chunk intermediates of the chunked (WY) evaluation and is fully
+ * rewritten by every call; its contents between calls are meaningless.
+ */
+size_t gdn_prefill_workspace_size(int64_t total_tokens, int32_t num_seqs, int32_t H, int32_t dk,
+                                  int32_t dv, int32_t chunk, gdn_dtype dt);
+
+/*
+ * Chunked prefill over packed variable-length sequences (App. A.3, last
+ * paragraph: the sequence is cut into chunks of `chunk` tokens, the delta
+ * corrections inside a chunk are batched through the WY representation and
+ * the state is carried from chunk to chunk).  The result equals the
+ * token-by-token recurrence above up to floating-point rounding.
+ *
+ *   q, k        [total_tokens, H, dk]   dt, contiguous, 16-byte aligned
+ *   v           [total_tokens, H, dv]   dt
+ *   g, beta     [total_tokens, H]       fp32 (log forget gate, write strength),
+ *               4-byte aligned
+ *   init_state  [num_seqs, H, dv, dk]   fp32, or NULL for zeros
+ *   cu_seqlens  device int32 [num_seqs + 1], sequence n owns tokens
+ *               [cu_seqlens[n], cu_seqlens[n+1]); NULL means one sequence
+ *               (num_seqs must then be 1).
+ *   cu_seqlens_host  optional host mirror of cu_seqlens (same values).  When
+ *               given it is validated on the host (GDN_ERR_BAD_SEQLENS) and
+ *               used to schedule sequences; when NULL the device copy is
+ *               trusted: invalid contents are clamped so no access leaves its
+ *               buffer, and the outputs are then unspecified.
+ *   scale       read scale of Eq. 19; scale <= 0 selects 1/sqrt(dk)
+ *   qk_l2norm   nonzero: L2-normalise q and k per (token, head)
+ *   o           [total_tokens, H, dv]   dt (written)
+ *   final_state [num_seqs, H, dv, dk]   fp32 (written), may be NULL, may
+ *               alias init_state exactly (in-place carry)
+ *   workspace   device buffer of at least gdn_prefill_workspace_size(...)
+ *               bytes, 256-byte aligned
+ * Sequences of length 0 are allowed: their final state equals the initial.
+ */
+gdn_status gdn_chunk_prefill(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                             const float* init_state, const int32_t* cu_seqlens,
+                             const int32_t* cu_seqlens_host, int32_t num_seqs, int64_t total_tokens,
+                             int32_t H, int32_t dk, int32_t dv, int32_t chunk, gdn_dtype dt, float scale,
+                             int32_t qk_l2norm, void* o, float* final_state, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The two stages of gdn_chunk_prefill, for callers that schedule or time them
+ * separately.  Same arguments and rules as gdn_chunk_prefill, plus `stages`:
+ *   GDN_STAGE_PREPARE    per-chunk work, fully parallel over (chunk, head):
+ *                        chunk table, q/k norms, cumulative log-decay, the
+ *                        triangular solve and the WY factors, written into the
+ *                        workspace (reads q, k, v, g, beta; writes only the
+ *                        workspace);
+ *   GDN_STAGE_PROPAGATE  the sequential pass over each sequence's chunks:
+ *                        state carry and outputs (reads the workspace left by
+ *                        a PREPARE on the same inputs and sizes, plus q and
+ *                        init_state; writes o and final_state);
+ *   GDN_STAGE_ALL        both, in order (what gdn_chunk_prefill does).
+ * Stages of one prefill must be enqueued in order on one stream (or ordered
+ * by the caller) with the same workspace.
+ */
+#define GDN_STAGE_PREPARE 1
+#define GDN_STAGE_PROPAGATE 2
+#define GDN_STAGE_ALL 3
+gdn_status gdn_chunk_prefill_staged(const void* q, const void* k, const void* v, const float* g,
+                                    const float* beta, const float* init_state, const int32_t* cu_seqlens,
+                                    const int32_t* cu_seqlens_host, int32_t num_seqs, int64_t total_tokens,
+                                    int32_t H, int32_t dk, int32_t dv, int32_t chunk, gdn_dtype dt, float scale,
+                                    int32_t qk_l2norm, void* o, float* final_state, void* workspace,
+                                    size_t workspace_bytes, int32_t stages, hipStream_t stream);
+
+/*
+ * One recurrent decode step for N independent sequences (the token-level
+ * recurrence above with one token per sequence; the serving form of the
+ * fixed-size state described in App. A.3 and the HyLo-Qwen GDN model card).
+ *
+ *   q, k   [N, H, dk]  dt;   v [N, H, dv] dt (16-byte aligned);
+ *   g, beta [N, H] fp32 (4-byte aligned)
+ *   state  [N, H, dv, dk] fp32, read and updated IN PLACE
+ *   o      [N, H, dv]  dt (written)
+ * Each state row is streamed from HBM exactly once (read, update, write).
+ */
+gdn_status gdn_decode_step(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                           float* state, int32_t N, int32_t H, int32_t dk, int32_t dv, gdn_dtype dt,
+                           float scale, int32_t qk_l2norm, void* o, hipStream_t stream);
+
+/* Static, human-readable name of a status code. */
+const char* gdn_status_string(gdn_status s);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t gdn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

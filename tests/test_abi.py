@@ -1,0 +1,131 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+declared in include/gdn.h, and rejects bad arguments on the host before any
+launch (every call below returns before touching the device)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from hybrid_linear_attention_delta_amd import gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(gdn_\w+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gdn.LIB_PATH):
+        pytest.fail("libgdn_mi355x.so is not built (run __graft_entry__.build())")
+    return gdn.load_library()
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for required in ("gdn_chunk_prefill", "gdn_decode_step", "gdn_prefill_workspace_size", "gdn_status_string"):
+        assert required in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", gdn.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT\s+(\w+)$", out, flags=re.M))
+    missing = [n for n in _declared_functions() if n not in exported]
+    assert not missing, f"declared but not exported: {missing}"
+    for n in _declared_functions():
+        getattr(lib, n)  # resolvable through ctypes
+
+
+def test_status_strings(lib):
+    for code, name in gdn.STATUS.items():
+        assert lib.gdn_status_string(code).decode().startswith(name)
+    assert lib.gdn_version() >= 100
+
+
+def test_workspace_size_queries(lib):
+    ws = lib.gdn_prefill_workspace_size(65536, 1, 6, 256, 256, 64, gdn.GDN_BF16)
+    assert ws > 0
+    # grows with tokens; unsupported combinations give 0
+    assert lib.gdn_prefill_workspace_size(131072, 1, 6, 256, 256, 64, gdn.GDN_BF16) > ws
+    assert lib.gdn_prefill_workspace_size(1024, 1, 6, 256, 256, 32, gdn.GDN_BF16) == 0
+    assert lib.gdn_prefill_workspace_size(1024, 1, 6, 48, 48, 64, gdn.GDN_F32) == 0
+    assert lib.gdn_prefill_workspace_size(64, 1, 2, 16, 16, 16, gdn.GDN_F32) > 0
+    assert lib.gdn_prefill_workspace_size(-1, 1, 2, 16, 16, 16, gdn.GDN_F32) == 0
+
+
+def _fake(addr=0x10000):
+    return ctypes.c_void_p(addr)
+
+
+def _prefill(lib, **kw):
+    a = dict(q=_fake(), k=_fake(), v=_fake(), g=_fake(), beta=_fake(), init=None, cu=None, cu_host=None, N=1,
+             T=128, H=2, dk=64, dv=64, chunk=64, dt=gdn.GDN_BF16, scale=-1.0, l2=1, o=_fake(), fs=None,
+             ws=_fake(0x100000), wsb=1 << 40, stream=None)
+    a.update(kw)
+    return lib.gdn_chunk_prefill(a["q"], a["k"], a["v"], a["g"], a["beta"], a["init"], a["cu"], a["cu_host"], a["N"],
+                                 a["T"], a["H"], a["dk"], a["dv"], a["chunk"], a["dt"], a["scale"], a["l2"], a["o"],
+                                 a["fs"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_prefill_host_validation(lib):
+    assert _prefill(lib, dk=48) == 3                       # unsupported
+    assert _prefill(lib, chunk=32) == 3                    # bf16 needs chunk 64
+    assert _prefill(lib, dt=7) == 3
+    assert _prefill(lib, T=-5) == 2
+    assert _prefill(lib, H=0) == 2
+    assert _prefill(lib, N=2) == 2                         # N > 1 needs cu_seqlens
+    assert _prefill(lib, q=None) == 1
+    assert _prefill(lib, ws=None) == 6
+    assert _prefill(lib, wsb=16) == 6
+    assert _prefill(lib, q=_fake(0x10004)) == 5            # misaligned
+    assert _prefill(lib, g=_fake(0x10002)) == 5            # gates need 4-byte alignment
+    assert _prefill(lib, g=_fake(0x10004)) != 5
+    assert _prefill(lib, ws=_fake(0x100010)) == 5          # workspace must be 256-byte aligned
+    cu = (ctypes.c_int32 * 3)(0, 100, 90)                  # not monotone
+    assert _prefill(lib, cu=_fake(0x20000), cu_host=cu, N=2, T=90) == 4
+    cu = (ctypes.c_int32 * 3)(0, 50, 120)                  # last != T
+    assert _prefill(lib, cu=_fake(0x20000), cu_host=cu, N=2, T=128) == 4
+    cu = (ctypes.c_int32 * 3)(1, 50, 128)                  # first != 0
+    assert _prefill(lib, cu=_fake(0x20000), cu_host=cu, N=2, T=128) == 4
+    # overlapping but distinct init/final state buffers
+    assert _prefill(lib, init=_fake(0x40000), fs=_fake(0x40010)) == 2
+
+
+def test_decode_host_validation(lib):
+    f = _fake()
+    call = lambda **kw: lib.gdn_decode_step(kw.get("q", f), f, f, f, f, kw.get("state", f), kw.get("N", 4), 2,
+                                            kw.get("dk", 64), kw.get("dv", 64), kw.get("dt", gdn.GDN_BF16), -1.0, 1,
+                                            kw.get("o", f), None)
+    assert call(dk=48) == 3
+    assert call(dv=1024) == 3
+    assert call(dt=3) == 3
+    assert call(N=-1) == 2
+    assert call(N=0) == 0                                  # nothing to do, nothing launched
+    assert call(state=None) == 1
+    assert call(o=_fake(0x10008)) == 5
+
+
+def test_binding_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(4, 1, 16)
+    with pytest.raises(ValueError, match="GPU"):
+        gdn.decode_step(q, q, q, torch.zeros(4, 1), torch.zeros(4, 1), torch.zeros(4, 1, 16, 16))
+    with pytest.raises(ValueError, match="GPU"):
+        gdn.chunk_prefill(q, q, q, torch.zeros(4, 1), torch.zeros(4, 1))
+
+
+def test_product_path_does_not_import_the_oracle():
+    pkg = os.path.join(ROOT, "hybrid_linear_attention_delta_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".cpp", ".h")):
+                txt = open(os.path.join(dirpath, fn)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", txt, flags=re.M), fn
+                assert "gdn_oracle" not in txt, fn

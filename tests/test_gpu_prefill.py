@@ -1,0 +1,205 @@
+"""GPU parity of gdn_chunk_prefill against the fp64 oracle (same seeded inputs).
+
+Tolerance on max|gpu - oracle| / rms(oracle), per tensor (o and final state):
+2e-2 for bf16 q/k/v with fp32 accumulation, 1e-4 for the all-fp32 path.
+Small cases compare every element and span several chunks with a ragged tail;
+full-size cases compare sampled state rows (rows evolve independently, so the
+oracle evaluates just those rows over the whole sequence)."""
+import numpy as np
+import pytest
+
+from _util import TOL_BF16, TOL_F32, bound_ratio, rel_err
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import oracle  # noqa: E402
+from hybrid_linear_attention_delta_amd import gdn, synth  # noqa: E402
+
+DEV = "cuda:0"
+
+
+def _gpu(inp, chunk, init=None, scale=None, l2=True, varlen=True):
+    bf = inp.bf16
+    t = lambda a, b=False: synth.to_torch(a, DEV, bf16=b)
+    cu = None
+    if varlen and inp.cu_seqlens.shape[0] > 2:
+        cu = torch.from_numpy(inp.cu_seqlens.astype(np.int32))
+    init_t = None if init is None else torch.from_numpy(np.ascontiguousarray(init, dtype=np.float32)).to(DEV)
+    o, fs = gdn.chunk_prefill(t(inp.q, bf), t(inp.k, bf), t(inp.v, bf), t(inp.g), t(inp.beta), init_state=init_t,
+                              cu_seqlens=cu, scale=scale, qk_l2norm=l2, chunk=chunk)
+    return o.float().cpu().numpy(), fs.cpu().numpy()
+
+
+def _check(inp, chunk, tol, init=None, rows=None, scale=None, l2=True):
+    o, fs = _gpu(inp, chunk, init=init, scale=scale, l2=l2)
+    o_ref, fs_ref = oracle.prefill(inp.q, inp.k, inp.v, inp.g, inp.beta, init, cu_seqlens=inp.cu_seqlens,
+                                   scale=scale, qk_l2norm=l2, rows=rows, bf16=inp.bf16)
+    if rows is not None:
+        o, o_ref = o[:, :, rows], o_ref[:, :, rows]
+        fs, fs_ref = fs[:, :, rows], fs_ref[:, :, rows]
+    eo, es = rel_err(o, o_ref), rel_err(fs, fs_ref)
+    ro = bound_ratio(o, o_ref, tol, stored_bf16=inp.bf16)
+    print(f"  o err {eo:.3e} (bound ratio {ro:.3f})  state err {es:.3e}")
+    assert ro <= 1.0 and es <= tol, (eo, ro, es)
+    return eo, es
+
+
+def test_tiny_fp32_workload():
+    """B=1, H=2, T=64, d=16, fp32, zero initial state, chunk 16."""
+    inp = synth.prefill_inputs(64, 2, 16, 16, "f32", seed=synth.seed_for("tiny"))
+    _check(inp, 16, TOL_F32)
+
+
+@pytest.mark.parametrize("T,H,dk,dv,C,gate", [
+    (200, 2, 32, 64, 32, "slow"),
+    (77, 3, 64, 16, 16, "default"),
+    (130, 1, 128, 128, 64, "slow"),
+    (64, 1, 16, 256, 64, "slow"),
+])
+def test_fp32_shapes_with_initial_state(T, H, dk, dv, C, gate):
+    inp = synth.prefill_inputs(T, H, dk, dv, "f32", seed=T + dk, gate=gate, init_state_std=0.5)
+    _check(inp, C, TOL_F32, init=inp.init_state)
+
+
+@pytest.mark.parametrize("gate", ["default", "slow"])
+def test_fp32_d256_T1024(gate):
+    """All-fp32 run of the production tile shape (d=256, chunk 64) at the tight tolerance."""
+    inp = synth.prefill_inputs(1024, 2, 256, 256, "f32", seed=77, gate=gate)
+    _check(inp, 64, TOL_F32)
+
+
+def test_fp32_no_norm_and_custom_scale():
+    inp = synth.prefill_inputs(96, 2, 64, 64, "f32", seed=3, gate="slow", init_state_std=0.3)
+    _check(inp, 32, TOL_F32, init=inp.init_state, scale=0.2, l2=False)
+
+
+@pytest.mark.parametrize("gate", ["default", "slow"])
+def test_bf16_small_ragged(gate):
+    inp = synth.prefill_inputs(300, 2, 256, 256, "bf16", seed=9, gate=gate, init_state_std=0.2)
+    _check(inp, 64, TOL_BF16, init=inp.init_state)
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 256), (256, 512)])
+def test_bf16_other_head_dims(dk, dv):
+    inp = synth.prefill_inputs(257, 2, dk, dv, "bf16", seed=dk + dv, gate="slow")
+    _check(inp, 64, TOL_BF16)
+
+
+def test_bf16_prefill_8k_workload():
+    """H=6, d=256, T=8192, bf16, chunk 64: every output and the final state."""
+    inp = synth.prefill_inputs(8192, 6, 256, 256, "bf16", seed=synth.seed_for("prefill8k"))
+    _check(inp, 64, TOL_BF16)
+
+
+def test_bf16_prefill_8k_slow_decay():
+    inp = synth.prefill_inputs(8192, 6, 256, 256, "bf16", seed=synth.seed_for("prefill8k") + 100, gate="slow")
+    _check(inp, 64, TOL_BF16)
+
+
+@pytest.mark.slow
+def test_bf16_prefill_64k_workload_sampled_rows():
+    """H=6, d=256, T=65536, bf16, chunk 64; 12 state rows per head checked over the whole sequence."""
+    inp = synth.prefill_inputs(65536, 6, 256, 256, "bf16", seed=synth.seed_for("prefill64k"))
+    rows = [0, 1, 15, 16, 63, 64, 100, 127, 128, 200, 254, 255]
+    _check(inp, 64, TOL_BF16, rows=rows)
+
+
+@pytest.mark.parametrize("dtype,lens", [
+    ("f32", [0, 1, 63, 64, 65, 130, 17]),
+    ("bf16", [5, 0, 200, 64, 129, 1]),
+])
+def test_varlen_packing(dtype, lens):
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    d = 64 if dtype == "f32" else 256
+    inp = synth.prefill_inputs(int(cu[-1]), 2, d, d, dtype, seed=31, gate="slow", cu_seqlens=cu,
+                               init_state_std=0.4)
+    _check(inp, 64, TOL_F32 if dtype == "f32" else TOL_BF16, init=inp.init_state)
+
+
+def test_varlen_device_seqlens_without_host_copy():
+    lens = [70, 3, 128]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    inp = synth.prefill_inputs(int(cu[-1]), 2, 32, 32, "f32", seed=41, gate="slow", cu_seqlens=cu)
+    t = lambda a: synth.to_torch(a, DEV)
+    o, fs = gdn.chunk_prefill(t(inp.q), t(inp.k), t(inp.v), t(inp.g), t(inp.beta),
+                              cu_seqlens=torch.from_numpy(cu.astype(np.int32)).to(DEV), chunk=32)
+    o_ref, fs_ref = oracle.prefill(inp.q, inp.k, inp.v, inp.g, inp.beta, cu_seqlens=cu)
+    assert rel_err(o.cpu().numpy(), o_ref) <= TOL_F32
+    assert rel_err(fs.cpu().numpy(), fs_ref) <= TOL_F32
+
+
+def test_continuation_and_decode_after_prefill():
+    """prefill [0,T1) then [T1,T) from the carried state, then decode steps, all
+    against one oracle run over the whole sequence."""
+    T, T1, m = 400, 137, 5
+    inp = synth.prefill_inputs(T + m, 2, 256, 256, "bf16", seed=51, gate="slow")
+    t = lambda a, b=False: synth.to_torch(a, DEV, bf16=b)
+    q, k, v, g, b = t(inp.q, True), t(inp.k, True), t(inp.v, True), t(inp.g), t(inp.beta)
+    o1, s1 = gdn.chunk_prefill(q[:T1].contiguous(), k[:T1].contiguous(), v[:T1].contiguous(), g[:T1].contiguous(),
+                               b[:T1].contiguous())
+    o2, s2 = gdn.chunk_prefill(q[T1:T].contiguous(), k[T1:T].contiguous(), v[T1:T].contiguous(),
+                               g[T1:T].contiguous(), b[T1:T].contiguous(), init_state=s1)
+    outs = [o1, o2]
+    state = s2.clone()
+    for t_ in range(T, T + m):
+        od = gdn.decode_step(q[t_:t_ + 1].contiguous(), k[t_:t_ + 1].contiguous(), v[t_:t_ + 1].contiguous(),
+                             g[t_:t_ + 1].contiguous(), b[t_:t_ + 1].contiguous(), state.view(1, 2, 256, 256))
+        outs.append(od)
+    o = torch.cat(outs).float().cpu().numpy()
+    o_ref, fs_ref = oracle.prefill(inp.q, inp.k, inp.v, inp.g, inp.beta, bf16=True)
+    assert bound_ratio(o, o_ref, TOL_BF16, stored_bf16=True) <= 1.0
+    assert rel_err(state.cpu().numpy(), fs_ref) <= TOL_BF16
+
+
+def test_in_place_state_carry():
+    inp = synth.prefill_inputs(150, 2, 64, 64, "f32", seed=61, gate="slow", init_state_std=0.5)
+    t = lambda a: synth.to_torch(a, DEV)
+    st = t(inp.init_state).clone()
+    o, fs = gdn.chunk_prefill(t(inp.q), t(inp.k), t(inp.v), t(inp.g), t(inp.beta), init_state=st, final_state=st,
+                              chunk=64)
+    o_ref, fs_ref = oracle.prefill(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.init_state)
+    assert fs.data_ptr() == st.data_ptr()
+    assert rel_err(st.cpu().numpy(), fs_ref) <= TOL_F32
+    assert rel_err(o.cpu().numpy(), o_ref) <= TOL_F32
+
+
+def test_empty_input_returns_initial_state():
+    t = lambda a: synth.to_torch(a, DEV)
+    inp = synth.prefill_inputs(0, 2, 64, 64, "f32", seed=1, init_state_std=1.0)
+    o, fs = gdn.chunk_prefill(t(inp.q), t(inp.k), t(inp.v), t(inp.g), t(inp.beta), init_state=t(inp.init_state))
+    assert o.shape == (0, 2, 64)
+    assert torch.equal(fs.cpu(), torch.from_numpy(inp.init_state))
+
+
+def test_prefill_deterministic():
+    inp = synth.prefill_inputs(1000, 6, 256, 256, "bf16", seed=71)
+    a = _gpu(inp, 64)
+    b = _gpu(inp, 64)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.slow
+def test_varlen_2m_workload_checked_subsets():
+    """2,097,152 tokens in 16 sequences (log-uniform lengths in [4K, 512K]), H=6, d=256, bf16.
+    The oracle checks the two shortest sequences in full (o and final state on sampled
+    rows) and the first 8192 outputs of every sequence (sampled rows)."""
+    lengths = synth.varlen_lengths(synth.seed_for("varlen2m"))
+    H, d = 6, 256
+    q, k, v, g, beta, cu = synth.varlen_torch_inputs(lengths, H, d, d, synth.seed_for("varlen2m"), DEV)
+    o, fs = gdn.chunk_prefill(q, k, v, g, beta, cu_seqlens=cu.cpu())
+    torch.cuda.synchronize()
+    cu_h = cu.cpu().numpy().astype(np.int64)
+    rows = [0, 37, 128, 255]
+    bits = lambda x: x.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    shortest = np.argsort(lengths)[:2]
+    for n in range(len(lengths)):
+        a = int(cu_h[n])
+        b = int(cu_h[n + 1]) if n in shortest else a + 8192
+        o_ref, fs_ref = oracle.prefill(bits(q[a:b]), bits(k[a:b]), bits(v[a:b]), g[a:b].cpu().numpy(),
+                                       beta[a:b].cpu().numpy(), rows=rows, bf16=True)
+        ro = bound_ratio(o[a:b][:, :, rows].float().cpu().numpy(), o_ref[:, :, rows], TOL_BF16, stored_bf16=True)
+        assert ro <= 1.0, (n, ro)
+        if n in shortest:
+            es = rel_err(fs[n:n + 1][:, :, rows].cpu().numpy(), fs_ref[:, :, rows])
+            assert es <= TOL_BF16, (n, es)
