@@ -15,17 +15,42 @@ typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 constexpr int kWave = 64;
 constexpr float kNormEps = 1e-6f;  // q/k L2 normalisation: x / sqrt(sum x^2 + eps)
 
-// bf16 <-> fp32.  Widening is exact; narrowing rounds to nearest even.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// bf16 <-> fp32.  Widening is exact; narrowing is the gfx950 hardware convert
+// (v_cvt_pk_bf16_f32, round to nearest even).
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
-__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f)
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
+// two values -> packed bf16 pair (first value in the low half)
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
 {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7f800000u) == 0x7f800000u) {           // inf / nan: keep, quiet the nan
-        return (uint16_t)((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
-    }
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+
+// hi = bf16(x), lo = bf16(x - hi) for a pair: hi + lo carries ~16 significant bits
+__device__ __forceinline__ void split_bf16x2(float a, float b, uint32_t& hi, uint32_t& lo)
+{
+    hi = pack_bf16x2(a, b);
+    lo = pack_bf16x2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
+}
+
+// Buffer resource over [base, base + bytes): loads past the end return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+__device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0));
 }
 
 // Element loads/stores for the two storage types of q, k, v, o.

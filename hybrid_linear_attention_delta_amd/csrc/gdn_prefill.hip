@@ -42,6 +42,8 @@
 //   sigma:    k = 16*(e/4) + 4g + e%4 (bf16), which is what a result tile of
 //             the transposed product hands a lane, so results can be stored
 //             as next-stage operands without a shuffle.
+#include <stdlib.h>
+
 #include "gdn_common.h"
 #include "gdn_launch.h"
 
@@ -100,8 +102,15 @@ template <typename TIn>
 __device__ __forceinline__ typename Mma<TIn>::Frag frag_from(const float* x)
 {
     typename Mma<TIn>::Frag f;
+    if constexpr (sizeof(TIn) == 2) {
+        u32x4 h;
 #pragma unroll
-    for (int e = 0; e < Mma<TIn>::E; ++e) f[e] = Mma<TIn>::cvt(x[e]);
+        for (int i = 0; i < 4; ++i) h[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
+        f = __builtin_bit_cast(typename Mma<TIn>::Frag, h);
+    } else {
+#pragma unroll
+        for (int e = 0; e < Mma<TIn>::E; ++e) f[e] = x[e];
+    }
     return f;
 }
 
@@ -172,45 +181,51 @@ struct Rec {
     static constexpr int VT = DV / 16;     // d_v tiles
     static constexpr int WH_OFF = 0;                                  // [RT][DKS][64][E] W hi, sigma over d_k
     static constexpr int WL_OFF = WH_OFF + C * DK;                    // [RT][DKS][64][E] W lo (bf16 only)
-    static constexpr int K_OFF = WL_OFF + (SPLIT ? C * DK : 0);       // [MT][CKS][64][E] raw K^T, identity over chunk
+    static constexpr int Q_OFF = WL_OFF + (SPLIT ? C * DK : 0);       // [RT][DKS][64][E] raw Q, sigma over d_k
+    static constexpr int K_OFF = Q_OFF + C * DK;                      // [MT][CKS][64][E] raw K^T, identity over chunk
     static constexpr int PH_OFF = K_OFF + C * DK;                     // [RT][CKS][64][E] P hi
     static constexpr int PL_OFF = PH_OFF + C * C;                     // [RT][CKS][64][E] P lo (bf16 only)
     static constexpr int OPER_ELEMS = PL_OFF + (SPLIT ? C * C : 0);
     static constexpr size_t U_BYTE_OFF = ((size_t)OPER_ELEMS * sizeof(TIn) + 15) / 16 * 16;  // f32 [RT][VT][64][4]
     static constexpr size_t QS_BYTE_OFF = U_BYTE_OFF + (size_t)C * DV * 4;  // f32 [C]: rq_r e^{gamma_r}
     static constexpr size_t KSC_BYTE_OFF = QS_BYTE_OFF + (size_t)C * 4;     // f32 [C]: rk_j e^{gamma_L - gamma_j}
-    static constexpr size_t BYTES = KSC_BYTE_OFF + (size_t)C * 4;
+    static constexpr size_t DEC_BYTE_OFF = KSC_BYTE_OFF + (size_t)C * 4;    // f32 [4]: e^{gamma_L}, 0, 0, 0
+    static constexpr size_t BYTES = DEC_BYTE_OFF + 16;
     static_assert(C % KS == 0 && DK % KS == 0, "tile shape");
 };
 
-// hi/lo storage of four fp32 values (bf16: two roundings; fp32: exact, lo unused)
-template <typename TIn> struct Split4;
-template <> struct Split4<uint16_t> {
-    static __device__ __forceinline__ void store(uint16_t* hi, uint16_t* lo, f32x4 v)
-    {
-        u16x4 h, l;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint16_t hb = f32_to_bf16_bits(v[i]);
-            h[i] = hb;
-            l[i] = f32_to_bf16_bits(v[i] - bf16_bits_to_f32(hb));
-        }
-        *reinterpret_cast<u16x4*>(hi) = h;
-        *reinterpret_cast<u16x4*>(lo) = l;
-    }
-};
-template <> struct Split4<float> {
-    static __device__ __forceinline__ void store(float* hi, float*, f32x4 v) { *reinterpret_cast<f32x4*>(hi) = v; }
-};
+// Position of the four consecutive columns 16*tile + 4*g .. +3 inside an LDS
+// row stored in sigma order: within each 32-column block (bf16) the columns a
+// lane group g needs for one k-step (4g..4g+3 and 16+4g..16+4g+3) sit next to
+// each other, so an operand is one 16-byte read.  fp32: natural order.
+template <typename TIn>
+__device__ __forceinline__ int quad_pos(int tile, int g)
+{
+    if constexpr (sizeof(TIn) == 2) return (tile >> 1) * 32 + 8 * g + 4 * (tile & 1);
+    return tile * 16 + 4 * g;
+}
 
 // hi/lo operand fragments from E fp32 values
 template <typename TIn>
 __device__ __forceinline__ void split_frag(const float* x, typename Mma<TIn>::Frag& hi, typename Mma<TIn>::Frag& lo)
 {
+    if constexpr (sizeof(TIn) == 2) {
+        u32x4 h, l;
 #pragma unroll
-    for (int e = 0; e < Mma<TIn>::E; ++e) {
-        hi[e] = Mma<TIn>::cvt(x[e]);
-        lo[e] = Mma<TIn>::cvt(x[e] - Mma<TIn>::wide(hi[e]));
+        for (int i = 0; i < 4; ++i) {
+            uint32_t hh, ll;
+            split_bf16x2(x[2 * i], x[2 * i + 1], hh, ll);
+            h[i] = hh;
+            l[i] = ll;
+        }
+        hi = __builtin_bit_cast(typename Mma<TIn>::Frag, h);
+        lo = __builtin_bit_cast(typename Mma<TIn>::Frag, l);
+    } else {
+#pragma unroll
+        for (int e = 0; e < Mma<TIn>::E; ++e) {
+            hi[e] = x[e];
+            lo[e] = 0.f;
+        }
     }
 }
 
@@ -297,13 +312,58 @@ __device__ __forceinline__ ChunkInfo chunk_info(const ChunkInfo* tab, bool varle
 // ------------------------------------------------------------------ intra-chunk kernel
 
 template <typename TIn, int C, int DK, int DV>
+struct IntraCfg {
+    static constexpr int VP = DV < DK ? DV : DK;                 // value columns staged per pass
+    static constexpr int NVP = DV / VP;                           // passes over d_v
+    static constexpr int XR = DK > VP ? DK : VP;                  // rows of the transposed staging buffer
+    static constexpr int XP = C + 2 * (16 / (int)sizeof(TIn));    // its pitch (elements), 16-byte rows
+    static constexpr int AP = C + 4;                              // fp32 pitch of A and T
+    static constexpr int VEC = 16 / (int)sizeof(TIn);             // elements per 16-byte load
+};
+
+template <typename TIn, int C, int DK, int DV>
 struct IntraSmem {
-    static constexpr int KTP = C + 16 / (int)sizeof(TIn) * 2;  // K^T row pitch (elements), keeps 16B alignment
-    static constexpr int AP = C + 4;                          // fp32 pitch of A/T and P
-    TIn kt[DK * KTP];       // raw K, transposed: kt[col][j]
-    float at[C * AP];       // A, then T
-    float p[C * AP];        // P
-    float gam[C], beta[C], rk[C], rq[C];
+    using Cf = IntraCfg<TIn, C, DK, DV>;
+    TIn xt[Cf::XR * Cf::XP];  // K^T, later V^T (one pass of value columns): xt[col][j]
+    float at[C * Cf::AP];     // A, strictly lower
+    float tt[C * Cf::AP];     // T = (I + A)^{-1}, unit lower
+    float gam[C], beta[C], rk[C], rq[C], sw[C], sb[C];
+};
+
+// Rows j < len of a [tokens][H][D] tensor, columns [col0, col0 + NCOL), written
+// transposed into dst[col - col0][j]; rows >= len are zero.  Lane = row j, so
+// each LDS store instruction of a wave writes 64 consecutive elements (no bank
+// conflicts); wave w takes 16-byte column groups w, w + 4, ...  Values are held
+// in registers between the (early) global loads and the LDS stores.
+template <typename TIn, int C, int NCOL, int XP>
+struct TransposeStage {
+    static constexpr int VEC = 16 / (int)sizeof(TIn);
+    static constexpr int GROUPS = NCOL / VEC;
+    static constexpr int ITEMS = (GROUPS + 3) / 4;
+    uint4 buf[ITEMS];
+    __device__ __forceinline__ void load(const TIn* base, int64_t row_stride, int col0, int len, int lane, int wave)
+    {
+#pragma unroll
+        for (int s = 0; s < ITEMS; ++s) {
+            const int cg = wave + 4 * s;
+            if (cg < GROUPS && lane < len)
+                buf[s] = *reinterpret_cast<const uint4*>(base + (int64_t)lane * row_stride + col0 + cg * VEC);
+            else
+                buf[s] = uint4{0u, 0u, 0u, 0u};
+        }
+    }
+    __device__ __forceinline__ void store(TIn* dst, int lane, int wave) const
+    {
+        if (lane >= C) return;
+#pragma unroll
+        for (int s = 0; s < ITEMS; ++s) {
+            const int cg = wave + 4 * s;
+            if (cg >= GROUPS) break;
+            const TIn* e = reinterpret_cast<const TIn*>(&buf[s]);
+#pragma unroll
+            for (int u = 0; u < VEC; ++u) dst[(cg * VEC + u) * XP + lane] = e[u];
+        }
+    }
 };
 
 template <typename TIn, int C, int DK, int DV>
@@ -315,11 +375,14 @@ __global__ __launch_bounds__(256) void intra_kernel(const TIn* __restrict__ q, c
                                                     unsigned char* __restrict__ records, size_t record_bytes)
 {
     using M = Mma<TIn>;
+    using F = Mma<float>;
     using R = Rec<TIn, C, DK, DV>;
+    using Cf = IntraCfg<TIn, C, DK, DV>;
     using Sm = IntraSmem<TIn, C, DK, DV>;
     typedef typename M::Frag Frag;
     constexpr int KS = M::KS, E = M::E;
-    constexpr int KTP = Sm::KTP, AP = Sm::AP;
+    constexpr int XP = Cf::XP, AP = Cf::AP;
+    constexpr int RT = R::RT;
 
     extern __shared__ __align__(16) unsigned char smem_raw[];
     Sm& sm = *reinterpret_cast<Sm*>(smem_raw);
@@ -330,41 +393,30 @@ __global__ __launch_bounds__(256) void intra_kernel(const TIn* __restrict__ q, c
     if (!varlen && c * C >= T) return;
     const ChunkInfo ci = chunk_info(tab, varlen, c, C, T);
     const int len = ci.len;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave: scalar branches
     const int g16 = lane >> 4, l16 = lane & 15;
 
-    TIn* rec = reinterpret_cast<TIn*>(records + ((size_t)c * H + h) * record_bytes);
-    float* recU = reinterpret_cast<float*>(records + ((size_t)c * H + h) * record_bytes + R::U_BYTE_OFF);
+    unsigned char* recb = records + ((size_t)c * H + h) * record_bytes;
+    TIn* rec = reinterpret_cast<TIn*>(recb);
+    float* recU = reinterpret_cast<float*>(recb + R::U_BYTE_OFF);
 
-    auto row_ptr = [&](const TIn* base, int r, int d) -> const TIn* {
-        return base + ((int64_t)(ci.tok0 + r) * H + h) * d;
-    };
+    const int64_t row0 = (int64_t)ci.tok0 * H + h;  // row index of token tok0 in [tokens*H]
+    auto qk_row = [&](const TIn* base, int r) -> const TIn* { return base + (row0 + (int64_t)r * H) * DK; };
 
-    // ---- stage K^T (raw) into LDS; rows j >= len are zero
-    {
-        constexpr int VEC = 16 / sizeof(TIn);  // elements per 16-byte load
-        constexpr int PER_ROW = DK / VEC;
-        for (int idx = tid; idx < C * PER_ROW; idx += 256) {
-            const int j = idx / PER_ROW, cv = (idx % PER_ROW) * VEC;
-            TIn buf[VEC];
-            if (j < len) {
-                *reinterpret_cast<uint4*>(buf) = *reinterpret_cast<const uint4*>(row_ptr(k, j, DK) + cv);
-            } else {
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) buf[e] = 0;
-            }
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) sm.kt[(cv + e) * KTP + j] = buf[e];
-        }
-    }
+    // ---- global loads first: K (to be transposed), the first pass of V (held in registers)
+    TransposeStage<TIn, C, DK, XP> kst;
+    kst.load(k + row0 * DK, (int64_t)H * DK, 0, len, lane, wave);
+    TransposeStage<TIn, C, Cf::VP, XP> vst;
+    vst.load(v + row0 * DV, (int64_t)H * DV, 0, len, lane, wave);
+
     // ---- gates: gamma (inclusive scan within the chunk), beta; rows >= len: g = 0, beta = 0
     if (wave == 0) {
         float gv = 0.f, bv = 0.f;
         if (lane < len) {
-            gv = g[(int64_t)(ci.tok0 + lane) * H + h];
-            bv = beta[(int64_t)(ci.tok0 + lane) * H + h];
+            gv = g[row0 + (int64_t)lane * H];
+            bv = beta[row0 + (int64_t)lane * H];
         }
-        if (lane >= C) gv = 0.f;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
             float y = __shfl_up(gv, off, 64);
@@ -380,8 +432,9 @@ __global__ __launch_bounds__(256) void intra_kernel(const TIn* __restrict__ q, c
         const int r = tid >> 2, part = tid & 3;
         float sk = 0.f, sq = 0.f;
         if (r < C && r < len) {
-            const TIn* kr = row_ptr(k, r, DK);
-            const TIn* qr = row_ptr(q, r, DK);
+            const TIn* kr = qk_row(k, r);
+            const TIn* qr = qk_row(q, r);
+#pragma unroll 4
             for (int cc = part * 4; cc < DK; cc += 16) {
                 float xk[4], xq[4];
                 Quad<TIn>::load(kr + cc, xk);
@@ -398,115 +451,168 @@ __global__ __launch_bounds__(256) void intra_kernel(const TIn* __restrict__ q, c
             sm.rq[r] = live ? (l2norm ? 1.0f / sqrtf(sq + kNormEps) : 1.0f) : 0.f;
         }
     }
-    __syncthreads();
-
-    // ---- G = K K^T, R = Q K^T on lower tiles -> A (strict), P (inclusive)
-    {
-        constexpr int NTILE = R::RT * (R::RT + 1) / 2;
-        for (int job = wave; job < 2 * NTILE; job += 4) {
-            const bool isP = job >= NTILE;
-            int tt = isP ? job - NTILE : job;
-            int ti = 0;
-            while (tt > ti) { tt -= ti + 1; ++ti; }
-            const int tj = tt;  // tj <= ti
-            const int ra = ti * 16 + l16, rb = tj * 16 + l16;
-            const TIn* pa = row_ptr(isP ? q : k, ra, DK);
-            const TIn* pb = row_ptr(k, rb, DK);
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-            for (int ks = 0; ks < R::DKS; ++ks) {
-                const int col = ks * KS + g16 * E;
-                Frag fa = ra < len ? ld_frag<TIn>(pa + col) : zero_frag<TIn>();
-                Frag fb = rb < len ? ld_frag<TIn>(pb + col) : zero_frag<TIn>();
-                acc = M::mma(fa, fb, acc);
-            }
-            const int j = tj * 16 + l16;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = ti * 16 + 4 * g16 + i;
-                float val = 0.f;
-                if (isP) {
-                    if (j <= r) val = sm.rq[r] * sm.rk[j] * acc[i] * expf(sm.gam[r] - sm.gam[j]);
-                    sm.p[r * AP + j] = val;
-                } else {
-                    if (j < r) val = sm.beta[r] * sm.rk[r] * sm.rk[j] * acc[i] * expf(sm.gam[r] - sm.gam[j]);
-                    sm.at[r * AP + j] = val;
-                }
-            }
-        }
-        // zero the upper tiles so later row reads see exact zeros
-        for (int idx = tid; idx < C * C; idx += 256) {
-            const int r = idx / C, j = idx % C;
-            if ((j >> 4) > (r >> 4)) {
-                sm.at[r * AP + j] = 0.f;
-                sm.p[r * AP + j] = 0.f;
-            }
-        }
-    }
+    kst.store(sm.xt, lane, wave);
     __syncthreads();
 
     const float gL = sm.gam[C - 1];  // rows >= len carry g = 0, so this is gamma at len-1
+    if (tid < C) {
+        const int j = tid;
+        sm.sw[j] = sm.beta[j] * expf(sm.gam[j]) * sm.rk[j];  // W = T diag(sw) K
+        sm.sb[j] = sm.beta[j];                                 // U = T diag(sb) V
+        float* qs = reinterpret_cast<float*>(recb + R::QS_BYTE_OFF);
+        float* ksc = reinterpret_cast<float*>(recb + R::KSC_BYTE_OFF);
+        qs[j] = sm.rq[j] * expf(sm.gam[j]);
+        ksc[j] = sm.rk[j] * expf(gL - sm.gam[j]);
+    }
 
-    if (wave == 0) {
-        // ---- T = (I + A)^{-1}: lane c solves column c, (I + A) t = e_c, rows in order
-        float t[C];
-        const int col = lane;
+    // ---- G = K K^T lower tiles -> A (strict, LDS);  R^T = K Q^T -> P fragments (sigma over j)
+    {
+        constexpr int NG = RT * (RT + 1) / 2;
+        constexpr int UPF = KS / 16;  // j tiles per P fragment
+        // P fragment jobs: (rt, ks) with ks*KS <= rt*16 + 15
+        constexpr int NP = [] {
+            int n = 0;
+            for (int rt = 0; rt < RT; ++rt) n += (rt * 16 + 16 + KS - 1) / KS;
+            return n;
+        }();
+        for (int job = wave; job < NG + NP; job += 4) {
+            if (job < NG) {
+                int tt_ = job, ti = 0;
+                while (tt_ > ti) { tt_ -= ti + 1; ++ti; }
+                const int tj = tt_;
+                const int ra = ti * 16 + l16, rb = tj * 16 + l16;
+                const TIn* pa = qk_row(k, ra);
+                const TIn* pb = qk_row(k, rb);
+                Frag fa[R::DKS], fb[R::DKS];
 #pragma unroll
-        for (int r = 0; r < C; ++r) {
-            float acc = (r == col) ? 1.f : 0.f;
-            const float* arow = sm.at + r * AP;
+                for (int ks = 0; ks < R::DKS; ++ks) {
+                    fa[ks] = ra < len ? ld_frag<TIn>(pa + ks * KS + g16 * E) : zero_frag<TIn>();
+                    fb[ks] = rb < len ? ld_frag<TIn>(pb + ks * KS + g16 * E) : zero_frag<TIn>();
+                }
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int j4 = 0; j4 < r; j4 += 4) {
-                f32x4 a4 = *reinterpret_cast<const f32x4*>(arow + j4);
+                for (int ks = 0; ks < R::DKS; ++ks) acc = M::mma(fa[ks], fb[ks], acc);
+                const int j = tj * 16 + l16;
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (j4 + e < r) acc -= a4[e] * t[j4 + e];
+                for (int i = 0; i < 4; ++i) {
+                    const int r = ti * 16 + 4 * g16 + i;
+                    float val = 0.f;
+                    if (j < r) val = sm.beta[r] * sm.rk[r] * sm.rk[j] * acc[i] * expf(sm.gam[r] - sm.gam[j]);
+                    sm.at[r * AP + j] = val;
+                }
+            } else {
+                int f = job - NG, rt = 0;
+                while (f >= (rt * 16 + 16 + KS - 1) / KS) { f -= (rt * 16 + 16 + KS - 1) / KS; ++rt; }
+                const int ks = f;
+                const int r = rt * 16 + l16;  // fixed per lane: B operand column
+                const TIn* pq = qk_row(q, r);
+                Frag fq[R::DKS];
+#pragma unroll
+                for (int dk = 0; dk < R::DKS; ++dk)
+                    fq[dk] = r < len ? ld_frag<TIn>(pq + dk * KS + g16 * E) : zero_frag<TIn>();
+                float x[E];
+#pragma unroll
+                for (int u = 0; u < UPF; ++u) {
+                    const int tj = ks * UPF + u;
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                    if (tj <= rt) {
+                        const int rk_row = tj * 16 + l16;
+                        const TIn* pk = qk_row(k, rk_row);
+#pragma unroll
+                        for (int dk = 0; dk < R::DKS; ++dk) {
+                            const Frag fk = rk_row < len ? ld_frag<TIn>(pk + dk * KS + g16 * E) : zero_frag<TIn>();
+                            acc = M::mma(fk, fq[dk], acc);
+                        }
+                    }
+                    // lane holds R[r][j] for j = tj*16 + 4*g16 + i
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int j = tj * 16 + 4 * g16 + i;
+                        x[u * 4 + i] = (tj <= rt && j <= r)
+                                           ? sm.rq[r] * sm.rk[j] * acc[i] * expf(sm.gam[r] - sm.gam[j])
+                                           : 0.f;
+                    }
+                }
+                Frag hi, lo;
+                split_frag<TIn>(x, hi, lo);
+                const size_t fo = ((size_t)(rt * R::CKS + ks) * 64 + lane) * E;
+                st_frag<TIn>(rec + R::PH_OFF + fo, hi);
+                if constexpr (R::SPLIT) st_frag<TIn>(rec + R::PL_OFF + fo, lo);
             }
-            t[r] = acc;
         }
-        if (col < C) {
-#pragma unroll
-            for (int r = 0; r < C; ++r) sm.at[r * AP + col] = t[r];
-        }
-    } else {
-        // ---- waves 1..3: raw K^T and P fragments (identity over the chunk), row scales
-        const int w3 = wave - 1;
-        for (int f = w3; f < R::MT * R::CKS; f += 3) {
-            const int mt = f / R::CKS, ks = f % R::CKS;
-            const int m = mt * 16 + l16;
-            const Frag fk = *reinterpret_cast<const Frag*>(sm.kt + m * KTP + ks * KS + g16 * E);
-            st_frag<TIn>(rec + R::K_OFF + ((size_t)f * 64 + lane) * E, fk);
-        }
-        for (int f = w3; f < R::RT * R::CKS; f += 3) {
-            const int rt = f / R::CKS, ks = f % R::CKS;
+        // raw Q fragments in sigma order over d_k (rows >= len are zero)
+        for (int f = wave; f < RT * R::DKS; f += 4) {
+            const int rt = f / R::DKS, ks = f % R::DKS;
             const int r = rt * 16 + l16;
-            const int j0 = ks * KS + g16 * E;
-            float x[E];
-#pragma unroll
-            for (int e = 0; e < E; ++e) x[e] = sm.p[r * AP + j0 + e];
-            Frag hi, lo;
-            split_frag<TIn>(x, hi, lo);
-            st_frag<TIn>(rec + R::PH_OFF + ((size_t)f * 64 + lane) * E, hi);
-            if constexpr (R::SPLIT) st_frag<TIn>(rec + R::PL_OFF + ((size_t)f * 64 + lane) * E, lo);
+            Frag fq;
+            if (r < len) {
+                fq = M::ld_sigma(qk_row(q, r) + ks * KS, g16);
+            } else {
+                fq = zero_frag<TIn>();
+            }
+            st_frag<TIn>(rec + R::Q_OFF + ((size_t)f * 64 + lane) * E, fq);
         }
-        if (wave == 1 && lane < C) {
-            float* qs = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(rec) + R::QS_BYTE_OFF);
-            float* ksc = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(rec) + R::KSC_BYTE_OFF);
-            const bool live = lane < len;
-            qs[lane] = live ? sm.rq[lane] * expf(sm.gam[lane]) : 0.f;
-            ksc[lane] = live ? sm.rk[lane] * expf(gL - sm.gam[lane]) : 0.f;
+        // raw K^T fragments for the state update (identity over the chunk)
+        for (int f = wave; f < R::MT * R::CKS; f += 4) {
+            const int mt = f / R::CKS, ks = f % R::CKS;
+            const Frag fk = *reinterpret_cast<const Frag*>(sm.xt + (mt * 16 + l16) * XP + ks * KS + g16 * E);
+            st_frag<TIn>(rec + R::K_OFF + ((size_t)f * 64 + lane) * E, fk);
         }
     }
     __syncthreads();
 
-    // ---- W^T = K^T T_s^T with T_s = T diag(beta e^{gamma} rk) (T_s split hi/lo, K exact);
-    //      the result tiles are the sigma-ordered W fragments, stored hi/lo
+    // ---- T = (I + A)^{-1}, blocked by 16: diagonal blocks by substitution, then
+    //      T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj on fp32 MFMA, by block distance
+    if (wave < RT) {
+        const int b0 = wave * 16, col = l16;
+        float t[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float acc = (r == col) ? 1.f : 0.f;
+            const float* arow = sm.at + (b0 + r) * AP + b0;
+#pragma unroll
+            for (int j = 0; j < r; ++j) acc -= arow[j] * t[j];
+            t[r] = acc;
+        }
+        if (lane < 16) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sm.tt[(b0 + r) * AP + b0 + col] = t[r];
+        }
+    }
+    for (int idx = tid; idx < C * C; idx += 256) {  // strictly upper blocks of T are zero
+        const int r = idx / C, j = idx % C;
+        if ((j >> 4) > (r >> 4)) sm.tt[r * AP + j] = 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int d = 1; d < RT; ++d) {
+        for (int jb = wave; jb + d < RT; jb += 4) {
+            const int ib = jb + d;
+            f32x4 X = {0.f, 0.f, 0.f, 0.f};
+            for (int mb = jb; mb < ib; ++mb) {
+                const f32x4 fa = *reinterpret_cast<const f32x4*>(sm.at + (ib * 16 + l16) * AP + mb * 16 + 4 * g16);
+                f32x4 fb;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) fb[e] = sm.tt[(mb * 16 + 4 * g16 + e) * AP + jb * 16 + l16];
+                X = F::mma(fa, fb, X);
+            }
+            const f32x4 fd = *reinterpret_cast<const f32x4*>(sm.tt + (ib * 16 + l16) * AP + ib * 16 + 4 * g16);
+            f32x4 Y = {0.f, 0.f, 0.f, 0.f};
+            Y = F::mma(fd, X, Y);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sm.tt[(ib * 16 + 4 * g16 + e) * AP + jb * 16 + l16] = -Y[e];
+        }
+        __syncthreads();
+    }
+
+    // ---- W^T = K^T (T diag(sw))^T, T diag(sw) split hi/lo, K exact: the result tiles
+    //      are the sigma-ordered W fragments of the chain kernel, stored hi/lo
     {
-        constexpr int MT_PER = KS / 16;  // d_k tiles per W fragment (2 bf16, 1 fp32)
-        for (int f = wave; f < R::RT * R::DKS; f += 4) {
+        constexpr int MT_PER = KS / 16;
+        for (int f = wave; f < RT * R::DKS; f += 4) {
             const int rt = f / R::DKS, ks = f % R::DKS;
-            const int r = rt * 16 + l16;                    // B operand column = chunk row r
-            const int nks = (rt * 16 + 16 + KS - 1) / KS;   // T[r][j] = 0 for j > r
+            const int r = rt * 16 + l16;
+            const int nks = (rt * 16 + 16 + KS - 1) / KS;  // T[r][j] = 0 for j > r
             f32x4 acc[MT_PER];
 #pragma unroll
             for (int u = 0; u < MT_PER; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -514,21 +620,16 @@ __global__ __launch_bounds__(256) void intra_kernel(const TIn* __restrict__ q, c
                 const int j0 = jk * KS + g16 * E;
                 float x[E];
 #pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const int j = j0 + e;
-                    x[e] = sm.at[r * AP + j] * sm.beta[j] * expf(sm.gam[j]) * sm.rk[j];
-                }
+                for (int e = 0; e < E; ++e) x[e] = sm.tt[r * AP + j0 + e] * sm.sw[j0 + e];
                 Frag bh, bl;
                 split_frag<TIn>(x, bh, bl);
 #pragma unroll
                 for (int u = 0; u < MT_PER; ++u) {
-                    const int m = (ks * MT_PER + u) * 16 + l16;
-                    const Frag fa = *reinterpret_cast<const Frag*>(sm.kt + m * KTP + j0);
+                    const Frag fa = *reinterpret_cast<const Frag*>(sm.xt + ((ks * MT_PER + u) * 16 + l16) * XP + j0);
                     acc[u] = M::mma(fa, bh, acc[u]);
                     if constexpr (R::SPLIT) acc[u] = M::mma(fa, bl, acc[u]);
                 }
             }
-            // lane holds W[r'][mt*16 + 4*g16 + i] with r' = rt*16 + l16: exactly sigma order
             float x[E];
 #pragma unroll
             for (int u = 0; u < MT_PER; ++u)
@@ -540,54 +641,134 @@ __global__ __launch_bounds__(256) void intra_kernel(const TIn* __restrict__ q, c
             if constexpr (R::SPLIT) st_frag<TIn>(rec + R::WL_OFF + ((size_t)f * 64 + lane) * E, lo);
         }
     }
-    // ---- U = (T diag(beta)) V (T diag(beta) split hi/lo, V exact), stored as fp32 result tiles
-    {
-        for (int f = wave; f < R::RT * R::VT; f += 4) {
-            const int rt = f / R::VT, ct = f % R::VT;
-            const int r = rt * 16 + l16;    // A operand row
-            const int col = ct * 16 + l16;  // B operand column (value index)
+
+    // ---- U = (T diag(sb)) V, T diag(sb) split hi/lo, V exact, in passes of VP value columns
+#pragma unroll 1
+    for (int pass = 0; pass < Cf::NVP; ++pass) {
+        if (pass > 0) vst.load(v + row0 * DV, (int64_t)H * DV, pass * Cf::VP, len, lane, wave);
+        __syncthreads();  // xt free (K^T readers done, or the previous pass done)
+        vst.store(sm.xt, lane, wave);
+        __syncthreads();
+        constexpr int CT = Cf::VP / 16;
+        for (int f = wave; f < RT * CT; f += 4) {
+            const int rt = f / CT, ctl = f % CT;
+            const int r = rt * 16 + l16;
             const int nks = (rt * 16 + 16 + KS - 1) / KS;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             for (int jk = 0; jk < nks; ++jk) {
                 const int j0 = jk * KS + g16 * E;
                 float xa[E];
-                Frag fb;
 #pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const int j = j0 + e;
-                    xa[e] = sm.at[r * AP + j] * sm.beta[j];
-                    fb[e] = j < len ? v[((int64_t)(ci.tok0 + j) * H + h) * DV + col] : (TIn)0;
-                }
+                for (int e = 0; e < E; ++e) xa[e] = sm.tt[r * AP + j0 + e] * sm.sb[j0 + e];
                 Frag ah, al;
                 split_frag<TIn>(xa, ah, al);
+                const Frag fb = *reinterpret_cast<const Frag*>(sm.xt + (ctl * 16 + l16) * XP + j0);
                 acc = M::mma(ah, fb, acc);
                 if constexpr (R::SPLIT) acc = M::mma(al, fb, acc);
             }
-            *reinterpret_cast<f32x4*>(recU + ((size_t)f * 64 + lane) * 4) = acc;
+            const int ct = pass * CT + ctl;
+            *reinterpret_cast<f32x4*>(recU + ((size_t)(rt * R::VT + ct) * 64 + lane) * 4) = acc;
         }
     }
-    if (tid == 0) decay_out[c * H + h] = expf(gL);
+    if (tid == 0) {
+        decay_out[c * H + h] = expf(gL);
+        *reinterpret_cast<f32x4*>(recb + R::DEC_BYTE_OFF) = f32x4{expf(gL), 0.f, 0.f, 0.f};
+    }
 }
 
 // ------------------------------------------------------------------ chain kernel
 
+// LDS of the chain kernel: the rounded state copy, Delta^T (two layouts), and a
+// ring of W and Q operand fragments filled by LDS-DMA (buffer_load ... lds),
+// one region per wave and ring stage.  Two stages when they fit (bf16), so the
+// fragments of chunk c+1 stream in while chunk c computes.
 template <typename TIn, int C, int DK, int NT, bool SPLIT>
-struct ChainSmem {
-    static constexpr int SP = DK + 16 / (int)sizeof(TIn);  // state copy pitch
+struct ChainLds {
+    static constexpr int SP = DK + 16 / (int)sizeof(TIn);  // state copy pitch (dwords = 4 mod 32)
     static constexpr int DP = C + 16 / (int)sizeof(TIn);   // Delta^T pitch
     static constexpr int NS = SPLIT ? 2 : 1;
-    TIn sr[NS][16 * NT * SP];   // rounded state rows S[r][col] (hi, lo)
-    TIn dt[NS][16 * NT * DP];   // Delta^T[r][j] (hi, lo)
-    TIn ds[NS][16 * NT * DP];   // (kscale o Delta)^T[r][j] (hi, lo)
+    static constexpr int DKS = DK / Mma<TIn>::KS;
+    static constexpr int RING_FRAGS = 2 * DKS;              // W then Q fragments of one chunk row tile
+    static constexpr size_t SR_BYTES = (size_t)NS * 16 * NT * SP * sizeof(TIn);
+    static constexpr size_t D_BYTES = (size_t)NS * 16 * NT * DP * sizeof(TIn);
+    static constexpr size_t FIXED = (SR_BYTES + 2 * D_BYTES + 255) / 256 * 256;
+    static constexpr size_t SINK_BYTES = 4 * 1024;           // per-wave 1 KB landing slot of L2 prefetches
+    static constexpr size_t STAGE_BYTES = (size_t)4 * RING_FRAGS * 1024;
+    static constexpr int STAGES = FIXED + SINK_BYTES + 2 * STAGE_BYTES <= 160 * 1024 ? 2 : 1;
+    static constexpr size_t RING_OFF = FIXED + SINK_BYTES;
+    static constexpr size_t BYTES = RING_OFF + STAGES * STAGE_BYTES;
+    static_assert(BYTES <= 160 * 1024, "chain kernel LDS");
 };
+
+// Register operands of one chunk step for one wave, loaded one step ahead.
+template <typename TIn, int C, int DK, int DV, int NT, bool SW>
+struct ChainOps {
+    using R = Rec<TIn, C, DK, DV>;
+    typedef typename Mma<TIn>::Frag Frag;
+    static constexpr int MT_W = (R::MT + 3) / 4;
+    Frag wl[SW ? R::DKS : 1];
+    Frag ph[R::CKS];
+    Frag pl[R::SPLIT ? R::CKS : 1];
+    Frag k[MT_W][R::CKS];
+    f32x4 u[NT];
+    f32x4 qs, ks;
+    float dec;
+    int32_t tok0, len;
+};
+
+template <typename TIn> struct OStore;
+template <> struct OStore<uint16_t> {
+    static __device__ __forceinline__ void st(__amdgpu_buffer_rsrc_t r, uint32_t voff, float x)
+    {
+        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(x), r, (int)voff, 0, 0);
+    }
+};
+template <> struct OStore<float> {
+    static __device__ __forceinline__ void st(__amdgpu_buffer_rsrc_t r, uint32_t voff, float x)
+    {
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, (int)voff, 0, 0);  // payload is raw bits
+    }
+};
+
+// Store four fp32 values as operand elements at p (hi) and p2 (lo, bf16 only).
+template <typename TIn, bool LO>
+__device__ __forceinline__ void store_quad(TIn* p, TIn* p2, f32x4 v)
+{
+    if constexpr (sizeof(TIn) == 2) {
+        uint32_t h0, l0, h1, l1;
+        split_bf16x2(v.x, v.y, h0, l0);
+        split_bf16x2(v.z, v.w, h1, l1);
+        *reinterpret_cast<u32x2*>(p) = u32x2{h0, h1};
+        if constexpr (LO) *reinterpret_cast<u32x2*>(p2) = u32x2{l0, l1};
+    } else {
+        *reinterpret_cast<f32x4*>(p) = v;
+    }
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Workgroup barrier that orders LDS only: waits for this wave's LDS operations
+// (lgkmcnt) but not for its outstanding global loads or LDS-DMA transfers, which
+// the chain kernel tracks itself with counted vmcnt waits.  The empty asm
+// statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt/expcnt untouched
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
 
 // SPLIT_S: the state enters W S^T and Q S^T as hi + lo (else hi only).
 // SPLIT_W: W enters as hi + lo (else hi only).
+// Workgroups are mapped so that all row tiles of one (sequence, head) pair run
+// on one XCD (workgroups are dealt to the 8 XCDs round-robin): they read the
+// same per-chunk records, which then come from that XCD's L2.
 template <typename TIn, int C, int DK, int DV, int NT, bool SPLIT_S, bool SPLIT_W>
-__global__ __launch_bounds__(256) void chain_kernel(const TIn* __restrict__ q, const int32_t* __restrict__ header,
+__global__ __launch_bounds__(256) void chain_kernel(const int32_t* __restrict__ header,
                                                     const ChunkInfo* __restrict__ tab,
                                                     const int32_t* __restrict__ seq_first, int32_t varlen, int64_t T,
-                                                    int32_t H, const float* __restrict__ decay,
+                                                    int32_t H, int32_t pairs, const float* __restrict__ decay,
                                                     const unsigned char* __restrict__ records, size_t record_bytes,
                                                     const float* __restrict__ init_state, float* __restrict__ final_state,
                                                     TIn* __restrict__ o, float scale)
@@ -597,19 +778,33 @@ __global__ __launch_bounds__(256) void chain_kernel(const TIn* __restrict__ q, c
     constexpr bool SPL = R::SPLIT;
     constexpr bool SS = SPL && SPLIT_S;
     constexpr bool SW = SPL && SPLIT_W;
-    using Sm = ChainSmem<TIn, C, DK, NT, SPL>;
+    using L = ChainLds<TIn, C, DK, NT, SPL>;
+    using Ops = ChainOps<TIn, C, DK, DV, NT, SW>;
     typedef typename M::Frag Frag;
     constexpr int KS = M::KS, E = M::E;
-    constexpr int SP = Sm::SP, DP = Sm::DP;
-    constexpr int MT_W = (R::MT + 3) / 4;  // d_k tiles per wave (state update)
+    constexpr int SP = L::SP, DP = L::DP, NS = L::NS;
+    constexpr int MT_W = Ops::MT_W;
+    constexpr int TILES = DV / (16 * NT);
+    constexpr uint32_t FB = 64 * 16;  // bytes of one operand fragment (64 lanes x 16 B)
+    constexpr uint32_t EB = sizeof(TIn);
 
-    __shared__ __align__(16) Sm sm;
+    extern __shared__ __align__(256) unsigned char lds[];
+    TIn* sr = reinterpret_cast<TIn*>(lds);                                   // [NS][16 NT][SP]
+    TIn* dt = reinterpret_cast<TIn*>(lds + L::SR_BYTES);                     // [NS][16 NT][DP]
+    TIn* ds = reinterpret_cast<TIn*>(lds + L::SR_BYTES + L::D_BYTES);        // [NS][16 NT][DP]
+    unsigned char* sink = lds + L::FIXED;                                    // [4][1 KB]
+    unsigned char* ring = lds + L::RING_OFF;                                 // [STAGES][4][RING_FRAGS][1 KB]
+    constexpr int SR_LO = (NS - 1) * 16 * NT * SP;
+    constexpr int D_LO = (NS - 1) * 16 * NT * DP;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave: scalar branches
     const int g16 = lane >> 4, l16 = lane & 15;
-    const int h = blockIdx.y;
-    const int n = blockIdx.z;
-    const int row0 = blockIdx.x * 16 * NT;  // first state row (value index) of this workgroup
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int pair = xcd + 8 * (slot / TILES);
+    if (pair >= pairs) return;
+    const int n = pair / H, h = pair % H;
+    const int row0 = (slot % TILES) * 16 * NT;  // first state row (value index) of this workgroup
 
     int64_t c_begin, c_end;
     if (varlen) {
@@ -634,8 +829,8 @@ __global__ __launch_bounds__(256) void chain_kernel(const TIn* __restrict__ q, c
                 S[a][nt] = *reinterpret_cast<const f32x4*>(init_state + st_base +
                                                            (size_t)(row0 + nt * 16 + l16) * DK + mt * 16 + 4 * g16);
             if (mt < R::MT) {
-                const int off = (nt * 16 + l16) * SP + mt * 16 + 4 * g16;
-                Split4<TIn>::store(sm.sr[0] + off, sm.sr[Sm::NS - 1] + off, S[a][nt]);
+                const int off = (nt * 16 + l16) * SP + quad_pos<TIn>(mt, g16);
+                store_quad<TIn, SPL>(sr + off, sr + SR_LO + off, S[a][nt]);
             }
         }
     }
@@ -643,118 +838,265 @@ __global__ __launch_bounds__(256) void chain_kernel(const TIn* __restrict__ q, c
 
     const bool has_rt = wave < R::RT;
     const int rt = wave;
+    const int pks = (rt * 16 + 16 + KS - 1) / KS;  // P k-steps up to the diagonal
 
-    for (int64_t c = c_begin; c < c_end; ++c) {
-        const ChunkInfo ci = chunk_info(tab, varlen, c, C, T);
-        const unsigned char* recb = records + ((size_t)c * H + h) * record_bytes;
-        const TIn* rec = reinterpret_cast<const TIn*>(recb);
-        const float* recU = reinterpret_cast<const float*>(recb + R::U_BYTE_OFF);
-        const float* qsc = reinterpret_cast<const float*>(recb + R::QS_BYTE_OFF);
-        const float* ksc = reinterpret_cast<const float*>(recb + R::KSC_BYTE_OFF);
+    // per-lane byte offsets inside a record (fragments are 64 lanes x 16 B)
+    const uint32_t lane_b = (uint32_t)lane * 16;
+    const uint32_t offWH = R::WH_OFF * EB + (uint32_t)rt * R::DKS * FB + lane_b;
+    const uint32_t offWL = R::WL_OFF * EB + (uint32_t)rt * R::DKS * FB + lane_b;
+    const uint32_t offQ = R::Q_OFF * EB + (uint32_t)rt * R::DKS * FB + lane_b;
+    const uint32_t offPH = R::PH_OFF * EB + (uint32_t)rt * R::CKS * FB + lane_b;
+    const uint32_t offPL = R::PL_OFF * EB + (uint32_t)rt * R::CKS * FB + lane_b;
+    const uint32_t offK = R::K_OFF * EB + lane_b;
+    const uint32_t offU = (uint32_t)R::U_BYTE_OFF + ((uint32_t)(rt * R::VT + (row0 >> 4)) * 64 + lane) * 16;
+    const uint32_t offQS = (uint32_t)R::QS_BYTE_OFF + (uint32_t)(rt * 16 + 4 * g16) * 4;
+    const uint32_t offKS = (uint32_t)R::KSC_BYTE_OFF + (uint32_t)(rt * 16 + 4 * g16) * 4;
+    const uint32_t rowstride_o = (uint32_t)H * DV * EB;
 
-        f32x4 Y[NT];
-        if (has_rt) {
-            // X = W S^T, Y = Q S^T over all of d_k; Delta = U - X
-            f32x4 X[NT];
+    auto rec_rsrc = [&](int64_t c) {
+        return make_rsrc(records + ((size_t)c * H + h) * record_bytes, (uint32_t)R::BYTES);
+    };
+    auto ring_frag = [&](int64_t c, int f) -> unsigned char* {
+        return ring + ((size_t)((c % L::STAGES) * 4 + wave) * L::RING_FRAGS + f) * 1024;
+    };
+    // W and Q fragment ks of chunk c -> this wave's ring region (LDS-DMA, no registers)
+    auto dma_ks = [&](const __amdgpu_buffer_rsrc_t& rr, int64_t c, int ks) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_ptr_t)ring_frag(c, ks), 16, offWH, ks * FB, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_ptr_t)ring_frag(c, R::DKS + ks), 16, offQ, ks * FB, 0, 0);
+    };
+    // register operands of chunk c, in NLD independent groups (issued spread over a step)
+    constexpr int NLD = 4;
+    auto load_part = [&](Ops& op, const __amdgpu_buffer_rsrc_t& rr, int64_t c, int part) {
+        if (part == 0) {
+            const ChunkInfo ci = chunk_info(tab, varlen, c, C, T);
+            op.tok0 = ci.tok0;
+            op.len = ci.len;
+            op.dec = __builtin_bit_cast(f32x4, buf_load16(rr, (uint32_t)R::DEC_BYTE_OFF, 0)).x;
+            if (has_rt) {
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                X[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-                Y[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int nt = 0; nt < NT; ++nt) op.u[nt] = __builtin_bit_cast(f32x4, buf_load16(rr, offU, nt * FB));
+                op.qs = __builtin_bit_cast(f32x4, buf_load16(rr, offQS, 0));
+                op.ks = __builtin_bit_cast(f32x4, buf_load16(rr, offKS, 0));
             }
-            const int rq = rt * 16 + l16;  // Q row this lane supplies
-            const TIn* qrow = q + ((int64_t)(ci.tok0 + rq) * H + h) * DK;
-            const bool qlive = rq < ci.len;
-#pragma unroll 2
-            for (int ks = 0; ks < R::DKS; ++ks) {
-                const size_t fo = ((size_t)(rt * R::DKS + ks) * 64 + lane) * E;
-                const Frag fwh = ld_frag<TIn>(rec + R::WH_OFF + fo);
-                Frag fwl;
-                if constexpr (SW) fwl = ld_frag<TIn>(rec + R::WL_OFF + fo);
-                const Frag fq = qlive ? M::ld_sigma(qrow + ks * KS, g16) : zero_frag<TIn>();
+        } else if (part == 1) {
+            if (has_rt) {
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    const int so = (nt * 16 + l16) * SP + ks * KS;
-                    const Frag bh = M::ld_sigma(sm.sr[0] + so, g16);
-                    X[nt] = M::mma(fwh, bh, X[nt]);
-                    Y[nt] = M::mma(fq, bh, Y[nt]);
-                    if constexpr (SW) X[nt] = M::mma(fwl, bh, X[nt]);
-                    if constexpr (SS) {
-                        const Frag bl = M::ld_sigma(sm.sr[1] + so, g16);
-                        X[nt] = M::mma(fwh, bl, X[nt]);
-                        Y[nt] = M::mma(fq, bl, Y[nt]);
-                    }
+                for (int ks = 0; ks < R::CKS; ++ks) {
+                    op.ph[ks] = __builtin_bit_cast(Frag, buf_load16(rr, offPH, ks * FB));
+                    if constexpr (SPL) op.pl[ks] = __builtin_bit_cast(Frag, buf_load16(rr, offPL, ks * FB));
+                }
+                if constexpr (SW) {
+#pragma unroll
+                    for (int ks = 0; ks < R::DKS; ++ks)
+                        op.wl[ks] = __builtin_bit_cast(Frag, buf_load16(rr, offWL, ks * FB));
                 }
             }
-            const f32x4 qs4 = *reinterpret_cast<const f32x4*>(qsc + rt * 16 + 4 * g16);
-            const f32x4 ks4 = *reinterpret_cast<const f32x4*>(ksc + rt * 16 + 4 * g16);
+        } else {
+            // K fragments, half of this wave's d_k tiles per part
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                Y[nt] *= qs4;
-                const f32x4 u = *reinterpret_cast<const f32x4*>(recU + ((size_t)(rt * R::VT + (row0 >> 4) + nt) * 64 + lane) * 4);
-                const f32x4 d = u - X[nt];
-                // Delta^T[r][j] for j = rt*16 + 4*g16 + i
-                const int off = (nt * 16 + l16) * DP + rt * 16 + 4 * g16;
-                Split4<TIn>::store(sm.dt[0] + off, sm.dt[Sm::NS - 1] + off, d);
-                Split4<TIn>::store(sm.ds[0] + off, sm.ds[Sm::NS - 1] + off, d * ks4);
+            for (int a = 0; a < MT_W; ++a) {
+                if ((a & 1) != (part & 1)) continue;
+                const int mt = wave + 4 * a;
+                if (mt < R::MT) {
+#pragma unroll
+                    for (int ks = 0; ks < R::CKS; ++ks)
+                        op.k[a][ks] = __builtin_bit_cast(Frag, buf_load16(rr, offK, (mt * R::CKS + ks) * FB));
+                }
             }
         }
-        __syncthreads();
+    };
+    // Cooperative L2 prefetch of the shared part of chunk c's record (W, Q, K, P):
+    // the TILES workgroups of this (sequence, head) each pull 1/TILES of it into
+    // their XCD's L2 (landing in a scratch LDS slot), so the loads one step later hit L2.
+    constexpr uint32_t SHARED_BYTES = (uint32_t)R::U_BYTE_OFF;
+    constexpr uint32_t PF_INSTR = (SHARED_BYTES / 1024 + TILES * 4 - 1) / (TILES * 4);  // per wave
+    const int tile = slot % TILES;
+    auto prefetch = [&](int64_t c) {
+        const __amdgpu_buffer_rsrc_t rr = rec_rsrc(c);
+#pragma unroll
+        for (uint32_t i = 0; i < PF_INSTR; ++i) {
+            uint32_t blk = (i * TILES + tile) * 4 + wave;  // 1 KB block of the record
+            blk = blk < SHARED_BYTES / 1024 ? blk : SHARED_BYTES / 1024 - 1;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_ptr_t)(sink + wave * 1024), 16, lane_b, blk * 1024, 0, 0);
+        }
+    };
+    // VMEM operations a wave with a chunk row tile issues after its last W/Q
+    // DMA of a step: the next chunk's U, row scales, P (and W lo), this chunk's
+    // outputs, the next chunk's K fragments and one prefetch.  Waiting until at
+    // most that many are outstanding means the DMA has landed (the counter
+    // retires in issue order).
+    constexpr int N_AFTER = (NT + 3 + R::CKS * (SPL ? 2 : 1) + (SW ? R::DKS : 0)) + 4 * NT +
+                            MT_W * R::CKS + (int)PF_INSTR;
+    static_assert(L::STAGES == 1 || N_AFTER < 64, "vmcnt range");
+    constexpr int WAIT_AFTER = (N_AFTER & 15) | ((N_AFTER >> 4) << 14) | (7 << 4) | (15 << 8);
 
+    auto step = [&](const Ops& op, Ops& nxt, int64_t c) {
+        const bool more = c + 1 < c_end;
+        const __amdgpu_buffer_rsrc_t rn = rec_rsrc(more ? c + 1 : c);
+        f32x4 Y[NT];
         if (has_rt) {
-            // O = scale (Y + P Delta), P lower-triangular: k-steps up to the diagonal
-            const int nks = (rt * 16 + 16 + KS - 1) / KS;
-            for (int ks = 0; ks < nks; ++ks) {
-                const size_t fo = ((size_t)(rt * R::CKS + ks) * 64 + lane) * E;
-                const Frag fph = ld_frag<TIn>(rec + R::PH_OFF + fo);
-                Frag fpl;
-                if constexpr (SPL) fpl = ld_frag<TIn>(rec + R::PL_OFF + fo);
+            // X = W S^T, Y = Q S^T over all of d_k (two accumulators each); Delta = U - X.
+            // The next chunk's W/Q fragments stream into the other ring stage meanwhile.
+            f32x4 X[NT], X2[NT], Y2[NT];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) X[nt] = X2[nt] = Y[nt] = Y2[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const unsigned char* rw = ring_frag(c, 0) + lane_b;
+            // operands of k-step ks are read from LDS one k-step ahead of their MFMAs
+            Frag fwn = *reinterpret_cast<const Frag*>(rw);
+            Frag fqn = *reinterpret_cast<const Frag*>(rw + R::DKS * 1024);
+            Frag bhn[NT];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) bhn[nt] = *reinterpret_cast<const Frag*>(sr + (nt * 16 + l16) * SP + g16 * E);
+#pragma unroll
+            for (int ks = 0; ks < R::DKS; ++ks) {
+                if constexpr (L::STAGES == 2) {
+                    if (more) dma_ks(rn, c + 1, ks);
+                }
+                const Frag fw = fwn, fq = fqn;
+                Frag bhc[NT];
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) bhc[nt] = bhn[nt];
+                if (ks + 1 < R::DKS) {
+                    fwn = *reinterpret_cast<const Frag*>(rw + (ks + 1) * 1024);
+                    fqn = *reinterpret_cast<const Frag*>(rw + (R::DKS + ks + 1) * 1024);
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt)
+                        bhn[nt] = *reinterpret_cast<const Frag*>(sr + (nt * 16 + l16) * SP + (ks + 1) * KS + g16 * E);
+                }
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {
-                    const int doff = (nt * 16 + l16) * DP + ks * KS + g16 * E;
-                    const Frag dh = *reinterpret_cast<const Frag*>(sm.dt[0] + doff);
-                    Y[nt] = M::mma(fph, dh, Y[nt]);
-                    if constexpr (SPL) {
-                        const Frag dl = *reinterpret_cast<const Frag*>(sm.dt[1] + doff);
-                        Y[nt] = M::mma(fpl, dh, Y[nt]);
-                        Y[nt] = M::mma(fph, dl, Y[nt]);
+                    const int so = (nt * 16 + l16) * SP + ks * KS + g16 * E;
+                    const Frag bh = bhc[nt];
+                    f32x4& xa = (ks & 1) ? X2[nt] : X[nt];
+                    f32x4& ya = (ks & 1) ? Y2[nt] : Y[nt];
+                    xa = M::mma(fw, bh, xa);
+                    ya = M::mma(fq, bh, ya);
+                    if constexpr (SW) xa = M::mma(op.wl[ks], bh, xa);
+                    if constexpr (SS) {
+                        const Frag bl = *reinterpret_cast<const Frag*>(sr + SR_LO + so);
+                        xa = M::mma(fw, bl, xa);
+                        ya = M::mma(fq, bl, ya);
                     }
                 }
             }
+            __builtin_amdgcn_sched_barrier(0);  // later VMEM stays after the DMA (exact vmcnt wait)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                Y[nt] = (Y[nt] + Y2[nt]) * op.qs;
+                const f32x4 d = op.u[nt] - (X[nt] + X2[nt]);
+                // Delta^T[r][j] for j = rt*16 + 4*g16 + i: sigma-ordered rows (dt), natural rows (ds)
+                const int row = (nt * 16 + l16) * DP;
+                const int pd = row + quad_pos<TIn>(rt, g16);
+                const int pn = row + rt * 16 + 4 * g16;
+                store_quad<TIn, SPL>(dt + pd, dt + D_LO + pd, d);
+                store_quad<TIn, SPL>(ds + pn, ds + D_LO + pn, d * op.ks);
+            }
+        }
+        lds_barrier();
+
+        if (has_rt) {
+            // O = scale (Y + P Delta); P fragments are sigma-ordered over j
+#pragma unroll
+            for (int ks = 0; ks < R::CKS; ++ks) {
+                if (ks < pks) {
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) {
+                        const int doff = (nt * 16 + l16) * DP + ks * KS + g16 * E;
+                        const Frag dh = *reinterpret_cast<const Frag*>(dt + doff);
+                        Y[nt] = M::mma(op.ph[ks], dh, Y[nt]);
+                        if constexpr (SPL) {
+                            const Frag dl = *reinterpret_cast<const Frag*>(dt + D_LO + doff);
+                            Y[nt] = M::mma(op.pl[ks], dh, Y[nt]);
+                            Y[nt] = M::mma(op.ph[ks], dl, Y[nt]);
+                        }
+                    }
+                }
+            }
+            // rows >= len lie past the end of this view: the stores are dropped
+            const __amdgpu_buffer_rsrc_t ro = make_rsrc(o + ((int64_t)op.tok0 * H + h) * DV,
+                                                        (uint32_t)(((op.len - 1) * H + 1) * DV * EB));
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = rt * 16 + 4 * g16 + i;
-                    if (r < ci.len)
-                        Elem<TIn>::store(o, ((int64_t)(ci.tok0 + r) * H + h) * DV + row0 + nt * 16 + l16,
-                                         scale * Y[nt][i]);
-                }
+                for (int i = 0; i < 4; ++i)
+                    OStore<TIn>::st(ro, (uint32_t)(rt * 16 + 4 * g16 + i) * rowstride_o +
+                                            (uint32_t)(row0 + nt * 16 + l16) * EB, scale * Y[nt][i]);
+        }
+        if (more) {
+            load_part(nxt, rn, c + 1, 0);
+            load_part(nxt, rn, c + 1, 1);
         }
         // state update on this wave's d_k tiles: S^T = e^{gamma_L} S^T + K^T (kscale o Delta)
-        const float dec = decay[c * H + h];
+        Frag dsh[R::CKS][NT], dsl[SPL ? R::CKS : 1][NT];
+#pragma unroll
+        for (int ks = 0; ks < R::CKS; ++ks)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const int doff = (nt * 16 + l16) * DP + ks * KS + g16 * E;
+                dsh[ks][nt] = *reinterpret_cast<const Frag*>(ds + doff);
+                if constexpr (SPL) dsl[ks][nt] = *reinterpret_cast<const Frag*>(ds + D_LO + doff);
+            }
 #pragma unroll
         for (int a = 0; a < MT_W; ++a) {
             const int mt = wave + 4 * a;
             if (mt >= R::MT) continue;
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) S[a][nt] *= dec;
+            for (int nt = 0; nt < NT; ++nt) S[a][nt] *= op.dec;
 #pragma unroll
             for (int ks = 0; ks < R::CKS; ++ks) {
-                const Frag fk = ld_frag<TIn>(rec + R::K_OFF + ((size_t)(mt * R::CKS + ks) * 64 + lane) * E);
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {
-                    const int doff = (nt * 16 + l16) * DP + ks * KS + g16 * E;
-                    S[a][nt] = M::mma(fk, *reinterpret_cast<const Frag*>(sm.ds[0] + doff), S[a][nt]);
-                    if constexpr (SPL) S[a][nt] = M::mma(fk, *reinterpret_cast<const Frag*>(sm.ds[1] + doff), S[a][nt]);
+                    S[a][nt] = M::mma(op.k[a][ks], dsh[ks][nt], S[a][nt]);
+                    if constexpr (SPL) S[a][nt] = M::mma(op.k[a][ks], dsl[ks][nt], S[a][nt]);
                 }
             }
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
-                const int off = (nt * 16 + l16) * SP + mt * 16 + 4 * g16;
-                Split4<TIn>::store(sm.sr[0] + off, sm.sr[Sm::NS - 1] + off, S[a][nt]);
+                const int off = (nt * 16 + l16) * SP + quad_pos<TIn>(mt, g16);
+                store_quad<TIn, SS>(sr + off, sr + SR_LO + off, S[a][nt]);
+            }
+            if (a == 0 && more) load_part(nxt, rn, c + 1, 2);  // K fragments for the next chunk,
+            if (a == 1 && more) load_part(nxt, rn, c + 1, 3);  // issued once this chunk's are used
+        }
+        if constexpr (L::STAGES == 2) prefetch(c + 2 < c_end ? c + 2 : c);
+        lds_barrier();
+    };
+
+    // Each iteration first waits for everything issued during the previous step
+    // (this chunk's W/Q DMA and register operands, the previous outputs and
+    // prefetches), then computes this chunk while issuing the next one's loads.
+    auto iter = [&](Ops& cur, Ops& nxt, int64_t c) {
+        if constexpr (L::STAGES == 1) {
+            const __amdgpu_buffer_rsrc_t rr = rec_rsrc(c);
+            if (has_rt) {
+#pragma unroll
+                for (int ks = 0; ks < R::DKS; ++ks) dma_ks(rr, c, ks);
+            }
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this chunk's DMA has landed
+        } else {
+            __builtin_amdgcn_s_waitcnt(WAIT_AFTER);  // this chunk's DMA (issued one step ago) has landed
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        step(cur, nxt, c);
+    };
+    Ops opA, opB;
+    if (c_begin < c_end) {
+        const __amdgpu_buffer_rsrc_t rr = rec_rsrc(c_begin);
+        if constexpr (L::STAGES == 2) {
+            if (has_rt) {
+#pragma unroll
+                for (int ks = 0; ks < R::DKS; ++ks) dma_ks(rr, c_begin, ks);
             }
         }
-        __syncthreads();
+#pragma unroll
+        for (int p_ = 0; p_ < NLD; ++p_) load_part(opA, rr, c_begin, p_);
+        if constexpr (L::STAGES == 2) prefetch(c_begin + 1 < c_end ? c_begin + 1 : c_begin);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): first chunk's operands are in
+    }
+    for (int64_t c = c_begin; c < c_end; c += 2) {
+        iter(opA, opB, c);
+        if (c + 1 >= c_end) break;
+        iter(opB, opA, c + 1);
     }
 
     if (final_state) {
@@ -771,6 +1113,20 @@ __global__ __launch_bounds__(256) void chain_kernel(const TIn* __restrict__ q, c
 }
 
 // ------------------------------------------------------------------ dispatch
+
+// Which bf16 hi/lo refinements the chain kernel applies to its two largest
+// products (state operand S and W): bit 0 = S, bit 1 = W.  Default none (the
+// errors stay well inside the bf16 tolerance); the environment variable
+// GDN_CHAIN_SPLIT (0..3) selects a refined variant.
+static int chain_split_mode()
+{
+    static int mode = -1;  // read once; racing initialisers store the same value
+    if (mode < 0) {
+        const char* e = getenv("GDN_CHAIN_SPLIT");
+        mode = (e && e[0] >= '0' && e[0] <= '3') ? e[0] - '0' : 0;
+    }
+    return mode;
+}
 
 template <typename TIn, int C, int DK, int DV>
 static hipError_t run_prefill(const PrefillArgs& a)
@@ -813,10 +1169,35 @@ static hipError_t run_prefill(const PrefillArgs& a)
     }
     if (!(a.stages & 2)) return hipSuccess;
     constexpr int NT = 1;
-    if (a.N > 65535) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((chain_kernel<TIn, C, DK, DV, NT, true, true>), dim3(DV / (16 * NT), a.H, a.N), dim3(256), 0,
-                       a.stream, (const TIn*)a.q, header, tab, first, varlen, a.T, a.H, decay, records,
-                       a.lay.record_bytes, a.init_state, a.final_state, (TIn*)a.o, a.scale);
+    const int64_t pairs = (int64_t)a.N * a.H;
+    const int64_t groups = (pairs + 7) / 8;
+    const int64_t blocks = groups * 8 * (DV / (16 * NT));
+    if (pairs > 0x7fffffff || blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+#define GDN_LAUNCH_CHAIN(SS_, SW_)                                                                                    \
+    do {                                                                                                              \
+        constexpr size_t lds_bytes = ChainLds<TIn, C, DK, NT, Rec<TIn, C, DK, DV>::SPLIT>::BYTES;                     \
+        static bool attr = false; /* idempotent; racing writers store the same value */                               \
+        if (!attr) {                                                                                                  \
+            hipError_t ea = hipFuncSetAttribute((const void*)chain_kernel<TIn, C, DK, DV, NT, SS_, SW_>,               \
+                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);          \
+            if (ea != hipSuccess) return ea;                                                                          \
+            attr = true;                                                                                              \
+        }                                                                                                             \
+        hipLaunchKernelGGL((chain_kernel<TIn, C, DK, DV, NT, SS_, SW_>), dim3((uint32_t)blocks), dim3(256), lds_bytes, \
+                           a.stream, header, tab, first, varlen, a.T, a.H, (int32_t)pairs, decay, records,            \
+                           a.lay.record_bytes, a.init_state, a.final_state, (TIn*)a.o, a.scale);                      \
+    } while (0)
+    if constexpr (sizeof(TIn) == 4) {
+        GDN_LAUNCH_CHAIN(false, false);  // fp32 operands: nothing to refine
+    } else {
+        switch (chain_split_mode()) {
+            case 0: GDN_LAUNCH_CHAIN(false, false); break;
+            case 1: GDN_LAUNCH_CHAIN(true, false); break;
+            case 2: GDN_LAUNCH_CHAIN(false, true); break;
+            default: GDN_LAUNCH_CHAIN(true, true); break;
+        }
+    }
+#undef GDN_LAUNCH_CHAIN
     return hipGetLastError();
 }
 
