@@ -189,7 +189,7 @@ struct Rec {
     static constexpr size_t U_BYTE_OFF = ((size_t)OPER_ELEMS * sizeof(TIn) + 15) / 16 * 16;  // f32 [RT][VT][64][4]
     static constexpr size_t QS_BYTE_OFF = U_BYTE_OFF + (size_t)C * DV * 4;  // f32 [C]: rq_r e^{gamma_r}
     static constexpr size_t KSC_BYTE_OFF = QS_BYTE_OFF + (size_t)C * 4;     // f32 [C]: rk_j e^{gamma_L - gamma_j}
-    static constexpr size_t DEC_BYTE_OFF = KSC_BYTE_OFF + (size_t)C * 4;    // f32 [4]: e^{gamma_L}, 0, 0, 0
+    static constexpr size_t DEC_BYTE_OFF = KSC_BYTE_OFF + (size_t)C * 4;    // {e^{gamma_L}, tok0, len, 0} (f32, i32, i32)
     static constexpr size_t BYTES = DEC_BYTE_OFF + 16;
     static_assert(C % KS == 0 && DK % KS == 0, "tile shape");
 };
@@ -672,49 +672,12 @@ __global__ __launch_bounds__(256) void intra_kernel(const TIn* __restrict__ q, c
     }
     if (tid == 0) {
         decay_out[c * H + h] = expf(gL);
-        *reinterpret_cast<f32x4*>(recb + R::DEC_BYTE_OFF) = f32x4{expf(gL), 0.f, 0.f, 0.f};
+        *reinterpret_cast<f32x4*>(recb + R::DEC_BYTE_OFF) =
+            f32x4{expf(gL), __int_as_float(ci.tok0), __int_as_float(ci.len), 0.f};
     }
 }
 
 // ------------------------------------------------------------------ chain kernel
-
-// LDS of the chain kernel: the rounded state copy, Delta^T (two layouts), and a
-// ring of W and Q operand fragments filled by LDS-DMA (buffer_load ... lds),
-// one region per wave and ring stage.  Two stages when they fit (bf16), so the
-// fragments of chunk c+1 stream in while chunk c computes.
-template <typename TIn, int C, int DK, int NT, bool SPLIT>
-struct ChainLds {
-    static constexpr int SP = DK + 16 / (int)sizeof(TIn);  // state copy pitch (dwords = 4 mod 32)
-    static constexpr int DP = C + 16 / (int)sizeof(TIn);   // Delta^T pitch
-    static constexpr int NS = SPLIT ? 2 : 1;
-    static constexpr int DKS = DK / Mma<TIn>::KS;
-    static constexpr int RING_FRAGS = 2 * DKS;              // W then Q fragments of one chunk row tile
-    static constexpr size_t SR_BYTES = (size_t)NS * 16 * NT * SP * sizeof(TIn);
-    static constexpr size_t D_BYTES = (size_t)NS * 16 * NT * DP * sizeof(TIn);
-    static constexpr size_t FIXED = (SR_BYTES + 2 * D_BYTES + 255) / 256 * 256;
-    static constexpr size_t SINK_BYTES = 4 * 1024;           // per-wave 1 KB landing slot of L2 prefetches
-    static constexpr size_t STAGE_BYTES = (size_t)4 * RING_FRAGS * 1024;
-    static constexpr int STAGES = FIXED + SINK_BYTES + 2 * STAGE_BYTES <= 160 * 1024 ? 2 : 1;
-    static constexpr size_t RING_OFF = FIXED + SINK_BYTES;
-    static constexpr size_t BYTES = RING_OFF + STAGES * STAGE_BYTES;
-    static_assert(BYTES <= 160 * 1024, "chain kernel LDS");
-};
-
-// Register operands of one chunk step for one wave, loaded one step ahead.
-template <typename TIn, int C, int DK, int DV, int NT, bool SW>
-struct ChainOps {
-    using R = Rec<TIn, C, DK, DV>;
-    typedef typename Mma<TIn>::Frag Frag;
-    static constexpr int MT_W = (R::MT + 3) / 4;
-    Frag wl[SW ? R::DKS : 1];
-    Frag ph[R::CKS];
-    Frag pl[R::SPLIT ? R::CKS : 1];
-    Frag k[MT_W][R::CKS];
-    f32x4 u[NT];
-    f32x4 qs, ks;
-    float dec;
-    int32_t tok0, len;
-};
 
 template <typename TIn> struct OStore;
 template <> struct OStore<uint16_t> {
@@ -745,12 +708,10 @@ __device__ __forceinline__ void store_quad(TIn* p, TIn* p2, f32x4 v)
     }
 }
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
 // Workgroup barrier that orders LDS only: waits for this wave's LDS operations
-// (lgkmcnt) but not for its outstanding global loads or LDS-DMA transfers, which
-// the chain kernel tracks itself with counted vmcnt waits.  The empty asm
-// statements keep the compiler from moving memory accesses across it.
+// (lgkmcnt) but not for its outstanding global loads, which are register
+// prefetches consumed by this wave alone.  The empty asm statements keep the
+// compiler from moving memory accesses across it.
 __device__ __forceinline__ void lds_barrier()
 {
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt/expcnt untouched
@@ -759,52 +720,118 @@ __device__ __forceinline__ void lds_barrier()
     asm volatile("" ::: "memory");
 }
 
-// SPLIT_S: the state enters W S^T and Q S^T as hi + lo (else hi only).
-// SPLIT_W: W enters as hi + lo (else hi only).
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// The chain kernel stages its operands in LDS for bf16 operands (chunk 64);
+// fp32 operands of the production shape would not fit and are read directly.
+template <typename TIn, int C>
+constexpr bool chain_staged() { return sizeof(TIn) == 2 && C == 64; }
+// Loader waves of the staged form (they bring in every operand and write o).
+template <typename TIn, int C>
+constexpr int chain_loaders() { return chain_staged<TIn, C>() ? 8 : 0; }
+
+// Work split of the chain kernel over NW compute waves (NW a multiple of 4).
+template <typename TIn, int C, int DK, int DV, int NW>
+struct ChainSplit {
+    using R = Rec<TIn, C, DK, DV>;
+    static constexpr int KQ = (NW / 4) < R::DKS ? (NW / 4) : R::DKS;  // d_k split of X and Y
+    static constexpr int KPW = R::DKS / KQ;                             // k-steps per phase-1 wave
+    static constexpr int MTW = (R::MT + NW - 1) / NW;                   // state d_k tiles per wave
+    static_assert(R::DKS % KQ == 0, "d_k split");
+};
+
+// LDS of the chain kernel.  In the staged form (STAGE) every per-chunk operand
+// is written here by dedicated loader waves; each operand region is
+// single-buffered and refilled as soon as its last reader has passed a
+// barrier.  Without STAGE (fp32 operands, which do not fit) the operands are
+// read from the records directly.
+template <typename TIn, int C, int DK, int DV, int NT, int NW, bool STAGE, bool SPLIT>
+struct ChainLds {
+    using R = Rec<TIn, C, DK, DV>;
+    using P = ChainSplit<TIn, C, DK, DV, NW>;
+    static constexpr int SP = DK + 16 / (int)sizeof(TIn);  // state copy pitch (dwords = 4 mod 32)
+    static constexpr int DP = C + 16 / (int)sizeof(TIn);   // Delta^T pitch
+    static constexpr int OP = 16 * NT + 4;                 // output tile pitch (elements)
+    static constexpr int NS = SPLIT ? 2 : 1;
+    static constexpr int RT = C / 16;
+    // operand fragment slots (1 KB each: 64 lanes x 16 B, lane order)
+    static constexpr int F_W = 0;                          // [RT][DKS] W hi
+    static constexpr int F_Q = F_W + RT * R::DKS;          // [RT][DKS] Q
+    static constexpr int F_K = F_Q + RT * R::DKS;          // [MT][CKS] K^T
+    static constexpr int F_P = F_K + R::MT * R::CKS;       // [NS][RT][CKS] P (hi, lo)
+    static constexpr int F_U = F_P + NS * RT * R::CKS;     // [RT][NT] U
+    static constexpr int F_SINK = F_U + RT * NT;           // landing slot of prefetch transfers
+    static constexpr int NFRAG = STAGE ? F_SINK + 1 : 1;
+    unsigned char frag[NFRAG][1024];
+    float qs[C], ksc[C];              // row scales
+    f32x4 meta[16];                   // [0] = e^{gamma_L}, tok0, len (a 256-byte landing area)
+    TIn sr[16 * NT * SP];             // state rows S[r][col] rounded to operands, sigma order
+    TIn dt[NS][16 * NT * DP];         // Delta^T[r][j], sigma order (hi, lo)
+    TIn ds[NS][16 * NT * DP];         // (kscale o Delta)^T[r][j], natural order (hi, lo)
+    f32x4 xp[P::KQ][RT][NT][64];      // partial W S^T per d_k part
+    f32x4 yp[P::KQ][RT][NT][64];      // partial Q S^T per d_k part
+    TIn ot[STAGE ? C * OP : 1];       // output tile of one chunk (staged form), row-major
+};
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// One workgroup per (sequence, head, 16*NT state rows), sequential over the
+// sequence's chunks: NW compute waves plus, in the staged form, NL loader waves.
+// Per chunk, compute waves:
+//   phase 1  wave (rt, kq) = (w % 4, w / 4): partial X = W S^T and Y = Q S^T of
+//            chunk row tile rt over d_k part kq (partials to LDS)
+//   phase 2  wave (rt, 0): Delta = U - X -> LDS (sigma and natural order, hi/lo)
+//   phase 3  wave (rt, 1 or 0): O = scale (qscale o Y + P Delta)
+//            every wave: its state d_k tiles, S^T = e^{gamma_L} S^T + K^T (kscale o Delta)
+// Loader waves (staged form) load every operand into registers, write it to
+// LDS before the barrier whose readers need it, and write o from an LDS tile
+// one chunk later (details at the loader transfer helpers).
 // Workgroups are mapped so that all row tiles of one (sequence, head) pair run
 // on one XCD (workgroups are dealt to the 8 XCDs round-robin): they read the
 // same per-chunk records, which then come from that XCD's L2.
-template <typename TIn, int C, int DK, int DV, int NT, bool SPLIT_S, bool SPLIT_W>
-__global__ __launch_bounds__(256) void chain_kernel(const int32_t* __restrict__ header,
-                                                    const ChunkInfo* __restrict__ tab,
-                                                    const int32_t* __restrict__ seq_first, int32_t varlen, int64_t T,
-                                                    int32_t H, int32_t pairs, const float* __restrict__ decay,
-                                                    const unsigned char* __restrict__ records, size_t record_bytes,
-                                                    const float* __restrict__ init_state, float* __restrict__ final_state,
-                                                    TIn* __restrict__ o, float scale)
+template <typename TIn, int C, int DK, int DV, int NT, int NW>
+__global__ __launch_bounds__((NW + chain_loaders<TIn, C>()) * 64) void chain_kernel(
+    const int32_t* __restrict__ header, const ChunkInfo* __restrict__ tab, const int32_t* __restrict__ seq_first,
+    int32_t varlen, int64_t T, int32_t H, int32_t pairs, const unsigned char* __restrict__ records,
+    size_t record_bytes, const float* __restrict__ init_state, float* __restrict__ final_state, TIn* __restrict__ o,
+    float scale)
 {
     using M = Mma<TIn>;
     using R = Rec<TIn, C, DK, DV>;
+    using P = ChainSplit<TIn, C, DK, DV, NW>;
     constexpr bool SPL = R::SPLIT;
-    constexpr bool SS = SPL && SPLIT_S;
-    constexpr bool SW = SPL && SPLIT_W;
-    using L = ChainLds<TIn, C, DK, NT, SPL>;
-    using Ops = ChainOps<TIn, C, DK, DV, NT, SW>;
+    constexpr bool STAGE = chain_staged<TIn, C>();
+    constexpr int NL = chain_loaders<TIn, C>();
+    using L = ChainLds<TIn, C, DK, DV, NT, NW, STAGE, SPL>;
     typedef typename M::Frag Frag;
     constexpr int KS = M::KS, E = M::E;
     constexpr int SP = L::SP, DP = L::DP, NS = L::NS;
-    constexpr int MT_W = Ops::MT_W;
+    constexpr int RT = R::RT;
     constexpr int TILES = DV / (16 * NT);
     constexpr uint32_t FB = 64 * 16;  // bytes of one operand fragment (64 lanes x 16 B)
     constexpr uint32_t EB = sizeof(TIn);
+    constexpr int SINK = STAGE ? L::F_SINK : 0;  // landing slot of prefetch transfers
+    static_assert(!STAGE || (C == 64 && NT == 1 && (NL == 4 || NL == 8)), "staged form: chunk 64, 16 state rows");
 
-    extern __shared__ __align__(256) unsigned char lds[];
-    TIn* sr = reinterpret_cast<TIn*>(lds);                                   // [NS][16 NT][SP]
-    TIn* dt = reinterpret_cast<TIn*>(lds + L::SR_BYTES);                     // [NS][16 NT][DP]
-    TIn* ds = reinterpret_cast<TIn*>(lds + L::SR_BYTES + L::D_BYTES);        // [NS][16 NT][DP]
-    unsigned char* sink = lds + L::FIXED;                                    // [4][1 KB]
-    unsigned char* ring = lds + L::RING_OFF;                                 // [STAGES][4][RING_FRAGS][1 KB]
-    constexpr int SR_LO = (NS - 1) * 16 * NT * SP;
-    constexpr int D_LO = (NS - 1) * 16 * NT * DP;
+    extern __shared__ __align__(16) unsigned char lds_raw[];
+    L& sm = *reinterpret_cast<L*>(lds_raw);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave: scalar branches
+    const bool loader = wave >= NW;
+    const int lw = wave - NW;                                    // loader index
     const int g16 = lane >> 4, l16 = lane & 15;
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
     const int pair = xcd + 8 * (slot / TILES);
     if (pair >= pairs) return;
     const int n = pair / H, h = pair % H;
-    const int row0 = (slot % TILES) * 16 * NT;  // first state row (value index) of this workgroup
+    const int tile = slot % TILES;
+    const int row0 = tile * 16 * NT;  // first state row (value index) of this workgroup
 
     int64_t c_begin, c_end;
     if (varlen) {
@@ -816,293 +843,355 @@ __global__ __launch_bounds__(256) void chain_kernel(const int32_t* __restrict__ 
         c_end = (T + C - 1) / C;
     }
 
+    // compute roles
+    const int rt = wave & 3, kq = wave >> 2;
+    const bool p1 = !loader && rt < RT && kq < P::KQ;                     // phase-1 partial products
+    const bool fin_d = !loader && rt < RT && kq == 0;                     // Delta finaliser of row tile rt
+    const bool fin_o = !loader && rt < RT && kq == (P::KQ > 1 ? 1 : 0);   // output finaliser of row tile rt
+    const int pks = (rt * 16 + 16 + KS - 1) / KS;                         // P k-steps up to the diagonal
+
+    // ---------------------------------------------------------------- operands
+    const uint32_t lane_b = (uint32_t)lane * 16;
+    auto rec_ptr = [&](int64_t c) { return records + ((size_t)c * H + h) * record_bytes; };
+    // fragment of the current chunk: LDS slot `f` (staged) or record byte offset `src` (direct)
+    __amdgpu_buffer_rsrc_t rcur = make_rsrc(records, 0u);
+    auto frag = [&](int f, uint32_t src) -> Frag {
+        if constexpr (STAGE) return *reinterpret_cast<const Frag*>(sm.frag[f] + lane_b);
+        else return __builtin_bit_cast(Frag, buf_load16(rcur, lane_b, src));
+    };
+    auto row4 = [&](const float* lds, size_t byte_off, int r) -> f32x4 {  // 4 row scales from r
+        if constexpr (STAGE) return *reinterpret_cast<const f32x4*>(lds + r);
+        else return __builtin_bit_cast(f32x4, buf_load16(rcur, (uint32_t)r * 4, (uint32_t)byte_off));
+    };
+    auto w_src = [&](int r, int ks) { return R::WH_OFF * EB + (uint32_t)(r * R::DKS + ks) * FB; };
+    auto q_src = [&](int r, int ks) { return R::Q_OFF * EB + (uint32_t)(r * R::DKS + ks) * FB; };
+    auto k_src = [&](int mt, int ks) { return R::K_OFF * EB + (uint32_t)(mt * R::CKS + ks) * FB; };
+    auto p_src = [&](int part, int r, int ks) {
+        return (part ? R::PL_OFF : R::PH_OFF) * EB + (uint32_t)(r * R::CKS + ks) * FB;
+    };
+    auto u_src = [&](int r, int nt) {
+        return (uint32_t)R::U_BYTE_OFF + (uint32_t)(r * R::VT + (row0 >> 4) + nt) * FB;
+    };
+
+    // ------------------------------------------------- loader transfers (staged form)
+    // Loader waves 0 .. NOP-1 load operands into registers and write them to LDS
+    // once they arrive; per chunk c:
+    //   group A (U, k scales of c)               load after C(c-1), write before A(c)
+    //   group B (K^T, P, q scales, meta of c)    load after C(c-1), write after A(c)
+    //   group W (W, Q of c+1)                    load after A(c),   write after B(c)
+    // (the first chunk's groups A and W are loaded before the loop).  Loaders
+    // 0..3 also write o of chunk c-1 from the LDS output tile after C(c-1).
+    // Every wave issues the same loads on every path (indices past the end are
+    // clamped to the last fragment), so the compiler's vmcnt waits stay exact.
+    // The last loader wave only prefetches: after C(c-1) it brings a share of
+    // chunk c+2's shared operands and this workgroup's U tiles into L2 by
+    // fire-and-forget LDS-DMA transfers into a sink slot; it waits for nothing
+    // in the loop, so the in-order vmcnt of the other waves never includes them.
+    constexpr int NLd = NL > 0 ? NL : 1;
+    constexpr int NOP = NLd > 1 ? NLd - 1 : 1;     // operand loaders
+    const bool pf_wave = lw == NOP;
+    constexpr int NK = R::MT * R::CKS, NP = NS * RT * R::CKS, NKP = NK + NP;
+    constexpr int NB = (NKP + NOP - 1) / NOP;      // K/P fragments per loader
+    constexpr int NWQ = 2 * RT * R::DKS;
+    constexpr int NWL = (NWQ + NOP - 1) / NOP;     // W/Q fragments per loader
+    constexpr int NU = RT * NT;
+    constexpr int L_KSC = NU % NOP, L_QS = (NU + 1) % NOP, L_META = (NU + 2) % NOP;
+    static_assert(!STAGE || (NU <= NOP && NOP >= 3), "one loader per U tile, distinct row-vector loaders");
+    // K^T fragments then P fragments are contiguous in the record: fragment f at K_OFF + f KB
+    static_assert(R::PH_OFF == R::K_OFF + C * DK && R::PL_OFF == R::PH_OFF + C * C, "record layout");
+    auto kp_src = [&](int f) { return R::K_OFF * EB + (uint32_t)f * FB; };
+    auto wq_src = [&](int f) -> uint32_t {
+        const int kind = f / (RT * R::DKS), rem = f % (RT * R::DKS);
+        return kind ? q_src(rem / R::DKS, rem % R::DKS) : w_src(rem / R::DKS, rem % R::DKS);
+    };
+    struct GroupA { u32x4 u; uint32_t x; };
+    struct GroupB { u32x4 f[NB]; uint32_t x; };
+    struct GroupW { u32x4 f[NWL]; };
+    // row vectors: loader L_KSC -> k scales, L_QS -> q scales, L_META -> meta (a 16-byte view)
+    auto load_a = [&](int64_t c, GroupA& g) {
+        const unsigned char* rb = rec_ptr(c);
+        if (lw < NU) g.u = buf_load16(make_rsrc(rb, (uint32_t)R::BYTES), lane_b, u_src(lw / NT, lw % NT));
+        if (lw == L_KSC) g.x = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(rb + R::KSC_BYTE_OFF, C * 4), lane * 4, 0, 0);
+    };
+    auto write_a = [&](const GroupA& g) {
+        if (lw < NU) *reinterpret_cast<u32x4*>(sm.frag[L::F_U + lw] + lane_b) = g.u;
+        if (lw == L_KSC) reinterpret_cast<uint32_t*>(sm.ksc)[lane] = g.x;
+    };
+    auto load_b = [&](int64_t c, GroupB& g) {
+        const unsigned char* rb = rec_ptr(c);
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(rb, (uint32_t)R::BYTES);
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const int f = min(lw + NOP * i, NKP - 1);
+            g.f[i] = buf_load16(r, lane_b, kp_src(f));
+        }
+        if (lw == L_QS) g.x = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(rb + R::QS_BYTE_OFF, C * 4), lane * 4, 0, 0);
+        if (lw == L_META) g.x = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(rb + R::DEC_BYTE_OFF, 16), lane * 4, 0, 0);
+    };
+    auto write_b = [&](const GroupB& g) {
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const int f = min(lw + NOP * i, NKP - 1);
+            *reinterpret_cast<u32x4*>(sm.frag[L::F_K + f] + lane_b) = g.f[i];  // F_P = F_K + NK
+        }
+        if (lw == L_QS) reinterpret_cast<uint32_t*>(sm.qs)[lane] = g.x;
+        if (lw == L_META) reinterpret_cast<uint32_t*>(sm.meta)[lane] = g.x;  // lanes >= 4 write 0 into the landing area
+    };
+    auto load_w = [&](int64_t c, GroupW& g) {
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(rec_ptr(c), (uint32_t)R::BYTES);
+#pragma unroll
+        for (int i = 0; i < NWL; ++i) g.f[i] = buf_load16(r, lane_b, wq_src(min(lw + NOP * i, NWQ - 1)));
+    };
+    auto write_w = [&](const GroupW& g) {
+#pragma unroll
+        for (int i = 0; i < NWL; ++i)
+            *reinterpret_cast<u32x4*>(sm.frag[L::F_W + min(lw + NOP * i, NWQ - 1)] + lane_b) = g.f[i];
+    };
+    // prefetch wave: a 1/TILES share of chunk cp's shared operands (W hi, Q,
+    // K^T, P: identical for all row tiles) and this workgroup's U tiles
+    constexpr uint32_t W_KB = (uint32_t)(C * DK * EB / 1024);
+    constexpr uint32_t REST_KB = (uint32_t)((R::U_BYTE_OFF - (size_t)R::Q_OFF * EB) / 1024);
+    constexpr uint32_t SHARED_KB = W_KB + REST_KB;
+    constexpr int PF = (int)((SHARED_KB + TILES - 1) / TILES);
+    auto prefetch = [&](int64_t cp) {
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(rec_ptr(cp), (uint32_t)R::BYTES);
+#pragma unroll
+        for (int i = 0; i < PF; ++i) {
+            uint32_t blk = (uint32_t)(i * TILES + tile);
+            blk = blk < SHARED_KB ? blk : SHARED_KB - 1;
+            const uint32_t src = blk < W_KB ? blk * 1024 : (uint32_t)R::Q_OFF * EB + (blk - W_KB) * 1024;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)sm.frag[SINK], 16, lane_b, src, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < NU; ++i) {
+            const uint32_t src = u_src(i / NT, i % NT);  // (a lambda call directly inside the builtin's
+                                                         // argument list drops the host-side kernel stub)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)sm.frag[SINK], 16, lane_b, src, 0, 0);
+        }
+    };
+    // output tile of one chunk (LDS, row-major) -> o by loaders 0..3, 4 values per
+    // lane; rows >= len fall outside the view
+    static_assert(!STAGE || (NOP >= 4 && 16 * NT == 16), "output tile store mapping");
+    const uint32_t rowstride_o = (uint32_t)H * DV * EB;
+    auto store_o = [&](int tok0, int len) {
+        if (lw < 4) {
+            const __amdgpu_buffer_rsrc_t ro =
+                make_rsrc(o + ((int64_t)tok0 * H + h) * DV, (uint32_t)(((len - 1) * H + 1) * DV * EB));
+            const int lt = lw * 64 + lane, row = lt >> 2, part = lt & 3;
+            const u32x2 val = *reinterpret_cast<const u32x2*>(sm.ot + row * L::OP + part * 4);
+            __builtin_amdgcn_raw_buffer_store_b64(val, ro, (int)((uint32_t)row * rowstride_o + (uint32_t)(row0 + part * 4) * EB),
+                                                  0, 0);
+        }
+    };
+
+    // ---------------------------------------------------------------- loader waves
+    if (loader) {
+        if constexpr (STAGE) {
+            if (pf_wave) {
+                __syncthreads();
+                for (int64_t c = c_begin; c < c_end; ++c) {
+                    if (c + 2 < c_end) prefetch(c + 2);
+                    lds_barrier();  // ---- A
+                    lds_barrier();  // ---- B
+                    lds_barrier();  // ---- C
+                }
+                wait_vmcnt<0>();  // no transfer may still target LDS when the workgroup ends
+                return;
+            }
+            if (c_begin < c_end) {
+                GroupA ga;
+                GroupW gw;
+                load_a(c_begin, ga);
+                load_w(c_begin, gw);
+                write_a(ga);
+                write_w(gw);
+            }
+            __syncthreads();
+            int otok0 = 0, olen = 0;  // chunk whose outputs sit in the output tile
+            for (int64_t c = c_begin; c < c_end; ++c) {
+                const int64_t cn = c + 1 < c_end ? c + 1 : c;  // W/Q source (the last chunk reloads its own)
+                GroupA ga;
+                GroupB gb;
+                GroupW gw;
+                load_a(c, ga);  // the first chunk's group A reloads the same values
+                load_b(c, gb);
+                if (c > c_begin) store_o(otok0, olen);
+                write_a(ga);
+                lds_barrier();  // ---- A
+                load_w(cn, gw);
+                write_b(gb);
+                lds_barrier();  // ---- B
+                const f32x4 meta = sm.meta[0];
+                otok0 = __builtin_amdgcn_readfirstlane(__float_as_int(meta.y));
+                olen = __builtin_amdgcn_readfirstlane(__float_as_int(meta.z));
+                write_w(gw);  // after the last chunk's B nobody reads the W/Q regions again
+                lds_barrier();  // ---- C
+            }
+            if (c_begin < c_end) store_o(otok0, olen);
+            wait_vmcnt<0>();
+        }
+        return;
+    }
+
+    // ---------------------------------------------------------------- compute waves
     // state tiles S^T[mt][nt] in result layout: lane holds S[row0 + nt*16 + l16][mt*16 + 4*g16 + i]
-    f32x4 S[MT_W][NT];
+    f32x4 S[P::MTW][NT];
     const size_t st_base = ((size_t)n * H + h) * DV * DK;
 #pragma unroll
-    for (int a = 0; a < MT_W; ++a) {
-        const int mt = wave + 4 * a;
+    for (int a = 0; a < P::MTW; ++a) {
+        const int mt = wave + NW * a;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             S[a][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (mt < R::MT && init_state)
-                S[a][nt] = *reinterpret_cast<const f32x4*>(init_state + st_base +
-                                                           (size_t)(row0 + nt * 16 + l16) * DK + mt * 16 + 4 * g16);
             if (mt < R::MT) {
+                if (init_state)
+                    S[a][nt] = *reinterpret_cast<const f32x4*>(init_state + st_base +
+                                                               (size_t)(row0 + nt * 16 + l16) * DK + mt * 16 + 4 * g16);
                 const int off = (nt * 16 + l16) * SP + quad_pos<TIn>(mt, g16);
-                store_quad<TIn, SPL>(sr + off, sr + SR_LO + off, S[a][nt]);
+                store_quad<TIn, false>(sm.sr + off, sm.sr + off, S[a][nt]);
             }
         }
     }
+
     __syncthreads();
 
-    const bool has_rt = wave < R::RT;
-    const int rt = wave;
-    const int pks = (rt * 16 + 16 + KS - 1) / KS;  // P k-steps up to the diagonal
-
-    // per-lane byte offsets inside a record (fragments are 64 lanes x 16 B)
-    const uint32_t lane_b = (uint32_t)lane * 16;
-    const uint32_t offWH = R::WH_OFF * EB + (uint32_t)rt * R::DKS * FB + lane_b;
-    const uint32_t offWL = R::WL_OFF * EB + (uint32_t)rt * R::DKS * FB + lane_b;
-    const uint32_t offQ = R::Q_OFF * EB + (uint32_t)rt * R::DKS * FB + lane_b;
-    const uint32_t offPH = R::PH_OFF * EB + (uint32_t)rt * R::CKS * FB + lane_b;
-    const uint32_t offPL = R::PL_OFF * EB + (uint32_t)rt * R::CKS * FB + lane_b;
-    const uint32_t offK = R::K_OFF * EB + lane_b;
-    const uint32_t offU = (uint32_t)R::U_BYTE_OFF + ((uint32_t)(rt * R::VT + (row0 >> 4)) * 64 + lane) * 16;
-    const uint32_t offQS = (uint32_t)R::QS_BYTE_OFF + (uint32_t)(rt * 16 + 4 * g16) * 4;
-    const uint32_t offKS = (uint32_t)R::KSC_BYTE_OFF + (uint32_t)(rt * 16 + 4 * g16) * 4;
-    const uint32_t rowstride_o = (uint32_t)H * DV * EB;
-
-    auto rec_rsrc = [&](int64_t c) {
-        return make_rsrc(records + ((size_t)c * H + h) * record_bytes, (uint32_t)R::BYTES);
-    };
-    auto ring_frag = [&](int64_t c, int f) -> unsigned char* {
-        return ring + ((size_t)((c % L::STAGES) * 4 + wave) * L::RING_FRAGS + f) * 1024;
-    };
-    // W and Q fragment ks of chunk c -> this wave's ring region (LDS-DMA, no registers)
-    auto dma_ks = [&](const __amdgpu_buffer_rsrc_t& rr, int64_t c, int ks) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_ptr_t)ring_frag(c, ks), 16, offWH, ks * FB, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_ptr_t)ring_frag(c, R::DKS + ks), 16, offQ, ks * FB, 0, 0);
-    };
-    // register operands of chunk c, in NLD independent groups (issued spread over a step)
-    constexpr int NLD = 4;
-    auto load_part = [&](Ops& op, const __amdgpu_buffer_rsrc_t& rr, int64_t c, int part) {
-        if (part == 0) {
-            const ChunkInfo ci = chunk_info(tab, varlen, c, C, T);
-            op.tok0 = ci.tok0;
-            op.len = ci.len;
-            op.dec = __builtin_bit_cast(f32x4, buf_load16(rr, (uint32_t)R::DEC_BYTE_OFF, 0)).x;
-            if (has_rt) {
+    for (int64_t c = c_begin; c < c_end; ++c) {
+        if constexpr (!STAGE) rcur = make_rsrc(rec_ptr(c), (uint32_t)R::BYTES);
+        if (p1) {
+            // ---- phase 1: partial X = W S^T and Y = Q S^T over this wave's d_k part
+            f32x4 X[NT], Y[NT];
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) op.u[nt] = __builtin_bit_cast(f32x4, buf_load16(rr, offU, nt * FB));
-                op.qs = __builtin_bit_cast(f32x4, buf_load16(rr, offQS, 0));
-                op.ks = __builtin_bit_cast(f32x4, buf_load16(rr, offKS, 0));
-            }
-        } else if (part == 1) {
-            if (has_rt) {
+            for (int nt = 0; nt < NT; ++nt) X[nt] = Y[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int ks = 0; ks < R::CKS; ++ks) {
-                    op.ph[ks] = __builtin_bit_cast(Frag, buf_load16(rr, offPH, ks * FB));
-                    if constexpr (SPL) op.pl[ks] = __builtin_bit_cast(Frag, buf_load16(rr, offPL, ks * FB));
-                }
-                if constexpr (SW) {
-#pragma unroll
-                    for (int ks = 0; ks < R::DKS; ++ks)
-                        op.wl[ks] = __builtin_bit_cast(Frag, buf_load16(rr, offWL, ks * FB));
-                }
-            }
-        } else {
-            // K fragments, half of this wave's d_k tiles per part
-#pragma unroll
-            for (int a = 0; a < MT_W; ++a) {
-                if ((a & 1) != (part & 1)) continue;
-                const int mt = wave + 4 * a;
-                if (mt < R::MT) {
-#pragma unroll
-                    for (int ks = 0; ks < R::CKS; ++ks)
-                        op.k[a][ks] = __builtin_bit_cast(Frag, buf_load16(rr, offK, (mt * R::CKS + ks) * FB));
-                }
-            }
-        }
-    };
-    // Cooperative L2 prefetch of the shared part of chunk c's record (W, Q, K, P):
-    // the TILES workgroups of this (sequence, head) each pull 1/TILES of it into
-    // their XCD's L2 (landing in a scratch LDS slot), so the loads one step later hit L2.
-    constexpr uint32_t SHARED_BYTES = (uint32_t)R::U_BYTE_OFF;
-    constexpr uint32_t PF_INSTR = (SHARED_BYTES / 1024 + TILES * 4 - 1) / (TILES * 4);  // per wave
-    const int tile = slot % TILES;
-    auto prefetch = [&](int64_t c) {
-        const __amdgpu_buffer_rsrc_t rr = rec_rsrc(c);
-#pragma unroll
-        for (uint32_t i = 0; i < PF_INSTR; ++i) {
-            uint32_t blk = (i * TILES + tile) * 4 + wave;  // 1 KB block of the record
-            blk = blk < SHARED_BYTES / 1024 ? blk : SHARED_BYTES / 1024 - 1;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_ptr_t)(sink + wave * 1024), 16, lane_b, blk * 1024, 0, 0);
-        }
-    };
-    // VMEM operations a wave with a chunk row tile issues after its last W/Q
-    // DMA of a step: the next chunk's U, row scales, P (and W lo), this chunk's
-    // outputs, the next chunk's K fragments and one prefetch.  Waiting until at
-    // most that many are outstanding means the DMA has landed (the counter
-    // retires in issue order).
-    constexpr int N_AFTER = (NT + 3 + R::CKS * (SPL ? 2 : 1) + (SW ? R::DKS : 0)) + 4 * NT +
-                            MT_W * R::CKS + (int)PF_INSTR;
-    static_assert(L::STAGES == 1 || N_AFTER < 64, "vmcnt range");
-    constexpr int WAIT_AFTER = (N_AFTER & 15) | ((N_AFTER >> 4) << 14) | (7 << 4) | (15 << 8);
-
-    auto step = [&](const Ops& op, Ops& nxt, int64_t c) {
-        const bool more = c + 1 < c_end;
-        const __amdgpu_buffer_rsrc_t rn = rec_rsrc(more ? c + 1 : c);
-        f32x4 Y[NT];
-        if (has_rt) {
-            // X = W S^T, Y = Q S^T over all of d_k (two accumulators each); Delta = U - X.
-            // The next chunk's W/Q fragments stream into the other ring stage meanwhile.
-            f32x4 X[NT], X2[NT], Y2[NT];
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) X[nt] = X2[nt] = Y[nt] = Y2[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const unsigned char* rw = ring_frag(c, 0) + lane_b;
-            // operands of k-step ks are read from LDS one k-step ahead of their MFMAs
-            Frag fwn = *reinterpret_cast<const Frag*>(rw);
-            Frag fqn = *reinterpret_cast<const Frag*>(rw + R::DKS * 1024);
-            Frag bhn[NT];
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) bhn[nt] = *reinterpret_cast<const Frag*>(sr + (nt * 16 + l16) * SP + g16 * E);
-#pragma unroll
-            for (int ks = 0; ks < R::DKS; ++ks) {
-                if constexpr (L::STAGES == 2) {
-                    if (more) dma_ks(rn, c + 1, ks);
-                }
-                const Frag fw = fwn, fq = fqn;
-                Frag bhc[NT];
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) bhc[nt] = bhn[nt];
-                if (ks + 1 < R::DKS) {
-                    fwn = *reinterpret_cast<const Frag*>(rw + (ks + 1) * 1024);
-                    fqn = *reinterpret_cast<const Frag*>(rw + (R::DKS + ks + 1) * 1024);
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt)
-                        bhn[nt] = *reinterpret_cast<const Frag*>(sr + (nt * 16 + l16) * SP + (ks + 1) * KS + g16 * E);
-                }
+            for (int i = 0; i < P::KPW; ++i) {
+                const int ks = kq * P::KPW + i;
+                const Frag fw = frag(L::F_W + rt * R::DKS + ks, w_src(rt, ks));
+                const Frag fq = frag(L::F_Q + rt * R::DKS + ks, q_src(rt, ks));
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {
-                    const int so = (nt * 16 + l16) * SP + ks * KS + g16 * E;
-                    const Frag bh = bhc[nt];
-                    f32x4& xa = (ks & 1) ? X2[nt] : X[nt];
-                    f32x4& ya = (ks & 1) ? Y2[nt] : Y[nt];
-                    xa = M::mma(fw, bh, xa);
-                    ya = M::mma(fq, bh, ya);
-                    if constexpr (SW) xa = M::mma(op.wl[ks], bh, xa);
-                    if constexpr (SS) {
-                        const Frag bl = *reinterpret_cast<const Frag*>(sr + SR_LO + so);
-                        xa = M::mma(fw, bl, xa);
-                        ya = M::mma(fq, bl, ya);
-                    }
+                    const Frag b = *reinterpret_cast<const Frag*>(sm.sr + (nt * 16 + l16) * SP + ks * KS + g16 * E);
+                    X[nt] = M::mma(fw, b, X[nt]);
+                    Y[nt] = M::mma(fq, b, Y[nt]);
                 }
             }
-            __builtin_amdgcn_sched_barrier(0);  // later VMEM stays after the DMA (exact vmcnt wait)
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
-                Y[nt] = (Y[nt] + Y2[nt]) * op.qs;
-                const f32x4 d = op.u[nt] - (X[nt] + X2[nt]);
-                // Delta^T[r][j] for j = rt*16 + 4*g16 + i: sigma-ordered rows (dt), natural rows (ds)
+                sm.xp[kq][rt][nt][lane] = X[nt];
+                sm.yp[kq][rt][nt][lane] = Y[nt];
+            }
+        }
+        lds_barrier();  // ---- A: partials visible; W/Q regions free
+
+        if (fin_d) {
+            // ---- phase 2: Delta = U - X for row tile rt (sigma-ordered dt, natural-order ds)
+            const f32x4 ks4 = row4(sm.ksc, R::KSC_BYTE_OFF, rt * 16 + 4 * g16);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                f32x4 X = sm.xp[0][rt][nt][lane];
+#pragma unroll
+                for (int qq = 1; qq < P::KQ; ++qq) X += sm.xp[qq][rt][nt][lane];
+                const f32x4 u = __builtin_bit_cast(f32x4, frag(L::F_U + rt * NT + nt, u_src(rt, nt)));
+                const f32x4 d = u - X;
                 const int row = (nt * 16 + l16) * DP;
                 const int pd = row + quad_pos<TIn>(rt, g16);
                 const int pn = row + rt * 16 + 4 * g16;
-                store_quad<TIn, SPL>(dt + pd, dt + D_LO + pd, d);
-                store_quad<TIn, SPL>(ds + pn, ds + D_LO + pn, d * op.ks);
+                store_quad<TIn, SPL>(sm.dt[0] + pd, sm.dt[NS - 1] + pd, d);
+                store_quad<TIn, SPL>(sm.ds[0] + pn, sm.ds[NS - 1] + pn, d * ks4);
             }
         }
-        lds_barrier();
+        lds_barrier();  // ---- B: Delta visible; U region free
 
-        if (has_rt) {
-            // O = scale (Y + P Delta); P fragments are sigma-ordered over j
+        f32x4 meta;
+        if constexpr (STAGE) meta = sm.meta[0];
+        else meta = __builtin_bit_cast(f32x4, buf_load16(rcur, 0, (uint32_t)R::DEC_BYTE_OFF));
+        const int tok0 = __builtin_amdgcn_readfirstlane(__float_as_int(meta.y));
+        const int len = __builtin_amdgcn_readfirstlane(__float_as_int(meta.z));
+        {
+            // ---- phase 3a: O = scale (qscale o Y + P Delta); P fragments are sigma-ordered over j
+            if constexpr (STAGE) {
+                if (fin_o) {
+                    f32x4 Y = sm.yp[0][rt][0][lane];
 #pragma unroll
-            for (int ks = 0; ks < R::CKS; ++ks) {
-                if (ks < pks) {
+                    for (int qq = 1; qq < P::KQ; ++qq) Y += sm.yp[qq][rt][0][lane];
+                    Y *= row4(sm.qs, R::QS_BYTE_OFF, rt * 16 + 4 * g16);
 #pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) {
-                        const int doff = (nt * 16 + l16) * DP + ks * KS + g16 * E;
-                        const Frag dh = *reinterpret_cast<const Frag*>(dt + doff);
-                        Y[nt] = M::mma(op.ph[ks], dh, Y[nt]);
-                        if constexpr (SPL) {
-                            const Frag dl = *reinterpret_cast<const Frag*>(dt + D_LO + doff);
-                            Y[nt] = M::mma(op.pl[ks], dh, Y[nt]);
-                            Y[nt] = M::mma(op.ph[ks], dl, Y[nt]);
+                    for (int ks = 0; ks < R::CKS; ++ks) {
+                        if (ks < pks) {
+                            const int doff = l16 * DP + ks * KS + g16 * E;
+                            const Frag ph = frag(L::F_P + rt * R::CKS + ks, 0);
+                            const Frag pl = frag(L::F_P + (RT + rt) * R::CKS + ks, 0);
+                            const Frag dh = *reinterpret_cast<const Frag*>(sm.dt[0] + doff);
+                            const Frag dl = *reinterpret_cast<const Frag*>(sm.dt[1] + doff);
+                            Y = M::mma(ph, dh, Y);
+                            Y = M::mma(pl, dh, Y);
+                            Y = M::mma(ph, dl, Y);
                         }
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        sm.ot[(rt * 16 + 4 * g16 + i) * L::OP + l16] = M::cvt(scale * Y[i]);
+                }
+            } else {
+                const __amdgpu_buffer_rsrc_t ro = make_rsrc(o + ((int64_t)tok0 * H + h) * DV,
+                                                            fin_o ? (uint32_t)(((len - 1) * H + 1) * DV * EB) : 0u);
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    if (fin_o) {
+                        f32x4 Y = sm.yp[0][rt][nt][lane];
+#pragma unroll
+                        for (int qq = 1; qq < P::KQ; ++qq) Y += sm.yp[qq][rt][nt][lane];
+                        Y *= row4(sm.qs, R::QS_BYTE_OFF, rt * 16 + 4 * g16);
+#pragma unroll
+                        for (int ks = 0; ks < R::CKS; ++ks) {
+                            if (ks < pks) {
+                                const int doff = (nt * 16 + l16) * DP + ks * KS + g16 * E;
+                                const Frag ph = frag(L::F_P + rt * R::CKS + ks, p_src(0, rt, ks));
+                                const Frag dh = *reinterpret_cast<const Frag*>(sm.dt[0] + doff);
+                                Y = M::mma(ph, dh, Y);
+                                if constexpr (SPL) {
+                                    const Frag pl = frag(L::F_P + (RT + rt) * R::CKS + ks, p_src(1, rt, ks));
+                                    const Frag dl = *reinterpret_cast<const Frag*>(sm.dt[1] + doff);
+                                    Y = M::mma(pl, dh, Y);
+                                    Y = M::mma(ph, dl, Y);
+                                }
+                            }
+                        }
+                        // rows >= len fall outside the view: dropped
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            OStore<TIn>::st(ro, (uint32_t)(rt * 16 + 4 * g16 + i) * rowstride_o +
+                                                    (uint32_t)(row0 + nt * 16 + l16) * EB, scale * Y[i]);
                     }
                 }
             }
-            // rows >= len lie past the end of this view: the stores are dropped
-            const __amdgpu_buffer_rsrc_t ro = make_rsrc(o + ((int64_t)op.tok0 * H + h) * DV,
-                                                        (uint32_t)(((op.len - 1) * H + 1) * DV * EB));
+            // ---- phase 3b: state update on this wave's d_k tiles
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    OStore<TIn>::st(ro, (uint32_t)(rt * 16 + 4 * g16 + i) * rowstride_o +
-                                            (uint32_t)(row0 + nt * 16 + l16) * EB, scale * Y[nt][i]);
-        }
-        if (more) {
-            load_part(nxt, rn, c + 1, 0);
-            load_part(nxt, rn, c + 1, 1);
-        }
-        // state update on this wave's d_k tiles: S^T = e^{gamma_L} S^T + K^T (kscale o Delta)
-        Frag dsh[R::CKS][NT], dsl[SPL ? R::CKS : 1][NT];
-#pragma unroll
-        for (int ks = 0; ks < R::CKS; ++ks)
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                const int doff = (nt * 16 + l16) * DP + ks * KS + g16 * E;
-                dsh[ks][nt] = *reinterpret_cast<const Frag*>(ds + doff);
-                if constexpr (SPL) dsl[ks][nt] = *reinterpret_cast<const Frag*>(ds + D_LO + doff);
-            }
-#pragma unroll
-        for (int a = 0; a < MT_W; ++a) {
-            const int mt = wave + 4 * a;
-            if (mt >= R::MT) continue;
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) S[a][nt] *= op.dec;
-#pragma unroll
-            for (int ks = 0; ks < R::CKS; ++ks) {
+            for (int a = 0; a < P::MTW; ++a) {
+                const int mt = wave + NW * a;
+                if (mt >= R::MT) continue;
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {
-                    S[a][nt] = M::mma(op.k[a][ks], dsh[ks][nt], S[a][nt]);
-                    if constexpr (SPL) S[a][nt] = M::mma(op.k[a][ks], dsl[ks][nt], S[a][nt]);
+                    f32x4 acc = S[a][nt] * meta.x;
+#pragma unroll
+                    for (int ks = 0; ks < R::CKS; ++ks) {
+                        const int doff = (nt * 16 + l16) * DP + ks * KS + g16 * E;
+                        const Frag fk = frag(L::F_K + mt * R::CKS + ks, k_src(mt, ks));
+                        acc = M::mma(fk, *reinterpret_cast<const Frag*>(sm.ds[0] + doff), acc);
+                        if constexpr (SPL) acc = M::mma(fk, *reinterpret_cast<const Frag*>(sm.ds[1] + doff), acc);
+                    }
+                    S[a][nt] = acc;
+                    const int off = (nt * 16 + l16) * SP + quad_pos<TIn>(mt, g16);
+                    store_quad<TIn, false>(sm.sr + off, sm.sr + off, acc);
                 }
             }
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                const int off = (nt * 16 + l16) * SP + quad_pos<TIn>(mt, g16);
-                store_quad<TIn, SS>(sr + off, sr + SR_LO + off, S[a][nt]);
-            }
-            if (a == 0 && more) load_part(nxt, rn, c + 1, 2);  // K fragments for the next chunk,
-            if (a == 1 && more) load_part(nxt, rn, c + 1, 3);  // issued once this chunk's are used
         }
-        if constexpr (L::STAGES == 2) prefetch(c + 2 < c_end ? c + 2 : c);
-        lds_barrier();
-    };
-
-    // Each iteration first waits for everything issued during the previous step
-    // (this chunk's W/Q DMA and register operands, the previous outputs and
-    // prefetches), then computes this chunk while issuing the next one's loads.
-    auto iter = [&](Ops& cur, Ops& nxt, int64_t c) {
-        if constexpr (L::STAGES == 1) {
-            const __amdgpu_buffer_rsrc_t rr = rec_rsrc(c);
-            if (has_rt) {
-#pragma unroll
-                for (int ks = 0; ks < R::DKS; ++ks) dma_ks(rr, c, ks);
-            }
-            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this chunk's DMA has landed
-        } else {
-            __builtin_amdgcn_s_waitcnt(WAIT_AFTER);  // this chunk's DMA (issued one step ago) has landed
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        step(cur, nxt, c);
-    };
-    Ops opA, opB;
-    if (c_begin < c_end) {
-        const __amdgpu_buffer_rsrc_t rr = rec_rsrc(c_begin);
-        if constexpr (L::STAGES == 2) {
-            if (has_rt) {
-#pragma unroll
-                for (int ks = 0; ks < R::DKS; ++ks) dma_ks(rr, c_begin, ks);
-            }
-        }
-#pragma unroll
-        for (int p_ = 0; p_ < NLD; ++p_) load_part(opA, rr, c_begin, p_);
-        if constexpr (L::STAGES == 2) prefetch(c_begin + 1 < c_end ? c_begin + 1 : c_begin);
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): first chunk's operands are in
-    }
-    for (int64_t c = c_begin; c < c_end; c += 2) {
-        iter(opA, opB, c);
-        if (c + 1 >= c_end) break;
-        iter(opB, opA, c + 1);
+        lds_barrier();  // ---- C: state copy and output tile visible; K, P regions free
     }
 
     if (final_state) {
 #pragma unroll
-        for (int a = 0; a < MT_W; ++a) {
-            const int mt = wave + 4 * a;
+        for (int a = 0; a < P::MTW; ++a) {
+            const int mt = wave + NW * a;
             if (mt >= R::MT) continue;
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
@@ -1113,20 +1202,6 @@ __global__ __launch_bounds__(256) void chain_kernel(const int32_t* __restrict__ 
 }
 
 // ------------------------------------------------------------------ dispatch
-
-// Which bf16 hi/lo refinements the chain kernel applies to its two largest
-// products (state operand S and W): bit 0 = S, bit 1 = W.  Default none (the
-// errors stay well inside the bf16 tolerance); the environment variable
-// GDN_CHAIN_SPLIT (0..3) selects a refined variant.
-static int chain_split_mode()
-{
-    static int mode = -1;  // read once; racing initialisers store the same value
-    if (mode < 0) {
-        const char* e = getenv("GDN_CHAIN_SPLIT");
-        mode = (e && e[0] >= '0' && e[0] <= '3') ? e[0] - '0' : 0;
-    }
-    return mode;
-}
 
 template <typename TIn, int C, int DK, int DV>
 static hipError_t run_prefill(const PrefillArgs& a)
@@ -1173,31 +1248,22 @@ static hipError_t run_prefill(const PrefillArgs& a)
     const int64_t groups = (pairs + 7) / 8;
     const int64_t blocks = groups * 8 * (DV / (16 * NT));
     if (pairs > 0x7fffffff || blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-#define GDN_LAUNCH_CHAIN(SS_, SW_)                                                                                    \
-    do {                                                                                                              \
-        constexpr size_t lds_bytes = ChainLds<TIn, C, DK, NT, Rec<TIn, C, DK, DV>::SPLIT>::BYTES;                     \
-        static bool attr = false; /* idempotent; racing writers store the same value */                               \
-        if (!attr) {                                                                                                  \
-            hipError_t ea = hipFuncSetAttribute((const void*)chain_kernel<TIn, C, DK, DV, NT, SS_, SW_>,               \
-                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);          \
-            if (ea != hipSuccess) return ea;                                                                          \
-            attr = true;                                                                                              \
-        }                                                                                                             \
-        hipLaunchKernelGGL((chain_kernel<TIn, C, DK, DV, NT, SS_, SW_>), dim3((uint32_t)blocks), dim3(256), lds_bytes, \
-                           a.stream, header, tab, first, varlen, a.T, a.H, (int32_t)pairs, decay, records,            \
-                           a.lay.record_bytes, a.init_state, a.final_state, (TIn*)a.o, a.scale);                      \
-    } while (0)
-    if constexpr (sizeof(TIn) == 4) {
-        GDN_LAUNCH_CHAIN(false, false);  // fp32 operands: nothing to refine
-    } else {
-        switch (chain_split_mode()) {
-            case 0: GDN_LAUNCH_CHAIN(false, false); break;
-            case 1: GDN_LAUNCH_CHAIN(true, false); break;
-            case 2: GDN_LAUNCH_CHAIN(false, true); break;
-            default: GDN_LAUNCH_CHAIN(true, true); break;
+    {
+        constexpr int NW = 8;
+        using Lds = ChainLds<TIn, C, DK, DV, NT, NW, chain_staged<TIn, C>(), Rec<TIn, C, DK, DV>::SPLIT>;
+        static_assert(sizeof(Lds) <= 160 * 1024, "chain kernel LDS");
+        static bool attr = false;  // idempotent attribute; racing writers store the same value
+        if (!attr) {
+            hipError_t ea = hipFuncSetAttribute((const void*)chain_kernel<TIn, C, DK, DV, NT, NW>,
+                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(Lds));
+            if (ea != hipSuccess) return ea;
+            attr = true;
         }
+        hipLaunchKernelGGL((chain_kernel<TIn, C, DK, DV, NT, NW>), dim3((uint32_t)blocks),
+                           dim3((NW + chain_loaders<TIn, C>()) * 64), sizeof(Lds), a.stream, header, tab, first, varlen,
+                           a.T, a.H, (int32_t)pairs, records, a.lay.record_bytes, a.init_state, a.final_state,
+                           (TIn*)a.o, a.scale);
     }
-#undef GDN_LAUNCH_CHAIN
     return hipGetLastError();
 }
 

@@ -43,6 +43,16 @@ def test_every_declared_symbol_is_exported(lib):
         getattr(lib, n)  # resolvable through ctypes
 
 
+def test_no_unresolved_internal_symbols():
+    """Every kernel the host code launches is defined in the library itself (a
+    host-side kernel stub that the compiler failed to emit shows up here as an
+    undefined gdn:: symbol, which only fails when the library is bound eagerly)."""
+    out = subprocess.run(["nm", "-u", gdn.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    bad = [l.split()[-1] for l in out.splitlines() if "_ZN3gdn" in l]
+    assert not bad, f"undefined internal symbols: {bad[:5]}"
+    ctypes.CDLL(gdn.LIB_PATH, mode=os.RTLD_NOW)
+
+
 def test_status_strings(lib):
     for code, name in gdn.STATUS.items():
         assert lib.gdn_status_string(code).decode().startswith(name)

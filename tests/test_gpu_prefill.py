@@ -86,6 +86,21 @@ def test_bf16_other_head_dims(dk, dv):
     _check(inp, 64, TOL_BF16)
 
 
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 256), (256, 256)])
+def test_bf16_repeat_is_deterministic(dk, dv):
+    """Five identical calls: each matches the oracle and all are bitwise equal.
+    The kernels use no atomics, so any run-to-run difference exposes an
+    ordering hazard between operand staging and its readers."""
+    inp = synth.prefill_inputs(321, 2, dk, dv, "bf16", seed=7 * dk + dv, gate="slow")
+    o_ref, fs_ref = oracle.prefill(inp.q, inp.k, inp.v, inp.g, inp.beta, None, cu_seqlens=inp.cu_seqlens, bf16=True)
+    runs = [_gpu(inp, 64) for _ in range(5)]
+    for o, fs in runs:
+        assert bound_ratio(o, o_ref, TOL_BF16, stored_bf16=True) <= 1.0
+        assert rel_err(fs, fs_ref) <= TOL_BF16
+    for o, fs in runs[1:]:
+        assert np.array_equal(o, runs[0][0]) and np.array_equal(fs, runs[0][1])
+
+
 def test_bf16_prefill_8k_workload():
     """H=6, d=256, T=8192, bf16, chunk 64: every output and the final state."""
     inp = synth.prefill_inputs(8192, 6, 256, 256, "bf16", seed=synth.seed_for("prefill8k"))
