@@ -63,12 +63,12 @@ PrefillLayout prefill_layout(int64_t T, int32_t N, int32_t H, int32_t dk, int32_
     memset(&L, 0, sizeof L);
     L.max_chunks = T / C + N;  // >= sum_n ceil(L_n / C)
     const size_t el = bf16 ? 2 : 4;
-    // record: W fragments (C x dk, hi+lo for bf16), raw Q fragments (C x dk),
-    // raw K^T fragments (dk x C), P fragments (C x C, hi+lo for bf16) in the
-    // operand element type; then U tiles (C x dv), two per-row scale vectors
-    // (C each) and the chunk decay in fp32.
+    // record: W fragments (C x dk), raw K^T fragments (dk x C), raw Q fragments
+    // (C x dk), P fragments (C x C, hi+lo for bf16) in the operand element type;
+    // then U tiles (C x dv), two per-row scale vectors (C each) and the chunk
+    // decay with the chunk's token range in fp32/int32.
     const size_t split = bf16 ? 2 : 1;
-    const size_t oper = align_up(((size_t)C * dk * (split + 2) + (size_t)C * C * split) * el, 16);
+    const size_t oper = align_up(((size_t)C * dk * 3 + (size_t)C * C * split) * el, 16);
     L.record_bytes = align_up(oper + (size_t)C * dv * 4 + (size_t)C * 8 + 16, 256);
     size_t off = 0;
     L.off_header = off;
@@ -80,7 +80,12 @@ PrefillLayout prefill_layout(int64_t T, int32_t N, int32_t H, int32_t dk, int32_
     L.off_decay = off;
     off = align_up(off + (size_t)L.max_chunks * H * 4, 256);
     L.off_records = off;
-    off += (size_t)L.max_chunks * H * L.record_bytes;
+    off = align_up(off + (size_t)L.max_chunks * H * L.record_bytes, 256);
+    // outputs of the state chain for the output kernel
+    L.off_states = off;
+    off = align_up(off + (size_t)L.max_chunks * H * dv * dk * el, 256);
+    L.off_deltas = off;
+    off += (size_t)L.max_chunks * H * split * dv * C * el;
     L.total = off;
     return L;
 }

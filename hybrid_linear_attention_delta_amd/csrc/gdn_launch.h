@@ -32,6 +32,8 @@ struct PrefillLayout {
     size_t off_decay;       // float[max_chunks][H]: e^{gamma_L} per chunk-head
     size_t off_records;     // per chunk-head operand records
     size_t record_bytes;    // bytes of one record
+    size_t off_states;      // per chunk-head state entering the chunk [dv][dk], operand type
+    size_t off_deltas;      // per chunk-head Delta^T [hi, lo][dv][C], operand type
     size_t total;
 };
 
@@ -55,7 +57,7 @@ struct PrefillArgs {
     float* final_state;
     unsigned char* ws;
     PrefillLayout lay;
-    int32_t stages;  // bit 0: prepare (chunk table + intra-chunk), bit 1: propagate (chain)
+    int32_t stages;  // bit 0: prepare (chunk table + intra-chunk), bit 1: propagate (state chain + outputs)
     hipStream_t stream;
 };
 

@@ -179,12 +179,12 @@ struct Rec {
     static constexpr int CKS = C / KS;     // k-steps over the chunk (KS <= C)
     static constexpr int MT = DK / 16;     // d_k tiles
     static constexpr int VT = DV / 16;     // d_v tiles
-    static constexpr int WH_OFF = 0;                                  // [RT][DKS][64][E] W hi, sigma over d_k
-    static constexpr int WL_OFF = WH_OFF + C * DK;                    // [RT][DKS][64][E] W lo (bf16 only)
-    static constexpr int Q_OFF = WL_OFF + (SPLIT ? C * DK : 0);       // [RT][DKS][64][E] raw Q, sigma over d_k
-    static constexpr int K_OFF = Q_OFF + C * DK;                      // [MT][CKS][64][E] raw K^T, identity over chunk
-    static constexpr int PH_OFF = K_OFF + C * DK;                     // [RT][CKS][64][E] P hi
+    static constexpr int WH_OFF = 0;                                  // [RT][DKS][64][E] W, sigma over d_k
+    static constexpr int K_OFF = WH_OFF + C * DK;                     // [MT][CKS][64][E] raw K^T, identity over chunk
+    static constexpr int Q_OFF = K_OFF + C * DK;                      // [RT][DKS][64][E] raw Q, sigma over d_k
+    static constexpr int PH_OFF = Q_OFF + C * DK;                     // [RT][CKS][64][E] P hi
     static constexpr int PL_OFF = PH_OFF + C * C;                     // [RT][CKS][64][E] P lo (bf16 only)
+    static constexpr int CHAIN_ELEMS = Q_OFF;                         // the state chain's shared operands: W, K^T
     static constexpr int OPER_ELEMS = PL_OFF + (SPLIT ? C * C : 0);
     static constexpr size_t U_BYTE_OFF = ((size_t)OPER_ELEMS * sizeof(TIn) + 15) / 16 * 16;  // f32 [RT][VT][64][4]
     static constexpr size_t QS_BYTE_OFF = U_BYTE_OFF + (size_t)C * DV * 4;  // f32 [C]: rq_r e^{gamma_r}
@@ -635,10 +635,7 @@ __global__ __launch_bounds__(256) void intra_kernel(const TIn* __restrict__ q, c
             for (int u = 0; u < MT_PER; ++u)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) x[u * 4 + i] = acc[u][i];
-            Frag hi, lo;
-            split_frag<TIn>(x, hi, lo);
-            st_frag<TIn>(rec + R::WH_OFF + ((size_t)f * 64 + lane) * E, hi);
-            if constexpr (R::SPLIT) st_frag<TIn>(rec + R::WL_OFF + ((size_t)f * 64 + lane) * E, lo);
+            st_frag<TIn>(rec + R::WH_OFF + ((size_t)f * 64 + lane) * E, frag_from<TIn>(x));
         }
     }
 
@@ -723,10 +720,11 @@ __device__ __forceinline__ void lds_barrier()
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // The chain kernel stages its operands in LDS for bf16 operands (chunk 64);
-// fp32 operands of the production shape would not fit and are read directly.
+// fp32 operands of the production shape are read from the records directly.
 template <typename TIn, int C>
 constexpr bool chain_staged() { return sizeof(TIn) == 2 && C == 64; }
-// Loader waves of the staged form (they bring in every operand and write o).
+// Loader waves of the staged form (they bring in every operand and write the
+// per-chunk states and Delta out).
 template <typename TIn, int C>
 constexpr int chain_loaders() { return chain_staged<TIn, C>() ? 8 : 0; }
 
@@ -734,43 +732,50 @@ constexpr int chain_loaders() { return chain_staged<TIn, C>() ? 8 : 0; }
 template <typename TIn, int C, int DK, int DV, int NW>
 struct ChainSplit {
     using R = Rec<TIn, C, DK, DV>;
-    static constexpr int KQ = (NW / 4) < R::DKS ? (NW / 4) : R::DKS;  // d_k split of X and Y
+    static constexpr int KQ = (NW / 4) < R::DKS ? (NW / 4) : R::DKS;  // d_k split of X = W S^T
     static constexpr int KPW = R::DKS / KQ;                             // k-steps per phase-1 wave
     static constexpr int MTW = (R::MT + NW - 1) / NW;                   // state d_k tiles per wave
     static_assert(R::DKS % KQ == 0, "d_k split");
 };
 
-// LDS of the chain kernel.  In the staged form (STAGE) every per-chunk operand
-// is written here by dedicated loader waves; each operand region is
+// Per-chunk outputs of the state chain, read by the output kernel.
+//   states: [chunk][H][DV][DK] operand type, the state entering the chunk; bf16
+//           rows are in sigma order within each 32-column block
+//   deltas: [chunk][H][NS][DV][C] operand type, Delta^T (hi, lo for bf16), sigma
+//           order over the chunk positions
+template <typename TIn, int C, int DK, int DV>
+struct ChainOut {
+    static constexpr int NS = sizeof(TIn) == 2 ? 2 : 1;
+    static constexpr size_t STATE_ELEMS = (size_t)DV * DK;
+    static constexpr size_t DELTA_ELEMS = (size_t)NS * DV * C;
+};
+
+// LDS of the chain kernel.  In the staged form every per-chunk operand is
+// written here by dedicated loader waves; each operand region is
 // single-buffered and refilled as soon as its last reader has passed a
-// barrier.  Without STAGE (fp32 operands, which do not fit) the operands are
-// read from the records directly.
-template <typename TIn, int C, int DK, int DV, int NT, int NW, bool STAGE, bool SPLIT>
+// barrier.  Without STAGE (fp32 operands) the operands are read from the
+// records directly.
+template <typename TIn, int C, int DK, int DV, int NW, bool STAGE>
 struct ChainLds {
     using R = Rec<TIn, C, DK, DV>;
     using P = ChainSplit<TIn, C, DK, DV, NW>;
     static constexpr int SP = DK + 16 / (int)sizeof(TIn);  // state copy pitch (dwords = 4 mod 32)
     static constexpr int DP = C + 16 / (int)sizeof(TIn);   // Delta^T pitch
-    static constexpr int OP = 16 * NT + 4;                 // output tile pitch (elements)
-    static constexpr int NS = SPLIT ? 2 : 1;
+    static constexpr int NS = R::SPLIT ? 2 : 1;
     static constexpr int RT = C / 16;
     // operand fragment slots (1 KB each: 64 lanes x 16 B, lane order)
-    static constexpr int F_W = 0;                          // [RT][DKS] W hi
-    static constexpr int F_Q = F_W + RT * R::DKS;          // [RT][DKS] Q
-    static constexpr int F_K = F_Q + RT * R::DKS;          // [MT][CKS] K^T
-    static constexpr int F_P = F_K + R::MT * R::CKS;       // [NS][RT][CKS] P (hi, lo)
-    static constexpr int F_U = F_P + NS * RT * R::CKS;     // [RT][NT] U
-    static constexpr int F_SINK = F_U + RT * NT;           // landing slot of prefetch transfers
+    static constexpr int F_W = 0;                          // [RT][DKS] W
+    static constexpr int F_K = F_W + RT * R::DKS;          // [MT][CKS] K^T
+    static constexpr int F_U = F_K + R::MT * R::CKS;       // [RT] U (this workgroup's 16 value columns)
+    static constexpr int F_SINK = F_U + RT;                // landing slot of prefetch transfers
     static constexpr int NFRAG = STAGE ? F_SINK + 1 : 1;
     unsigned char frag[NFRAG][1024];
-    float qs[C], ksc[C];              // row scales
+    float ksc[C];                     // k row scales
     f32x4 meta[16];                   // [0] = e^{gamma_L}, tok0, len (a 256-byte landing area)
-    TIn sr[16 * NT * SP];             // state rows S[r][col] rounded to operands, sigma order
-    TIn dt[NS][16 * NT * DP];         // Delta^T[r][j], sigma order (hi, lo)
-    TIn ds[NS][16 * NT * DP];         // (kscale o Delta)^T[r][j], natural order (hi, lo)
-    f32x4 xp[P::KQ][RT][NT][64];      // partial W S^T per d_k part
-    f32x4 yp[P::KQ][RT][NT][64];      // partial Q S^T per d_k part
-    TIn ot[STAGE ? C * OP : 1];       // output tile of one chunk (staged form), row-major
+    TIn sr[16 * SP];                  // state rows S[r][col] rounded to operands, sigma order
+    TIn dt[NS][16 * DP];              // Delta^T[r][j], sigma order (hi, lo)
+    TIn ds[NS][16 * DP];              // (kscale o Delta)^T[r][j], natural order (hi, lo)
+    f32x4 xp[P::KQ][RT][64];          // partial W S^T per d_k part
 };
 
 template <int N>
@@ -780,43 +785,44 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// One workgroup per (sequence, head, 16*NT state rows), sequential over the
-// sequence's chunks: NW compute waves plus, in the staged form, NL loader waves.
-// Per chunk, compute waves:
-//   phase 1  wave (rt, kq) = (w % 4, w / 4): partial X = W S^T and Y = Q S^T of
-//            chunk row tile rt over d_k part kq (partials to LDS)
+// State chain: one workgroup per (sequence, head, 16 state rows), sequential
+// over the sequence's chunks.  Per chunk c, the NW compute waves
+//   phase 1  wave (rt, kq) = (w % 4, w / 4): partial X = W S^T of chunk row
+//            tile rt over d_k part kq (partials to LDS)
 //   phase 2  wave (rt, 0): Delta = U - X -> LDS (sigma and natural order, hi/lo)
-//   phase 3  wave (rt, 1 or 0): O = scale (qscale o Y + P Delta)
-//            every wave: its state d_k tiles, S^T = e^{gamma_L} S^T + K^T (kscale o Delta)
-// Loader waves (staged form) load every operand into registers, write it to
-// LDS before the barrier whose readers need it, and write o from an LDS tile
-// one chunk later (details at the loader transfer helpers).
+//   phase 3  every wave, its state d_k tiles: S^T = e^{gamma_L} S^T + K^T (kscale o Delta)
+// separated by the barriers A, B, C.  The state entering chunk c and Delta of
+// chunk c go to `states` and `deltas` for the output kernel (by the loader
+// waves in the staged form, else by the compute waves).
 // Workgroups are mapped so that all row tiles of one (sequence, head) pair run
 // on one XCD (workgroups are dealt to the 8 XCDs round-robin): they read the
 // same per-chunk records, which then come from that XCD's L2.
-template <typename TIn, int C, int DK, int DV, int NT, int NW>
+template <typename TIn, int C, int DK, int DV, int NW>
 __global__ __launch_bounds__((NW + chain_loaders<TIn, C>()) * 64) void chain_kernel(
-    const int32_t* __restrict__ header, const ChunkInfo* __restrict__ tab, const int32_t* __restrict__ seq_first,
-    int32_t varlen, int64_t T, int32_t H, int32_t pairs, const unsigned char* __restrict__ records,
-    size_t record_bytes, const float* __restrict__ init_state, float* __restrict__ final_state, TIn* __restrict__ o,
-    float scale)
+    const int32_t* __restrict__ header, const int32_t* __restrict__ seq_first, int32_t varlen, int64_t T, int32_t H,
+    int32_t pairs, const unsigned char* records, size_t record_bytes, const float* __restrict__ init_state,
+    float* __restrict__ final_state, TIn* __restrict__ states, TIn* __restrict__ deltas)
+// (records is deliberately not __restrict__: a restrict read-only argument lets
+// the compiler treat its loads as invariant and sink them across the barriers
+// to their use, which would turn the loaders' early loads into late ones)
 {
     using M = Mma<TIn>;
     using R = Rec<TIn, C, DK, DV>;
     using P = ChainSplit<TIn, C, DK, DV, NW>;
+    using CO = ChainOut<TIn, C, DK, DV>;
     constexpr bool SPL = R::SPLIT;
     constexpr bool STAGE = chain_staged<TIn, C>();
     constexpr int NL = chain_loaders<TIn, C>();
-    using L = ChainLds<TIn, C, DK, DV, NT, NW, STAGE, SPL>;
+    using L = ChainLds<TIn, C, DK, DV, NW, STAGE>;
     typedef typename M::Frag Frag;
     constexpr int KS = M::KS, E = M::E;
     constexpr int SP = L::SP, DP = L::DP, NS = L::NS;
     constexpr int RT = R::RT;
-    constexpr int TILES = DV / (16 * NT);
+    constexpr int TILES = DV / 16;
     constexpr uint32_t FB = 64 * 16;  // bytes of one operand fragment (64 lanes x 16 B)
     constexpr uint32_t EB = sizeof(TIn);
-    constexpr int SINK = STAGE ? L::F_SINK : 0;  // landing slot of prefetch transfers
-    static_assert(!STAGE || (C == 64 && NT == 1 && (NL == 4 || NL == 8)), "staged form: chunk 64, 16 state rows");
+    constexpr int SINK = STAGE ? L::F_SINK : 0;
+    static_assert(!STAGE || (C == 64 && NL == 8), "staged form: chunk 64, 8 loader waves");
 
     extern __shared__ __align__(16) unsigned char lds_raw[];
     L& sm = *reinterpret_cast<L*>(lds_raw);
@@ -831,7 +837,7 @@ __global__ __launch_bounds__((NW + chain_loaders<TIn, C>()) * 64) void chain_ker
     if (pair >= pairs) return;
     const int n = pair / H, h = pair % H;
     const int tile = slot % TILES;
-    const int row0 = tile * 16 * NT;  // first state row (value index) of this workgroup
+    const int row0 = tile * 16;  // first state row (value index) of this workgroup
 
     int64_t c_begin, c_end;
     if (varlen) {
@@ -843,151 +849,134 @@ __global__ __launch_bounds__((NW + chain_loaders<TIn, C>()) * 64) void chain_ker
         c_end = (T + C - 1) / C;
     }
 
-    // compute roles
-    const int rt = wave & 3, kq = wave >> 2;
-    const bool p1 = !loader && rt < RT && kq < P::KQ;                     // phase-1 partial products
-    const bool fin_d = !loader && rt < RT && kq == 0;                     // Delta finaliser of row tile rt
-    const bool fin_o = !loader && rt < RT && kq == (P::KQ > 1 ? 1 : 0);   // output finaliser of row tile rt
-    const int pks = (rt * 16 + 16 + KS - 1) / KS;                         // P k-steps up to the diagonal
-
     // ---------------------------------------------------------------- operands
     const uint32_t lane_b = (uint32_t)lane * 16;
     auto rec_ptr = [&](int64_t c) { return records + ((size_t)c * H + h) * record_bytes; };
-    // fragment of the current chunk: LDS slot `f` (staged) or record byte offset `src` (direct)
-    __amdgpu_buffer_rsrc_t rcur = make_rsrc(records, 0u);
-    auto frag = [&](int f, uint32_t src) -> Frag {
-        if constexpr (STAGE) return *reinterpret_cast<const Frag*>(sm.frag[f] + lane_b);
-        else return __builtin_bit_cast(Frag, buf_load16(rcur, lane_b, src));
-    };
-    auto row4 = [&](const float* lds, size_t byte_off, int r) -> f32x4 {  // 4 row scales from r
-        if constexpr (STAGE) return *reinterpret_cast<const f32x4*>(lds + r);
-        else return __builtin_bit_cast(f32x4, buf_load16(rcur, (uint32_t)r * 4, (uint32_t)byte_off));
-    };
     auto w_src = [&](int r, int ks) { return R::WH_OFF * EB + (uint32_t)(r * R::DKS + ks) * FB; };
-    auto q_src = [&](int r, int ks) { return R::Q_OFF * EB + (uint32_t)(r * R::DKS + ks) * FB; };
     auto k_src = [&](int mt, int ks) { return R::K_OFF * EB + (uint32_t)(mt * R::CKS + ks) * FB; };
-    auto p_src = [&](int part, int r, int ks) {
-        return (part ? R::PL_OFF : R::PH_OFF) * EB + (uint32_t)(r * R::CKS + ks) * FB;
-    };
-    auto u_src = [&](int r, int nt) {
-        return (uint32_t)R::U_BYTE_OFF + (uint32_t)(r * R::VT + (row0 >> 4) + nt) * FB;
-    };
-
-    // ------------------------------------------------- loader transfers (staged form)
-    // Loader waves 0 .. NOP-1 load operands into registers and write them to LDS
-    // once they arrive; per chunk c:
-    //   group A (U, k scales of c)               load after C(c-1), write before A(c)
-    //   group B (K^T, P, q scales, meta of c)    load after C(c-1), write after A(c)
-    //   group W (W, Q of c+1)                    load after A(c),   write after B(c)
-    // (the first chunk's groups A and W are loaded before the loop).  Loaders
-    // 0..3 also write o of chunk c-1 from the LDS output tile after C(c-1).
-    // Every wave issues the same loads on every path (indices past the end are
-    // clamped to the last fragment), so the compiler's vmcnt waits stay exact.
-    // The last loader wave only prefetches: after C(c-1) it brings a share of
-    // chunk c+2's shared operands and this workgroup's U tiles into L2 by
-    // fire-and-forget LDS-DMA transfers into a sink slot; it waits for nothing
-    // in the loop, so the in-order vmcnt of the other waves never includes them.
-    constexpr int NLd = NL > 0 ? NL : 1;
-    constexpr int NOP = NLd > 1 ? NLd - 1 : 1;     // operand loaders
-    const bool pf_wave = lw == NOP;
-    constexpr int NK = R::MT * R::CKS, NP = NS * RT * R::CKS, NKP = NK + NP;
-    constexpr int NB = (NKP + NOP - 1) / NOP;      // K/P fragments per loader
-    constexpr int NWQ = 2 * RT * R::DKS;
-    constexpr int NWL = (NWQ + NOP - 1) / NOP;     // W/Q fragments per loader
-    constexpr int NU = RT * NT;
-    constexpr int L_KSC = NU % NOP, L_QS = (NU + 1) % NOP, L_META = (NU + 2) % NOP;
-    static_assert(!STAGE || (NU <= NOP && NOP >= 3), "one loader per U tile, distinct row-vector loaders");
-    // K^T fragments then P fragments are contiguous in the record: fragment f at K_OFF + f KB
-    static_assert(R::PH_OFF == R::K_OFF + C * DK && R::PL_OFF == R::PH_OFF + C * C, "record layout");
-    auto kp_src = [&](int f) { return R::K_OFF * EB + (uint32_t)f * FB; };
-    auto wq_src = [&](int f) -> uint32_t {
-        const int kind = f / (RT * R::DKS), rem = f % (RT * R::DKS);
-        return kind ? q_src(rem / R::DKS, rem % R::DKS) : w_src(rem / R::DKS, rem % R::DKS);
-    };
-    struct GroupA { u32x4 u; uint32_t x; };
-    struct GroupB { u32x4 f[NB]; uint32_t x; };
-    struct GroupW { u32x4 f[NWL]; };
-    // row vectors: loader L_KSC -> k scales, L_QS -> q scales, L_META -> meta (a 16-byte view)
-    auto load_a = [&](int64_t c, GroupA& g) {
-        const unsigned char* rb = rec_ptr(c);
-        if (lw < NU) g.u = buf_load16(make_rsrc(rb, (uint32_t)R::BYTES), lane_b, u_src(lw / NT, lw % NT));
-        if (lw == L_KSC) g.x = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(rb + R::KSC_BYTE_OFF, C * 4), lane * 4, 0, 0);
-    };
-    auto write_a = [&](const GroupA& g) {
-        if (lw < NU) *reinterpret_cast<u32x4*>(sm.frag[L::F_U + lw] + lane_b) = g.u;
-        if (lw == L_KSC) reinterpret_cast<uint32_t*>(sm.ksc)[lane] = g.x;
-    };
-    auto load_b = [&](int64_t c, GroupB& g) {
-        const unsigned char* rb = rec_ptr(c);
-        const __amdgpu_buffer_rsrc_t r = make_rsrc(rb, (uint32_t)R::BYTES);
-#pragma unroll
-        for (int i = 0; i < NB; ++i) {
-            const int f = min(lw + NOP * i, NKP - 1);
-            g.f[i] = buf_load16(r, lane_b, kp_src(f));
-        }
-        if (lw == L_QS) g.x = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(rb + R::QS_BYTE_OFF, C * 4), lane * 4, 0, 0);
-        if (lw == L_META) g.x = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(rb + R::DEC_BYTE_OFF, 16), lane * 4, 0, 0);
-    };
-    auto write_b = [&](const GroupB& g) {
-#pragma unroll
-        for (int i = 0; i < NB; ++i) {
-            const int f = min(lw + NOP * i, NKP - 1);
-            *reinterpret_cast<u32x4*>(sm.frag[L::F_K + f] + lane_b) = g.f[i];  // F_P = F_K + NK
-        }
-        if (lw == L_QS) reinterpret_cast<uint32_t*>(sm.qs)[lane] = g.x;
-        if (lw == L_META) reinterpret_cast<uint32_t*>(sm.meta)[lane] = g.x;  // lanes >= 4 write 0 into the landing area
-    };
-    auto load_w = [&](int64_t c, GroupW& g) {
-        const __amdgpu_buffer_rsrc_t r = make_rsrc(rec_ptr(c), (uint32_t)R::BYTES);
-#pragma unroll
-        for (int i = 0; i < NWL; ++i) g.f[i] = buf_load16(r, lane_b, wq_src(min(lw + NOP * i, NWQ - 1)));
-    };
-    auto write_w = [&](const GroupW& g) {
-#pragma unroll
-        for (int i = 0; i < NWL; ++i)
-            *reinterpret_cast<u32x4*>(sm.frag[L::F_W + min(lw + NOP * i, NWQ - 1)] + lane_b) = g.f[i];
-    };
-    // prefetch wave: a 1/TILES share of chunk cp's shared operands (W hi, Q,
-    // K^T, P: identical for all row tiles) and this workgroup's U tiles
-    constexpr uint32_t W_KB = (uint32_t)(C * DK * EB / 1024);
-    constexpr uint32_t REST_KB = (uint32_t)((R::U_BYTE_OFF - (size_t)R::Q_OFF * EB) / 1024);
-    constexpr uint32_t SHARED_KB = W_KB + REST_KB;
-    constexpr int PF = (int)((SHARED_KB + TILES - 1) / TILES);
-    auto prefetch = [&](int64_t cp) {
-        const __amdgpu_buffer_rsrc_t r = make_rsrc(rec_ptr(cp), (uint32_t)R::BYTES);
-#pragma unroll
-        for (int i = 0; i < PF; ++i) {
-            uint32_t blk = (uint32_t)(i * TILES + tile);
-            blk = blk < SHARED_KB ? blk : SHARED_KB - 1;
-            const uint32_t src = blk < W_KB ? blk * 1024 : (uint32_t)R::Q_OFF * EB + (blk - W_KB) * 1024;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)sm.frag[SINK], 16, lane_b, src, 0, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < NU; ++i) {
-            const uint32_t src = u_src(i / NT, i % NT);  // (a lambda call directly inside the builtin's
-                                                         // argument list drops the host-side kernel stub)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)sm.frag[SINK], 16, lane_b, src, 0, 0);
-        }
-    };
-    // output tile of one chunk (LDS, row-major) -> o by loaders 0..3, 4 values per
-    // lane; rows >= len fall outside the view
-    static_assert(!STAGE || (NOP >= 4 && 16 * NT == 16), "output tile store mapping");
-    const uint32_t rowstride_o = (uint32_t)H * DV * EB;
-    auto store_o = [&](int tok0, int len) {
-        if (lw < 4) {
-            const __amdgpu_buffer_rsrc_t ro =
-                make_rsrc(o + ((int64_t)tok0 * H + h) * DV, (uint32_t)(((len - 1) * H + 1) * DV * EB));
-            const int lt = lw * 64 + lane, row = lt >> 2, part = lt & 3;
-            const u32x2 val = *reinterpret_cast<const u32x2*>(sm.ot + row * L::OP + part * 4);
-            __builtin_amdgcn_raw_buffer_store_b64(val, ro, (int)((uint32_t)row * rowstride_o + (uint32_t)(row0 + part * 4) * EB),
-                                                  0, 0);
-        }
+    auto u_src = [&](int r) { return (uint32_t)R::U_BYTE_OFF + (uint32_t)(r * R::VT + tile) * FB; };
+    auto state_out = [&](int64_t c) { return states + ((size_t)c * H + h) * CO::STATE_ELEMS + (size_t)row0 * DK; };
+    auto delta_out = [&](int64_t c, int part) {
+        return deltas + ((size_t)c * H + h) * CO::DELTA_ELEMS + ((size_t)part * DV + row0) * C;
     };
 
-    // ---------------------------------------------------------------- loader waves
+    // ------------------------------------------------- loader waves (staged form)
+    // The compute waves read, in the three phases of chunk c: W(c) (phase 1),
+    // U(c) and the k scales (phase 2), K^T(c) and the decay (phase 3).  Each LDS
+    // region is refilled in the phase after its last read, from registers that
+    // the operand loaders (waves 0 .. NOP-1) loaded about one and a half phases
+    // earlier, so no barrier waits for a load that was just issued:
+    //   phase 1 of c:  write K^T(c), meta(c);  load U(c+1), k scales(c+1)
+    //   phase 2 of c:  write W(c+1);           load K^T(c+1), meta(c+1)
+    //   phase 3 of c:  write U(c+1), k scales; load W(c+2)
+    // Chunk indices past the sequence are clamped to its last chunk (harmless
+    // reloads).  Loaders 0..3 copy the state rows entering chunk c to `states`
+    // (phase 1 of c, before phase 3 rewrites them) and loaders 3..6 copy Delta
+    // of chunk c to `deltas` (phase 3 of c).  Every loader issues the same loads
+    // on every path (fragment indices past the end are clamped), so the
+    // compiler's vmcnt waits stay exact.  The last loader wave only prefetches:
+    // each phase 1 it brings its share of chunk c+2's W and K^T and this
+    // workgroup's U tiles into L2 by fire-and-forget LDS-DMA transfers into a
+    // sink slot; it waits for nothing in the loop, so the in-order vmcnt of the
+    // other waves never includes them.
     if (loader) {
         if constexpr (STAGE) {
-            if (pf_wave) {
+            constexpr int NOP = NL - 1;  // operand loaders
+            constexpr int NWF = RT * R::DKS, NKF = R::MT * R::CKS;
+            constexpr int NWL = (NWF + NOP - 1) / NOP, NKL = (NKF + NOP - 1) / NOP;
+            constexpr int L_KSC = RT % NOP, L_META = (RT + 1) % NOP;
+            static_assert(RT + 2 <= NOP && NOP >= 7, "one loader per U tile, distinct row-vector loaders");
+            struct GroupU { u32x4 u; uint32_t x; };
+            struct GroupK { u32x4 f[NKL]; uint32_t x; };
+            struct GroupW { u32x4 f[NWL]; };
+            // Every loader issues the same loads and stores; a wave without the role
+            // reads a duplicate or stores through an empty view (dropped).
+            auto load_u = [&](int64_t c, GroupU& g) {
+                const unsigned char* rb = rec_ptr(c);
+                g.u = buf_load16(make_rsrc(rb, (uint32_t)R::BYTES), lane_b, u_src(lw % RT));
+                g.x = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(rb + R::KSC_BYTE_OFF, C * 4), lane * 4, 0, 0);
+            };
+            auto write_u = [&](const GroupU& g) {
+                if (lw < RT) *reinterpret_cast<u32x4*>(sm.frag[L::F_U + lw] + lane_b) = g.u;
+                if (lw == L_KSC) reinterpret_cast<uint32_t*>(sm.ksc)[lane] = g.x;
+            };
+            auto load_k = [&](int64_t c, GroupK& g) {
+                const unsigned char* rb = rec_ptr(c);
+                const __amdgpu_buffer_rsrc_t r = make_rsrc(rb, (uint32_t)R::BYTES);
+#pragma unroll
+                for (int i = 0; i < NKL; ++i) {
+                    const int f = min(lw + NOP * i, NKF - 1);
+                    g.f[i] = buf_load16(r, lane_b, k_src(f / R::CKS, f % R::CKS));
+                }
+                g.x = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(rb + R::DEC_BYTE_OFF, 16), lane * 4, 0, 0);
+            };
+            auto write_k = [&](const GroupK& g) {
+#pragma unroll
+                for (int i = 0; i < NKL; ++i) {
+                    const int f = min(lw + NOP * i, NKF - 1);
+                    *reinterpret_cast<u32x4*>(sm.frag[L::F_K + f] + lane_b) = g.f[i];
+                }
+                if (lw == L_META) reinterpret_cast<uint32_t*>(sm.meta)[lane] = g.x;  // lanes >= 4 write 0
+            };
+            auto load_w = [&](int64_t c, GroupW& g) {
+                const __amdgpu_buffer_rsrc_t r = make_rsrc(rec_ptr(c), (uint32_t)R::BYTES);
+#pragma unroll
+                for (int i = 0; i < NWL; ++i) {
+                    const int f = min(lw + NOP * i, NWF - 1);
+                    g.f[i] = buf_load16(r, lane_b, w_src(f / R::DKS, f % R::DKS));
+                }
+            };
+            auto write_w = [&](const GroupW& g) {
+#pragma unroll
+                for (int i = 0; i < NWL; ++i)
+                    *reinterpret_cast<u32x4*>(sm.frag[L::F_W + min(lw + NOP * i, NWF - 1)] + lane_b) = g.f[i];
+            };
+            // LDS rows -> global rows, 16 bytes per lane
+            constexpr int SROW = DK * (int)EB / 16;          // 16-byte units per state row
+            constexpr int SU = (16 * SROW + 255) / 256;      // units per lane of loaders 0..3
+            auto store_state = [&](int64_t c) {
+                const __amdgpu_buffer_rsrc_t r = make_rsrc(state_out(c), lw < 4 ? 16u * DK * EB : 0u);
+#pragma unroll
+                for (int i = 0; i < SU; ++i) {
+                    int u = ((lw & 3) * 64 + lane) + 256 * i;
+                    u = u < 16 * SROW ? u : 16 * SROW;  // past the rows: offset past the view, dropped
+                    const int row = min(u / SROW, 15), part = u % SROW;
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(sm.sr + row * SP + part * 8);
+                    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)((uint32_t)u * 16), 0, 0);
+                }
+            };
+            constexpr int DROW = C * (int)EB / 16;           // 16-byte units per Delta row (8)
+            static_assert(NS == 2 && 16 * DROW == 128, "one Delta unit per lane of loaders 3..6, two per part");
+            auto store_delta = [&](int64_t c) {
+                const bool live = lw >= 3 && lw < 7;
+                const int part = ((lw + 1) >> 1) & 1;  // loaders 3, 4 -> hi; 5, 6 -> lo (wave-uniform)
+                const int u = ((lw + 1) & 1) * 64 + lane, row = u / DROW, q = u % DROW;
+                const u32x4 v = *reinterpret_cast<const u32x4*>(sm.dt[part] + row * DP + q * 8);
+                const __amdgpu_buffer_rsrc_t r = make_rsrc(delta_out(c, part), live ? 16u * C * EB : 0u);
+                __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)((uint32_t)row * C * EB + q * 16), 0, 0);
+            };
+            // prefetch wave: a 1/TILES share of chunk cp's W and K^T (identical for
+            // all row tiles) and this workgroup's U tiles
+            constexpr uint32_t SHARED_KB = (uint32_t)((size_t)R::CHAIN_ELEMS * EB / 1024);
+            constexpr int PF = (int)((SHARED_KB + TILES - 1) / TILES);
+            auto prefetch = [&](int64_t cp) {
+                const __amdgpu_buffer_rsrc_t r = make_rsrc(rec_ptr(cp), (uint32_t)R::BYTES);
+#pragma unroll
+                for (int i = 0; i < PF; ++i) {
+                    uint32_t blk = (uint32_t)(i * TILES + tile);
+                    blk = blk < SHARED_KB ? blk : SHARED_KB - 1;
+                    const uint32_t src = blk * 1024;
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)sm.frag[SINK], 16, lane_b, src, 0, 0);
+                }
+#pragma unroll
+                for (int i = 0; i < RT; ++i) {
+                    const uint32_t src = u_src(i);  // (a lambda call inside the builtin's argument list
+                                                    // drops the host-side kernel stub)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)sm.frag[SINK], 16, lane_b, src, 0, 0);
+                }
+            };
+
+            if (lw == NOP) {
                 __syncthreads();
                 for (int64_t c = c_begin; c < c_end; ++c) {
                     if (c + 2 < c_end) prefetch(c + 2);
@@ -998,206 +987,275 @@ __global__ __launch_bounds__((NW + chain_loaders<TIn, C>()) * 64) void chain_ker
                 wait_vmcnt<0>();  // no transfer may still target LDS when the workgroup ends
                 return;
             }
+            const int64_t last = c_end - 1;
+            GroupK gk;  // K^T, meta of the next chunk to write
+            GroupW gw;  // W of the chunk after the current one
             if (c_begin < c_end) {
-                GroupA ga;
-                GroupW gw;
-                load_a(c_begin, ga);
-                load_w(c_begin, gw);
-                write_a(ga);
-                write_w(gw);
+                GroupU gu;
+                GroupW w0;
+                load_u(c_begin, gu);
+                load_w(c_begin, w0);
+                load_k(c_begin, gk);
+                load_w(min(c_begin + 1, last), gw);
+                write_u(gu);
+                write_w(w0);
             }
-            __syncthreads();
-            int otok0 = 0, olen = 0;  // chunk whose outputs sit in the output tile
+            __syncthreads();  // the compute waves have written the initial state rows
             for (int64_t c = c_begin; c < c_end; ++c) {
-                const int64_t cn = c + 1 < c_end ? c + 1 : c;  // W/Q source (the last chunk reloads its own)
-                GroupA ga;
-                GroupB gb;
-                GroupW gw;
-                load_a(c, ga);  // the first chunk's group A reloads the same values
-                load_b(c, gb);
-                if (c > c_begin) store_o(otok0, olen);
-                write_a(ga);
+                GroupU gu;
+                // ---- phase 1 of c
+                write_k(gk);
+                store_state(c);
+                load_u(min(c + 1, last), gu);
                 lds_barrier();  // ---- A
-                load_w(cn, gw);
-                write_b(gb);
+                // ---- phase 2 of c
+                load_k(min(c + 1, last), gk);
+                write_w(gw);
                 lds_barrier();  // ---- B
-                const f32x4 meta = sm.meta[0];
-                otok0 = __builtin_amdgcn_readfirstlane(__float_as_int(meta.y));
-                olen = __builtin_amdgcn_readfirstlane(__float_as_int(meta.z));
-                write_w(gw);  // after the last chunk's B nobody reads the W/Q regions again
+                // ---- phase 3 of c
+                write_u(gu);
+                store_delta(c);
+                load_w(min(c + 2, last), gw);
                 lds_barrier();  // ---- C
             }
-            if (c_begin < c_end) store_o(otok0, olen);
             wait_vmcnt<0>();
         }
         return;
     }
 
     // ---------------------------------------------------------------- compute waves
-    // state tiles S^T[mt][nt] in result layout: lane holds S[row0 + nt*16 + l16][mt*16 + 4*g16 + i]
-    f32x4 S[P::MTW][NT];
+    // fragment of the current chunk: LDS slot `f` (staged) or record byte offset `src` (direct)
+    __amdgpu_buffer_rsrc_t rcur = make_rsrc(records, 0u);
+    auto frag = [&](int f, uint32_t src) -> Frag {
+        if constexpr (STAGE) return *reinterpret_cast<const Frag*>(sm.frag[f] + lane_b);
+        else return __builtin_bit_cast(Frag, buf_load16(rcur, lane_b, src));
+    };
+    const int rt = wave & 3, kq = wave >> 2;
+    const bool p1 = rt < RT && kq < P::KQ;   // phase-1 partial products
+    const bool fin_d = rt < RT && kq == 0;   // Delta finaliser of row tile rt
+
+    // state tiles S^T[mt] in result layout: lane holds S[row0 + l16][mt*16 + 4*g16 + i]
+    f32x4 S[P::MTW];
     const size_t st_base = ((size_t)n * H + h) * DV * DK;
 #pragma unroll
     for (int a = 0; a < P::MTW; ++a) {
         const int mt = wave + NW * a;
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            S[a][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (mt < R::MT) {
-                if (init_state)
-                    S[a][nt] = *reinterpret_cast<const f32x4*>(init_state + st_base +
-                                                               (size_t)(row0 + nt * 16 + l16) * DK + mt * 16 + 4 * g16);
-                const int off = (nt * 16 + l16) * SP + quad_pos<TIn>(mt, g16);
-                store_quad<TIn, false>(sm.sr + off, sm.sr + off, S[a][nt]);
-            }
+        S[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (mt < R::MT) {
+            if (init_state)
+                S[a] = *reinterpret_cast<const f32x4*>(init_state + st_base + (size_t)(row0 + l16) * DK + mt * 16 +
+                                                       4 * g16);
+            store_quad<TIn, false>(sm.sr + l16 * SP + quad_pos<TIn>(mt, g16), nullptr, S[a]);
         }
     }
-
     __syncthreads();
 
     for (int64_t c = c_begin; c < c_end; ++c) {
-        if constexpr (!STAGE) rcur = make_rsrc(rec_ptr(c), (uint32_t)R::BYTES);
-        if (p1) {
-            // ---- phase 1: partial X = W S^T and Y = Q S^T over this wave's d_k part
-            f32x4 X[NT], Y[NT];
+        if constexpr (!STAGE) {
+            rcur = make_rsrc(rec_ptr(c), (uint32_t)R::BYTES);
+            // the state entering chunk c (fp32, natural order)
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) X[nt] = Y[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int a = 0; a < P::MTW; ++a) {
+                const int mt = wave + NW * a;
+                if (mt < R::MT)
+                    *reinterpret_cast<f32x4*>(state_out(c) + (size_t)l16 * DK + mt * 16 + 4 * g16) = S[a];
+            }
+        }
+        if (p1) {
+            // ---- phase 1: partial X = W S^T over this wave's d_k part
+            f32x4 X = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int i = 0; i < P::KPW; ++i) {
                 const int ks = kq * P::KPW + i;
                 const Frag fw = frag(L::F_W + rt * R::DKS + ks, w_src(rt, ks));
-                const Frag fq = frag(L::F_Q + rt * R::DKS + ks, q_src(rt, ks));
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    const Frag b = *reinterpret_cast<const Frag*>(sm.sr + (nt * 16 + l16) * SP + ks * KS + g16 * E);
-                    X[nt] = M::mma(fw, b, X[nt]);
-                    Y[nt] = M::mma(fq, b, Y[nt]);
-                }
+                X = M::mma(fw, *reinterpret_cast<const Frag*>(sm.sr + l16 * SP + ks * KS + g16 * E), X);
             }
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                sm.xp[kq][rt][nt][lane] = X[nt];
-                sm.yp[kq][rt][nt][lane] = Y[nt];
-            }
+            sm.xp[kq][rt][lane] = X;
         }
-        lds_barrier();  // ---- A: partials visible; W/Q regions free
+        lds_barrier();  // ---- A: partials visible; W region free
 
         if (fin_d) {
             // ---- phase 2: Delta = U - X for row tile rt (sigma-ordered dt, natural-order ds)
-            const f32x4 ks4 = row4(sm.ksc, R::KSC_BYTE_OFF, rt * 16 + 4 * g16);
+            const f32x4 ks4 = STAGE ? *reinterpret_cast<const f32x4*>(sm.ksc + rt * 16 + 4 * g16)
+                                    : __builtin_bit_cast(f32x4, buf_load16(rcur, (uint32_t)(rt * 16 + 4 * g16) * 4,
+                                                                           (uint32_t)R::KSC_BYTE_OFF));
+            f32x4 X = sm.xp[0][rt][lane];
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                f32x4 X = sm.xp[0][rt][nt][lane];
-#pragma unroll
-                for (int qq = 1; qq < P::KQ; ++qq) X += sm.xp[qq][rt][nt][lane];
-                const f32x4 u = __builtin_bit_cast(f32x4, frag(L::F_U + rt * NT + nt, u_src(rt, nt)));
-                const f32x4 d = u - X;
-                const int row = (nt * 16 + l16) * DP;
-                const int pd = row + quad_pos<TIn>(rt, g16);
-                const int pn = row + rt * 16 + 4 * g16;
-                store_quad<TIn, SPL>(sm.dt[0] + pd, sm.dt[NS - 1] + pd, d);
-                store_quad<TIn, SPL>(sm.ds[0] + pn, sm.ds[NS - 1] + pn, d * ks4);
-            }
+            for (int qq = 1; qq < P::KQ; ++qq) X += sm.xp[qq][rt][lane];
+            const f32x4 d = __builtin_bit_cast(f32x4, frag(L::F_U + rt, u_src(rt))) - X;
+            const int pd = l16 * DP + quad_pos<TIn>(rt, g16);
+            const int pn = l16 * DP + rt * 16 + 4 * g16;
+            store_quad<TIn, SPL>(sm.dt[0] + pd, sm.dt[NS - 1] + pd, d);
+            store_quad<TIn, SPL>(sm.ds[0] + pn, sm.ds[NS - 1] + pn, d * ks4);
+            if constexpr (!STAGE)  // Delta^T rows (fp32, natural order over the chunk)
+                *reinterpret_cast<f32x4*>(delta_out(c, 0) + (size_t)l16 * C + rt * 16 + 4 * g16) = d;
         }
         lds_barrier();  // ---- B: Delta visible; U region free
 
-        f32x4 meta;
-        if constexpr (STAGE) meta = sm.meta[0];
-        else meta = __builtin_bit_cast(f32x4, buf_load16(rcur, 0, (uint32_t)R::DEC_BYTE_OFF));
-        const int tok0 = __builtin_amdgcn_readfirstlane(__float_as_int(meta.y));
-        const int len = __builtin_amdgcn_readfirstlane(__float_as_int(meta.z));
-        {
-            // ---- phase 3a: O = scale (qscale o Y + P Delta); P fragments are sigma-ordered over j
-            if constexpr (STAGE) {
-                if (fin_o) {
-                    f32x4 Y = sm.yp[0][rt][0][lane];
+        // ---- phase 3: state update on this wave's d_k tiles
+        const float decay = STAGE ? sm.meta[0].x
+                                  : __builtin_bit_cast(f32x4, buf_load16(rcur, 0, (uint32_t)R::DEC_BYTE_OFF)).x;
 #pragma unroll
-                    for (int qq = 1; qq < P::KQ; ++qq) Y += sm.yp[qq][rt][0][lane];
-                    Y *= row4(sm.qs, R::QS_BYTE_OFF, rt * 16 + 4 * g16);
+        for (int a = 0; a < P::MTW; ++a) {
+            const int mt = wave + NW * a;
+            if (mt >= R::MT) continue;
+            f32x4 acc = S[a] * decay;
 #pragma unroll
-                    for (int ks = 0; ks < R::CKS; ++ks) {
-                        if (ks < pks) {
-                            const int doff = l16 * DP + ks * KS + g16 * E;
-                            const Frag ph = frag(L::F_P + rt * R::CKS + ks, 0);
-                            const Frag pl = frag(L::F_P + (RT + rt) * R::CKS + ks, 0);
-                            const Frag dh = *reinterpret_cast<const Frag*>(sm.dt[0] + doff);
-                            const Frag dl = *reinterpret_cast<const Frag*>(sm.dt[1] + doff);
-                            Y = M::mma(ph, dh, Y);
-                            Y = M::mma(pl, dh, Y);
-                            Y = M::mma(ph, dl, Y);
-                        }
-                    }
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        sm.ot[(rt * 16 + 4 * g16 + i) * L::OP + l16] = M::cvt(scale * Y[i]);
-                }
-            } else {
-                const __amdgpu_buffer_rsrc_t ro = make_rsrc(o + ((int64_t)tok0 * H + h) * DV,
-                                                            fin_o ? (uint32_t)(((len - 1) * H + 1) * DV * EB) : 0u);
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    if (fin_o) {
-                        f32x4 Y = sm.yp[0][rt][nt][lane];
-#pragma unroll
-                        for (int qq = 1; qq < P::KQ; ++qq) Y += sm.yp[qq][rt][nt][lane];
-                        Y *= row4(sm.qs, R::QS_BYTE_OFF, rt * 16 + 4 * g16);
-#pragma unroll
-                        for (int ks = 0; ks < R::CKS; ++ks) {
-                            if (ks < pks) {
-                                const int doff = (nt * 16 + l16) * DP + ks * KS + g16 * E;
-                                const Frag ph = frag(L::F_P + rt * R::CKS + ks, p_src(0, rt, ks));
-                                const Frag dh = *reinterpret_cast<const Frag*>(sm.dt[0] + doff);
-                                Y = M::mma(ph, dh, Y);
-                                if constexpr (SPL) {
-                                    const Frag pl = frag(L::F_P + (RT + rt) * R::CKS + ks, p_src(1, rt, ks));
-                                    const Frag dl = *reinterpret_cast<const Frag*>(sm.dt[1] + doff);
-                                    Y = M::mma(pl, dh, Y);
-                                    Y = M::mma(ph, dl, Y);
-                                }
-                            }
-                        }
-                        // rows >= len fall outside the view: dropped
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            OStore<TIn>::st(ro, (uint32_t)(rt * 16 + 4 * g16 + i) * rowstride_o +
-                                                    (uint32_t)(row0 + nt * 16 + l16) * EB, scale * Y[i]);
-                    }
-                }
+            for (int ks = 0; ks < R::CKS; ++ks) {
+                const int doff = l16 * DP + ks * KS + g16 * E;
+                const Frag fk = frag(L::F_K + mt * R::CKS + ks, k_src(mt, ks));
+                acc = M::mma(fk, *reinterpret_cast<const Frag*>(sm.ds[0] + doff), acc);
+                if constexpr (SPL) acc = M::mma(fk, *reinterpret_cast<const Frag*>(sm.ds[1] + doff), acc);
             }
-            // ---- phase 3b: state update on this wave's d_k tiles
-#pragma unroll
-            for (int a = 0; a < P::MTW; ++a) {
-                const int mt = wave + NW * a;
-                if (mt >= R::MT) continue;
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    f32x4 acc = S[a][nt] * meta.x;
-#pragma unroll
-                    for (int ks = 0; ks < R::CKS; ++ks) {
-                        const int doff = (nt * 16 + l16) * DP + ks * KS + g16 * E;
-                        const Frag fk = frag(L::F_K + mt * R::CKS + ks, k_src(mt, ks));
-                        acc = M::mma(fk, *reinterpret_cast<const Frag*>(sm.ds[0] + doff), acc);
-                        if constexpr (SPL) acc = M::mma(fk, *reinterpret_cast<const Frag*>(sm.ds[1] + doff), acc);
-                    }
-                    S[a][nt] = acc;
-                    const int off = (nt * 16 + l16) * SP + quad_pos<TIn>(mt, g16);
-                    store_quad<TIn, false>(sm.sr + off, sm.sr + off, acc);
-                }
-            }
+            S[a] = acc;
+            store_quad<TIn, false>(sm.sr + l16 * SP + quad_pos<TIn>(mt, g16), nullptr, acc);
         }
-        lds_barrier();  // ---- C: state copy and output tile visible; K, P regions free
+        lds_barrier();  // ---- C: state copy visible; K region free
     }
 
     if (final_state) {
 #pragma unroll
         for (int a = 0; a < P::MTW; ++a) {
             const int mt = wave + NW * a;
-            if (mt >= R::MT) continue;
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-                *reinterpret_cast<f32x4*>(final_state + st_base + (size_t)(row0 + nt * 16 + l16) * DK + mt * 16 +
-                                          4 * g16) = S[a][nt];
+            if (mt < R::MT)
+                *reinterpret_cast<f32x4*>(final_state + st_base + (size_t)(row0 + l16) * DK + mt * 16 + 4 * g16) = S[a];
         }
+    }
+}
+
+// Output kernel: one workgroup of 4 waves per (chunk, head), all chunks in
+// parallel.  O = scale (qscale o (Q S_c^T) + P Delta_c) for the chunk's rows,
+// with S_c the state entering the chunk and Delta_c its corrected values, both
+// from the state chain; wave w computes value tiles w, w + 4, ... in groups of
+// up to VG tiles.  The output rows are staged in LDS and written 16 bytes per
+// lane; rows >= len fall outside the buffer view.
+template <typename TIn, int C, int DK, int DV>
+struct OutCfg {
+    static constexpr int VT = DV / 16;
+    static constexpr int VTW = (VT + 3) / 4;               // value tiles per wave
+    static constexpr int VG = VTW < 4 ? VTW : 4;           // tiles per accumulation group
+    static constexpr int OP = DV + 16 / (int)sizeof(TIn);  // LDS output row pitch (elements)
+};
+
+template <typename TIn, int C, int DK, int DV>
+__global__ __launch_bounds__(256) void output_kernel(const int32_t* __restrict__ header,
+                                                     const ChunkInfo* __restrict__ tab, int32_t varlen, int64_t T,
+                                                     int32_t H, const unsigned char* __restrict__ records,
+                                                     size_t record_bytes, const TIn* __restrict__ states,
+                                                     const TIn* __restrict__ deltas, TIn* __restrict__ o, float scale)
+{
+    using M = Mma<TIn>;
+    using R = Rec<TIn, C, DK, DV>;
+    using CO = ChainOut<TIn, C, DK, DV>;
+    using G = OutCfg<TIn, C, DK, DV>;
+    typedef typename M::Frag Frag;
+    constexpr int KS = M::KS, E = M::E, RT = R::RT, NS = CO::NS;
+    constexpr uint32_t FB = 64 * 16, EB = sizeof(TIn);
+    static_assert(G::VTW % G::VG == 0, "value tile groups");
+
+    extern __shared__ __align__(16) unsigned char out_lds[];
+    TIn* ot = reinterpret_cast<TIn*>(out_lds);  // [C][OP]
+
+    const int64_t c = blockIdx.x;
+    const int h = blockIdx.y;
+    if (varlen && c >= header[1]) return;
+    if (!varlen && c * C >= T) return;
+    const ChunkInfo ci = chunk_info(tab, varlen, c, C, T);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g16 = lane >> 4, l16 = lane & 15;
+    const uint32_t lane_b = (uint32_t)lane * 16;
+
+    const unsigned char* recb = records + ((size_t)c * H + h) * record_bytes;
+    const __amdgpu_buffer_rsrc_t rr = make_rsrc(recb, (uint32_t)R::BYTES);
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(states + ((size_t)c * H + h) * CO::STATE_ELEMS, (uint32_t)(CO::STATE_ELEMS * EB));
+    const __amdgpu_buffer_rsrc_t rd =
+        make_rsrc(deltas + ((size_t)c * H + h) * CO::DELTA_ELEMS, (uint32_t)(CO::DELTA_ELEMS * EB));
+
+    f32x4 qs[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+        qs[rt] = __builtin_bit_cast(f32x4, buf_load16(rr, (uint32_t)(rt * 16 + 4 * g16) * 4, (uint32_t)R::QS_BYTE_OFF));
+
+#pragma unroll 1
+    for (int grp = 0; grp < G::VTW / G::VG; ++grp) {
+        f32x4 acc[RT][G::VG];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int v = 0; v < G::VG; ++v) acc[rt][v] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // Q S^T over d_k
+#pragma unroll 2
+        for (int ks = 0; ks < R::DKS; ++ks) {
+            Frag fq[RT], fs[G::VG];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+                fq[rt] = __builtin_bit_cast(Frag, buf_load16(rr, lane_b, R::Q_OFF * EB + (uint32_t)(rt * R::DKS + ks) * FB));
+#pragma unroll
+            for (int v = 0; v < G::VG; ++v) {
+                const int vt = min(wave + 4 * (grp * G::VG + v), G::VT - 1);  // waves past the last tile recompute it
+                fs[v] = __builtin_bit_cast(
+                    Frag, buf_load16(rs, (uint32_t)((vt * 16 + l16) * DK + ks * KS + g16 * E) * EB, 0));
+            }
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int v = 0; v < G::VG; ++v) acc[rt][v] = M::mma(fq[rt], fs[v], acc[rt][v]);
+        }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int v = 0; v < G::VG; ++v) acc[rt][v] *= qs[rt];
+        // + P Delta over the chunk (P is lower triangular: k-steps up to the diagonal)
+#pragma unroll
+        for (int ks = 0; ks < R::CKS; ++ks) {
+            Frag dh[G::VG], dl[G::VG];
+#pragma unroll
+            for (int v = 0; v < G::VG; ++v) {
+                const int vt = min(wave + 4 * (grp * G::VG + v), G::VT - 1);
+                const uint32_t off = (uint32_t)((vt * 16 + l16) * C + ks * KS + g16 * E) * EB;
+                dh[v] = __builtin_bit_cast(Frag, buf_load16(rd, off, 0));
+                if constexpr (NS > 1) dl[v] = __builtin_bit_cast(Frag, buf_load16(rd, off, (uint32_t)(DV * C) * EB));
+            }
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                if (ks * KS > rt * 16 + 15) continue;
+                const uint32_t po = (uint32_t)(rt * R::CKS + ks) * FB;
+                const Frag ph = __builtin_bit_cast(Frag, buf_load16(rr, lane_b, R::PH_OFF * EB + po));
+                Frag pl;
+                if constexpr (NS > 1) pl = __builtin_bit_cast(Frag, buf_load16(rr, lane_b, R::PL_OFF * EB + po));
+#pragma unroll
+                for (int v = 0; v < G::VG; ++v) {
+                    acc[rt][v] = M::mma(ph, dh[v], acc[rt][v]);
+                    if constexpr (NS > 1) {
+                        acc[rt][v] = M::mma(pl, dh[v], acc[rt][v]);
+                        acc[rt][v] = M::mma(ph, dl[v], acc[rt][v]);
+                    }
+                }
+            }
+        }
+        // result layout: lane holds rows rt*16 + 4*g16 + i of column vt*16 + l16
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int v = 0; v < G::VG; ++v) {
+                const int vt = wave + 4 * (grp * G::VG + v);
+                if (vt >= G::VT) continue;  // (only when fewer than 4 value tiles)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    ot[(rt * 16 + 4 * g16 + i) * G::OP + vt * 16 + l16] = M::cvt(scale * acc[rt][v][i]);
+            }
+    }
+    __syncthreads();
+    // rows of the output tile -> o, 16 bytes per lane
+    constexpr int UROW = DV * (int)EB / 16;
+    const __amdgpu_buffer_rsrc_t ro =
+        make_rsrc(o + ((int64_t)ci.tok0 * H + h) * DV, (uint32_t)(((ci.len - 1) * H + 1) * DV * EB));
+    for (int u = tid; u < C * UROW; u += 256) {
+        const int row = u / UROW, q = u % UROW;
+        const u32x4 val = *reinterpret_cast<const u32x4*>(ot + row * G::OP + q * (16 / EB));
+        __builtin_amdgcn_raw_buffer_store_b128(val, ro, (int)((uint32_t)row * H * DV * EB + q * 16), 0, 0);
     }
 }
 
@@ -1243,25 +1301,42 @@ static hipError_t run_prefill(const PrefillArgs& a)
         }
     }
     if (!(a.stages & 2)) return hipSuccess;
-    constexpr int NT = 1;
     const int64_t pairs = (int64_t)a.N * a.H;
     const int64_t groups = (pairs + 7) / 8;
-    const int64_t blocks = groups * 8 * (DV / (16 * NT));
+    const int64_t blocks = groups * 8 * (DV / 16);
     if (pairs > 0x7fffffff || blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    TIn* states = reinterpret_cast<TIn*>(a.ws + a.lay.off_states);
+    TIn* deltas = reinterpret_cast<TIn*>(a.ws + a.lay.off_deltas);
     {
         constexpr int NW = 8;
-        using Lds = ChainLds<TIn, C, DK, DV, NT, NW, chain_staged<TIn, C>(), Rec<TIn, C, DK, DV>::SPLIT>;
+        using Lds = ChainLds<TIn, C, DK, DV, NW, chain_staged<TIn, C>()>;
         static_assert(sizeof(Lds) <= 160 * 1024, "chain kernel LDS");
         static bool attr = false;  // idempotent attribute; racing writers store the same value
         if (!attr) {
-            hipError_t ea = hipFuncSetAttribute((const void*)chain_kernel<TIn, C, DK, DV, NT, NW>,
+            hipError_t ea = hipFuncSetAttribute((const void*)chain_kernel<TIn, C, DK, DV, NW>,
                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(Lds));
             if (ea != hipSuccess) return ea;
             attr = true;
         }
-        hipLaunchKernelGGL((chain_kernel<TIn, C, DK, DV, NT, NW>), dim3((uint32_t)blocks),
-                           dim3((NW + chain_loaders<TIn, C>()) * 64), sizeof(Lds), a.stream, header, tab, first, varlen,
-                           a.T, a.H, (int32_t)pairs, records, a.lay.record_bytes, a.init_state, a.final_state,
+        hipLaunchKernelGGL((chain_kernel<TIn, C, DK, DV, NW>), dim3((uint32_t)blocks),
+                           dim3((NW + chain_loaders<TIn, C>()) * 64), sizeof(Lds), a.stream, header, first, varlen,
+                           a.T, a.H, (int32_t)pairs, records, a.lay.record_bytes, a.init_state, a.final_state, states,
+                           deltas);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const int64_t grid_chunks = varlen ? a.lay.max_chunks : (a.T + C - 1) / C;
+    if (grid_chunks > 0) {
+        const size_t smem = (size_t)C * OutCfg<TIn, C, DK, DV>::OP * sizeof(TIn);
+        static bool attr = false;  // idempotent attribute; racing writers store the same value
+        if (!attr) {
+            hipError_t ea = hipFuncSetAttribute((const void*)output_kernel<TIn, C, DK, DV>,
+                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+            if (ea != hipSuccess) return ea;
+            attr = true;
+        }
+        hipLaunchKernelGGL((output_kernel<TIn, C, DK, DV>), dim3((uint32_t)grid_chunks, a.H), dim3(256), smem,
+                           a.stream, header, tab, varlen, a.T, a.H, records, a.lay.record_bytes, states, deltas,
                            (TIn*)a.o, a.scale);
     }
     return hipGetLastError();
