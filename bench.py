@@ -3,19 +3,22 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
-One step = one chunked prefill (both stages: per-chunk preparation and the
-sequential propagation with outputs) of the long-context workload: B=1, H=6,
+One step = one chunked prefill of the long-context workload: B=1, H=6,
 d_k = d_v = 256, T = 65,536 tokens, bf16 q/k/v, fp32 gates and state, chunk
-64, inputs resident in HBM.  ``value`` is prefill tokens/s.  The decode
-workload (256 sequences x 6 heads, d = 256, 128 consecutive single-token
-steps, fp32 state updated in place) is timed in the same run and reported
-under "decode" (state GB/s).
+64, inputs resident in HBM.  It runs as its three stages (per-chunk
+preparation, the sequential state chain, the per-chunk outputs), each timed
+with HIP events on the stream it runs on.  ``value`` is prefill tokens/s.
+The decode workload (256 sequences x 6 heads, d = 256, 128 consecutive
+single-token steps, fp32 state updated in place) is timed in the same run and
+reported under "decode" (state GB/s).
 
-Roofline: the dominant kernel of the step is the propagation (chain) kernel;
-its achieved rate is its algorithmic flops per launch (SURVEY-style count,
-not the dense tiles it issues) over its average duration, timed with HIP
-events on the stream it runs on.  Algorithmic work per token and head, with
-C = 64:  chain 6 d_k d_v + C d_v;  preparation C (3 d_k + d_v) + C^2 / 3.
+Roofline: the dominant kernel of the step is the state chain.  Its achieved
+rate is its algorithmic flops per launch over its average launch duration:
+4 d_k d_v flops per token and head (Delta = U - W S^T and the rank-C state
+update, 2 d_k d_v each), the dense contraction it performs; peak is dense
+bf16 MFMA.  Whole-path figures use F_tok = H [6 d_k d_v + C (3 d_k + 2 d_v)
++ C^2 / 3] flops per token and the minimum HBM traffic (q, k, v, o in bf16,
+g and beta in fp32).
 
 cpu_baseline: the fp64 oracle (plain sequential recurrence, one thread per
 (sequence, head) chain) run on the host on the same 64K-token inputs.
@@ -48,11 +51,18 @@ def log(*a):
 
 
 def flops_chain_per_token():
-    return H * (6 * DK * DV + C * DV)
+    """State chain: Delta = U - W S^T and S <- decay S + K^T Delta, per token (all heads)."""
+    return H * 4 * DK * DV
 
 
-def flops_prepare_per_token():
-    return H * (C * (3 * DK + DV) + C * C / 3.0)
+def flops_path_per_token():
+    """Whole prefill path per token (all heads), the algorithmic count."""
+    return H * (6 * DK * DV + C * (3 * DK + 2 * DV) + C * C / 3.0)
+
+
+def prefill_min_bytes():
+    """q, k, v, o in bf16, g and beta in fp32, initial and final fp32 state."""
+    return T * H * (2 * DK + 2 * DV) * 2 + T * H * 8 + 2 * H * DK * DV * 4
 
 
 def decode_bytes_per_step(N=DEC_N):
@@ -103,22 +113,21 @@ def bench_prefill(torch, gdn, synth, steps, warmup):
     ws = torch.empty(gdn.prefill_workspace_size(T, 1, H, DK, DV, C), dtype=torch.uint8, device=dev)
     log(f"[bench] workspace {ws.numel() / 2**20:.0f} MiB")
 
+    stages = (gdn.STAGE_PREPARE, gdn.STAGE_PROPAGATE, gdn.STAGE_OUTPUT)
+
     def step(evs=None):
+        for i, st in enumerate(stages):
+            if evs is not None:
+                evs[i].record()
+            gdn.chunk_prefill(q, k, v, g, beta, chunk=C, out=o, final_state=fs, workspace=ws, stages=st)
         if evs is not None:
-            evs[0].record()
-        gdn.chunk_prefill(q, k, v, g, beta, chunk=C, out=o, final_state=fs, workspace=ws, stages=gdn.STAGE_PREPARE)
-        if evs is not None:
-            evs[1].record()
-        gdn.chunk_prefill(q, k, v, g, beta, chunk=C, out=o, final_state=fs, workspace=ws,
-                          stages=gdn.STAGE_PROPAGATE)
-        if evs is not None:
-            evs[2].record()
+            evs[len(stages)].record()
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     log(f"[bench] prefill warmup done ({warmup} steps)")
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(steps)]
     t_all0 = torch.cuda.Event(enable_timing=True)
     t_all1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -130,12 +139,11 @@ def bench_prefill(torch, gdn, synth, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     total_ms = t_all0.elapsed_time(t_all1)
-    prep = [e[0].elapsed_time(e[1]) for e in evs]
-    prop = [e[1].elapsed_time(e[2]) for e in evs]
-    log(f"[bench] prefill {steps} steps: {total_ms / steps:.3f} ms/step (prepare {sum(prep) / steps:.3f}, "
-        f"propagate {sum(prop) / steps:.3f}); wall {wall / steps * 1e3:.3f} ms/step")
-    return dict(ms_per_step=total_ms / steps, wall_ms_per_step=wall * 1e3 / steps,
-                prepare_ms=sum(prep) / steps, propagate_ms=sum(prop) / steps, inputs=inp)
+    stage_ms = [sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps for j in range(len(stages))]
+    log(f"[bench] prefill {steps} steps: {total_ms / steps:.3f} ms/step (prepare {stage_ms[0]:.3f}, "
+        f"chain {stage_ms[1]:.3f}, output {stage_ms[2]:.3f}); wall {wall / steps * 1e3:.3f} ms/step")
+    return dict(ms_per_step=total_ms / steps, wall_ms_per_step=wall * 1e3 / steps, prepare_ms=stage_ms[0],
+                chain_ms=stage_ms[1], output_ms=stage_ms[2], inputs=inp)
 
 
 def bench_decode(torch, gdn, synth, n_steps, warmup=3):
@@ -211,9 +219,10 @@ def main():
     dec = None if a.no_decode else bench_decode(torch, gdn, synth, a.decode_steps)
 
     tok_s = T / (pre["ms_per_step"] / 1e3)
-    chain_tflops = flops_chain_per_token() * T / (pre["propagate_ms"] / 1e3) / 1e12
-    whole_tflops = (flops_chain_per_token() + flops_prepare_per_token()) * T / (pre["ms_per_step"] / 1e3) / 1e12
-    min_bytes = T * H * (2 * DK + 2 * DV) * 2 + T * H * 8  # q, k, v, o bf16 + g, beta fp32
+    chain_flops = flops_chain_per_token() * T
+    chain_tflops = chain_flops / (pre["chain_ms"] / 1e3) / 1e12
+    path_tflops = flops_path_per_token() * T / (pre["ms_per_step"] / 1e3) / 1e12
+    path_gbps = prefill_min_bytes() / (pre["ms_per_step"] / 1e3) / 1e9
     out = {
         "metric": METRIC,
         "value": tok_s,
@@ -231,25 +240,29 @@ def main():
                    "global_batch": 1, "seq_len": T, "heads": H, "d_k": DK, "d_v": DV, "chunk": C,
                    "parallelism": "single-gpu"},
         "roofline": {
-            "kernel": "chain_kernel (sequential state propagation + outputs)",
+            "kernel": "chain_kernel (sequential state chain)",
             "bound": "mfma",
             "achieved": chain_tflops,
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": chain_tflops / PEAK_BF16_TFLOPS,
             "traffic": traffic_from_profiles("chain_kernel"),
-            "avg_launch_ms": pre["propagate_ms"],
-            "algorithmic_flops_per_launch": flops_chain_per_token() * T,
+            "avg_launch_ms": pre["chain_ms"],
+            "algorithmic_flops_per_launch": chain_flops,
         },
         "prefill": {
             "tokens_per_s": tok_s,
             "prepare_ms": pre["prepare_ms"],
-            "propagate_ms": pre["propagate_ms"],
+            "chain_ms": pre["chain_ms"],
+            "output_ms": pre["output_ms"],
             "wall_ms_per_step": pre["wall_ms_per_step"],
-            "whole_path_tflops": whole_tflops,
-            "whole_path_mfma_frac": whole_tflops / PEAK_BF16_TFLOPS,
-            "min_traffic_GBps": min_bytes / (pre["ms_per_step"] / 1e3) / 1e9,
-            "algorithmic_flops_per_token": flops_chain_per_token() + flops_prepare_per_token(),
+            "path_tflops": path_tflops,
+            "path_mfma_frac": path_tflops / PEAK_BF16_TFLOPS,
+            "path_min_traffic_GBps": path_gbps,
+            "path_hbm_frac": path_gbps / PEAK_HBM_GBPS,
+            "algorithmic_flops_per_token": flops_path_per_token(),
+            "traffic": {"intra_kernel": traffic_from_profiles("intra_kernel"),
+                        "output_kernel": traffic_from_profiles("output_kernel")},
         },
     }
     if dec is not None:

@@ -57,7 +57,7 @@ struct PrefillArgs {
     float* final_state;
     unsigned char* ws;
     PrefillLayout lay;
-    int32_t stages;  // bit 0: prepare (chunk table + intra-chunk), bit 1: propagate (state chain + outputs)
+    int32_t stages;  // bit 0: prepare (chunk table + intra-chunk), bit 1: propagate (state chain), bit 2: outputs
     hipStream_t stream;
 };
 

@@ -1300,14 +1300,13 @@ static hipError_t run_prefill(const PrefillArgs& a)
             if (e != hipSuccess) return e;
         }
     }
-    if (!(a.stages & 2)) return hipSuccess;
     const int64_t pairs = (int64_t)a.N * a.H;
     const int64_t groups = (pairs + 7) / 8;
     const int64_t blocks = groups * 8 * (DV / 16);
     if (pairs > 0x7fffffff || blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     TIn* states = reinterpret_cast<TIn*>(a.ws + a.lay.off_states);
     TIn* deltas = reinterpret_cast<TIn*>(a.ws + a.lay.off_deltas);
-    {
+    if (a.stages & 2) {
         constexpr int NW = 8;
         using Lds = ChainLds<TIn, C, DK, DV, NW, chain_staged<TIn, C>()>;
         static_assert(sizeof(Lds) <= 160 * 1024, "chain kernel LDS");
@@ -1325,6 +1324,7 @@ static hipError_t run_prefill(const PrefillArgs& a)
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
+    if (!(a.stages & 4)) return hipSuccess;
     const int64_t grid_chunks = varlen ? a.lay.max_chunks : (a.T + C - 1) / C;
     if (grid_chunks > 0) {
         const size_t smem = (size_t)C * OutCfg<TIn, C, DK, DV>::OP * sizeof(TIn);

@@ -20,7 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdn_mi355x.so")
 
 GDN_F32, GDN_BF16 = 0, 1
-STAGE_PREPARE, STAGE_PROPAGATE, STAGE_ALL = 1, 2, 3
+STAGE_PREPARE, STAGE_PROPAGATE, STAGE_OUTPUT, STAGE_ALL = 1, 2, 4, 7
 STATUS = {
     0: "GDN_OK", 1: "GDN_ERR_NULL_ARG", 2: "GDN_ERR_BAD_SHAPE", 3: "GDN_ERR_UNSUPPORTED",
     4: "GDN_ERR_BAD_SEQLENS", 5: "GDN_ERR_ALIGNMENT", 6: "GDN_ERR_WORKSPACE", 7: "GDN_ERR_LAUNCH",
@@ -119,8 +119,9 @@ def chunk_prefill(q, k, v, g, beta, init_state=None, cu_seqlens=None, scale=None
     q, k [T, H, dk]; v [T, H, dv] (bf16 or fp32, same dtype); g, beta [T, H] fp32;
     init_state [N, H, dv, dk] fp32 or None; cu_seqlens int [N+1] (list, CPU or GPU
     tensor) or None for one sequence.  Returns (o [T, H, dv], final_state [N, H, dv, dk]).
-    ``stages`` selects STAGE_PREPARE / STAGE_PROPAGATE / STAGE_ALL (see include/gdn.h);
-    a PROPAGATE-only call must get the workspace of a PREPARE on the same inputs.
+    ``stages`` is a bit set of STAGE_PREPARE / STAGE_PROPAGATE / STAGE_OUTPUT (STAGE_ALL:
+    all three; see include/gdn.h); a later stage must get the workspace of the earlier
+    ones on the same inputs.
     """
     torch = _torch()
     lib = load_library()

@@ -111,24 +111,30 @@ gdn_status gdn_chunk_prefill(const void* q, const void* k, const void* v, const 
                              size_t workspace_bytes, hipStream_t stream);
 
 /*
- * The two stages of gdn_chunk_prefill, for callers that schedule or time them
- * separately.  Same arguments and rules as gdn_chunk_prefill, plus `stages`:
+ * The stages of gdn_chunk_prefill, for callers that schedule or time them
+ * separately.  Same arguments and rules as gdn_chunk_prefill, plus `stages`,
+ * a bit set of:
  *   GDN_STAGE_PREPARE    per-chunk work, fully parallel over (chunk, head):
  *                        chunk table, q/k norms, cumulative log-decay, the
- *                        triangular solve and the WY factors, written into the
- *                        workspace (reads q, k, v, g, beta; writes only the
- *                        workspace);
- *   GDN_STAGE_PROPAGATE  the sequential pass over each sequence's chunks:
- *                        state carry and outputs (reads the workspace left by
- *                        a PREPARE on the same inputs and sizes, plus q and
- *                        init_state; writes o and final_state);
- *   GDN_STAGE_ALL        both, in order (what gdn_chunk_prefill does).
+ *                        triangular solve, the WY factors W and U and the
+ *                        intra-chunk scores P, written into the workspace
+ *                        (reads q, k, v, g, beta; writes only the workspace);
+ *   GDN_STAGE_PROPAGATE  the sequential pass over each sequence's chunks (the
+ *                        state carry): reads the workspace left by PREPARE and
+ *                        init_state; writes final_state and, into the
+ *                        workspace, the state entering every chunk and the
+ *                        chunk's corrected values;
+ *   GDN_STAGE_OUTPUT     the outputs of every chunk, fully parallel over
+ *                        (chunk, head), from the workspace left by PREPARE and
+ *                        PROPAGATE; writes o;
+ *   GDN_STAGE_ALL        all three, in order (what gdn_chunk_prefill does).
  * Stages of one prefill must be enqueued in order on one stream (or ordered
- * by the caller) with the same workspace.
+ * by the caller) with the same workspace and the same inputs and sizes.
  */
 #define GDN_STAGE_PREPARE 1
 #define GDN_STAGE_PROPAGATE 2
-#define GDN_STAGE_ALL 3
+#define GDN_STAGE_OUTPUT 4
+#define GDN_STAGE_ALL 7
 gdn_status gdn_chunk_prefill_staged(const void* q, const void* k, const void* v, const float* g,
                                     const float* beta, const float* init_state, const int32_t* cu_seqlens,
                                     const int32_t* cu_seqlens_host, int32_t num_seqs, int64_t total_tokens,

@@ -1,0 +1,216 @@
+#!/usr/bin/env python
+"""Profiles behind the bench figures, collected with rocprofv3 on one MI355X.
+
+    python profile_bench.py trace     # kernel trace + stats of a short bench run   (GPU)
+    python profile_bench.py traffic   # HBM bytes per launch from FETCH_SIZE / WRITE_SIZE (GPU)
+    python profile_bench.py render    # summaries under profiles/ from the raw output (no GPU)
+    python profile_bench.py copy      # (the calibration program the traffic mode profiles)
+
+The GPU modes keep rocprofv3's raw output and their results under
+gpurun_out/profile_bench/; `render` turns those into the short summaries that
+are kept under profiles/.
+
+`trace` runs ``rocprofv3 --kernel-trace --stats`` over ``bench.py`` and writes
+profiles/prefill64k_decode_kernel_trace.md: the command, the per-kernel
+launch statistics and the bench JSON line of the same run.
+
+`traffic` runs one ``rocprofv3 --pmc`` pass per counter (FETCH_SIZE, then
+WRITE_SIZE; KiB per dispatch) over a short bench run and over a plain device
+copy of a known number of bytes.  The copy's reading calibrates each counter
+(factor = bytes moved / bytes counted); the kernels' readings are scaled by
+it.  Results go to profiles/traffic.json, keyed by a digest of the kernel
+sources (bench.py reports a traffic figure only while the sources are
+unchanged), with a readable summary in profiles/traffic_prefill64k_decode.md.
+
+This script starts rocprofv3 as a child process and touches the GPU only
+through it (and through `copy`, which the profiler runs).
+"""
+from __future__ import annotations
+
+import csv
+import glob
+import json
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+OUT = os.path.join(ROOT, "gpurun_out", "profile_bench")
+PROFILES = os.path.join(ROOT, "profiles")
+KERNELS = ("chain_kernel", "intra_kernel", "output_kernel", "decode_kernel", "chunk_table_kernel")
+COPY_BYTES = 1 << 30
+BENCH_TRACE = ["bench.py", "--steps", "5", "--warmup", "2", "--decode-steps", "32", "--no-cpu-baseline"]
+BENCH_PMC = ["bench.py", "--steps", "1", "--warmup", "1", "--decode-steps", "4", "--no-cpu-baseline"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def run_profiler(args, tag, timeout):
+    d = os.path.join(OUT, tag)
+    os.makedirs(d, exist_ok=True)
+    cmd = ["rocprofv3", *args, "-d", d, "-o", "run", "--output-format", "csv", "--", sys.executable]
+    log(f"[profile] {tag}: {' '.join(cmd[:-1])} python3 ...")
+    env = dict(os.environ, TMPDIR="/tmp")
+    return cmd, d, env, timeout
+
+
+def launch(cmd_tail, prof_args, tag, timeout):
+    cmd, d, env, timeout = run_profiler(prof_args, tag, timeout)
+    full = cmd + cmd_tail
+    with open(os.path.join(d, "stdout.txt"), "w") as so, open(os.path.join(d, "stderr.txt"), "w") as se:
+        r = subprocess.run(["timeout", "-s", "KILL", str(timeout)] + full, cwd=ROOT, env=env, stdout=so, stderr=se)
+    log(f"[profile] {tag}: exit {r.returncode}")
+    return r.returncode, d, " ".join(["rocprofv3", *prof_args, "-d", os.path.relpath(d, ROOT), "-o", "run",
+                                      "--output-format", "csv", "--", "python3", *cmd_tail])
+
+
+def kernel_key(name):
+    for k in KERNELS:
+        if k in name:
+            return k
+    return None
+
+
+def find(d, suffix):
+    hits = glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True)
+    return hits[0] if hits else None
+
+
+def mode_trace():
+    rc, d, cmd = launch(BENCH_TRACE, ["--kernel-trace", "--stats"], "trace", 900)
+    with open(os.path.join(d, "command.txt"), "w") as f:
+        f.write(cmd + "\n")
+    if rc != 0 or find(d, "kernel_stats.csv") is None:
+        raise SystemExit(f"trace run failed (exit {rc})")
+
+
+def render_trace():
+    d = os.path.join(OUT, "trace")
+    stats = find(d, "kernel_stats.csv")
+    if stats is None:
+        log("[profile] no trace output to render")
+        return
+    cmd = open(os.path.join(d, "command.txt")).read().strip()
+    bench_line = ""
+    with open(os.path.join(d, "stdout.txt")) as f:
+        for line in f:
+            if line.startswith("{"):
+                bench_line = line.strip()
+    rows = []
+    with open(stats) as f:
+        for r in csv.DictReader(f):
+            rows.append((r["Name"], int(r["Calls"]), float(r["AverageNs"]), float(r["MinNs"]), float(r["MaxNs"]),
+                         float(r["Percentage"])))
+    lines = ["# Kernel trace: 64K-token prefill (H=6, d=256, bf16) and batched decode", "",
+             "Command (repository root, one MI355X):", "", "```", cmd, "```", "",
+             "| kernel | calls | avg us | min us | max us | % of GPU time |", "|---|---|---|---|---|---|"]
+    for name, calls, avg, mn, mx, pct in rows:
+        short = name.split("(")[0].replace("void ", "")
+        lines.append(f"| `{short}` | {calls} | {avg / 1e3:.1f} | {mn / 1e3:.1f} | {mx / 1e3:.1f} | {pct:.1f} |")
+    lines += ["", "Bench JSON line of the same run:", "", "```", bench_line, "```", ""]
+    path = os.path.join(PROFILES, "prefill64k_decode_kernel_trace.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines))
+    log(f"[profile] wrote {path}")
+
+
+def counter_sums(d):
+    """{kernel key: (sum over dispatches of the counter in KiB, dispatches)}, {copy: ...}."""
+    f = find(d, "counter_collection.csv")
+    if f is None:
+        return {}
+    acc = {}
+    with open(f) as fh:
+        for r in csv.DictReader(fh):
+            name = r["Kernel_Name"]
+            key = kernel_key(name) or ("copy" if "copy" in name.lower() else None)
+            if key is None:
+                continue
+            v, n = acc.get(key, (0.0, set()))
+            n.add(r["Dispatch_Id"])
+            acc[key] = (v + float(r["Counter_Value"]), n)
+    return {k: (v, len(n)) for k, (v, n) in acc.items()}
+
+
+def mode_traffic():
+    sys.path.insert(0, ROOT)
+    import bench
+
+    result = {"sources_digest": bench.kernel_sources_digest(), "counters": {}, "calibration": {}, "kernels": {}}
+    cmds = []
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        rc, d, cmd = launch(["profile_bench.py", "copy"], ["--pmc", counter], f"copy_{counter}", 240)
+        cmds.append(cmd)
+        cs = counter_sums(d).get("copy")
+        if rc != 0 or cs is None:
+            raise SystemExit(f"copy calibration for {counter} failed (exit {rc})")
+        kib, n = cs
+        factor = COPY_BYTES / (kib * 1024.0 / n)
+        result["calibration"][counter] = {"copy_bytes": COPY_BYTES, "counted_KiB_per_dispatch": kib / n,
+                                          "factor": factor}
+        rc, d, cmd = launch(BENCH_PMC, ["--pmc", counter, "--kernel-include-regex",
+                                        "chain_kernel|intra_kernel|output_kernel|decode_kernel"],
+                            f"bench_{counter}", 600)
+        cmds.append(cmd)
+        if rc != 0:
+            raise SystemExit(f"bench pass for {counter} failed (exit {rc})")
+        for key, (kib, n) in counter_sums(d).items():
+            if key == "copy":
+                continue
+            result["counters"].setdefault(key, {})[counter] = {"KiB_per_dispatch": kib / n, "dispatches": n}
+    for key, ent in result["counters"].items():
+        fetch = ent["FETCH_SIZE"]["KiB_per_dispatch"] * 1024 * result["calibration"]["FETCH_SIZE"]["factor"]
+        write = ent["WRITE_SIZE"]["KiB_per_dispatch"] * 1024 * result["calibration"]["WRITE_SIZE"]["factor"]
+        result["kernels"][key] = {"fetch_bytes_per_launch": fetch, "write_bytes_per_launch": write,
+                                  "hbm_bytes_per_launch": fetch + write}
+    result["commands"] = cmds
+    with open(os.path.join(OUT, "traffic.json"), "w") as f:
+        json.dump(result, f, indent=1)
+    log("[profile] wrote gpurun_out/profile_bench/traffic.json")
+
+
+def render_traffic():
+    p = os.path.join(OUT, "traffic.json")
+    if not os.path.exists(p):
+        log("[profile] no traffic output to render")
+        return
+    with open(p) as f:
+        result = json.load(f)
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(os.path.join(PROFILES, "traffic.json"), "w") as f:
+        json.dump(result, f, indent=1)
+    lines = ["# HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE, copy-calibrated)", "",
+             "Commands (repository root, one MI355X), one counter per pass:", "", "```", *result["commands"], "```", "",
+             "Calibration (a device copy of 1 GiB): "
+             + ", ".join(f"{c} factor {v['factor']:.3f}" for c, v in result["calibration"].items()), "",
+             "| kernel | fetch MB/launch | write MB/launch | total MB/launch |", "|---|---|---|---|"]
+    for key, ent in sorted(result["kernels"].items()):
+        lines.append(f"| `{key}` | {ent['fetch_bytes_per_launch'] / 1e6:.1f} | {ent['write_bytes_per_launch'] / 1e6:.1f}"
+                     f" | {ent['hbm_bytes_per_launch'] / 1e6:.1f} |")
+    lines += ["", f"Kernel sources digest: `{result['sources_digest']}`", ""]
+    with open(os.path.join(PROFILES, "traffic_prefill64k_decode.md"), "w") as f:
+        f.write("\n".join(lines))
+    log("[profile] wrote profiles/traffic.json and profiles/traffic_prefill64k_decode.md")
+
+
+def mode_render():
+    render_trace()
+    render_traffic()
+
+
+def mode_copy():
+    import torch
+
+    a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")  # no fill: the copy is the only kernel
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    print("copied", COPY_BYTES, "bytes", flush=True)
+
+
+if __name__ == "__main__":
+    mode = sys.argv[1] if len(sys.argv) > 1 else "trace"
+    {"trace": mode_trace, "traffic": mode_traffic, "render": mode_render, "copy": mode_copy}[mode]()
