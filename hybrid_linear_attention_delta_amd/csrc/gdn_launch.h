@@ -29,7 +29,6 @@ struct PrefillLayout {
     size_t off_header;      // int32[16]: [0] error flag, [1] number of chunks
     size_t off_chunk_tab;   // int32[max_chunks][4]: tok0, len, seq, 0
     size_t off_seq_first;   // int32[N + 1]: first chunk of each sequence
-    size_t off_decay;       // float[max_chunks][H]: e^{gamma_L} per chunk-head
     size_t off_records;     // per chunk-head operand records
     size_t record_bytes;    // bytes of one record
     size_t off_states;      // per chunk-head state entering the chunk [dv][dk], operand type

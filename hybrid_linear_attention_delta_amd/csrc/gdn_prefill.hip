@@ -27,11 +27,19 @@
 //                       operand record per chunk-head whose fragments are laid
 //                       out exactly in the per-lane order of the MFMA operands
 //                       of the chain kernel (one 16-byte load per operand).
-//   chain_kernel        one workgroup per (sequence, head, 16*NT state rows):
+//   chain_kernel        one workgroup per (sequence, head, 16 state rows):
 //                       sequential over the sequence's chunks; state tile in
 //                       fp32 MFMA accumulators, a rounded copy in LDS as the
-//                       MFMA operand; computes Delta, the outputs, the state
-//                       update; writes o and the final state.
+//                       MFMA operand; computes Delta and the state update;
+//                       writes the state entering every chunk, every chunk's
+//                       Delta and the final state.  Eight compute waves run
+//                       only LDS and MFMA work between three barriers per
+//                       chunk; in the bf16 form, seven loader waves stage the
+//                       operands through registers into LDS and one wave
+//                       prefetches chunks ahead into L2.
+//   output_kernel       one workgroup per (chunk, head), fully parallel: the
+//                       outputs O of the chunk from Q, P, the state entering
+//                       the chunk and Delta.
 //
 // MFMA conventions (v_mfma_f32_16x16x32_bf16 / v_mfma_f32_16x16x4_f32): lane
 // l supplies row (l % 16) of A and column (l % 16) of B, with its "k-slots"
@@ -371,7 +379,7 @@ __global__ __launch_bounds__(256) void intra_kernel(const TIn* __restrict__ q, c
                                                     const TIn* __restrict__ v, const float* __restrict__ g,
                                                     const float* __restrict__ beta, const int32_t* __restrict__ header,
                                                     const ChunkInfo* __restrict__ tab, int32_t varlen, int64_t T,
-                                                    int32_t H, int32_t l2norm, float* __restrict__ decay_out,
+                                                    int32_t H, int32_t l2norm,
                                                     unsigned char* __restrict__ records, size_t record_bytes)
 {
     using M = Mma<TIn>;
@@ -668,7 +676,6 @@ __global__ __launch_bounds__(256) void intra_kernel(const TIn* __restrict__ q, c
         }
     }
     if (tid == 0) {
-        decay_out[c * H + h] = expf(gL);
         *reinterpret_cast<f32x4*>(recb + R::DEC_BYTE_OFF) =
             f32x4{expf(gL), __int_as_float(ci.tok0), __int_as_float(ci.len), 0.f};
     }
@@ -1269,7 +1276,6 @@ static hipError_t run_prefill(const PrefillArgs& a)
     int32_t* header = reinterpret_cast<int32_t*>(a.ws + a.lay.off_header);
     ChunkInfo* tab = reinterpret_cast<ChunkInfo*>(a.ws + a.lay.off_chunk_tab);
     int32_t* first = reinterpret_cast<int32_t*>(a.ws + a.lay.off_seq_first);
-    float* decay = reinterpret_cast<float*>(a.ws + a.lay.off_decay);
     unsigned char* records = a.ws + a.lay.off_records;
     const int varlen = a.cu_seqlens != nullptr;
 
@@ -1295,7 +1301,7 @@ static hipError_t run_prefill(const PrefillArgs& a)
             }
             hipLaunchKernelGGL((intra_kernel<TIn, C, DK, DV>), dim3((uint32_t)grid_chunks, a.H), dim3(256), smem,
                                a.stream, (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, a.g, a.beta, header, tab,
-                               varlen, a.T, a.H, a.l2norm, decay, records, a.lay.record_bytes);
+                               varlen, a.T, a.H, a.l2norm, records, a.lay.record_bytes);
             e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
