@@ -56,6 +56,9 @@ __device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t vo
 // Element loads/stores for the two storage types of q, k, v, o.
 template <typename T> struct Elem;
 template <> struct Elem<float> {
+    typedef f32x4 Raw4;  // four stored elements, before widening
+    static __device__ __forceinline__ Raw4 raw4(const float* p, int64_t i) { return *reinterpret_cast<const f32x4*>(p + i); }
+    static __device__ __forceinline__ f32x4 widen4(Raw4 r) { return r; }
     static __device__ __forceinline__ float load(const float* p, int64_t i) { return p[i]; }
     static __device__ __forceinline__ void store(float* p, int64_t i, float x) { p[i] = x; }
     // four consecutive elements starting at p[i] (i multiple of 4)
@@ -65,6 +68,12 @@ template <> struct Elem<float> {
     }
 };
 template <> struct Elem<uint16_t> {  // bf16 stored as raw bits
+    typedef u16x4 Raw4;
+    static __device__ __forceinline__ Raw4 raw4(const uint16_t* p, int64_t i) { return *reinterpret_cast<const u16x4*>(p + i); }
+    static __device__ __forceinline__ f32x4 widen4(Raw4 b)
+    {
+        return f32x4{bf16_bits_to_f32(b.x), bf16_bits_to_f32(b.y), bf16_bits_to_f32(b.z), bf16_bits_to_f32(b.w)};
+    }
     static __device__ __forceinline__ float load(const uint16_t* p, int64_t i) { return bf16_bits_to_f32(p[i]); }
     static __device__ __forceinline__ void store(uint16_t* p, int64_t i, float x) { p[i] = f32_to_bf16_bits(x); }
     static __device__ __forceinline__ f32x4 load4(const uint16_t* p, int64_t i)

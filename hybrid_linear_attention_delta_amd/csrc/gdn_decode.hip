@@ -17,10 +17,13 @@
 // Mapping: a row of d_k fp32 values is split over RL = d_k/16 lanes, each lane
 // owning 16 columns as four 16-byte vectors strided by RL*4 columns, so every
 // load instruction of a row group touches RL*16 contiguous bytes.  A wave holds
-// 64/RL rows per pass and runs ITERS passes with all loads issued up front
-// (16 rows of 1 KiB in flight per wave at d_k = 256).  The state is streamed
-// with non-temporal loads and stores: it is touched once per step and is
-// larger than the last-level cache in the workloads this serves.
+// 64/RL rows per pass (4 rows of 1 KiB at d_k = 256, one pass); q, k and v are
+// loaded first, then all state rows, and only then are q and k widened and
+// normalised, so that work overlaps the state loads.  Small waves and many of
+// them measured faster than deeper per-wave queues (more workgroups in flight
+// per CU).  The state is streamed with non-temporal loads and stores: it is
+// touched once per step and is larger than the last-level cache in the
+// workloads this serves.
 #include "gdn_common.h"
 #include "gdn_launch.h"
 
@@ -31,7 +34,7 @@ struct DecodeShape {
     static_assert(DK % 16 == 0 && DK >= 16 && DK <= 1024, "d_k");
     static constexpr int RL = DK / 16;                         // lanes per row
     static constexpr int ROWS_PER_PASS = kWave / RL;           // rows per wave per pass
-    static constexpr int ITERS = ROWS_PER_PASS >= 16 ? 1 : 16 / ROWS_PER_PASS;
+    static constexpr int ITERS = ROWS_PER_PASS >= 4 ? 1 : 4 / ROWS_PER_PASS;
     static constexpr int ROWS_PER_WAVE = ROWS_PER_PASS * ITERS;
     static constexpr int WAVES = 4;
     static constexpr int ROWS_PER_BLOCK = ROWS_PER_WAVE * WAVES;
@@ -53,15 +56,38 @@ __global__ __launch_bounds__(256) void decode_kernel(const TIn* __restrict__ q, 
     const int j = lane % RL;          // lane within its row group
     const int rsub = lane / RL;       // row group within the wave
 
-    // Columns owned by this lane: 4 vectors, vector m covers 4*(j + RL*m) .. +3.
+    // q, k and v first (raw), then every state row of this wave, then the
+    // widening and norm math: vmcnt retires in issue order, so that math waits
+    // for q, k, v only while the state rows are in flight.
     const int64_t qk_base = nh * DK;
+    typename Elem<TIn>::Raw4 kraw[4], qraw[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int col = 4 * (j + RL * m);  // columns owned by this lane: vector m covers col .. col+3
+        kraw[m] = Elem<TIn>::raw4(k, qk_base + col);
+        qraw[m] = Elem<TIn>::raw4(q, qk_base + col);
+    }
+    const int row0 = rb * S::ROWS_PER_BLOCK + wave * S::ROWS_PER_WAVE;
+    TIn vraw[S::ITERS];
+#pragma unroll
+    for (int it = 0; it < S::ITERS; ++it)  // rows past d_v: loaded, not stored
+        vraw[it] = v[nh * dv + min(row0 + it * S::ROWS_PER_PASS + rsub, dv - 1)];
+    float* srow_base = state + nh * (int64_t)dv * DK;
+    f32x4 s[S::ITERS][4];
+#pragma unroll
+    for (int it = 0; it < S::ITERS; ++it) {
+        const int row = min(row0 + it * S::ROWS_PER_PASS + rsub, dv - 1);
+        const f32x4* p = reinterpret_cast<const f32x4*>(srow_base + (int64_t)row * DK);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) s[it][m] = __builtin_nontemporal_load(p + j + RL * m);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the widening below the state loads
     f32x4 kv[4], qv[4];
     float ss_k = 0.f, ss_q = 0.f, qk = 0.f;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-        const int col = 4 * (j + RL * m);
-        kv[m] = Elem<TIn>::load4(k, qk_base + col);
-        qv[m] = Elem<TIn>::load4(q, qk_base + col);
+        kv[m] = Elem<TIn>::widen4(kraw[m]);
+        qv[m] = Elem<TIn>::widen4(qraw[m]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             ss_k += kv[m][e] * kv[m][e];
@@ -87,23 +113,6 @@ __global__ __launch_bounds__(256) void decode_kernel(const TIn* __restrict__ q, 
     const float alpha = expf(g[nh]);
     const float b = beta[nh];
 
-    const int row0 = rb * S::ROWS_PER_BLOCK + wave * S::ROWS_PER_WAVE;
-    float* srow_base = state + nh * (int64_t)dv * DK;
-
-    f32x4 s[S::ITERS][4];
-#pragma unroll
-    for (int it = 0; it < S::ITERS; ++it) {
-        const int row = row0 + it * S::ROWS_PER_PASS + rsub;
-        if (row < dv) {
-            const f32x4* p = reinterpret_cast<const f32x4*>(srow_base + (int64_t)row * DK);
-#pragma unroll
-            for (int m = 0; m < 4; ++m) s[it][m] = __builtin_nontemporal_load(p + j + RL * m);
-        } else {
-#pragma unroll
-            for (int m = 0; m < 4; ++m) s[it][m] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-    }
-
 #pragma unroll
     for (int it = 0; it < S::ITERS; ++it) {
         const int row = row0 + it * S::ROWS_PER_PASS + rsub;
@@ -117,7 +126,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const TIn* __restrict__ q, 
             }
         a = group_sum<RL>(a);
         bq = group_sum<RL>(bq);
-        const float vi = row < dv ? Elem<TIn>::load(v, nh * dv + row) : 0.f;
+        const float vi = Elem<TIn>::load(vraw, it);
         const float c = b * (vi - alpha * a);
         if (row < dv) {
             f32x4* p = reinterpret_cast<f32x4*>(srow_base + (int64_t)row * DK);
