@@ -5,15 +5,19 @@
 
 One step = one chunked prefill of the long-context workload: B=1, H=6,
 d_k = d_v = 256, T = 65,536 tokens, bf16 q/k/v, fp32 gates and state, chunk
-64, inputs resident in HBM.  It runs as its three stages (per-chunk
-preparation, the sequential state chain, the per-chunk outputs), each timed
-with HIP events on the stream it runs on.  ``value`` is prefill tokens/s.
+64, inputs resident in HBM, as one whole-prefill call (the library pipelines
+segments of its three stages over streams).  ``value`` is prefill tokens/s
+of those steps.  The same work is then run stage by stage (per-chunk
+preparation, the sequential state chain as one launch over all chunks, the
+per-chunk outputs), each stage timed with HIP events on the stream it runs
+on, for the breakdown and the roofline.
 The decode workload (256 sequences x 6 heads, d = 256, 128 consecutive
 single-token steps, fp32 state updated in place) is timed in the same run and
 reported under "decode" (state GB/s).
 
 Roofline: the dominant kernel of the step is the state chain.  Its achieved
-rate is its algorithmic flops per launch over its average launch duration:
+rate is its algorithmic flops per launch over its average launch duration
+(the one-launch form of the stage-by-stage run):
 4 d_k d_v flops per token and head (Delta = U - W S^T and the rank-C state
 update, 2 d_k d_v each), the dense contraction it performs; peak is dense
 bf16 MFMA.  Whole-path figures use F_tok = H [6 d_k d_v + C (3 d_k + 2 d_v)
@@ -113,37 +117,46 @@ def bench_prefill(torch, gdn, synth, steps, warmup):
     ws = torch.empty(gdn.prefill_workspace_size(T, 1, H, DK, DV, C), dtype=torch.uint8, device=dev)
     log(f"[bench] workspace {ws.numel() / 2**20:.0f} MiB")
 
-    stages = (gdn.STAGE_PREPARE, gdn.STAGE_PROPAGATE, gdn.STAGE_OUTPUT)
+    def run(st):
+        gdn.chunk_prefill(q, k, v, g, beta, chunk=C, out=o, final_state=fs, workspace=ws, stages=st)
 
-    def step(evs=None):
-        for i, st in enumerate(stages):
-            if evs is not None:
-                evs[i].record()
-            gdn.chunk_prefill(q, k, v, g, beta, chunk=C, out=o, final_state=fs, workspace=ws, stages=st)
-        if evs is not None:
-            evs[len(stages)].record()
-
+    # --- the step as a caller runs it: one whole-prefill call (the library
+    #     pipelines its stages over streams internally)
     for _ in range(warmup):
-        step()
+        run(gdn.STAGE_ALL)
     torch.cuda.synchronize()
     log(f"[bench] prefill warmup done ({warmup} steps)")
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(steps)]
-    t_all0 = torch.cuda.Event(enable_timing=True)
-    t_all1 = torch.cuda.Event(enable_timing=True)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
-    t_all0.record()
-    for i in range(steps):
-        step(evs[i])
-    t_all1.record()
+    t0.record()
+    for _ in range(steps):
+        run(gdn.STAGE_ALL)
+    t1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
-    total_ms = t_all0.elapsed_time(t_all1)
+    total_ms = t0.elapsed_time(t1)
+
+    # --- the same work stage by stage, each stage timed with events on the
+    #     stream it runs on (the chain here is one launch over all chunks)
+    stages = (gdn.STAGE_PREPARE, gdn.STAGE_PROPAGATE, gdn.STAGE_OUTPUT)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(steps)]
+    for st in stages:
+        run(st)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        for j, st in enumerate(stages):
+            evs[i][j].record()
+            run(st)
+        evs[i][len(stages)].record()
+    torch.cuda.synchronize()
     stage_ms = [sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps for j in range(len(stages))]
-    log(f"[bench] prefill {steps} steps: {total_ms / steps:.3f} ms/step (prepare {stage_ms[0]:.3f}, "
-        f"chain {stage_ms[1]:.3f}, output {stage_ms[2]:.3f}); wall {wall / steps * 1e3:.3f} ms/step")
+    log(f"[bench] prefill {steps} steps: {total_ms / steps:.3f} ms/step; wall {wall / steps * 1e3:.3f} ms/step; "
+        f"stage by stage: prepare {stage_ms[0]:.3f}, chain {stage_ms[1]:.3f}, output {stage_ms[2]:.3f} "
+        f"(sum {sum(stage_ms):.3f})")
     return dict(ms_per_step=total_ms / steps, wall_ms_per_step=wall * 1e3 / steps, prepare_ms=stage_ms[0],
-                chain_ms=stage_ms[1], output_ms=stage_ms[2], inputs=inp)
+                chain_ms=stage_ms[1], output_ms=stage_ms[2], staged_ms=sum(stage_ms), inputs=inp)
 
 
 def bench_decode(torch, gdn, synth, n_steps, warmup=3):
@@ -240,7 +253,7 @@ def main():
                    "global_batch": 1, "seq_len": T, "heads": H, "d_k": DK, "d_v": DV, "chunk": C,
                    "parallelism": "single-gpu"},
         "roofline": {
-            "kernel": "chain_kernel (sequential state chain)",
+            "kernel": "chain_kernel (sequential state chain, one launch over all chunks)",
             "bound": "mfma",
             "achieved": chain_tflops,
             "peak": PEAK_BF16_TFLOPS,
@@ -255,6 +268,7 @@ def main():
             "prepare_ms": pre["prepare_ms"],
             "chain_ms": pre["chain_ms"],
             "output_ms": pre["output_ms"],
+            "stage_by_stage_ms": pre["staged_ms"],
             "wall_ms_per_step": pre["wall_ms_per_step"],
             "path_tflops": path_tflops,
             "path_mfma_frac": path_tflops / PEAK_BF16_TFLOPS,

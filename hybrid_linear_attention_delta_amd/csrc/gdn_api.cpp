@@ -83,7 +83,9 @@ PrefillLayout prefill_layout(int64_t T, int32_t N, int32_t H, int32_t dk, int32_
     L.off_states = off;
     off = align_up(off + (size_t)L.max_chunks * H * dv * dk * el, 256);
     L.off_deltas = off;
-    off += (size_t)L.max_chunks * H * split * dv * C * el;
+    off = align_up(off + (size_t)L.max_chunks * H * split * dv * C * el, 256);
+    L.off_carry = off;
+    off += (size_t)N * H * dv * dk * 4;
     L.total = off;
     return L;
 }

@@ -33,6 +33,7 @@ struct PrefillLayout {
     size_t record_bytes;    // bytes of one record
     size_t off_states;      // per chunk-head state entering the chunk [dv][dk], operand type
     size_t off_deltas;      // per chunk-head Delta^T [hi, lo][dv][C], operand type
+    size_t off_carry;       // fp32 [N][H][dv][dk]: state carried between pipeline segments
     size_t total;
 };
 

@@ -52,6 +52,9 @@
 //             as next-stage operands without a shuffle.
 #include <stdlib.h>
 
+#include <algorithm>
+#include <mutex>
+
 #include "gdn_common.h"
 #include "gdn_launch.h"
 
@@ -375,12 +378,13 @@ struct TransposeStage {
 };
 
 template <typename TIn, int C, int DK, int DV>
-__global__ __launch_bounds__(256) void intra_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
+__device__ __forceinline__ void intra_chunk(const TIn* __restrict__ q, const TIn* __restrict__ k,
                                                     const TIn* __restrict__ v, const float* __restrict__ g,
                                                     const float* __restrict__ beta, const int32_t* __restrict__ header,
                                                     const ChunkInfo* __restrict__ tab, int32_t varlen, int64_t T,
                                                     int32_t H, int32_t l2norm,
-                                                    unsigned char* __restrict__ records, size_t record_bytes)
+                                                    unsigned char* __restrict__ records, size_t record_bytes,
+                                                    int64_t c)
 {
     using M = Mma<TIn>;
     using F = Mma<float>;
@@ -395,7 +399,6 @@ __global__ __launch_bounds__(256) void intra_kernel(const TIn* __restrict__ q, c
     extern __shared__ __align__(16) unsigned char smem_raw[];
     Sm& sm = *reinterpret_cast<Sm*>(smem_raw);
 
-    const int64_t c = blockIdx.x;
     const int h = blockIdx.y;
     if (varlen && c >= header[1]) return;
     if (!varlen && c * C >= T) return;
@@ -681,6 +684,408 @@ __global__ __launch_bounds__(256) void intra_kernel(const TIn* __restrict__ q, c
     }
 }
 
+// ---- bf16 form (C = 64)
+//
+// The chunk's rows are read once, with 16-byte loads along each row: K into
+// LDS (row-major), V into registers (written to LDS once K is no longer
+// needed), and Q straight into the operand registers of the wave that owns
+// its rows.  Wave w owns chunk rows 16w..16w+15: it forms G = K K^T and
+// R = K Q^T for those columns against K row tiles 0..w (both products share
+// the K operand), the row norms from the operand fragments themselves, and
+// writes its rows of A, its P fragments, its Q fragments and its per-row
+// scales.  The K^T fragments of the state update are read down the columns
+// of the LDS rows.  T, W and U follow as in the general form.
+
+// Row-major bf16 tile in LDS, W elements per row.  The 16-byte chunks of row
+// j are stored in the order chunk ^ mask(j), which spreads 16-byte row
+// writes, 8-byte reads of one column group over 16 consecutive rows, and
+// 2-byte reads down a column at rows 8 apart, over all banks.
+template <int W>
+struct RowTile {
+    static constexpr int CPR = W / 8;  // 16-byte chunks per row
+    static __device__ __forceinline__ int chunk(int j, int ch) { return ch ^ ((j ^ (j >> 3)) & (CPR - 1)); }
+    static __device__ __forceinline__ int at(int j, int col) { return j * W + (chunk(j, col >> 3) << 3) + (col & 7); }
+};
+
+template <int DK, int DV>
+struct IntraBf {
+    static constexpr int C = 64;
+    static constexpr int VP = DV < 256 ? DV : 256;  // value columns per pass
+    static constexpr int NVP = DV / VP;
+    static constexpr int XW = DK > VP ? DK : VP;    // row width of the tile region
+    static constexpr int AP = C + 4;                // fp32 pitch of A and T
+    static constexpr int KLD = C * (DK / 8) / 256;  // 16-byte loads per thread: K
+    static constexpr int VLD = C * (VP / 8) / 256;  //                           V (one pass)
+    static constexpr int DKS = DK / 32;             // d_k blocks of one k-step
+    static constexpr int DBW = (DKS + 3) / 4;       // d_k blocks per wave
+    static constexpr int VTP = VP / 16;             // value tiles per pass
+    static constexpr int VTW = (VTP + 3) / 4;       // value tiles per wave and pass
+    static_assert(KLD >= 1 && VLD >= 1, "row loads");
+};
+
+template <int DK, int DV>
+struct IntraBfSmem {
+    using Cf = IntraBf<DK, DV>;
+    uint16_t x[Cf::C * Cf::XW];  // K rows, later V rows of one pass
+    float at[Cf::C * Cf::AP];    // A, strictly lower
+    float tt[Cf::C * Cf::AP];    // T = (I + A)^{-1}, lower blocks
+    float gam[Cf::C], beta[Cf::C], sw[Cf::C];
+};
+
+template <int DK, int DV>
+__device__ __forceinline__ void intra_chunk_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                                 const uint16_t* __restrict__ v, const float* __restrict__ g,
+                                                 const float* __restrict__ beta, const int32_t* __restrict__ header,
+                                                 const ChunkInfo* __restrict__ tab, int32_t varlen, int64_t T,
+                                                 int32_t H, int32_t l2norm, unsigned char* __restrict__ records,
+                                                 size_t record_bytes, int64_t c)
+{
+    using M = Mma<uint16_t>;
+    using F = Mma<float>;
+    using Cf = IntraBf<DK, DV>;
+    using R = Rec<uint16_t, 64, DK, DV>;
+    using KX = RowTile<DK>;
+    using VX = RowTile<Cf::VP>;
+    typedef typename M::Frag Frag;
+    constexpr int C = 64, AP = Cf::AP, RT = 4, DKS = Cf::DKS, E = 8;
+    constexpr int KCPR = DK / 8, VCPR = Cf::VP / 8;
+
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    IntraBfSmem<DK, DV>& sm = *reinterpret_cast<IntraBfSmem<DK, DV>*>(smem_raw);
+
+    const int h = blockIdx.y;
+    if (varlen && c >= header[1]) return;
+    if (!varlen && c * C >= T) return;
+    const ChunkInfo ci = chunk_info(tab, varlen, c, C, T);
+    const int len = ci.len;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // = the row tile this wave owns
+    const int g16 = lane >> 4, l16 = lane & 15;
+
+    unsigned char* recb = records + ((size_t)c * H + h) * record_bytes;
+    uint16_t* rec = reinterpret_cast<uint16_t*>(recb);
+    float* recU = reinterpret_cast<float*>(recb + R::U_BYTE_OFF);
+    const int64_t row0 = (int64_t)ci.tok0 * H + h;  // row index of token tok0 in [tokens*H]
+
+    // ---- phase 1: every global read of the chunk, issued up front
+    float gv = 0.f, bv = 0.f;
+    if (wave == 0 && lane < len) {
+        gv = g[row0 + (int64_t)lane * H];
+        bv = beta[row0 + (int64_t)lane * H];
+    }
+    uint4 kr[Cf::KLD];
+#pragma unroll
+    for (int s = 0; s < Cf::KLD; ++s) {
+        const int qi = s * 256 + tid, j = qi / KCPR, ch = qi % KCPR;
+        kr[s] = j < len ? *reinterpret_cast<const uint4*>(k + (row0 + (int64_t)j * H) * DK + ch * 8)
+                        : uint4{0u, 0u, 0u, 0u};
+    }
+    const int r_own = wave * 16 + l16;  // the chunk row (column of the products) this lane owns
+    const bool live = r_own < len;
+    Frag qf[DKS];  // Q row r_own in sigma order over d_k: operand of R and the stored Q fragments
+#pragma unroll
+    for (int ks = 0; ks < DKS; ++ks)
+        qf[ks] = live ? M::ld_sigma(q + (row0 + (int64_t)r_own * H) * DK + ks * 32, g16) : zero_frag<uint16_t>();
+    uint4 vr[Cf::VLD];
+    auto load_v = [&](int pass) {
+#pragma unroll
+        for (int s = 0; s < Cf::VLD; ++s) {
+            const int qi = s * 256 + tid, j = qi / VCPR, ch = qi % VCPR;
+            vr[s] = j < len ? *reinterpret_cast<const uint4*>(v + (row0 + (int64_t)j * H) * DV + pass * Cf::VP + ch * 8)
+                            : uint4{0u, 0u, 0u, 0u};
+        }
+    };
+    load_v(0);
+
+    // gates: gamma (inclusive scan within the chunk), beta; rows >= len: g = 0, beta = 0
+    if (wave == 0) {
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float y = __shfl_up(gv, off, 64);
+            if (lane >= off) gv += y;
+        }
+        sm.gam[lane] = gv;
+        sm.beta[lane] = bv;
+    }
+#pragma unroll
+    for (int s = 0; s < Cf::KLD; ++s) {
+        const int qi = s * 256 + tid, j = qi / KCPR, ch = qi % KCPR;
+        *reinterpret_cast<uint4*>(sm.x + j * DK + (KX::chunk(j, ch) << 3)) = kr[s];
+    }
+    __syncthreads();
+
+    // ---- phase 2: G, R against K row tiles 0..wave; A rows, P, Q fragments, row scales
+    auto lds_sigma = [&](int r, int ks) -> Frag {
+        const u16x4 lo = *reinterpret_cast<const u16x4*>(sm.x + KX::at(r, ks * 32 + 4 * g16));
+        const u16x4 hi = *reinterpret_cast<const u16x4*>(sm.x + KX::at(r, ks * 32 + 16 + 4 * g16));
+        Frag f;
+        f[0] = lo.x; f[1] = lo.y; f[2] = lo.z; f[3] = lo.w;
+        f[4] = hi.x; f[5] = hi.y; f[6] = hi.z; f[7] = hi.w;
+        return f;
+    };
+    // 1/||x|| of the row whose sigma fragments this lane and its three partner lanes hold
+    auto inv_norm = [&](const Frag* f, bool row_live) -> float {
+        float ss = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < DKS; ++ks)
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const float x = bf16_bits_to_f32(f[ks][e]);
+                ss += x * x;
+            }
+        ss += __shfl_xor(ss, 16, 64);
+        ss += __shfl_xor(ss, 32, 64);
+        return row_live ? (l2norm ? 1.0f / sqrtf(ss + kNormEps) : 1.0f) : 0.f;
+    };
+    const float rq = inv_norm(qf, live);
+    Frag kw[DKS];
+#pragma unroll
+    for (int ks = 0; ks < DKS; ++ks) kw[ks] = lds_sigma(r_own, ks);
+    const float rk = inv_norm(kw, live);
+    const float gam_r = sm.gam[r_own], beta_r = sm.beta[r_own];
+    float px[2][8];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) px[u][e] = 0.f;
+#pragma unroll
+    for (int tj = 0; tj < RT; ++tj) {
+        if (tj > wave) break;
+        Frag kt[DKS];
+#pragma unroll
+        for (int ks = 0; ks < DKS; ++ks) kt[ks] = lds_sigma(tj * 16 + l16, ks);
+        const float rkt = inv_norm(kt, tj * 16 + l16 < len);
+        f32x4 aG = {0.f, 0.f, 0.f, 0.f}, aR = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < DKS; ++ks) {
+            aG = M::mma(kt[ks], kw[ks], aG);
+            aR = M::mma(kt[ks], qf[ks], aR);
+        }
+        // lane holds rows j = 16 tj + 4 g16 + i of column r_own of K K^T and K Q^T
+        f32x4 av;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int j = tj * 16 + 4 * g16 + i;
+            const float rkj = __shfl(rkt, 4 * g16 + i, 64);
+            const float d = expf(gam_r - sm.gam[j]);  // used only for j <= r_own, where the exponent is <= 0
+            av[i] = j < r_own ? beta_r * rk * rkj * aG[i] * d : 0.f;
+            px[tj >> 1][(tj & 1) * 4 + i] = j <= r_own ? rq * rkj * aR[i] * d : 0.f;
+        }
+        *reinterpret_cast<f32x4*>(sm.at + r_own * AP + tj * 16 + 4 * g16) = av;
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        if (ks > wave / 2) break;  // P row tile `wave` has k-steps up to its diagonal
+        Frag hi, lo;
+        split_frag<uint16_t>(px[ks], hi, lo);
+        const size_t fo = ((size_t)(wave * R::CKS + ks) * 64 + lane) * E;
+        st_frag<uint16_t>(rec + R::PH_OFF + fo, hi);
+        st_frag<uint16_t>(rec + R::PL_OFF + fo, lo);
+    }
+#pragma unroll
+    for (int ks = 0; ks < DKS; ++ks) st_frag<uint16_t>(rec + R::Q_OFF + ((size_t)(wave * DKS + ks) * 64 + lane) * E, qf[ks]);
+    if (g16 == 0) {
+        const float gL = sm.gam[C - 1];  // rows >= len carry g = 0, so this is gamma at len-1
+        const float eg = expf(gam_r);
+        sm.sw[r_own] = beta_r * eg * rk;  // W = T diag(sw) K
+        reinterpret_cast<float*>(recb + R::QS_BYTE_OFF)[r_own] = rq * eg;
+        reinterpret_cast<float*>(recb + R::KSC_BYTE_OFF)[r_own] = rk * expf(gL - gam_r);
+    }
+    // raw K^T fragments (identity over the chunk) of this wave's d_k blocks: stored,
+    // and kept as the W operand
+    Frag kT[Cf::DBW][2][2];
+#pragma unroll
+    for (int b = 0; b < Cf::DBW; ++b) {
+        const int dks = wave + 4 * b;
+        if (dks >= DKS) break;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int jk = 0; jk < 2; ++jk) {
+                const int col = (2 * dks + u) * 16 + l16;
+                Frag f;
+#pragma unroll
+                for (int e = 0; e < E; ++e) f[e] = sm.x[KX::at(jk * 32 + g16 * 8 + e, col)];
+                kT[b][u][jk] = f;
+                st_frag<uint16_t>(rec + R::K_OFF + ((size_t)((2 * dks + u) * R::CKS + jk) * 64 + lane) * E, f);
+            }
+    }
+    __syncthreads();  // K rows no longer read; A complete
+
+    // ---- phase 3: V rows into LDS; T = (I + A)^{-1}
+    auto store_v = [&]() {
+#pragma unroll
+        for (int s = 0; s < Cf::VLD; ++s) {
+            const int qi = s * 256 + tid, j = qi / VCPR, ch = qi % VCPR;
+            *reinterpret_cast<uint4*>(sm.x + j * Cf::VP + (VX::chunk(j, ch) << 3)) = vr[s];
+        }
+    };
+    store_v();
+    if constexpr (Cf::NVP > 1) load_v(1);
+    if (tid == 0) {
+        *reinterpret_cast<f32x4*>(recb + R::DEC_BYTE_OFF) =
+            f32x4{expf(sm.gam[C - 1]), __int_as_float(ci.tok0), __int_as_float(ci.len), 0.f};
+    }
+    {   // diagonal 16x16 blocks by forward substitution, one per wave
+        const int b0 = wave * 16, col = l16;
+        float t[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float acc = (r == col) ? 1.f : 0.f;
+            const float* arow = sm.at + (b0 + r) * AP + b0;
+#pragma unroll
+            for (int j = 0; j < r; ++j) acc -= arow[j] * t[j];
+            t[r] = acc;
+        }
+        if (lane < 16) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sm.tt[(b0 + r) * AP + b0 + col] = t[r];
+        }
+    }
+    __syncthreads();
+    // T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj on fp32 MFMA, by block distance
+#pragma unroll
+    for (int dd = 1; dd < RT; ++dd) {
+        const int jb = wave, ib = wave + dd;
+        if (ib < RT) {
+            f32x4 X = {0.f, 0.f, 0.f, 0.f};
+            for (int mb = jb; mb < ib; ++mb) {
+                const f32x4 fa = *reinterpret_cast<const f32x4*>(sm.at + (ib * 16 + l16) * AP + mb * 16 + 4 * g16);
+                f32x4 fb;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) fb[e] = sm.tt[(mb * 16 + 4 * g16 + e) * AP + jb * 16 + l16];
+                X = F::mma(fa, fb, X);
+            }
+            const f32x4 fd = *reinterpret_cast<const f32x4*>(sm.tt + (ib * 16 + l16) * AP + ib * 16 + 4 * g16);
+            f32x4 Y = {0.f, 0.f, 0.f, 0.f};
+            Y = F::mma(fd, X, Y);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sm.tt[(ib * 16 + 4 * g16 + e) * AP + jb * 16 + l16] = -Y[e];
+        }
+        __syncthreads();
+    }
+
+    // ---- phase 4: W^T = K^T (T diag(sw))^T and U = (T diag(beta)) V, T split hi/lo.
+    // Row r = 16 rt + l16 of T diag(x) over k-step jk is both the B operand of W^T
+    // and the A operand of U; entries above the diagonal are zero (masked here,
+    // the blocks above the diagonal are never written).
+    auto t_frags = [&](int rt, int jk, bool want_w, Frag& swh, Frag& swl, Frag& sbh, Frag& sbl) {
+        const int r = rt * 16 + l16, j0 = jk * 32 + g16 * 8;
+        const f32x4 t0 = *reinterpret_cast<const f32x4*>(sm.tt + r * AP + j0);
+        const f32x4 t1 = *reinterpret_cast<const f32x4*>(sm.tt + r * AP + j0 + 4);
+        float xs[E], xb[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const float tv = j0 + e <= r ? (e < 4 ? t0[e] : t1[e - 4]) : 0.f;
+            xs[e] = tv * sm.sw[j0 + e];
+            xb[e] = tv * sm.beta[j0 + e];
+        }
+        if (want_w) split_frag<uint16_t>(xs, swh, swl);
+        split_frag<uint16_t>(xb, sbh, sbl);
+    };
+    auto v_frags = [&](Frag (&vf)[Cf::VTW][2]) {
+#pragma unroll
+        for (int t = 0; t < Cf::VTW; ++t) {
+            const int vt = wave + 4 * t;
+            if (vt >= Cf::VTP) break;
+#pragma unroll
+            for (int jk = 0; jk < 2; ++jk) {
+                Frag f;
+#pragma unroll
+                for (int e = 0; e < E; ++e) f[e] = sm.x[VX::at(jk * 32 + g16 * 8 + e, vt * 16 + l16)];
+                vf[t][jk] = f;
+            }
+        }
+    };
+    auto u_tiles = [&](int pass, int rt, int nks, const Frag (&vf)[Cf::VTW][2], const Frag* sbh, const Frag* sbl) {
+#pragma unroll
+        for (int t = 0; t < Cf::VTW; ++t) {
+            const int vt = wave + 4 * t;
+            if (vt >= Cf::VTP) break;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int jk = 0; jk < 2; ++jk) {
+                if (jk >= nks) break;
+                acc = M::mma(sbh[jk], vf[t][jk], acc);
+                acc = M::mma(sbl[jk], vf[t][jk], acc);
+            }
+            const int vg = pass * Cf::VTP + vt;
+            *reinterpret_cast<f32x4*>(recU + ((size_t)(rt * R::VT + vg) * 64 + lane) * 4) = acc;
+        }
+    };
+    {
+        Frag vf[Cf::VTW][2];
+        v_frags(vf);
+#pragma unroll 1
+        for (int rt = 0; rt < RT; ++rt) {
+            const int nks = rt / 2 + 1;  // T[r][j] = 0 for j > r
+            Frag swh[2], swl[2], sbh[2], sbl[2];
+#pragma unroll
+            for (int jk = 0; jk < 2; ++jk)
+                if (jk < nks) t_frags(rt, jk, true, swh[jk], swl[jk], sbh[jk], sbl[jk]);
+#pragma unroll
+            for (int b = 0; b < Cf::DBW; ++b) {
+                const int dks = wave + 4 * b;
+                if (dks >= DKS) break;
+                f32x4 acc[2];
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int jk = 0; jk < 2; ++jk) {
+                        if (jk >= nks) break;
+                        acc[u] = M::mma(kT[b][u][jk], swh[jk], acc[u]);
+                        acc[u] = M::mma(kT[b][u][jk], swl[jk], acc[u]);
+                    }
+                }
+                float x[E];
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) x[u * 4 + i] = acc[u][i];
+                st_frag<uint16_t>(rec + R::WH_OFF + ((size_t)(rt * DKS + dks) * 64 + lane) * E, frag_from<uint16_t>(x));
+            }
+            u_tiles(0, rt, nks, vf, sbh, sbl);
+        }
+    }
+#pragma unroll 1
+    for (int pass = 1; pass < Cf::NVP; ++pass) {
+        __syncthreads();  // the previous pass's value rows are no longer read
+        store_v();
+        if (pass + 1 < Cf::NVP) load_v(pass + 1);
+        __syncthreads();
+        Frag vf[Cf::VTW][2];
+        v_frags(vf);
+#pragma unroll 1
+        for (int rt = 0; rt < RT; ++rt) {
+            const int nks = rt / 2 + 1;
+            Frag swh[2], swl[2], sbh[2], sbl[2];
+#pragma unroll
+            for (int jk = 0; jk < 2; ++jk)
+                if (jk < nks) t_frags(rt, jk, false, swh[jk], swl[jk], sbh[jk], sbl[jk]);
+            u_tiles(pass, rt, nks, vf, sbh, sbl);
+        }
+    }
+}
+
+// One workgroup per (chunk, head), for the chunks [c_base, c_end).
+template <typename TIn, int C, int DK, int DV>
+__global__ __launch_bounds__(256) void intra_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
+                                                    const TIn* __restrict__ v, const float* __restrict__ g,
+                                                    const float* __restrict__ beta, const int32_t* __restrict__ header,
+                                                    const ChunkInfo* __restrict__ tab, int32_t varlen, int64_t T,
+                                                    int32_t H, int32_t l2norm,
+                                                    unsigned char* __restrict__ records, size_t record_bytes,
+                                                    int64_t c_base, int64_t c_end)
+{
+    const int64_t c = c_base + blockIdx.x;
+    if (c >= c_end) return;
+    if constexpr (sizeof(TIn) == 2 && C == 64)
+        intra_chunk_bf16<DK, DV>(q, k, v, g, beta, header, tab, varlen, T, H, l2norm, records, record_bytes, c);
+    else
+        intra_chunk<TIn, C, DK, DV>(q, k, v, g, beta, header, tab, varlen, T, H, l2norm, records, record_bytes, c);
+}
+
 // ------------------------------------------------------------------ chain kernel
 
 template <typename TIn> struct OStore;
@@ -804,11 +1209,12 @@ __device__ __forceinline__ void wait_vmcnt()
 // Workgroups are mapped so that all row tiles of one (sequence, head) pair run
 // on one XCD (workgroups are dealt to the 8 XCDs round-robin): they read the
 // same per-chunk records, which then come from that XCD's L2.
-template <typename TIn, int C, int DK, int DV, int NW>
+template <typename TIn, int C, int DK, int DV, int NW, bool SEG>
 __global__ __launch_bounds__((NW + chain_loaders<TIn, C>()) * 64) void chain_kernel(
     const int32_t* __restrict__ header, const int32_t* __restrict__ seq_first, int32_t varlen, int64_t T, int32_t H,
-    int32_t pairs, const unsigned char* records, size_t record_bytes, const float* __restrict__ init_state,
-    float* __restrict__ final_state, TIn* __restrict__ states, TIn* __restrict__ deltas)
+    int32_t pairs, const unsigned char* records, size_t record_bytes, const float* init_state,
+    float* final_state, TIn* __restrict__ states, TIn* __restrict__ deltas, int64_t seg_begin, int64_t seg_end,
+    float* carry)
 // (records is deliberately not __restrict__: a restrict read-only argument lets
 // the compiler treat its loads as invariant and sink them across the barriers
 // to their use, which would turn the loaders' early loads into late ones)
@@ -846,15 +1252,26 @@ __global__ __launch_bounds__((NW + chain_loaders<TIn, C>()) * 64) void chain_ker
     const int tile = slot % TILES;
     const int row0 = tile * 16;  // first state row (value index) of this workgroup
 
-    int64_t c_begin, c_end;
+    // SEG: this launch covers the chunks [seg_begin, seg_end) of the global
+    // chunk order; a sequence crossing a segment boundary carries its state
+    // through `carry` ([N][H][d_v][d_k] fp32).  The state enters from
+    // init_state (or zero) at the sequence's first chunk, else from carry, and
+    // leaves to final_state after the sequence's last chunk, else to carry.
+    // Without SEG the launch covers every chunk.
+    int64_t s_first, s_last;  // the sequence's chunk range
     if (varlen) {
         if (header[0] != 0) return;
-        c_begin = seq_first[n];
-        c_end = seq_first[n + 1];
+        s_first = seq_first[n];
+        s_last = seq_first[n + 1];
     } else {
-        c_begin = 0;
-        c_end = (T + C - 1) / C;
+        s_first = 0;
+        s_last = (T + C - 1) / C;
     }
+    const int64_t c_begin = SEG && s_first < seg_begin ? seg_begin : s_first;
+    const int64_t c_end = SEG && s_last > seg_end ? seg_end : s_last;
+    if (c_begin >= c_end && !(s_first == s_last && s_first >= seg_begin && s_first < seg_end)) return;
+    const float* state_in = c_begin == s_first ? init_state : carry;
+    float* state_out_ptr = c_end == s_last ? final_state : carry;
 
     // ---------------------------------------------------------------- operands
     const uint32_t lane_b = (uint32_t)lane * 16;
@@ -1049,8 +1466,8 @@ __global__ __launch_bounds__((NW + chain_loaders<TIn, C>()) * 64) void chain_ker
         const int mt = wave + NW * a;
         S[a] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (mt < R::MT) {
-            if (init_state)
-                S[a] = *reinterpret_cast<const f32x4*>(init_state + st_base + (size_t)(row0 + l16) * DK + mt * 16 +
+            if (state_in)
+                S[a] = *reinterpret_cast<const f32x4*>(state_in + st_base + (size_t)(row0 + l16) * DK + mt * 16 +
                                                        4 * g16);
             store_quad<TIn, false>(sm.sr + l16 * SP + quad_pos<TIn>(mt, g16), nullptr, S[a]);
         }
@@ -1120,12 +1537,13 @@ __global__ __launch_bounds__((NW + chain_loaders<TIn, C>()) * 64) void chain_ker
         lds_barrier();  // ---- C: state copy visible; K region free
     }
 
-    if (final_state) {
+    if (state_out_ptr) {
 #pragma unroll
         for (int a = 0; a < P::MTW; ++a) {
             const int mt = wave + NW * a;
             if (mt < R::MT)
-                *reinterpret_cast<f32x4*>(final_state + st_base + (size_t)(row0 + l16) * DK + mt * 16 + 4 * g16) = S[a];
+                *reinterpret_cast<f32x4*>(state_out_ptr + st_base + (size_t)(row0 + l16) * DK + mt * 16 + 4 * g16) =
+                    S[a];
         }
     }
 }
@@ -1145,11 +1563,12 @@ struct OutCfg {
 };
 
 template <typename TIn, int C, int DK, int DV>
-__global__ __launch_bounds__(256) void output_kernel(const int32_t* __restrict__ header,
+__device__ __forceinline__ void output_chunk(const int32_t* __restrict__ header,
                                                      const ChunkInfo* __restrict__ tab, int32_t varlen, int64_t T,
                                                      int32_t H, const unsigned char* __restrict__ records,
                                                      size_t record_bytes, const TIn* __restrict__ states,
-                                                     const TIn* __restrict__ deltas, TIn* __restrict__ o, float scale)
+                                                     const TIn* __restrict__ deltas, TIn* __restrict__ o, float scale,
+                                                     int64_t c)
 {
     using M = Mma<TIn>;
     using R = Rec<TIn, C, DK, DV>;
@@ -1163,7 +1582,6 @@ __global__ __launch_bounds__(256) void output_kernel(const int32_t* __restrict__
     extern __shared__ __align__(16) unsigned char out_lds[];
     TIn* ot = reinterpret_cast<TIn*>(out_lds);  // [C][OP]
 
-    const int64_t c = blockIdx.x;
     const int h = blockIdx.y;
     if (varlen && c >= header[1]) return;
     if (!varlen && c * C >= T) return;
@@ -1266,7 +1684,56 @@ __global__ __launch_bounds__(256) void output_kernel(const int32_t* __restrict__
     }
 }
 
+template <typename TIn, int C, int DK, int DV>
+__global__ __launch_bounds__(256) void output_kernel(const int32_t* __restrict__ header,
+                                                     const ChunkInfo* __restrict__ tab, int32_t varlen, int64_t T,
+                                                     int32_t H, const unsigned char* __restrict__ records,
+                                                     size_t record_bytes, const TIn* __restrict__ states,
+                                                     const TIn* __restrict__ deltas, TIn* __restrict__ o, float scale,
+                                                     int64_t c_base, int64_t c_end)
+{
+    const int64_t c = c_base + blockIdx.x;
+    if (c >= c_end) return;
+    output_chunk<TIn, C, DK, DV>(header, tab, varlen, T, H, records, record_bytes, states, deltas, o, scale, c);
+}
+
 // ------------------------------------------------------------------ dispatch
+
+// Side streams and events of the pipelined prefill, created once per device
+// and kept for the life of the process (default priority, non-blocking with
+// respect to the legacy default stream).
+struct PipeRes {
+    static constexpr int MAX_SEG = 16;
+    hipStream_t intra_s = nullptr, out_s = nullptr;
+    hipEvent_t start, intra_done[MAX_SEG], chain_done[MAX_SEG], intra_end, out_end;
+    bool ok = false;
+};
+
+static hipError_t pipe_res(PipeRes** out)
+{
+    static std::mutex mu;
+    static PipeRes res[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    PipeRes& r = res[dev];
+    if (!r.ok) {
+        if ((e = hipStreamCreateWithFlags(&r.intra_s, hipStreamNonBlocking)) != hipSuccess) return e;
+        if ((e = hipStreamCreateWithFlags(&r.out_s, hipStreamNonBlocking)) != hipSuccess) return e;
+        hipEvent_t* evs[] = {&r.start, &r.intra_end, &r.out_end};
+        for (hipEvent_t* ev : evs)
+            if ((e = hipEventCreateWithFlags(ev, hipEventDisableTiming)) != hipSuccess) return e;
+        for (int i = 0; i < PipeRes::MAX_SEG; ++i) {
+            if ((e = hipEventCreateWithFlags(&r.intra_done[i], hipEventDisableTiming)) != hipSuccess) return e;
+            if ((e = hipEventCreateWithFlags(&r.chain_done[i], hipEventDisableTiming)) != hipSuccess) return e;
+        }
+        r.ok = true;
+    }
+    *out = &r;
+    return hipSuccess;
+}
 
 template <typename TIn, int C, int DK, int DV>
 static hipError_t run_prefill(const PrefillArgs& a)
@@ -1277,75 +1744,126 @@ static hipError_t run_prefill(const PrefillArgs& a)
     ChunkInfo* tab = reinterpret_cast<ChunkInfo*>(a.ws + a.lay.off_chunk_tab);
     int32_t* first = reinterpret_cast<int32_t*>(a.ws + a.lay.off_seq_first);
     unsigned char* records = a.ws + a.lay.off_records;
-    const int varlen = a.cu_seqlens != nullptr;
-
-    if (a.stages & 1) {
-        int64_t grid_chunks;
-        if (varlen) {
-            hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(256), 0, a.stream, a.cu_seqlens, a.N, a.T, (int32_t)C,
-                               a.lay.max_chunks, header, tab, first);
-            grid_chunks = a.lay.max_chunks;
-        } else {
-            grid_chunks = (a.T + C - 1) / C;
-        }
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        if (grid_chunks > 0) {
-            const size_t smem = sizeof(IntraSmem<TIn, C, DK, DV>);
-            static bool attr_set = false;  // idempotent attribute; racing writers store the same value
-            if (!attr_set) {
-                e = hipFuncSetAttribute((const void*)intra_kernel<TIn, C, DK, DV>,
-                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-                if (e != hipSuccess) return e;
-                attr_set = true;
-            }
-            hipLaunchKernelGGL((intra_kernel<TIn, C, DK, DV>), dim3((uint32_t)grid_chunks, a.H), dim3(256), smem,
-                               a.stream, (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, a.g, a.beta, header, tab,
-                               varlen, a.T, a.H, a.l2norm, records, a.lay.record_bytes);
-            e = hipGetLastError();
-            if (e != hipSuccess) return e;
-        }
-    }
-    const int64_t pairs = (int64_t)a.N * a.H;
-    const int64_t groups = (pairs + 7) / 8;
-    const int64_t blocks = groups * 8 * (DV / 16);
-    if (pairs > 0x7fffffff || blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     TIn* states = reinterpret_cast<TIn*>(a.ws + a.lay.off_states);
     TIn* deltas = reinterpret_cast<TIn*>(a.ws + a.lay.off_deltas);
-    if (a.stages & 2) {
+    float* carry = reinterpret_cast<float*>(a.ws + a.lay.off_carry);
+    const int varlen = a.cu_seqlens != nullptr;
+    const int64_t grid_chunks = varlen ? a.lay.max_chunks : (a.T + C - 1) / C;
+    const int64_t pairs = (int64_t)a.N * a.H;
+    const int64_t chain_blocks = (pairs + 7) / 8 * 8 * (DV / 16);
+    if (pairs > 0x7fffffff || chain_blocks > 0x7fffffff || grid_chunks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    constexpr int64_t ALL = INT64_MAX;
+
+    auto launch_intra = [&](int64_t c0, int64_t c1, hipStream_t st) -> hipError_t {
+        if (c1 <= c0) return hipSuccess;
+        size_t smem = sizeof(IntraSmem<TIn, C, DK, DV>);
+        if constexpr (sizeof(TIn) == 2 && C == 64) smem = sizeof(IntraBfSmem<DK, DV>);
+        static bool attr = false;  // idempotent attribute; racing writers store the same value
+        if (!attr) {
+            hipError_t e = hipFuncSetAttribute((const void*)intra_kernel<TIn, C, DK, DV>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+            if (e != hipSuccess) return e;
+            attr = true;
+        }
+        hipLaunchKernelGGL((intra_kernel<TIn, C, DK, DV>), dim3((uint32_t)(c1 - c0), a.H), dim3(256), smem,
+                           st, (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, a.g, a.beta, header, tab, varlen,
+                           a.T, a.H, a.l2norm, records, a.lay.record_bytes, c0, c1);
+        return hipGetLastError();
+    };
+    auto launch_chain = [&](int64_t c0, int64_t c1, hipStream_t st) -> hipError_t {
         constexpr int NW = 8;
         using Lds = ChainLds<TIn, C, DK, DV, NW, chain_staged<TIn, C>()>;
         static_assert(sizeof(Lds) <= 160 * 1024, "chain kernel LDS");
-        static bool attr = false;  // idempotent attribute; racing writers store the same value
-        if (!attr) {
-            hipError_t ea = hipFuncSetAttribute((const void*)chain_kernel<TIn, C, DK, DV, NW>,
-                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(Lds));
-            if (ea != hipSuccess) return ea;
-            attr = true;
+        const bool seg = !(c0 == 0 && c1 == ALL);
+        const void* fn = seg ? (const void*)chain_kernel<TIn, C, DK, DV, NW, true>
+                             : (const void*)chain_kernel<TIn, C, DK, DV, NW, false>;
+        static bool attr[2] = {false, false};  // idempotent attributes; racing writers store the same value
+        if (!attr[seg]) {
+            hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(Lds));
+            if (e != hipSuccess) return e;
+            attr[seg] = true;
         }
-        hipLaunchKernelGGL((chain_kernel<TIn, C, DK, DV, NW>), dim3((uint32_t)blocks),
-                           dim3((NW + chain_loaders<TIn, C>()) * 64), sizeof(Lds), a.stream, header, first, varlen,
-                           a.T, a.H, (int32_t)pairs, records, a.lay.record_bytes, a.init_state, a.final_state, states,
-                           deltas);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    if (!(a.stages & 4)) return hipSuccess;
-    const int64_t grid_chunks = varlen ? a.lay.max_chunks : (a.T + C - 1) / C;
-    if (grid_chunks > 0) {
+        const dim3 grid((uint32_t)chain_blocks), block((NW + chain_loaders<TIn, C>()) * 64);
+        if (seg)
+            hipLaunchKernelGGL((chain_kernel<TIn, C, DK, DV, NW, true>), grid, block, sizeof(Lds), st, header, first,
+                               varlen, a.T, a.H, (int32_t)pairs, records, a.lay.record_bytes, a.init_state,
+                               a.final_state, states, deltas, c0, c1, carry);
+        else
+            hipLaunchKernelGGL((chain_kernel<TIn, C, DK, DV, NW, false>), grid, block, sizeof(Lds), st, header, first,
+                               varlen, a.T, a.H, (int32_t)pairs, records, a.lay.record_bytes, a.init_state,
+                               a.final_state, states, deltas, c0, c1, carry);
+        return hipGetLastError();
+    };
+    auto launch_output = [&](int64_t c0, int64_t c1, hipStream_t st) -> hipError_t {
+        if (c1 <= c0) return hipSuccess;
         const size_t smem = (size_t)C * OutCfg<TIn, C, DK, DV>::OP * sizeof(TIn);
         static bool attr = false;  // idempotent attribute; racing writers store the same value
         if (!attr) {
-            hipError_t ea = hipFuncSetAttribute((const void*)output_kernel<TIn, C, DK, DV>,
-                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-            if (ea != hipSuccess) return ea;
+            hipError_t e = hipFuncSetAttribute((const void*)output_kernel<TIn, C, DK, DV>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+            if (e != hipSuccess) return e;
             attr = true;
         }
-        hipLaunchKernelGGL((output_kernel<TIn, C, DK, DV>), dim3((uint32_t)grid_chunks, a.H), dim3(256), smem,
-                           a.stream, header, tab, varlen, a.T, a.H, records, a.lay.record_bytes, states, deltas,
-                           (TIn*)a.o, a.scale);
+        hipLaunchKernelGGL((output_kernel<TIn, C, DK, DV>), dim3((uint32_t)(c1 - c0), a.H), dim3(256),
+                           smem, st, header, tab, varlen, a.T, a.H, records, a.lay.record_bytes, states, deltas,
+                           (TIn*)a.o, a.scale, c0, c1);
+        return hipGetLastError();
+    };
+#define GDN_TRY(x)                       \
+    do {                                 \
+        hipError_t e_ = (x);             \
+        if (e_ != hipSuccess) return e_; \
+    } while (0)
+
+    if ((a.stages & 1) && varlen) {
+        hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(256), 0, a.stream, a.cu_seqlens, a.N, a.T, (int32_t)C,
+                           a.lay.max_chunks, header, tab, first);
+        GDN_TRY(hipGetLastError());
     }
-    return hipGetLastError();
+
+    // The state chain keeps only (sequences x heads x d_v/16) workgroups busy.
+    // When that leaves most of the GPU idle and every stage runs in this call,
+    // the chunks are cut into segments and pipelined over three streams: the
+    // chain of segment s (caller's stream) runs while the intra-chunk kernel
+    // prepares later segments and the output kernel finishes earlier ones on
+    // side streams; events order each segment's three kernels.
+    constexpr int64_t SEG_MIN = 64;
+    int nseg = 1;
+    if (a.stages == 7 && chain_blocks < 256 && grid_chunks >= 2 * SEG_MIN)
+        nseg = (int)std::min<int64_t>(8, grid_chunks / SEG_MIN);
+    if (nseg == 1) {
+        if (a.stages & 1) GDN_TRY(launch_intra(0, grid_chunks, a.stream));
+        if (a.stages & 2) GDN_TRY(launch_chain(0, ALL, a.stream));
+        if (a.stages & 4) GDN_TRY(launch_output(0, grid_chunks, a.stream));
+        return hipSuccess;
+    }
+    PipeRes* pr = nullptr;
+    GDN_TRY(pipe_res(&pr));
+    const int64_t seg = (grid_chunks + nseg - 1) / nseg;
+    auto seg_lo = [&](int s) { return std::min<int64_t>(grid_chunks, (int64_t)s * seg); };
+    // the side streams start after everything already queued on the caller's stream
+    GDN_TRY(hipEventRecord(pr->start, a.stream));
+    GDN_TRY(hipStreamWaitEvent(pr->intra_s, pr->start, 0));
+    GDN_TRY(hipStreamWaitEvent(pr->out_s, pr->start, 0));
+    GDN_TRY(launch_intra(0, seg_lo(1), a.stream));
+    for (int s = 1; s < nseg; ++s) {  // later segments' preparation, in order, on its own stream
+        GDN_TRY(launch_intra(seg_lo(s), seg_lo(s + 1), pr->intra_s));
+        GDN_TRY(hipEventRecord(pr->intra_done[s], pr->intra_s));
+    }
+    for (int s = 0; s < nseg; ++s) {
+        if (s > 0) GDN_TRY(hipStreamWaitEvent(a.stream, pr->intra_done[s], 0));
+        GDN_TRY(launch_chain(seg_lo(s), s + 1 < nseg ? seg_lo(s + 1) : ALL, a.stream));
+        GDN_TRY(hipEventRecord(pr->chain_done[s], a.stream));
+        GDN_TRY(hipStreamWaitEvent(pr->out_s, pr->chain_done[s], 0));
+        GDN_TRY(launch_output(seg_lo(s), seg_lo(s + 1), pr->out_s));
+    }
+    // the caller's stream resumes after both side streams
+    GDN_TRY(hipEventRecord(pr->intra_end, pr->intra_s));
+    GDN_TRY(hipEventRecord(pr->out_end, pr->out_s));
+    GDN_TRY(hipStreamWaitEvent(a.stream, pr->intra_end, 0));
+    GDN_TRY(hipStreamWaitEvent(a.stream, pr->out_end, 0));
+#undef GDN_TRY
+    return hipSuccess;
 }
 
 template <typename TIn, int C, int DK>

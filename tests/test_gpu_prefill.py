@@ -132,6 +132,36 @@ def test_varlen_packing(dtype, lens):
     _check(inp, 64, TOL_F32 if dtype == "f32" else TOL_BF16, init=inp.init_state)
 
 
+@pytest.mark.parametrize("dk,dv", [(64, 64), (256, 256)])
+def test_pipelined_segments_match_oracle_and_unsegmented(dk, dv):
+    """Few long packed sequences leave the state chain most of the GPU, so a
+    whole-prefill call pipelines segments of chunks over three streams and
+    carries each sequence's state across segment boundaries.  The result must
+    match the oracle and be bitwise equal to the same prefill run stage by
+    stage (one chain launch over all chunks)."""
+    lens = [5000, 3000, 4100] if dk == 64 else [4100, 4000]
+    H = 2 if dk == 64 else 3
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    inp = synth.prefill_inputs(int(cu[-1]), H, dk, dv, "bf16", seed=dk + 77, gate="slow", cu_seqlens=cu,
+                               init_state_std=0.3)
+    o, fs = _gpu(inp, 64, init=inp.init_state)
+    o_ref, fs_ref = oracle.prefill(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.init_state, cu_seqlens=cu, bf16=True)
+    assert bound_ratio(o, o_ref, TOL_BF16, stored_bf16=True) <= 1.0
+    assert rel_err(fs, fs_ref) <= TOL_BF16
+    t = lambda a, b=False: synth.to_torch(a, DEV, bf16=b)
+    args = (t(inp.q, True), t(inp.k, True), t(inp.v, True), t(inp.g), t(inp.beta))
+    init = torch.from_numpy(inp.init_state).to(DEV)
+    cu_t = torch.from_numpy(cu.astype(np.int32))
+    ws = torch.empty(gdn.prefill_workspace_size(int(cu[-1]), len(lens), H, dk, dv, 64), dtype=torch.uint8,
+                     device=DEV)
+    out = torch.empty((int(cu[-1]), H, dv), dtype=torch.bfloat16, device=DEV)
+    fin = torch.empty((len(lens), H, dv, dk), dtype=torch.float32, device=DEV)
+    for st in (gdn.STAGE_PREPARE, gdn.STAGE_PROPAGATE, gdn.STAGE_OUTPUT):
+        gdn.chunk_prefill(*args, init_state=init, cu_seqlens=cu_t, out=out, final_state=fin, workspace=ws, stages=st)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.float().cpu().numpy(), o) and np.array_equal(fin.cpu().numpy(), fs)
+
+
 def test_varlen_device_seqlens_without_host_copy():
     lens = [70, 3, 128]
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
