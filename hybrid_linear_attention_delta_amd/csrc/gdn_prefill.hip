@@ -1830,7 +1830,7 @@ static hipError_t run_prefill(const PrefillArgs& a)
     constexpr int64_t SEG_MIN = 64;
     int nseg = 1;
     if (a.stages == 7 && chain_blocks < 256 && grid_chunks >= 2 * SEG_MIN)
-        nseg = (int)std::min<int64_t>(8, grid_chunks / SEG_MIN);
+        nseg = (int)std::min<int64_t>(4, grid_chunks / SEG_MIN);
     if (nseg == 1) {
         if (a.stages & 1) GDN_TRY(launch_intra(0, grid_chunks, a.stream));
         if (a.stages & 2) GDN_TRY(launch_chain(0, ALL, a.stream));
