@@ -116,47 +116,76 @@ def render_trace():
     log(f"[profile] wrote {path}")
 
 
+def full_launch(name, grid, groups):
+    """True for the dispatch group that covers the whole workload: the
+    non-segmented chain instance, else the largest grid of the kernel."""
+    if "chain_kernel" in name:
+        return ", false>" in name
+    return grid == max(g for (nm, g) in groups if kernel_key(nm) == kernel_key(name))
+
+
 def counter_sums(d):
-    """{kernel key: (sum over dispatches of the counter in KiB, dispatches)}, {copy: ...}."""
+    """{kernel key: (sum over its whole-workload dispatches of the counter in KiB,
+    dispatches)}, plus {copy: ...}.  The pipelined prefill also launches the
+    kernels over segments of the chunks; those dispatches are left out, so the
+    figure is per launch over all chunks (as timed for the roofline)."""
     f = find(d, "counter_collection.csv")
     if f is None:
         return {}
-    acc = {}
+    groups = {}
     with open(f) as fh:
         for r in csv.DictReader(fh):
             name = r["Kernel_Name"]
-            key = kernel_key(name) or ("copy" if "copy" in name.lower() else None)
-            if key is None:
+            if kernel_key(name) is None and "copy" not in name.lower():
                 continue
-            v, n = acc.get(key, (0.0, set()))
+            v, n = groups.get((name, int(r["Grid_Size"])), (0.0, set()))
             n.add(r["Dispatch_Id"])
-            acc[key] = (v + float(r["Counter_Value"]), n)
-    return {k: (v, len(n)) for k, (v, n) in acc.items()}
+            groups[(name, int(r["Grid_Size"]))] = (v + float(r["Counter_Value"]), n)
+    acc = {}
+    for (name, grid), (v, n) in groups.items():
+        key = kernel_key(name)
+        if key is None:
+            key = "copy"
+        elif not full_launch(name, grid, groups):
+            continue
+        v0, n0 = acc.get(key, (0.0, 0))
+        acc[key] = (v0 + v, n0 + len(n))
+    return acc
 
 
 def mode_traffic():
     sys.path.insert(0, ROOT)
     import bench
 
-    result = {"sources_digest": bench.kernel_sources_digest(), "counters": {}, "calibration": {}, "kernels": {}}
     cmds = []
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
         rc, d, cmd = launch(["profile_bench.py", "copy"], ["--pmc", counter], f"copy_{counter}", 240)
         cmds.append(cmd)
-        cs = counter_sums(d).get("copy")
-        if rc != 0 or cs is None:
+        if rc != 0 or counter_sums(d).get("copy") is None:
             raise SystemExit(f"copy calibration for {counter} failed (exit {rc})")
-        kib, n = cs
-        factor = COPY_BYTES / (kib * 1024.0 / n)
-        result["calibration"][counter] = {"copy_bytes": COPY_BYTES, "counted_KiB_per_dispatch": kib / n,
-                                          "factor": factor}
         rc, d, cmd = launch(BENCH_PMC, ["--pmc", counter, "--kernel-include-regex",
                                         "chain_kernel|intra_kernel|output_kernel|decode_kernel"],
                             f"bench_{counter}", 600)
         cmds.append(cmd)
         if rc != 0:
             raise SystemExit(f"bench pass for {counter} failed (exit {rc})")
-        for key, (kib, n) in counter_sums(d).items():
+    # the kernel sources these counters belong to
+    with open(os.path.join(OUT, "traffic_meta.json"), "w") as f:
+        json.dump({"sources_digest": bench.kernel_sources_digest(), "commands": cmds}, f, indent=1)
+    summarize_traffic()
+
+
+def summarize_traffic():
+    """gpurun_out/profile_bench/traffic.json from the raw counter passes."""
+    with open(os.path.join(OUT, "traffic_meta.json")) as f:
+        meta = json.load(f)
+    result = {"sources_digest": meta["sources_digest"], "counters": {}, "calibration": {}, "kernels": {}}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        kib, n = counter_sums(os.path.join(OUT, f"copy_{counter}"))["copy"]
+        factor = COPY_BYTES / (kib * 1024.0 / n)
+        result["calibration"][counter] = {"copy_bytes": COPY_BYTES, "counted_KiB_per_dispatch": kib / n,
+                                          "factor": factor}
+        for key, (kib, n) in counter_sums(os.path.join(OUT, f"bench_{counter}")).items():
             if key == "copy":
                 continue
             result["counters"].setdefault(key, {})[counter] = {"KiB_per_dispatch": kib / n, "dispatches": n}
@@ -165,13 +194,15 @@ def mode_traffic():
         write = ent["WRITE_SIZE"]["KiB_per_dispatch"] * 1024 * result["calibration"]["WRITE_SIZE"]["factor"]
         result["kernels"][key] = {"fetch_bytes_per_launch": fetch, "write_bytes_per_launch": write,
                                   "hbm_bytes_per_launch": fetch + write}
-    result["commands"] = cmds
+    result["commands"] = meta["commands"]
     with open(os.path.join(OUT, "traffic.json"), "w") as f:
         json.dump(result, f, indent=1)
     log("[profile] wrote gpurun_out/profile_bench/traffic.json")
 
 
 def render_traffic():
+    if os.path.exists(os.path.join(OUT, "traffic_meta.json")):
+        summarize_traffic()
     p = os.path.join(OUT, "traffic.json")
     if not os.path.exists(p):
         log("[profile] no traffic output to render")
@@ -185,6 +216,8 @@ def render_traffic():
              "Commands (repository root, one MI355X), one counter per pass:", "", "```", *result["commands"], "```", "",
              "Calibration (a device copy of 1 GiB): "
              + ", ".join(f"{c} factor {v['factor']:.3f}" for c, v in result["calibration"].items()), "",
+             "Per launch over the whole workload (the pipelined prefill's launches over",
+             "segments of the chunks are left out).", "",
              "| kernel | fetch MB/launch | write MB/launch | total MB/launch |", "|---|---|---|---|"]
     for key, ent in sorted(result["kernels"].items()):
         lines.append(f"| `{key}` | {ent['fetch_bytes_per_launch'] / 1e6:.1f} | {ent['write_bytes_per_launch'] / 1e6:.1f}"
