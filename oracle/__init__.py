@@ -181,3 +181,59 @@ def decode_step(q, k, v, g, beta, state, scale=None, qk_l2norm=True, eps=DEFAULT
     if rc != 0:
         raise RuntimeError("oracle_decode_f64 rejected its arguments")
     return o
+
+
+# ----------------------------------------------------------------- gated RMSNorm read-out
+
+DEFAULT_NORM_EPS = 1e-6
+
+# Planted mistakes of the gated read-out, used only by the pin-strength tests.
+NORM_MUTATIONS = {
+    "sigmoid_gate": 1,     # sigma(z) instead of z sigma(z)
+    "sum_not_mean": 2,     # sum of squares over d_v instead of the mean
+    "no_eps": 3,           # eps dropped
+    "no_weight": 4,        # per-channel weight ignored
+    "norm_over_heads": 5,  # statistics over all heads of a token instead of per head
+}
+
+
+def _widen(a, bf16):
+    a = np.asarray(a)
+    if bf16:
+        if a.dtype != np.uint16:
+            raise ValueError("bf16 data must be passed as raw uint16 bit patterns")
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def gated_rmsnorm(o, z, weight=None, eps=DEFAULT_NORM_EPS, bf16=False, mutation=0):
+    """Gated RMSNorm read-out of "Long-Context Aware Upcycling: A New Frontier for
+    Hybrid LLM Scaling" (arXiv:2604.24715), App. A.3 Eq. 20: the read of the
+    updated state (Eq. 19) is normalised by its root mean square and gated by a
+    projection of the layer input, before the output projection of Eq. 21.
+
+    Read here, per (token, head), over the d_v values of that head:
+
+        y = o / sqrt(mean_v(o_v^2) + eps) * w * silu(z),   silu(x) = x / (1 + e^{-x})
+
+    ``o`` is the read-out [..., H, d_v] (fp64, e.g. this oracle's prefill or
+    decode output, with its 1/sqrt(d_k) scale), ``z`` [..., H, d_v] the gate input
+    W_G x_t (raw bf16 bit patterns when ``bf16``), ``weight`` [d_v] the per-channel
+    scale shared by the heads (None: ones).  The projection W_G itself is not part
+    of this path.  Returns fp64 [..., H, d_v].
+    """
+    o = np.asarray(o, dtype=np.float64)
+    zz = _widen(z, bf16)
+    if zz.shape != o.shape:
+        raise ValueError("z must have the shape of o")
+    w = np.ones(o.shape[-1]) if (weight is None or mutation == 4) else np.asarray(weight, dtype=np.float64)
+    if mutation == 5:
+        ms = np.mean(o * o, axis=(-2, -1), keepdims=True)
+    elif mutation == 2:
+        ms = np.sum(o * o, axis=-1, keepdims=True)
+    else:
+        ms = np.mean(o * o, axis=-1, keepdims=True)
+    e = 0.0 if mutation == 3 else float(eps)
+    sig = 1.0 / (1.0 + np.exp(-zz))
+    gate = sig if mutation == 1 else zz * sig
+    return o / np.sqrt(ms + e) * w * gate

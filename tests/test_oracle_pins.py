@@ -284,3 +284,72 @@ def test_bad_arguments_are_rejected():
     with pytest.raises(RuntimeError):
         oracle.prefill(q, k, v, g, beta, S0, rows=[4])
     assert math.isclose(1.0 / math.sqrt(4), 0.5)
+
+
+# ----------------------------------------------------------------- gated RMSNorm read-out (Eq. 20)
+
+def check_norm_constant_rows(mutation=0):
+    """A row of equal values c with weight w and gate z: y = c / sqrt(c^2 + eps) * w * silu(z),
+    with silu(z) = z / (1 + e^{-z}) written out by hand for z = 0 (0), z = ln 3 (0.75 ln 3)
+    and z = -ln 3 (-0.25 ln 3)."""
+    eps = 1e-3
+    c = np.array([0.02, -0.5, 3.0])[:, None, None] * np.ones((3, 2, 8))  # [token, head, d_v]
+    w = np.linspace(0.5, 2.0, 8)
+    z = np.zeros((3, 2, 8))
+    z[:, 0, :4] = math.log(3.0)
+    z[:, 1, 4:] = -math.log(3.0)
+    y = oracle.gated_rmsnorm(c, z, w, eps=eps, mutation=mutation)
+    gate = np.zeros((3, 2, 8))
+    gate[:, 0, :4] = 0.75 * math.log(3.0)
+    gate[:, 1, 4:] = -0.25 * math.log(3.0)
+    ref = c / np.sqrt(c * c + eps) * w * gate
+    return bool(np.allclose(y, ref, rtol=1e-14, atol=1e-15))
+
+
+def check_norm_unit_rms_per_head(mutation=0):
+    """eps = 0: silu(z) - silu(-z) = z, so y(z) - y(-z) = (o / rms_head(o)) w z, and o / rms
+    has mean square exactly 1 within every (token, head), whatever the scale of each head."""
+    rng = np.random.default_rng(70)
+    o = rng.standard_normal((5, 3, 16)) * np.array([1e-3, 1.0, 40.0])[None, :, None]
+    z = rng.standard_normal((5, 3, 16))
+    w = rng.uniform(0.5, 1.5, 16)
+    d = oracle.gated_rmsnorm(o, z, w, eps=0.0, mutation=mutation) - oracle.gated_rmsnorm(o, -z, w, eps=0.0,
+                                                                                      mutation=mutation)
+    n = d / (w * z)
+    return bool(np.allclose(np.mean(n * n, axis=-1), 1.0, rtol=0, atol=1e-12) and np.all(n * o > 0))
+
+
+def check_norm_scale_invariance(mutation=0):
+    """eps = 0: y(c o) = y(o) for any c > 0 per (token, head), and y = 0 where z = 0."""
+    rng = np.random.default_rng(71)
+    o = rng.standard_normal((4, 2, 12))
+    z = rng.standard_normal((4, 2, 12))
+    z[0, 0, 3] = 0.0
+    c = rng.uniform(0.01, 100.0, (4, 2, 1))
+    y1 = oracle.gated_rmsnorm(o, z, eps=0.0, mutation=mutation)
+    y2 = oracle.gated_rmsnorm(o * c, z, eps=0.0, mutation=mutation)
+    return bool(np.allclose(y1, y2, rtol=1e-13, atol=0) and y1[0, 0, 3] == 0.0)
+
+
+NORM_CHECKS = [check_norm_constant_rows, check_norm_unit_rms_per_head, check_norm_scale_invariance]
+
+
+@pytest.mark.parametrize("check", NORM_CHECKS, ids=lambda c: c.__name__)
+def test_norm_pin(check):
+    assert check()
+
+
+@pytest.mark.parametrize("name", sorted(oracle.NORM_MUTATIONS))
+def test_norm_planted_mistakes_are_caught(name):
+    m = oracle.NORM_MUTATIONS[name]
+    assert not all(check(mutation=m) for check in NORM_CHECKS), name
+
+
+def test_norm_bf16_gate_is_widened_exactly():
+    """bf16 gate inputs are the stored bit patterns: 0x3F80 is 1.0, 0xC000 is -2.0."""
+    z = np.array([[[0x3F80, 0xC000]]], dtype=np.uint16)
+    o = np.array([[[1.0, -1.0]]])
+    y = oracle.gated_rmsnorm(o, z, eps=0.0, bf16=True)
+    ref = np.array([[[1.0 / (1.0 + math.exp(-1.0)), -1.0 * -2.0 / (1.0 + math.exp(2.0))]]])
+    return_ok = np.allclose(y, ref, rtol=1e-15, atol=0)
+    assert return_ok
