@@ -131,12 +131,25 @@ gdn_status gdn_chunk_prefill(const void* q, const void* k, const void* v, const 
                                     workspace_bytes, GDN_STAGE_ALL, stream);
 }
 
-gdn_status gdn_chunk_prefill_staged(const void* q, const void* k, const void* v, const float* g, const float* beta,
-                                    const float* init_state, const int32_t* cu_seqlens,
-                                    const int32_t* cu_seqlens_host, int32_t num_seqs, int64_t total_tokens,
-                                    int32_t H, int32_t dk, int32_t dv, int32_t chunk, gdn_dtype dt, float scale,
-                                    int32_t qk_l2norm, void* o, float* final_state, void* workspace,
-                                    size_t workspace_bytes, int32_t stages, hipStream_t stream)
+}  // extern "C"
+
+namespace {
+
+// Checks of the gated-norm epilogue arguments (z has the layout and type of o).
+gdn_status check_norm(const gdn::GatedNorm& nm, bool need_z)
+{
+    if (!nm.z) return need_z ? GDN_ERR_NULL_ARG : GDN_OK;
+    if (!aligned16(nm.z)) return GDN_ERR_ALIGNMENT;
+    if (nm.w && !aligned4(nm.w)) return GDN_ERR_ALIGNMENT;
+    if (!(nm.eps >= 0.f) || !(nm.eps < INFINITY)) return GDN_ERR_BAD_SHAPE;
+    return GDN_OK;
+}
+
+gdn_status prefill_impl(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                        const float* init_state, const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                        int32_t num_seqs, int64_t total_tokens, int32_t H, int32_t dk, int32_t dv, int32_t chunk,
+                        gdn_dtype dt, float scale, int32_t qk_l2norm, void* o, float* final_state, void* workspace,
+                        size_t workspace_bytes, int32_t stages, const gdn::GatedNorm& norm, hipStream_t stream)
 {
     if (stages < 1 || stages > GDN_STAGE_ALL) return GDN_ERR_BAD_SHAPE;
     if (dt != GDN_F32 && dt != GDN_BF16) return GDN_ERR_UNSUPPORTED;
@@ -180,13 +193,14 @@ gdn_status gdn_chunk_prefill_staged(const void* q, const void* k, const void* v,
     a.ws = (unsigned char*)workspace;
     a.lay = lay;
     a.stages = stages;
+    a.norm = norm;
     a.stream = stream;
     return finish(gdn::launch_prefill(a), stream);
 }
 
-gdn_status gdn_decode_step(const void* q, const void* k, const void* v, const float* g, const float* beta,
-                           float* state, int32_t N, int32_t H, int32_t dk, int32_t dv, gdn_dtype dt, float scale,
-                           int32_t qk_l2norm, void* o, hipStream_t stream)
+gdn_status decode_impl(const void* q, const void* k, const void* v, const float* g, const float* beta, float* state,
+                       int32_t N, int32_t H, int32_t dk, int32_t dv, gdn_dtype dt, float scale, int32_t qk_l2norm,
+                       void* o, const gdn::GatedNorm& norm, hipStream_t stream)
 {
     static const int32_t ds[] = {16, 32, 64, 128, 256};
     static const int32_t dvs[] = {16, 32, 64, 128, 256, 512};
@@ -206,8 +220,67 @@ gdn_status gdn_decode_step(const void* q, const void* k, const void* v, const fl
     a.bf16 = dt == GDN_BF16;
     a.scale = scale > 0.f ? scale : 1.0f / sqrtf((float)dk);
     a.l2norm = qk_l2norm ? 1 : 0;
+    a.norm = norm;
     a.stream = stream;
     return finish(gdn::launch_decode(a), stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_chunk_prefill_staged(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                                    const float* init_state, const int32_t* cu_seqlens,
+                                    const int32_t* cu_seqlens_host, int32_t num_seqs, int64_t total_tokens,
+                                    int32_t H, int32_t dk, int32_t dv, int32_t chunk, gdn_dtype dt, float scale,
+                                    int32_t qk_l2norm, void* o, float* final_state, void* workspace,
+                                    size_t workspace_bytes, int32_t stages, hipStream_t stream)
+{
+    return prefill_impl(q, k, v, g, beta, init_state, cu_seqlens, cu_seqlens_host, num_seqs, total_tokens, H, dk, dv,
+                        chunk, dt, scale, qk_l2norm, o, final_state, workspace, workspace_bytes, stages,
+                        gdn::GatedNorm{}, stream);
+}
+
+gdn_status gdn_chunk_prefill_gated(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                                   const float* init_state, const int32_t* cu_seqlens,
+                                   const int32_t* cu_seqlens_host, int32_t num_seqs, int64_t total_tokens, int32_t H,
+                                   int32_t dk, int32_t dv, int32_t chunk, gdn_dtype dt, float scale,
+                                   int32_t qk_l2norm, const void* gate, const float* norm_weight, float norm_eps,
+                                   void* o, float* final_state, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream)
+{
+    gdn::GatedNorm nm;
+    nm.z = gate;
+    nm.w = norm_weight;
+    nm.eps = norm_eps;
+    const gdn_status st = check_norm(nm, total_tokens > 0);
+    if (st != GDN_OK) return st;
+    if (!nm.z) nm.z = o;  // no tokens: nothing is read
+    return prefill_impl(q, k, v, g, beta, init_state, cu_seqlens, cu_seqlens_host, num_seqs, total_tokens, H, dk, dv,
+                        chunk, dt, scale, qk_l2norm, o, final_state, workspace, workspace_bytes, GDN_STAGE_ALL, nm,
+                        stream);
+}
+
+gdn_status gdn_decode_step(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                           float* state, int32_t N, int32_t H, int32_t dk, int32_t dv, gdn_dtype dt, float scale,
+                           int32_t qk_l2norm, void* o, hipStream_t stream)
+{
+    return decode_impl(q, k, v, g, beta, state, N, H, dk, dv, dt, scale, qk_l2norm, o, gdn::GatedNorm{}, stream);
+}
+
+gdn_status gdn_decode_step_gated(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                                 float* state, int32_t N, int32_t H, int32_t dk, int32_t dv, gdn_dtype dt,
+                                 float scale, int32_t qk_l2norm, const void* gate, const float* norm_weight,
+                                 float norm_eps, void* o, hipStream_t stream)
+{
+    gdn::GatedNorm nm;
+    nm.z = gate;
+    nm.w = norm_weight;
+    nm.eps = norm_eps;
+    const gdn_status st = check_norm(nm, N > 0);
+    if (st != GDN_OK) return st;
+    if (!nm.z) nm.z = o;
+    return decode_impl(q, k, v, g, beta, state, N, H, dk, dv, dt, scale, qk_l2norm, o, nm, stream);
 }
 
 }  // extern "C"

@@ -140,6 +140,37 @@ __global__ __launch_bounds__(256) void decode_kernel(const TIn* __restrict__ q, 
     }
 }
 
+// Gated RMSNorm epilogue of a decode step ("Long-Context Aware Upcycling",
+// App. A.3, Eq. 20): one wave per (sequence, head) output row of d_v values,
+// normalised in place after the step has written it (the step's rows of one
+// head are spread over several workgroups, so the mean square over d_v needs
+// this second, tiny pass; it reads the row as stored, i.e. bf16-rounded for
+// bf16 outputs).
+template <typename TIn>
+__global__ __launch_bounds__(256) void gated_norm_rows_kernel(TIn* __restrict__ o, const TIn* __restrict__ z,
+                                                              const float* __restrict__ w, int64_t rows,
+                                                              int32_t dv, float eps)
+{
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;  // whole waves
+    const int lane = threadIdx.x & (kWave - 1);
+    TIn* orow = o + row * dv;
+    const TIn* zrow = z + row * dv;
+    float ss = 0.f;
+    for (int c = lane; c < dv; c += kWave) {
+        const float x = Elem<TIn>::load(orow, c);
+        ss += x * x;
+    }
+    ss = group_sum<kWave>(ss);
+    const float r = 1.0f / sqrtf(ss / (float)dv + eps);
+    for (int c = lane; c < dv; c += kWave) {
+        const float x = Elem<TIn>::load(orow, c);
+        const float zv = Elem<TIn>::load(zrow, c);
+        const float wv = w ? w[c] : 1.0f;
+        Elem<TIn>::store(orow, c, x * r * wv * (zv / (1.0f + expf(-zv))));
+    }
+}
+
 template <typename TIn, int DK>
 static hipError_t launch_decode_t(const DecodeArgs& a)
 {
@@ -151,6 +182,11 @@ static hipError_t launch_decode_t(const DecodeArgs& a)
     hipLaunchKernelGGL((decode_kernel<TIn, DK>), dim3((uint32_t)blocks), dim3(256), 0, a.stream,
                        (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, a.g, a.beta, a.state, (TIn*)a.o, a.H,
                        a.dv, bph, a.scale, a.l2norm);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !a.norm.z) return e;
+    const int64_t rows = (int64_t)a.N * a.H;
+    hipLaunchKernelGGL((gated_norm_rows_kernel<TIn>), dim3((uint32_t)((rows + 3) / 4)), dim3(256), 0, a.stream,
+                       (TIn*)a.o, (const TIn*)a.norm.z, a.norm.w, rows, a.dv, a.norm.eps);
     return hipGetLastError();
 }
 

@@ -8,6 +8,14 @@
 
 namespace gdn {
 
+// Gated RMSNorm of the read-out (optional epilogue): o <- o / sqrt(mean_v o^2 + eps) * w * silu(z)
+// per (token, head) over the d_v values.  z has the layout and type of o; w is [d_v] fp32 or NULL.
+struct GatedNorm {
+    const void* z = nullptr;  // NULL: no epilogue
+    const float* w = nullptr;
+    float eps = 0.f;
+};
+
 struct DecodeArgs {
     const void *q, *k, *v;
     const float *g, *beta;
@@ -17,6 +25,7 @@ struct DecodeArgs {
     bool bf16;
     float scale;
     int32_t l2norm;
+    GatedNorm norm;
     hipStream_t stream;
 };
 
@@ -58,6 +67,7 @@ struct PrefillArgs {
     unsigned char* ws;
     PrefillLayout lay;
     int32_t stages;  // bit 0: prepare (chunk table + intra-chunk), bit 1: propagate (state chain), bit 2: outputs
+    GatedNorm norm;  // epilogue of the output stage
     hipStream_t stream;
 };
 

@@ -1560,15 +1560,24 @@ struct OutCfg {
     static constexpr int VTW = (VT + 3) / 4;               // value tiles per wave
     static constexpr int VG = VTW < 4 ? VTW : 4;           // tiles per accumulation group
     static constexpr int OP = DV + 16 / (int)sizeof(TIn);  // LDS output row pitch (elements)
+    static constexpr int OPF = DV + 4;                     // fp32 row pitch with the gated epilogue
+    static constexpr size_t lds_bytes(bool gated)
+    {
+        return gated ? (size_t)C * OPF * 4 : (size_t)C * OP * sizeof(TIn);
+    }
 };
 
-template <typename TIn, int C, int DK, int DV>
+// With GATED, the epilogue of App. A.3 Eq. 20 follows the read: every output
+// row (one token and head, d_v values) is staged in fp32, normalised by its
+// root mean square, scaled by the per-channel weight and gated by silu(z).
+template <typename TIn, int C, int DK, int DV, bool GATED>
 __device__ __forceinline__ void output_chunk(const int32_t* __restrict__ header,
                                                      const ChunkInfo* __restrict__ tab, int32_t varlen, int64_t T,
                                                      int32_t H, const unsigned char* __restrict__ records,
                                                      size_t record_bytes, const TIn* __restrict__ states,
                                                      const TIn* __restrict__ deltas, TIn* __restrict__ o, float scale,
-                                                     int64_t c)
+                                                     const TIn* __restrict__ gz, const float* __restrict__ gw,
+                                                     float geps, int64_t c)
 {
     using M = Mma<TIn>;
     using R = Rec<TIn, C, DK, DV>;
@@ -1580,7 +1589,8 @@ __device__ __forceinline__ void output_chunk(const int32_t* __restrict__ header,
     static_assert(G::VTW % G::VG == 0, "value tile groups");
 
     extern __shared__ __align__(16) unsigned char out_lds[];
-    TIn* ot = reinterpret_cast<TIn*>(out_lds);  // [C][OP]
+    TIn* ot = reinterpret_cast<TIn*>(out_lds);     // [C][OP]   (plain read-out)
+    float* otf = reinterpret_cast<float*>(out_lds);  // [C][OPF]  (gated epilogue)
 
     const int h = blockIdx.y;
     if (varlen && c >= header[1]) return;
@@ -1668,11 +1678,46 @@ __device__ __forceinline__ void output_chunk(const int32_t* __restrict__ header,
                 const int vt = wave + 4 * (grp * G::VG + v);
                 if (vt >= G::VT) continue;  // (only when fewer than 4 value tiles)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    ot[(rt * 16 + 4 * g16 + i) * G::OP + vt * 16 + l16] = M::cvt(scale * acc[rt][v][i]);
+                for (int i = 0; i < 4; ++i) {
+                    if constexpr (GATED)
+                        otf[(rt * 16 + 4 * g16 + i) * G::OPF + vt * 16 + l16] = scale * acc[rt][v][i];
+                    else
+                        ot[(rt * 16 + 4 * g16 + i) * G::OP + vt * 16 + l16] = M::cvt(scale * acc[rt][v][i]);
+                }
             }
     }
     __syncthreads();
+    if constexpr (GATED) {
+        // 8 values of a row per thread; the DV/8 threads of a row are adjacent lanes
+        constexpr int G8 = DV / 8;
+        static_assert(G8 >= 2 && G8 <= 64 && (G8 & (G8 - 1)) == 0, "a row's threads are aligned lanes of one wave");
+        for (int u = tid; u < C * G8; u += 256) {
+            const int row = u / G8, q8 = u % G8;
+            const float* src = otf + row * G::OPF + q8 * 8;
+            const f32x4 a = *reinterpret_cast<const f32x4*>(src);
+            const f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
+            float ss = a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w + b.x * b.x + b.y * b.y + b.z * b.z + b.w * b.w;
+            ss = group_sum<G8>(ss);
+            const float r = 1.0f / sqrtf(ss / (float)DV + geps);
+            if (row < ci.len) {
+                const int64_t base = ((int64_t)(ci.tok0 + row) * H + h) * DV + q8 * 8;
+                float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+                float zv[8];
+                const f32x4 z0 = Elem<TIn>::load4(gz, base), z1 = Elem<TIn>::load4(gz, base + 4);
+                zv[0] = z0.x; zv[1] = z0.y; zv[2] = z0.z; zv[3] = z0.w;
+                zv[4] = z1.x; zv[5] = z1.y; zv[6] = z1.z; zv[7] = z1.w;
+                float y[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float wv = gw ? gw[q8 * 8 + e] : 1.0f;
+                    y[e] = x[e] * r * wv * (zv[e] / (1.0f + expf(-zv[e])));
+                }
+                Quad<TIn>::store(o + base, f32x4{y[0], y[1], y[2], y[3]});
+                Quad<TIn>::store(o + base + 4, f32x4{y[4], y[5], y[6], y[7]});
+            }
+        }
+        return;
+    }
     // rows of the output tile -> o, 16 bytes per lane
     constexpr int UROW = DV * (int)EB / 16;
     const __amdgpu_buffer_rsrc_t ro =
@@ -1684,17 +1729,19 @@ __device__ __forceinline__ void output_chunk(const int32_t* __restrict__ header,
     }
 }
 
-template <typename TIn, int C, int DK, int DV>
+template <typename TIn, int C, int DK, int DV, bool GATED>
 __global__ __launch_bounds__(256) void output_kernel(const int32_t* __restrict__ header,
                                                      const ChunkInfo* __restrict__ tab, int32_t varlen, int64_t T,
                                                      int32_t H, const unsigned char* __restrict__ records,
                                                      size_t record_bytes, const TIn* __restrict__ states,
                                                      const TIn* __restrict__ deltas, TIn* __restrict__ o, float scale,
-                                                     int64_t c_base, int64_t c_end)
+                                                     const TIn* __restrict__ gz, const float* __restrict__ gw,
+                                                     float geps, int64_t c_base, int64_t c_end)
 {
     const int64_t c = c_base + blockIdx.x;
     if (c >= c_end) return;
-    output_chunk<TIn, C, DK, DV>(header, tab, varlen, T, H, records, record_bytes, states, deltas, o, scale, c);
+    output_chunk<TIn, C, DK, DV, GATED>(header, tab, varlen, T, H, records, record_bytes, states, deltas, o, scale,
+                                        gz, gw, geps, c);
 }
 
 // ------------------------------------------------------------------ dispatch
@@ -1796,17 +1843,25 @@ static hipError_t run_prefill(const PrefillArgs& a)
     };
     auto launch_output = [&](int64_t c0, int64_t c1, hipStream_t st) -> hipError_t {
         if (c1 <= c0) return hipSuccess;
-        const size_t smem = (size_t)C * OutCfg<TIn, C, DK, DV>::OP * sizeof(TIn);
-        static bool attr = false;  // idempotent attribute; racing writers store the same value
-        if (!attr) {
-            hipError_t e = hipFuncSetAttribute((const void*)output_kernel<TIn, C, DK, DV>,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        const bool gated = a.norm.z != nullptr;
+        const size_t smem = OutCfg<TIn, C, DK, DV>::lds_bytes(gated);
+        const void* fn = gated ? (const void*)output_kernel<TIn, C, DK, DV, true>
+                               : (const void*)output_kernel<TIn, C, DK, DV, false>;
+        static bool attr[2] = {false, false};  // idempotent attributes; racing writers store the same value
+        if (!attr[gated]) {
+            hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
             if (e != hipSuccess) return e;
-            attr = true;
+            attr[gated] = true;
         }
-        hipLaunchKernelGGL((output_kernel<TIn, C, DK, DV>), dim3((uint32_t)(c1 - c0), a.H), dim3(256),
-                           smem, st, header, tab, varlen, a.T, a.H, records, a.lay.record_bytes, states, deltas,
-                           (TIn*)a.o, a.scale, c0, c1);
+        const dim3 grid((uint32_t)(c1 - c0), a.H);
+        if (gated)
+            hipLaunchKernelGGL((output_kernel<TIn, C, DK, DV, true>), grid, dim3(256), smem, st, header, tab, varlen,
+                               a.T, a.H, records, a.lay.record_bytes, states, deltas, (TIn*)a.o, a.scale,
+                               (const TIn*)a.norm.z, a.norm.w, a.norm.eps, c0, c1);
+        else
+            hipLaunchKernelGGL((output_kernel<TIn, C, DK, DV, false>), grid, dim3(256), smem, st, header, tab, varlen,
+                               a.T, a.H, records, a.lay.record_bytes, states, deltas, (TIn*)a.o, a.scale,
+                               (const TIn*)nullptr, (const float*)nullptr, 0.f, c0, c1);
         return hipGetLastError();
     };
 #define GDN_TRY(x)                       \

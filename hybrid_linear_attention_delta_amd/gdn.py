@@ -20,6 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdn_mi355x.so")
 
 GDN_F32, GDN_BF16 = 0, 1
+DEFAULT_NORM_EPS = 1e-6
 STAGE_PREPARE, STAGE_PROPAGATE, STAGE_OUTPUT, STAGE_ALL = 1, 2, 4, 7
 STATUS = {
     0: "GDN_OK", 1: "GDN_ERR_NULL_ARG", 2: "GDN_ERR_BAD_SHAPE", 3: "GDN_ERR_UNSUPPORTED",
@@ -59,6 +60,12 @@ def load_library(path: str | None = None):
             lib.gdn_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int, f32, i32,
                                             vp, vp]
             lib.gdn_decode_step.restype = ctypes.c_int
+            lib.gdn_chunk_prefill_gated.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32,
+                                                    ctypes.c_int, f32, i32, vp, vp, f32, vp, vp, vp, sz, vp]
+            lib.gdn_chunk_prefill_gated.restype = ctypes.c_int
+            lib.gdn_decode_step_gated.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int, f32,
+                                                  i32, vp, vp, f32, vp, vp]
+            lib.gdn_decode_step_gated.restype = ctypes.c_int
             lib.gdn_status_string.argtypes = [ctypes.c_int]
             lib.gdn_status_string.restype = ctypes.c_char_p
             lib.gdn_version.argtypes = []
@@ -112,8 +119,20 @@ def prefill_workspace_size(total_tokens: int, num_seqs: int, H: int, dk: int, dv
     return int(load_library().gdn_prefill_workspace_size(total_tokens, num_seqs, H, dk, dv, chunk, code))
 
 
+def _norm_args(gate, norm_weight, shape, dt, dev):
+    torch = _torch()
+    _check(gate, "gate", dtype=dt, device=dev)
+    if tuple(gate.shape) != tuple(shape):
+        raise ValueError(f"gate must be {list(shape)}")
+    if norm_weight is not None:
+        _check(norm_weight, "norm_weight", dtype=torch.float32, device=dev)
+        if tuple(norm_weight.shape) != (shape[-1],):
+            raise ValueError(f"norm_weight must be [{shape[-1]}]")
+
+
 def chunk_prefill(q, k, v, g, beta, init_state=None, cu_seqlens=None, scale=None, qk_l2norm=True, chunk=64,
-                  out=None, final_state=None, workspace=None, return_final_state=True, stages=STAGE_ALL):
+                  out=None, final_state=None, workspace=None, return_final_state=True, stages=STAGE_ALL,
+                  gate=None, norm_weight=None, norm_eps=DEFAULT_NORM_EPS):
     """Chunked gated delta-rule prefill over packed sequences.
 
     q, k [T, H, dk]; v [T, H, dv] (bf16 or fp32, same dtype); g, beta [T, H] fp32;
@@ -121,7 +140,9 @@ def chunk_prefill(q, k, v, g, beta, init_state=None, cu_seqlens=None, scale=None
     tensor) or None for one sequence.  Returns (o [T, H, dv], final_state [N, H, dv, dk]).
     ``stages`` is a bit set of STAGE_PREPARE / STAGE_PROPAGATE / STAGE_OUTPUT (STAGE_ALL:
     all three; see include/gdn.h); a later stage must get the workspace of the earlier
-    ones on the same inputs.
+    ones on the same inputs.  With ``gate`` [T, H, dv] (dtype of q) the outputs get the
+    gated RMSNorm read-out of App. A.3 Eq. 20 (``norm_weight`` [dv] fp32 or None,
+    ``norm_eps``); it needs all stages in one call.
     """
     torch = _torch()
     lib = load_library()
@@ -170,6 +191,18 @@ def chunk_prefill(q, k, v, g, beta, init_state=None, cu_seqlens=None, scale=None
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     s = -1.0 if scale is None else float(scale)
     cu_host_ptr = None if cu_host is None else ctypes.c_void_p(cu_host.data_ptr())
+    if gate is not None:
+        if stages != STAGE_ALL:
+            raise ValueError("the gated read-out needs all stages in one call")
+        _norm_args(gate, norm_weight, (T, H, dv), dt, dev)
+        st = lib.gdn_chunk_prefill_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(init_state),
+                                         _ptr(cu_dev), cu_host_ptr, N, T, H, dk, dv, chunk, code, s,
+                                         int(bool(qk_l2norm)), _ptr(gate), _ptr(norm_weight), float(norm_eps),
+                                         _ptr(out), _ptr(final_state), _ptr(workspace), workspace.numel(),
+                                         _stream(dev))
+        if st != 0:
+            raise GdnError(st, "gdn_chunk_prefill_gated")
+        return out, final_state
     st = lib.gdn_chunk_prefill_staged(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(init_state),
                                       _ptr(cu_dev), cu_host_ptr, N, T, H, dk, dv, chunk, code, s,
                                       int(bool(qk_l2norm)), _ptr(out), _ptr(final_state), _ptr(workspace),
@@ -179,9 +212,11 @@ def chunk_prefill(q, k, v, g, beta, init_state=None, cu_seqlens=None, scale=None
     return out, final_state
 
 
-def decode_step(q, k, v, g, beta, state, scale=None, qk_l2norm=True, out=None):
+def decode_step(q, k, v, g, beta, state, scale=None, qk_l2norm=True, out=None, gate=None, norm_weight=None,
+                norm_eps=DEFAULT_NORM_EPS):
     """One recurrent decode step: q, k [N, H, dk]; v [N, H, dv]; g, beta [N, H] fp32;
-    state [N, H, dv, dk] fp32 updated in place.  Returns o [N, H, dv]."""
+    state [N, H, dv, dk] fp32 updated in place.  Returns o [N, H, dv].  With ``gate``
+    [N, H, dv] the output gets the gated RMSNorm read-out (App. A.3 Eq. 20)."""
     torch = _torch()
     lib = load_library()
     dev = q.device
@@ -199,6 +234,14 @@ def decode_step(q, k, v, g, beta, state, scale=None, qk_l2norm=True, out=None):
     if out is None:
         out = torch.empty((N, H, dv), dtype=dt, device=dev)
     s = -1.0 if scale is None else float(scale)
+    if gate is not None:
+        _norm_args(gate, norm_weight, (N, H, dv), dt, dev)
+        st = lib.gdn_decode_step_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), N, H, dk, dv,
+                                       _dtype_code(q), s, int(bool(qk_l2norm)), _ptr(gate), _ptr(norm_weight),
+                                       float(norm_eps), _ptr(out), _stream(dev))
+        if st != 0:
+            raise GdnError(st, "gdn_decode_step_gated")
+        return out
     st = lib.gdn_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), N, H, dk, dv,
                              _dtype_code(q), s, int(bool(qk_l2norm)), _ptr(out), _stream(dev))
     if st != 0:

@@ -157,6 +157,16 @@ def decode_step_inputs(N: int, H: int, dk: int, dv: int, dtype: str, seed: int, 
     return q, k, v, g, beta
 
 
+def norm_inputs(shape, dtype: str, seed: int):
+    """Inputs of the gated read-out: the gate input z ~ N(0, 1) of the given shape
+    [..., d_v] stored in `dtype`, and a per-channel weight U(0.5, 1.5) [d_v] fp32."""
+    ss = np.random.SeedSequence([seed, 7919])
+    rz, rw = [np.random.default_rng(s) for s in ss.spawn(2)]
+    z = _store(rz.standard_normal(tuple(shape)), dtype)
+    w = rw.uniform(0.5, 1.5, size=shape[-1]).astype(np.float32)
+    return z, w
+
+
 def varlen_lengths(seed: int, n_seqs: int = 16, total: int = 2_097_152, lo: int = 4096,
                    hi: int = 524_288) -> np.ndarray:
     """Sequence lengths drawn log-uniform on [lo, hi], redrawn until the sum is

@@ -157,6 +157,41 @@ gdn_status gdn_decode_step(const void* q, const void* k, const void* v, const fl
                            float* state, int32_t N, int32_t H, int32_t dk, int32_t dv, gdn_dtype dt,
                            float scale, int32_t qk_l2norm, void* o, hipStream_t stream);
 
+/*
+ * Gated RMSNorm read-out (App. A.3, Eq. 20: the read of the updated state is
+ * normalised and gated by a projection of the layer input before the output
+ * projection of Eq. 21).  Same as gdn_chunk_prefill / gdn_decode_step, except
+ * that every output row -- one token and head, d_v values -- becomes
+ *
+ *     y = o / sqrt(mean_v(o_v^2) + norm_eps) * norm_weight * silu(gate)
+ *
+ * with o the read of Eq. 19 (scale included) and silu(x) = x / (1 + e^{-x}).
+ *
+ *   gate        [tokens (or N), H, dv]  dt, the gate input W_G x_t (the
+ *               projection itself is the caller's), 16-byte aligned; required
+ *               when there is at least one token
+ *   norm_weight [dv] fp32 per-channel weight shared by all heads, 4-byte
+ *               aligned, or NULL for ones
+ *   norm_eps    >= 0 and finite (GDN_ERR_BAD_SHAPE otherwise)
+ *
+ * The prefill applies the norm to the fp32 outputs inside its output stage.
+ * The decode step applies it in a second small kernel to the row as stored in
+ * o (rounded to bf16 when dt is GDN_BF16), since one head's rows are spread
+ * over several workgroups.
+ */
+gdn_status gdn_chunk_prefill_gated(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                                   const float* init_state, const int32_t* cu_seqlens,
+                                   const int32_t* cu_seqlens_host, int32_t num_seqs, int64_t total_tokens, int32_t H,
+                                   int32_t dk, int32_t dv, int32_t chunk, gdn_dtype dt, float scale,
+                                   int32_t qk_l2norm, const void* gate, const float* norm_weight, float norm_eps,
+                                   void* o, float* final_state, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
+
+gdn_status gdn_decode_step_gated(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                                 float* state, int32_t N, int32_t H, int32_t dk, int32_t dv, gdn_dtype dt,
+                                 float scale, int32_t qk_l2norm, const void* gate, const float* norm_weight,
+                                 float norm_eps, void* o, hipStream_t stream);
+
 /* Static, human-readable name of a status code. */
 const char* gdn_status_string(gdn_status s);
 

@@ -53,3 +53,22 @@ def bound_ratio(x, ref, tol, stored_bf16=False) -> float:
     allow = tol * rms + (BF16_STORE if stored_bf16 else 0.0) * np.abs(ref)
     allow = np.maximum(allow, np.finfo(np.float64).tiny)
     return float(np.max(np.abs(x - ref) / allow))
+
+
+def gated_bound_ratio(y, y_ref, gate, tol, stored_bf16=False) -> float:
+    """Bound for the gated RMSNorm read-out y = n * gate, n = o / rms_row(o) (unit mean
+    square per token and head), gate = w * silu(z) exact per element: the read-out
+    bound tol, taken per row, carried through the gate factor, plus the bf16
+    storage rounding of y itself (and of o, where the decode step's second pass
+    reads the stored row):
+        |y - y_ref| <= tol * |gate| + 2^-8 * |y_ref|
+    Returns the max over elements of |y - y_ref| / allowance; must be <= 1."""
+    y = np.asarray(y, dtype=np.float64)
+    y_ref = np.asarray(y_ref, dtype=np.float64)
+    if y.size == 0:
+        return 0.0
+    if not np.all(np.isfinite(y)):
+        return float("inf")
+    allow = tol * np.abs(np.asarray(gate, dtype=np.float64)) + (BF16_STORE if stored_bf16 else 0.0) * np.abs(y_ref)
+    allow = np.maximum(allow, np.finfo(np.float64).tiny)
+    return float(np.max(np.abs(y - y_ref) / allow))

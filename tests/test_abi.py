@@ -139,3 +139,26 @@ def test_product_path_does_not_import_the_oracle():
                 txt = open(os.path.join(dirpath, fn)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle\b", txt, flags=re.M), fn
                 assert "gdn_oracle" not in txt, fn
+
+
+def test_gated_entry_points_reject_bad_norm_arguments(lib):
+    """The gated read-out checks its own arguments first: a missing gate, a gate
+    or weight off alignment, and a negative or non-finite eps return before any
+    launch."""
+    f = _fake()
+    base = [f, f, f, f, f, None, None, None, 1, 128, 2, 64, 64, 64, gdn.GDN_BF16, -1.0, 1]
+    tail = [f, None, _fake(0x100000), 1 << 40, None]
+    call = lambda gate, w, eps: lib.gdn_chunk_prefill_gated(*base, gate, w, eps, *tail)
+    assert call(None, None, 1e-6) == 1           # GDN_ERR_NULL_ARG
+    assert call(_fake(0x10008), None, 1e-6) == 5  # GDN_ERR_ALIGNMENT (gate)
+    assert call(f, _fake(0x10002), 1e-6) == 5     # GDN_ERR_ALIGNMENT (weight)
+    assert call(f, None, -1e-3) == 2              # GDN_ERR_BAD_SHAPE
+    assert call(f, None, float("inf")) == 2
+    assert call(f, None, float("nan")) == 2
+    dec = lambda gate, eps: lib.gdn_decode_step_gated(f, f, f, f, f, f, 4, 2, 64, 64, gdn.GDN_BF16, -1.0, 1, gate,
+                                                      None, eps, f, None)
+    assert dec(None, 1e-6) == 1
+    assert dec(f, -1.0) == 2
+    # nothing to do: no tokens / no sequences, no gate needed
+    assert lib.gdn_decode_step_gated(f, f, f, f, f, f, 0, 2, 64, 64, gdn.GDN_BF16, -1.0, 1, None, None, 1e-6, f,
+                                     None) == 0
