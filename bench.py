@@ -155,8 +155,26 @@ def bench_prefill(torch, gdn, synth, steps, warmup):
     log(f"[bench] prefill {steps} steps: {total_ms / steps:.3f} ms/step; wall {wall / steps * 1e3:.3f} ms/step; "
         f"stage by stage: prepare {stage_ms[0]:.3f}, chain {stage_ms[1]:.3f}, output {stage_ms[2]:.3f} "
         f"(sum {sum(stage_ms):.3f})")
+
+    # --- the same prefill with the gated RMSNorm read-out (App. A.3 Eq. 20)
+    #     fused into its output stage
+    z, w = synth.norm_inputs((T, H, DV), "bf16", synth.seed_for("prefill64k"))
+    zt = synth.to_torch(z, dev, bf16=True)
+    wt = synth.to_torch(w, dev)
+    gated = lambda: gdn.chunk_prefill(q, k, v, g, beta, chunk=C, out=o, final_state=fs, workspace=ws, gate=zt,
+                                      norm_weight=wt)
+    for _ in range(max(1, warmup)):
+        gated()
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(steps):
+        gated()
+    t1.record()
+    torch.cuda.synchronize()
+    gated_ms = t0.elapsed_time(t1) / steps
+    log(f"[bench] gated prefill {steps} steps: {gated_ms:.3f} ms/step")
     return dict(ms_per_step=total_ms / steps, wall_ms_per_step=wall * 1e3 / steps, prepare_ms=stage_ms[0],
-                chain_ms=stage_ms[1], output_ms=stage_ms[2], staged_ms=sum(stage_ms), inputs=inp)
+                chain_ms=stage_ms[1], output_ms=stage_ms[2], staged_ms=sum(stage_ms), gated_ms=gated_ms, inputs=inp)
 
 
 def bench_decode(torch, gdn, synth, n_steps, warmup=3):
@@ -187,7 +205,17 @@ def bench_decode(torch, gdn, synth, n_steps, warmup=3):
     times.sort()
     med = times[len(times) // 2]
     log(f"[bench] decode {n_steps} steps: mean {ms * 1e3:.1f} us/step, median {med * 1e3:.1f} us/step")
-    return dict(ms_per_step=ms, median_ms=med)
+    # the same steps with the gated RMSNorm read-out (its second small kernel)
+    z, w = synth.norm_inputs((DEC_N, H, DV), "bf16", seed)
+    zt, wt = synth.to_torch(z, dev, bf16=True), synth.to_torch(w, dev)
+    evs[0].record()
+    for s in range(n_steps):
+        gdn.decode_step(*per_step[s], state, out=o, gate=zt, norm_weight=wt)
+    evs[1].record()
+    torch.cuda.synchronize()
+    gated = evs[0].elapsed_time(evs[1]) / n_steps
+    log(f"[bench] gated decode {n_steps} steps: mean {gated * 1e3:.1f} us/step")
+    return dict(ms_per_step=ms, median_ms=med, gated_ms=gated)
 
 
 def cpu_baseline(inp, max_threads=16):
@@ -277,6 +305,8 @@ def main():
             "algorithmic_flops_per_token": flops_path_per_token(),
             "traffic": {"intra_kernel": traffic_from_profiles("intra_kernel"),
                         "output_kernel": traffic_from_profiles("output_kernel")},
+            "gated_rmsnorm": {"ms_per_step": pre["gated_ms"], "tokens_per_s": T / (pre["gated_ms"] / 1e3),
+                              "overhead_ms": pre["gated_ms"] - pre["ms_per_step"]},
         },
     }
     if dec is not None:
@@ -288,6 +318,7 @@ def main():
                         f"{a.decode_steps} steps",
             "ms_per_step": dec["ms_per_step"],
             "median_ms_per_step": dec["median_ms"],
+            "gated_rmsnorm_ms_per_step": dec["gated_ms"],
             "tokens_per_s": DEC_N / (dec["ms_per_step"] / 1e3),
             "state_GBps": state_gbps,
             "roofline": {"kernel": "decode_kernel", "bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_GBPS,
