@@ -51,6 +51,7 @@
 //             the transposed product hands a lane, so results can be stored
 //             as next-stage operands without a shuffle.
 #include <stdlib.h>
+#include <string.h>
 
 #include <algorithm>
 #include <mutex>
@@ -1176,9 +1177,7 @@ struct ChainLds {
     static constexpr int NS = R::SPLIT ? 2 : 1;
     static constexpr int RT = C / 16;
     // operand fragment slots (1 KB each: 64 lanes x 16 B, lane order)
-    static constexpr int F_W = 0;                          // [RT][DKS] W
-    static constexpr int F_K = F_W + RT * R::DKS;          // [MT][CKS] K^T
-    static constexpr int F_U = F_K + R::MT * R::CKS;       // [RT] U (this workgroup's 16 value columns)
+    static constexpr int F_U = 0;                          // [RT] U (this workgroup's 16 value columns)
     static constexpr int F_SINK = F_U + RT;                // landing slot of prefetch transfers
     static constexpr int NFRAG = STAGE ? F_SINK + 1 : 1;
     unsigned char frag[NFRAG][1024];
@@ -1306,54 +1305,21 @@ __global__ __launch_bounds__((NW + chain_loaders<TIn, C>()) * 64) void chain_ker
     if (loader) {
         if constexpr (STAGE) {
             constexpr int NOP = NL - 1;  // operand loaders
-            constexpr int NWF = RT * R::DKS, NKF = R::MT * R::CKS;
-            constexpr int NWL = (NWF + NOP - 1) / NOP, NKL = (NKF + NOP - 1) / NOP;
             constexpr int L_KSC = RT % NOP, L_META = (RT + 1) % NOP;
             static_assert(RT + 2 <= NOP && NOP >= 7, "one loader per U tile, distinct row-vector loaders");
-            struct GroupU { u32x4 u; uint32_t x; };
-            struct GroupK { u32x4 f[NKL]; uint32_t x; };
-            struct GroupW { u32x4 f[NWL]; };
+            struct GroupU { u32x4 u; uint32_t x, m; };
             // Every loader issues the same loads and stores; a wave without the role
             // reads a duplicate or stores through an empty view (dropped).
             auto load_u = [&](int64_t c, GroupU& g) {
                 const unsigned char* rb = rec_ptr(c);
                 g.u = buf_load16(make_rsrc(rb, (uint32_t)R::BYTES), lane_b, u_src(lw % RT));
                 g.x = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(rb + R::KSC_BYTE_OFF, C * 4), lane * 4, 0, 0);
+                g.m = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(rb + R::DEC_BYTE_OFF, 16), lane * 4, 0, 0);
             };
             auto write_u = [&](const GroupU& g) {
                 if (lw < RT) *reinterpret_cast<u32x4*>(sm.frag[L::F_U + lw] + lane_b) = g.u;
                 if (lw == L_KSC) reinterpret_cast<uint32_t*>(sm.ksc)[lane] = g.x;
-            };
-            auto load_k = [&](int64_t c, GroupK& g) {
-                const unsigned char* rb = rec_ptr(c);
-                const __amdgpu_buffer_rsrc_t r = make_rsrc(rb, (uint32_t)R::BYTES);
-#pragma unroll
-                for (int i = 0; i < NKL; ++i) {
-                    const int f = min(lw + NOP * i, NKF - 1);
-                    g.f[i] = buf_load16(r, lane_b, k_src(f / R::CKS, f % R::CKS));
-                }
-                g.x = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(rb + R::DEC_BYTE_OFF, 16), lane * 4, 0, 0);
-            };
-            auto write_k = [&](const GroupK& g) {
-#pragma unroll
-                for (int i = 0; i < NKL; ++i) {
-                    const int f = min(lw + NOP * i, NKF - 1);
-                    *reinterpret_cast<u32x4*>(sm.frag[L::F_K + f] + lane_b) = g.f[i];
-                }
-                if (lw == L_META) reinterpret_cast<uint32_t*>(sm.meta)[lane] = g.x;  // lanes >= 4 write 0
-            };
-            auto load_w = [&](int64_t c, GroupW& g) {
-                const __amdgpu_buffer_rsrc_t r = make_rsrc(rec_ptr(c), (uint32_t)R::BYTES);
-#pragma unroll
-                for (int i = 0; i < NWL; ++i) {
-                    const int f = min(lw + NOP * i, NWF - 1);
-                    g.f[i] = buf_load16(r, lane_b, w_src(f / R::DKS, f % R::DKS));
-                }
-            };
-            auto write_w = [&](const GroupW& g) {
-#pragma unroll
-                for (int i = 0; i < NWL; ++i)
-                    *reinterpret_cast<u32x4*>(sm.frag[L::F_W + min(lw + NOP * i, NWF - 1)] + lane_b) = g.f[i];
+                if (lw == L_META) reinterpret_cast<uint32_t*>(sm.meta)[lane] = g.m;  // lanes >= 4 write 0
             };
             // LDS rows -> global rows, 16 bytes per lane
             constexpr int SROW = DK * (int)EB / 16;          // 16-byte units per state row
@@ -1404,7 +1370,6 @@ __global__ __launch_bounds__((NW + chain_loaders<TIn, C>()) * 64) void chain_ker
                 __syncthreads();
                 for (int64_t c = c_begin; c < c_end; ++c) {
                     if (c + 2 < c_end) prefetch(c + 2);
-                    lds_barrier();  // ---- A
                     lds_barrier();  // ---- B
                     lds_barrier();  // ---- C
                 }
@@ -1412,34 +1377,21 @@ __global__ __launch_bounds__((NW + chain_loaders<TIn, C>()) * 64) void chain_ker
                 return;
             }
             const int64_t last = c_end - 1;
-            GroupK gk;  // K^T, meta of the next chunk to write
-            GroupW gw;  // W of the chunk after the current one
             if (c_begin < c_end) {
                 GroupU gu;
-                GroupW w0;
                 load_u(c_begin, gu);
-                load_w(c_begin, w0);
-                load_k(c_begin, gk);
-                load_w(min(c_begin + 1, last), gw);
                 write_u(gu);
-                write_w(w0);
             }
             __syncthreads();  // the compute waves have written the initial state rows
             for (int64_t c = c_begin; c < c_end; ++c) {
                 GroupU gu;
                 // ---- phase 1 of c
-                write_k(gk);
                 store_state(c);
                 load_u(min(c + 1, last), gu);
-                lds_barrier();  // ---- A
-                // ---- phase 2 of c
-                load_k(min(c + 1, last), gk);
-                write_w(gw);
                 lds_barrier();  // ---- B
-                // ---- phase 3 of c
+                // ---- phase 2 of c (U, the scales and the decay of c were read in phase 1)
                 write_u(gu);
                 store_delta(c);
-                load_w(min(c + 2, last), gw);
                 lds_barrier();  // ---- C
             }
             wait_vmcnt<0>();
@@ -1448,15 +1400,43 @@ __global__ __launch_bounds__((NW + chain_loaders<TIn, C>()) * 64) void chain_ker
     }
 
     // ---------------------------------------------------------------- compute waves
-    // fragment of the current chunk: LDS slot `f` (staged) or record byte offset `src` (direct)
+    // general form: fragment of the current chunk at record byte offset `src`
     __amdgpu_buffer_rsrc_t rcur = make_rsrc(records, 0u);
-    auto frag = [&](int f, uint32_t src) -> Frag {
-        if constexpr (STAGE) return *reinterpret_cast<const Frag*>(sm.frag[f] + lane_b);
-        else return __builtin_bit_cast(Frag, buf_load16(rcur, lane_b, src));
-    };
+    auto frag = [&](int, uint32_t src) -> Frag { return __builtin_bit_cast(Frag, buf_load16(rcur, lane_b, src)); };
     const int rt = wave & 3, kq = wave >> 2;
     const bool p1 = rt < RT && kq < P::KQ;   // phase-1 partial products
     const bool fin_d = rt < RT && kq == 0;   // Delta finaliser of row tile rt
+    // Staged form: every compute wave reads its own W and K^T fragments (each is
+    // used by exactly one wave) straight into registers, one chunk ahead of use;
+    // the loads are the same on every compute wave (tile indices past the end are
+    // clamped), so the compiler's vmcnt waits stay exact.  The prefetch wave has
+    // brought them into L2 two chunks earlier.
+    Frag wreg[STAGE ? R::DKS : 1], kreg[STAGE ? P::MTW : 1][STAGE ? R::CKS : 1];
+    auto load_wk_w = [&](int64_t cc) {  // the W row tile of waves 0 .. RT-1
+        if constexpr (STAGE) {
+            if (wave < RT) {
+                const __amdgpu_buffer_rsrc_t r = make_rsrc(rec_ptr(cc), (uint32_t)R::BYTES);
+#pragma unroll
+                for (int ks = 0; ks < R::DKS; ++ks) {
+                    const uint32_t src = w_src(wave, ks);
+                    wreg[ks] = __builtin_bit_cast(Frag, buf_load16(r, lane_b, src));
+                }
+            }
+        }
+    };
+    auto load_wk_k = [&](int64_t cc) {
+        if constexpr (STAGE) {
+            const __amdgpu_buffer_rsrc_t r = make_rsrc(rec_ptr(cc), (uint32_t)R::BYTES);
+#pragma unroll
+            for (int a = 0; a < P::MTW; ++a)
+#pragma unroll
+                for (int ks = 0; ks < R::CKS; ++ks) {
+                    const uint32_t src = k_src(min(wave + NW * a, R::MT - 1), ks);
+                    kreg[a][ks] = __builtin_bit_cast(Frag, buf_load16(r, lane_b, src));
+                }
+        }
+    };
+    const int64_t last_c = c_end - 1;
 
     // state tiles S^T[mt] in result layout: lane holds S[row0 + l16][mt*16 + 4*g16 + i]
     f32x4 S[P::MTW];
@@ -1472,10 +1452,62 @@ __global__ __launch_bounds__((NW + chain_loaders<TIn, C>()) * 64) void chain_ker
             store_quad<TIn, false>(sm.sr + l16 * SP + quad_pos<TIn>(mt, g16), nullptr, S[a]);
         }
     }
+    if (c_begin < c_end) {
+        load_wk_w(c_begin);
+        load_wk_k(c_begin);
+    }
     __syncthreads();
 
-    for (int64_t c = c_begin; c < c_end; ++c) {
-        if constexpr (!STAGE) {
+    if constexpr (STAGE) {
+        // Two phases per chunk: waves 0 .. RT-1 form X = W S^T of their row tile
+        // over all of d_k (two accumulators) and Delta = U - X at once; then
+        // every wave updates its state tiles.
+        for (int64_t c = c_begin; c < c_end; ++c) {
+            if (wave < RT) {
+                // ---- phase 1: Delta of row tile `wave` (sigma-ordered dt, natural-order ds)
+                f32x4 X0 = {0.f, 0.f, 0.f, 0.f}, X1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < R::DKS; ks += 2) {
+                    X0 = M::mma(wreg[ks], *reinterpret_cast<const Frag*>(sm.sr + l16 * SP + ks * KS + g16 * E), X0);
+                    if (ks + 1 < R::DKS)
+                        X1 = M::mma(wreg[ks + 1],
+                                    *reinterpret_cast<const Frag*>(sm.sr + l16 * SP + (ks + 1) * KS + g16 * E), X1);
+                }
+                const f32x4 ks4 = *reinterpret_cast<const f32x4*>(sm.ksc + wave * 16 + 4 * g16);
+                const f32x4 d = __builtin_bit_cast(f32x4, *reinterpret_cast<const u32x4*>(sm.frag[L::F_U + wave] + lane_b)) -
+                                (X0 + X1);
+                const int pd = l16 * DP + quad_pos<TIn>(wave, g16);
+                const int pn = l16 * DP + wave * 16 + 4 * g16;
+                store_quad<TIn, SPL>(sm.dt[0] + pd, sm.dt[NS - 1] + pd, d);
+                store_quad<TIn, SPL>(sm.ds[0] + pn, sm.ds[NS - 1] + pn, d * ks4);
+            }
+            load_wk_w(min(c + 1, last_c));
+            const float decay = sm.meta[0].x;  // read before the loaders refill its slot
+            lds_barrier();  // ---- B: Delta visible; U, scales and decay free
+
+            // ---- phase 2: state update on this wave's d_k tiles
+#pragma unroll
+            for (int a = 0; a < P::MTW; ++a) {
+                const int mt = wave + NW * a;
+                if (mt >= R::MT) continue;
+                f32x4 acc0 = S[a] * decay, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < R::CKS; ++ks) {
+                    const int doff = l16 * DP + ks * KS + g16 * E;
+                    acc0 = M::mma(kreg[a][ks], *reinterpret_cast<const Frag*>(sm.ds[0] + doff), acc0);
+                    acc1 = M::mma(kreg[a][ks], *reinterpret_cast<const Frag*>(sm.ds[1] + doff), acc1);
+                }
+                S[a] = acc0 + acc1;
+                store_quad<TIn, false>(sm.sr + l16 * SP + quad_pos<TIn>(mt, g16), nullptr, S[a]);
+            }
+            load_wk_k(min(c + 1, last_c));
+            lds_barrier();  // ---- C: state copy visible
+        }
+    }
+    if constexpr (!STAGE) {
+        // General form (fp32 operands): three phases per chunk, operands read
+        // from the record directly.
+        for (int64_t c = c_begin; c < c_end; ++c) {
             rcur = make_rsrc(rec_ptr(c), (uint32_t)R::BYTES);
             // the state entering chunk c (fp32, natural order)
 #pragma unroll
@@ -1484,57 +1516,51 @@ __global__ __launch_bounds__((NW + chain_loaders<TIn, C>()) * 64) void chain_ker
                 if (mt < R::MT)
                     *reinterpret_cast<f32x4*>(state_out(c) + (size_t)l16 * DK + mt * 16 + 4 * g16) = S[a];
             }
-        }
-        if (p1) {
-            // ---- phase 1: partial X = W S^T over this wave's d_k part
-            f32x4 X = {0.f, 0.f, 0.f, 0.f};
+            if (p1) {
+                // ---- phase 1: partial X = W S^T over this wave's d_k part
+                f32x4 X = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int i = 0; i < P::KPW; ++i) {
-                const int ks = kq * P::KPW + i;
-                const Frag fw = frag(L::F_W + rt * R::DKS + ks, w_src(rt, ks));
-                X = M::mma(fw, *reinterpret_cast<const Frag*>(sm.sr + l16 * SP + ks * KS + g16 * E), X);
+                for (int i = 0; i < P::KPW; ++i) {
+                    const int ks = kq * P::KPW + i;
+                    X = M::mma(frag(0, w_src(rt, ks)), *reinterpret_cast<const Frag*>(sm.sr + l16 * SP + ks * KS + g16 * E),
+                               X);
+                }
+                sm.xp[kq][rt][lane] = X;
             }
-            sm.xp[kq][rt][lane] = X;
-        }
-        lds_barrier();  // ---- A: partials visible; W region free
+            lds_barrier();  // ---- A: partials visible
 
-        if (fin_d) {
-            // ---- phase 2: Delta = U - X for row tile rt (sigma-ordered dt, natural-order ds)
-            const f32x4 ks4 = STAGE ? *reinterpret_cast<const f32x4*>(sm.ksc + rt * 16 + 4 * g16)
-                                    : __builtin_bit_cast(f32x4, buf_load16(rcur, (uint32_t)(rt * 16 + 4 * g16) * 4,
-                                                                           (uint32_t)R::KSC_BYTE_OFF));
-            f32x4 X = sm.xp[0][rt][lane];
+            if (fin_d) {
+                // ---- phase 2: Delta = U - X for row tile rt (natural order, k-scaled in ds)
+                const f32x4 ks4 = __builtin_bit_cast(
+                    f32x4, buf_load16(rcur, (uint32_t)(rt * 16 + 4 * g16) * 4, (uint32_t)R::KSC_BYTE_OFF));
+                f32x4 X = sm.xp[0][rt][lane];
 #pragma unroll
-            for (int qq = 1; qq < P::KQ; ++qq) X += sm.xp[qq][rt][lane];
-            const f32x4 d = __builtin_bit_cast(f32x4, frag(L::F_U + rt, u_src(rt))) - X;
-            const int pd = l16 * DP + quad_pos<TIn>(rt, g16);
-            const int pn = l16 * DP + rt * 16 + 4 * g16;
-            store_quad<TIn, SPL>(sm.dt[0] + pd, sm.dt[NS - 1] + pd, d);
-            store_quad<TIn, SPL>(sm.ds[0] + pn, sm.ds[NS - 1] + pn, d * ks4);
-            if constexpr (!STAGE)  // Delta^T rows (fp32, natural order over the chunk)
+                for (int qq = 1; qq < P::KQ; ++qq) X += sm.xp[qq][rt][lane];
+                const f32x4 d = __builtin_bit_cast(f32x4, frag(0, u_src(rt))) - X;
+                const int pn = l16 * DP + rt * 16 + 4 * g16;
+                store_quad<TIn, SPL>(sm.ds[0] + pn, sm.ds[NS - 1] + pn, d * ks4);
+                // Delta^T rows (fp32, natural order over the chunk)
                 *reinterpret_cast<f32x4*>(delta_out(c, 0) + (size_t)l16 * C + rt * 16 + 4 * g16) = d;
-        }
-        lds_barrier();  // ---- B: Delta visible; U region free
-
-        // ---- phase 3: state update on this wave's d_k tiles
-        const float decay = STAGE ? sm.meta[0].x
-                                  : __builtin_bit_cast(f32x4, buf_load16(rcur, 0, (uint32_t)R::DEC_BYTE_OFF)).x;
-#pragma unroll
-        for (int a = 0; a < P::MTW; ++a) {
-            const int mt = wave + NW * a;
-            if (mt >= R::MT) continue;
-            f32x4 acc = S[a] * decay;
-#pragma unroll
-            for (int ks = 0; ks < R::CKS; ++ks) {
-                const int doff = l16 * DP + ks * KS + g16 * E;
-                const Frag fk = frag(L::F_K + mt * R::CKS + ks, k_src(mt, ks));
-                acc = M::mma(fk, *reinterpret_cast<const Frag*>(sm.ds[0] + doff), acc);
-                if constexpr (SPL) acc = M::mma(fk, *reinterpret_cast<const Frag*>(sm.ds[1] + doff), acc);
             }
-            S[a] = acc;
-            store_quad<TIn, false>(sm.sr + l16 * SP + quad_pos<TIn>(mt, g16), nullptr, acc);
+            const float decay = __builtin_bit_cast(f32x4, buf_load16(rcur, 0, (uint32_t)R::DEC_BYTE_OFF)).x;
+            lds_barrier();  // ---- B: Delta visible
+
+            // ---- phase 3: state update on this wave's d_k tiles
+#pragma unroll
+            for (int a = 0; a < P::MTW; ++a) {
+                const int mt = wave + NW * a;
+                if (mt >= R::MT) continue;
+                f32x4 acc = S[a] * decay;
+#pragma unroll
+                for (int ks = 0; ks < R::CKS; ++ks) {
+                    const int doff = l16 * DP + ks * KS + g16 * E;
+                    acc = M::mma(frag(0, k_src(mt, ks)), *reinterpret_cast<const Frag*>(sm.ds[0] + doff), acc);
+                }
+                S[a] = acc;
+                store_quad<TIn, false>(sm.sr + l16 * SP + quad_pos<TIn>(mt, g16), nullptr, acc);
+            }
+            lds_barrier();  // ---- C: state copy visible
         }
-        lds_barrier();  // ---- C: state copy visible; K region free
     }
 
     if (state_out_ptr) {
@@ -1746,39 +1772,70 @@ __global__ __launch_bounds__(256) void output_kernel(const int32_t* __restrict__
 
 // ------------------------------------------------------------------ dispatch
 
-// Side streams and events of the pipelined prefill, created once per device
-// and kept for the life of the process (default priority, non-blocking with
-// respect to the legacy default stream).
+// Streams and events of the pipelined prefill, created once per device and CU
+// split and kept for the life of the process (default priority, non-blocking
+// with respect to the legacy default stream).  The state chain gets a stream
+// of its own, CU-masked to the same number of CUs on every XCD, and the
+// per-segment intra-chunk and output kernels two more streams on all other
+// CUs: the chain's workgroups then never share a CU with the parallel kernels
+// and never wait for one to drain.  CU mask bit i is CU i / 8 of XCD i % 8
+// (the driver numbers CUs round-robin over the XCDs).
 struct PipeRes {
     static constexpr int MAX_SEG = 16;
-    hipStream_t intra_s = nullptr, out_s = nullptr;
+    int dev = -1;
+    uint8_t chain_cus[8] = {0, 0, 0, 0, 0, 0, 0, 0};  // CUs of each XCD reserved for the chain
+    hipStream_t chain_s = nullptr, intra_s = nullptr, out_s = nullptr;
     hipEvent_t start, intra_done[MAX_SEG], chain_done[MAX_SEG], intra_end, out_end;
     bool ok = false;
 };
 
-static hipError_t pipe_res(PipeRes** out)
+// chain_cus[x]: workgroups of the chain that run on XCD x (<= 32 each)
+static hipError_t pipe_res(const uint8_t* chain_cus, PipeRes** out)
 {
     static std::mutex mu;
-    static PipeRes res[64];
+    static PipeRes res[32];
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
     std::lock_guard<std::mutex> lock(mu);
-    PipeRes& r = res[dev];
-    if (!r.ok) {
-        if ((e = hipStreamCreateWithFlags(&r.intra_s, hipStreamNonBlocking)) != hipSuccess) return e;
-        if ((e = hipStreamCreateWithFlags(&r.out_s, hipStreamNonBlocking)) != hipSuccess) return e;
-        hipEvent_t* evs[] = {&r.start, &r.intra_end, &r.out_end};
-        for (hipEvent_t* ev : evs)
-            if ((e = hipEventCreateWithFlags(ev, hipEventDisableTiming)) != hipSuccess) return e;
-        for (int i = 0; i < PipeRes::MAX_SEG; ++i) {
-            if ((e = hipEventCreateWithFlags(&r.intra_done[i], hipEventDisableTiming)) != hipSuccess) return e;
-            if ((e = hipEventCreateWithFlags(&r.chain_done[i], hipEventDisableTiming)) != hipSuccess) return e;
+    PipeRes* r = nullptr;
+    for (PipeRes& c : res) {
+        if (c.ok && c.dev == dev && memcmp(c.chain_cus, chain_cus, 8) == 0) {
+            *out = &c;
+            return hipSuccess;
         }
-        r.ok = true;
+        if (!c.ok && !r) r = &c;
     }
-    *out = &r;
+    if (!r) return hipErrorOutOfMemory;  // too many distinct splits: the caller runs unpipelined
+    int cus = 0;
+    if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    if (cus == 256) {
+        uint32_t mine[8] = {0, 0, 0, 0, 0, 0, 0, 0}, rest[8];
+        for (int x = 0; x < 8; ++x)
+            for (int c = 0; c < chain_cus[x]; ++c) {
+                const int bit = x + 8 * c;
+                mine[bit >> 5] |= 1u << (bit & 31);
+            }
+        for (int w = 0; w < 8; ++w) rest[w] = ~mine[w];
+        if ((e = hipExtStreamCreateWithCUMask(&r->chain_s, 8, mine)) != hipSuccess) return e;
+        if ((e = hipExtStreamCreateWithCUMask(&r->intra_s, 8, rest)) != hipSuccess) return e;
+        if ((e = hipExtStreamCreateWithCUMask(&r->out_s, 8, rest)) != hipSuccess) return e;
+    } else {
+        if ((e = hipStreamCreateWithFlags(&r->chain_s, hipStreamNonBlocking)) != hipSuccess) return e;
+        if ((e = hipStreamCreateWithFlags(&r->intra_s, hipStreamNonBlocking)) != hipSuccess) return e;
+        if ((e = hipStreamCreateWithFlags(&r->out_s, hipStreamNonBlocking)) != hipSuccess) return e;
+    }
+    hipEvent_t* evs[] = {&r->start, &r->intra_end, &r->out_end};
+    for (hipEvent_t* ev : evs)
+        if ((e = hipEventCreateWithFlags(ev, hipEventDisableTiming)) != hipSuccess) return e;
+    for (int i = 0; i < PipeRes::MAX_SEG; ++i) {
+        if ((e = hipEventCreateWithFlags(&r->intra_done[i], hipEventDisableTiming)) != hipSuccess) return e;
+        if ((e = hipEventCreateWithFlags(&r->chain_done[i], hipEventDisableTiming)) != hipSuccess) return e;
+    }
+    r->dev = dev;
+    memcpy(r->chain_cus, chain_cus, 8);
+    r->ok = true;
+    *out = r;
     return hipSuccess;
 }
 
@@ -1877,14 +1934,14 @@ static hipError_t run_prefill(const PrefillArgs& a)
     }
 
     // The state chain keeps only (sequences x heads x d_v/16) workgroups busy.
-    // When that leaves most of the GPU idle and every stage runs in this call,
-    // the chunks are cut into segments and pipelined over three streams: the
-    // chain of segment s (caller's stream) runs while the intra-chunk kernel
-    // prepares later segments and the output kernel finishes earlier ones on
-    // side streams; events order each segment's three kernels.
+    // When they fit on half of every XCD and every stage runs in this call, the
+    // chunks are cut into segments and pipelined: the chain of segment s runs
+    // on its own half of the CUs while the intra-chunk kernel prepares later
+    // segments and the output kernel finishes earlier ones on the other half;
+    // events order each segment's three kernels.
     constexpr int64_t SEG_MIN = 64;
     int nseg = 1;
-    if (a.stages == 7 && chain_blocks < 256 && grid_chunks >= 2 * SEG_MIN)
+    if (a.stages == 7 && chain_blocks <= 128 && grid_chunks >= 2 * SEG_MIN)
         nseg = (int)std::min<int64_t>(4, grid_chunks / SEG_MIN);
     if (nseg == 1) {
         if (a.stages & 1) GDN_TRY(launch_intra(0, grid_chunks, a.stream));
@@ -1892,31 +1949,53 @@ static hipError_t run_prefill(const PrefillArgs& a)
         if (a.stages & 4) GDN_TRY(launch_output(0, grid_chunks, a.stream));
         return hipSuccess;
     }
+    // CUs of every XCD for the chain: as many as its most loaded XCD has
+    // workgroups (the pairs p with p % 8 == x, TILES each).  The same count on
+    // every XCD: with unequal per-XCD masks the workgroups are no longer dealt
+    // round-robin over the XCDs, and a pair's row tiles pile up on a few CUs.
+    uint8_t chain_cus[8];
+    {
+        const int64_t most = ((pairs + 7) / 8) * (DV / 16);
+        for (int x = 0; x < 8; ++x) chain_cus[x] = (uint8_t)most;
+    }
     PipeRes* pr = nullptr;
-    GDN_TRY(pipe_res(&pr));
+    if (pipe_res(chain_cus, &pr) != hipSuccess) pr = nullptr;
+    if (!pr) {  // no pipeline streams: stage by stage on the caller's stream
+        GDN_TRY(launch_intra(0, grid_chunks, a.stream));
+        GDN_TRY(launch_chain(0, ALL, a.stream));
+        GDN_TRY(launch_output(0, grid_chunks, a.stream));
+        return hipSuccess;
+    }
     const int64_t seg = (grid_chunks + nseg - 1) / nseg;
     auto seg_lo = [&](int s) { return std::min<int64_t>(grid_chunks, (int64_t)s * seg); };
-    // the side streams start after everything already queued on the caller's stream
+    // The first segment's preparation and the last segment's outputs run on the
+    // caller's stream over the whole GPU (nothing else runs then); everything in
+    // between overlaps on the three pipeline streams.
+    GDN_TRY(launch_intra(0, seg_lo(1), a.stream));
     GDN_TRY(hipEventRecord(pr->start, a.stream));
+    GDN_TRY(hipStreamWaitEvent(pr->chain_s, pr->start, 0));
     GDN_TRY(hipStreamWaitEvent(pr->intra_s, pr->start, 0));
     GDN_TRY(hipStreamWaitEvent(pr->out_s, pr->start, 0));
-    GDN_TRY(launch_intra(0, seg_lo(1), a.stream));
     for (int s = 1; s < nseg; ++s) {  // later segments' preparation, in order, on its own stream
         GDN_TRY(launch_intra(seg_lo(s), seg_lo(s + 1), pr->intra_s));
         GDN_TRY(hipEventRecord(pr->intra_done[s], pr->intra_s));
     }
     for (int s = 0; s < nseg; ++s) {
-        if (s > 0) GDN_TRY(hipStreamWaitEvent(a.stream, pr->intra_done[s], 0));
-        GDN_TRY(launch_chain(seg_lo(s), s + 1 < nseg ? seg_lo(s + 1) : ALL, a.stream));
-        GDN_TRY(hipEventRecord(pr->chain_done[s], a.stream));
-        GDN_TRY(hipStreamWaitEvent(pr->out_s, pr->chain_done[s], 0));
-        GDN_TRY(launch_output(seg_lo(s), seg_lo(s + 1), pr->out_s));
+        if (s > 0) GDN_TRY(hipStreamWaitEvent(pr->chain_s, pr->intra_done[s], 0));
+        GDN_TRY(launch_chain(seg_lo(s), s + 1 < nseg ? seg_lo(s + 1) : ALL, pr->chain_s));
+        GDN_TRY(hipEventRecord(pr->chain_done[s], pr->chain_s));
+        if (s + 1 < nseg) {
+            GDN_TRY(hipStreamWaitEvent(pr->out_s, pr->chain_done[s], 0));
+            GDN_TRY(launch_output(seg_lo(s), seg_lo(s + 1), pr->out_s));
+        }
     }
-    // the caller's stream resumes after both side streams
+    // the caller's stream resumes after the pipeline streams, then finishes the last segment
     GDN_TRY(hipEventRecord(pr->intra_end, pr->intra_s));
     GDN_TRY(hipEventRecord(pr->out_end, pr->out_s));
     GDN_TRY(hipStreamWaitEvent(a.stream, pr->intra_end, 0));
     GDN_TRY(hipStreamWaitEvent(a.stream, pr->out_end, 0));
+    GDN_TRY(hipStreamWaitEvent(a.stream, pr->chain_done[nseg - 1], 0));
+    GDN_TRY(launch_output(seg_lo(nseg - 1), seg_lo(nseg), a.stream));
 #undef GDN_TRY
     return hipSuccess;
 }
