@@ -78,11 +78,30 @@ def find(d, suffix):
     return hits[0] if hits else None
 
 
+def finished(d):
+    """The profiled program printed its last line (the bench JSON line or 'copied ...')."""
+    try:
+        with open(os.path.join(d, "stdout.txt")) as f:
+            lines = [l for l in f.read().splitlines() if l.strip()]
+    except OSError:
+        return False
+    return bool(lines) and (lines[-1].startswith("{") or lines[-1].startswith("copied"))
+
+
+def profiler_ok(rc, d, result_suffix):
+    """rocprofv3 can itself segfault while tearing down after the program has
+    finished and its output is complete; that exit is accepted when the
+    program's last line was printed and the result file exists."""
+    if find(d, result_suffix) is None or not finished(d):
+        return False
+    return rc == 0 or rc in (-11, 139)
+
+
 def mode_trace():
     rc, d, cmd = launch(BENCH_TRACE, ["--kernel-trace", "--stats"], "trace", 900)
     with open(os.path.join(d, "command.txt"), "w") as f:
         f.write(cmd + "\n")
-    if rc != 0 or find(d, "kernel_stats.csv") is None:
+    if not profiler_ok(rc, d, "kernel_stats.csv"):
         raise SystemExit(f"trace run failed (exit {rc})")
 
 
@@ -161,13 +180,13 @@ def mode_traffic():
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
         rc, d, cmd = launch(["profile_bench.py", "copy"], ["--pmc", counter], f"copy_{counter}", 240)
         cmds.append(cmd)
-        if rc != 0 or counter_sums(d).get("copy") is None:
+        if not profiler_ok(rc, d, "counter_collection.csv") or counter_sums(d).get("copy") is None:
             raise SystemExit(f"copy calibration for {counter} failed (exit {rc})")
         rc, d, cmd = launch(BENCH_PMC, ["--pmc", counter, "--kernel-include-regex",
                                         "chain_kernel|intra_kernel|output_kernel|decode_kernel"],
                             f"bench_{counter}", 600)
         cmds.append(cmd)
-        if rc != 0:
+        if not profiler_ok(rc, d, "counter_collection.csv"):
             raise SystemExit(f"bench pass for {counter} failed (exit {rc})")
     # the kernel sources these counters belong to
     with open(os.path.join(OUT, "traffic_meta.json"), "w") as f:
