@@ -221,3 +221,51 @@ def varlen_torch_inputs(lengths, H: int, dk: int, dv: int, seed: int, device):
         t0 += L
     cu = torch.tensor([0] + list(np.cumsum(lengths)), dtype=torch.int32, device=device)
     return q, k, v, g, beta, cu
+
+
+@dataclass
+class FrontendInputs:
+    """Inputs of the mixer's front end: the projections before the short convolution
+    (xq, xk [T, H*dk], xv [T, H*dv] in the storage dtype), the depthwise taps
+    [2*H*dk + H*dv, 4] fp32 (oldest first, channels of q, then k, then v), the gate
+    projections a = W_alpha x, b = W_beta x [T, H] fp32, A_log and dt_bias [H] fp32,
+    and an optional conv state [N, 3, 2*H*dk + H*dv] in the storage dtype."""
+    xq: np.ndarray
+    xk: np.ndarray
+    xv: np.ndarray
+    conv_weight: np.ndarray
+    a: np.ndarray
+    b: np.ndarray
+    A_log: np.ndarray
+    dt_bias: np.ndarray
+    cu_seqlens: np.ndarray
+    dtype: str
+    conv_state: np.ndarray | None = None
+
+    @property
+    def bf16(self) -> bool:
+        return self.dtype == "bf16"
+
+
+def frontend_inputs(T: int, H: int, dk: int, dv: int, dtype: str, seed: int, cu_seqlens=None,
+                    with_state: bool = False, N: int | None = None) -> FrontendInputs:
+    """Front-end inputs.  Projections ~ N(0, 1); taps ~ U(-1/2, 1/2), the uniform
+    default initialisation of a 4-tap depthwise convolution (bound 1/sqrt(4));
+    A_log = log U(0.5, 2) and dt_bias = 2 + U(-0.5, 0.5) per head, a, b ~ N(0, 1),
+    so that g = -e^{A_log} softplus(a + dt_bias) spreads around the prefill
+    workloads' -softplus(N(0, 1) + 2); conv state ~ N(0, 1) when asked for."""
+    ss = np.random.SeedSequence([seed, 4242])
+    rq, rk, rv, rw, ra, rb, rp, rs = [np.random.default_rng(s) for s in ss.spawn(8)]
+    cu = np.array([0, T], dtype=np.int64) if cu_seqlens is None else np.asarray(cu_seqlens, dtype=np.int64)
+    n_seqs = cu.shape[0] - 1 if N is None else N
+    ctot = 2 * H * dk + H * dv
+    xq = _store(rq.standard_normal((T, H * dk)), dtype)
+    xk = _store(rk.standard_normal((T, H * dk)), dtype)
+    xv = _store(rv.standard_normal((T, H * dv)), dtype)
+    w = rw.uniform(-0.5, 0.5, size=(ctot, 4)).astype(np.float32)
+    a = ra.standard_normal((T, H)).astype(np.float32)
+    b = rb.standard_normal((T, H)).astype(np.float32)
+    A_log = np.log(rp.uniform(0.5, 2.0, size=H)).astype(np.float32)
+    dt_bias = (2.0 + rp.uniform(-0.5, 0.5, size=H)).astype(np.float32)
+    st = _store(rs.standard_normal((n_seqs, 3, ctot)), dtype) if with_state else None
+    return FrontendInputs(xq, xk, xv, w, a, b, A_log, dt_bias, cu, dtype, st)

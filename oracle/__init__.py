@@ -237,3 +237,8 @@ def gated_rmsnorm(o, z, weight=None, eps=DEFAULT_NORM_EPS, bf16=False, mutation=
     sig = 1.0 / (1.0 + np.exp(-zz))
     gate = sig if mutation == 1 else zz * sig
     return o / np.sqrt(ms + e) * w * gate
+
+
+# ----------------------------------------------------------------- front end (conv + gates)
+
+from .frontend import CONV_MUTATIONS, GATE_MUTATIONS, gates, short_conv_silu  # noqa: E402,F401
