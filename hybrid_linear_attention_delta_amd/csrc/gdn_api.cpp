@@ -284,3 +284,96 @@ gdn_status gdn_decode_step_gated(const void* q, const void* k, const void* v, co
 }
 
 }  // extern "C"
+
+namespace {
+
+// Checks shared by the two front-end entry points.
+gdn_status check_frontend(const void* xq, const void* xk, const void* xv, const float* w, const float* a,
+                          const float* b, const float* A_log, const float* dt_bias, const void* q, const void* k,
+                          const void* v, const float* g, const float* beta, int32_t H, int32_t dk, int32_t dv,
+                          gdn_dtype dt)
+{
+    if (dt != GDN_F32 && dt != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+    if (H < 1 || dk < 1 || dv < 1) return GDN_ERR_BAD_SHAPE;
+    if (dk % 8 != 0 || dv % 8 != 0) return GDN_ERR_UNSUPPORTED;
+    if ((int64_t)H * (2 * (int64_t)dk + dv) > (1 << 24)) return GDN_ERR_BAD_SHAPE;
+    if (!xq || !xk || !xv || !w || !a || !b || !A_log || !dt_bias || !q || !k || !v || !g || !beta)
+        return GDN_ERR_NULL_ARG;
+    const void* p16[] = {xq, xk, xv, w, q, k, v};
+    for (const void* p : p16)
+        if (!aligned16(p)) return GDN_ERR_ALIGNMENT;
+    const void* p4[] = {a, b, A_log, dt_bias, g, beta};
+    for (const void* p : p4)
+        if (!aligned4(p)) return GDN_ERR_ALIGNMENT;
+    return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_frontend_prefill(const void* xq, const void* xk, const void* xv, const float* conv_weight,
+                                const float* a, const float* b, const float* A_log, const float* dt_bias,
+                                const void* conv_state_in, const int32_t* cu_seqlens, int32_t num_seqs,
+                                int64_t total_tokens, int32_t H, int32_t dk, int32_t dv, gdn_dtype dt, void* q,
+                                void* k, void* v, float* g, float* beta, void* conv_state_out, hipStream_t stream)
+{
+    if (total_tokens < 0 || num_seqs < 1) return GDN_ERR_BAD_SHAPE;
+    if (total_tokens > ((int64_t)1 << 31) - 1) return GDN_ERR_BAD_SHAPE;
+    if (!cu_seqlens && num_seqs != 1) return GDN_ERR_BAD_SHAPE;
+    if (total_tokens == 0 && !conv_state_out) return GDN_OK;
+    if (total_tokens > 0) {
+        const gdn_status st = check_frontend(xq, xk, xv, conv_weight, a, b, A_log, dt_bias, q, k, v, g, beta, H,
+                                             dk, dv, dt);
+        if (st != GDN_OK) return st;
+    } else {
+        if (dt != GDN_F32 && dt != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+        if (H < 1 || dk < 1 || dv < 1) return GDN_ERR_BAD_SHAPE;
+        if (dk % 8 != 0 || dv % 8 != 0) return GDN_ERR_UNSUPPORTED;
+    }
+    if ((conv_state_in && !aligned16(conv_state_in)) || (conv_state_out && !aligned16(conv_state_out)))
+        return GDN_ERR_ALIGNMENT;
+    if (conv_state_in && conv_state_out && conv_state_in != conv_state_out) {
+        const size_t bytes = (size_t)num_seqs * 3 * (size_t)H * (2 * (size_t)dk + dv) * (dt == GDN_BF16 ? 2 : 4);
+        const char* a0 = (const char*)conv_state_in;
+        const char* b0 = (const char*)conv_state_out;
+        if (a0 < b0 + bytes && b0 < a0 + bytes) return GDN_ERR_BAD_SHAPE;  // partial overlap
+    }
+    gdn::FrontendArgs fa;
+    fa.xq = xq; fa.xk = xk; fa.xv = xv; fa.w = conv_weight;
+    fa.a = a; fa.b = b; fa.A_log = A_log; fa.dt_bias = dt_bias;
+    fa.state_in = conv_state_in; fa.state_out = conv_state_out;
+    fa.cu = cu_seqlens; fa.N = num_seqs; fa.T = total_tokens;
+    fa.H = H; fa.dk = dk; fa.dv = dv; fa.bf16 = dt == GDN_BF16; fa.decode = false;
+    fa.q = q; fa.k = k; fa.v = v; fa.g = g; fa.beta = beta;
+    fa.stream = stream;
+    return finish(gdn::launch_frontend(fa), stream);
+}
+
+gdn_status gdn_frontend_decode(const void* xq, const void* xk, const void* xv, const float* conv_weight,
+                               const float* a, const float* b, const float* A_log, const float* dt_bias,
+                               void* conv_state, int32_t N, int32_t H, int32_t dk, int32_t dv, gdn_dtype dt, void* q,
+                               void* k, void* v, float* g, float* beta, hipStream_t stream)
+{
+    if (N < 0) return GDN_ERR_BAD_SHAPE;
+    if (N == 0) {
+        if (dt != GDN_F32 && dt != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+        return (H < 1 || dk < 1 || dv < 1) ? GDN_ERR_BAD_SHAPE : GDN_OK;
+    }
+    const gdn_status st = check_frontend(xq, xk, xv, conv_weight, a, b, A_log, dt_bias, q, k, v, g, beta, H, dk,
+                                         dv, dt);
+    if (st != GDN_OK) return st;
+    if (!conv_state) return GDN_ERR_NULL_ARG;
+    if (!aligned16(conv_state)) return GDN_ERR_ALIGNMENT;
+    gdn::FrontendArgs fa;
+    fa.xq = xq; fa.xk = xk; fa.xv = xv; fa.w = conv_weight;
+    fa.a = a; fa.b = b; fa.A_log = A_log; fa.dt_bias = dt_bias;
+    fa.state_in = conv_state; fa.state_out = conv_state;
+    fa.cu = nullptr; fa.N = N; fa.T = N;
+    fa.H = H; fa.dk = dk; fa.dv = dv; fa.bf16 = dt == GDN_BF16; fa.decode = true;
+    fa.q = q; fa.k = k; fa.v = v; fa.g = g; fa.beta = beta;
+    fa.stream = stream;
+    return finish(gdn::launch_frontend(fa), stream);
+}
+
+}  // extern "C"

@@ -73,4 +73,26 @@ struct PrefillArgs {
 
 hipError_t launch_prefill(const PrefillArgs& a);
 
+// Front end: short causal conv + SiLU on the q, k, v projections and the gate
+// math.  Channels of q, k, v form one axis of 2 H dk + H dv (q, k, v in order)
+// for the taps w [ctot][4] fp32 and the conv state [N][3][ctot] (type of x).
+struct FrontendArgs {
+    const void *xq, *xk, *xv;  // [T (or N)][H dk | H dv]
+    const float* w;
+    const float *a, *b, *A_log, *dt_bias;
+    const void* state_in;      // prefill: [N][3][ctot] or NULL (zeros)
+    void* state_out;           // prefill: may be NULL or alias state_in; decode: the state, in place
+    const int32_t* cu;         // prefill: device [N + 1] or NULL (one sequence)
+    int32_t N;
+    int64_t T;
+    int32_t H, dk, dv;
+    bool bf16;
+    bool decode;
+    void *q, *k, *v;
+    float *g, *beta;
+    hipStream_t stream;
+};
+
+hipError_t launch_frontend(const FrontendArgs& a);
+
 }  // namespace gdn

@@ -66,6 +66,12 @@ def load_library(path: str | None = None):
             lib.gdn_decode_step_gated.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int, f32,
                                                   i32, vp, vp, f32, vp, vp]
             lib.gdn_decode_step_gated.restype = ctypes.c_int
+            lib.gdn_frontend_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
+                                                 ctypes.c_int, vp, vp, vp, vp, vp, vp, vp]
+            lib.gdn_frontend_prefill.restype = ctypes.c_int
+            lib.gdn_frontend_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int,
+                                                vp, vp, vp, vp, vp, vp]
+            lib.gdn_frontend_decode.restype = ctypes.c_int
             lib.gdn_status_string.argtypes = [ctypes.c_int]
             lib.gdn_status_string.restype = ctypes.c_char_p
             lib.gdn_version.argtypes = []
@@ -247,6 +253,98 @@ def decode_step(q, k, v, g, beta, state, scale=None, qk_l2norm=True, out=None, g
     if st != 0:
         raise GdnError(st, "gdn_decode_step")
     return out
+
+
+def _frontend_args(xq, xk, xv, conv_weight, a, b, A_log, dt_bias):
+    torch = _torch()
+    dev = xq.device
+    _check(xq, "xq", device=dev)
+    dt = xq.dtype
+    _dtype_code(xq)
+    for name, t in (("xk", xk), ("xv", xv)):
+        _check(t, name, dtype=dt, device=dev)
+    for name, t in (("conv_weight", conv_weight), ("a", a), ("b", b), ("A_log", A_log), ("dt_bias", dt_bias)):
+        _check(t, name, dtype=torch.float32, device=dev)
+    T, H, dk = xq.shape
+    dv = xv.shape[2]
+    if xk.shape != (T, H, dk) or xv.shape[:2] != (T, H) or a.shape != (T, H) or b.shape != (T, H):
+        raise ValueError("shape mismatch among xq, xk, xv, a, b")
+    if A_log.shape != (H,) or dt_bias.shape != (H,):
+        raise ValueError(f"A_log and dt_bias must be [{H}]")
+    ctot = H * (2 * dk + dv)
+    if conv_weight.shape != (ctot, 4):
+        raise ValueError(f"conv_weight must be [{ctot}, 4] (channels of q, then k, then v)")
+    return dev, dt, T, H, dk, dv, ctot
+
+
+def frontend_prefill(xq, xk, xv, conv_weight, a, b, A_log, dt_bias, conv_state=None, cu_seqlens=None,
+                     return_conv_state=True, conv_state_out=None):
+    """Front end of App. A.3 over packed sequences: the 4-tap causal depthwise
+    convolution with SiLU on the q, k, v projections and the gates
+    g = -exp(A_log) softplus(a + dt_bias), beta = sigmoid(b).
+
+    xq, xk [T, H, dk]; xv [T, H, dv] (bf16 or fp32); conv_weight [H(2dk+dv), 4] fp32
+    (channels of q, then k, then v; taps oldest first); a, b [T, H] fp32; A_log, dt_bias
+    [H] fp32; conv_state [N, 3, H(2dk+dv)] (dtype of xq) or None (zeros); cu_seqlens as
+    for ``chunk_prefill``.  Returns (q, k, v, g, beta, conv_state_out); conv_state_out
+    is None unless asked for (``conv_state_out`` may be the input state: in place).
+    """
+    torch = _torch()
+    lib = load_library()
+    dev, dt, T, H, dk, dv, ctot = _frontend_args(xq, xk, xv, conv_weight, a, b, A_log, dt_bias)
+    cu_dev = None
+    if cu_seqlens is None:
+        N = 1
+    else:
+        if isinstance(cu_seqlens, torch.Tensor) and cu_seqlens.device.type == "cuda":
+            cu_dev = cu_seqlens.to(torch.int32).contiguous()
+        else:
+            cu_dev = torch.as_tensor(cu_seqlens, dtype=torch.int32).contiguous().to(dev)
+        N = cu_dev.shape[0] - 1
+    if conv_state is not None:
+        _check(conv_state, "conv_state", dtype=dt, device=dev)
+        if conv_state.shape != (N, 3, ctot):
+            raise ValueError(f"conv_state must be [{N}, 3, {ctot}]")
+    if conv_state_out is None and return_conv_state:
+        conv_state_out = torch.empty((N, 3, ctot), dtype=dt, device=dev)
+    elif conv_state_out is not None:
+        _check(conv_state_out, "conv_state_out", dtype=dt, device=dev)
+        if conv_state_out.shape != (N, 3, ctot):
+            raise ValueError(f"conv_state_out must be [{N}, 3, {ctot}]")
+    q = torch.empty_like(xq)
+    k = torch.empty_like(xk)
+    v = torch.empty_like(xv)
+    g = torch.empty((T, H), dtype=torch.float32, device=dev)
+    beta = torch.empty((T, H), dtype=torch.float32, device=dev)
+    st = lib.gdn_frontend_prefill(_ptr(xq), _ptr(xk), _ptr(xv), _ptr(conv_weight), _ptr(a), _ptr(b), _ptr(A_log),
+                                  _ptr(dt_bias), _ptr(conv_state), _ptr(cu_dev), N, T, H, dk, dv, _dtype_code(xq),
+                                  _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(conv_state_out), _stream(dev))
+    if st != 0:
+        raise GdnError(st, "gdn_frontend_prefill")
+    return q, k, v, g, beta, conv_state_out
+
+
+def frontend_decode(xq, xk, xv, conv_weight, a, b, A_log, dt_bias, conv_state):
+    """Front end for one decode token per sequence: xq, xk [N, H, dk]; xv [N, H, dv];
+    a, b [N, H]; conv_state [N, 3, H(2dk+dv)] updated in place.  Returns (q, k, v, g, beta),
+    the inputs of ``decode_step``."""
+    torch = _torch()
+    lib = load_library()
+    dev, dt, N, H, dk, dv, ctot = _frontend_args(xq, xk, xv, conv_weight, a, b, A_log, dt_bias)
+    _check(conv_state, "conv_state", dtype=dt, device=dev)
+    if conv_state.shape != (N, 3, ctot):
+        raise ValueError(f"conv_state must be [{N}, 3, {ctot}]")
+    q = torch.empty_like(xq)
+    k = torch.empty_like(xk)
+    v = torch.empty_like(xv)
+    g = torch.empty((N, H), dtype=torch.float32, device=dev)
+    beta = torch.empty((N, H), dtype=torch.float32, device=dev)
+    st = lib.gdn_frontend_decode(_ptr(xq), _ptr(xk), _ptr(xv), _ptr(conv_weight), _ptr(a), _ptr(b), _ptr(A_log),
+                                 _ptr(dt_bias), _ptr(conv_state), N, H, dk, dv, _dtype_code(xq), _ptr(q), _ptr(k),
+                                 _ptr(v), _ptr(g), _ptr(beta), _stream(dev))
+    if st != 0:
+        raise GdnError(st, "gdn_frontend_decode")
+    return q, k, v, g, beta
 
 
 def default_scale(dk: int) -> float:

@@ -192,6 +192,54 @@ gdn_status gdn_decode_step_gated(const void* q, const void* k, const void* v, co
                                  float scale, int32_t qk_l2norm, const void* gate, const float* norm_weight,
                                  float norm_eps, void* o, hipStream_t stream);
 
+/*
+ * Front end of the mixer (App. A.3): the short convolution with SiLU applied
+ * to Q, K and V before the recurrence (the paragraph under Table 8: kernel
+ * size 4), and the gates of the paragraph after Eq. 21:
+ *
+ *     q_t[c] = silu(sum_{j=0..3} w[c][j] xq_{t-3+j}[c])       (likewise k, v)
+ *     g_t    = -exp(A_log[h]) * softplus(a_t[h] + dt_bias[h])
+ *     beta_t = sigmoid(b_t[h])
+ *
+ * The convolution is causal and depthwise (each channel mixes only its own
+ * past three inputs and the current one; tap 3 multiplies the current token)
+ * and has no bias.  silu(u) = u / (1 + e^{-u}), softplus(u) = log(1 + e^u),
+ * sigmoid(u) = 1 / (1 + e^{-u}); the arithmetic is fp32, the outputs q, k, v
+ * are rounded to dt (round to nearest even).  The projections W_Q x, W_K x,
+ * W_V x, W_alpha x, W_beta x are the caller's: their results are the inputs.
+ *
+ * Channel axis: the channels of q, k and v are numbered as one axis of
+ * ctot = 2 H dk + H dv channels -- q's H*dk (head-major), then k's, then v's.
+ *
+ *   xq, xk        [tokens, H, dk]  dt;  xv [tokens, H, dv] dt (16-byte aligned)
+ *   conv_weight   [ctot][4] fp32 taps, oldest first (16-byte aligned)
+ *   a, b          [tokens, H] fp32: W_alpha x_t and W_beta x_t
+ *   A_log, dt_bias [H] fp32
+ *   q, k, v       outputs shaped like xq, xk, xv (dt); g, beta [tokens, H] fp32
+ *   conv state    [num_seqs (or N), 3, ctot] dt: the three inputs before the
+ *                 next token of each sequence, oldest first.  dk and dv must
+ *                 be multiples of 8.
+ *
+ * Prefill: sequence n of cu_seqlens (as for gdn_chunk_prefill; NULL = one
+ * sequence) starts from conv_state_in[n] (NULL: zeros) and nothing crosses a
+ * sequence boundary.  conv_state_out (may be NULL; may alias conv_state_in
+ * exactly) receives the last three inputs of every sequence, reaching into
+ * conv_state_in for sequences shorter than three tokens.  The outputs q, k,
+ * v, g, beta are the inputs of gdn_chunk_prefill.
+ * Decode: one token per sequence; conv_state is read and updated in place.
+ * The outputs are the inputs of gdn_decode_step.
+ */
+gdn_status gdn_frontend_prefill(const void* xq, const void* xk, const void* xv, const float* conv_weight,
+                                const float* a, const float* b, const float* A_log, const float* dt_bias,
+                                const void* conv_state_in, const int32_t* cu_seqlens, int32_t num_seqs,
+                                int64_t total_tokens, int32_t H, int32_t dk, int32_t dv, gdn_dtype dt, void* q,
+                                void* k, void* v, float* g, float* beta, void* conv_state_out, hipStream_t stream);
+
+gdn_status gdn_frontend_decode(const void* xq, const void* xk, const void* xv, const float* conv_weight,
+                               const float* a, const float* b, const float* A_log, const float* dt_bias,
+                               void* conv_state, int32_t N, int32_t H, int32_t dk, int32_t dv, gdn_dtype dt, void* q,
+                               void* k, void* v, float* g, float* beta, hipStream_t stream);
+
 /* Static, human-readable name of a status code. */
 const char* gdn_status_string(gdn_status s);
 

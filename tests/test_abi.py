@@ -162,3 +162,33 @@ def test_gated_entry_points_reject_bad_norm_arguments(lib):
     # nothing to do: no tokens / no sequences, no gate needed
     assert lib.gdn_decode_step_gated(f, f, f, f, f, f, 0, 2, 64, 64, gdn.GDN_BF16, -1.0, 1, None, None, 1e-6, f,
                                      None) == 0
+
+
+def test_frontend_host_validation(lib):
+    """The front-end entry points check sizes, pointers, alignment and state
+    overlap on the host and return before any launch."""
+    f = _fake()
+
+    def pre(**kw):
+        return lib.gdn_frontend_prefill(f, f, f, kw.get("w", f), f, f, f, f, kw.get("st_in", None), kw.get("cu", None),
+                                        kw.get("N", 1), kw.get("T", 64), 2, kw.get("dk", 64), 64,
+                                        kw.get("dt", gdn.GDN_BF16), kw.get("q", f), f, f, f, f,
+                                        kw.get("st_out", None), None)
+
+    assert pre(dk=12) == 3                      # d_k not a multiple of 8
+    assert pre(dt=5) == 3
+    assert pre(T=-1) == 2
+    assert pre(N=2) == 2                        # several sequences need cu_seqlens
+    assert pre(q=None) == 1
+    assert pre(w=_fake(0x10004)) == 5           # taps must be 16-byte aligned
+    assert pre(st_in=_fake(0x40000), st_out=_fake(0x40010)) == 2  # partial overlap
+    assert pre(T=0) == 0                        # nothing to do
+
+    def dec(**kw):
+        return lib.gdn_frontend_decode(f, f, f, f, f, f, f, f, kw.get("st", f), kw.get("N", 4), 2, 64, 64,
+                                       gdn.GDN_BF16, f, f, f, f, f, None)
+
+    assert dec(st=None) == 1
+    assert dec(N=-1) == 2
+    assert dec(N=0) == 0
+    assert dec(st=_fake(0x10008)) == 5
