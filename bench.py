@@ -32,6 +32,7 @@ Prints ONE JSON line on stdout; progress goes to stderr.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -218,6 +219,82 @@ def bench_decode(torch, gdn, synth, n_steps, warmup=3):
     return dict(ms_per_step=ms, median_ms=med, gated_ms=gated)
 
 
+def frontend_bytes(tokens):
+    """Front end, algorithmic HBM bytes: the q, k, v projections read and the
+    convolved q, k, v written (bf16), a and b read and g, beta written (fp32),
+    the taps read once."""
+    ctot = H * (2 * DK + DV)
+    return 2 * tokens * ctot * 2 + 4 * tokens * H * 4 + ctot * 4 * 4
+
+
+def bench_frontend(torch, gdn, synth, steps, warmup):
+    """The front end (App. A.3: 4-tap causal conv + SiLU on q, k, v and the gate
+    math) over the 64K-token workload, alone and followed by the prefill; and
+    its decode form for the 256-sequence decode batch."""
+    dev = torch.device("cuda:0")
+    log(f"[bench] generating front-end inputs T={T} H={H} d={DK} bf16")
+    f = synth.frontend_inputs(T, H, DK, DV, "bf16", seed=synth.seed_for("prefill64k"))
+    xq = synth.to_torch(f.xq, dev, bf16=True).view(T, H, DK)
+    xk = synth.to_torch(f.xk, dev, bf16=True).view(T, H, DK)
+    xv = synth.to_torch(f.xv, dev, bf16=True).view(T, H, DV)
+    w, a_, b_, al, db = (synth.to_torch(x, dev) for x in (f.conv_weight, f.a, f.b, f.A_log, f.dt_bias))
+    o = torch.empty((T, H, DV), dtype=torch.bfloat16, device=dev)
+    fs = torch.empty((1, H, DV, DK), dtype=torch.float32, device=dev)
+    ws = torch.empty(gdn.prefill_workspace_size(T, 1, H, DK, DV, C), dtype=torch.uint8, device=dev)
+    fo = (torch.empty_like(xq), torch.empty_like(xk), torch.empty_like(xv),
+          torch.empty((T, H), dtype=torch.float32, device=dev), torch.empty((T, H), dtype=torch.float32, device=dev))
+    front = lambda: gdn.frontend_prefill(xq, xk, xv, w, a_, b_, al, db, return_conv_state=False, out=fo)
+
+    def both():
+        q, k, v, g, beta, _ = front()
+        gdn.chunk_prefill(q, k, v, g, beta, chunk=C, out=o, final_state=fs, workspace=ws)
+
+    res = {}
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    for name, fn in (("frontend", front), ("frontend_then_prefill", both)):
+        for _ in range(max(1, warmup)):
+            fn()
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(steps):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        res[name] = t0.elapsed_time(t1) / steps
+    log(f"[bench] front end {res['frontend'] * 1e3:.1f} us; front end + prefill {res['frontend_then_prefill']:.3f} ms")
+
+    fd = synth.frontend_inputs(DEC_N, H, DK, DV, "bf16", seed=synth.seed_for("decode"), with_state=True,
+                               N=DEC_N)
+    st = synth.to_torch(fd.conv_state, dev, bf16=True)
+    dq = synth.to_torch(fd.xq, dev, bf16=True).view(DEC_N, H, DK)
+    dk_ = synth.to_torch(fd.xk, dev, bf16=True).view(DEC_N, H, DK)
+    dv_ = synth.to_torch(fd.xv, dev, bf16=True).view(DEC_N, H, DV)
+    dw, da, dbb, dal, ddb = (synth.to_torch(x, dev) for x in (fd.conv_weight, fd.a, fd.b, fd.A_log, fd.dt_bias))
+    n_dec = 128
+    do = (torch.empty_like(dq), torch.empty_like(dk_), torch.empty_like(dv_),
+          torch.empty((DEC_N, H), dtype=torch.float32, device=dev),
+          torch.empty((DEC_N, H), dtype=torch.float32, device=dev))
+    gdn.frontend_decode(dq, dk_, dv_, dw, da, dbb, dal, ddb, st, out=do)  # checks the arguments once
+    # then the C entry point itself, arguments marshalled once (as a serving loop
+    # would): the per-call Python checks cost more than this small kernel
+    lib = gdn.load_library()
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    args = [P(dq), P(dk_), P(dv_), P(dw), P(da), P(dbb), P(dal), P(ddb), P(st), DEC_N, H, DK, DV, gdn.GDN_BF16,
+            *[P(t) for t in do], ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)]
+    for _ in range(max(1, warmup)):
+        assert lib.gdn_frontend_decode(*args) == 0
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(n_dec):
+        lib.gdn_frontend_decode(*args)
+    t1.record()
+    torch.cuda.synchronize()
+    res["decode_frontend"] = t0.elapsed_time(t1) / n_dec
+    log(f"[bench] decode front end {res['decode_frontend'] * 1e3:.1f} us/step")
+    return res
+
+
 def cpu_baseline(inp, max_threads=16):
     import oracle
 
@@ -258,6 +335,7 @@ def main():
     gdn.load_library()
     pre = bench_prefill(torch, gdn, synth, a.steps, a.warmup)
     dec = None if a.no_decode else bench_decode(torch, gdn, synth, a.decode_steps)
+    fe = bench_frontend(torch, gdn, synth, a.steps, a.warmup)
 
     tok_s = T / (pre["ms_per_step"] / 1e3)
     chain_flops = flops_chain_per_token() * T
@@ -326,6 +404,21 @@ def main():
                          "traffic": traffic_from_profiles("decode_kernel"),
                          "algorithmic_bytes_per_launch": b},
         }
+    fb = frontend_bytes(T)
+    ctot = H * (2 * DK + DV)
+    dec_fb = 2 * DEC_N * ctot * 2 + 2 * 3 * DEC_N * ctot * 2 + 4 * DEC_N * H * 4 + ctot * 16
+    out["frontend"] = {
+        "workload": f"gdn_frontend_prefill T={T} H={H} d={DK} bf16 (4-tap conv + SiLU on q, k, v; gates)",
+        "ms_per_step": fe["frontend"],
+        "frontend_then_prefill_ms": fe["frontend_then_prefill"],
+        "frontend_then_prefill_tokens_per_s": T / (fe["frontend_then_prefill"] / 1e3),
+        "roofline": {"kernel": "conv_silu_kernel", "bound": "hbm", "achieved": fb / (fe["frontend"] / 1e3) / 1e9,
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": fb / (fe["frontend"] / 1e3) / 1e9 / PEAK_HBM_GBPS,
+                     "traffic": traffic_from_profiles("conv_silu_kernel"), "algorithmic_bytes_per_launch": fb},
+        "decode_frontend_ms_per_step": fe["decode_frontend"],
+        "decode_frontend_GBps": dec_fb / (fe["decode_frontend"] / 1e3) / 1e9,
+    }
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(pre["inputs"])
     print(json.dumps(out), flush=True)

@@ -277,8 +277,27 @@ def _frontend_args(xq, xk, xv, conv_weight, a, b, A_log, dt_bias):
     return dev, dt, T, H, dk, dv, ctot
 
 
+def _frontend_outputs(out, xq, xk, xv, rows, H, dev):
+    """The five outputs (q, k, v, g, beta): the caller's, checked, or new tensors."""
+    torch = _torch()
+    if out is None:
+        return (torch.empty_like(xq), torch.empty_like(xk), torch.empty_like(xv),
+                torch.empty((rows, H), dtype=torch.float32, device=dev),
+                torch.empty((rows, H), dtype=torch.float32, device=dev))
+    q, k, v, g, beta = out
+    for name, t, ref in (("q", q, xq), ("k", k, xk), ("v", v, xv)):
+        _check(t, name, dtype=ref.dtype, device=dev)
+        if t.shape != ref.shape:
+            raise ValueError(f"{name} must have the shape of x{name}")
+    for name, t in (("g", g), ("beta", beta)):
+        _check(t, name, dtype=torch.float32, device=dev)
+        if t.shape != (rows, H):
+            raise ValueError(f"{name} must be [{rows}, {H}]")
+    return q, k, v, g, beta
+
+
 def frontend_prefill(xq, xk, xv, conv_weight, a, b, A_log, dt_bias, conv_state=None, cu_seqlens=None,
-                     return_conv_state=True, conv_state_out=None):
+                     return_conv_state=True, conv_state_out=None, out=None):
     """Front end of App. A.3 over packed sequences: the 4-tap causal depthwise
     convolution with SiLU on the q, k, v projections and the gates
     g = -exp(A_log) softplus(a + dt_bias), beta = sigmoid(b).
@@ -288,6 +307,7 @@ def frontend_prefill(xq, xk, xv, conv_weight, a, b, A_log, dt_bias, conv_state=N
     [H] fp32; conv_state [N, 3, H(2dk+dv)] (dtype of xq) or None (zeros); cu_seqlens as
     for ``chunk_prefill``.  Returns (q, k, v, g, beta, conv_state_out); conv_state_out
     is None unless asked for (``conv_state_out`` may be the input state: in place).
+    ``out`` optionally gives the (q, k, v, g, beta) tensors to write.
     """
     torch = _torch()
     lib = load_library()
@@ -311,11 +331,7 @@ def frontend_prefill(xq, xk, xv, conv_weight, a, b, A_log, dt_bias, conv_state=N
         _check(conv_state_out, "conv_state_out", dtype=dt, device=dev)
         if conv_state_out.shape != (N, 3, ctot):
             raise ValueError(f"conv_state_out must be [{N}, 3, {ctot}]")
-    q = torch.empty_like(xq)
-    k = torch.empty_like(xk)
-    v = torch.empty_like(xv)
-    g = torch.empty((T, H), dtype=torch.float32, device=dev)
-    beta = torch.empty((T, H), dtype=torch.float32, device=dev)
+    q, k, v, g, beta = _frontend_outputs(out, xq, xk, xv, T, H, dev)
     st = lib.gdn_frontend_prefill(_ptr(xq), _ptr(xk), _ptr(xv), _ptr(conv_weight), _ptr(a), _ptr(b), _ptr(A_log),
                                   _ptr(dt_bias), _ptr(conv_state), _ptr(cu_dev), N, T, H, dk, dv, _dtype_code(xq),
                                   _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(conv_state_out), _stream(dev))
@@ -324,21 +340,17 @@ def frontend_prefill(xq, xk, xv, conv_weight, a, b, A_log, dt_bias, conv_state=N
     return q, k, v, g, beta, conv_state_out
 
 
-def frontend_decode(xq, xk, xv, conv_weight, a, b, A_log, dt_bias, conv_state):
+def frontend_decode(xq, xk, xv, conv_weight, a, b, A_log, dt_bias, conv_state, out=None):
     """Front end for one decode token per sequence: xq, xk [N, H, dk]; xv [N, H, dv];
     a, b [N, H]; conv_state [N, 3, H(2dk+dv)] updated in place.  Returns (q, k, v, g, beta),
-    the inputs of ``decode_step``."""
+    the inputs of ``decode_step``; ``out`` optionally gives those five tensors."""
     torch = _torch()
     lib = load_library()
     dev, dt, N, H, dk, dv, ctot = _frontend_args(xq, xk, xv, conv_weight, a, b, A_log, dt_bias)
     _check(conv_state, "conv_state", dtype=dt, device=dev)
     if conv_state.shape != (N, 3, ctot):
         raise ValueError(f"conv_state must be [{N}, 3, {ctot}]")
-    q = torch.empty_like(xq)
-    k = torch.empty_like(xk)
-    v = torch.empty_like(xv)
-    g = torch.empty((N, H), dtype=torch.float32, device=dev)
-    beta = torch.empty((N, H), dtype=torch.float32, device=dev)
+    q, k, v, g, beta = _frontend_outputs(out, xq, xk, xv, N, H, dev)
     st = lib.gdn_frontend_decode(_ptr(xq), _ptr(xk), _ptr(xv), _ptr(conv_weight), _ptr(a), _ptr(b), _ptr(A_log),
                                  _ptr(dt_bias), _ptr(conv_state), N, H, dk, dv, _dtype_code(xq), _ptr(q), _ptr(k),
                                  _ptr(v), _ptr(g), _ptr(beta), _stream(dev))

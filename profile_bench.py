@@ -37,7 +37,9 @@ import sys
 ROOT = os.path.dirname(os.path.abspath(__file__))
 OUT = os.path.join(ROOT, "gpurun_out", "profile_bench")
 PROFILES = os.path.join(ROOT, "profiles")
-KERNELS = ("chain_kernel", "intra_kernel", "output_kernel", "decode_kernel", "chunk_table_kernel")
+# more specific names first: a kernel is keyed by the first entry its name contains
+KERNELS = ("conv_silu_kernel", "conv_decode_kernel", "chain_kernel", "intra_kernel", "output_kernel", "decode_kernel",
+           "chunk_table_kernel")
 COPY_BYTES = 1 << 30
 BENCH_TRACE = ["bench.py", "--steps", "5", "--warmup", "2", "--decode-steps", "32", "--no-cpu-baseline"]
 BENCH_PMC = ["bench.py", "--steps", "1", "--warmup", "1", "--decode-steps", "4", "--no-cpu-baseline"]
@@ -122,7 +124,7 @@ def render_trace():
         for r in csv.DictReader(f):
             rows.append((r["Name"], int(r["Calls"]), float(r["AverageNs"]), float(r["MinNs"]), float(r["MaxNs"]),
                          float(r["Percentage"])))
-    lines = ["# Kernel trace: 64K-token prefill (H=6, d=256, bf16) and batched decode", "",
+    lines = ["# Kernel trace: 64K-token prefill (H=6, d=256, bf16), batched decode, front end", "",
              "Command (repository root, one MI355X):", "", "```", cmd, "```", "",
              "| kernel | calls | avg us | min us | max us | % of GPU time |", "|---|---|---|---|---|---|"]
     for name, calls, avg, mn, mx, pct in rows:
@@ -183,7 +185,7 @@ def mode_traffic():
         if not profiler_ok(rc, d, "counter_collection.csv") or counter_sums(d).get("copy") is None:
             raise SystemExit(f"copy calibration for {counter} failed (exit {rc})")
         rc, d, cmd = launch(BENCH_PMC, ["--pmc", counter, "--kernel-include-regex",
-                                        "chain_kernel|intra_kernel|output_kernel|decode_kernel"],
+                                        "chain_kernel|intra_kernel|output_kernel|decode_kernel|conv_silu_kernel"],
                             f"bench_{counter}", 600)
         cmds.append(cmd)
         if not profiler_ok(rc, d, "counter_collection.csv"):
