@@ -128,7 +128,7 @@ def render_trace():
              "Command (repository root, one MI355X):", "", "```", cmd, "```", "",
              "| kernel | calls | avg us | min us | max us | % of GPU time |", "|---|---|---|---|---|---|"]
     for name, calls, avg, mn, mx, pct in rows:
-        short = name.split("(")[0].replace("void ", "")
+        short = name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
         lines.append(f"| `{short}` | {calls} | {avg / 1e3:.1f} | {mn / 1e3:.1f} | {mx / 1e3:.1f} | {pct:.1f} |")
     lines += ["", "Bench JSON line of the same run:", "", "```", bench_line, "```", ""]
     path = os.path.join(PROFILES, "prefill64k_decode_kernel_trace.md")
