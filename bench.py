@@ -39,6 +39,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
@@ -216,7 +218,70 @@ def bench_decode(torch, gdn, synth, n_steps, warmup=3):
     torch.cuda.synchronize()
     gated = evs[0].elapsed_time(evs[1]) / n_steps
     log(f"[bench] gated decode {n_steps} steps: mean {gated * 1e3:.1f} us/step")
-    return dict(ms_per_step=ms, median_ms=med, gated_ms=gated)
+    # the same n_steps launches captured once in a HIP graph and replayed
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            for s in range(n_steps):
+                gdn.decode_step(*per_step[s], state, out=o)
+    torch.cuda.current_stream(dev).wait_stream(side)
+    graph.replay()
+    torch.cuda.synchronize()
+    evs[0].record()
+    graph.replay()
+    evs[1].record()
+    torch.cuda.synchronize()
+    graphed = evs[0].elapsed_time(evs[1]) / n_steps
+    log(f"[bench] decode {n_steps} steps in one HIP graph: {graphed * 1e3:.1f} us/step")
+    return dict(ms_per_step=ms, median_ms=med, gated_ms=gated, graph_ms=graphed)
+
+
+def bench_prefill_other(torch, gdn, synth, steps, warmup):
+    """The two other prefill workloads, timed as whole-prefill calls: 8K tokens
+    (B=1, H=6, d=256, bf16) and the packed 2M-token batch (16 sequences,
+    log-uniform lengths in [4K, 512K])."""
+    dev = torch.device("cuda:0")
+    res = {}
+    inp = synth.prefill_inputs(8192, H, DK, DV, "bf16", seed=synth.seed_for("prefill8k"))
+    q, k, v = (synth.to_torch(x, dev, bf16=True) for x in (inp.q, inp.k, inp.v))
+    g, beta = synth.to_torch(inp.g, dev), synth.to_torch(inp.beta, dev)
+    cases = [("prefill_8k", (q, k, v, g, beta), None, None)]
+    lengths = synth.varlen_lengths(synth.seed_for("varlen2m"))
+    log(f"[bench] generating the 2M-token packed batch (lengths {list(map(int, lengths))})")
+    vq, vk, vv, vg, vb, cu = synth.varlen_torch_inputs(lengths, H, DK, DV, synth.seed_for("varlen2m"), dev)
+    cu_host = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    cases.append(("varlen_2m", (vq, vk, vv, vg, vb), cu_host, lengths))
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    for name, (a, b, c, d, e), cuh, lens in cases:
+        Tn, N = a.shape[0], (1 if cuh is None else len(lens))
+        o = torch.empty((Tn, H, DV), dtype=torch.bfloat16, device=dev)
+        fs = torch.empty((N, H, DV, DK), dtype=torch.float32, device=dev)
+        ws = torch.empty(gdn.prefill_workspace_size(Tn, N, H, DK, DV, C), dtype=torch.uint8, device=dev)
+        cu_arg = None if cuh is None else torch.from_numpy(cuh)
+        run = lambda: gdn.chunk_prefill(a, b, c, d, e, cu_seqlens=cu_arg, chunk=C, out=o, final_state=fs,
+                                        workspace=ws)
+        n_steps = steps if cuh is None else max(2, steps // 3)
+        for _ in range(max(1, warmup)):
+            run()
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(n_steps):
+            run()
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / n_steps
+        ent = {"tokens": int(Tn), "ms_per_step": ms, "tokens_per_s": Tn / (ms / 1e3),
+               "mfma_frac": flops_path_per_token() * Tn / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+               "min_traffic_hbm_frac": Tn * H * ((2 * DK + 2 * DV) * 2 + 8) / (ms / 1e3) / 1e9 / PEAK_HBM_GBPS}
+        if lens is not None:
+            ent["lengths"] = [int(x) for x in lens]
+        res[name] = ent
+        log(f"[bench] {name}: {ms:.3f} ms/step, {ent['tokens_per_s'] / 1e6:.1f} M tokens/s")
+        del o, fs, ws
+    return res
 
 
 def frontend_bytes(tokens):
@@ -318,6 +383,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=128)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other", action="store_true", help="skip the 8K and 2M-token prefill figures")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -336,6 +402,7 @@ def main():
     pre = bench_prefill(torch, gdn, synth, a.steps, a.warmup)
     dec = None if a.no_decode else bench_decode(torch, gdn, synth, a.decode_steps)
     fe = bench_frontend(torch, gdn, synth, a.steps, a.warmup)
+    other = None if a.no_other else bench_prefill_other(torch, gdn, synth, a.steps, a.warmup)
 
     tok_s = T / (pre["ms_per_step"] / 1e3)
     chain_flops = flops_chain_per_token() * T
@@ -397,6 +464,7 @@ def main():
             "ms_per_step": dec["ms_per_step"],
             "median_ms_per_step": dec["median_ms"],
             "gated_rmsnorm_ms_per_step": dec["gated_ms"],
+            "hip_graph_ms_per_step": dec["graph_ms"],
             "tokens_per_s": DEC_N / (dec["ms_per_step"] / 1e3),
             "state_GBps": state_gbps,
             "roofline": {"kernel": "decode_kernel", "bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_GBPS,
@@ -404,6 +472,8 @@ def main():
                          "traffic": traffic_from_profiles("decode_kernel"),
                          "algorithmic_bytes_per_launch": b},
         }
+    if other is not None:
+        out["prefill"]["other_workloads"] = other
     fb = frontend_bytes(T)
     ctot = H * (2 * DK + DV)
     dec_fb = 2 * DEC_N * ctot * 2 + 2 * 3 * DEC_N * ctot * 2 + 4 * DEC_N * H * 4 + ctot * 16

@@ -41,8 +41,8 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNELS = ("conv_silu_kernel", "conv_decode_kernel", "chain_kernel", "intra_kernel", "output_kernel", "decode_kernel",
            "chunk_table_kernel")
 COPY_BYTES = 1 << 30
-BENCH_TRACE = ["bench.py", "--steps", "5", "--warmup", "2", "--decode-steps", "32", "--no-cpu-baseline"]
-BENCH_PMC = ["bench.py", "--steps", "1", "--warmup", "1", "--decode-steps", "4", "--no-cpu-baseline"]
+BENCH_TRACE = ["bench.py", "--steps", "5", "--warmup", "2", "--decode-steps", "32", "--no-cpu-baseline", "--no-other"]
+BENCH_PMC = ["bench.py", "--steps", "1", "--warmup", "1", "--decode-steps", "4", "--no-cpu-baseline", "--no-other"]
 
 
 def log(*a):

@@ -87,3 +87,43 @@ def test_decode_deterministic():
     o2 = gdn.decode_step(*args, s2)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+def test_decode_steps_in_a_hip_graph_match_eager():
+    """Consecutive decode steps captured once in a HIP graph: every replay, with
+    eager work and synchronisations between replays, equals the same steps run
+    eagerly from the same state (bit for bit), and the first replay matches the
+    oracle."""
+    N, H, dk, dv, steps, seed = 8, 3, 256, 256, 4, 4242
+    st0 = torch.from_numpy(synth.decode_state(N, H, dk, dv, seed)).to(DEV)
+    ins = [[_tt(x, b) for x, b in zip(synth.decode_step_inputs(N, H, dk, dv, "bf16", seed, s),
+                                      (True, True, True, False, False))] for s in range(steps)]
+    outs = [torch.empty((N, H, dv), dtype=torch.bfloat16, device=DEV) for _ in range(steps)]
+    state = st0.clone()
+    # eager reference from st0
+    ref_state = st0.clone()
+    ref_outs = [gdn.decode_step(*ins[s], ref_state).clone() for s in range(steps)]
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream(device=DEV)
+    side.wait_stream(torch.cuda.current_stream(DEV))
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            for s in range(steps):
+                gdn.decode_step(*ins[s], state, out=outs[s])
+    torch.cuda.current_stream(DEV).wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        state.copy_(st0)                       # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(state, ref_state), rep
+        for s in range(steps):
+            assert torch.equal(outs[s], ref_outs[s]), (rep, s)
+    ref = np.ascontiguousarray(st0.cpu().numpy().astype(np.float64))
+    for s in range(steps):
+        q, k, v, g, beta = synth.decode_step_inputs(N, H, dk, dv, "bf16", seed, s)
+        o_ref = oracle.decode_step(q, k, v, g, beta, ref, bf16=True)
+        assert bound_ratio(outs[s].float().cpu().numpy(), o_ref, TOL_BF16, stored_bf16=True) <= 1.0
+    assert rel_err(state.cpu().numpy(), ref) <= TOL_BF16
