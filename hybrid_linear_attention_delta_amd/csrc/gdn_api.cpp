@@ -77,6 +77,8 @@ PrefillLayout prefill_layout(int64_t T, int32_t N, int32_t H, int32_t dk, int32_
     off = align_up(off + (size_t)L.max_chunks * 16, 256);
     L.off_seq_first = off;
     off = align_up(off + ((size_t)N + 1) * 4, 256);
+    L.off_seq_order = off;
+    off = align_up(off + (size_t)N * 4, 256);
     L.off_records = off;
     off = align_up(off + (size_t)L.max_chunks * H * L.record_bytes, 256);
     // outputs of the state chain for the output kernel

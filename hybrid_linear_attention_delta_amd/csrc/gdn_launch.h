@@ -38,6 +38,7 @@ struct PrefillLayout {
     size_t off_header;      // int32[16]: [0] error flag, [1] number of chunks
     size_t off_chunk_tab;   // int32[max_chunks][4]: tok0, len, seq, 0
     size_t off_seq_first;   // int32[N + 1]: first chunk of each sequence
+    size_t off_seq_order;   // int32[N]: sequences by descending length (the chain's dispatch order)
     size_t off_records;     // per chunk-head operand records
     size_t record_bytes;    // bytes of one record
     size_t off_states;      // per chunk-head state entering the chunk [dv][dk], operand type

@@ -247,13 +247,21 @@ struct ChunkInfo {
     int32_t tok0, len, seq, pad;
 };
 
+// Sequences ranked by length for the state chain's dispatch order up to this
+// many sequences (the ranking is quadratic); beyond it, the order of the batch.
+constexpr int32_t kSortMax = 2048;
+
 // One workgroup.  Validates cu_seqlens (0 = c_0 <= ... <= c_N = T), writes the
 // first chunk of every sequence and the (tok0, len, seq) of every chunk.  On
 // invalid input it raises header[0] and publishes zero chunks, so later
-// kernels touch nothing.
+// kernels touch nothing.  Also writes order[r] = the sequence of rank r by
+// length (longest first, ties by index): the chain hands its workgroups to
+// (sequence, head) pairs in this order, so the longest sequential chains are
+// dispatched first and the shorter ones fill the CUs around them.
 __global__ __launch_bounds__(256) void chunk_table_kernel(const int32_t* __restrict__ cu, int32_t N, int64_t T,
                                                           int32_t C, int64_t max_chunks, int32_t* __restrict__ header,
-                                                          ChunkInfo* __restrict__ tab, int32_t* __restrict__ first)
+                                                          ChunkInfo* __restrict__ tab, int32_t* __restrict__ first,
+                                                          int32_t* __restrict__ order)
 {
     __shared__ int64_t part[256];
     __shared__ int bad;
@@ -295,6 +303,18 @@ __global__ __launch_bounds__(256) void chunk_table_kernel(const int32_t* __restr
         header[1] = (int32_t)tot;
     }
     __syncthreads();
+    for (int32_t i = t; i < N; i += 256) {
+        int32_t r = i;
+        if (N <= kSortMax) {
+            const int32_t Li = max(cu[i + 1] - cu[i], 0);
+            r = 0;
+            for (int32_t j = 0; j < N; ++j) {
+                const int32_t Lj = max(cu[j + 1] - cu[j], 0);
+                r += (Lj > Li || (Lj == Li && j < i)) ? 1 : 0;
+            }
+        }
+        order[r] = i;  // ranks form a permutation of 0 .. N-1
+    }
     for (int64_t j = t; j < tot; j += 256) {
         int32_t lo = 0, hi = N - 1;  // last n with first[n] <= j
         while (lo < hi) {
@@ -1207,11 +1227,13 @@ __device__ __forceinline__ void wait_vmcnt()
 // waves in the staged form, else by the compute waves).
 // Workgroups are mapped so that all row tiles of one (sequence, head) pair run
 // on one XCD (workgroups are dealt to the 8 XCDs round-robin): they read the
-// same per-chunk records, which then come from that XCD's L2.
+// same per-chunk records, which then come from that XCD's L2.  Pair indices
+// follow seq_order (longest sequence first) in a packed batch, so when there
+// are more workgroups than CUs the longest chains start in the first round.
 template <typename TIn, int C, int DK, int DV, int NW, bool SEG>
 __global__ __launch_bounds__((NW + chain_loaders<TIn, C>()) * 64) void chain_kernel(
-    const int32_t* __restrict__ header, const int32_t* __restrict__ seq_first, int32_t varlen, int64_t T, int32_t H,
-    int32_t pairs, const unsigned char* records, size_t record_bytes, const float* init_state,
+    const int32_t* __restrict__ header, const int32_t* __restrict__ seq_first,
+    const int32_t* __restrict__ seq_order, int32_t varlen, int64_t T, int32_t H, int32_t pairs, const unsigned char* records, size_t record_bytes, const float* init_state,
     float* final_state, TIn* __restrict__ states, TIn* __restrict__ deltas, int64_t seg_begin, int64_t seg_end,
     float* carry)
 // (records is deliberately not __restrict__: a restrict read-only argument lets
@@ -1247,7 +1269,7 @@ __global__ __launch_bounds__((NW + chain_loaders<TIn, C>()) * 64) void chain_ker
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
     const int pair = xcd + 8 * (slot / TILES);
     if (pair >= pairs) return;
-    const int n = pair / H, h = pair % H;
+    const int n = varlen ? seq_order[pair / H] : pair / H, h = pair % H;  // longest sequences first
     const int tile = slot % TILES;
     const int row0 = tile * 16;  // first state row (value index) of this workgroup
 
@@ -1847,6 +1869,7 @@ static hipError_t run_prefill(const PrefillArgs& a)
     int32_t* header = reinterpret_cast<int32_t*>(a.ws + a.lay.off_header);
     ChunkInfo* tab = reinterpret_cast<ChunkInfo*>(a.ws + a.lay.off_chunk_tab);
     int32_t* first = reinterpret_cast<int32_t*>(a.ws + a.lay.off_seq_first);
+    int32_t* order = reinterpret_cast<int32_t*>(a.ws + a.lay.off_seq_order);
     unsigned char* records = a.ws + a.lay.off_records;
     TIn* states = reinterpret_cast<TIn*>(a.ws + a.lay.off_states);
     TIn* deltas = reinterpret_cast<TIn*>(a.ws + a.lay.off_deltas);
@@ -1890,11 +1913,11 @@ static hipError_t run_prefill(const PrefillArgs& a)
         const dim3 grid((uint32_t)chain_blocks), block((NW + chain_loaders<TIn, C>()) * 64);
         if (seg)
             hipLaunchKernelGGL((chain_kernel<TIn, C, DK, DV, NW, true>), grid, block, sizeof(Lds), st, header, first,
-                               varlen, a.T, a.H, (int32_t)pairs, records, a.lay.record_bytes, a.init_state,
+                               order, varlen, a.T, a.H, (int32_t)pairs, records, a.lay.record_bytes, a.init_state,
                                a.final_state, states, deltas, c0, c1, carry);
         else
             hipLaunchKernelGGL((chain_kernel<TIn, C, DK, DV, NW, false>), grid, block, sizeof(Lds), st, header, first,
-                               varlen, a.T, a.H, (int32_t)pairs, records, a.lay.record_bytes, a.init_state,
+                               order, varlen, a.T, a.H, (int32_t)pairs, records, a.lay.record_bytes, a.init_state,
                                a.final_state, states, deltas, c0, c1, carry);
         return hipGetLastError();
     };
@@ -1929,7 +1952,7 @@ static hipError_t run_prefill(const PrefillArgs& a)
 
     if ((a.stages & 1) && varlen) {
         hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(256), 0, a.stream, a.cu_seqlens, a.N, a.T, (int32_t)C,
-                           a.lay.max_chunks, header, tab, first);
+                           a.lay.max_chunks, header, tab, first, order);
         GDN_TRY(hipGetLastError());
     }
 
