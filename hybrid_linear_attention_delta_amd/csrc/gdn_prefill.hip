@@ -1962,9 +1962,13 @@ static hipError_t run_prefill(const PrefillArgs& a)
     // on its own half of the CUs while the intra-chunk kernel prepares later
     // segments and the output kernel finishes earlier ones on the other half;
     // events order each segment's three kernels.
-    constexpr int64_t SEG_MIN = 64;
+    // The hand-offs between the pipeline streams cost about 0.14 ms per call
+    // (measured: 8K tokens 0.38 ms pipelined against 0.24 ms stage by stage),
+    // which the overlap repays only past about 36K tokens of one sequence
+    // (32K: 1.07 against 1.04 ms; 40K: 1.26 against 1.30 ms).
+    constexpr int64_t SEG_MIN = 64, PIPE_MIN_CHUNKS = 576;
     int nseg = 1;
-    if (a.stages == 7 && chain_blocks <= 128 && grid_chunks >= 2 * SEG_MIN)
+    if (a.stages == 7 && chain_blocks <= 128 && grid_chunks >= PIPE_MIN_CHUNKS)
         nseg = (int)std::min<int64_t>(4, grid_chunks / SEG_MIN);
     if (nseg == 1) {
         if (a.stages & 1) GDN_TRY(launch_intra(0, grid_chunks, a.stream));

@@ -62,9 +62,10 @@ def test_prefill_gated_matches_oracle(dtype, T, H, dk, dv, C, lens, use_w, eps):
 
 
 def test_prefill_gated_pipelined_equals_oracle():
-    """A long sequence takes the segmented (pipelined) path; the epilogue runs in
-    every segment's output launch."""
-    T, H, d = 8300, 2, 256
+    """A long sequence (past the pipeline's 576-chunk threshold) takes the
+    segmented (pipelined) path; the epilogue runs in every segment's output
+    launch."""
+    T, H, d = 37000, 2, 256
     inp = synth.prefill_inputs(T, H, d, d, "bf16", seed=977, gate="slow")
     z, w = synth.norm_inputs((T, H, d), "bf16", 977)
     t = lambda a, b=False: synth.to_torch(a, DEV, bf16=b)
