@@ -54,6 +54,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 
 #include "gdn_common.h"
@@ -1804,6 +1805,7 @@ __global__ __launch_bounds__(256) void output_kernel(const int32_t* __restrict__
 // (the driver numbers CUs round-robin over the XCDs).
 struct PipeRes {
     static constexpr int MAX_SEG = 16;
+    std::mutex use;  // held while one call enqueues its pipeline: the events are reused by every call
     int dev = -1;
     uint8_t chain_cus[8] = {0, 0, 0, 0, 0, 0, 0, 0};  // CUs of each XCD reserved for the chain
     hipStream_t chain_s = nullptr, intra_s = nullptr, out_s = nullptr;
@@ -1861,6 +1863,25 @@ static hipError_t pipe_res(const uint8_t* chain_cus, PipeRes** out)
     return hipSuccess;
 }
 
+// Raises a kernel's dynamic-LDS limit once per (kernel, device): the attribute
+// belongs to the device that is current, and first callers racing on one
+// device both store the same value.
+constexpr int kMaxDevices = 64;
+struct SmemAttr {
+    std::atomic<bool> done[kMaxDevices]{};
+};
+static hipError_t ensure_smem(SmemAttr& at, const void* fn, int bytes)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const bool cached = dev >= 0 && dev < kMaxDevices;
+    if (cached && at.done[dev].load(std::memory_order_acquire)) return hipSuccess;
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess && cached) at.done[dev].store(true, std::memory_order_release);
+    return e;
+}
+
 template <typename TIn, int C, int DK, int DV>
 static hipError_t run_prefill(const PrefillArgs& a)
 {
@@ -1885,13 +1906,9 @@ static hipError_t run_prefill(const PrefillArgs& a)
         if (c1 <= c0) return hipSuccess;
         size_t smem = sizeof(IntraSmem<TIn, C, DK, DV>);
         if constexpr (sizeof(TIn) == 2 && C == 64) smem = sizeof(IntraBfSmem<DK, DV>);
-        static bool attr = false;  // idempotent attribute; racing writers store the same value
-        if (!attr) {
-            hipError_t e = hipFuncSetAttribute((const void*)intra_kernel<TIn, C, DK, DV>,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-            if (e != hipSuccess) return e;
-            attr = true;
-        }
+        static SmemAttr attr;
+        const hipError_t e = ensure_smem(attr, (const void*)intra_kernel<TIn, C, DK, DV>, (int)smem);
+        if (e != hipSuccess) return e;
         hipLaunchKernelGGL((intra_kernel<TIn, C, DK, DV>), dim3((uint32_t)(c1 - c0), a.H), dim3(256), smem,
                            st, (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, a.g, a.beta, header, tab, varlen,
                            a.T, a.H, a.l2norm, records, a.lay.record_bytes, c0, c1);
@@ -1904,12 +1921,9 @@ static hipError_t run_prefill(const PrefillArgs& a)
         const bool seg = !(c0 == 0 && c1 == ALL);
         const void* fn = seg ? (const void*)chain_kernel<TIn, C, DK, DV, NW, true>
                              : (const void*)chain_kernel<TIn, C, DK, DV, NW, false>;
-        static bool attr[2] = {false, false};  // idempotent attributes; racing writers store the same value
-        if (!attr[seg]) {
-            hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(Lds));
-            if (e != hipSuccess) return e;
-            attr[seg] = true;
-        }
+        static SmemAttr attr[2];
+        const hipError_t e = ensure_smem(attr[seg], fn, (int)sizeof(Lds));
+        if (e != hipSuccess) return e;
         const dim3 grid((uint32_t)chain_blocks), block((NW + chain_loaders<TIn, C>()) * 64);
         if (seg)
             hipLaunchKernelGGL((chain_kernel<TIn, C, DK, DV, NW, true>), grid, block, sizeof(Lds), st, header, first,
@@ -1927,12 +1941,9 @@ static hipError_t run_prefill(const PrefillArgs& a)
         const size_t smem = OutCfg<TIn, C, DK, DV>::lds_bytes(gated);
         const void* fn = gated ? (const void*)output_kernel<TIn, C, DK, DV, true>
                                : (const void*)output_kernel<TIn, C, DK, DV, false>;
-        static bool attr[2] = {false, false};  // idempotent attributes; racing writers store the same value
-        if (!attr[gated]) {
-            hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-            if (e != hipSuccess) return e;
-            attr[gated] = true;
-        }
+        static SmemAttr attr[2];
+        const hipError_t e = ensure_smem(attr[gated], fn, (int)smem);
+        if (e != hipSuccess) return e;
         const dim3 grid((uint32_t)(c1 - c0), a.H);
         if (gated)
             hipLaunchKernelGGL((output_kernel<TIn, C, DK, DV, true>), grid, dim3(256), smem, st, header, tab, varlen,
@@ -1993,6 +2004,8 @@ static hipError_t run_prefill(const PrefillArgs& a)
         GDN_TRY(launch_output(0, grid_chunks, a.stream));
         return hipSuccess;
     }
+    // One call at a time records and waits on this device's pipeline events.
+    std::lock_guard<std::mutex> pipe_lock(pr->use);
     const int64_t seg = (grid_chunks + nseg - 1) / nseg;
     auto seg_lo = [&](int s) { return std::min<int64_t>(grid_chunks, (int64_t)s * seg); };
     // The first segment's preparation and the last segment's outputs run on the

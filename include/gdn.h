@@ -23,7 +23,11 @@
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers unless the name ends in _host.
  *   - The caller owns and allocates every buffer (including the workspace);
- *     the library never allocates device memory and keeps no global state.
+ *     the library never allocates device memory.  Its only process-wide
+ *     state: per device, the three streams and the events of the pipelined
+ *     prefill (created by the first prefill long enough to use them, kept
+ *     until the process ends), and the kernels' LDS limits, raised once per
+ *     device.  Calls that share those streams enqueue one at a time.
  *   - Work is enqueued on `stream` and runs asynchronously; no call
  *     synchronises the device (unless GDN_DEBUG_SYNC=1 is set, which makes
  *     each call wait for its kernels and report launch/device errors).

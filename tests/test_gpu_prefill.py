@@ -249,3 +249,39 @@ def test_varlen_2m_workload_checked_subsets():
         if n in shortest:
             es = rel_err(fs[n:n + 1][:, :, rows].cpu().numpy(), fs_ref[:, :, rows])
             assert es <= TOL_BF16, (n, es)
+
+
+def test_concurrent_pipelined_calls_from_two_threads():
+    """Two host threads enqueue long (pipelined) prefills on their own streams at
+    the same time; the pipeline's shared streams and events are used by one call
+    at a time, so both results equal a single-threaded run bit for bit."""
+    import threading
+
+    T, H, d = 37000, 2, 256
+    inps = [synth.prefill_inputs(T, H, d, d, "bf16", seed=600 + i, gate="slow") for i in range(2)]
+    t = lambda a, b=False: synth.to_torch(a, DEV, bf16=b)
+    args = [(t(x.q, True), t(x.k, True), t(x.v, True), t(x.g), t(x.beta)) for x in inps]
+    ref = [gdn.chunk_prefill(*a) for a in args]
+    torch.cuda.synchronize()
+    ref = [(o.clone(), s.clone()) for o, s in ref]
+    results = [None, None]
+    streams = [torch.cuda.Stream(device=DEV) for _ in range(2)]
+    barrier = threading.Barrier(2)
+
+    def work(i):
+        with torch.cuda.stream(streams[i]):
+            outs = []
+            barrier.wait()
+            for _ in range(3):
+                outs.append(gdn.chunk_prefill(*args[i]))
+            streams[i].synchronize()
+            results[i] = outs
+
+    th = [threading.Thread(target=work, args=(i,)) for i in range(2)]
+    for x in th:
+        x.start()
+    for x in th:
+        x.join()
+    for i in range(2):
+        for o, s in results[i]:
+            assert torch.equal(o, ref[i][0]) and torch.equal(s, ref[i][1]), i
