@@ -242,3 +242,4 @@ def gated_rmsnorm(o, z, weight=None, eps=DEFAULT_NORM_EPS, bf16=False, mutation=
 # ----------------------------------------------------------------- front end (conv + gates)
 
 from .frontend import CONV_MUTATIONS, GATE_MUTATIONS, gates, short_conv_silu  # noqa: E402,F401
+from .backward import BWD_MUTATIONS, prefill_vjp  # noqa: E402,F401

@@ -1,0 +1,100 @@
+"""Pins of the gradient oracle (``oracle/backward.py``): the vector-Jacobian
+product of the gated delta rule ("Long-Context Aware Upcycling", App. A.3,
+Eqs. 16-19).  It is tied to the forward oracle (the C recurrence, which shares
+no code with it) by central finite differences, and to closed forms.  Each
+planted mistake must fail a pin."""
+import numpy as np
+import pytest
+
+import oracle
+
+
+def _case(seed, l2=True):
+    rng = np.random.default_rng(seed)
+    cu = np.array([0, 4, 7], dtype=np.int64)
+    T, H, dk, dv = 7, 2, 3, 2
+    x = dict(q=rng.standard_normal((T, H, dk)), k=rng.standard_normal((T, H, dk)),
+             v=rng.standard_normal((T, H, dv)), g=-rng.uniform(0.1, 1.0, (T, H)),
+             beta=rng.uniform(0.2, 0.9, (T, H)), init=rng.standard_normal((2, H, dv, dk)) * 0.5)
+    do = rng.standard_normal((T, H, dv))
+    ds = rng.standard_normal((2, H, dv, dk))
+    return x, do, ds, cu
+
+
+def _loss(x, do, ds, cu, l2):
+    o, fs = oracle.prefill(x["q"], x["k"], x["v"], x["g"], x["beta"], x["init"], cu_seqlens=cu, qk_l2norm=l2,
+                           n_threads=1)
+    return float(np.sum(do * o) + np.sum(ds * fs))
+
+
+def check_finite_differences(mutation=0, l2=True):
+    """Central differences (h = 1e-5) of L = <do, o> + <dS, S_final> through the
+    forward oracle agree with the gradient oracle for every input element."""
+    x, do, ds, cu = _case(3, l2)
+    gr = oracle.prefill_vjp(x["q"], x["k"], x["v"], x["g"], x["beta"], do, ds, x["init"], cu_seqlens=cu,
+                            qk_l2norm=l2, mutation=mutation)
+    names = {"q": "dq", "k": "dk", "v": "dv", "g": "dg", "beta": "dbeta", "init": "dinit"}
+    h = 1e-5
+    worst = 0.0
+    for key, gkey in names.items():
+        a = x[key]
+        fd = np.zeros_like(a)
+        for idx in np.ndindex(a.shape):
+            old = a[idx]
+            a[idx] = old + h
+            lp = _loss(x, do, ds, cu, l2)
+            a[idx] = old - h
+            lm = _loss(x, do, ds, cu, l2)
+            a[idx] = old
+            fd[idx] = (lp - lm) / (2 * h)
+        worst = max(worst, float(np.max(np.abs(fd - gr[gkey]))) / max(1.0, float(np.max(np.abs(fd)))))
+    return worst < 1e-7
+
+
+def check_identity_gates_closed_form(mutation=0):
+    """alpha = 1, beta = 0, no normalisation: the state never changes, so
+    dS_0 = dS_N + scale sum_t do_t q_t^T, dq_t = scale S_0^T do_t, dv = 0."""
+    x, do, ds, cu = _case(4, False)
+    x["g"][:] = 0.0
+    x["beta"][:] = 0.0
+    scale = 0.7
+    gr = oracle.prefill_vjp(x["q"], x["k"], x["v"], x["g"], x["beta"], do, ds, x["init"], cu_seqlens=cu,
+                            scale=scale, qk_l2norm=False, mutation=mutation)
+    ok = np.allclose(gr["dv"], 0.0, atol=0)
+    for n in range(2):
+        s, e = cu[n], cu[n + 1]
+        for hh in range(2):
+            ref = ds[n, hh] + scale * sum(np.outer(do[t, hh], x["q"][t, hh]) for t in range(s, e))
+            ok &= np.allclose(gr["dinit"][n, hh], ref, rtol=1e-13, atol=1e-13)
+            for t in range(s, e):
+                ok &= np.allclose(gr["dq"][t, hh], scale * x["init"][n, hh].T @ do[t, hh], rtol=1e-13, atol=1e-13)
+    return bool(ok)
+
+
+def check_normalised_grads_are_orthogonal(mutation=0):
+    """With eps = 0 the outputs do not change when q_t or k_t is scaled, so each
+    dq_t is orthogonal to q_t and each dk_t to k_t."""
+    x, do, ds, cu = _case(5)
+    gr = oracle.prefill_vjp(x["q"], x["k"], x["v"], x["g"], x["beta"], do, ds, x["init"], cu_seqlens=cu, eps=0.0,
+                            mutation=mutation)
+    dots = [np.sum(gr["dq"] * x["q"], axis=-1), np.sum(gr["dk"] * x["k"], axis=-1)]
+    mags = max(float(np.max(np.abs(gr["dq"]))), float(np.max(np.abs(gr["dk"]))))
+    return bool(max(float(np.max(np.abs(d))) for d in dots) < 1e-12 * max(1.0, mags))
+
+
+BWD_CHECKS = [check_finite_differences, check_identity_gates_closed_form, check_normalised_grads_are_orthogonal]
+
+
+@pytest.mark.parametrize("check", BWD_CHECKS, ids=lambda c: c.__name__)
+def test_backward_pin(check):
+    assert check()
+
+
+def test_finite_differences_without_normalisation():
+    assert check_finite_differences(l2=False)
+
+
+@pytest.mark.parametrize("name", sorted(oracle.BWD_MUTATIONS))
+def test_backward_planted_mistakes_are_caught(name):
+    m = oracle.BWD_MUTATIONS[name]
+    assert not all(check(mutation=m) for check in BWD_CHECKS), name
