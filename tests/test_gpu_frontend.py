@@ -211,3 +211,21 @@ def test_frontend_rejects_bad_arguments():
     hh = torch.zeros(H, device=DEV)
     with pytest.raises(gdn.GdnError):
         gdn.frontend_prefill(xq, xq, xv, w, ab, ab, hh, hh)
+
+
+def test_frontend_then_pipelined_prefill_sampled_rows():
+    """37K tokens (past the prefill's pipelining threshold) through the front end
+    and the pipelined prefill, against the oracle's front end (rounded to bf16)
+    and the oracle recurrence on sampled state rows."""
+    T, H, d = 37000, 2, 256
+    f = synth.frontend_inputs(T, H, d, d, "bf16", seed=99)
+    q, k, v, g, beta, _ = _gpu_frontend(f, T, H, d, d, None, None)
+    o, fs = gdn.chunk_prefill(q, k, v, g, beta)
+    torch.cuda.synchronize()
+    rq, rk, rv, rg, rb, _ = _oracle_frontend(f, H, d, d, None, None)
+    st = lambda y: synth._store(y, "bf16").reshape(T, H, d)
+    rows = [0, 101, 255]
+    o_ref, fs_ref = oracle.prefill(st(rq), st(rk), st(rv), rg.astype(np.float32), rb.astype(np.float32), bf16=True,
+                                   rows=rows)
+    assert bound_ratio(o.float().cpu().numpy()[:, :, rows], o_ref[:, :, rows], TOL_BF16, stored_bf16=True) <= 1.0
+    assert rel_err(fs.cpu().numpy()[:, :, rows], fs_ref[:, :, rows]) <= TOL_BF16
