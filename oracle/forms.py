@@ -83,3 +83,109 @@ def chunked_wy(q, k, v, g, beta, S0, scale, C):
         chunks.append(dict(gamma=gam, A=A, T=Tm, W=W, U=U, Delta=Delta, P=P, S_start=S.copy()))
         S = np.exp(gam[-1]) * S + Delta.T @ (np.exp(gam[-1] - gam)[:, None] * K)
     return o, S, chunks
+
+
+def chunked_wy_vjp(q, k, v, g, beta, S0, scale, C, dO, dS_end):
+    """Gradients of <dO, o> + <dS_end, S_end> for ``chunked_wy`` on one chain,
+    by reverse-mode differentiation of the chunked WY form itself (the form a
+    chunked backward kernel evaluates).  q, k are used as given (normalise them
+    beforehand and apply the normalisation's own gradient after).  Per chunk,
+    in reverse order, with dS the gradient of the state after the chunk and
+    D = diag(e^{gamma_L - gamma}):
+
+        from S_end = e^{gamma_L} S + Delta^T D K:  dS_in  = e^{gamma_L} dS
+                                                  dDelta = D K dS^T,  dK = D Delta dS
+        from O = scale [diag(e^gamma) Q S^T + P Delta]:
+            dQ += diag(e^gamma) dO' S,  dS_in += dO'^T diag(e^gamma) Q,
+            dP = tril(dO' Delta^T),     dDelta += P^T dO'          (dO' = scale dO)
+        from P_rj = (q_r . k_j) e^{gamma_r - gamma_j}:  dQ += (dP o Gamma) K, dK += (dP o Gamma)^T Q
+        from Delta = U - W S^T:  dU = dDelta, dW = -dDelta S, dS_in -= dDelta^T W
+        from U = T diag(b) V, W = T diag(b e^gamma) K:
+            dT = dU (diag(b) V)^T + dW (diag(b e^gamma) K)^T
+            dV = diag(b) T^T dU,  dK += diag(b e^gamma) T^T dW
+        from T = (I + A)^{-1}:  dA = -T^T dT T^T (strictly lower part)
+        from A_rj = b_r (k_r . k_j) e^{gamma_r - gamma_j}:  dK += diag(b)(dA o Gamma) K + (diag(b)(dA o Gamma))^T K
+    and the beta and gamma terms of each product; dg is the reverse cumulative
+    sum of dgamma within the chunk.  Returns dq, dk, dv, dg, dbeta, dS0.
+    """
+    T_, dk = q.shape
+    dv = v.shape[1]
+    _, _, chunks = chunked_wy(q, k, v, g, beta, S0, scale, C)
+    dq = np.zeros_like(q, dtype=np.float64)
+    dkk = np.zeros_like(k, dtype=np.float64)
+    dvv = np.zeros_like(v, dtype=np.float64)
+    dg = np.zeros(T_)
+    db = np.zeros(T_)
+    dS = np.array(dS_end, dtype=np.float64, copy=True)
+    for ci in range(len(chunks) - 1, -1, -1):
+        ch = chunks[ci]
+        c0 = ci * C
+        L = ch["gamma"].shape[0]
+        Q, K, V = q[c0:c0 + L], k[c0:c0 + L], v[c0:c0 + L]
+        b = beta[c0:c0 + L]
+        gam, Tm, W, Delta, P, A, S = ch["gamma"], ch["T"], ch["W"], ch["Delta"], ch["P"], ch["A"], ch["S_start"]
+        eg = np.exp(gam)
+        gL = gam[-1]
+        dd = np.exp(gL - gam)
+        incl = np.tril(np.ones((L, L), dtype=bool), 0)
+        lower = np.tril(np.ones((L, L), dtype=bool), -1)
+        Gam = np.zeros((L, L))
+        Gam[incl] = np.exp((gam[:, None] - gam[None, :])[incl])
+        dgam = np.zeros(L)
+        dQ = np.zeros((L, dk))
+        dK = np.zeros((L, dk))
+        # S_end = e^{gL} S + Delta^T D K
+        dS_in = np.exp(gL) * dS
+        dgL = np.exp(gL) * np.sum(dS * S)
+        dDelta = dd[:, None] * (K @ dS.T)
+        dK += dd[:, None] * (Delta @ dS)
+        d_dd = np.sum(Delta * (K @ dS.T), axis=1)
+        dgL += np.sum(d_dd * dd)
+        dgam -= d_dd * dd
+        # O = scale [diag(e^gam) Q S^T + P Delta]
+        dOs = scale * dO[c0:c0 + L]
+        QS = Q @ S.T
+        dQ += eg[:, None] * (dOs @ S)
+        dS_in += dOs.T @ (eg[:, None] * Q)
+        dgam += eg * np.sum(dOs * QS, axis=1)
+        dP = np.where(incl, dOs @ Delta.T, 0.0)
+        dDelta += P.T @ dOs
+        # P = tril_incl((Q K^T) o Gamma)
+        dPG = dP * Gam
+        dQ += dPG @ K
+        dK += dPG.T @ Q
+        dgam += np.sum(dP * P, axis=1)
+        dgam -= np.sum(dP * P, axis=0)
+        # Delta = U - W S^T
+        dU = dDelta
+        dW = -dDelta @ S
+        dS_in -= dDelta.T @ W
+        # U = T diag(b) V, W = T diag(b e^gam) K
+        Vb = b[:, None] * V
+        Kb = (b * eg)[:, None] * K
+        dT = dU @ Vb.T + dW @ Kb.T
+        dVb = Tm.T @ dU
+        dKb = Tm.T @ dW
+        dV = b[:, None] * dVb
+        db_c = np.sum(dVb * V, axis=1)
+        dK += (b * eg)[:, None] * dKb
+        db_c += eg * np.sum(dKb * K, axis=1)
+        dgam += b * eg * np.sum(dKb * K, axis=1)
+        # T = (I + A)^{-1}
+        dA = np.where(lower, -Tm.T @ dT @ Tm.T, 0.0)
+        # A = tril_strict(diag(b) (K K^T) o Gamma)
+        dAG = dA * Gam
+        dK += (b[:, None] * dAG) @ K
+        dK += (b[:, None] * dAG).T @ K
+        db_c += np.sum(dA * (K @ K.T) * Gam, axis=1)
+        dgam += np.sum(dA * A, axis=1)
+        dgam -= np.sum(dA * A, axis=0)
+        # gamma = cumsum(g) within the chunk (gamma_L is gamma[-1])
+        dgam[-1] += dgL
+        dg[c0:c0 + L] = np.cumsum(dgam[::-1])[::-1]
+        db[c0:c0 + L] = db_c
+        dq[c0:c0 + L] = dQ
+        dkk[c0:c0 + L] = dK
+        dvv[c0:c0 + L] = dV
+        dS = dS_in
+    return dq, dkk, dvv, dg, db, dS

@@ -98,3 +98,28 @@ def test_finite_differences_without_normalisation():
 def test_backward_planted_mistakes_are_caught(name):
     m = oracle.BWD_MUTATIONS[name]
     assert not all(check(mutation=m) for check in BWD_CHECKS), name
+
+
+@pytest.mark.parametrize("C", [1, 3, 16, 64])
+def test_chunked_wy_backward_matches_token_gradients(C):
+    """Differentiating the chunked WY form (the form a chunked backward kernel
+    evaluates) gives the gradients of the token recurrence for any chunk size:
+    chunking changes the order of the arithmetic, not the map."""
+    from oracle import forms
+
+    rng = np.random.default_rng(40 + C)
+    T, dk, dv = 50, 5, 3
+    q, k = rng.standard_normal((T, dk)), rng.standard_normal((T, dk))
+    v = rng.standard_normal((T, dv))
+    g, beta = -rng.uniform(0.0, 0.5, T), rng.uniform(0.1, 0.9, T)
+    S0 = rng.standard_normal((dv, dk)) * 0.5
+    dO, dS = rng.standard_normal((T, dv)), rng.standard_normal((dv, dk))
+    scale = 0.6
+    got = forms.chunked_wy_vjp(q, k, v, g, beta, S0, scale, C, dO, dS)
+    ref = oracle.prefill_vjp(q[:, None], k[:, None], v[:, None], g[:, None], beta[:, None], dO[:, None], dS[None, None],
+                             S0[None, None], scale=scale, qk_l2norm=False)
+    names = ("dq", "dk", "dv", "dg", "dbeta")
+    for x, name in zip(got[:5], names):
+        r = ref[name][:, 0]
+        assert np.allclose(x, r, rtol=1e-10, atol=1e-10 * np.max(np.abs(r))), name
+    assert np.allclose(got[5], ref["dinit"][0, 0], rtol=1e-10, atol=1e-10)
