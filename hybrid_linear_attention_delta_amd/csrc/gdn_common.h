@@ -99,4 +99,13 @@ __device__ __forceinline__ float group_sum(float x)
 
 __device__ __forceinline__ float fast_exp(float x) { return __expf(x); }
 
+// silu(u) = u / (1 + e^{-u}) on the hardware exp2 and reciprocal (about 1 ulp
+// each): the IEEE expf and divide cost more ALU time than the streaming
+// kernels that apply it can hide.  Large |u| reach the exact limits
+// (e^{-u} = inf gives u * 0).
+__device__ __forceinline__ float fast_silu(float u)
+{
+    return u * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * u));
+}
+
 }  // namespace gdn

@@ -167,7 +167,7 @@ __global__ __launch_bounds__(256) void gated_norm_rows_kernel(TIn* __restrict__ 
         const float x = Elem<TIn>::load(orow, c);
         const float zv = Elem<TIn>::load(zrow, c);
         const float wv = w ? w[c] : 1.0f;
-        Elem<TIn>::store(orow, c, x * r * wv * (zv / (1.0f + expf(-zv))));
+        Elem<TIn>::store(orow, c, x * r * wv * fast_silu(zv));
     }
 }
 

@@ -1768,7 +1768,7 @@ __device__ __forceinline__ void output_chunk(const int32_t* __restrict__ header,
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const float wv = gw ? gw[q8 * 8 + e] : 1.0f;
-                    y[e] = x[e] * r * wv * (zv[e] / (1.0f + expf(-zv[e])));
+                    y[e] = x[e] * r * wv * fast_silu(zv[e]);
                 }
                 Quad<TIn>::store(o + base, f32x4{y[0], y[1], y[2], y[3]});
                 Quad<TIn>::store(o + base + 4, f32x4{y[4], y[5], y[6], y[7]});
