@@ -77,6 +77,12 @@ def decode_bytes_per_step(N=DEC_N):
     return 2 * N * H * DK * DV * 4 + N * H * (2 * DK + 2 * DV) * 2 + 2 * N * H * 4
 
 
+def decode_bytes_per_step_dv(N, dv):
+    """Decode bytes per step at value width dv: state read and written (fp32),
+    q, k read and v, o (bf16), g and beta (fp32)."""
+    return 2 * N * H * DK * dv * 4 + N * H * (2 * DK + 2 * dv) * 2 + 2 * N * H * 4
+
+
 def kernel_sources_digest():
     h = hashlib.sha256()
     d = os.path.join(ROOT, "hybrid_linear_attention_delta_amd", "csrc")
@@ -235,7 +241,24 @@ def bench_decode(torch, gdn, synth, n_steps, warmup=3):
     torch.cuda.synchronize()
     graphed = evs[0].elapsed_time(evs[1]) / n_steps
     log(f"[bench] decode {n_steps} steps in one HIP graph: {graphed * 1e3:.1f} us/step")
-    return dict(ms_per_step=ms, median_ms=med, gated_ms=gated, graph_ms=graphed)
+    # d_v = 512 (the pages' value width): twice the state per sequence and head
+    st5 = torch.from_numpy(synth.decode_state(DEC_N, H, DK, 2 * DV, seed)).to(dev)
+    qn, kn, vn, gn, bn = synth.decode_step_inputs(DEC_N, H, DK, 2 * DV, "bf16", seed, 0)
+    a5 = (synth.to_torch(qn, dev, bf16=True), synth.to_torch(kn, dev, bf16=True), synth.to_torch(vn, dev, bf16=True),
+          synth.to_torch(gn, dev), synth.to_torch(bn, dev))
+    o5 = torch.empty((DEC_N, H, 2 * DV), dtype=torch.bfloat16, device=dev)
+    for _ in range(3):
+        gdn.decode_step(*a5, st5, out=o5)
+    torch.cuda.synchronize()
+    evs[0].record()
+    for _ in range(32):
+        gdn.decode_step(*a5, st5, out=o5)
+    evs[1].record()
+    torch.cuda.synchronize()
+    dv512 = evs[0].elapsed_time(evs[1]) / 32
+    log(f"[bench] decode d_v=512: {dv512 * 1e3:.1f} us/step")
+    del st5
+    return dict(ms_per_step=ms, median_ms=med, gated_ms=gated, graph_ms=graphed, dv512_ms=dv512)
 
 
 def bench_prefill_other(torch, gdn, synth, steps, warmup):
@@ -248,6 +271,11 @@ def bench_prefill_other(torch, gdn, synth, steps, warmup):
     q, k, v = (synth.to_torch(x, dev, bf16=True) for x in (inp.q, inp.k, inp.v))
     g, beta = synth.to_torch(inp.g, dev), synth.to_torch(inp.beta, dev)
     cases = [("prefill_8k", (q, k, v, g, beta), None, None)]
+    # d_v = 2 d_k = 512, the value width of the pages' GDN layer (64K tokens)
+    inp5 = synth.prefill_inputs(T, H, DK, 2 * DV, "bf16", seed=synth.seed_for("prefill64k"))
+    cases.append(("prefill_64k_dv512", tuple(synth.to_torch(x, dev, bf16=True) for x in (inp5.q, inp5.k, inp5.v))
+                  + (synth.to_torch(inp5.g, dev), synth.to_torch(inp5.beta, dev)), None, None))
+    del inp5
     lengths = synth.varlen_lengths(synth.seed_for("varlen2m"))
     log(f"[bench] generating the 2M-token packed batch (lengths {list(map(int, lengths))})")
     vq, vk, vv, vg, vb, cu = synth.varlen_torch_inputs(lengths, H, DK, DV, synth.seed_for("varlen2m"), dev)
@@ -256,10 +284,10 @@ def bench_prefill_other(torch, gdn, synth, steps, warmup):
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     for name, (a, b, c, d, e), cuh, lens in cases:
-        Tn, N = a.shape[0], (1 if cuh is None else len(lens))
-        o = torch.empty((Tn, H, DV), dtype=torch.bfloat16, device=dev)
-        fs = torch.empty((N, H, DV, DK), dtype=torch.float32, device=dev)
-        ws = torch.empty(gdn.prefill_workspace_size(Tn, N, H, DK, DV, C), dtype=torch.uint8, device=dev)
+        Tn, N, dvn = a.shape[0], (1 if cuh is None else len(lens)), c.shape[2]
+        o = torch.empty((Tn, H, dvn), dtype=torch.bfloat16, device=dev)
+        fs = torch.empty((N, H, dvn, DK), dtype=torch.float32, device=dev)
+        ws = torch.empty(gdn.prefill_workspace_size(Tn, N, H, DK, dvn, C), dtype=torch.uint8, device=dev)
         cu_arg = None if cuh is None else torch.from_numpy(cuh)
         run = lambda: gdn.chunk_prefill(a, b, c, d, e, cu_seqlens=cu_arg, chunk=C, out=o, final_state=fs,
                                         workspace=ws)
@@ -273,9 +301,10 @@ def bench_prefill_other(torch, gdn, synth, steps, warmup):
         t1.record()
         torch.cuda.synchronize()
         ms = t0.elapsed_time(t1) / n_steps
-        ent = {"tokens": int(Tn), "ms_per_step": ms, "tokens_per_s": Tn / (ms / 1e3),
-               "mfma_frac": flops_path_per_token() * Tn / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
-               "min_traffic_hbm_frac": Tn * H * ((2 * DK + 2 * DV) * 2 + 8) / (ms / 1e3) / 1e9 / PEAK_HBM_GBPS}
+        f_tok = H * (6 * DK * dvn + C * (3 * DK + 2 * dvn) + C * C / 3.0)
+        ent = {"tokens": int(Tn), "d_v": int(dvn), "ms_per_step": ms, "tokens_per_s": Tn / (ms / 1e3),
+               "mfma_frac": f_tok * Tn / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+               "min_traffic_hbm_frac": Tn * H * ((2 * DK + 2 * dvn) * 2 + 8) / (ms / 1e3) / 1e9 / PEAK_HBM_GBPS}
         if lens is not None:
             ent["lengths"] = [int(x) for x in lens]
         res[name] = ent
@@ -465,6 +494,9 @@ def main():
             "median_ms_per_step": dec["median_ms"],
             "gated_rmsnorm_ms_per_step": dec["gated_ms"],
             "hip_graph_ms_per_step": dec["graph_ms"],
+            "dv512": {"ms_per_step": dec["dv512_ms"],
+                      "hbm_frac": decode_bytes_per_step_dv(DEC_N, 2 * DV) / (dec["dv512_ms"] / 1e3) / 1e9
+                      / PEAK_HBM_GBPS},
             "tokens_per_s": DEC_N / (dec["ms_per_step"] / 1e3),
             "state_GBps": state_gbps,
             "roofline": {"kernel": "decode_kernel", "bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_GBPS,
