@@ -416,7 +416,7 @@ def main():
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the mixer shards by head, state row or sequence without collectives; see DESIGN.md). "
+              "(the mixer shards by head, state row or sequence without collectives). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 

@@ -1239,7 +1239,7 @@ __device__ __forceinline__ void wait_vmcnt()
 // on one XCD (workgroups are dealt to the 8 XCDs round-robin): they read the
 // same per-chunk records, which then come from that XCD's L2.  Pair indices
 // follow seq_order (longest sequence first) in a packed batch, so when there
-// are more workgroups than CUs the longest chains start in the first round.
+// are more workgroups than CUs the longest chains are dispatched first.
 template <typename TIn, int C, int DK, int DV, int NW, bool SEG>
 __global__ __launch_bounds__((NW + chain_loaders<TIn, C>()) * 64) void chain_kernel(
     const int32_t* __restrict__ header, const int32_t* __restrict__ seq_first,
@@ -1811,7 +1811,7 @@ __global__ __launch_bounds__(256) void output_kernel(const int32_t* __restrict__
 // per-segment intra-chunk and output kernels two more streams on all other
 // CUs: the chain's workgroups then never share a CU with the parallel kernels
 // and never wait for one to drain.  CU mask bit i is CU i / 8 of XCD i % 8
-// (the driver numbers CUs round-robin over the XCDs).
+// (CU masks number the CUs round-robin over the XCDs).
 struct PipeRes {
     static constexpr int MAX_SEG = 16;
     std::mutex use;  // held while one call enqueues its pipeline: the events are reused by every call

@@ -1,14 +1,14 @@
 #!/usr/bin/env python
 """Profiles behind the bench figures, collected with rocprofv3 on one MI355X.
 
-    python profile_bench.py trace     # kernel trace + stats of a short bench run   (GPU)
-    python profile_bench.py traffic   # HBM bytes per launch from FETCH_SIZE / WRITE_SIZE (GPU)
-    python profile_bench.py render    # summaries under profiles/ from the raw output (no GPU)
-    python profile_bench.py copy      # (the calibration program the traffic mode profiles)
+    python profile_bench.py trace   [--out DIR]  # kernel trace + stats of a short bench run   (GPU)
+    python profile_bench.py traffic [--out DIR]  # HBM bytes per launch from FETCH_SIZE / WRITE_SIZE (GPU)
+    python profile_bench.py render  [--out DIR]  # summaries under profiles/ from the raw output (no GPU)
+    python profile_bench.py copy                 # (the calibration program the traffic mode profiles)
 
-The GPU modes keep rocprofv3's raw output and their results under
-gpurun_out/profile_bench/; `render` turns those into the short summaries that
-are kept under profiles/.
+The GPU modes keep rocprofv3's raw output and their results under the
+output directory (``--out DIR``, default ``profile_out/``, not committed);
+`render` turns those into the short summaries that are kept under profiles/.
 
 `trace` runs ``rocprofv3 --kernel-trace --stats`` over ``bench.py`` and writes
 profiles/prefill64k_decode_kernel_trace.md: the command, the per-kernel
@@ -35,7 +35,7 @@ import subprocess
 import sys
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-OUT = os.path.join(ROOT, "gpurun_out", "profile_bench")
+OUT = os.path.join(ROOT, "profile_out")  # raw profiler output; set by --out
 PROFILES = os.path.join(ROOT, "profiles")
 # more specific names first: a kernel is keyed by the first entry its name contains
 KERNELS = ("conv_silu_kernel", "conv_decode_kernel", "chain_kernel", "intra_kernel", "output_kernel", "decode_kernel",
@@ -197,7 +197,7 @@ def mode_traffic():
 
 
 def summarize_traffic():
-    """gpurun_out/profile_bench/traffic.json from the raw counter passes."""
+    """traffic.json in the output directory, from the raw counter passes."""
     with open(os.path.join(OUT, "traffic_meta.json")) as f:
         meta = json.load(f)
     result = {"sources_digest": meta["sources_digest"], "counters": {}, "calibration": {}, "kernels": {}}
@@ -218,7 +218,7 @@ def summarize_traffic():
     result["commands"] = meta["commands"]
     with open(os.path.join(OUT, "traffic.json"), "w") as f:
         json.dump(result, f, indent=1)
-    log("[profile] wrote gpurun_out/profile_bench/traffic.json")
+    log(f"[profile] wrote {os.path.join(OUT, 'traffic.json')}")
 
 
 def render_traffic():
@@ -266,5 +266,10 @@ def mode_copy():
 
 
 if __name__ == "__main__":
-    mode = sys.argv[1] if len(sys.argv) > 1 else "trace"
+    args = sys.argv[1:]
+    if "--out" in args:
+        i = args.index("--out")
+        OUT = os.path.abspath(args[i + 1])
+        del args[i:i + 2]
+    mode = args[0] if args else "trace"
     {"trace": mode_trace, "traffic": mode_traffic, "render": mode_render, "copy": mode_copy}[mode]()
