@@ -285,3 +285,23 @@ def test_concurrent_pipelined_calls_from_two_threads():
     for i in range(2):
         for o, s in results[i]:
             assert torch.equal(o, ref[i][0]) and torch.equal(s, ref[i][1]), i
+
+
+def test_in_place_state_carry_on_the_pipelined_path():
+    """final_state aliasing init_state on a 37K-token batch (the pipelined path:
+    the state crosses segments through the carry buffer) gives bit for bit the
+    result of separate initial and final state buffers."""
+    T, H, d = 37000, 2, 256
+    lens = [20000, 17000]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    inp = synth.prefill_inputs(T, H, d, d, "bf16", seed=707, gate="slow", cu_seqlens=cu, init_state_std=0.3)
+    t = lambda a, b=False: synth.to_torch(a, DEV, bf16=b)
+    args = (t(inp.q, True), t(inp.k, True), t(inp.v, True), t(inp.g), t(inp.beta))
+    cu_t = torch.from_numpy(cu.astype(np.int32))
+    init = t(inp.init_state)
+    o_ref, fs_ref = gdn.chunk_prefill(*args, init_state=init.clone(), cu_seqlens=cu_t)
+    st = init.clone()
+    o, fs = gdn.chunk_prefill(*args, init_state=st, cu_seqlens=cu_t, final_state=st)
+    torch.cuda.synchronize()
+    assert fs.data_ptr() == st.data_ptr()
+    assert torch.equal(o, o_ref) and torch.equal(st, fs_ref)
