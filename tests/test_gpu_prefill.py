@@ -305,3 +305,38 @@ def test_in_place_state_carry_on_the_pipelined_path():
     torch.cuda.synchronize()
     assert fs.data_ptr() == st.data_ptr()
     assert torch.equal(o, o_ref) and torch.equal(st, fs_ref)
+
+
+@pytest.mark.parametrize("T", [8192, 37000])
+def test_prefill_in_a_hip_graph_matches_eager(T):
+    """One whole-prefill call captured in a HIP graph -- the single-stream path at
+    8K tokens and the pipelined path (its side streams fork from and join the
+    captured stream) at 37K -- replayed three times with eager work between the
+    replays: every replay equals the eager result bit for bit."""
+    H, d = 2, 256
+    inp = synth.prefill_inputs(T, H, d, d, "bf16", seed=808 + T, gate="slow", init_state_std=0.3)
+    t = lambda a, b=False: synth.to_torch(a, DEV, bf16=b)
+    args = (t(inp.q, True), t(inp.k, True), t(inp.v, True), t(inp.g), t(inp.beta))
+    init = t(inp.init_state)
+    ws = torch.empty(gdn.prefill_workspace_size(T, 1, H, d, d, 64), dtype=torch.uint8, device=DEV)
+    o = torch.empty((T, H, d), dtype=torch.bfloat16, device=DEV)
+    fs = torch.empty((1, H, d, d), dtype=torch.float32, device=DEV)
+    run = lambda: gdn.chunk_prefill(*args, init_state=init, out=o, final_state=fs, workspace=ws)
+    run()  # eager: creates the pipeline streams and raises the kernels' LDS limits
+    torch.cuda.synchronize()
+    o_ref, fs_ref = o.clone(), fs.clone()
+    side = torch.cuda.Stream(device=DEV)
+    side.wait_stream(torch.cuda.current_stream(DEV))
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            run()
+    torch.cuda.current_stream(DEV).wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        o.zero_()
+        fs.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(fs, fs_ref), rep
