@@ -313,13 +313,18 @@ __global__ __launch_bounds__(256) void chunk_table_kernel(const int32_t* __restr
         header[1] = (int32_t)tot;
     }
     __syncthreads();
+    // the lengths staged in LDS once: the ranking reads each of them N times
+    __shared__ int32_t len_s[kSortMax];
+    if (N <= kSortMax)
+        for (int32_t i = t; i < N; i += 256) len_s[i] = max(cu[i + 1] - cu[i], 0);
+    __syncthreads();
     for (int32_t i = t; i < N; i += 256) {
         int32_t r = i;
         if (N <= kSortMax) {
-            const int32_t Li = max(cu[i + 1] - cu[i], 0);
+            const int32_t Li = len_s[i];
             r = 0;
             for (int32_t j = 0; j < N; ++j) {
-                const int32_t Lj = max(cu[j + 1] - cu[j], 0);
+                const int32_t Lj = len_s[j];
                 r += (Lj > Li || (Lj == Li && j < i)) ? 1 : 0;
             }
         }

@@ -340,3 +340,16 @@ def test_prefill_in_a_hip_graph_matches_eager(T):
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(o, o_ref) and torch.equal(fs, fs_ref), rep
+
+
+@pytest.mark.parametrize("N", [2000, 2100])
+def test_many_short_sequences(N):
+    """Thousands of packed sequences of 0-40 tokens: the longest-first ranking of
+    the chain's dispatch order (up to 2048 sequences; batch order beyond) and
+    thousands of chain workgroups, against the oracle."""
+    rng = np.random.default_rng(N)
+    lens = rng.integers(0, 41, size=N)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    inp = synth.prefill_inputs(int(cu[-1]), 1, 64, 64, "f32", seed=N, gate="slow", cu_seqlens=cu,
+                               init_state_std=0.3)
+    _check(inp, 64, TOL_F32, init=inp.init_state)
