@@ -16,12 +16,11 @@ bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 
 bool debug_sync()
 {
-    static int cached = -1;  // read once; a plain int written with the same value is benign
-    if (cached < 0) {
+    static const bool on = [] {  // read once; function-local static initialisation is thread-safe
         const char* s = getenv("GDN_DEBUG_SYNC");
-        cached = (s && s[0] == '1') ? 1 : 0;
-    }
-    return cached == 1;
+        return s != nullptr && s[0] == '1';
+    }();
+    return on;
 }
 
 bool in_list(int32_t x, const int32_t* xs, int n)
