@@ -353,3 +353,12 @@ def test_many_short_sequences(N):
     inp = synth.prefill_inputs(int(cu[-1]), 1, 64, 64, "f32", seed=N, gate="slow", cu_seqlens=cu,
                                init_state_std=0.3)
     _check(inp, 64, TOL_F32, init=inp.init_state)
+
+
+def test_fp32_pipelined_path():
+    """The fp32 operands at 37K tokens (past the pipelining threshold): the
+    general form of the state chain in segmented launches, carrying the state
+    through the carry buffer, against the oracle at the fp32 bound."""
+    T, H, d = 37000, 2, 64
+    inp = synth.prefill_inputs(T, H, d, d, "f32", seed=3700, gate="slow", init_state_std=0.3)
+    _check(inp, 64, TOL_F32, init=inp.init_state)
