@@ -85,7 +85,7 @@ def chunked_wy(q, k, v, g, beta, S0, scale, C):
     return o, S, chunks
 
 
-def chunked_wy_vjp(q, k, v, g, beta, S0, scale, C, dO, dS_end):
+def chunked_wy_vjp(q, k, v, g, beta, S0, scale, C, dO, dS_end, chunk_grads=None):
     """Gradients of <dO, o> + <dS_end, S_end> for ``chunked_wy`` on one chain,
     by reverse-mode differentiation of the chunked WY form itself (the form a
     chunked backward kernel evaluates).  q, k are used as given (normalise them
@@ -106,7 +106,10 @@ def chunked_wy_vjp(q, k, v, g, beta, S0, scale, C, dO, dS_end):
         from T = (I + A)^{-1}:  dA = -T^T dT T^T (strictly lower part)
         from A_rj = b_r (k_r . k_j) e^{gamma_r - gamma_j}:  dK += diag(b)(dA o Gamma) K + (diag(b)(dA o Gamma))^T K
     and the beta and gamma terms of each product; dg is the reverse cumulative
-    sum of dgamma within the chunk.  Returns dq, dk, dv, dg, dbeta, dS0.
+    sum of dgamma within the chunk.  Returns dq, dk, dv, dg, dbeta, dS0.  If
+    ``chunk_grads`` is a list, it receives, per chunk in chunk order, a dict with
+    dDelta (the chunk's total Delta gradient) and dS_after (the gradient of the
+    state after the chunk): the outputs of a reverse state-gradient chain.
     """
     T_, dk = q.shape
     dv = v.shape[1]
@@ -187,5 +190,7 @@ def chunked_wy_vjp(q, k, v, g, beta, S0, scale, C, dO, dS_end):
         dq[c0:c0 + L] = dQ
         dkk[c0:c0 + L] = dK
         dvv[c0:c0 + L] = dV
+        if chunk_grads is not None:
+            chunk_grads.insert(0, dict(dDelta=dDelta.copy(), dS_after=dS.copy()))
         dS = dS_in
     return dq, dkk, dvv, dg, db, dS

@@ -123,3 +123,50 @@ def test_chunked_wy_backward_matches_token_gradients(C):
         r = ref[name][:, 0]
         assert np.allclose(x, r, rtol=1e-10, atol=1e-10 * np.max(np.abs(r))), name
     assert np.allclose(got[5], ref["dinit"][0, 0], rtol=1e-10, atol=1e-10)
+
+
+def test_chain_fold_identity():
+    """The state chain's next product without the next state: with
+    Y_{c+1} = W_{c+1} S_c^T and M_{c+1} = W_{c+1} K_c^T diag(e^{gamma_L - gamma}),
+    W_{c+1} S_{c+1}^T = e^{gamma_L} Y_{c+1} + M_{c+1} Delta_c (chunked WY form)."""
+    from oracle import forms
+
+    rng = np.random.default_rng(9)
+    T, dk, dv, C = 200, 8, 6, 32
+    q = forms.l2_normalise(rng.standard_normal((T, dk)))
+    k = forms.l2_normalise(rng.standard_normal((T, dk)))
+    v = rng.standard_normal((T, dv))
+    g, beta = -rng.uniform(0.0, 0.3, T), rng.uniform(0.1, 0.9, T)
+    _, _, ch = forms.chunked_wy(q, k, v, g, beta, rng.standard_normal((dv, dk)), 0.5, C)
+    for c in range(len(ch) - 1):
+        a, n = ch[c], ch[c + 1]
+        K = k[c * C:(c + 1) * C]
+        M = n["W"] @ (np.exp(a["gamma"][-1] - a["gamma"])[:, None] * K).T
+        lhs = n["W"] @ n["S_start"].T
+        rhs = np.exp(a["gamma"][-1]) * (n["W"] @ a["S_start"].T) + M @ a["Delta"]
+        assert np.allclose(lhs, rhs, rtol=1e-12, atol=1e-12), c
+
+
+def test_chunk_gradients_chain_recurrence():
+    """The per-chunk outputs of the reverse state-gradient chain satisfy its
+    recurrence: dS before chunk c = e^{gamma_L} dS_after + dO'^T diag(e^gamma) Q
+    - dDelta^T W, and the first one equals the initial-state gradient."""
+    from oracle import forms
+
+    rng = np.random.default_rng(10)
+    T, dk, dv, C, scale = 100, 5, 4, 16, 0.7
+    q, k = rng.standard_normal((T, dk)), rng.standard_normal((T, dk))
+    v = rng.standard_normal((T, dv))
+    g, beta = -rng.uniform(0.0, 0.5, T), rng.uniform(0.1, 0.9, T)
+    S0, dO, dS = rng.standard_normal((dv, dk)), rng.standard_normal((T, dv)), rng.standard_normal((dv, dk))
+    cg = []
+    out = forms.chunked_wy_vjp(q, k, v, g, beta, S0, scale, C, dO, dS, chunk_grads=cg)
+    _, _, ch = forms.chunked_wy(q, k, v, g, beta, S0, scale, C)
+    assert len(cg) == len(ch) and np.array_equal(cg[-1]["dS_after"], dS)
+    for c in range(len(ch)):
+        gam = ch[c]["gamma"]
+        Q = q[c * C:c * C + gam.shape[0]]
+        dOs = scale * dO[c * C:c * C + gam.shape[0]]
+        before = np.exp(gam[-1]) * cg[c]["dS_after"] + dOs.T @ (np.exp(gam)[:, None] * Q) - cg[c]["dDelta"].T @ ch[c]["W"]
+        expect = out[5] if c == 0 else cg[c - 1]["dS_after"]
+        assert np.allclose(before, expect, rtol=1e-12, atol=1e-12), c
