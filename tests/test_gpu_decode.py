@@ -127,3 +127,10 @@ def test_decode_steps_in_a_hip_graph_match_eager():
         o_ref = oracle.decode_step(q, k, v, g, beta, ref, bf16=True)
         assert bound_ratio(outs[s].float().cpu().numpy(), o_ref, TOL_BF16, stored_bf16=True) <= 1.0
     assert rel_err(state.cpu().numpy(), ref) <= TOL_BF16
+
+
+@pytest.mark.parametrize("N,dk,dv", [(1, 256, 256), (1000, 128, 256), (3, 64, 512)])
+def test_decode_odd_batch_sizes(N, dk, dv):
+    """One sequence, a thousand, and a few with d_v = 8 d_k: every state row of
+    every (sequence, head) pair is updated and read out."""
+    _run_decode(N, 2, dk, dv, "bf16", 3, seed=N + dk + dv)

@@ -229,3 +229,19 @@ def test_frontend_then_pipelined_prefill_sampled_rows():
                                    rows=rows)
     assert bound_ratio(o.float().cpu().numpy()[:, :, rows], o_ref[:, :, rows], TOL_BF16, stored_bf16=True) <= 1.0
     assert rel_err(fs.cpu().numpy()[:, :, rows], fs_ref[:, :, rows]) <= TOL_BF16
+
+
+def test_frontend_prefill_non_square_heads():
+    """H = 6, d_k = 128, d_v = 256 (q and k channel blocks narrower than v's)."""
+    H, dk, dv, lens = 6, 128, 256, [90, 3, 160]
+    T = sum(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    f = synth.frontend_inputs(T, H, dk, dv, "bf16", seed=1282, cu_seqlens=cu, with_state=True)
+    q, k, v, g, beta, st_out = _gpu_frontend(f, T, H, dk, dv, cu, _t(f.conv_state, True))
+    torch.cuda.synchronize()
+    rq, rk, rv, rg, rb, rst = _oracle_frontend(f, H, dk, dv, cu, f.conv_state)
+    for gpu, ref in ((q, rq), (k, rk), (v, rv)):
+        _check_qkv(gpu, ref, True)
+    assert rel_err(g.cpu().numpy(), rg) <= TOL_F32 and rel_err(beta.cpu().numpy(), rb) <= TOL_F32
+    got = _widen(st_out.cpu().view(torch.int16).numpy().view(np.uint16), True)
+    assert np.array_equal(got, rst)

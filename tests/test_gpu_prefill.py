@@ -362,3 +362,18 @@ def test_fp32_pipelined_path():
     T, H, d = 37000, 2, 64
     inp = synth.prefill_inputs(T, H, d, d, "f32", seed=3700, gate="slow", init_state_std=0.3)
     _check(inp, 64, TOL_F32, init=inp.init_state)
+
+
+def test_bf16_dk128_pipelined_sampled_rows():
+    """bf16, d_k = 128, d_v = 256 at 37K tokens: the pipelined path with the d_k = 128
+    chain, against the oracle on sampled state rows."""
+    T, H = 37000, 3
+    inp = synth.prefill_inputs(T, H, 128, 256, "bf16", seed=12837, gate="slow", init_state_std=0.3)
+    _check(inp, 64, TOL_BF16, init=inp.init_state, rows=[0, 63, 200, 255])
+
+
+def test_bf16_8k_custom_scale_without_norm():
+    """8K tokens, bf16, read scale 0.3 and no q/k normalisation (inputs already unit
+    rows from the data recipe, so the recurrence stays bounded)."""
+    inp = synth.prefill_inputs(8192, 2, 256, 256, "bf16", seed=8191, gate="default")
+    _check(inp, 64, TOL_BF16, scale=0.3, l2=False, rows=[1, 128, 254])
