@@ -3,6 +3,7 @@
 
     python profile_bench.py trace   [--out DIR]  # kernel trace + stats of a short bench run   (GPU)
     python profile_bench.py traffic [--out DIR]  # HBM bytes per launch from FETCH_SIZE / WRITE_SIZE (GPU)
+    python profile_bench.py mfma    [--out DIR]  # MFMA flops executed and MFMA busy share per launch (GPU)
     python profile_bench.py render  [--out DIR]  # summaries under profiles/ from the raw output (no GPU)
     python profile_bench.py copy                 # (the calibration program the traffic mode profiles)
 
@@ -21,6 +22,13 @@ copy of a known number of bytes.  The copy's reading calibrates each counter
 it.  Results go to profiles/traffic.json, keyed by a digest of the kernel
 sources (bench.py reports a traffic figure only while the sources are
 unchanged), with a readable summary in profiles/traffic_prefill64k_decode.md.
+
+`mfma` runs one ``rocprofv3 --pmc MfmaUtil MfmaFlops MfmaFlopsBF16`` pass over
+the same short bench run and writes profiles/mfma_prefill64k.md: per
+whole-workload launch of the MFMA kernels, the matrix flops the hardware
+executed (the bf16 splits of fp32 operands included), their rate over the
+dispatch's duration, the MFMA units' busy share of the whole chip, and for the
+state chain the ratio of executed to algorithmic flops.
 
 This script starts rocprofv3 as a child process and touches the GPU only
 through it (and through `copy`, which the profiler runs).
@@ -249,9 +257,91 @@ def render_traffic():
     log("[profile] wrote profiles/traffic.json and profiles/traffic_prefill64k_decode.md")
 
 
+MFMA_COUNTERS = ("MfmaUtil", "MfmaFlops", "MfmaFlopsBF16")
+MFMA_KERNELS = "chain_kernel|intra_kernel|output_kernel"
+
+
+def mode_mfma():
+    rc, d, cmd = launch(BENCH_PMC, ["--pmc", *MFMA_COUNTERS, "--kernel-include-regex", MFMA_KERNELS], "mfma", 600)
+    with open(os.path.join(d, "command.txt"), "w") as f:
+        f.write(cmd + "\n")
+    if not profiler_ok(rc, d, "counter_collection.csv"):
+        raise SystemExit(f"mfma pass failed (exit {rc})")
+
+
+def mfma_table(d):
+    """{kernel key: {counter: mean per whole-workload dispatch, "ns": mean duration, "n": dispatches}}."""
+    f = find(d, "counter_collection.csv")
+    if f is None:
+        return {}
+    per = {}  # (name, grid) -> {dispatch: {counter: value, "ns": duration}}
+    with open(f) as fh:
+        for r in csv.DictReader(fh):
+            name = r["Kernel_Name"]
+            if kernel_key(name) is None:
+                continue
+            disp = per.setdefault((name, int(r["Grid_Size"])), {}).setdefault(r["Dispatch_Id"], {})
+            disp[r["Counter_Name"]] = disp.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            disp["ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+            disp["wg"] = int(r["Grid_Size"]) // max(1, int(r["Workgroup_Size"]))
+    out = {}
+    for (name, grid), disps in per.items():
+        if not full_launch(name, grid, per):
+            continue
+        key = kernel_key(name)
+        n = len(disps)
+        ent = {c: sum(v.get(c, 0.0) for v in disps.values()) / n for c in (*MFMA_COUNTERS, "ns", "wg")}
+        ent["n"] = n
+        out[key] = ent
+    return out
+
+
+def render_mfma():
+    d = os.path.join(OUT, "mfma")
+    table = mfma_table(d)
+    if not table:
+        log("[profile] no mfma output to render")
+        return
+    sys.path.insert(0, ROOT)
+    import bench
+
+    chain_alg = bench.flops_chain_per_token() * bench.T
+    cmd = open(os.path.join(d, "command.txt")).read().strip()
+    lines = ["# MFMA work per launch: 64K-token prefill (H=6, d=256, bf16)", "",
+             "Command (repository root, one MI355X), one counter pass:", "", "```", cmd, "```", "",
+             "Per launch over the whole workload (the pipelined prefill's launches over",
+             "segments of the chunks are left out).  `MfmaFlops` counts the matrix flops",
+             "the hardware executed, fp32 operands split into bf16 parts included;",
+             "`MfmaUtil` is the MFMA units' busy share over all 1024 SIMDs of the chip for",
+             "the dispatch's duration (the dispatch runs alone while counters are taken);",
+             "the last column rescales it to the CUs the working workgroups occupy (one",
+             "per CU when there are fewer than the chip's 256 CUs; the chain's grid is",
+             "padded to whole groups of 8 (sequence, head) pairs, and the padding's",
+             "workgroups return at once, so 6 heads x 16 row blocks = 96 work).", "",
+             "| kernel | dispatches | workgroups | us (counter run) | executed GFLOP | of which bf16"
+             " | executed TFLOP/s | MfmaUtil % | % per occupied CU |", "|---|---|---|---|---|---|---|---|---|"]
+    for key in ("intra_kernel", "chain_kernel", "output_kernel"):
+        e = table.get(key)
+        if e is None:
+            continue
+        tf = e["MfmaFlops"] / (e["ns"] * 1e-9) / 1e12 if e["ns"] > 0 else float("nan")
+        working = bench.H * (bench.DV // 16) if key == "chain_kernel" else e["wg"]
+        occ = e["MfmaUtil"] * 256 / min(256.0, max(1.0, working))
+        lines.append(f"| `{key}` | {e['n']} | {e['wg']:.0f} | {e['ns'] / 1e3:.0f} | {e['MfmaFlops'] / 1e9:.1f}"
+                     f" | {e['MfmaFlopsBF16'] / 1e9:.1f} | {tf:.1f} | {e['MfmaUtil']:.2f} | {occ:.2f} |")
+    ch = table.get("chain_kernel")
+    if ch is not None:
+        lines += ["", f"State chain: algorithmic {chain_alg / 1e9:.1f} GFLOP per launch (4 d_k d_v per token and head);",
+                  f"executed / algorithmic = {ch['MfmaFlops'] / chain_alg:.2f}.", ""]
+    with open(os.path.join(PROFILES, "mfma_prefill64k.md"), "w") as f:
+        f.write("\n".join(lines))
+    log("[profile] wrote profiles/mfma_prefill64k.md")
+
+
 def mode_render():
     render_trace()
     render_traffic()
+    render_mfma()
 
 
 def mode_copy():
@@ -272,4 +362,5 @@ if __name__ == "__main__":
         OUT = os.path.abspath(args[i + 1])
         del args[i:i + 2]
     mode = args[0] if args else "trace"
-    {"trace": mode_trace, "traffic": mode_traffic, "render": mode_render, "copy": mode_copy}[mode]()
+    {"trace": mode_trace, "traffic": mode_traffic, "mfma": mode_mfma, "render": mode_render,
+     "copy": mode_copy}[mode]()
