@@ -22,7 +22,7 @@ BUILD_DIR = os.path.join(ROOT, "_build", "gdn")
 LIB_NAME = "libgdn_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["gdn_api.cpp", "gdn_decode.hip", "gdn_prefill.hip", "gdn_frontend.hip"]
+SOURCES = ["gdn_api.cpp", "gdn_decode.hip", "gdn_prefill.hip", "gdn_frontend.hip", "gdn_backward.hip"]
 HEADERS = ["gdn_common.h", "gdn_launch.h"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")

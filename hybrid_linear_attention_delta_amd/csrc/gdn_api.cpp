@@ -378,3 +378,61 @@ gdn_status gdn_frontend_decode(const void* xq, const void* xk, const void* xv, c
 }
 
 }  // extern "C"
+
+extern "C" {
+
+size_t gdn_prefill_backward_workspace_size(int64_t total_tokens, int32_t num_seqs, int32_t H, int32_t dk, int32_t dv)
+{
+    if (total_tokens < 0 || num_seqs < 1 || H < 1) return 0;
+    if (!gdn::backward_supported(dk, dv)) return 0;
+    return gdn::backward_layout(total_tokens, num_seqs, H, dk, dv).total;
+}
+
+gdn_status gdn_chunk_prefill_backward(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                                      const float* init_state, const void* d_o, const float* d_final_state,
+                                      const int32_t* cu_seqlens, const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                      int64_t total_tokens, int32_t H, int32_t dk, int32_t dv, gdn_dtype dt,
+                                      float scale, int32_t qk_l2norm, float* grad_q, float* grad_k, float* grad_v,
+                                      float* grad_g, float* grad_beta, float* grad_init_state, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream)
+{
+    if (dt != GDN_F32 && dt != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+    if (total_tokens < 0 || num_seqs < 1 || H < 1 || dk < 1 || dv < 1) return GDN_ERR_BAD_SHAPE;
+    if (total_tokens > ((int64_t)1 << 31) - 1) return GDN_ERR_BAD_SHAPE;
+    if (!cu_seqlens && num_seqs != 1) return GDN_ERR_BAD_SHAPE;
+    if (!gdn::backward_supported(dk, dv)) return GDN_ERR_UNSUPPORTED;
+    if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !d_o || !grad_q || !grad_k || !grad_v || !grad_g ||
+                             !grad_beta))
+        return GDN_ERR_NULL_ARG;
+    if (!workspace) return GDN_ERR_WORKSPACE;
+    const void* p16[] = {q, k, v, d_o, init_state, d_final_state, grad_q, grad_k, grad_v, grad_init_state};
+    for (const void* p : p16)
+        if (p && !aligned16(p)) return GDN_ERR_ALIGNMENT;
+    const void* p4[] = {g, beta, grad_g, grad_beta};
+    for (const void* p : p4)
+        if (!aligned4(p)) return GDN_ERR_ALIGNMENT;
+    if (((uintptr_t)workspace & 255u) != 0) return GDN_ERR_ALIGNMENT;
+    if (cu_seqlens_host) {
+        if (cu_seqlens_host[0] != 0 || cu_seqlens_host[num_seqs] != total_tokens) return GDN_ERR_BAD_SEQLENS;
+        for (int32_t n = 0; n < num_seqs; ++n)
+            if (cu_seqlens_host[n + 1] < cu_seqlens_host[n]) return GDN_ERR_BAD_SEQLENS;
+    }
+    const gdn::BwdLayout lay = gdn::backward_layout(total_tokens, num_seqs, H, dk, dv);
+    if (workspace_bytes < lay.total) return GDN_ERR_WORKSPACE;
+    gdn::BwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.dO = d_o; a.g = g; a.beta = beta;
+    a.init_state = init_state; a.dstate = d_final_state;
+    a.cu_seqlens = cu_seqlens;
+    a.N = num_seqs; a.T = total_tokens; a.H = H; a.dk = dk; a.dv = dv;
+    a.bf16 = dt == GDN_BF16;
+    a.scale = scale > 0.f ? scale : 1.0f / sqrtf((float)dk);
+    a.l2norm = qk_l2norm ? 1 : 0;
+    a.dq = grad_q; a.dk_out = grad_k; a.dv_out = grad_v; a.dg = grad_g; a.dbeta = grad_beta;
+    a.dinit = grad_init_state;
+    a.ws = (unsigned char*)workspace;
+    a.lay = lay;
+    a.stream = stream;
+    return finish(gdn::launch_backward(a), stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,803 @@
+// gdn_backward.hip -- gradients of the chunked gated delta rule (gfx950), fp32.
+//
+// Training evaluates the recurrence of "Long-Context Aware Upcycling: A New
+// Frontier for Hybrid LLM Scaling" (arXiv:2604.24715, App. A.3, Eqs. 16-19)
+// in chunks (the paragraph after Eq. 21).  This file differentiates that
+// chunked (WY) evaluation.  Per chunk of C = 64 tokens of one (sequence, head),
+// with chunk-local cumulative log-decay gamma, Gamma_rj = e^{gamma_r - gamma_j}
+// (j <= r), D = diag(e^{gamma_L - gamma}) and S the state entering the chunk:
+//
+//     A = strict_lower(diag(beta) (K K^T) o Gamma),  T = (I + A)^{-1}
+//     W = T diag(beta e^gamma) K,   U = T diag(beta) V,   Delta = U - W S^T
+//     P = lower(Q K^T o Gamma)
+//     O = scale [diag(e^gamma) Q S^T + P Delta],   S' = e^{gamma_L} S + Delta^T D K
+//
+// (Q, K the L2-normalised queries and keys).  The backward runs in four launches:
+//
+//   1. bwd_table_kernel   chunk table of the packed batch (one workgroup).
+//   2. bwd_local_kernel   per chunk-head: normalise and pad the chunk's rows,
+//                         form Gamma, A, T, P, W, U, D K, scale e^gamma dO and
+//                         dDelta_local = scale P^T dO into a workspace.
+//   3. bwd_chain_kernel   twice.  Forward over the chunks of each sequence: the
+//                         state entering every chunk and its Delta.  Reverse:
+//                         the state gradient after every chunk, from
+//                             dDelta = dDelta_local + D K dS^T
+//                             dS    <- e^{gamma_L} dS + (scale e^gamma dO)^T Q - dDelta^T W.
+//                         Both are the same row-split recurrence, so one kernel
+//                         serves them with different operands.
+//   4. bwd_grad_kernel    per chunk-head: dQ, dK, dV, dg, dbeta of the chunk from
+//                         S, dS, Delta and dDelta, then through the L2 norm
+//                         (dx = r (dx^ - x^ (x^ . dx^))).
+//
+// Ragged chunks are padded to C rows with q = k = v = dO = 0, beta = 0 and
+// g = 0, which leaves every product of the real rows unchanged.
+//
+// Everything is fp32 on the vector ALUs: the per-chunk products go through one
+// LDS-tiled 64 x 64 block routine (4 x 4 outputs per thread).  This is a first,
+// plain evaluation of the gradient; its contractions are not yet on the matrix
+// cores.
+#include <string.h>
+
+#include "gdn_common.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+namespace {
+
+constexpr int BC = 64;  // chunk length of the backward
+constexpr int LD = 68;  // LDS row pitch of the tile routine (floats)
+
+// acc[i][j] += sum_k A(r, k) B(k, n) for r = 4 tr + i in [0, 64), n = n0 + 4 tc + j,
+// with A(r, k) = A[r * ars + k * acs] * (kscale ? kscale[k] : 1) and
+// B(k, n) = B[k * brs + n * bcs]; K a multiple of 16, [n0, n0 + 64) inside B.
+// All 256 threads take part (two barriers per 16-wide k step).
+__device__ void mm64(float acc[4][4], const float* __restrict__ A, int ars, int acs, const float* kscale,
+                     const float* __restrict__ B, int brs, int bcs, int K, int n0, float* as, float* bs)
+{
+    const int t = threadIdx.x;
+    const int tr = t >> 4, tc = t & 15;
+    for (int k0 = 0; k0 < K; k0 += 16) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = t + 256 * i;
+            const int r = e >> 4, kk = e & 15;
+            float x = A[(int64_t)r * ars + (int64_t)(k0 + kk) * acs];
+            if (kscale) x *= kscale[k0 + kk];
+            as[kk * LD + r] = x;
+            const int kb = e >> 6, n = e & 63;
+            bs[kb * LD + n] = B[(int64_t)(k0 + kb) * brs + (int64_t)(n0 + n) * bcs];
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int kk = 0; kk < 16; ++kk) {
+            const f32x4 a = *reinterpret_cast<const f32x4*>(as + kk * LD + 4 * tr);
+            const f32x4 b = *reinterpret_cast<const f32x4*>(bs + kk * LD + 4 * tc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] += a[i] * b[j];
+        }
+        __syncthreads();
+    }
+}
+
+__device__ __forceinline__ void zero(float acc[4][4])
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+}
+
+// Per chunk-head slices of the workspace.
+struct Slices {
+    float *Q, *K, *V, *dO, *rq, *rk, *gam, *bet, *T, *P, *KKG, *W, *U, *DK, *E, *dDl;
+    float *S, *Dl, *dS, *dD, *dQ, *dK, *dW, *dPG, *dT, *X1, *Bd;
+};
+
+__device__ Slices slices(const BwdArgs& a, int64_t b)
+{
+    const BwdLayout& L = a.lay;
+    unsigned char* ws = a.ws;
+    const int64_t cdk = (int64_t)BC * a.dk, cdv = (int64_t)BC * a.dv, cc = BC * BC, dvdk = (int64_t)a.dv * a.dk;
+    auto f = [&](size_t off, int64_t per) { return reinterpret_cast<float*>(ws + off) + b * per; };
+    Slices s;
+    s.Q = f(L.off_Q, cdk);
+    s.K = f(L.off_K, cdk);
+    s.V = f(L.off_V, cdv);
+    s.dO = f(L.off_dO, cdv);
+    s.rq = f(L.off_rq, BC);
+    s.rk = f(L.off_rk, BC);
+    s.gam = f(L.off_gam, BC);
+    s.bet = f(L.off_bet, BC);
+    s.T = f(L.off_T, cc);
+    s.P = f(L.off_P, cc);
+    s.KKG = f(L.off_KKG, cc);
+    s.W = f(L.off_W, cdk);
+    s.U = f(L.off_U, cdv);
+    s.DK = f(L.off_DK, cdk);
+    s.E = f(L.off_E, cdv);
+    s.dDl = f(L.off_dDl, cdv);
+    s.S = f(L.off_S, dvdk);
+    s.Dl = f(L.off_Dl, cdv);
+    s.dS = f(L.off_dS, dvdk);
+    s.dD = f(L.off_dD, cdv);
+    s.dQ = f(L.off_dQ, cdk);
+    s.dK = f(L.off_dK, cdk);
+    s.dW = f(L.off_dW, cdk);
+    s.dPG = f(L.off_dPG, cc);
+    s.dT = f(L.off_dT, cc);
+    s.X1 = f(L.off_X1, cc);
+    s.Bd = f(L.off_Bd, cc);
+    return s;
+}
+
+// Chunk table: header[0] = 1 if cu_seqlens is invalid (then no chunk is
+// processed), header[1] = number of chunks; tab[c] = {first token, length,
+// sequence, 0}; seq_first[n] = first chunk of sequence n.
+__global__ __launch_bounds__(64) void bwd_table_kernel(const int32_t* __restrict__ cu, int32_t N, int64_t T,
+                                                       int64_t max_chunks, int32_t* __restrict__ header,
+                                                       int32_t* __restrict__ tab, int32_t* __restrict__ seq_first)
+{
+    if (threadIdx.x != 0) return;
+    bool ok = true;
+    if (cu) {
+        ok = cu[0] == 0 && (int64_t)cu[N] == T;
+        for (int32_t n = 0; ok && n < N; ++n) ok = cu[n + 1] >= cu[n];
+    }
+    int64_t count = 0;
+    for (int32_t n = 0; n < N; ++n) {
+        seq_first[n] = (int32_t)count;
+        if (!ok) continue;
+        const int64_t s = cu ? cu[n] : 0, e = cu ? cu[n + 1] : T;
+        for (int64_t p = s; p < e && count < max_chunks; p += BC, ++count) {
+            tab[4 * count + 0] = (int32_t)p;
+            tab[4 * count + 1] = (int32_t)min((int64_t)BC, e - p);
+            tab[4 * count + 2] = n;
+            tab[4 * count + 3] = 0;
+        }
+    }
+    seq_first[N] = (int32_t)count;
+    header[0] = ok ? 0 : 1;
+    header[1] = (int32_t)count;
+}
+
+template <typename TIn>
+__global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a)
+{
+    const int64_t b = blockIdx.x;
+    const int32_t* header = reinterpret_cast<const int32_t*>(a.ws + a.lay.off_header);
+    const int32_t* tab = reinterpret_cast<const int32_t*>(a.ws + a.lay.off_tab);
+    const int64_t c = b / a.H;
+    const int h = (int)(b % a.H);
+    if (c >= header[1]) return;
+    const int tok0 = tab[4 * c], len = tab[4 * c + 1];
+    const int dk = a.dk, dv = a.dv, H = a.H;
+    Slices s = slices(a, b);
+    __shared__ __align__(16) float as[16 * LD], bs[16 * LD];
+    __shared__ float gam[BC], bet[BC], bge[BC], dd[BC], eg[BC];
+    __shared__ float Am[BC][BC + 1], Ts[BC][BC + 1];
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    const TIn* q = (const TIn*)a.q;
+    const TIn* k = (const TIn*)a.k;
+    const TIn* v = (const TIn*)a.v;
+    const TIn* dO = (const TIn*)a.dO;
+
+    // rows of the chunk, normalised and padded with zeros
+    for (int r = wv; r < BC; r += 4) {
+        const bool live = r < len;
+        const int64_t row = (int64_t)(tok0 + (live ? r : 0)) * H + h;
+        float ssq = 0.f, ssk = 0.f;
+        for (int col = lane; col < dk; col += 64) {
+            const float xq = live ? Elem<TIn>::load(q, row * dk + col) : 0.f;
+            const float xk = live ? Elem<TIn>::load(k, row * dk + col) : 0.f;
+            ssq += xq * xq;
+            ssk += xk * xk;
+        }
+        ssq = group_sum<64>(ssq);
+        ssk = group_sum<64>(ssk);
+        const float rq = a.l2norm ? 1.0f / sqrtf(ssq + kNormEps) : 1.f;
+        const float rk = a.l2norm ? 1.0f / sqrtf(ssk + kNormEps) : 1.f;
+        for (int col = lane; col < dk; col += 64) {
+            s.Q[r * dk + col] = live ? Elem<TIn>::load(q, row * dk + col) * rq : 0.f;
+            s.K[r * dk + col] = live ? Elem<TIn>::load(k, row * dk + col) * rk : 0.f;
+        }
+        for (int col = lane; col < dv; col += 64) {
+            s.V[r * dv + col] = live ? Elem<TIn>::load(v, row * dv + col) : 0.f;
+            s.dO[r * dv + col] = live ? Elem<TIn>::load(dO, row * dv + col) : 0.f;
+        }
+        if (lane == 0) {
+            s.rq[r] = rq;
+            s.rk[r] = rk;
+        }
+    }
+    if (t == 0) {
+        float acc = 0.f;
+        for (int r = 0; r < BC; ++r) {
+            const bool live = r < len;
+            const int64_t row = (int64_t)(tok0 + (live ? r : 0)) * H + h;
+            acc += live ? a.g[row] : 0.f;
+            gam[r] = acc;
+            bet[r] = live ? a.beta[row] : 0.f;
+        }
+    }
+    __syncthreads();
+    if (t < BC) {
+        eg[t] = expf(gam[t]);
+        dd[t] = expf(gam[BC - 1] - gam[t]);
+        bge[t] = bet[t] * eg[t];
+        s.gam[t] = gam[t];
+        s.bet[t] = bet[t];
+    }
+    __syncthreads();  // also publishes the rows written above to the whole workgroup
+
+    const int tr = t >> 4, tc = t & 15;
+    float acc[4][4];
+    // K K^T -> KKG = strict_lower(K K^T o Gamma), A = diag(beta) KKG
+    zero(acc);
+    mm64(acc, s.K, dk, 1, nullptr, s.K, 1, dk, dk, 0, as, bs);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 4 * tr + i, n = 4 * tc + j;
+            const float x = n < r ? acc[i][j] * expf(gam[r] - gam[n]) : 0.f;
+            s.KKG[r * BC + n] = x;
+            Am[r][n] = bet[r] * x;
+        }
+    // Q K^T -> P = lower(Q K^T o Gamma)
+    zero(acc);
+    mm64(acc, s.Q, dk, 1, nullptr, s.K, 1, dk, dk, 0, as, bs);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 4 * tr + i, n = 4 * tc + j;
+            s.P[r * BC + n] = n <= r ? acc[i][j] * expf(gam[r] - gam[n]) : 0.f;
+        }
+    __syncthreads();
+    // T = (I + A)^{-1} by forward substitution, one row per step
+    for (int r = 0; r < BC; ++r) {
+        if (t < BC) {
+            float x = (t == r) ? 1.f : 0.f;
+            for (int j = 0; j < r; ++j) x -= Am[r][j] * Ts[j][t];
+            Ts[r][t] = x;
+        }
+        __syncthreads();
+    }
+    for (int e = t; e < BC * BC; e += 256) s.T[e] = Ts[e >> 6][e & 63];
+    __syncthreads();
+    // W = T diag(beta e^gamma) K,  D K,  then U = T diag(beta) V,  E = scale e^gamma dO
+    for (int n0 = 0; n0 < dk; n0 += 64) {
+        zero(acc);
+        mm64(acc, s.T, BC, 1, bge, s.K, dk, 1, BC, n0, as, bs);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 4 * tr + i, n = n0 + 4 * tc + j;
+                s.W[r * dk + n] = acc[i][j];
+                s.DK[r * dk + n] = dd[r] * s.K[r * dk + n];
+            }
+    }
+    for (int n0 = 0; n0 < dv; n0 += 64) {
+        zero(acc);
+        mm64(acc, s.T, BC, 1, bet, s.V, dv, 1, BC, n0, as, bs);
+        float acc2[4][4];
+        zero(acc2);
+        mm64(acc2, s.P, 1, BC, nullptr, s.dO, dv, 1, BC, n0, as, bs);  // P^T dO
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 4 * tr + i, n = n0 + 4 * tc + j;
+                s.U[r * dv + n] = acc[i][j];
+                s.E[r * dv + n] = a.scale * eg[r] * s.dO[r * dv + n];
+                s.dDl[r * dv + n] = a.scale * acc2[i][j];
+            }
+    }
+}
+
+// One row-split recurrence over the chunks of each sequence (see the header):
+//     Delta = X + ysign Y S^T                 (C x 16 rows of this workgroup)
+//     S    <- e^{gamma_L} S + zsign Delta^T Z + E^T F
+// storing S before each chunk (S_store) and Delta (D_store).  A workgroup owns
+// 16 rows of one (sequence, head) state; 16 lanes share a row, each holding
+// DK/16 columns as float4 vectors at columns 4 (j + 16 m).
+template <int DK>
+__global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs a, const float* __restrict__ X, size_t off_X,
+                                                        size_t off_Y, float ysign, size_t off_Z, float zsign,
+                                                        size_t off_E, size_t off_F, const float* __restrict__ S_init,
+                                                        float* __restrict__ S_final, size_t off_Sst, size_t off_Dst,
+                                                        int reverse)
+{
+    constexpr int NV = DK / 64;
+    const int dv = a.dv, H = a.H;
+    const int rblocks = dv / 16;
+    const int64_t pair = blockIdx.x / rblocks;
+    const int rb = (int)(blockIdx.x % rblocks);
+    const int n = (int)(pair / H), h = (int)(pair % H);
+    const int t = threadIdx.x, rl = t >> 4, j = t & 15;
+    const int row = rb * 16 + rl;
+    const int32_t* seq_first = reinterpret_cast<const int32_t*>(a.ws + a.lay.off_seq_first);
+    const float* gamv = reinterpret_cast<const float*>(a.ws + a.lay.off_gam);
+    auto wsf = [&](size_t off) { return reinterpret_cast<float*>(a.ws + off); };
+    const float* Xb = X ? X : wsf(off_X);
+    const float* Yb = wsf(off_Y);
+    const float* Zb = wsf(off_Z);
+    const float* Eb = off_E ? wsf(off_E) : nullptr;
+    const float* Fb = off_F ? wsf(off_F) : nullptr;
+    float* Sst = wsf(off_Sst);
+    float* Dst = wsf(off_Dst);
+    __shared__ f32x4 buf[BC * DK / 4];
+    __shared__ float xs[BC][16], es[BC][16], dsm[BC][16];
+
+    f32x4 s[NV];
+    const int64_t srow = ((int64_t)(n * H + h) * dv + row) * DK;
+#pragma unroll
+    for (int m = 0; m < NV; ++m)
+        s[m] = S_init ? *reinterpret_cast<const f32x4*>(S_init + srow + 4 * (j + 16 * m)) : f32x4{0.f, 0.f, 0.f, 0.f};
+    const int c0 = seq_first[n], c1 = seq_first[n + 1];
+    for (int it = 0; it < c1 - c0; ++it) {
+        const int64_t c = reverse ? c1 - 1 - it : c0 + it;
+        const int64_t ch = c * H + h;
+        const int64_t srec = (ch * dv + row) * DK;
+#pragma unroll
+        for (int m = 0; m < NV; ++m) *reinterpret_cast<f32x4*>(Sst + srec + 4 * (j + 16 * m)) = s[m];
+        __syncthreads();  // previous step's readers of buf, xs, es, dsm are done
+        const f32x4* Y4 = reinterpret_cast<const f32x4*>(Yb + ch * BC * DK);
+        for (int e = t; e < BC * DK / 4; e += 256) buf[e] = Y4[e];
+        for (int e = t; e < BC * 16; e += 256) {
+            const int cc = e >> 4, rr = e & 15;
+            const int64_t gi = (ch * BC + cc) * dv + rb * 16 + rr;
+            xs[cc][rr] = Xb[gi];
+            es[cc][rr] = Eb ? Eb[gi] : 0.f;
+        }
+        __syncthreads();
+        float p[BC];
+#pragma unroll
+        for (int cc = 0; cc < BC; ++cc) {
+            float x = 0.f;
+#pragma unroll
+            for (int m = 0; m < NV; ++m) {
+                const f32x4 y = buf[cc * (DK / 4) + j + 16 * m];
+                x += y.x * s[m].x + y.y * s[m].y + y.z * s[m].z + y.w * s[m].w;
+            }
+            p[cc] = x;
+        }
+#pragma unroll
+        for (int cc = 0; cc < BC; ++cc) p[cc] = xs[cc][rl] + ysign * group_sum<16>(p[cc]);
+        if (j == 0)
+#pragma unroll
+            for (int cc = 0; cc < BC; ++cc) dsm[cc][rl] = p[cc];
+        __syncthreads();  // buf (Y) and dsm complete
+        const f32x4* Z4 = reinterpret_cast<const f32x4*>(Zb + ch * BC * DK);
+        for (int e = t; e < BC * DK / 4; e += 256) buf[e] = Z4[e];
+        for (int e = t; e < BC * 16; e += 256) {
+            const int cc = e >> 4, rr = e & 15;
+            Dst[(ch * BC + cc) * dv + rb * 16 + rr] = dsm[cc][rr];
+        }
+        __syncthreads();
+        const float decay = expf(gamv[ch * BC + BC - 1]);
+#pragma unroll
+        for (int m = 0; m < NV; ++m) s[m] *= decay;
+#pragma unroll
+        for (int cc = 0; cc < BC; ++cc) {
+            const float w = zsign * p[cc];
+#pragma unroll
+            for (int m = 0; m < NV; ++m) s[m] += w * buf[cc * (DK / 4) + j + 16 * m];
+        }
+        if (Fb) {
+            __syncthreads();
+            const f32x4* F4 = reinterpret_cast<const f32x4*>(Fb + ch * BC * DK);
+            for (int e = t; e < BC * DK / 4; e += 256) buf[e] = F4[e];
+            __syncthreads();
+#pragma unroll
+            for (int cc = 0; cc < BC; ++cc) {
+                const float w = es[cc][rl];
+#pragma unroll
+                for (int m = 0; m < NV; ++m) s[m] += w * buf[cc * (DK / 4) + j + 16 * m];
+            }
+        }
+    }
+    if (S_final)
+#pragma unroll
+        for (int m = 0; m < NV; ++m) *reinterpret_cast<f32x4*>(S_final + srow + 4 * (j + 16 * m)) = s[m];
+}
+
+__global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a)
+{
+    const int64_t b = blockIdx.x;
+    const int32_t* header = reinterpret_cast<const int32_t*>(a.ws + a.lay.off_header);
+    const int32_t* tab = reinterpret_cast<const int32_t*>(a.ws + a.lay.off_tab);
+    const int64_t c = b / a.H;
+    const int h = (int)(b % a.H);
+    if (c >= header[1]) return;
+    const int tok0 = tab[4 * c], len = tab[4 * c + 1];
+    const int dk = a.dk, dv = a.dv, H = a.H;
+    const float scale = a.scale;
+    Slices s = slices(a, b);
+    __shared__ __align__(16) float as[16 * LD], bs[16 * LD];
+    __shared__ float gam[BC], bet[BC], eg[BC], dd[BC], bge[BC], dgam[BC], dbet[BC];
+    __shared__ float red[4];
+    __shared__ float cs[16][BC];
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    const int tr = t >> 4, tc = t & 15;
+    if (t < BC) {
+        gam[t] = s.gam[t];
+        bet[t] = s.bet[t];
+        dgam[t] = 0.f;
+        dbet[t] = 0.f;
+    }
+    __syncthreads();
+    if (t < BC) {
+        eg[t] = expf(gam[t]);
+        dd[t] = expf(gam[BC - 1] - gam[t]);
+        bge[t] = bet[t] * eg[t];
+    }
+    __syncthreads();
+    float acc[4][4];
+    float rowp[4];
+
+    // Reductions in a fixed order (the results do not depend on scheduling):
+    // a row r = 4 tr + i of a 64 x 64 block belongs to the 16 lanes of one tr,
+    // whose lane tc = 0 is its only writer; column sums go through cs.
+    auto row_add = [&](float* dst, float sgn) {  // dst[r] += sgn * rowp[i] summed over the 16 lanes of a row
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float x = group_sum<16>(rowp[i]);
+            if (tc == 0) dst[4 * tr + i] += sgn * x;
+        }
+    };
+    auto col_sub = [&](float* dst, const float colp[4]) {  // dst[n] -= column n summed over all rows
+#pragma unroll
+        for (int j = 0; j < 4; ++j) cs[tr][4 * tc + j] = colp[j];
+        __syncthreads();
+        if (t < BC) {
+            float x = 0.f;
+            for (int i = 0; i < 16; ++i) x += cs[i][t];
+            dst[t] -= x;
+        }
+        __syncthreads();
+    };
+
+    // dQ = scale e^gamma (dO S);  dgamma_r += Q_r . dQ_r
+    rowp[0] = rowp[1] = rowp[2] = rowp[3] = 0.f;
+    for (int n0 = 0; n0 < dk; n0 += 64) {
+        zero(acc);
+        mm64(acc, s.dO, dv, 1, nullptr, s.S, dk, 1, dv, n0, as, bs);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 4 * tr + i, n = n0 + 4 * tc + j;
+                const float x = scale * eg[r] * acc[i][j];
+                s.dQ[r * dk + n] = x;
+                rowp[i] += s.Q[r * dk + n] * x;
+            }
+    }
+    row_add(dgam, 1.f);
+    // dK = D (Delta dS);  d(dd)_r = K_r . (Delta dS)_r
+    rowp[0] = rowp[1] = rowp[2] = rowp[3] = 0.f;
+    for (int n0 = 0; n0 < dk; n0 += 64) {
+        zero(acc);
+        mm64(acc, s.Dl, dv, 1, nullptr, s.dS, dk, 1, dv, n0, as, bs);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 4 * tr + i, n = n0 + 4 * tc + j;
+                s.dK[r * dk + n] = dd[r] * acc[i][j];
+                rowp[i] += s.K[r * dk + n] * acc[i][j];
+            }
+    }
+    float dgL = 0.f;  // gradient of gamma_L, reduced over the workgroup below
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float x = group_sum<16>(rowp[i]);
+        const int r = 4 * tr + i;
+        if (tc == 0) {
+            dgam[r] -= x * dd[r];
+            dgL += x * dd[r];
+        }
+    }
+    // + e^{gamma_L} <dS, S>
+    {
+        const int64_t n4 = (int64_t)dv * dk / 4;
+        const f32x4* S4 = reinterpret_cast<const f32x4*>(s.S);
+        const f32x4* dS4 = reinterpret_cast<const f32x4*>(s.dS);
+        float x = 0.f;
+        for (int64_t e = t; e < n4; e += 256) {
+            const f32x4 u = S4[e], w = dS4[e];
+            x += u.x * w.x + u.y * w.y + u.z * w.z + u.w * w.w;
+        }
+        dgL += expf(gam[BC - 1]) * x;
+    }
+    dgL = group_sum<64>(dgL);
+    if (lane == 0) red[wv] = dgL;
+    __syncthreads();
+    // dP = scale lower(dO Delta^T);  dgamma from P;  dPG = dP o Gamma
+    zero(acc);
+    mm64(acc, s.dO, dv, 1, nullptr, s.Dl, 1, dv, dv, 0, as, bs);
+    {
+        float colp[4] = {0.f, 0.f, 0.f, 0.f};
+        rowp[0] = rowp[1] = rowp[2] = rowp[3] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 4 * tr + i, n = 4 * tc + j;
+                const float dp = n <= r ? scale * acc[i][j] : 0.f;
+                const float m = dp * s.P[r * BC + n];
+                rowp[i] += m;
+                colp[j] += m;
+                s.dPG[r * BC + n] = n <= r ? dp * expf(gam[r] - gam[n]) : 0.f;
+            }
+        row_add(dgam, 1.f);
+        col_sub(dgam, colp);  // its barriers also complete dPG
+    }
+    // dQ += dPG K;  dK += dPG^T Q
+    for (int n0 = 0; n0 < dk; n0 += 64) {
+        zero(acc);
+        mm64(acc, s.dPG, BC, 1, nullptr, s.K, dk, 1, BC, n0, as, bs);
+        float acc2[4][4];
+        zero(acc2);
+        mm64(acc2, s.dPG, 1, BC, nullptr, s.Q, dk, 1, BC, n0, as, bs);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 4 * tr + i, n = n0 + 4 * tc + j;
+                s.dQ[r * dk + n] += acc[i][j];
+                s.dK[r * dk + n] += acc2[i][j];
+            }
+    }
+    // dW = -(dDelta S)
+    for (int n0 = 0; n0 < dk; n0 += 64) {
+        zero(acc);
+        mm64(acc, s.dD, dv, 1, nullptr, s.S, dk, 1, dv, n0, as, bs);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) s.dW[(4 * tr + i) * dk + n0 + 4 * tc + j] = -acc[i][j];
+    }
+    __syncthreads();  // dW complete
+    // dT = (dDelta V^T) diag(beta) + (dW K^T) diag(beta e^gamma)
+    {
+        zero(acc);
+        mm64(acc, s.dD, dv, 1, nullptr, s.V, 1, dv, dv, 0, as, bs);
+        float acc2[4][4];
+        zero(acc2);
+        mm64(acc2, s.dW, dk, 1, nullptr, s.K, 1, dk, dk, 0, as, bs);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 4 * tr + i, n = 4 * tc + j;
+                s.dT[r * BC + n] = acc[i][j] * bet[n] + acc2[i][j] * bge[n];
+            }
+    }
+    // dV = diag(beta) T^T dDelta;  dbeta_r += (T^T dDelta)_r . V_r
+    rowp[0] = rowp[1] = rowp[2] = rowp[3] = 0.f;
+    for (int n0 = 0; n0 < dv; n0 += 64) {
+        zero(acc);
+        mm64(acc, s.T, 1, BC, nullptr, s.dD, dv, 1, BC, n0, as, bs);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 4 * tr + i, n = n0 + 4 * tc + j;
+                rowp[i] += acc[i][j] * s.V[r * dv + n];
+                if (r < len) a.dv_out[((int64_t)(tok0 + r) * H + h) * dv + n] = bet[r] * acc[i][j];
+            }
+    }
+    row_add(dbet, 1.f);
+    // dK += diag(beta e^gamma) T^T dW;  (T^T dW)_r . K_r feeds dbeta and dgamma
+    rowp[0] = rowp[1] = rowp[2] = rowp[3] = 0.f;
+    for (int n0 = 0; n0 < dk; n0 += 64) {
+        zero(acc);
+        mm64(acc, s.T, 1, BC, nullptr, s.dW, dk, 1, BC, n0, as, bs);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 4 * tr + i, n = n0 + 4 * tc + j;
+                s.dK[r * dk + n] += bge[r] * acc[i][j];
+                rowp[i] += acc[i][j] * s.K[r * dk + n];
+            }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float x = group_sum<16>(rowp[i]);
+        const int r = 4 * tr + i;
+        if (tc == 0) {
+            dbet[r] += eg[r] * x;
+            dgam[r] += bge[r] * x;
+        }
+    }
+    __syncthreads();  // dT complete
+    // X1 = dT T^T
+    zero(acc);
+    mm64(acc, s.dT, BC, 1, nullptr, s.T, 1, BC, BC, 0, as, bs);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s.X1[(4 * tr + i) * BC + 4 * tc + j] = acc[i][j];
+    __syncthreads();
+    // dA = -strict_lower(T^T X1);  Bd = diag(beta) (dA o Gamma);  dbeta, dgamma from A
+    zero(acc);
+    mm64(acc, s.T, 1, BC, nullptr, s.X1, BC, 1, BC, 0, as, bs);
+    {
+        float colp[4] = {0.f, 0.f, 0.f, 0.f};
+        float rowb[4] = {0.f, 0.f, 0.f, 0.f};
+        rowp[0] = rowp[1] = rowp[2] = rowp[3] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 4 * tr + i, n = 4 * tc + j;
+                const float da = n < r ? -acc[i][j] : 0.f;
+                const float kkg = s.KKG[r * BC + n];  // zero unless n < r
+                const float m = da * bet[r] * kkg;  // dA o A
+                rowb[i] += da * kkg;
+                rowp[i] += m;
+                colp[j] += m;
+                s.Bd[r * BC + n] = n < r ? bet[r] * da * expf(gam[r] - gam[n]) : 0.f;
+            }
+        row_add(dgam, 1.f);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rowp[i] = rowb[i];
+        row_add(dbet, 1.f);
+        col_sub(dgam, colp);  // its barriers also complete Bd
+    }
+    // dK += Bd K + Bd^T K
+    for (int n0 = 0; n0 < dk; n0 += 64) {
+        zero(acc);
+        mm64(acc, s.Bd, BC, 1, nullptr, s.K, dk, 1, BC, n0, as, bs);
+        mm64(acc, s.Bd, 1, BC, nullptr, s.K, dk, 1, BC, n0, as, bs);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) s.dK[(4 * tr + i) * dk + n0 + 4 * tc + j] += acc[i][j];
+    }
+    __syncthreads();  // dQ, dK, dgam, dbet complete
+    // dg: reverse cumulative sum of dgamma (gamma_L is the last, padded-constant, entry)
+    if (t == 0) {
+        float run = red[0] + red[1] + red[2] + red[3];
+        for (int r = BC - 1; r >= 0; --r) {
+            run += dgam[r];
+            if (r < len) {
+                const int64_t row = (int64_t)(tok0 + r) * H + h;
+                a.dg[row] = run;
+                a.dbeta[row] = dbet[r];
+            }
+        }
+    }
+    // through the L2 norms: dx = r (dx^ - x^ (x^ . dx^))
+    for (int r = wv; r < len; r += 4) {
+        const int64_t row = (int64_t)(tok0 + r) * H + h;
+        float pq = 0.f, pk = 0.f;
+        for (int col = lane; col < dk; col += 64) {
+            pq += s.Q[r * dk + col] * s.dQ[r * dk + col];
+            pk += s.K[r * dk + col] * s.dK[r * dk + col];
+        }
+        pq = a.l2norm ? group_sum<64>(pq) : 0.f;
+        pk = a.l2norm ? group_sum<64>(pk) : 0.f;
+        const float rq = s.rq[r], rk = s.rk[r];
+        for (int col = lane; col < dk; col += 64) {
+            a.dq[row * dk + col] = rq * (s.dQ[r * dk + col] - s.Q[r * dk + col] * pq);
+            a.dk_out[row * dk + col] = rk * (s.dK[r * dk + col] - s.K[r * dk + col] * pk);
+        }
+    }
+}
+
+template <int DK>
+hipError_t launch_chain(const BwdArgs& a, const float* X, size_t off_X, size_t off_Y, float ysign, size_t off_Z,
+                        float zsign, size_t off_E, size_t off_F, const float* S_init, float* S_final, size_t off_Sst,
+                        size_t off_Dst, int reverse)
+{
+    const int64_t blocks = (int64_t)a.N * a.H * (a.dv / 16);
+    hipLaunchKernelGGL((bwd_chain_kernel<DK>), dim3((uint32_t)blocks), dim3(256), 0, a.stream, a, X, off_X, off_Y,
+                       ysign, off_Z, zsign, off_E, off_F, S_init, S_final, off_Sst, off_Dst, reverse);
+    return hipGetLastError();
+}
+
+hipError_t chain_dispatch(const BwdArgs& a, const float* X, size_t off_X, size_t off_Y, float ysign, size_t off_Z,
+                          float zsign, size_t off_E, size_t off_F, const float* S_init, float* S_final,
+                          size_t off_Sst, size_t off_Dst, int reverse)
+{
+    switch (a.dk) {
+        case 64: return launch_chain<64>(a, X, off_X, off_Y, ysign, off_Z, zsign, off_E, off_F, S_init, S_final,
+                                         off_Sst, off_Dst, reverse);
+        case 128: return launch_chain<128>(a, X, off_X, off_Y, ysign, off_Z, zsign, off_E, off_F, S_init, S_final,
+                                           off_Sst, off_Dst, reverse);
+        case 256: return launch_chain<256>(a, X, off_X, off_Y, ysign, off_Z, zsign, off_E, off_F, S_init, S_final,
+                                           off_Sst, off_Dst, reverse);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+bool backward_supported(int32_t dk, int32_t dv)
+{
+    return (dk == 64 || dk == 128 || dk == 256) && (dv == 64 || dv == 128 || dv == 256);
+}
+
+BwdLayout backward_layout(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv)
+{
+    BwdLayout L;
+    memset(&L, 0, sizeof L);
+    L.max_chunks = T / BC + N;
+    const size_t chs = (size_t)L.max_chunks * H;
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = up(off + bytes);
+        return o;
+    };
+    L.off_header = take(64);
+    L.off_tab = take((size_t)L.max_chunks * 16);
+    L.off_seq_first = take(((size_t)N + 1) * 4);
+    const size_t cdk = chs * BC * dk * 4, cdv = chs * BC * dv * 4, cc = chs * BC * BC * 4, c1 = chs * BC * 4;
+    const size_t st = chs * (size_t)dv * dk * 4;
+    L.off_Q = take(cdk);
+    L.off_K = take(cdk);
+    L.off_V = take(cdv);
+    L.off_dO = take(cdv);
+    L.off_rq = take(c1);
+    L.off_rk = take(c1);
+    L.off_gam = take(c1);
+    L.off_bet = take(c1);
+    L.off_T = take(cc);
+    L.off_P = take(cc);
+    L.off_KKG = take(cc);
+    L.off_W = take(cdk);
+    L.off_U = take(cdv);
+    L.off_DK = take(cdk);
+    L.off_E = take(cdv);
+    L.off_dDl = take(cdv);
+    L.off_S = take(st);
+    L.off_Dl = take(cdv);
+    L.off_dS = take(st);
+    L.off_dD = take(cdv);
+    L.off_dQ = take(cdk);
+    L.off_dK = take(cdk);
+    L.off_dW = take(cdk);
+    L.off_dPG = take(cc);
+    L.off_dT = take(cc);
+    L.off_X1 = take(cc);
+    L.off_Bd = take(cc);
+    L.total = off;
+    return L;
+}
+
+hipError_t launch_backward(const BwdArgs& a)
+{
+    const BwdLayout& L = a.lay;
+    int32_t* header = reinterpret_cast<int32_t*>(a.ws + L.off_header);
+    hipLaunchKernelGGL(bwd_table_kernel, dim3(1), dim3(64), 0, a.stream, a.cu_seqlens, a.N, a.T, L.max_chunks, header,
+                       reinterpret_cast<int32_t*>(a.ws + L.off_tab), reinterpret_cast<int32_t*>(a.ws + L.off_seq_first));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t chblocks = L.max_chunks * a.H;
+    if (chblocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    if (a.bf16)
+        hipLaunchKernelGGL((bwd_local_kernel<uint16_t>), dim3((uint32_t)chblocks), dim3(256), 0, a.stream, a);
+    else
+        hipLaunchKernelGGL((bwd_local_kernel<float>), dim3((uint32_t)chblocks), dim3(256), 0, a.stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // forward: Delta = U - W S^T,  S <- e^{gamma_L} S + Delta^T (D K); records S and Delta
+    e = chain_dispatch(a, nullptr, L.off_U, L.off_W, -1.f, L.off_DK, 1.f, 0, 0, a.init_state, nullptr, L.off_S,
+                       L.off_Dl, 0);
+    if (e != hipSuccess) return e;
+    // reverse: dDelta = dDelta_local + (D K) dS^T,  dS <- e^{gamma_L} dS - dDelta^T W + E^T Q
+    e = chain_dispatch(a, nullptr, L.off_dDl, L.off_DK, 1.f, L.off_W, -1.f, L.off_E, L.off_Q, a.dstate, a.dinit,
+                       L.off_dS, L.off_dD, 1);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_grad_kernel, dim3((uint32_t)chblocks), dim3(256), 0, a.stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -96,4 +96,39 @@ struct FrontendArgs {
 
 hipError_t launch_frontend(const FrontendArgs& a);
 
+// Backward of the chunked prefill (fp32 workspace, chunk 64).  Offsets are
+// bytes into the workspace; per chunk-head arrays hold max_chunks * H slices.
+struct BwdLayout {
+    int64_t max_chunks;  // upper bound on sum_n ceil(L_n / 64)
+    size_t off_header, off_tab, off_seq_first;
+    size_t off_Q, off_K, off_V, off_dO, off_rq, off_rk, off_gam, off_bet;
+    size_t off_T, off_P, off_KKG, off_W, off_U, off_DK, off_E, off_dDl;
+    size_t off_S, off_Dl, off_dS, off_dD;
+    size_t off_dQ, off_dK, off_dW, off_dPG, off_dT, off_X1, off_Bd;
+    size_t total;
+};
+
+bool backward_supported(int32_t dk, int32_t dv);
+BwdLayout backward_layout(int64_t total_tokens, int32_t num_seqs, int32_t H, int32_t dk, int32_t dv);
+
+struct BwdArgs {
+    const void *q, *k, *v, *dO;           // [T][H][d], bf16 or fp32 (one type)
+    const float *g, *beta;                // [T][H]
+    const float *init_state, *dstate;     // [N][H][dv][dk] or NULL (zeros)
+    const int32_t* cu_seqlens;            // device [N + 1] or NULL (one sequence)
+    int32_t N;
+    int64_t T;
+    int32_t H, dk, dv;
+    bool bf16;
+    float scale;
+    int32_t l2norm;
+    float *dq, *dk_out, *dv_out, *dg, *dbeta;  // fp32, shapes of the inputs
+    float* dinit;                              // [N][H][dv][dk] or NULL
+    unsigned char* ws;
+    BwdLayout lay;
+    hipStream_t stream;
+};
+
+hipError_t launch_backward(const BwdArgs& a);
+
 }  // namespace gdn

@@ -72,6 +72,12 @@ def load_library(path: str | None = None):
             lib.gdn_frontend_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int,
                                                 vp, vp, vp, vp, vp, vp]
             lib.gdn_frontend_decode.restype = ctypes.c_int
+            lib.gdn_prefill_backward_workspace_size.argtypes = [i64, i32, i32, i32, i32]
+            lib.gdn_prefill_backward_workspace_size.restype = sz
+            lib.gdn_chunk_prefill_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32,
+                                                       i32, ctypes.c_int, f32, i32, vp, vp, vp, vp, vp, vp, vp, sz,
+                                                       vp]
+            lib.gdn_chunk_prefill_backward.restype = ctypes.c_int
             lib.gdn_status_string.argtypes = [ctypes.c_int]
             lib.gdn_status_string.restype = ctypes.c_char_p
             lib.gdn_version.argtypes = []
@@ -216,6 +222,79 @@ def chunk_prefill(q, k, v, g, beta, init_state=None, cu_seqlens=None, scale=None
     if st != 0:
         raise GdnError(st, "gdn_chunk_prefill")
     return out, final_state
+
+
+def _seqlens(cu_seqlens, dev):
+    """(device int32 tensor or None, host int32 tensor or None, N)."""
+    torch = _torch()
+    if cu_seqlens is None:
+        return None, None, 1
+    cu_host = None
+    if isinstance(cu_seqlens, torch.Tensor) and cu_seqlens.device.type == "cuda":
+        cu_dev = cu_seqlens.to(torch.int32).contiguous()
+    else:
+        cu_host = torch.as_tensor(cu_seqlens, dtype=torch.int32).contiguous().cpu()
+        cu_dev = cu_host.to(dev)
+    N = cu_dev.shape[0] - 1
+    if N < 1:
+        raise ValueError("cu_seqlens needs at least two entries")
+    return cu_dev, cu_host, N
+
+
+def prefill_backward_workspace_size(total_tokens: int, num_seqs: int, H: int, dk: int, dv: int) -> int:
+    return int(load_library().gdn_prefill_backward_workspace_size(total_tokens, num_seqs, H, dk, dv))
+
+
+def chunk_prefill_backward(q, k, v, g, beta, do, init_state=None, dstate=None, cu_seqlens=None, scale=None,
+                           qk_l2norm=True, workspace=None, return_dinit=True):
+    """Gradients of L = <do, o> + <dstate, final_state> for ``chunk_prefill``.
+
+    Inputs as for ``chunk_prefill``; do [T, H, dv] in the dtype of q; dstate
+    [N, H, dv, dk] fp32 or None (zeros).  Returns a dict of fp32 tensors dq, dk
+    [T, H, dk], dv [T, H, dv], dg, dbeta [T, H] and dinit [N, H, dv, dk] (None
+    when ``return_dinit`` is false).
+    """
+    torch = _torch()
+    lib = load_library()
+    dev = q.device
+    _check(q, "q", device=dev)
+    dt = q.dtype
+    for name, t in (("k", k), ("v", v), ("do", do)):
+        _check(t, name, dtype=dt, device=dev)
+    _check(g, "g", dtype=torch.float32, device=dev)
+    _check(beta, "beta", dtype=torch.float32, device=dev)
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    if (k.shape != (T, H, dk) or v.shape[:2] != (T, H) or do.shape != (T, H, dv) or g.shape != (T, H)
+            or beta.shape != (T, H)):
+        raise ValueError("shape mismatch among q, k, v, do, g, beta")
+    cu_dev, cu_host, N = _seqlens(cu_seqlens, dev)
+    for name, t in (("init_state", init_state), ("dstate", dstate)):
+        if t is not None:
+            _check(t, name, dtype=torch.float32, device=dev)
+            if t.shape != (N, H, dv, dk):
+                raise ValueError(f"{name} must be [{N}, {H}, {dv}, {dk}]")
+    code = _dtype_code(q)
+    need = int(lib.gdn_prefill_backward_workspace_size(T, N, H, dk, dv))
+    if need == 0:
+        raise GdnError(3, "gdn_prefill_backward_workspace_size")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    f32 = torch.float32
+    out = {"dq": torch.empty((T, H, dk), dtype=f32, device=dev), "dk": torch.empty((T, H, dk), dtype=f32, device=dev),
+           "dv": torch.empty((T, H, dv), dtype=f32, device=dev), "dg": torch.empty((T, H), dtype=f32, device=dev),
+           "dbeta": torch.empty((T, H), dtype=f32, device=dev),
+           "dinit": torch.empty((N, H, dv, dk), dtype=f32, device=dev) if return_dinit else None}
+    s = -1.0 if scale is None else float(scale)
+    cu_host_ptr = None if cu_host is None else ctypes.c_void_p(cu_host.data_ptr())
+    st = lib.gdn_chunk_prefill_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(init_state), _ptr(do),
+                                        _ptr(dstate), _ptr(cu_dev), cu_host_ptr, N, T, H, dk, dv, code, s,
+                                        int(bool(qk_l2norm)), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                                        _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out["dinit"]), _ptr(workspace),
+                                        workspace.numel(), _stream(dev))
+    if st != 0:
+        raise GdnError(st, "gdn_chunk_prefill_backward")
+    return out
 
 
 def decode_step(q, k, v, g, beta, state, scale=None, qk_l2norm=True, out=None, gate=None, norm_weight=None,

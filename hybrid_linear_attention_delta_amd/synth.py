@@ -139,6 +139,17 @@ def prefill_inputs(T: int, H: int, dk: int, dv: int, dtype: str, seed: int, gate
     return PrefillInputs(q, k, v, g, beta, cu, dtype, init, dict(seed=seed, gate=gate))
 
 
+def backward_cotangents(T: int, H: int, dk: int, dv: int, N: int, dtype: str, seed: int,
+                        dstate_std: float | None = 0.1):
+    """Cotangents for a prefill backward: do [T,H,dv] ~ N(0,1) stored in ``dtype``
+    and dstate [N,H,dv,dk] fp32 ~ N(0, dstate_std^2) (None when dstate_std is None)."""
+    ss = np.random.SeedSequence([seed, 7])
+    ro, rs = [np.random.default_rng(s) for s in ss.spawn(2)]
+    do = _store(ro.standard_normal((T, H, dv)), dtype)
+    ds = None if dstate_std is None else (rs.standard_normal((N, H, dv, dk)) * dstate_std).astype(np.float32)
+    return do, ds
+
+
 def decode_state(N: int, H: int, dk: int, dv: int, seed: int, std: float = 0.02) -> np.ndarray:
     ss = np.random.SeedSequence(seed)
     rs = np.random.default_rng(ss.spawn(6)[5])

@@ -244,6 +244,51 @@ gdn_status gdn_frontend_decode(const void* xq, const void* xk, const void* xv, c
                                void* conv_state, int32_t N, int32_t H, int32_t dk, int32_t dv, gdn_dtype dt, void* q,
                                void* k, void* v, float* g, float* beta, hipStream_t stream);
 
+/*
+ * Bytes of device workspace gdn_chunk_prefill_backward needs for these sizes
+ * (0 for an unsupported or invalid combination).  It holds fp32 per-chunk
+ * intermediates, among them the state entering every chunk and the state
+ * gradient after it: about max_chunks * H * (2 dv dk + 14 * 64 (dk + dv))
+ * * 4 bytes, max_chunks = total_tokens / 64 + num_seqs.
+ */
+size_t gdn_prefill_backward_workspace_size(int64_t total_tokens, int32_t num_seqs, int32_t H, int32_t dk,
+                                           int32_t dv);
+
+/*
+ * Gradients of the chunked prefill.  Training evaluates the mixer in chunks
+ * (App. A.3, the paragraph after Eq. 21), so this differentiates the chunked
+ * (WY) form of gdn_chunk_prefill with chunk 64: given the cotangents d_o of
+ * the outputs and d_final_state of the final states, it returns the
+ * gradients of  L = sum <d_o, o> + sum <d_final_state, final_state>  with
+ * respect to q, k, v, g, beta and the initial state, through the optional
+ * q/k L2 normalisation.  It recomputes the forward from the inputs (nothing
+ * of a previous gdn_chunk_prefill call is reused).
+ *
+ *   q, k, v, g, beta, init_state, cu_seqlens, cu_seqlens_host, num_seqs,
+ *   total_tokens, H, dk, dv, dt, scale, qk_l2norm
+ *               as for gdn_chunk_prefill
+ *   d_o         [total_tokens, H, dv]  dt
+ *   d_final_state [num_seqs, H, dv, dk] fp32, or NULL for zeros
+ *   grad_q, grad_k [total_tokens, H, dk]  fp32 (written)
+ *   grad_v      [total_tokens, H, dv]  fp32 (written)
+ *   grad_g, grad_beta [total_tokens, H] fp32 (written)
+ *   grad_init_state [num_seqs, H, dv, dk] fp32 (written), or NULL
+ *   workspace   at least gdn_prefill_backward_workspace_size(...) bytes,
+ *               256-byte aligned
+ * Supported: dt in {GDN_F32, GDN_BF16}, dk and dv in {64, 128, 256}; the
+ * arithmetic is fp32 throughout.  Gradient buffers must not overlap the
+ * inputs or each other.  With an invalid device cu_seqlens (and no host
+ * mirror) no chunk is processed and the gradients are unspecified.
+ */
+gdn_status gdn_chunk_prefill_backward(const void* q, const void* k, const void* v, const float* g,
+                                      const float* beta, const float* init_state, const void* d_o,
+                                      const float* d_final_state, const int32_t* cu_seqlens,
+                                      const int32_t* cu_seqlens_host, int32_t num_seqs, int64_t total_tokens,
+                                      int32_t H, int32_t dk, int32_t dv, gdn_dtype dt, float scale,
+                                      int32_t qk_l2norm, float* grad_q, float* grad_k, float* grad_v,
+                                      float* grad_g, float* grad_beta, float* grad_init_state, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream);
+
 /* Static, human-readable name of a status code. */
 const char* gdn_status_string(gdn_status s);
 

@@ -192,3 +192,33 @@ def test_frontend_host_validation(lib):
     assert dec(N=-1) == 2
     assert dec(N=0) == 0
     assert dec(st=_fake(0x10008)) == 5
+
+
+def test_backward_host_validation(lib):
+    """The backward entry point checks sizes, support, pointers, alignment,
+    sequence bounds and the workspace on the host and returns before any launch."""
+    f = _fake()
+    need = lib.gdn_prefill_backward_workspace_size(128, 1, 2, 64, 64)
+    assert need > 0
+    assert lib.gdn_prefill_backward_workspace_size(128, 1, 2, 48, 64) == 0
+    assert lib.gdn_prefill_backward_workspace_size(128, 0, 2, 64, 64) == 0
+
+    def bwd(**kw):
+        return lib.gdn_chunk_prefill_backward(kw.get("q", f), f, f, f, f, None, f, None, kw.get("cu", None),
+                                              kw.get("cu_host", None), kw.get("N", 1), kw.get("T", 128), 2,
+                                              kw.get("dk", 64), 64, kw.get("dt", gdn.GDN_BF16), -1.0, 1,
+                                              kw.get("gq", f), f, f, f, f, None, kw.get("ws", f),
+                                              kw.get("wsb", need), None)
+
+    assert bwd(dk=96) == 3
+    assert bwd(dt=7) == 3
+    assert bwd(T=-1) == 2
+    assert bwd(N=2) == 2                       # several sequences need cu_seqlens
+    assert bwd(q=None) == 1
+    assert bwd(gq=None) == 1
+    assert bwd(gq=_fake(0x10004)) == 5         # gradients must be 16-byte aligned
+    assert bwd(ws=None) == 6
+    assert bwd(wsb=need - 1) == 6
+    assert bwd(ws=_fake(0x10010)) == 5         # workspace 256-byte aligned
+    bad = (ctypes.c_int32 * 3)(0, 100, 90)
+    assert bwd(N=2, cu=f, cu_host=bad) == 4
