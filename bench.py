@@ -48,6 +48,7 @@ if ROOT not in sys.path:
 METRIC = "GDN prefill tokens/s (H=6,d=256,T=64K) + decode state GB/s; % of roofline"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
 
 T, H, DK, DV, C = 65536, 6, 256, 256, 64
 DEC_N = 256
@@ -408,6 +409,40 @@ def bench_frontend(torch, gdn, synth, steps, warmup):
     return res
 
 
+def flops_backward_per_token():
+    """Chunked backward per token (all heads), algorithmic: the d_k d_v
+    contractions (forward chain 2, reverse chain 3, per-chunk dQ, dK, dW 3, each
+    2 d_k d_v flops), the C d terms (K K^T, Q K^T, W, dPG K, dPG^T Q, dT, T^T dW,
+    dA-terms of dK: 18 C d_k; U, P^T dO, dP, dT, dV: 10 C d_v) and the C x C ones."""
+    return H * (16 * DK * DV + 18 * C * DK + 10 * C * DV + 4 * C * C)
+
+
+def bench_backward(torch, gdn, synth, inp, steps, warmup):
+    """Gradients of the 64K-token prefill (gdn_chunk_prefill_backward): all
+    launches are on the current stream, timed with events around whole calls."""
+    dev = torch.device("cuda:0")
+    t = lambda a, b=False: synth.to_torch(a, dev, bf16=b)
+    q, k, v, g, beta = t(inp.q, True), t(inp.k, True), t(inp.v, True), t(inp.g), t(inp.beta)
+    do, ds = synth.backward_cotangents(T, H, DK, DV, 1, "bf16", synth.seed_for("prefill64k"))
+    do, ds = t(do, True), t(ds)
+    ws = torch.empty(gdn.prefill_backward_workspace_size(T, 1, H, DK, DV), dtype=torch.uint8, device=dev)
+    log(f"[bench] backward: workspace {ws.numel() / 2**30:.1f} GiB")
+    run = lambda: gdn.chunk_prefill_backward(q, k, v, g, beta, do, dstate=ds, workspace=ws)
+    for _ in range(max(1, warmup)):
+        run()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        run()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    log(f"[bench] backward {ms:.2f} ms per 64K-token step")
+    return ms
+
+
 def cpu_baseline(inp, max_threads=16):
     import oracle
 
@@ -432,6 +467,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other", action="store_true", help="skip the 8K and 2M-token prefill figures")
+    ap.add_argument("--no-backward", action="store_true", help="skip the prefill backward")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -451,6 +487,7 @@ def main():
     dec = None if a.no_decode else bench_decode(torch, gdn, synth, a.decode_steps)
     fe = bench_frontend(torch, gdn, synth, a.steps, a.warmup)
     other = None if a.no_other else bench_prefill_other(torch, gdn, synth, a.steps, a.warmup)
+    bwd_ms = None if a.no_backward else bench_backward(torch, gdn, synth, pre["inputs"], min(a.steps, 3), 1)
 
     tok_s = T / (pre["ms_per_step"] / 1e3)
     chain_flops = flops_chain_per_token() * T
@@ -541,6 +578,17 @@ def main():
         "decode_frontend_ms_per_step": fe["decode_frontend"],
         "decode_frontend_GBps": dec_fb / (fe["decode_frontend"] / 1e3) / 1e9,
     }
+    if bwd_ms is not None:
+        bf = flops_backward_per_token() * T
+        tf = bf / (bwd_ms / 1e3) / 1e12
+        out["backward"] = {
+            "workload": f"gdn_chunk_prefill_backward B=1 H={H} d_k={DK} d_v={DV} T={T} bf16 inputs, fp32 gradients",
+            "ms_per_step": bwd_ms,
+            "tokens_per_s": T / (bwd_ms / 1e3),
+            "algorithmic_flops_per_token": flops_backward_per_token(),
+            "roofline": {"kernel": "whole backward (fp32 on the vector ALUs)", "bound": "alu", "achieved": tf,
+                         "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s", "frac": tf / PEAK_F32_TFLOPS},
+        }
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(pre["inputs"])
     print(json.dumps(out), flush=True)

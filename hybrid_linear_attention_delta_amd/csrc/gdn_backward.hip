@@ -329,8 +329,36 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs a, const float* 
     const float* Fb = off_F ? wsf(off_F) : nullptr;
     float* Sst = wsf(off_Sst);
     float* Dst = wsf(off_Dst);
-    __shared__ f32x4 buf[BC * DK / 4];
+    // Operands pass through registers into two LDS buffers: each thread loads
+    // its share of a whole 64 x DK operand at once (PER vector loads in
+    // flight), and the loads of the next operand are issued before the
+    // arithmetic on the current one (Z during Y S^T, F or the next chunk's Y
+    // during the update).
+    constexpr int PER = BC * DK / 4 / 256;
+    __shared__ f32x4 bufA[BC * DK / 4], bufB[BC * DK / 4];
     __shared__ float xs[BC][16], es[BC][16], dsm[BC][16];
+    f32x4 reg[PER];
+    auto fetch = [&](const float* base, int64_t chx) {
+        const f32x4* p4 = reinterpret_cast<const f32x4*>(base + chx * BC * DK);
+#pragma unroll
+        for (int i = 0; i < PER; ++i) reg[i] = p4[t + 256 * i];
+    };
+    auto put = [&](f32x4* dst) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) dst[t + 256 * i] = reg[i];
+    };
+    // the chunk's X and E columns of this workgroup's rows, and its decay, fetched with Y
+    float xr[BC * 16 / 256], er[BC * 16 / 256], gl = 0.f;
+    auto fetch_small = [&](int64_t chx) {
+#pragma unroll
+        for (int i = 0; i < BC * 16 / 256; ++i) {
+            const int e = t + 256 * i;
+            const int64_t gi = (chx * BC + (e >> 4)) * dv + rb * 16 + (e & 15);
+            xr[i] = Xb[gi];
+            er[i] = Eb ? Eb[gi] : 0.f;
+        }
+        gl = gamv[chx * BC + BC - 1];
+    };
 
     f32x4 s[NV];
     const int64_t srow = ((int64_t)(n * H + h) * dv + row) * DK;
@@ -338,21 +366,27 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs a, const float* 
     for (int m = 0; m < NV; ++m)
         s[m] = S_init ? *reinterpret_cast<const f32x4*>(S_init + srow + 4 * (j + 16 * m)) : f32x4{0.f, 0.f, 0.f, 0.f};
     const int c0 = seq_first[n], c1 = seq_first[n + 1];
-    for (int it = 0; it < c1 - c0; ++it) {
-        const int64_t c = reverse ? c1 - 1 - it : c0 + it;
-        const int64_t ch = c * H + h;
+    const int steps = c1 - c0;
+    auto chunk_of = [&](int it) -> int64_t { return (int64_t)(reverse ? c1 - 1 - it : c0 + it) * H + h; };
+    if (steps > 0) {
+        fetch(Yb, chunk_of(0));
+        fetch_small(chunk_of(0));
+    }
+    for (int it = 0; it < steps; ++it) {
+        const int64_t ch = chunk_of(it);
+        const float decay = expf(gl);
         const int64_t srec = (ch * dv + row) * DK;
 #pragma unroll
         for (int m = 0; m < NV; ++m) *reinterpret_cast<f32x4*>(Sst + srec + 4 * (j + 16 * m)) = s[m];
-        __syncthreads();  // previous step's readers of buf, xs, es, dsm are done
-        const f32x4* Y4 = reinterpret_cast<const f32x4*>(Yb + ch * BC * DK);
-        for (int e = t; e < BC * DK / 4; e += 256) buf[e] = Y4[e];
-        for (int e = t; e < BC * 16; e += 256) {
-            const int cc = e >> 4, rr = e & 15;
-            const int64_t gi = (ch * BC + cc) * dv + rb * 16 + rr;
-            xs[cc][rr] = Xb[gi];
-            es[cc][rr] = Eb ? Eb[gi] : 0.f;
+        __syncthreads();  // the previous step's readers of bufA, bufB, xs, es, dsm are done
+        put(bufA);        // Y
+#pragma unroll
+        for (int i = 0; i < BC * 16 / 256; ++i) {
+            const int e = t + 256 * i;
+            xs[e >> 4][e & 15] = xr[i];
+            es[e >> 4][e & 15] = er[i];
         }
+        fetch(Zb, ch);
         __syncthreads();
         float p[BC];
 #pragma unroll
@@ -360,7 +394,7 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs a, const float* 
             float x = 0.f;
 #pragma unroll
             for (int m = 0; m < NV; ++m) {
-                const f32x4 y = buf[cc * (DK / 4) + j + 16 * m];
+                const f32x4 y = bufA[cc * (DK / 4) + j + 16 * m];
                 x += y.x * s[m].x + y.y * s[m].y + y.z * s[m].z + y.w * s[m].w;
             }
             p[cc] = x;
@@ -370,33 +404,38 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs a, const float* 
         if (j == 0)
 #pragma unroll
             for (int cc = 0; cc < BC; ++cc) dsm[cc][rl] = p[cc];
-        __syncthreads();  // buf (Y) and dsm complete
-        const f32x4* Z4 = reinterpret_cast<const f32x4*>(Zb + ch * BC * DK);
-        for (int e = t; e < BC * DK / 4; e += 256) buf[e] = Z4[e];
+        put(bufB);  // Z
+        if (Fb) {
+            fetch(Fb, ch);
+        } else if (it + 1 < steps) {
+            fetch(Yb, chunk_of(it + 1));
+            fetch_small(chunk_of(it + 1));
+        }
+        __syncthreads();  // bufB and dsm complete; bufA (Y) no longer read
         for (int e = t; e < BC * 16; e += 256) {
             const int cc = e >> 4, rr = e & 15;
             Dst[(ch * BC + cc) * dv + rb * 16 + rr] = dsm[cc][rr];
         }
-        __syncthreads();
-        const float decay = expf(gamv[ch * BC + BC - 1]);
 #pragma unroll
         for (int m = 0; m < NV; ++m) s[m] *= decay;
 #pragma unroll
         for (int cc = 0; cc < BC; ++cc) {
             const float w = zsign * p[cc];
 #pragma unroll
-            for (int m = 0; m < NV; ++m) s[m] += w * buf[cc * (DK / 4) + j + 16 * m];
+            for (int m = 0; m < NV; ++m) s[m] += w * bufB[cc * (DK / 4) + j + 16 * m];
         }
         if (Fb) {
-            __syncthreads();
-            const f32x4* F4 = reinterpret_cast<const f32x4*>(Fb + ch * BC * DK);
-            for (int e = t; e < BC * DK / 4; e += 256) buf[e] = F4[e];
+            put(bufA);  // F
+            if (it + 1 < steps) {
+                fetch(Yb, chunk_of(it + 1));
+                fetch_small(chunk_of(it + 1));
+            }
             __syncthreads();
 #pragma unroll
             for (int cc = 0; cc < BC; ++cc) {
                 const float w = es[cc][rl];
 #pragma unroll
-                for (int m = 0; m < NV; ++m) s[m] += w * buf[cc * (DK / 4) + j + 16 * m];
+                for (int m = 0; m < NV; ++m) s[m] += w * bufA[cc * (DK / 4) + j + 16 * m];
             }
         }
     }

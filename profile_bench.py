@@ -46,11 +46,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 OUT = os.path.join(ROOT, "profile_out")  # raw profiler output; set by --out
 PROFILES = os.path.join(ROOT, "profiles")
 # more specific names first: a kernel is keyed by the first entry its name contains
-KERNELS = ("conv_silu_kernel", "conv_decode_kernel", "chain_kernel", "intra_kernel", "output_kernel", "decode_kernel",
-           "chunk_table_kernel")
+KERNELS = ("bwd_chain_kernel", "bwd_local_kernel", "bwd_grad_kernel", "bwd_table_kernel", "conv_silu_kernel",
+           "conv_decode_kernel", "chain_kernel", "intra_kernel", "output_kernel", "decode_kernel", "chunk_table_kernel")
 COPY_BYTES = 1 << 30
 BENCH_TRACE = ["bench.py", "--steps", "5", "--warmup", "2", "--decode-steps", "32", "--no-cpu-baseline", "--no-other"]
-BENCH_PMC = ["bench.py", "--steps", "1", "--warmup", "1", "--decode-steps", "4", "--no-cpu-baseline", "--no-other"]
+BENCH_PMC = ["bench.py", "--steps", "1", "--warmup", "1", "--decode-steps", "4", "--no-cpu-baseline", "--no-other",
+             "--no-backward"]
 
 
 def log(*a):
@@ -132,7 +133,7 @@ def render_trace():
         for r in csv.DictReader(f):
             rows.append((r["Name"], int(r["Calls"]), float(r["AverageNs"]), float(r["MinNs"]), float(r["MaxNs"]),
                          float(r["Percentage"])))
-    lines = ["# Kernel trace: 64K-token prefill (H=6, d=256, bf16), batched decode, front end", "",
+    lines = ["# Kernel trace: 64K-token prefill (H=6, d=256, bf16), batched decode, front end, prefill backward", "",
              "Command (repository root, one MI355X):", "", "```", cmd, "```", "",
              "| kernel | calls | avg us | min us | max us | % of GPU time |", "|---|---|---|---|---|---|"]
     for name, calls, avg, mn, mx, pct in rows:
@@ -147,10 +148,15 @@ def render_trace():
 
 def full_launch(name, grid, groups):
     """True for the dispatch group that covers the whole workload: the
-    non-segmented chain instance, else the largest grid of the kernel."""
+    non-segmented chain instance; for the decode kernel the d_v = 256 batch
+    (the smaller of its two grids: the bench also times a d_v = 512 batch);
+    else the largest grid of the kernel."""
     if "chain_kernel" in name:
         return ", false>" in name
-    return grid == max(g for (nm, g) in groups if kernel_key(nm) == kernel_key(name))
+    grids = [g for (nm, g) in groups if kernel_key(nm) == kernel_key(name)]
+    if kernel_key(name) == "decode_kernel":
+        return grid == min(grids)
+    return grid == max(grids)
 
 
 def counter_sums(d):
