@@ -302,8 +302,17 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a)
 //     Delta = X + ysign Y S^T                 (C x 16 rows of this workgroup)
 //     S    <- e^{gamma_L} S + zsign Delta^T Z + E^T F
 // storing S before each chunk (S_store) and Delta (D_store).  A workgroup owns
-// 16 rows of one (sequence, head) state; 16 lanes share a row, each holding
-// DK/16 columns as float4 vectors at columns 4 (j + 16 m).
+// 16 rows of one (sequence, head) state.  Both products run on the fp32
+// matrix cores (v_mfma_f32_16x16x4_f32: exact fp32 products, fp32 sums):
+//   - S Y^T (16 x 64, K = DK): wave w computes the 16 chunk rows 16w..16w+15;
+//     A = S (from LDS), B = Y^T (from LDS);
+//   - Delta^T Z + E^T F (16 x DK, K = 64): wave w owns the DK/4 state columns
+//     w DK/4 .. and keeps them in registers in the accumulator layout
+//     (lane l: rows 4 (l / 16) + i, column l % 16 of each 16-column tile);
+//     A = Delta^T (from LDS) and E^T (registers), B = Z and F (from LDS).
+// Operands pass through registers into two LDS buffers (row pitch DK + 4):
+// each thread loads its share of a whole 64 x DK operand at once, and the
+// next operand is in flight during the arithmetic on the current one.
 template <int DK>
 __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs a, const float* __restrict__ X, size_t off_X,
                                                         size_t off_Y, float ysign, size_t off_Z, float zsign,
@@ -311,14 +320,15 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs a, const float* 
                                                         float* __restrict__ S_final, size_t off_Sst, size_t off_Dst,
                                                         int reverse)
 {
-    constexpr int NV = DK / 64;
+    constexpr int PER = BC * DK / 4 / 256;  // float4 of one operand per thread
+    constexpr int P = DK + 4;               // LDS row pitch (floats)
+    constexpr int NT = DK / 64;             // 16-column tiles per wave
     const int dv = a.dv, H = a.H;
     const int rblocks = dv / 16;
     const int64_t pair = blockIdx.x / rblocks;
     const int rb = (int)(blockIdx.x % rblocks);
     const int n = (int)(pair / H), h = (int)(pair % H);
-    const int t = threadIdx.x, rl = t >> 4, j = t & 15;
-    const int row = rb * 16 + rl;
+    const int t = threadIdx.x, w = t >> 6, l = t & 63, r16 = l & 15, g = l >> 4;
     const int32_t* seq_first = reinterpret_cast<const int32_t*>(a.ws + a.lay.off_seq_first);
     const float* gamv = reinterpret_cast<const float*>(a.ws + a.lay.off_gam);
     auto wsf = [&](size_t off) { return reinterpret_cast<float*>(a.ws + off); };
@@ -329,42 +339,41 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs a, const float* 
     const float* Fb = off_F ? wsf(off_F) : nullptr;
     float* Sst = wsf(off_Sst);
     float* Dst = wsf(off_Dst);
-    // Operands pass through registers into two LDS buffers: each thread loads
-    // its share of a whole 64 x DK operand at once (PER vector loads in
-    // flight), and the loads of the next operand are issued before the
-    // arithmetic on the current one (Z during Y S^T, F or the next chunk's Y
-    // during the update).
-    constexpr int PER = BC * DK / 4 / 256;
-    __shared__ f32x4 bufA[BC * DK / 4], bufB[BC * DK / 4];
-    __shared__ float xs[BC][16], es[BC][16], dsm[BC][16];
+    __shared__ __align__(16) float bufA[BC * P], bufB[BC * P];
+    __shared__ float Ssh[16 * P];
+    __shared__ float dsm[BC * 17];
+
     f32x4 reg[PER];
     auto fetch = [&](const float* base, int64_t chx) {
         const f32x4* p4 = reinterpret_cast<const f32x4*>(base + chx * BC * DK);
 #pragma unroll
         for (int i = 0; i < PER; ++i) reg[i] = p4[t + 256 * i];
     };
-    auto put = [&](f32x4* dst) {
+    auto put = [&](float* dst) {
 #pragma unroll
-        for (int i = 0; i < PER; ++i) dst[t + 256 * i] = reg[i];
+        for (int i = 0; i < PER; ++i) {
+            const int e = t + 256 * i;
+            *reinterpret_cast<f32x4*>(dst + (e / (DK / 4)) * P + 4 * (e % (DK / 4))) = reg[i];
+        }
     };
-    // the chunk's X and E columns of this workgroup's rows, and its decay, fetched with Y
-    float xr[BC * 16 / 256], er[BC * 16 / 256], gl = 0.f;
+    // the chunk's X at this lane's Delta positions, E at its A-operand positions, and the decay
+    float xr[4], er[16], gl = 0.f;
     auto fetch_small = [&](int64_t chx) {
 #pragma unroll
-        for (int i = 0; i < BC * 16 / 256; ++i) {
-            const int e = t + 256 * i;
-            const int64_t gi = (chx * BC + (e >> 4)) * dv + rb * 16 + (e & 15);
-            xr[i] = Xb[gi];
-            er[i] = Eb ? Eb[gi] : 0.f;
-        }
+        for (int i = 0; i < 4; ++i) xr[i] = Xb[(chx * BC + 16 * w + r16) * dv + rb * 16 + 4 * g + i];
+#pragma unroll
+        for (int s4 = 0; s4 < 16; ++s4) er[s4] = Eb ? Eb[(chx * BC + 4 * s4 + g) * dv + rb * 16 + r16] : 0.f;
         gl = gamv[chx * BC + BC - 1];
     };
 
-    f32x4 s[NV];
-    const int64_t srow = ((int64_t)(n * H + h) * dv + row) * DK;
+    // this wave's state columns, accumulator layout
+    f32x4 sreg[NT];
+    const int64_t sbase = (int64_t)(n * H + h) * dv + rb * 16;
 #pragma unroll
-    for (int m = 0; m < NV; ++m)
-        s[m] = S_init ? *reinterpret_cast<const f32x4*>(S_init + srow + 4 * (j + 16 * m)) : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            sreg[tt][i] = S_init ? S_init[(sbase + 4 * g + i) * DK + w * (DK / 4) + 16 * tt + r16] : 0.f;
     const int c0 = seq_first[n], c1 = seq_first[n + 1];
     const int steps = c1 - c0;
     auto chunk_of = [&](int it) -> int64_t { return (int64_t)(reverse ? c1 - 1 - it : c0 + it) * H + h; };
@@ -375,35 +384,34 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs a, const float* 
     for (int it = 0; it < steps; ++it) {
         const int64_t ch = chunk_of(it);
         const float decay = expf(gl);
-        const int64_t srec = (ch * dv + row) * DK;
+        float xc[4];
 #pragma unroll
-        for (int m = 0; m < NV; ++m) *reinterpret_cast<f32x4*>(Sst + srec + 4 * (j + 16 * m)) = s[m];
-        __syncthreads();  // the previous step's readers of bufA, bufB, xs, es, dsm are done
+        for (int i = 0; i < 4; ++i) xc[i] = xr[i];
+        float ec[16];
+#pragma unroll
+        for (int s4 = 0; s4 < 16; ++s4) ec[s4] = er[s4];
+        // the state before the chunk: to the record and to LDS (A operand of S Y^T)
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 4 * g + i, col = w * (DK / 4) + 16 * tt + r16;
+                Sst[(ch * dv + rb * 16 + row) * DK + col] = sreg[tt][i];
+                Ssh[row * P + col] = sreg[tt][i];
+            }
+        __syncthreads();  // Ssh written; the previous step's readers of bufA, bufB, dsm are done
         put(bufA);        // Y
-#pragma unroll
-        for (int i = 0; i < BC * 16 / 256; ++i) {
-            const int e = t + 256 * i;
-            xs[e >> 4][e & 15] = xr[i];
-            es[e >> 4][e & 15] = er[i];
-        }
         fetch(Zb, ch);
         __syncthreads();
-        float p[BC];
+        // (S Y^T)[row][16 w + n]: A(m, k) = S[m][k], B(k, n) = Y[16 w + n][k]
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+        for (int s4 = 0; s4 < DK / 4; ++s4)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(Ssh[r16 * P + 4 * s4 + g], bufA[(16 * w + r16) * P + 4 * s4 + g],
+                                                       acc, 0, 0, 0);
+        // lane holds rows 4 g + i of chunk row 16 w + r16
 #pragma unroll
-        for (int cc = 0; cc < BC; ++cc) {
-            float x = 0.f;
-#pragma unroll
-            for (int m = 0; m < NV; ++m) {
-                const f32x4 y = bufA[cc * (DK / 4) + j + 16 * m];
-                x += y.x * s[m].x + y.y * s[m].y + y.z * s[m].z + y.w * s[m].w;
-            }
-            p[cc] = x;
-        }
-#pragma unroll
-        for (int cc = 0; cc < BC; ++cc) p[cc] = xs[cc][rl] + ysign * group_sum<16>(p[cc]);
-        if (j == 0)
-#pragma unroll
-            for (int cc = 0; cc < BC; ++cc) dsm[cc][rl] = p[cc];
+        for (int i = 0; i < 4; ++i) dsm[(16 * w + r16) * 17 + 4 * g + i] = xc[i] + ysign * acc[i];
         put(bufB);  // Z
         if (Fb) {
             fetch(Fb, ch);
@@ -411,18 +419,21 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs a, const float* 
             fetch(Yb, chunk_of(it + 1));
             fetch_small(chunk_of(it + 1));
         }
-        __syncthreads();  // bufB and dsm complete; bufA (Y) no longer read
+        __syncthreads();  // dsm and bufB complete; bufA (Y) and Ssh no longer read
         for (int e = t; e < BC * 16; e += 256) {
             const int cc = e >> 4, rr = e & 15;
-            Dst[(ch * BC + cc) * dv + rb * 16 + rr] = dsm[cc][rr];
+            Dst[(ch * BC + cc) * dv + rb * 16 + rr] = dsm[cc * 17 + rr];
         }
+        // S <- decay S + zsign Delta^T Z: A(m, k) = Delta[k][m], B(k, n) = Z[k][col n]
 #pragma unroll
-        for (int m = 0; m < NV; ++m) s[m] *= decay;
+        for (int tt = 0; tt < NT; ++tt) {
+            f32x4 sacc = sreg[tt] * decay;
+            const int col = w * (DK / 4) + 16 * tt + r16;
 #pragma unroll
-        for (int cc = 0; cc < BC; ++cc) {
-            const float w = zsign * p[cc];
-#pragma unroll
-            for (int m = 0; m < NV; ++m) s[m] += w * bufB[cc * (DK / 4) + j + 16 * m];
+            for (int s4 = 0; s4 < 16; ++s4)
+                sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(zsign * dsm[(4 * s4 + g) * 17 + r16],
+                                                            bufB[(4 * s4 + g) * P + col], sacc, 0, 0, 0);
+            sreg[tt] = sacc;
         }
         if (Fb) {
             put(bufA);  // F
@@ -431,17 +442,24 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs a, const float* 
                 fetch_small(chunk_of(it + 1));
             }
             __syncthreads();
+            // S += E^T F: A(m, k) = E[k][m], B(k, n) = F[k][col n]
 #pragma unroll
-            for (int cc = 0; cc < BC; ++cc) {
-                const float w = es[cc][rl];
+            for (int tt = 0; tt < NT; ++tt) {
+                f32x4 sacc = sreg[tt];
+                const int col = w * (DK / 4) + 16 * tt + r16;
 #pragma unroll
-                for (int m = 0; m < NV; ++m) s[m] += w * bufA[cc * (DK / 4) + j + 16 * m];
+                for (int s4 = 0; s4 < 16; ++s4)
+                    sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(ec[s4], bufA[(4 * s4 + g) * P + col], sacc, 0, 0, 0);
+                sreg[tt] = sacc;
             }
         }
     }
     if (S_final)
 #pragma unroll
-        for (int m = 0; m < NV; ++m) *reinterpret_cast<f32x4*>(S_final + srow + 4 * (j + 16 * m)) = s[m];
+        for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                S_final[(sbase + 4 * g + i) * DK + w * (DK / 4) + 16 * tt + r16] = sreg[tt][i];
 }
 
 __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a)
