@@ -48,7 +48,7 @@ if ROOT not in sys.path:
 METRIC = "GDN prefill tokens/s (H=6,d=256,T=64K) + decode state GB/s; % of roofline"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
-PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
+PEAK_F32_TFLOPS = 157.3     # MI355X dense fp32 (matrix cores; the vector rate is the same)
 
 T, H, DK, DV, C = 65536, 6, 256, 256, 64
 DEC_N = 256
@@ -586,8 +586,8 @@ def main():
             "ms_per_step": bwd_ms,
             "tokens_per_s": T / (bwd_ms / 1e3),
             "algorithmic_flops_per_token": flops_backward_per_token(),
-            "roofline": {"kernel": "whole backward (fp32 on the vector ALUs)", "bound": "alu", "achieved": tf,
-                         "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s", "frac": tf / PEAK_F32_TFLOPS},
+            "roofline": {"kernel": "whole backward (fp32 contractions on the fp32 matrix cores)", "bound": "mfma",
+                         "achieved": tf, "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s", "frac": tf / PEAK_F32_TFLOPS},
         }
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(pre["inputs"])

@@ -46,39 +46,58 @@ namespace {
 
 constexpr int BC = 64;  // chunk length of the backward
 constexpr int LD = 68;  // LDS row pitch of the tile routine (floats)
+constexpr int KT = 16;  // k extent of one LDS block of the tile routine (64 measured slower: fewer resident workgroups)
 
-// acc[i][j] += sum_k A(r, k) B(k, n) for r = 4 tr + i in [0, 64), n = n0 + 4 tc + j,
-// with A(r, k) = A[r * ars + k * acs] * (kscale ? kscale[k] : 1) and
-// B(k, n) = B[k * brs + n * bcs]; K a multiple of 16, [n0, n0 + 64) inside B.
-// All 256 threads take part (two barriers per 16-wide k step).
+// acc[i][j] += sum_k A(r, k) B(k, n) for r = 4 tr + i in [0, 64), n = n0 + 16 j + tc
+// (tr = threadIdx / 16, tc = threadIdx % 16), with
+// A(r, k) = A[r * ars + k * acs] * (kscale ? kscale[k] : 1) and
+// B(k, n) = B[k * brs + n * bcs]; K a multiple of KT = 16, [n0, n0 + 64)
+// inside B.  All 256 threads take part (two barriers per KT-wide k block; as
+// and bs hold KT x LD floats each).  The products
+// run on the fp32 matrix cores (v_mfma_f32_16x16x4_f32, exact fp32 products
+// and fp32 sums): wave w computes rows 16 w .. 16 w + 15 as four 16 x 16
+// tiles, and its accumulator layout (lane l: rows 4 (l / 16) + i, column
+// l % 16 of each tile) is the (r, n) map above.
 __device__ void mm64(float acc[4][4], const float* __restrict__ A, int ars, int acs, const float* kscale,
                      const float* __restrict__ B, int brs, int bcs, int K, int n0, float* as, float* bs)
 {
     const int t = threadIdx.x;
-    const int tr = t >> 4, tc = t & 15;
-    for (int k0 = 0; k0 < K; k0 += 16) {
+    const int w = t >> 6, l = t & 63, r16 = l & 15, g = l >> 4;
+    f32x4 d[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 4; ++j) d[j] = f32x4{acc[0][j], acc[1][j], acc[2][j], acc[3][j]};
+    for (int k0 = 0; k0 < K; k0 += KT) {
+        // the 64 x KT block of A and the KT x 64 block of B: all loads in flight, then to LDS
+        float xa[KT / 4], xb[KT / 4];
+#pragma unroll
+        for (int i = 0; i < KT / 4; ++i) {
             const int e = t + 256 * i;
-            const int r = e >> 4, kk = e & 15;
-            float x = A[(int64_t)r * ars + (int64_t)(k0 + kk) * acs];
-            if (kscale) x *= kscale[k0 + kk];
-            as[kk * LD + r] = x;
+            const int r = e / KT, kk = e % KT;
+            xa[i] = A[(int64_t)r * ars + (int64_t)(k0 + kk) * acs];
+            if (kscale) xa[i] *= kscale[k0 + kk];
             const int kb = e >> 6, n = e & 63;
-            bs[kb * LD + n] = B[(int64_t)(k0 + kb) * brs + (int64_t)(n0 + n) * bcs];
+            xb[i] = B[(int64_t)(k0 + kb) * brs + (int64_t)(n0 + n) * bcs];
+        }
+#pragma unroll
+        for (int i = 0; i < KT / 4; ++i) {
+            const int e = t + 256 * i;
+            as[(e % KT) * LD + e / KT] = xa[i];
+            bs[(e >> 6) * LD + (e & 63)] = xb[i];
         }
         __syncthreads();
-#pragma unroll 4
-        for (int kk = 0; kk < 16; ++kk) {
-            const f32x4 a = *reinterpret_cast<const f32x4*>(as + kk * LD + 4 * tr);
-            const f32x4 b = *reinterpret_cast<const f32x4*>(bs + kk * LD + 4 * tc);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+        for (int kq = 0; kq < KT / 4; ++kq) {
+            const float av = as[(4 * kq + g) * LD + 16 * w + r16];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] += a[i] * b[j];
+            for (int j = 0; j < 4; ++j)
+                d[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bs[(4 * kq + g) * LD + 16 * j + r16], d[j], 0, 0, 0);
         }
         __syncthreads();
     }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i][j] = d[j][i];
 }
 
 __device__ __forceinline__ void zero(float acc[4][4])
@@ -174,7 +193,7 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a)
     const int tok0 = tab[4 * c], len = tab[4 * c + 1];
     const int dk = a.dk, dv = a.dv, H = a.H;
     Slices s = slices(a, b);
-    __shared__ __align__(16) float as[16 * LD], bs[16 * LD];
+    __shared__ __align__(16) float as[KT * LD], bs[KT * LD];
     __shared__ float gam[BC], bet[BC], bge[BC], dd[BC], eg[BC];
     __shared__ float Am[BC][BC + 1], Ts[BC][BC + 1];
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
@@ -240,7 +259,7 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a)
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int r = 4 * tr + i, n = 4 * tc + j;
+            const int r = 4 * tr + i, n = 16 * j + tc;
             const float x = n < r ? acc[i][j] * expf(gam[r] - gam[n]) : 0.f;
             s.KKG[r * BC + n] = x;
             Am[r][n] = bet[r] * x;
@@ -252,7 +271,7 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a)
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int r = 4 * tr + i, n = 4 * tc + j;
+            const int r = 4 * tr + i, n = 16 * j + tc;
             s.P[r * BC + n] = n <= r ? acc[i][j] * expf(gam[r] - gam[n]) : 0.f;
         }
     __syncthreads();
@@ -275,7 +294,7 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a)
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int r = 4 * tr + i, n = n0 + 4 * tc + j;
+                const int r = 4 * tr + i, n = n0 + 16 * j + tc;
                 s.W[r * dk + n] = acc[i][j];
                 s.DK[r * dk + n] = dd[r] * s.K[r * dk + n];
             }
@@ -290,7 +309,7 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a)
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int r = 4 * tr + i, n = n0 + 4 * tc + j;
+                const int r = 4 * tr + i, n = n0 + 16 * j + tc;
                 s.U[r * dv + n] = acc[i][j];
                 s.E[r * dv + n] = a.scale * eg[r] * s.dO[r * dv + n];
                 s.dDl[r * dv + n] = a.scale * acc2[i][j];
@@ -474,7 +493,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a)
     const int dk = a.dk, dv = a.dv, H = a.H;
     const float scale = a.scale;
     Slices s = slices(a, b);
-    __shared__ __align__(16) float as[16 * LD], bs[16 * LD];
+    __shared__ __align__(16) float as[KT * LD], bs[KT * LD];
     __shared__ float gam[BC], bet[BC], eg[BC], dd[BC], bge[BC], dgam[BC], dbet[BC];
     __shared__ float red[4];
     __shared__ float cs[16][BC];
@@ -508,7 +527,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a)
     };
     auto col_sub = [&](float* dst, const float colp[4]) {  // dst[n] -= column n summed over all rows
 #pragma unroll
-        for (int j = 0; j < 4; ++j) cs[tr][4 * tc + j] = colp[j];
+        for (int j = 0; j < 4; ++j) cs[tr][16 * j + tc] = colp[j];
         __syncthreads();
         if (t < BC) {
             float x = 0.f;
@@ -527,7 +546,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a)
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int r = 4 * tr + i, n = n0 + 4 * tc + j;
+                const int r = 4 * tr + i, n = n0 + 16 * j + tc;
                 const float x = scale * eg[r] * acc[i][j];
                 s.dQ[r * dk + n] = x;
                 rowp[i] += s.Q[r * dk + n] * x;
@@ -543,7 +562,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a)
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int r = 4 * tr + i, n = n0 + 4 * tc + j;
+                const int r = 4 * tr + i, n = n0 + 16 * j + tc;
                 s.dK[r * dk + n] = dd[r] * acc[i][j];
                 rowp[i] += s.K[r * dk + n] * acc[i][j];
             }
@@ -583,7 +602,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a)
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int r = 4 * tr + i, n = 4 * tc + j;
+                const int r = 4 * tr + i, n = 16 * j + tc;
                 const float dp = n <= r ? scale * acc[i][j] : 0.f;
                 const float m = dp * s.P[r * BC + n];
                 rowp[i] += m;
@@ -604,7 +623,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a)
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int r = 4 * tr + i, n = n0 + 4 * tc + j;
+                const int r = 4 * tr + i, n = n0 + 16 * j + tc;
                 s.dQ[r * dk + n] += acc[i][j];
                 s.dK[r * dk + n] += acc2[i][j];
             }
@@ -616,7 +635,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) s.dW[(4 * tr + i) * dk + n0 + 4 * tc + j] = -acc[i][j];
+            for (int j = 0; j < 4; ++j) s.dW[(4 * tr + i) * dk + n0 + 16 * j + tc] = -acc[i][j];
     }
     __syncthreads();  // dW complete
     // dT = (dDelta V^T) diag(beta) + (dW K^T) diag(beta e^gamma)
@@ -630,7 +649,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a)
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int r = 4 * tr + i, n = 4 * tc + j;
+                const int r = 4 * tr + i, n = 16 * j + tc;
                 s.dT[r * BC + n] = acc[i][j] * bet[n] + acc2[i][j] * bge[n];
             }
     }
@@ -643,7 +662,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a)
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int r = 4 * tr + i, n = n0 + 4 * tc + j;
+                const int r = 4 * tr + i, n = n0 + 16 * j + tc;
                 rowp[i] += acc[i][j] * s.V[r * dv + n];
                 if (r < len) a.dv_out[((int64_t)(tok0 + r) * H + h) * dv + n] = bet[r] * acc[i][j];
             }
@@ -658,7 +677,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a)
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int r = 4 * tr + i, n = n0 + 4 * tc + j;
+                const int r = 4 * tr + i, n = n0 + 16 * j + tc;
                 s.dK[r * dk + n] += bge[r] * acc[i][j];
                 rowp[i] += acc[i][j] * s.K[r * dk + n];
             }
@@ -679,7 +698,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) s.X1[(4 * tr + i) * BC + 4 * tc + j] = acc[i][j];
+        for (int j = 0; j < 4; ++j) s.X1[(4 * tr + i) * BC + 16 * j + tc] = acc[i][j];
     __syncthreads();
     // dA = -strict_lower(T^T X1);  Bd = diag(beta) (dA o Gamma);  dbeta, dgamma from A
     zero(acc);
@@ -692,7 +711,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a)
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int r = 4 * tr + i, n = 4 * tc + j;
+                const int r = 4 * tr + i, n = 16 * j + tc;
                 const float da = n < r ? -acc[i][j] : 0.f;
                 const float kkg = s.KKG[r * BC + n];  // zero unless n < r
                 const float m = da * bet[r] * kkg;  // dA o A
@@ -715,7 +734,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) s.dK[(4 * tr + i) * dk + n0 + 4 * tc + j] += acc[i][j];
+            for (int j = 0; j < 4; ++j) s.dK[(4 * tr + i) * dk + n0 + 16 * j + tc] += acc[i][j];
     }
     __syncthreads();  // dQ, dK, dgam, dbet complete
     // dg: reverse cumulative sum of dgamma (gamma_L is the last, padded-constant, entry)
