@@ -83,3 +83,37 @@ def test_no_tokens():
     got = gdn.chunk_prefill_backward(q, q, v, g, g, v, dstate=ds)
     torch.cuda.synchronize()
     assert torch.equal(got["dinit"], ds)
+
+
+def test_backward_in_a_hip_graph_matches_eager():
+    """The backward captured once in a HIP graph (device cu_seqlens, caller's
+    workspace): every replay, with eager work and synchronisations between
+    replays, equals the eager call bit for bit (the kernels use no atomics and
+    a fixed reduction order)."""
+    T, H, dk, dv, seed = 330, 2, 64, 128, 21
+    cu = [0, 37, 37, 200, 330]
+    inp = synth.prefill_inputs(T, H, dk, dv, "bf16", seed=seed, cu_seqlens=cu, init_state_std=0.2)
+    do, ds = synth.backward_cotangents(T, H, dk, dv, len(cu) - 1, "bf16", seed)
+    t = lambda a, b=False: synth.to_torch(a, DEV, bf16=b)
+    args = (t(inp.q, True), t(inp.k, True), t(inp.v, True), t(inp.g), t(inp.beta), t(do, True))
+    kw = dict(init_state=t(inp.init_state), dstate=t(ds), cu_seqlens=torch.tensor(cu, dtype=torch.int32, device=DEV))
+    ws = torch.empty(gdn.prefill_backward_workspace_size(T, len(cu) - 1, H, dk, dv), dtype=torch.uint8, device=DEV)
+    ref = {k: (None if v is None else v.clone()) for k, v in gdn.chunk_prefill_backward(*args, workspace=ws,
+                                                                                          **kw).items()}
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream(device=DEV)
+    side.wait_stream(torch.cuda.current_stream(DEV))
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            got = gdn.chunk_prefill_backward(*args, workspace=ws, **kw)
+    torch.cuda.current_stream(DEV).wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for v in got.values():
+            v.zero_()                           # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name in NAMES:
+            assert torch.equal(got[name], ref[name]), (rep, name)
