@@ -45,19 +45,23 @@ namespace gdn {
 namespace {
 
 constexpr int BC = 64;  // chunk length of the backward
-constexpr int LD = 68;  // LDS row pitch of the tile routine (floats)
-constexpr int KT = 16;  // k extent of one LDS block of the tile routine (64 measured slower: fewer resident workgroups)
+constexpr int LD = 68;   // LDS row pitch of the tile routine (floats)
+constexpr int KTL = 16;  // its k block in the local kernel
+constexpr int KTG = 32;  // and in the gradient kernel
 
 // acc[i][j] += sum_k A(r, k) B(k, n) for r = 4 tr + i in [0, 64), n = n0 + 16 j + tc
 // (tr = threadIdx / 16, tc = threadIdx % 16), with
 // A(r, k) = A[r * ars + k * acs] * (kscale ? kscale[k] : 1) and
-// B(k, n) = B[k * brs + n * bcs]; K a multiple of KT = 16, [n0, n0 + 64)
+// B(k, n) = B[k * brs + n * bcs]; K a multiple of the k block KT, [n0, n0 + 64)
 // inside B.  All 256 threads take part (two barriers per KT-wide k block; as
-// and bs hold KT x LD floats each).  The products
+// and bs hold KT x LD floats each).  A wider block keeps more loads in flight
+// but needs more registers: 32 measured best for the gradient kernel, 16 for
+// the local one (64 left one workgroup per CU and was slower in both).  The products
 // run on the fp32 matrix cores (v_mfma_f32_16x16x4_f32, exact fp32 products
 // and fp32 sums): wave w computes rows 16 w .. 16 w + 15 as four 16 x 16
 // tiles, and its accumulator layout (lane l: rows 4 (l / 16) + i, column
 // l % 16 of each tile) is the (r, n) map above.
+template <int KT>
 __device__ void mm64(float acc[4][4], const float* __restrict__ A, int ars, int acs, const float* kscale,
                      const float* __restrict__ B, int brs, int bcs, int K, int n0, float* as, float* bs)
 {
@@ -193,7 +197,7 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a)
     const int tok0 = tab[4 * c], len = tab[4 * c + 1];
     const int dk = a.dk, dv = a.dv, H = a.H;
     Slices s = slices(a, b);
-    __shared__ __align__(16) float as[KT * LD], bs[KT * LD];
+    __shared__ __align__(16) float as[KTL * LD], bs[KTL * LD];
     __shared__ float gam[BC], bet[BC], bge[BC], dd[BC], eg[BC];
     __shared__ float Am[BC][BC + 1], Ts[BC][BC + 1];
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
@@ -254,7 +258,7 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a)
     float acc[4][4];
     // K K^T -> KKG = strict_lower(K K^T o Gamma), A = diag(beta) KKG
     zero(acc);
-    mm64(acc, s.K, dk, 1, nullptr, s.K, 1, dk, dk, 0, as, bs);
+    mm64<KTL>(acc, s.K, dk, 1, nullptr, s.K, 1, dk, dk, 0, as, bs);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -266,7 +270,7 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a)
         }
     // Q K^T -> P = lower(Q K^T o Gamma)
     zero(acc);
-    mm64(acc, s.Q, dk, 1, nullptr, s.K, 1, dk, dk, 0, as, bs);
+    mm64<KTL>(acc, s.Q, dk, 1, nullptr, s.K, 1, dk, dk, 0, as, bs);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -289,7 +293,7 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a)
     // W = T diag(beta e^gamma) K,  D K,  then U = T diag(beta) V,  E = scale e^gamma dO
     for (int n0 = 0; n0 < dk; n0 += 64) {
         zero(acc);
-        mm64(acc, s.T, BC, 1, bge, s.K, dk, 1, BC, n0, as, bs);
+        mm64<KTL>(acc, s.T, BC, 1, bge, s.K, dk, 1, BC, n0, as, bs);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -301,10 +305,10 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a)
     }
     for (int n0 = 0; n0 < dv; n0 += 64) {
         zero(acc);
-        mm64(acc, s.T, BC, 1, bet, s.V, dv, 1, BC, n0, as, bs);
+        mm64<KTL>(acc, s.T, BC, 1, bet, s.V, dv, 1, BC, n0, as, bs);
         float acc2[4][4];
         zero(acc2);
-        mm64(acc2, s.P, 1, BC, nullptr, s.dO, dv, 1, BC, n0, as, bs);  // P^T dO
+        mm64<KTL>(acc2, s.P, 1, BC, nullptr, s.dO, dv, 1, BC, n0, as, bs);  // P^T dO
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -493,7 +497,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a)
     const int dk = a.dk, dv = a.dv, H = a.H;
     const float scale = a.scale;
     Slices s = slices(a, b);
-    __shared__ __align__(16) float as[KT * LD], bs[KT * LD];
+    __shared__ __align__(16) float as[KTG * LD], bs[KTG * LD];
     __shared__ float gam[BC], bet[BC], eg[BC], dd[BC], bge[BC], dgam[BC], dbet[BC];
     __shared__ float red[4];
     __shared__ float cs[16][BC];
@@ -541,7 +545,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a)
     rowp[0] = rowp[1] = rowp[2] = rowp[3] = 0.f;
     for (int n0 = 0; n0 < dk; n0 += 64) {
         zero(acc);
-        mm64(acc, s.dO, dv, 1, nullptr, s.S, dk, 1, dv, n0, as, bs);
+        mm64<KTG>(acc, s.dO, dv, 1, nullptr, s.S, dk, 1, dv, n0, as, bs);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -557,7 +561,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a)
     rowp[0] = rowp[1] = rowp[2] = rowp[3] = 0.f;
     for (int n0 = 0; n0 < dk; n0 += 64) {
         zero(acc);
-        mm64(acc, s.Dl, dv, 1, nullptr, s.dS, dk, 1, dv, n0, as, bs);
+        mm64<KTG>(acc, s.Dl, dv, 1, nullptr, s.dS, dk, 1, dv, n0, as, bs);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -594,7 +598,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a)
     __syncthreads();
     // dP = scale lower(dO Delta^T);  dgamma from P;  dPG = dP o Gamma
     zero(acc);
-    mm64(acc, s.dO, dv, 1, nullptr, s.Dl, 1, dv, dv, 0, as, bs);
+    mm64<KTG>(acc, s.dO, dv, 1, nullptr, s.Dl, 1, dv, dv, 0, as, bs);
     {
         float colp[4] = {0.f, 0.f, 0.f, 0.f};
         rowp[0] = rowp[1] = rowp[2] = rowp[3] = 0.f;
@@ -615,10 +619,10 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a)
     // dQ += dPG K;  dK += dPG^T Q
     for (int n0 = 0; n0 < dk; n0 += 64) {
         zero(acc);
-        mm64(acc, s.dPG, BC, 1, nullptr, s.K, dk, 1, BC, n0, as, bs);
+        mm64<KTG>(acc, s.dPG, BC, 1, nullptr, s.K, dk, 1, BC, n0, as, bs);
         float acc2[4][4];
         zero(acc2);
-        mm64(acc2, s.dPG, 1, BC, nullptr, s.Q, dk, 1, BC, n0, as, bs);
+        mm64<KTG>(acc2, s.dPG, 1, BC, nullptr, s.Q, dk, 1, BC, n0, as, bs);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -631,7 +635,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a)
     // dW = -(dDelta S)
     for (int n0 = 0; n0 < dk; n0 += 64) {
         zero(acc);
-        mm64(acc, s.dD, dv, 1, nullptr, s.S, dk, 1, dv, n0, as, bs);
+        mm64<KTG>(acc, s.dD, dv, 1, nullptr, s.S, dk, 1, dv, n0, as, bs);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -641,10 +645,10 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a)
     // dT = (dDelta V^T) diag(beta) + (dW K^T) diag(beta e^gamma)
     {
         zero(acc);
-        mm64(acc, s.dD, dv, 1, nullptr, s.V, 1, dv, dv, 0, as, bs);
+        mm64<KTG>(acc, s.dD, dv, 1, nullptr, s.V, 1, dv, dv, 0, as, bs);
         float acc2[4][4];
         zero(acc2);
-        mm64(acc2, s.dW, dk, 1, nullptr, s.K, 1, dk, dk, 0, as, bs);
+        mm64<KTG>(acc2, s.dW, dk, 1, nullptr, s.K, 1, dk, dk, 0, as, bs);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -657,7 +661,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a)
     rowp[0] = rowp[1] = rowp[2] = rowp[3] = 0.f;
     for (int n0 = 0; n0 < dv; n0 += 64) {
         zero(acc);
-        mm64(acc, s.T, 1, BC, nullptr, s.dD, dv, 1, BC, n0, as, bs);
+        mm64<KTG>(acc, s.T, 1, BC, nullptr, s.dD, dv, 1, BC, n0, as, bs);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -672,7 +676,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a)
     rowp[0] = rowp[1] = rowp[2] = rowp[3] = 0.f;
     for (int n0 = 0; n0 < dk; n0 += 64) {
         zero(acc);
-        mm64(acc, s.T, 1, BC, nullptr, s.dW, dk, 1, BC, n0, as, bs);
+        mm64<KTG>(acc, s.T, 1, BC, nullptr, s.dW, dk, 1, BC, n0, as, bs);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -694,7 +698,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a)
     __syncthreads();  // dT complete
     // X1 = dT T^T
     zero(acc);
-    mm64(acc, s.dT, BC, 1, nullptr, s.T, 1, BC, BC, 0, as, bs);
+    mm64<KTG>(acc, s.dT, BC, 1, nullptr, s.T, 1, BC, BC, 0, as, bs);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -702,7 +706,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a)
     __syncthreads();
     // dA = -strict_lower(T^T X1);  Bd = diag(beta) (dA o Gamma);  dbeta, dgamma from A
     zero(acc);
-    mm64(acc, s.T, 1, BC, nullptr, s.X1, BC, 1, BC, 0, as, bs);
+    mm64<KTG>(acc, s.T, 1, BC, nullptr, s.X1, BC, 1, BC, 0, as, bs);
     {
         float colp[4] = {0.f, 0.f, 0.f, 0.f};
         float rowb[4] = {0.f, 0.f, 0.f, 0.f};
@@ -729,8 +733,8 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a)
     // dK += Bd K + Bd^T K
     for (int n0 = 0; n0 < dk; n0 += 64) {
         zero(acc);
-        mm64(acc, s.Bd, BC, 1, nullptr, s.K, dk, 1, BC, n0, as, bs);
-        mm64(acc, s.Bd, 1, BC, nullptr, s.K, dk, 1, BC, n0, as, bs);
+        mm64<KTG>(acc, s.Bd, BC, 1, nullptr, s.K, dk, 1, BC, n0, as, bs);
+        mm64<KTG>(acc, s.Bd, 1, BC, nullptr, s.K, dk, 1, BC, n0, as, bs);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
