@@ -73,6 +73,21 @@ def test_exact_chunk_multiple_no_state():
     _run(256, 3, 64, 256, "bf16", seed=16, dstate_std=None)
 
 
+def test_many_short_sequences_with_empty_ones():
+    """40 packed sequences of 0 to 100 tokens (several empty, several of one
+    token), d = 128: every sequence's chain starts and ends at its own chunks."""
+    rng = np.random.default_rng(40)
+    lens = rng.integers(0, 101, size=40)
+    lens[[3, 17, 30]] = 0
+    lens[[5, 22]] = 1
+    cu = np.concatenate([[0], np.cumsum(lens)]).tolist()
+    _run(int(cu[-1]), 2, 128, 128, "bf16", seed=17, cu=cu, init_std=0.2)
+
+
+def test_single_token():
+    _run(1, 3, 64, 64, "f32", seed=18, init_std=0.5)
+
+
 def test_no_tokens():
     """Zero tokens: the initial-state gradient is the final-state cotangent."""
     H, dk, dv = 2, 64, 64
@@ -117,3 +132,31 @@ def test_backward_in_a_hip_graph_matches_eager():
         torch.cuda.synchronize()
         for name in NAMES:
             assert torch.equal(got[name], ref[name]), (rep, name)
+
+
+def test_backward_64k_last_two_chunks_of_every_head():
+    """The 64K-token workload the bench times (B=1, H=6, d=256, bf16), in the
+    same call.  The gradients of a token depend only on the state before it
+    and on the cotangents from it on, so the oracle evaluates the last 128
+    tokens exactly: the fp64 forward over the first T - 128 tokens gives the
+    state, then the reverse sweep over the last 128 (with the final-state
+    cotangent).  This checks the GPU's forward chain over 1022 chunks and its
+    reverse chain's start, at full size."""
+    T, H, d, tail = 65536, 6, 256, 128
+    seed = synth.seed_for("prefill64k")
+    inp = synth.prefill_inputs(T, H, d, d, "bf16", seed=seed)
+    do, ds = synth.backward_cotangents(T, H, d, d, 1, "bf16", seed)
+    t = lambda a, b=False: synth.to_torch(a, DEV, bf16=b)
+    print(f"  backward T={T} H={H} d={d} bf16 (bench workload), last {tail} tokens", flush=True)
+    got = gdn.chunk_prefill_backward(t(inp.q, True), t(inp.k, True), t(inp.v, True), t(inp.g), t(inp.beta),
+                                     t(do, True), dstate=t(ds), return_dinit=False)
+    torch.cuda.synchronize()
+    got = {k: v[T - tail:].cpu().numpy() for k, v in got.items() if v is not None}
+    s = T - tail
+    _, S_mid = oracle.prefill(inp.q[:s], inp.k[:s], inp.v[:s], inp.g[:s], inp.beta[:s], bf16=True, n_threads=H)
+    ref = oracle.prefill_vjp(inp.q[s:], inp.k[s:], inp.v[s:], inp.g[s:], inp.beta[s:], synth.bf16_to_f32(do[s:]),
+                             dstate=ds, init_state=S_mid, bf16=True)
+    errs = {name: rel_err(got[name], ref[name]) for name in ("dq", "dk", "dv", "dg", "dbeta")}
+    print("  " + "  ".join(f"{n} {e:.2e}" for n, e in errs.items()), flush=True)
+    for name, e in errs.items():
+        assert e <= TOL_BWD, (name, e)
