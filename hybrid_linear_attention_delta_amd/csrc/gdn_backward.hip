@@ -18,8 +18,9 @@
 //   2. bwd_local_kernel   per chunk-head: normalise and pad the chunk's rows,
 //                         form Gamma, A, T, P, W, U, D K, scale e^gamma dO and
 //                         dDelta_local = scale P^T dO into a workspace.
-//   3. bwd_chain_kernel   twice.  Forward over the chunks of each sequence: the
-//                         state entering every chunk and its Delta.  Reverse:
+//   3. bwd_chain_kernel   both directions in one launch.  Forward over the chunks
+//                         of each sequence: the state entering every chunk and
+//                         its Delta.  Reverse:
 //                         the state gradient after every chunk, from
 //                             dDelta = dDelta_local + D K dS^T
 //                             dS    <- e^{gamma_L} dS + (scale e^gamma dO)^T Q - dDelta^T W.
@@ -336,32 +337,50 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a)
 // Operands pass through registers into two LDS buffers (row pitch DK + 4):
 // each thread loads its share of a whole 64 x DK operand at once, and the
 // next operand is in flight during the arithmetic on the current one.
+// The operands of one direction of the chain (workspace byte offsets; E and
+// F absent when their offset is 0).
+struct ChainOps {
+    size_t off_X, off_Y, off_Z, off_E, off_F, off_Sst, off_Dst;
+    const float* S_init;  // [N][H][dv][dk] or NULL (zeros)
+    float* S_final;       // [N][H][dv][dk] or NULL
+    float ysign, zsign;
+    int reverse;
+};
+
+// The forward and the reverse recurrence need nothing from each other (only
+// the gradient kernel reads both), so one launch runs them side by side: the
+// first half of the grid is the reverse chain (the longer one), the second
+// half the forward chain.
 template <int DK>
-__global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs a, const float* __restrict__ X, size_t off_X,
-                                                        size_t off_Y, float ysign, size_t off_Z, float zsign,
-                                                        size_t off_E, size_t off_F, const float* __restrict__ S_init,
-                                                        float* __restrict__ S_final, size_t off_Sst, size_t off_Dst,
-                                                        int reverse)
+__global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs a, ChainOps rev_ops, ChainOps fwd_ops)
 {
     constexpr int PER = BC * DK / 4 / 256;  // float4 of one operand per thread
     constexpr int P = DK + 4;               // LDS row pitch (floats)
     constexpr int NT = DK / 64;             // 16-column tiles per wave
     const int dv = a.dv, H = a.H;
     const int rblocks = dv / 16;
-    const int64_t pair = blockIdx.x / rblocks;
-    const int rb = (int)(blockIdx.x % rblocks);
+    const int64_t half = (int64_t)a.N * H * rblocks;
+    const bool is_rev = blockIdx.x < half;
+    const ChainOps op = is_rev ? rev_ops : fwd_ops;
+    const int64_t bid = is_rev ? (int64_t)blockIdx.x : (int64_t)blockIdx.x - half;
+    const float ysign = op.ysign, zsign = op.zsign;
+    const float* __restrict__ S_init = op.S_init;
+    float* __restrict__ S_final = op.S_final;
+    const int reverse = op.reverse;
+    const int64_t pair = bid / rblocks;
+    const int rb = (int)(bid % rblocks);
     const int n = (int)(pair / H), h = (int)(pair % H);
     const int t = threadIdx.x, w = t >> 6, l = t & 63, r16 = l & 15, g = l >> 4;
     const int32_t* seq_first = reinterpret_cast<const int32_t*>(a.ws + a.lay.off_seq_first);
     const float* gamv = reinterpret_cast<const float*>(a.ws + a.lay.off_gam);
     auto wsf = [&](size_t off) { return reinterpret_cast<float*>(a.ws + off); };
-    const float* Xb = X ? X : wsf(off_X);
-    const float* Yb = wsf(off_Y);
-    const float* Zb = wsf(off_Z);
-    const float* Eb = off_E ? wsf(off_E) : nullptr;
-    const float* Fb = off_F ? wsf(off_F) : nullptr;
-    float* Sst = wsf(off_Sst);
-    float* Dst = wsf(off_Dst);
+    const float* Xb = wsf(op.off_X);
+    const float* Yb = wsf(op.off_Y);
+    const float* Zb = wsf(op.off_Z);
+    const float* Eb = op.off_E ? wsf(op.off_E) : nullptr;
+    const float* Fb = op.off_F ? wsf(op.off_F) : nullptr;
+    float* Sst = wsf(op.off_Sst);
+    float* Dst = wsf(op.off_Dst);
     __shared__ __align__(16) float bufA[BC * P], bufB[BC * P];
     __shared__ float Ssh[16 * P];
     __shared__ float dsm[BC * 17];
@@ -772,27 +791,20 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a)
 }
 
 template <int DK>
-hipError_t launch_chain(const BwdArgs& a, const float* X, size_t off_X, size_t off_Y, float ysign, size_t off_Z,
-                        float zsign, size_t off_E, size_t off_F, const float* S_init, float* S_final, size_t off_Sst,
-                        size_t off_Dst, int reverse)
+hipError_t launch_chain(const BwdArgs& a, const ChainOps& rev, const ChainOps& fwd)
 {
-    const int64_t blocks = (int64_t)a.N * a.H * (a.dv / 16);
-    hipLaunchKernelGGL((bwd_chain_kernel<DK>), dim3((uint32_t)blocks), dim3(256), 0, a.stream, a, X, off_X, off_Y,
-                       ysign, off_Z, zsign, off_E, off_F, S_init, S_final, off_Sst, off_Dst, reverse);
+    const int64_t blocks = 2 * (int64_t)a.N * a.H * (a.dv / 16);
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((bwd_chain_kernel<DK>), dim3((uint32_t)blocks), dim3(256), 0, a.stream, a, rev, fwd);
     return hipGetLastError();
 }
 
-hipError_t chain_dispatch(const BwdArgs& a, const float* X, size_t off_X, size_t off_Y, float ysign, size_t off_Z,
-                          float zsign, size_t off_E, size_t off_F, const float* S_init, float* S_final,
-                          size_t off_Sst, size_t off_Dst, int reverse)
+hipError_t chain_dispatch(const BwdArgs& a, const ChainOps& rev, const ChainOps& fwd)
 {
     switch (a.dk) {
-        case 64: return launch_chain<64>(a, X, off_X, off_Y, ysign, off_Z, zsign, off_E, off_F, S_init, S_final,
-                                         off_Sst, off_Dst, reverse);
-        case 128: return launch_chain<128>(a, X, off_X, off_Y, ysign, off_Z, zsign, off_E, off_F, S_init, S_final,
-                                           off_Sst, off_Dst, reverse);
-        case 256: return launch_chain<256>(a, X, off_X, off_Y, ysign, off_Z, zsign, off_E, off_F, S_init, S_final,
-                                           off_Sst, off_Dst, reverse);
+        case 64: return launch_chain<64>(a, rev, fwd);
+        case 128: return launch_chain<128>(a, rev, fwd);
+        case 256: return launch_chain<256>(a, rev, fwd);
         default: return hipErrorInvalidValue;
     }
 }
@@ -869,12 +881,18 @@ hipError_t launch_backward(const BwdArgs& a)
         hipLaunchKernelGGL((bwd_local_kernel<float>), dim3((uint32_t)chblocks), dim3(256), 0, a.stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // forward: Delta = U - W S^T,  S <- e^{gamma_L} S + Delta^T (D K); records S and Delta
-    e = chain_dispatch(a, nullptr, L.off_U, L.off_W, -1.f, L.off_DK, 1.f, 0, 0, a.init_state, nullptr, L.off_S,
-                       L.off_Dl, 0);
-    if (e != hipSuccess) return e;
+    ChainOps fwd;
+    fwd.off_X = L.off_U; fwd.off_Y = L.off_W; fwd.off_Z = L.off_DK; fwd.off_E = 0; fwd.off_F = 0;
+    fwd.off_Sst = L.off_S; fwd.off_Dst = L.off_Dl;
+    fwd.S_init = a.init_state; fwd.S_final = nullptr;
+    fwd.ysign = -1.f; fwd.zsign = 1.f; fwd.reverse = 0;
     // reverse: dDelta = dDelta_local + (D K) dS^T,  dS <- e^{gamma_L} dS - dDelta^T W + E^T Q
-    e = chain_dispatch(a, nullptr, L.off_dDl, L.off_DK, 1.f, L.off_W, -1.f, L.off_E, L.off_Q, a.dstate, a.dinit,
-                       L.off_dS, L.off_dD, 1);
+    ChainOps rev;
+    rev.off_X = L.off_dDl; rev.off_Y = L.off_DK; rev.off_Z = L.off_W; rev.off_E = L.off_E; rev.off_F = L.off_Q;
+    rev.off_Sst = L.off_dS; rev.off_Dst = L.off_dD;
+    rev.S_init = a.dstate; rev.S_final = a.dinit;
+    rev.ysign = 1.f; rev.zsign = -1.f; rev.reverse = 1;
+    e = chain_dispatch(a, rev, fwd);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_grad_kernel, dim3((uint32_t)chblocks), dim3(256), 0, a.stream, a);
     return hipGetLastError();
