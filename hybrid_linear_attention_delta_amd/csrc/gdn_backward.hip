@@ -207,32 +207,54 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a)
     const TIn* v = (const TIn*)a.v;
     const TIn* dO = (const TIn*)a.dO;
 
-    // rows of the chunk, normalised and padded with zeros
-    for (int r = wv; r < BC; r += 4) {
-        const bool live = r < len;
-        const int64_t row = (int64_t)(tok0 + (live ? r : 0)) * H + h;
-        float ssq = 0.f, ssk = 0.f;
-        for (int col = lane; col < dk; col += 64) {
-            const float xq = live ? Elem<TIn>::load(q, row * dk + col) : 0.f;
-            const float xk = live ? Elem<TIn>::load(k, row * dk + col) : 0.f;
-            ssq += xq * xq;
-            ssk += xk * xk;
+    // rows of the chunk, normalised and padded with zeros; each wave takes its
+    // 16 rows four at a time with all of their loads in flight (d <= 256: at
+    // most four values per lane and row)
+    for (int r0 = wv; r0 < BC; r0 += 16) {
+        float xq[4][4], xk[4][4], xv[4][4], xo[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = r0 + 4 * i;
+            const bool live = r < len;
+            const int64_t row = (int64_t)(tok0 + (live ? r : 0)) * H + h;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int col = lane + 64 * m;
+                xq[i][m] = (live && col < dk) ? Elem<TIn>::load(q, row * dk + col) : 0.f;
+                xk[i][m] = (live && col < dk) ? Elem<TIn>::load(k, row * dk + col) : 0.f;
+                xv[i][m] = (live && col < dv) ? Elem<TIn>::load(v, row * dv + col) : 0.f;
+                xo[i][m] = (live && col < dv) ? Elem<TIn>::load(dO, row * dv + col) : 0.f;
+            }
         }
-        ssq = group_sum<64>(ssq);
-        ssk = group_sum<64>(ssk);
-        const float rq = a.l2norm ? 1.0f / sqrtf(ssq + kNormEps) : 1.f;
-        const float rk = a.l2norm ? 1.0f / sqrtf(ssk + kNormEps) : 1.f;
-        for (int col = lane; col < dk; col += 64) {
-            s.Q[r * dk + col] = live ? Elem<TIn>::load(q, row * dk + col) * rq : 0.f;
-            s.K[r * dk + col] = live ? Elem<TIn>::load(k, row * dk + col) * rk : 0.f;
-        }
-        for (int col = lane; col < dv; col += 64) {
-            s.V[r * dv + col] = live ? Elem<TIn>::load(v, row * dv + col) : 0.f;
-            s.dO[r * dv + col] = live ? Elem<TIn>::load(dO, row * dv + col) : 0.f;
-        }
-        if (lane == 0) {
-            s.rq[r] = rq;
-            s.rk[r] = rk;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = r0 + 4 * i;
+            float ssq = 0.f, ssk = 0.f;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                ssq += xq[i][m] * xq[i][m];
+                ssk += xk[i][m] * xk[i][m];
+            }
+            ssq = group_sum<64>(ssq);
+            ssk = group_sum<64>(ssk);
+            const float rq = a.l2norm ? 1.0f / sqrtf(ssq + kNormEps) : 1.f;
+            const float rk = a.l2norm ? 1.0f / sqrtf(ssk + kNormEps) : 1.f;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int col = lane + 64 * m;
+                if (col < dk) {
+                    s.Q[r * dk + col] = xq[i][m] * rq;
+                    s.K[r * dk + col] = xk[i][m] * rk;
+                }
+                if (col < dv) {
+                    s.V[r * dv + col] = xv[i][m];
+                    s.dO[r * dv + col] = xo[i][m];
+                }
+            }
+            if (lane == 0) {
+                s.rq[r] = rq;
+                s.rk[r] = rk;
+            }
         }
     }
     if (t == 0) {
@@ -772,20 +794,42 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a)
             }
         }
     }
-    // through the L2 norms: dx = r (dx^ - x^ (x^ . dx^))
-    for (int r = wv; r < len; r += 4) {
-        const int64_t row = (int64_t)(tok0 + r) * H + h;
-        float pq = 0.f, pk = 0.f;
-        for (int col = lane; col < dk; col += 64) {
-            pq += s.Q[r * dk + col] * s.dQ[r * dk + col];
-            pk += s.K[r * dk + col] * s.dK[r * dk + col];
-        }
-        pq = a.l2norm ? group_sum<64>(pq) : 0.f;
-        pk = a.l2norm ? group_sum<64>(pk) : 0.f;
-        const float rq = s.rq[r], rk = s.rk[r];
-        for (int col = lane; col < dk; col += 64) {
-            a.dq[row * dk + col] = rq * (s.dQ[r * dk + col] - s.Q[r * dk + col] * pq);
-            a.dk_out[row * dk + col] = rk * (s.dK[r * dk + col] - s.K[r * dk + col] * pk);
+    // through the L2 norms: dx = r (dx^ - x^ (x^ . dx^)); four rows per wave in flight
+    for (int r0 = wv; r0 < BC; r0 += 16) {
+        float xq[4][4], gq[4][4], xk[4][4], gk[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int r = r0 + 4 * i, col = lane + 64 * m;
+                const bool in = col < dk;
+                xq[i][m] = in ? s.Q[r * dk + col] : 0.f;
+                gq[i][m] = in ? s.dQ[r * dk + col] : 0.f;
+                xk[i][m] = in ? s.K[r * dk + col] : 0.f;
+                gk[i][m] = in ? s.dK[r * dk + col] : 0.f;
+            }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = r0 + 4 * i;
+            float pq = 0.f, pk = 0.f;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                pq += xq[i][m] * gq[i][m];
+                pk += xk[i][m] * gk[i][m];
+            }
+            pq = a.l2norm ? group_sum<64>(pq) : 0.f;
+            pk = a.l2norm ? group_sum<64>(pk) : 0.f;
+            if (r >= len) continue;  // wave-uniform
+            const int64_t row = (int64_t)(tok0 + r) * H + h;
+            const float rq = s.rq[r], rk = s.rk[r];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int col = lane + 64 * m;
+                if (col < dk) {
+                    a.dq[row * dk + col] = rq * (gq[i][m] - xq[i][m] * pq);
+                    a.dk_out[row * dk + col] = rk * (gk[i][m] - xk[i][m] * pk);
+                }
+            }
         }
     }
 }
