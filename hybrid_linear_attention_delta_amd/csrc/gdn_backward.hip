@@ -628,9 +628,16 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a)
         const f32x4* S4 = reinterpret_cast<const f32x4*>(s.S);
         const f32x4* dS4 = reinterpret_cast<const f32x4*>(s.dS);
         float x = 0.f;
-        for (int64_t e = t; e < n4; e += 256) {
-            const f32x4 u = S4[e], w = dS4[e];
-            x += u.x * w.x + u.y * w.y + u.z * w.z + u.w * w.w;
+        for (int64_t e0 = t; e0 < n4; e0 += 256 * 8) {  // eight vector pairs in flight per thread
+            f32x4 u[8], w[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int64_t e = e0 + 256 * j;
+                u[j] = e < n4 ? S4[e] : f32x4{0.f, 0.f, 0.f, 0.f};
+                w[j] = e < n4 ? dS4[e] : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) x += u[j].x * w[j].x + u[j].y * w[j].y + u[j].z * w[j].z + u[j].w * w[j].w;
         }
         dgL += expf(gam[BC - 1]) * x;
     }
