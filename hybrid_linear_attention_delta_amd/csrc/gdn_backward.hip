@@ -33,10 +33,10 @@
 // Ragged chunks are padded to C rows with q = k = v = dO = 0, beta = 0 and
 // g = 0, which leaves every product of the real rows unchanged.
 //
-// Everything is fp32 on the vector ALUs: the per-chunk products go through one
-// LDS-tiled 64 x 64 block routine (4 x 4 outputs per thread).  This is a first,
-// plain evaluation of the gradient; its contractions are not yet on the matrix
-// cores.
+// Everything is fp32.  The contractions run on the fp32 matrix cores
+// (v_mfma_f32_16x16x4_f32: exact fp32 products, fp32 sums); the per-chunk
+// products go through one LDS-tiled 64 x 64 block routine.  Results do not
+// depend on scheduling: no atomics, fixed reduction orders.
 #include <string.h>
 
 #include "gdn_common.h"
