@@ -419,6 +419,15 @@ gdn_status gdn_chunk_prefill_backward(const void* q, const void* k, const void* 
     }
     const gdn::BwdLayout lay = gdn::backward_layout(total_tokens, num_seqs, H, dk, dv);
     if (workspace_bytes < lay.total) return GDN_ERR_WORKSPACE;
+    if (grad_init_state) {
+        // the two chains run side by side: the initial-state gradient, written at
+        // the end of the reverse chain, must not share memory with either state input
+        const size_t bytes = (size_t)num_seqs * H * dv * dk * 4;
+        const char* o0 = (const char*)grad_init_state;
+        const char* ins[] = {(const char*)init_state, (const char*)d_final_state};
+        for (const char* p : ins)
+            if (p && p < o0 + bytes && o0 < p + bytes) return GDN_ERR_BAD_SHAPE;
+    }
     gdn::BwdArgs a;
     a.q = q; a.k = k; a.v = v; a.dO = d_o; a.g = g; a.beta = beta;
     a.init_state = init_state; a.dstate = d_final_state;

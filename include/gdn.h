@@ -277,7 +277,8 @@ size_t gdn_prefill_backward_workspace_size(int64_t total_tokens, int32_t num_seq
  *               256-byte aligned
  * Supported: dt in {GDN_F32, GDN_BF16}, dk and dv in {64, 128, 256}; the
  * arithmetic is fp32 throughout.  Gradient buffers must not overlap the
- * inputs or each other.  With an invalid device cu_seqlens (and no host
+ * inputs or each other; for grad_init_state against init_state and
+ * d_final_state this is checked (GDN_ERR_BAD_SHAPE).  With an invalid device cu_seqlens (and no host
  * mirror) no chunk is processed and the gradients are unspecified.
  */
 gdn_status gdn_chunk_prefill_backward(const void* q, const void* k, const void* v, const float* g,

@@ -222,3 +222,11 @@ def test_backward_host_validation(lib):
     assert bwd(ws=_fake(0x10010)) == 5         # workspace 256-byte aligned
     bad = (ctypes.c_int32 * 3)(0, 100, 90)
     assert bwd(N=2, cu=f, cu_host=bad) == 4
+
+    def bwd_states(init, dfinal, dinit):
+        return lib.gdn_chunk_prefill_backward(f, f, f, f, f, init, f, dfinal, None, None, 1, 128, 2, 64, 64,
+                                              gdn.GDN_BF16, -1.0, 1, f, f, f, f, f, dinit, f, need, None)
+
+    assert bwd_states(_fake(0x40000), None, _fake(0x40000)) == 2   # the initial-state gradient over init_state
+    assert bwd_states(None, _fake(0x40000), _fake(0x44000)) == 2   # partly over d_final_state
+    assert bwd_states(None, _fake(0x40000), _fake(0x40000)) == 2   # or exactly
