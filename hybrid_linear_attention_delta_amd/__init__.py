@@ -8,9 +8,14 @@ and the kernel sources (``csrc``).
 from .gdn import (  # noqa: F401
     GdnError,
     chunk_prefill,
+    chunk_prefill_backward,
     decode_step,
+    frontend_decode,
+    frontend_prefill,
     load_library,
+    prefill_backward_workspace_size,
     prefill_workspace_size,
 )
 
-__all__ = ["chunk_prefill", "decode_step", "prefill_workspace_size", "load_library", "GdnError"]
+__all__ = ["chunk_prefill", "chunk_prefill_backward", "decode_step", "frontend_prefill", "frontend_decode",
+           "prefill_workspace_size", "prefill_backward_workspace_size", "load_library", "GdnError"]
