@@ -151,6 +151,8 @@ def full_launch(name, grid, groups):
     non-segmented chain instance; for the decode kernel the d_v = 256 batch
     (the smaller of its two grids: the bench also times a d_v = 512 batch);
     else the largest grid of the kernel."""
+    if kernel_key(name).startswith("bwd_"):
+        return True  # the backward has no segmented launches
     if "chain_kernel" in name:
         return ", false>" in name
     grids = [g for (nm, g) in groups if kernel_key(nm) == kernel_key(name)]
@@ -263,16 +265,20 @@ def render_traffic():
     log("[profile] wrote profiles/traffic.json and profiles/traffic_prefill64k_decode.md")
 
 
-MFMA_COUNTERS = ("MfmaUtil", "MfmaFlops", "MfmaFlopsBF16")
+MFMA_COUNTERS = ("MfmaUtil", "MfmaFlops", "MfmaFlopsBF16", "MfmaFlopsF32")
 MFMA_KERNELS = "chain_kernel|intra_kernel|output_kernel"
+BENCH_PMC_BWD = ["bench.py", "--steps", "1", "--warmup", "1", "--no-decode", "--no-other", "--no-cpu-baseline"]
 
 
 def mode_mfma():
-    rc, d, cmd = launch(BENCH_PMC, ["--pmc", *MFMA_COUNTERS, "--kernel-include-regex", MFMA_KERNELS], "mfma", 600)
-    with open(os.path.join(d, "command.txt"), "w") as f:
-        f.write(cmd + "\n")
-    if not profiler_ok(rc, d, "counter_collection.csv"):
-        raise SystemExit(f"mfma pass failed (exit {rc})")
+    passes = ((BENCH_PMC, MFMA_KERNELS, "mfma"), (BENCH_PMC_BWD, "bwd_local_kernel|bwd_chain_kernel|bwd_grad_kernel",
+                                                   "mfma_bwd"))
+    for bench_cmd, regex, tag in passes:
+        rc, d, cmd = launch(bench_cmd, ["--pmc", *MFMA_COUNTERS, "--kernel-include-regex", regex], tag, 600)
+        with open(os.path.join(d, "command.txt"), "w") as f:
+            f.write(cmd + "\n")
+        if not profiler_ok(rc, d, "counter_collection.csv"):
+            raise SystemExit(f"{tag} pass failed (exit {rc})")
 
 
 def mfma_table(d):
@@ -297,6 +303,8 @@ def mfma_table(d):
         key = kernel_key(name)
         n = len(disps)
         ent = {c: sum(v.get(c, 0.0) for v in disps.values()) / n for c in (*MFMA_COUNTERS, "ns", "wg")}
+        if key in out:  # several whole-workload instances (the backward chain per d_k): keep the first
+            continue
         ent["n"] = n
         out[key] = ent
     return out
@@ -339,6 +347,26 @@ def render_mfma():
     if ch is not None:
         lines += ["", f"State chain: algorithmic {chain_alg / 1e9:.1f} GFLOP per launch (4 d_k d_v per token and head);",
                   f"executed / algorithmic = {ch['MfmaFlops'] / chain_alg:.2f}.", ""]
+    bwd = mfma_table(os.path.join(OUT, "mfma_bwd"))
+    if bwd:
+        bcmd = open(os.path.join(OUT, "mfma_bwd", "command.txt")).read().strip()
+        alg = bench.flops_backward_per_token() * bench.T
+        lines += ["", "## Backward of the same prefill (fp32)", "", "```", bcmd, "```", "",
+                  "| kernel | dispatches | workgroups | us (counter run) | executed GFLOP | of which fp32"
+                  " | executed TFLOP/s | MfmaUtil % |", "|---|---|---|---|---|---|---|---|"]
+        total = 0.0
+        for key in ("bwd_local_kernel", "bwd_chain_kernel", "bwd_grad_kernel"):
+            e = bwd.get(key)
+            if e is None:
+                continue
+            total += e["MfmaFlops"]
+            tf = e["MfmaFlops"] / (e["ns"] * 1e-9) / 1e12 if e["ns"] > 0 else float("nan")
+            lines.append(f"| `{key}` | {e['n']} | {e['wg']:.0f} | {e['ns'] / 1e3:.0f} | {e['MfmaFlops'] / 1e9:.1f}"
+                         f" | {e['MfmaFlopsF32'] / 1e9:.1f} | {tf:.1f} | {e['MfmaUtil']:.2f} |")
+        lines += ["", f"Algorithmic {alg / 1e9:.1f} GFLOP per backward (bench.py's count);",
+                  f"executed on MFMA / algorithmic = {total / alg:.2f}.  The executed figure leaves out the",
+                  "vector-ALU work (forward substitution, reductions, norms) and counts the",
+                  "triangular products as full 64 x 64 blocks.", ""]
     with open(os.path.join(PROFILES, "mfma_prefill64k.md"), "w") as f:
         f.write("\n".join(lines))
     log("[profile] wrote profiles/mfma_prefill64k.md")
