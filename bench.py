@@ -5,8 +5,9 @@
 
 One step = one chunked prefill of the long-context workload: B=1, H=6,
 d_k = d_v = 256, T = 65,536 tokens, bf16 q/k/v, fp32 gates and state, chunk
-64, inputs resident in HBM, as one whole-prefill call (the library pipelines
-segments of its three stages over streams).  ``value`` is prefill tokens/s
+64, inputs resident in HBM, as one whole-prefill call with an execution
+context created once beforehand (gdn_chunk_prefill_ctx: the library pipelines
+segments of its three stages over the context's streams).  ``value`` is prefill tokens/s
 of those steps.  The same work is then run stage by stage (per-chunk
 preparation, the sequential state chain as one launch over all chunks, the
 per-chunk outputs), each stage timed with HIP events on the stream it runs
@@ -25,7 +26,9 @@ bf16 MFMA.  Whole-path figures use F_tok = H [6 d_k d_v + C (3 d_k + 2 d_v)
 g and beta in fp32).
 
 cpu_baseline: the fp64 oracle (plain sequential recurrence, one thread per
-(sequence, head) chain) run on the host on the same 64K-token inputs.
+(sequence, head) chain, threads = min(chains, host cores)) run on the host on
+the same 64K-token inputs, timed around its computation only; plus one head's
+chain on a single thread for a per-core figure.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -113,7 +116,7 @@ def traffic_from_profiles(kernel_key):
     return None if ent is None else ent.get("hbm_bytes_per_launch")
 
 
-def bench_prefill(torch, gdn, synth, steps, warmup):
+def bench_prefill(torch, gdn, synth, steps, warmup, ctx):
     dev = torch.device("cuda:0")
     log(f"[bench] generating prefill inputs T={T} H={H} d={DK} bf16")
     inp = synth.prefill_inputs(T, H, DK, DV, "bf16", seed=synth.seed_for("prefill64k"))
@@ -128,7 +131,7 @@ def bench_prefill(torch, gdn, synth, steps, warmup):
     log(f"[bench] workspace {ws.numel() / 2**20:.0f} MiB")
 
     def run(st):
-        gdn.chunk_prefill(q, k, v, g, beta, chunk=C, out=o, final_state=fs, workspace=ws, stages=st)
+        gdn.chunk_prefill(q, k, v, g, beta, chunk=C, out=o, final_state=fs, workspace=ws, stages=st, ctx=ctx)
 
     # --- the step as a caller runs it: one whole-prefill call (the library
     #     pipelines its stages over streams internally)
@@ -172,7 +175,7 @@ def bench_prefill(torch, gdn, synth, steps, warmup):
     zt = synth.to_torch(z, dev, bf16=True)
     wt = synth.to_torch(w, dev)
     gated = lambda: gdn.chunk_prefill(q, k, v, g, beta, chunk=C, out=o, final_state=fs, workspace=ws, gate=zt,
-                                      norm_weight=wt)
+                                      norm_weight=wt, ctx=ctx)
     for _ in range(max(1, warmup)):
         gated()
     torch.cuda.synchronize()
@@ -201,6 +204,8 @@ def bench_prefill(torch, gdn, synth, steps, warmup):
     torch.cuda.synchronize()
     graph_ms = t0.elapsed_time(t1) / steps
     log(f"[bench] prefill replayed from a HIP graph: {graph_ms:.3f} ms/step")
+    del graph  # release the graph (and its references to the context's streams) before the context
+    torch.cuda.synchronize()
     return dict(ms_per_step=total_ms / steps, wall_ms_per_step=wall * 1e3 / steps, prepare_ms=stage_ms[0],
                 chain_ms=stage_ms[1], output_ms=stage_ms[2], staged_ms=sum(stage_ms), gated_ms=gated_ms,
                 graph_ms=graph_ms, inputs=inp)
@@ -261,6 +266,8 @@ def bench_decode(torch, gdn, synth, n_steps, warmup=3):
     torch.cuda.synchronize()
     graphed = evs[0].elapsed_time(evs[1]) / n_steps
     log(f"[bench] decode {n_steps} steps in one HIP graph: {graphed * 1e3:.1f} us/step")
+    del graph
+    torch.cuda.synchronize()
     # d_v = 512 (the pages' value width): twice the state per sequence and head
     st5 = torch.from_numpy(synth.decode_state(DEC_N, H, DK, 2 * DV, seed)).to(dev)
     qn, kn, vn, gn, bn = synth.decode_step_inputs(DEC_N, H, DK, 2 * DV, "bf16", seed, 0)
@@ -281,7 +288,7 @@ def bench_decode(torch, gdn, synth, n_steps, warmup=3):
     return dict(ms_per_step=ms, median_ms=med, gated_ms=gated, graph_ms=graphed, dv512_ms=dv512)
 
 
-def bench_prefill_other(torch, gdn, synth, steps, warmup):
+def bench_prefill_other(torch, gdn, synth, steps, warmup, ctx):
     """The two other prefill workloads, timed as whole-prefill calls: 8K tokens
     (B=1, H=6, d=256, bf16) and the packed 2M-token batch (16 sequences,
     log-uniform lengths in [4K, 512K])."""
@@ -310,7 +317,7 @@ def bench_prefill_other(torch, gdn, synth, steps, warmup):
         ws = torch.empty(gdn.prefill_workspace_size(Tn, N, H, DK, dvn, C), dtype=torch.uint8, device=dev)
         cu_arg = None if cuh is None else torch.from_numpy(cuh)
         run = lambda: gdn.chunk_prefill(a, b, c, d, e, cu_seqlens=cu_arg, chunk=C, out=o, final_state=fs,
-                                        workspace=ws)
+                                        workspace=ws, ctx=ctx)
         n_steps = steps if cuh is None else max(2, steps // 3)
         for _ in range(max(1, warmup)):
             run()
@@ -341,7 +348,7 @@ def frontend_bytes(tokens):
     return 2 * tokens * ctot * 2 + 4 * tokens * H * 4 + ctot * 4 * 4
 
 
-def bench_frontend(torch, gdn, synth, steps, warmup):
+def bench_frontend(torch, gdn, synth, steps, warmup, ctx):
     """The front end (App. A.3: 4-tap causal conv + SiLU on q, k, v and the gate
     math) over the 64K-token workload, alone and followed by the prefill; and
     its decode form for the 256-sequence decode batch."""
@@ -361,7 +368,7 @@ def bench_frontend(torch, gdn, synth, steps, warmup):
 
     def both():
         q, k, v, g, beta, _ = front()
-        gdn.chunk_prefill(q, k, v, g, beta, chunk=C, out=o, final_state=fs, workspace=ws)
+        gdn.chunk_prefill(q, k, v, g, beta, chunk=C, out=o, final_state=fs, workspace=ws, ctx=ctx)
 
     res = {}
     t0 = torch.cuda.Event(enable_timing=True)
@@ -443,19 +450,48 @@ def bench_backward(torch, gdn, synth, inp, steps, warmup):
     return ms
 
 
+def host_cores():
+    """CPU cores this process may run on (its affinity set), and os.cpu_count()."""
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count() or 1
+    return usable, os.cpu_count() or usable
+
+
 def cpu_baseline(inp, max_threads=16):
+    """The fp64 oracle on the host, timed around its computation only.
+
+    Leg 1: the whole 64K-token workload, one thread per (sequence, head) chain,
+    threads = min(chains, usable cores, 16) (16 = one GPU's share of the host).
+    Leg 2: one head's chain (the first) on one thread, for a per-core figure.
+    fp64 work: 7 d_k d_v flops per token and head (the retrieval dot product,
+    the decay-plus-write update and the read, 2 + 3 + 2 per state element)."""
     import oracle
 
+    usable, count = host_cores()
     chains = H
-    threads = max(1, min(chains, os.cpu_count() or 1, max_threads))
-    log(f"[bench] cpu baseline: fp64 oracle on {T} tokens x {H} heads, {threads} threads")
-    t0 = time.perf_counter()
-    oracle.prefill(inp.q, inp.k, inp.v, inp.g, inp.beta, bf16=True, n_threads=threads)
-    dt = time.perf_counter() - t0
-    log(f"[bench] cpu baseline {dt:.1f} s")
+    threads = max(1, min(chains, usable, max_threads))
+    flop_tok_head = 7.0 * DK * DV
+    log(f"[bench] cpu baseline: fp64 oracle on {T} tokens x {H} heads, {threads} threads "
+        f"(usable cores {usable}, os.cpu_count {count})")
+    tm = {}
+    oracle.prefill(inp.q, inp.k, inp.v, inp.g, inp.beta, bf16=True, n_threads=threads, timing=tm)
+    dt = tm["seconds"]
+    tm1 = {}
+    oracle.prefill(inp.q[:, :1], inp.k[:, :1], inp.v[:, :1], inp.g[:, :1], inp.beta[:, :1], bf16=True, n_threads=1,
+                   timing=tm1)
+    dt1 = tm1["seconds"]
+    log(f"[bench] cpu baseline {dt:.2f} s ({threads} threads); one head on one thread {dt1:.2f} s")
     return dict(value=T / dt, unit="tokens/s", cores=threads, kind="oracle",
                 sample=f"full prefill workload: {T} tokens x {H} heads, d={DK}, fp64 sequential recurrence, "
-                       f"{dt:.1f} s wall")
+                       f"{threads} threads (one per head chain), {dt:.2f} s of computation; per-core leg: head 0 "
+                       f"alone on one thread, {dt1:.2f} s",
+                nproc=usable, os_cpu_count=count, threads=threads, seconds=dt,
+                gflops_fp64=flop_tok_head * T * H / dt / 1e9,
+                single_thread={"tokens_per_s_per_core": T / (H * dt1), "seconds_one_head": dt1,
+                               "gflops_fp64": flop_tok_head * T / dt1 / 1e9},
+                flops_per_token_head=flop_tok_head)
 
 
 def main():
@@ -483,11 +519,14 @@ def main():
         print("bench.py needs a GPU (cuda:0)", file=sys.stderr)
         sys.exit(2)
     gdn.load_library()
-    pre = bench_prefill(torch, gdn, synth, a.steps, a.warmup)
+    ctx = gdn.Context()  # streams and events of the overlapped prefill, created once
+    pre = bench_prefill(torch, gdn, synth, a.steps, a.warmup, ctx)
     dec = None if a.no_decode else bench_decode(torch, gdn, synth, a.decode_steps)
-    fe = bench_frontend(torch, gdn, synth, a.steps, a.warmup)
-    other = None if a.no_other else bench_prefill_other(torch, gdn, synth, a.steps, a.warmup)
+    fe = bench_frontend(torch, gdn, synth, a.steps, a.warmup, ctx)
+    other = None if a.no_other else bench_prefill_other(torch, gdn, synth, a.steps, a.warmup, ctx)
     bwd_ms = None if a.no_backward else bench_backward(torch, gdn, synth, pre["inputs"], min(a.steps, 3), 1)
+    torch.cuda.synchronize()
+    ctx.close()  # every HIP object the library made is released before the process ends
 
     tok_s = T / (pre["ms_per_step"] / 1e3)
     chain_flops = flops_chain_per_token() * T

@@ -6,6 +6,7 @@ ctypes binding (``gdn``), the seeded synthetic workload generators (``synth``)
 and the kernel sources (``csrc``).
 """
 from .gdn import (  # noqa: F401
+    Context,
     GdnError,
     chunk_prefill,
     chunk_prefill_backward,
@@ -18,4 +19,4 @@ from .gdn import (  # noqa: F401
 )
 
 __all__ = ["chunk_prefill", "chunk_prefill_backward", "decode_step", "frontend_prefill", "frontend_decode",
-           "prefill_workspace_size", "prefill_backward_workspace_size", "load_library", "GdnError"]
+           "prefill_workspace_size", "prefill_backward_workspace_size", "load_library", "GdnError", "Context"]

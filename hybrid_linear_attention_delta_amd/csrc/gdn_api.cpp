@@ -1,5 +1,6 @@
 // gdn_api.cpp -- C-ABI entry points: argument validation, workspace layout,
-// dispatch onto the caller's stream.  No device allocation, no global state.
+// dispatch onto the caller's stream (and a caller-owned context's streams).  No device
+// allocation, no global state.
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
@@ -106,11 +107,12 @@ const char* gdn_status_string(gdn_status s)
         case GDN_ERR_ALIGNMENT: return "GDN_ERR_ALIGNMENT: tensor pointers must be 16-byte aligned";
         case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE: workspace missing or too small";
         case GDN_ERR_LAUNCH: return "GDN_ERR_LAUNCH: kernel launch or execution failed";
+        case GDN_ERR_CONTEXT: return "GDN_ERR_CONTEXT: context creation failed or context of another device";
     }
     return "GDN_ERR_UNKNOWN";
 }
 
-int32_t gdn_version(void) { return 100; }
+int32_t gdn_version(void) { return 200; }
 
 size_t gdn_prefill_workspace_size(int64_t total_tokens, int32_t num_seqs, int32_t H, int32_t dk, int32_t dv,
                                   int32_t chunk, gdn_dtype dt)
@@ -121,15 +123,18 @@ size_t gdn_prefill_workspace_size(int64_t total_tokens, int32_t num_seqs, int32_
     return gdn::prefill_layout(total_tokens, num_seqs, H, dk, dv, chunk, dt == GDN_BF16).total;
 }
 
-gdn_status gdn_chunk_prefill(const void* q, const void* k, const void* v, const float* g, const float* beta,
-                             const float* init_state, const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
-                             int32_t num_seqs, int64_t total_tokens, int32_t H, int32_t dk, int32_t dv,
-                             int32_t chunk, gdn_dtype dt, float scale, int32_t qk_l2norm, void* o,
-                             float* final_state, void* workspace, size_t workspace_bytes, hipStream_t stream)
+gdn_status gdn_context_create(int32_t chain_cus_per_xcd, gdn_context_t* ctx)
 {
-    return gdn_chunk_prefill_staged(q, k, v, g, beta, init_state, cu_seqlens, cu_seqlens_host, num_seqs,
-                                    total_tokens, H, dk, dv, chunk, dt, scale, qk_l2norm, o, final_state, workspace,
-                                    workspace_bytes, GDN_STAGE_ALL, stream);
+    if (!ctx) return GDN_ERR_NULL_ARG;
+    *ctx = nullptr;
+    if (chain_cus_per_xcd > 31) return GDN_ERR_BAD_SHAPE;
+    return gdn::context_create(chain_cus_per_xcd, ctx) == hipSuccess ? GDN_OK : GDN_ERR_CONTEXT;
+}
+
+gdn_status gdn_context_destroy(gdn_context_t ctx)
+{
+    if (!ctx) return GDN_ERR_NULL_ARG;
+    return gdn::context_destroy(ctx) == hipSuccess ? GDN_OK : GDN_ERR_CONTEXT;
 }
 
 }  // extern "C"
@@ -150,7 +155,8 @@ gdn_status prefill_impl(const void* q, const void* k, const void* v, const float
                         const float* init_state, const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
                         int32_t num_seqs, int64_t total_tokens, int32_t H, int32_t dk, int32_t dv, int32_t chunk,
                         gdn_dtype dt, float scale, int32_t qk_l2norm, void* o, float* final_state, void* workspace,
-                        size_t workspace_bytes, int32_t stages, const gdn::GatedNorm& norm, hipStream_t stream)
+                        size_t workspace_bytes, int32_t stages, const gdn::GatedNorm& norm, gdn_context* ctx,
+                        hipStream_t stream)
 {
     if (stages < 1 || stages > GDN_STAGE_ALL) return GDN_ERR_BAD_SHAPE;
     if (dt != GDN_F32 && dt != GDN_BF16) return GDN_ERR_UNSUPPORTED;
@@ -180,6 +186,10 @@ gdn_status prefill_impl(const void* q, const void* k, const void* v, const float
         size_t bytes = (size_t)num_seqs * H * dv * dk * 4;
         if (a0 < b0 + bytes && b0 < a0 + bytes) return GDN_ERR_BAD_SHAPE;
     }
+    if (ctx) {
+        int dev = -1;
+        if (hipGetDevice(&dev) != hipSuccess || dev != gdn::context_device(ctx)) return GDN_ERR_CONTEXT;
+    }
 
     gdn::PrefillArgs a;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
@@ -195,6 +205,7 @@ gdn_status prefill_impl(const void* q, const void* k, const void* v, const float
     a.lay = lay;
     a.stages = stages;
     a.norm = norm;
+    a.ctx = ctx;
     a.stream = stream;
     return finish(gdn::launch_prefill(a), stream);
 }
@@ -239,16 +250,39 @@ gdn_status gdn_chunk_prefill_staged(const void* q, const void* k, const void* v,
 {
     return prefill_impl(q, k, v, g, beta, init_state, cu_seqlens, cu_seqlens_host, num_seqs, total_tokens, H, dk, dv,
                         chunk, dt, scale, qk_l2norm, o, final_state, workspace, workspace_bytes, stages,
-                        gdn::GatedNorm{}, stream);
+                        gdn::GatedNorm{}, nullptr, stream);
 }
 
-gdn_status gdn_chunk_prefill_gated(const void* q, const void* k, const void* v, const float* g, const float* beta,
-                                   const float* init_state, const int32_t* cu_seqlens,
-                                   const int32_t* cu_seqlens_host, int32_t num_seqs, int64_t total_tokens, int32_t H,
-                                   int32_t dk, int32_t dv, int32_t chunk, gdn_dtype dt, float scale,
-                                   int32_t qk_l2norm, const void* gate, const float* norm_weight, float norm_eps,
-                                   void* o, float* final_state, void* workspace, size_t workspace_bytes,
-                                   hipStream_t stream)
+gdn_status gdn_chunk_prefill(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                             const float* init_state, const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                             int32_t num_seqs, int64_t total_tokens, int32_t H, int32_t dk, int32_t dv,
+                             int32_t chunk, gdn_dtype dt, float scale, int32_t qk_l2norm, void* o,
+                             float* final_state, void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    return prefill_impl(q, k, v, g, beta, init_state, cu_seqlens, cu_seqlens_host, num_seqs, total_tokens, H, dk, dv,
+                        chunk, dt, scale, qk_l2norm, o, final_state, workspace, workspace_bytes, GDN_STAGE_ALL,
+                        gdn::GatedNorm{}, nullptr, stream);
+}
+
+gdn_status gdn_chunk_prefill_ctx(gdn_context_t ctx, const void* q, const void* k, const void* v, const float* g,
+                                 const float* beta, const float* init_state, const int32_t* cu_seqlens,
+                                 const int32_t* cu_seqlens_host, int32_t num_seqs, int64_t total_tokens, int32_t H,
+                                 int32_t dk, int32_t dv, int32_t chunk, gdn_dtype dt, float scale,
+                                 int32_t qk_l2norm, void* o, float* final_state, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream)
+{
+    return prefill_impl(q, k, v, g, beta, init_state, cu_seqlens, cu_seqlens_host, num_seqs, total_tokens, H, dk, dv,
+                        chunk, dt, scale, qk_l2norm, o, final_state, workspace, workspace_bytes, GDN_STAGE_ALL,
+                        gdn::GatedNorm{}, ctx, stream);
+}
+
+gdn_status gdn_chunk_prefill_gated_ctx(gdn_context_t ctx, const void* q, const void* k, const void* v,
+                                       const float* g, const float* beta, const float* init_state,
+                                       const int32_t* cu_seqlens, const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                       int64_t total_tokens, int32_t H, int32_t dk, int32_t dv, int32_t chunk,
+                                       gdn_dtype dt, float scale, int32_t qk_l2norm, const void* gate,
+                                       const float* norm_weight, float norm_eps, void* o, float* final_state,
+                                       void* workspace, size_t workspace_bytes, hipStream_t stream)
 {
     gdn::GatedNorm nm;
     nm.z = gate;
@@ -259,7 +293,20 @@ gdn_status gdn_chunk_prefill_gated(const void* q, const void* k, const void* v, 
     if (!nm.z) nm.z = o;  // no tokens: nothing is read
     return prefill_impl(q, k, v, g, beta, init_state, cu_seqlens, cu_seqlens_host, num_seqs, total_tokens, H, dk, dv,
                         chunk, dt, scale, qk_l2norm, o, final_state, workspace, workspace_bytes, GDN_STAGE_ALL, nm,
-                        stream);
+                        ctx, stream);
+}
+
+gdn_status gdn_chunk_prefill_gated(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                                   const float* init_state, const int32_t* cu_seqlens,
+                                   const int32_t* cu_seqlens_host, int32_t num_seqs, int64_t total_tokens, int32_t H,
+                                   int32_t dk, int32_t dv, int32_t chunk, gdn_dtype dt, float scale,
+                                   int32_t qk_l2norm, const void* gate, const float* norm_weight, float norm_eps,
+                                   void* o, float* final_state, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream)
+{
+    return gdn_chunk_prefill_gated_ctx(nullptr, q, k, v, g, beta, init_state, cu_seqlens, cu_seqlens_host, num_seqs,
+                                       total_tokens, H, dk, dv, chunk, dt, scale, qk_l2norm, gate, norm_weight,
+                                       norm_eps, o, final_state, workspace, workspace_bytes, stream);
 }
 
 gdn_status gdn_decode_step(const void* q, const void* k, const void* v, const float* g, const float* beta,

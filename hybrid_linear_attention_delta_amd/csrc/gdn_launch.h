@@ -6,7 +6,18 @@
 #include <stddef.h>
 #include <stdint.h>
 
+// Execution context of the pipelined prefill (the opaque gdn_context_t of the
+// C ABI): the streams and events one prefill call uses to overlap its stages.
+struct gdn_context;
+
 namespace gdn {
+
+// Context management (gdn_prefill.hip).  context_create makes the streams and
+// events on the current device; context_destroy waits for them and frees them.
+hipError_t context_create(int32_t chain_cus_per_xcd, gdn_context** out);
+hipError_t context_destroy(gdn_context* ctx);
+int context_device(const gdn_context* ctx);
+constexpr int32_t kDefaultChainCus = 16;  // chain CUs per XCD of the B=1, H=6, d=256 workload
 
 // Gated RMSNorm of the read-out (optional epilogue): o <- o / sqrt(mean_v o^2 + eps) * w * silu(z)
 // per (token, head) over the d_v values.  z has the layout and type of o; w is [d_v] fp32 or NULL.
@@ -69,6 +80,7 @@ struct PrefillArgs {
     PrefillLayout lay;
     int32_t stages;  // bit 0: prepare (chunk table + intra-chunk), bit 1: propagate (state chain), bit 2: outputs
     GatedNorm norm;  // epilogue of the output stage
+    gdn_context* ctx;  // NULL: every kernel on `stream`
     hipStream_t stream;
 };
 

@@ -54,8 +54,8 @@
 #include <string.h>
 
 #include <algorithm>
-#include <atomic>
 #include <mutex>
+#include <new>
 
 #include "gdn_common.h"
 #include "gdn_launch.h"
@@ -1809,91 +1809,107 @@ __global__ __launch_bounds__(256) void output_kernel(const int32_t* __restrict__
 
 // ------------------------------------------------------------------ dispatch
 
-// Streams and events of the pipelined prefill, created once per device and CU
-// split and kept for the life of the process (default priority, non-blocking
+}  // namespace gdn
+
+// Streams and events of the pipelined prefill, owned by the caller through
+// gdn_context_create / gdn_context_destroy (default priority, non-blocking
 // with respect to the legacy default stream).  The state chain gets a stream
 // of its own, CU-masked to the same number of CUs on every XCD, and the
 // per-segment intra-chunk and output kernels two more streams on all other
 // CUs: the chain's workgroups then never share a CU with the parallel kernels
 // and never wait for one to drain.  CU mask bit i is CU i / 8 of XCD i % 8
 // (CU masks number the CUs round-robin over the XCDs).
-struct PipeRes {
+struct gdn_context {
     static constexpr int MAX_SEG = 16;
     std::mutex use;  // held while one call enqueues its pipeline: the events are reused by every call
     int dev = -1;
-    uint8_t chain_cus[8] = {0, 0, 0, 0, 0, 0, 0, 0};  // CUs of each XCD reserved for the chain
+    int32_t chain_cus = 0;  // CUs of each XCD reserved for the chain
     hipStream_t chain_s = nullptr, intra_s = nullptr, out_s = nullptr;
-    hipEvent_t start, intra_done[MAX_SEG], chain_done[MAX_SEG], intra_end, out_end;
-    bool ok = false;
+    hipEvent_t start = nullptr, intra_end = nullptr, out_end = nullptr;
+    hipEvent_t intra_done[MAX_SEG] = {}, chain_done[MAX_SEG] = {};
 };
 
-// chain_cus[x]: workgroups of the chain that run on XCD x (<= 32 each)
-static hipError_t pipe_res(const uint8_t* chain_cus, PipeRes** out)
+namespace gdn {
+
+// Releases whatever part of the context exists (streams are waited for first).
+static hipError_t context_release(gdn_context* r)
 {
-    static std::mutex mu;
-    static PipeRes res[32];
+    hipError_t first = hipSuccess;
+    auto keep = [&](hipError_t e) {
+        if (first == hipSuccess && e != hipSuccess) first = e;
+    };
+    for (hipStream_t s : {r->chain_s, r->intra_s, r->out_s})
+        if (s) keep(hipStreamSynchronize(s));
+    hipEvent_t* evs[] = {&r->start, &r->intra_end, &r->out_end};
+    for (hipEvent_t* ev : evs)
+        if (*ev) keep(hipEventDestroy(*ev));
+    for (int i = 0; i < gdn_context::MAX_SEG; ++i) {
+        if (r->intra_done[i]) keep(hipEventDestroy(r->intra_done[i]));
+        if (r->chain_done[i]) keep(hipEventDestroy(r->chain_done[i]));
+    }
+    for (hipStream_t s : {r->chain_s, r->intra_s, r->out_s})
+        if (s) keep(hipStreamDestroy(s));
+    delete r;
+    return first;
+}
+
+hipError_t context_create(int32_t chain_cus_per_xcd, gdn_context** out)
+{
+    *out = nullptr;
+    const int32_t per_xcd = chain_cus_per_xcd > 0 ? chain_cus_per_xcd : kDefaultChainCus;
+    if (per_xcd > 31) return hipErrorInvalidValue;
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    std::lock_guard<std::mutex> lock(mu);
-    PipeRes* r = nullptr;
-    for (PipeRes& c : res) {
-        if (c.ok && c.dev == dev && memcmp(c.chain_cus, chain_cus, 8) == 0) {
-            *out = &c;
-            return hipSuccess;
-        }
-        if (!c.ok && !r) r = &c;
-    }
-    if (!r) return hipErrorOutOfMemory;  // too many distinct splits: the caller runs unpipelined
     int cus = 0;
     if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    gdn_context* r = new (std::nothrow) gdn_context;
+    if (!r) return hipErrorOutOfMemory;
+    r->dev = dev;
+    r->chain_cus = per_xcd;
+    auto fail = [&](hipError_t err) {
+        (void)context_release(r);  // frees what was created before the failure
+        return err;
+    };
     if (cus == 256) {
         uint32_t mine[8] = {0, 0, 0, 0, 0, 0, 0, 0}, rest[8];
         for (int x = 0; x < 8; ++x)
-            for (int c = 0; c < chain_cus[x]; ++c) {
+            for (int c = 0; c < per_xcd; ++c) {
                 const int bit = x + 8 * c;
                 mine[bit >> 5] |= 1u << (bit & 31);
             }
         for (int w = 0; w < 8; ++w) rest[w] = ~mine[w];
-        if ((e = hipExtStreamCreateWithCUMask(&r->chain_s, 8, mine)) != hipSuccess) return e;
-        if ((e = hipExtStreamCreateWithCUMask(&r->intra_s, 8, rest)) != hipSuccess) return e;
-        if ((e = hipExtStreamCreateWithCUMask(&r->out_s, 8, rest)) != hipSuccess) return e;
+        if ((e = hipExtStreamCreateWithCUMask(&r->chain_s, 8, mine)) != hipSuccess) return fail(e);
+        if ((e = hipExtStreamCreateWithCUMask(&r->intra_s, 8, rest)) != hipSuccess) return fail(e);
+        if ((e = hipExtStreamCreateWithCUMask(&r->out_s, 8, rest)) != hipSuccess) return fail(e);
     } else {
-        if ((e = hipStreamCreateWithFlags(&r->chain_s, hipStreamNonBlocking)) != hipSuccess) return e;
-        if ((e = hipStreamCreateWithFlags(&r->intra_s, hipStreamNonBlocking)) != hipSuccess) return e;
-        if ((e = hipStreamCreateWithFlags(&r->out_s, hipStreamNonBlocking)) != hipSuccess) return e;
+        if ((e = hipStreamCreateWithFlags(&r->chain_s, hipStreamNonBlocking)) != hipSuccess) return fail(e);
+        if ((e = hipStreamCreateWithFlags(&r->intra_s, hipStreamNonBlocking)) != hipSuccess) return fail(e);
+        if ((e = hipStreamCreateWithFlags(&r->out_s, hipStreamNonBlocking)) != hipSuccess) return fail(e);
     }
     hipEvent_t* evs[] = {&r->start, &r->intra_end, &r->out_end};
     for (hipEvent_t* ev : evs)
-        if ((e = hipEventCreateWithFlags(ev, hipEventDisableTiming)) != hipSuccess) return e;
-    for (int i = 0; i < PipeRes::MAX_SEG; ++i) {
-        if ((e = hipEventCreateWithFlags(&r->intra_done[i], hipEventDisableTiming)) != hipSuccess) return e;
-        if ((e = hipEventCreateWithFlags(&r->chain_done[i], hipEventDisableTiming)) != hipSuccess) return e;
+        if ((e = hipEventCreateWithFlags(ev, hipEventDisableTiming)) != hipSuccess) return fail(e);
+    for (int i = 0; i < gdn_context::MAX_SEG; ++i) {
+        if ((e = hipEventCreateWithFlags(&r->intra_done[i], hipEventDisableTiming)) != hipSuccess) return fail(e);
+        if ((e = hipEventCreateWithFlags(&r->chain_done[i], hipEventDisableTiming)) != hipSuccess) return fail(e);
     }
-    r->dev = dev;
-    memcpy(r->chain_cus, chain_cus, 8);
-    r->ok = true;
     *out = r;
     return hipSuccess;
 }
 
-// Raises a kernel's dynamic-LDS limit once per (kernel, device): the attribute
-// belongs to the device that is current, and first callers racing on one
-// device both store the same value.
-constexpr int kMaxDevices = 64;
-struct SmemAttr {
-    std::atomic<bool> done[kMaxDevices]{};
-};
-static hipError_t ensure_smem(SmemAttr& at, const void* fn, int bytes)
+hipError_t context_destroy(gdn_context* ctx) { return context_release(ctx); }
+
+int context_device(const gdn_context* ctx) { return ctx->dev; }
+
+// Raises a kernel's dynamic-LDS limit to what this launch uses.  Set on every
+// launch that needs more than the default 64 KB (a host-side attribute of the
+// kernel on the current device, idempotent, not a stream operation, so it is
+// also legal while the stream is being captured); nothing is cached.
+static hipError_t lds_limit(const void* fn, size_t bytes)
 {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    const bool cached = dev >= 0 && dev < kMaxDevices;
-    if (cached && at.done[dev].load(std::memory_order_acquire)) return hipSuccess;
-    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-    if (e == hipSuccess && cached) at.done[dev].store(true, std::memory_order_release);
-    return e;
+    if (bytes <= 64 * 1024) return hipSuccess;
+    return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
 template <typename TIn, int C, int DK, int DV>
@@ -1920,8 +1936,7 @@ static hipError_t run_prefill(const PrefillArgs& a)
         if (c1 <= c0) return hipSuccess;
         size_t smem = sizeof(IntraSmem<TIn, C, DK, DV>);
         if constexpr (sizeof(TIn) == 2 && C == 64) smem = sizeof(IntraBfSmem<DK, DV>);
-        static SmemAttr attr;
-        const hipError_t e = ensure_smem(attr, (const void*)intra_kernel<TIn, C, DK, DV>, (int)smem);
+        const hipError_t e = lds_limit((const void*)intra_kernel<TIn, C, DK, DV>, smem);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL((intra_kernel<TIn, C, DK, DV>), dim3((uint32_t)(c1 - c0), a.H), dim3(256), smem,
                            st, (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, a.g, a.beta, header, tab, varlen,
@@ -1935,8 +1950,7 @@ static hipError_t run_prefill(const PrefillArgs& a)
         const bool seg = !(c0 == 0 && c1 == ALL);
         const void* fn = seg ? (const void*)chain_kernel<TIn, C, DK, DV, NW, true>
                              : (const void*)chain_kernel<TIn, C, DK, DV, NW, false>;
-        static SmemAttr attr[2];
-        const hipError_t e = ensure_smem(attr[seg], fn, (int)sizeof(Lds));
+        const hipError_t e = lds_limit(fn, sizeof(Lds));
         if (e != hipSuccess) return e;
         const dim3 grid((uint32_t)chain_blocks), block((NW + chain_loaders<TIn, C>()) * 64);
         if (seg)
@@ -1955,8 +1969,7 @@ static hipError_t run_prefill(const PrefillArgs& a)
         const size_t smem = OutCfg<TIn, C, DK, DV>::lds_bytes(gated);
         const void* fn = gated ? (const void*)output_kernel<TIn, C, DK, DV, true>
                                : (const void*)output_kernel<TIn, C, DK, DV, false>;
-        static SmemAttr attr[2];
-        const hipError_t e = ensure_smem(attr[gated], fn, (int)smem);
+        const hipError_t e = lds_limit(fn, smem);
         if (e != hipSuccess) return e;
         const dim3 grid((uint32_t)(c1 - c0), a.H);
         if (gated)
@@ -1982,18 +1995,23 @@ static hipError_t run_prefill(const PrefillArgs& a)
     }
 
     // The state chain keeps only (sequences x heads x d_v/16) workgroups busy.
-    // When they fit on half of every XCD and every stage runs in this call, the
-    // chunks are cut into segments and pipelined: the chain of segment s runs
-    // on its own half of the CUs while the intra-chunk kernel prepares later
-    // segments and the output kernel finishes earlier ones on the other half;
-    // events order each segment's three kernels.
+    // With an execution context whose chain reservation holds them (the
+    // pairs p with p % 8 == x, TILES each, on XCD x), when every stage runs in
+    // this call, the chunks are cut into segments and pipelined: the chain of
+    // segment s runs on the context's CU-masked chain stream while the
+    // intra-chunk kernel prepares later segments and the output kernel
+    // finishes earlier ones on the other CUs; events order each segment's
+    // three kernels.  The kernels and their arguments are the same either way,
+    // so the results are too.
     // The hand-offs between the pipeline streams cost about 0.14 ms per call
     // (measured: 8K tokens 0.38 ms pipelined against 0.24 ms stage by stage),
     // which the overlap repays only past about 36K tokens of one sequence
     // (32K: 1.07 against 1.04 ms; 40K: 1.26 against 1.30 ms).
     constexpr int64_t PIPE_MIN_CHUNKS = 576, GEOM_MIN_CHUNKS = 768;
+    const int64_t chain_per_xcd = ((pairs + 7) / 8) * (DV / 16);
+    gdn_context* pr = a.ctx;
     int nseg = 1;
-    if (a.stages == 7 && chain_blocks <= 128 && grid_chunks >= PIPE_MIN_CHUNKS)
+    if (pr && a.stages == 7 && chain_per_xcd <= pr->chain_cus && grid_chunks >= PIPE_MIN_CHUNKS)
         nseg = (grid_chunks >= GEOM_MIN_CHUNKS && !a.norm.z) ? 6 : 4;
     if (nseg == 1) {
         if (a.stages & 1) GDN_TRY(launch_intra(0, grid_chunks, a.stream));
@@ -2001,24 +2019,7 @@ static hipError_t run_prefill(const PrefillArgs& a)
         if (a.stages & 4) GDN_TRY(launch_output(0, grid_chunks, a.stream));
         return hipSuccess;
     }
-    // CUs of every XCD for the chain: as many as its most loaded XCD has
-    // workgroups (the pairs p with p % 8 == x, TILES each).  The same count on
-    // every XCD: with unequal per-XCD masks the workgroups are no longer dealt
-    // round-robin over the XCDs, and a pair's row tiles pile up on a few CUs.
-    uint8_t chain_cus[8];
-    {
-        const int64_t most = ((pairs + 7) / 8) * (DV / 16);
-        for (int x = 0; x < 8; ++x) chain_cus[x] = (uint8_t)most;
-    }
-    PipeRes* pr = nullptr;
-    if (pipe_res(chain_cus, &pr) != hipSuccess) pr = nullptr;
-    if (!pr) {  // no pipeline streams: stage by stage on the caller's stream
-        GDN_TRY(launch_intra(0, grid_chunks, a.stream));
-        GDN_TRY(launch_chain(0, ALL, a.stream));
-        GDN_TRY(launch_output(0, grid_chunks, a.stream));
-        return hipSuccess;
-    }
-    // One call at a time records and waits on this device's pipeline events.
+    // One call at a time records and waits on the context's events.
     std::lock_guard<std::mutex> pipe_lock(pr->use);
     // Segment sizes.  From 768 chunks on, six segments in the ratio
     // 1 : 2 : 4 : 4 : 2 : 1: the first preparation and the last outputs, which
@@ -2029,7 +2030,7 @@ static hipError_t run_prefill(const PrefillArgs& a)
     // finish a large middle segment under the next, shorter chain segment
     // (2.01 against 1.93 ms at 64K).
     static constexpr int kGeom[6] = {1, 2, 4, 4, 2, 1};
-    int64_t bounds[PipeRes::MAX_SEG + 1];
+    int64_t bounds[gdn_context::MAX_SEG + 1];
     {
         const int sum = nseg == 6 ? 14 : nseg;
         int acc = 0;

@@ -25,6 +25,7 @@ STAGE_PREPARE, STAGE_PROPAGATE, STAGE_OUTPUT, STAGE_ALL = 1, 2, 4, 7
 STATUS = {
     0: "GDN_OK", 1: "GDN_ERR_NULL_ARG", 2: "GDN_ERR_BAD_SHAPE", 3: "GDN_ERR_UNSUPPORTED",
     4: "GDN_ERR_BAD_SEQLENS", 5: "GDN_ERR_ALIGNMENT", 6: "GDN_ERR_WORKSPACE", 7: "GDN_ERR_LAUNCH",
+    8: "GDN_ERR_CONTEXT",
 }
 
 _lock = threading.Lock()
@@ -57,12 +58,20 @@ def load_library(path: str | None = None):
             lib.gdn_chunk_prefill_staged.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32,
                                                      ctypes.c_int, f32, i32, vp, vp, vp, sz, i32, vp]
             lib.gdn_chunk_prefill_staged.restype = ctypes.c_int
+            lib.gdn_context_create.argtypes = [i32, ctypes.POINTER(vp)]
+            lib.gdn_context_create.restype = ctypes.c_int
+            lib.gdn_context_destroy.argtypes = [vp]
+            lib.gdn_context_destroy.restype = ctypes.c_int
+            lib.gdn_chunk_prefill_ctx.argtypes = [vp] + lib.gdn_chunk_prefill.argtypes
+            lib.gdn_chunk_prefill_ctx.restype = ctypes.c_int
             lib.gdn_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int, f32, i32,
                                             vp, vp]
             lib.gdn_decode_step.restype = ctypes.c_int
             lib.gdn_chunk_prefill_gated.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32,
                                                     ctypes.c_int, f32, i32, vp, vp, f32, vp, vp, vp, sz, vp]
             lib.gdn_chunk_prefill_gated.restype = ctypes.c_int
+            lib.gdn_chunk_prefill_gated_ctx.argtypes = [vp] + lib.gdn_chunk_prefill_gated.argtypes
+            lib.gdn_chunk_prefill_gated_ctx.restype = ctypes.c_int
             lib.gdn_decode_step_gated.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int, f32,
                                                   i32, vp, vp, f32, vp, vp]
             lib.gdn_decode_step_gated.restype = ctypes.c_int
@@ -84,6 +93,47 @@ def load_library(path: str | None = None):
             lib.gdn_version.restype = i32
             _lib = lib
     return _lib
+
+
+class Context:
+    """Execution context of the overlapped prefill (gdn_context_create): the
+    streams and events that let one ``chunk_prefill(..., ctx=...)`` call overlap
+    its three stages.  Created on the current device; ``close()`` (or leaving a
+    ``with`` block) waits for its streams and releases them.  Results with and
+    without a context are bit-identical."""
+
+    def __init__(self, chain_cus_per_xcd: int = 0):
+        lib = load_library()
+        h = ctypes.c_void_p()
+        st = lib.gdn_context_create(int(chain_cus_per_xcd), ctypes.byref(h))
+        if st != 0:
+            raise GdnError(st, "gdn_context_create")
+        self._h = h
+
+    @property
+    def handle(self):
+        if self._h is None:
+            raise ValueError("the context is closed")
+        return self._h
+
+    def close(self):
+        h, self._h = getattr(self, "_h", None), None
+        if h is not None and h.value:
+            st = load_library().gdn_context_destroy(h)
+            if st != 0:
+                raise GdnError(st, "gdn_context_destroy")
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def _torch():
@@ -144,7 +194,7 @@ def _norm_args(gate, norm_weight, shape, dt, dev):
 
 def chunk_prefill(q, k, v, g, beta, init_state=None, cu_seqlens=None, scale=None, qk_l2norm=True, chunk=64,
                   out=None, final_state=None, workspace=None, return_final_state=True, stages=STAGE_ALL,
-                  gate=None, norm_weight=None, norm_eps=DEFAULT_NORM_EPS):
+                  gate=None, norm_weight=None, norm_eps=DEFAULT_NORM_EPS, ctx=None):
     """Chunked gated delta-rule prefill over packed sequences.
 
     q, k [T, H, dk]; v [T, H, dv] (bf16 or fp32, same dtype); g, beta [T, H] fp32;
@@ -154,7 +204,8 @@ def chunk_prefill(q, k, v, g, beta, init_state=None, cu_seqlens=None, scale=None
     all three; see include/gdn.h); a later stage must get the workspace of the earlier
     ones on the same inputs.  With ``gate`` [T, H, dv] (dtype of q) the outputs get the
     gated RMSNorm read-out of App. A.3 Eq. 20 (``norm_weight`` [dv] fp32 or None,
-    ``norm_eps``); it needs all stages in one call.
+    ``norm_eps``); it needs all stages in one call.  ``ctx`` (a ``Context``) lets a
+    whole-prefill call overlap its stages on the context's streams.
     """
     torch = _torch()
     lib = load_library()
@@ -207,20 +258,28 @@ def chunk_prefill(q, k, v, g, beta, init_state=None, cu_seqlens=None, scale=None
         if stages != STAGE_ALL:
             raise ValueError("the gated read-out needs all stages in one call")
         _norm_args(gate, norm_weight, (T, H, dv), dt, dev)
-        st = lib.gdn_chunk_prefill_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(init_state),
-                                         _ptr(cu_dev), cu_host_ptr, N, T, H, dk, dv, chunk, code, s,
-                                         int(bool(qk_l2norm)), _ptr(gate), _ptr(norm_weight), float(norm_eps),
-                                         _ptr(out), _ptr(final_state), _ptr(workspace), workspace.numel(),
-                                         _stream(dev))
+        st = lib.gdn_chunk_prefill_gated_ctx(None if ctx is None else ctx.handle, _ptr(q), _ptr(k), _ptr(v),
+                                             _ptr(g), _ptr(beta), _ptr(init_state), _ptr(cu_dev), cu_host_ptr, N, T,
+                                             H, dk, dv, chunk, code, s, int(bool(qk_l2norm)), _ptr(gate),
+                                             _ptr(norm_weight), float(norm_eps), _ptr(out), _ptr(final_state),
+                                             _ptr(workspace), workspace.numel(), _stream(dev))
         if st != 0:
-            raise GdnError(st, "gdn_chunk_prefill_gated")
+            raise GdnError(st, "gdn_chunk_prefill_gated_ctx")
+        return out, final_state
+    if stages == STAGE_ALL:
+        st = lib.gdn_chunk_prefill_ctx(None if ctx is None else ctx.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                       _ptr(beta), _ptr(init_state), _ptr(cu_dev), cu_host_ptr, N, T, H, dk, dv,
+                                       chunk, code, s, int(bool(qk_l2norm)), _ptr(out), _ptr(final_state),
+                                       _ptr(workspace), workspace.numel(), _stream(dev))
+        if st != 0:
+            raise GdnError(st, "gdn_chunk_prefill_ctx")
         return out, final_state
     st = lib.gdn_chunk_prefill_staged(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(init_state),
                                       _ptr(cu_dev), cu_host_ptr, N, T, H, dk, dv, chunk, code, s,
                                       int(bool(qk_l2norm)), _ptr(out), _ptr(final_state), _ptr(workspace),
                                       workspace.numel(), int(stages), _stream(dev))
     if st != 0:
-        raise GdnError(st, "gdn_chunk_prefill")
+        raise GdnError(st, "gdn_chunk_prefill_staged")
     return out, final_state
 
 

@@ -23,14 +23,16 @@
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers unless the name ends in _host.
  *   - The caller owns and allocates every buffer (including the workspace);
- *     the library never allocates device memory.  Its only process-wide
- *     state: per device, the three streams and the events of the pipelined
- *     prefill (created by the first prefill long enough to use them, kept
- *     until the process ends), and the kernels' LDS limits, raised once per
- *     device.  Calls that share those streams enqueue one at a time.
- *   - Work is enqueued on `stream` and runs asynchronously; no call
- *     synchronises the device (unless GDN_DEBUG_SYNC=1 is set, which makes
- *     each call wait for its kernels and report launch/device errors).
+ *     the library never allocates device memory and keeps no process-wide
+ *     state.  The only HIP objects it creates are those of an execution
+ *     context (gdn_context_create), which the caller owns and destroys.
+ *   - Work is enqueued on `stream` (and, for the _ctx calls, on the streams
+ *     of the context, forked from and joined back to `stream`) and runs
+ *     asynchronously; no call synchronises the device (unless
+ *     GDN_DEBUG_SYNC=1 is set, which makes each call wait for its kernels and
+ *     report launch/device errors).  Every call may be captured into a HIP
+ *     graph, the first one included: nothing a call enqueues is a memset, a
+ *     copy or a synchronisation.
  *   - Argument errors are detected on the host before anything is launched
  *     and returned as a gdn_status; nothing is written in that case.
  *   - Results are deterministic: no atomics, fixed reduction order.
@@ -56,7 +58,8 @@ typedef enum {
     GDN_ERR_BAD_SEQLENS = 4,  /* cu_seqlens not 0 = c_0 <= c_1 <= ... <= c_N = total_tokens  */
     GDN_ERR_ALIGNMENT = 5,    /* q/k/v/o/state not 16-byte, g/beta not 4-byte aligned       */
     GDN_ERR_WORKSPACE = 6,    /* workspace NULL or smaller than gdn_prefill_workspace_size */
-    GDN_ERR_LAUNCH = 7        /* a kernel launch failed (or, under GDN_DEBUG_SYNC, faulted) */
+    GDN_ERR_LAUNCH = 7,       /* a kernel launch failed (or, under GDN_DEBUG_SYNC, faulted) */
+    GDN_ERR_CONTEXT = 8       /* context creation failed, or the context belongs to another device */
 } gdn_status;
 
 /* Element type of q, k, v and o.  Gates, beta and states are always fp32. */
@@ -147,6 +150,51 @@ gdn_status gdn_chunk_prefill_staged(const void* q, const void* k, const void* v,
                                     size_t workspace_bytes, int32_t stages, hipStream_t stream);
 
 /*
+ * Execution context of the overlapped (pipelined) prefill.  Opaque and owned
+ * by the caller, like a library handle: gdn_context_create makes, on the
+ * device that is current, the streams and events that let one prefill call
+ * overlap its three stages -- one stream for the sequential state chain,
+ * CU-masked to `chain_cus_per_xcd` compute units of every XCD (the chain of
+ * the 64K-token workload, B=1, H=6, d=256, needs 16), and two streams for the
+ * per-chunk preparation and output kernels on the other CUs -- and
+ * gdn_context_destroy waits for the context's streams and releases them.
+ *
+ *   chain_cus_per_xcd  CUs reserved for the chain on each XCD, 1..31; 0 or
+ *                      less selects the default (16).  On a device that is not
+ *                      a 256-CU MI355X the streams are created without masks.
+ *
+ * A context serves calls on its own device only (GDN_ERR_CONTEXT otherwise);
+ * calls that share a context are ordered on the host by a lock inside it
+ * (they may come from several threads).  It must not be destroyed while a
+ * call that uses it is being enqueued or captured, nor while a captured graph
+ * that contains its streams' work is still to be replayed.
+ * Errors: GDN_ERR_NULL_ARG (ctx == NULL), GDN_ERR_BAD_SHAPE
+ * (chain_cus_per_xcd > 31), GDN_ERR_CONTEXT (a stream or event could not be
+ * created; nothing is left allocated).
+ */
+typedef struct gdn_context* gdn_context_t;
+gdn_status gdn_context_create(int32_t chain_cus_per_xcd, gdn_context_t* ctx);
+gdn_status gdn_context_destroy(gdn_context_t ctx);
+
+/*
+ * gdn_chunk_prefill with an execution context: when the sequences' state
+ * chains fit in the context's CU reservation and the batch is long enough for
+ * the overlap to pay (at least 576 chunks), the chunks are cut into segments
+ * and the chain of each segment runs on the context's chain stream while the
+ * preparation of later segments and the outputs of earlier ones run beside
+ * it; otherwise, and with ctx == NULL, it is exactly gdn_chunk_prefill.  The
+ * results are bit-identical to gdn_chunk_prefill's either way.  The context's
+ * streams wait for `stream` on entry and `stream` waits for them before the
+ * call's last kernel, so the call is ordered on `stream` like any other.
+ */
+gdn_status gdn_chunk_prefill_ctx(gdn_context_t ctx, const void* q, const void* k, const void* v, const float* g,
+                                 const float* beta, const float* init_state, const int32_t* cu_seqlens,
+                                 const int32_t* cu_seqlens_host, int32_t num_seqs, int64_t total_tokens, int32_t H,
+                                 int32_t dk, int32_t dv, int32_t chunk, gdn_dtype dt, float scale,
+                                 int32_t qk_l2norm, void* o, float* final_state, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
+
+/*
  * One recurrent decode step for N independent sequences (the token-level
  * recurrence above with one token per sequence; the serving form of the
  * fixed-size state described in App. A.3 and the HyLo-Qwen GDN model card).
@@ -190,6 +238,15 @@ gdn_status gdn_chunk_prefill_gated(const void* q, const void* k, const void* v, 
                                    int32_t qk_l2norm, const void* gate, const float* norm_weight, float norm_eps,
                                    void* o, float* final_state, void* workspace, size_t workspace_bytes,
                                    hipStream_t stream);
+
+/* gdn_chunk_prefill_gated with an execution context (see gdn_chunk_prefill_ctx). */
+gdn_status gdn_chunk_prefill_gated_ctx(gdn_context_t ctx, const void* q, const void* k, const void* v,
+                                       const float* g, const float* beta, const float* init_state,
+                                       const int32_t* cu_seqlens, const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                       int64_t total_tokens, int32_t H, int32_t dk, int32_t dv, int32_t chunk,
+                                       gdn_dtype dt, float scale, int32_t qk_l2norm, const void* gate,
+                                       const float* norm_weight, float norm_eps, void* o, float* final_state,
+                                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 gdn_status gdn_decode_step_gated(const void* q, const void* k, const void* v, const float* g, const float* beta,
                                  float* state, int32_t N, int32_t H, int32_t dk, int32_t dv, gdn_dtype dt,

@@ -20,6 +20,7 @@ import ctypes
 import os
 import subprocess
 import threading
+import time
 
 import numpy as np
 
@@ -101,7 +102,7 @@ def default_threads() -> int:
 
 
 def prefill(q, k, v, g, beta, init_state=None, cu_seqlens=None, scale=None, qk_l2norm=True,
-            eps=DEFAULT_EPS, rows=None, bf16=False, n_threads=None, mutation=0):
+            eps=DEFAULT_EPS, rows=None, bf16=False, n_threads=None, mutation=0, timing=None):
     """Sequential fp64 gated delta rule over packed sequences.
 
     q, k: [T, H, dk]; v: [T, H, dv]; g, beta: [T, H] (g is the log forget gate,
@@ -110,6 +111,9 @@ def prefill(q, k, v, g, beta, init_state=None, cu_seqlens=None, scale=None, qk_l
     rows: optional list of state rows (value indices) to evaluate; other
     entries of the returned o / final_state are NaN.
     Returns (o [T, H, dv] fp64, final_state [N, H, dv, dk] fp64).
+    ``timing``: optional dict; its "seconds" is set to the wall time of the
+    oracle's own computation (the C call alone: argument checks, allocation of
+    the outputs and conversions happen outside the timed region).
     """
     q = np.ascontiguousarray(q)
     k = np.ascontiguousarray(k)
@@ -144,13 +148,16 @@ def prefill(q, k, v, g, beta, init_state=None, cu_seqlens=None, scale=None, qk_l
     o = np.full((T, H, dv), fill, dtype=np.float64)
     fs = np.full((N, H, dv, dk), fill, dtype=np.float64)
     lib = _load()
-    rc = lib.oracle_prefill_f64(
-        _ptr(q), _ptr(k), _ptr(v), _code(q, bf16),
-        _ptr(g), _ptr(beta), _code(g, False),
-        _ptr(init_state), _code(init_state, False) if init_state is not None else OR_F64,
-        _ptr(cu), N, H, dk, dv, float(scale), int(bool(qk_l2norm)), float(eps),
-        _ptr(r), 0 if r is None else int(r.shape[0]),
-        _ptr(o), _ptr(fs), int(n_threads or default_threads()), int(mutation))
+    args = (_ptr(q), _ptr(k), _ptr(v), _code(q, bf16),
+            _ptr(g), _ptr(beta), _code(g, False),
+            _ptr(init_state), _code(init_state, False) if init_state is not None else OR_F64,
+            _ptr(cu), N, H, dk, dv, float(scale), int(bool(qk_l2norm)), float(eps),
+            _ptr(r), 0 if r is None else int(r.shape[0]),
+            _ptr(o), _ptr(fs), int(n_threads or default_threads()), int(mutation))
+    t0 = time.perf_counter()
+    rc = lib.oracle_prefill_f64(*args)
+    if timing is not None:
+        timing["seconds"] = time.perf_counter() - t0
     if rc != 0:
         raise RuntimeError("oracle_prefill_f64 rejected its arguments")
     return o, fs

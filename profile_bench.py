@@ -100,12 +100,9 @@ def finished(d):
 
 
 def profiler_ok(rc, d, result_suffix):
-    """rocprofv3 can itself segfault while tearing down after the program has
-    finished and its output is complete; that exit is accepted when the
-    program's last line was printed and the result file exists."""
-    if find(d, result_suffix) is None or not finished(d):
-        return False
-    return rc == 0 or rc in (-11, 139)
+    """The profiled program exited 0, printed its last line, and the result
+    file exists.  Any other exit, the profiler's own included, is a failure."""
+    return rc == 0 and find(d, result_suffix) is not None and finished(d)
 
 
 def mode_trace():

@@ -122,6 +122,26 @@ def test_decode_host_validation(lib):
     assert call(o=_fake(0x10008)) == 5
 
 
+def test_context_entry_points_check_arguments(lib):
+    """gdn_context_create / gdn_context_destroy check their arguments before any
+    HIP call; without a GPU, creation fails cleanly (GDN_ERR_CONTEXT) and leaves
+    the handle NULL.  gdn_chunk_prefill_ctx validates like gdn_chunk_prefill."""
+    h = ctypes.c_void_p()
+    assert lib.gdn_context_create(0, None) == 1                # GDN_ERR_NULL_ARG
+    assert lib.gdn_context_create(32, ctypes.byref(h)) == 2    # more CUs than an XCD has
+    assert lib.gdn_context_destroy(None) == 1
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        assert lib.gdn_context_create(0, ctypes.byref(h)) == 8  # GDN_ERR_CONTEXT
+        assert h.value is None
+    f = _fake()
+    ctx_call = lambda **kw: lib.gdn_chunk_prefill_ctx(None, f, f, f, f, f, None, None, None, 1, 128, 2,
+                                                      kw.get("dk", 64), 64, 64, gdn.GDN_BF16, -1.0, 1, f, None,
+                                                      kw.get("ws", _fake(0x100000)), 1 << 40, None)
+    assert ctx_call(dk=48) == 3
+    assert ctx_call(ws=None) == 6
+
+
 def test_binding_refuses_cpu_tensors():
     torch = pytest.importorskip("torch")
     q = torch.zeros(4, 1, 16)

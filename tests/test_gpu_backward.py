@@ -3,11 +3,10 @@
 seeded inputs and cotangents.
 
 The kernels compute in fp32 throughout (bf16 inputs are widened exactly), so
-the bound is an fp32 one: max|gpu - oracle| / rms(oracle) <= TOL_BWD = 2e-4 per
-gradient tensor, about 3000 fp32 ulps, left for the chunked evaluation's
-longer dependency chains (the inverse T = (I + A)^{-1}, sums over 64-256
-terms, and the two state recurrences over up to 32 chunks here).  The
-measured errors are 1e-6 to 3e-5."""
+the bound is the fp32 one of the forward path: max|gpu - oracle| / rms(oracle)
+<= TOL_BWD = 1e-4 per gradient tensor.  The measured errors are 1e-6 to 7e-5
+(the largest on the longest dependency chains: the inverse
+T = (I + A)^{-1}, sums over 64-256 terms and the two state recurrences)."""
 import numpy as np
 import pytest
 
@@ -20,7 +19,7 @@ import oracle  # noqa: E402
 from hybrid_linear_attention_delta_amd import gdn, synth  # noqa: E402
 
 DEV = "cuda:0"
-TOL_BWD = 2e-4
+TOL_BWD = 1e-4
 NAMES = ("dq", "dk", "dv", "dg", "dbeta", "dinit")
 
 
@@ -160,3 +159,25 @@ def test_backward_64k_last_two_chunks_of_every_head():
     print("  " + "  ".join(f"{n} {e:.2e}" for n, e in errs.items()), flush=True)
     for name, e in errs.items():
         assert e <= TOL_BWD, (name, e)
+
+
+def test_invalid_device_seqlens_raise_the_flag():
+    """The backward with invalid cu_seqlens on the device only: its chunk table
+    raises the error flag (workspace header word 0) and publishes zero chunks,
+    so no per-chunk kernel runs and no access leaves its buffer (the call
+    completes; the gradients are unspecified)."""
+    T, H, d = 130, 2, 64
+    cu = np.array([0, 70, 130], dtype=np.int64)
+    inp = synth.prefill_inputs(T, H, d, d, "bf16", seed=4141, cu_seqlens=cu)
+    do, ds = synth.backward_cotangents(T, H, d, d, 2, "bf16", 4141)
+    t = lambda a, b=False: synth.to_torch(a, DEV, bf16=b)
+    ws = torch.empty(gdn.prefill_backward_workspace_size(T, 2, H, d, d), dtype=torch.uint8, device=DEV)
+    for bad in ([0, 90, 60], [0, 70, 129], [1, 70, 130]):
+        print(f"  invalid device cu_seqlens {bad}", flush=True)
+        ws.fill_(0)
+        gdn.chunk_prefill_backward(t(inp.q, True), t(inp.k, True), t(inp.v, True), t(inp.g), t(inp.beta),
+                                   t(do, True), dstate=t(ds), workspace=ws,
+                                   cu_seqlens=torch.tensor(bad, dtype=torch.int32, device=DEV))
+        torch.cuda.synchronize()
+        hdr = ws[:8].view(torch.int32).cpu().tolist()
+        assert hdr == [1, 0], (bad, hdr)

@@ -132,5 +132,8 @@ def test_decode_steps_in_a_hip_graph_match_eager():
 @pytest.mark.parametrize("N,dk,dv", [(1, 256, 256), (1000, 128, 256), (3, 64, 512)])
 def test_decode_odd_batch_sizes(N, dk, dv):
     """One sequence, a thousand, and a few with d_v = 8 d_k: every state row of
-    every (sequence, head) pair is updated and read out."""
-    _run_decode(N, 2, dk, dv, "bf16", 3, seed=N + dk + dv)
+    every (sequence, head) pair is updated and read out, and every output and
+    the final state of every pair match the oracle."""
+    eo, es = _run_decode(N, 2, dk, dv, "bf16", 3, seed=N + dk + dv)
+    print(f"decode N={N} dk={dk} dv={dv}: o err {eo:.3e} (bound {TOL_BF16}), state err {es:.3e}")
+    assert eo <= TOL_BF16 and es <= TOL_BF16, (eo, es)

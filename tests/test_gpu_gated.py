@@ -62,16 +62,20 @@ def test_prefill_gated_matches_oracle(dtype, T, H, dk, dv, C, lens, use_w, eps):
 
 
 def test_prefill_gated_pipelined_equals_oracle():
-    """A long sequence (past the pipeline's 576-chunk threshold) takes the
-    segmented (pipelined) path; the epilogue runs in every segment's output
-    launch."""
+    """A long sequence (past the pipeline's 576-chunk threshold) with an
+    execution context takes the segmented (pipelined) path; the epilogue runs in
+    every segment's output launch.  The same call without a context (one
+    stream, stage by stage) gives the same bits."""
     T, H, d = 37000, 2, 256
     inp = synth.prefill_inputs(T, H, d, d, "bf16", seed=977, gate="slow")
     z, w = synth.norm_inputs((T, H, d), "bf16", 977)
     t = lambda a, b=False: synth.to_torch(a, DEV, bf16=b)
-    o, _ = gdn.chunk_prefill(t(inp.q, True), t(inp.k, True), t(inp.v, True), t(inp.g), t(inp.beta),
-                             gate=t(z, True), norm_weight=t(w), norm_eps=1e-6)
-    torch.cuda.synchronize()
+    args = (t(inp.q, True), t(inp.k, True), t(inp.v, True), t(inp.g), t(inp.beta))
+    with gdn.Context() as c:
+        o, _ = gdn.chunk_prefill(*args, gate=t(z, True), norm_weight=t(w), norm_eps=1e-6, ctx=c)
+        o1, _ = gdn.chunk_prefill(*args, gate=t(z, True), norm_weight=t(w), norm_eps=1e-6)
+        torch.cuda.synchronize()
+    assert torch.equal(o, o1)
     rows = [0, 77, 255]
     o_ref, _ = oracle.prefill(inp.q, inp.k, inp.v, inp.g, inp.beta, bf16=True)
     y_ref = oracle.gated_rmsnorm(o_ref, z, w, eps=1e-6, bf16=True)

@@ -19,7 +19,15 @@ from hybrid_linear_attention_delta_amd import gdn, synth  # noqa: E402
 DEV = "cuda:0"
 
 
-def _gpu(inp, chunk, init=None, scale=None, l2=True, varlen=True):
+@pytest.fixture(scope="module")
+def ctx():
+    """One execution context for the calls that take the pipelined path."""
+    c = gdn.Context()
+    yield c
+    c.close()
+
+
+def _gpu(inp, chunk, init=None, scale=None, l2=True, varlen=True, ctx=None):
     bf = inp.bf16
     t = lambda a, b=False: synth.to_torch(a, DEV, bf16=b)
     cu = None
@@ -27,12 +35,12 @@ def _gpu(inp, chunk, init=None, scale=None, l2=True, varlen=True):
         cu = torch.from_numpy(inp.cu_seqlens.astype(np.int32))
     init_t = None if init is None else torch.from_numpy(np.ascontiguousarray(init, dtype=np.float32)).to(DEV)
     o, fs = gdn.chunk_prefill(t(inp.q, bf), t(inp.k, bf), t(inp.v, bf), t(inp.g), t(inp.beta), init_state=init_t,
-                              cu_seqlens=cu, scale=scale, qk_l2norm=l2, chunk=chunk)
+                              cu_seqlens=cu, scale=scale, qk_l2norm=l2, chunk=chunk, ctx=ctx)
     return o.float().cpu().numpy(), fs.cpu().numpy()
 
 
-def _check(inp, chunk, tol, init=None, rows=None, scale=None, l2=True):
-    o, fs = _gpu(inp, chunk, init=init, scale=scale, l2=l2)
+def _check(inp, chunk, tol, init=None, rows=None, scale=None, l2=True, ctx=None):
+    o, fs = _gpu(inp, chunk, init=init, scale=scale, l2=l2, ctx=ctx)
     o_ref, fs_ref = oracle.prefill(inp.q, inp.k, inp.v, inp.g, inp.beta, init, cu_seqlens=inp.cu_seqlens,
                                    scale=scale, qk_l2norm=l2, rows=rows, bf16=inp.bf16)
     if rows is not None:
@@ -133,9 +141,10 @@ def test_varlen_packing(dtype, lens):
 
 
 @pytest.mark.parametrize("dk,dv", [(64, 64), (256, 256)])
-def test_pipelined_segments_match_oracle_and_unsegmented(dk, dv):
+def test_pipelined_segments_match_oracle_and_unsegmented(dk, dv, ctx):
     """Few long packed sequences leave the state chain most of the GPU, so a
-    whole-prefill call pipelines segments of chunks over three streams and
+    whole-prefill call with an execution context pipelines segments of chunks
+    over the context's three streams and
     carries each sequence's state across segment boundaries.  The result must
     match the oracle and be bitwise equal to the same prefill run stage by
     stage (one chain launch over all chunks).  The pipeline starts at 576
@@ -145,7 +154,7 @@ def test_pipelined_segments_match_oracle_and_unsegmented(dk, dv):
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
     inp = synth.prefill_inputs(int(cu[-1]), H, dk, dv, "bf16", seed=dk + 77, gate="slow", cu_seqlens=cu,
                                init_state_std=0.3)
-    o, fs = _gpu(inp, 64, init=inp.init_state)
+    o, fs = _gpu(inp, 64, init=inp.init_state, ctx=ctx)
     o_ref, fs_ref = oracle.prefill(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.init_state, cu_seqlens=cu, bf16=True)
     assert bound_ratio(o, o_ref, TOL_BF16, stored_bf16=True) <= 1.0
     assert rel_err(fs, fs_ref) <= TOL_BF16
@@ -173,6 +182,37 @@ def test_varlen_device_seqlens_without_host_copy():
     o_ref, fs_ref = oracle.prefill(inp.q, inp.k, inp.v, inp.g, inp.beta, cu_seqlens=cu)
     assert rel_err(o.cpu().numpy(), o_ref) <= TOL_F32
     assert rel_err(fs.cpu().numpy(), fs_ref) <= TOL_F32
+
+
+def test_invalid_device_seqlens_raise_the_flag_and_write_nothing():
+    """cu_seqlens given on the device only (no host mirror to validate) and
+    invalid -- not monotone, not ending at T, not starting at 0, a negative
+    length: the chunk table raises the workspace's error flag (header word 0)
+    and publishes zero chunks (word 1), so no kernel writes o or the final
+    state (both keep their sentinel).  The next call with valid lengths on the
+    same workspace is correct."""
+    T, H, d = 200, 2, 64
+    cu_ok = np.array([0, 120, 200], dtype=np.int64)
+    inp = synth.prefill_inputs(T, H, d, d, "bf16", seed=4040, gate="slow", cu_seqlens=cu_ok)
+    t = lambda a, b=False: synth.to_torch(a, DEV, bf16=b)
+    args = (t(inp.q, True), t(inp.k, True), t(inp.v, True), t(inp.g), t(inp.beta))
+    ws = torch.empty(gdn.prefill_workspace_size(T, 2, H, d, d, 64), dtype=torch.uint8, device=DEV)
+    for bad in ([0, 150, 100], [0, 100, 199], [3, 100, 200], [0, -5, 200]):
+        print(f"  invalid device cu_seqlens {bad}", flush=True)
+        o = torch.full((T, H, d), 7.0, dtype=torch.bfloat16, device=DEV)
+        fs = torch.full((2, H, d, d), -3.0, dtype=torch.float32, device=DEV)
+        gdn.chunk_prefill(*args, cu_seqlens=torch.tensor(bad, dtype=torch.int32, device=DEV), out=o,
+                          final_state=fs, workspace=ws)
+        torch.cuda.synchronize()
+        hdr = ws[:8].view(torch.int32).cpu().tolist()
+        assert hdr == [1, 0], (bad, hdr)
+        assert bool((o == 7.0).all()) and bool((fs == -3.0).all()), bad
+    o, fs = gdn.chunk_prefill(*args, cu_seqlens=torch.from_numpy(cu_ok.astype(np.int32)).to(DEV), workspace=ws)
+    torch.cuda.synchronize()
+    assert ws[:8].view(torch.int32).cpu().tolist() == [0, 4]
+    o_ref, fs_ref = oracle.prefill(inp.q, inp.k, inp.v, inp.g, inp.beta, cu_seqlens=cu_ok, bf16=True)
+    assert bound_ratio(o.float().cpu().numpy(), o_ref, TOL_BF16, stored_bf16=True) <= 1.0
+    assert rel_err(fs.cpu().numpy(), fs_ref) <= TOL_BF16
 
 
 def test_continuation_and_decode_after_prefill():
@@ -251,17 +291,17 @@ def test_varlen_2m_workload_checked_subsets():
             assert es <= TOL_BF16, (n, es)
 
 
-def test_concurrent_pipelined_calls_from_two_threads():
+def test_concurrent_pipelined_calls_from_two_threads(ctx):
     """Two host threads enqueue long (pipelined) prefills on their own streams at
-    the same time; the pipeline's shared streams and events are used by one call
-    at a time, so both results equal a single-threaded run bit for bit."""
+    the same time through one context; its streams and events are used by one
+    call at a time, so both results equal a single-threaded run bit for bit."""
     import threading
 
     T, H, d = 37000, 2, 256
     inps = [synth.prefill_inputs(T, H, d, d, "bf16", seed=600 + i, gate="slow") for i in range(2)]
     t = lambda a, b=False: synth.to_torch(a, DEV, bf16=b)
     args = [(t(x.q, True), t(x.k, True), t(x.v, True), t(x.g), t(x.beta)) for x in inps]
-    ref = [gdn.chunk_prefill(*a) for a in args]
+    ref = [gdn.chunk_prefill(*a, ctx=ctx) for a in args]
     torch.cuda.synchronize()
     ref = [(o.clone(), s.clone()) for o, s in ref]
     results = [None, None]
@@ -273,7 +313,7 @@ def test_concurrent_pipelined_calls_from_two_threads():
             outs = []
             barrier.wait()
             for _ in range(3):
-                outs.append(gdn.chunk_prefill(*args[i]))
+                outs.append(gdn.chunk_prefill(*args[i], ctx=ctx))
             streams[i].synchronize()
             results[i] = outs
 
@@ -287,7 +327,7 @@ def test_concurrent_pipelined_calls_from_two_threads():
             assert torch.equal(o, ref[i][0]) and torch.equal(s, ref[i][1]), i
 
 
-def test_in_place_state_carry_on_the_pipelined_path():
+def test_in_place_state_carry_on_the_pipelined_path(ctx):
     """final_state aliasing init_state on a 37K-token batch (the pipelined path:
     the state crosses segments through the carry buffer) gives bit for bit the
     result of separate initial and final state buffers."""
@@ -299,9 +339,9 @@ def test_in_place_state_carry_on_the_pipelined_path():
     args = (t(inp.q, True), t(inp.k, True), t(inp.v, True), t(inp.g), t(inp.beta))
     cu_t = torch.from_numpy(cu.astype(np.int32))
     init = t(inp.init_state)
-    o_ref, fs_ref = gdn.chunk_prefill(*args, init_state=init.clone(), cu_seqlens=cu_t)
+    o_ref, fs_ref = gdn.chunk_prefill(*args, init_state=init.clone(), cu_seqlens=cu_t, ctx=ctx)
     st = init.clone()
-    o, fs = gdn.chunk_prefill(*args, init_state=st, cu_seqlens=cu_t, final_state=st)
+    o, fs = gdn.chunk_prefill(*args, init_state=st, cu_seqlens=cu_t, final_state=st, ctx=ctx)
     torch.cuda.synchronize()
     assert fs.data_ptr() == st.data_ptr()
     assert torch.equal(o, o_ref) and torch.equal(st, fs_ref)
@@ -309,10 +349,13 @@ def test_in_place_state_carry_on_the_pipelined_path():
 
 @pytest.mark.parametrize("T", [8192, 37000])
 def test_prefill_in_a_hip_graph_matches_eager(T):
-    """One whole-prefill call captured in a HIP graph -- the single-stream path at
-    8K tokens and the pipelined path (its side streams fork from and join the
-    captured stream) at 37K -- replayed three times with eager work between the
-    replays: every replay equals the eager result bit for bit."""
+    """The first whole-prefill call of a fresh context, captured in a HIP graph
+    (nothing of the library has run on these sizes before: the capture is the
+    first call) -- the single-stream path at 8K tokens and the pipelined path
+    (the context's streams fork from and join the captured stream) at 37K --
+    replayed three times with eager work between the replays: every replay
+    equals the eager result bit for bit, and the eager result matches the
+    stage-by-stage call without a context."""
     H, d = 2, 256
     inp = synth.prefill_inputs(T, H, d, d, "bf16", seed=808 + T, gate="slow", init_state_std=0.3)
     t = lambda a, b=False: synth.to_torch(a, DEV, bf16=b)
@@ -321,25 +364,53 @@ def test_prefill_in_a_hip_graph_matches_eager(T):
     ws = torch.empty(gdn.prefill_workspace_size(T, 1, H, d, d, 64), dtype=torch.uint8, device=DEV)
     o = torch.empty((T, H, d), dtype=torch.bfloat16, device=DEV)
     fs = torch.empty((1, H, d, d), dtype=torch.float32, device=DEV)
-    run = lambda: gdn.chunk_prefill(*args, init_state=init, out=o, final_state=fs, workspace=ws)
-    run()  # eager: creates the pipeline streams and raises the kernels' LDS limits
-    torch.cuda.synchronize()
-    o_ref, fs_ref = o.clone(), fs.clone()
-    side = torch.cuda.Stream(device=DEV)
-    side.wait_stream(torch.cuda.current_stream(DEV))
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(side):
-        with torch.cuda.graph(graph, stream=side):
-            run()
-    torch.cuda.current_stream(DEV).wait_stream(side)
-    torch.cuda.synchronize()
-    for rep in range(3):
-        o.zero_()
-        fs.zero_()
+    with gdn.Context() as c:
+        run = lambda: gdn.chunk_prefill(*args, init_state=init, out=o, final_state=fs, workspace=ws, ctx=c)
+        side = torch.cuda.Stream(device=DEV)
+        side.wait_stream(torch.cuda.current_stream(DEV))
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                run()
+        torch.cuda.current_stream(DEV).wait_stream(side)
         torch.cuda.synchronize()
-        graph.replay()
+        run()  # eager, after the capture
         torch.cuda.synchronize()
-        assert torch.equal(o, o_ref) and torch.equal(fs, fs_ref), rep
+        o_ref, fs_ref = o.clone(), fs.clone()
+        o_plain, fs_plain = gdn.chunk_prefill(*args, init_state=init)  # no context: one stream
+        torch.cuda.synchronize()
+        assert torch.equal(o_plain, o_ref) and torch.equal(fs_plain, fs_ref)
+        for rep in range(3):
+            o.zero_()
+            fs.zero_()
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(o, o_ref) and torch.equal(fs, fs_ref), rep
+        del graph
+        torch.cuda.synchronize()
+
+
+def test_context_create_destroy_and_single_stream_fallback():
+    """Contexts are created and destroyed repeatedly (default and explicit CU
+    reservations); a reservation too small for the chain's workgroups makes the
+    call run stage by stage on the caller's stream; every way gives the same
+    bits as the call without a context."""
+    T, H, d = 37000, 2, 256
+    inp = synth.prefill_inputs(T, H, d, d, "bf16", seed=909, gate="slow")
+    t = lambda a, b=False: synth.to_torch(a, DEV, bf16=b)
+    args = (t(inp.q, True), t(inp.k, True), t(inp.v, True), t(inp.g), t(inp.beta))
+    o_ref, fs_ref = gdn.chunk_prefill(*args)
+    torch.cuda.synchronize()
+    for cus in (0, 16, 31, 1):
+        for _ in range(2):
+            c = gdn.Context(cus)
+            o, fs = gdn.chunk_prefill(*args, ctx=c)
+            c.close()  # waits for the context's streams
+            torch.cuda.synchronize()
+            assert torch.equal(o, o_ref) and torch.equal(fs, fs_ref), cus
+    with pytest.raises(gdn.GdnError):
+        gdn.Context(32)
 
 
 @pytest.mark.parametrize("N", [2000, 2100])
@@ -355,21 +426,21 @@ def test_many_short_sequences(N):
     _check(inp, 64, TOL_F32, init=inp.init_state)
 
 
-def test_fp32_pipelined_path():
+def test_fp32_pipelined_path(ctx):
     """The fp32 operands at 37K tokens (past the pipelining threshold): the
     general form of the state chain in segmented launches, carrying the state
     through the carry buffer, against the oracle at the fp32 bound."""
     T, H, d = 37000, 2, 64
     inp = synth.prefill_inputs(T, H, d, d, "f32", seed=3700, gate="slow", init_state_std=0.3)
-    _check(inp, 64, TOL_F32, init=inp.init_state)
+    _check(inp, 64, TOL_F32, init=inp.init_state, ctx=ctx)
 
 
-def test_bf16_dk128_pipelined_sampled_rows():
+def test_bf16_dk128_pipelined_sampled_rows(ctx):
     """bf16, d_k = 128, d_v = 256 at 37K tokens: the pipelined path with the d_k = 128
     chain, against the oracle on sampled state rows."""
     T, H = 37000, 3
     inp = synth.prefill_inputs(T, H, 128, 256, "bf16", seed=12837, gate="slow", init_state_std=0.3)
-    _check(inp, 64, TOL_BF16, init=inp.init_state, rows=[0, 63, 200, 255])
+    _check(inp, 64, TOL_BF16, init=inp.init_state, rows=[0, 63, 200, 255], ctx=ctx)
 
 
 def test_bf16_8k_custom_scale_without_norm():
