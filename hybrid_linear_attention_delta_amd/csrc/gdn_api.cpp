@@ -10,6 +10,8 @@
 #include "../../include/gdn.h"
 #include "gdn_launch.h"
 
+static_assert(gdn::kScratchBytes == GDN_NOALLOC_SCRATCH_BYTES, "scratch size of the no-allocation prefill");
+
 namespace {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -57,11 +59,14 @@ bool prefill_supported(bool bf16, int32_t dk, int32_t dv, int32_t chunk)
     return in_list(dk, f32_d, 5) && in_list(dv, f32_d, 5) && in_list(chunk, f32_c, 3);
 }
 
-PrefillLayout prefill_layout(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv, int32_t C, bool bf16)
+PrefillLayout prefill_layout(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv, int32_t C, bool bf16,
+                             int64_t window_chunks)
 {
     PrefillLayout L;
     memset(&L, 0, sizeof L);
     L.max_chunks = T / C + N;  // >= sum_n ceil(L_n / C)
+    // chunks whose per-chunk data the workspace holds at once
+    const int64_t held = window_chunks > 0 && window_chunks < L.max_chunks ? window_chunks : L.max_chunks;
     const size_t el = bf16 ? 2 : 4;
     // record: W fragments (C x dk), raw K^T fragments (dk x C), raw Q fragments
     // (C x dk), P fragments (C x C, hi+lo for bf16) in the operand element type;
@@ -80,12 +85,12 @@ PrefillLayout prefill_layout(int64_t T, int32_t N, int32_t H, int32_t dk, int32_
     L.off_seq_order = off;
     off = align_up(off + (size_t)N * 4, 256);
     L.off_records = off;
-    off = align_up(off + (size_t)L.max_chunks * H * L.record_bytes, 256);
+    off = align_up(off + (size_t)held * H * L.record_bytes, 256);
     // outputs of the state chain for the output kernel
     L.off_states = off;
-    off = align_up(off + (size_t)L.max_chunks * H * dv * dk * el, 256);
+    off = align_up(off + (size_t)held * H * dv * dk * el, 256);
     L.off_deltas = off;
-    off = align_up(off + (size_t)L.max_chunks * H * split * dv * C * el, 256);
+    off = align_up(off + (size_t)held * H * split * dv * C * el, 256);
     L.off_carry = off;
     off += (size_t)N * H * dv * dk * 4;
     L.total = off;
@@ -156,7 +161,7 @@ gdn_status prefill_impl(const void* q, const void* k, const void* v, const float
                         int32_t num_seqs, int64_t total_tokens, int32_t H, int32_t dk, int32_t dv, int32_t chunk,
                         gdn_dtype dt, float scale, int32_t qk_l2norm, void* o, float* final_state, void* workspace,
                         size_t workspace_bytes, int32_t stages, const gdn::GatedNorm& norm, gdn_context* ctx,
-                        hipStream_t stream)
+                        hipStream_t stream, bool use_scratch = false)
 {
     if (stages < 1 || stages > GDN_STAGE_ALL) return GDN_ERR_BAD_SHAPE;
     if (dt != GDN_F32 && dt != GDN_BF16) return GDN_ERR_UNSUPPORTED;
@@ -165,7 +170,7 @@ gdn_status prefill_impl(const void* q, const void* k, const void* v, const float
     if (!cu_seqlens && num_seqs != 1) return GDN_ERR_BAD_SHAPE;
     if (!gdn::prefill_supported(dt == GDN_BF16, dk, dv, chunk)) return GDN_ERR_UNSUPPORTED;
     if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL_ARG;
-    if (!workspace) return GDN_ERR_WORKSPACE;
+    if (!workspace && !use_scratch) return GDN_ERR_WORKSPACE;
     const bool bf16 = dt == GDN_BF16;
     const void* ptrs[] = {q, k, v, init_state, o, final_state};
     for (const void* p : ptrs)
@@ -178,6 +183,25 @@ gdn_status prefill_impl(const void* q, const void* k, const void* v, const float
             if (cu_seqlens_host[n + 1] < cu_seqlens_host[n]) return GDN_ERR_BAD_SEQLENS;
     }
     gdn::PrefillLayout lay = gdn::prefill_layout(total_tokens, num_seqs, H, dk, dv, chunk, bf16);
+    int64_t window = 0;
+    if (use_scratch) {
+        // The library's scratch array: the whole workspace if it fits, else the
+        // largest window of chunks that does (binary search; at least one chunk).
+        if (lay.total > gdn::kScratchBytes) {
+            if (gdn::prefill_layout(total_tokens, num_seqs, H, dk, dv, chunk, bf16, 1).total > gdn::kScratchBytes)
+                return GDN_ERR_WORKSPACE;
+            int64_t lo = 1, hi = lay.max_chunks;  // layout(lo) fits, layout(hi) does not
+            while (hi - lo > 1) {
+                const int64_t mid = lo + (hi - lo) / 2;
+                const size_t need = gdn::prefill_layout(total_tokens, num_seqs, H, dk, dv, chunk, bf16, mid).total;
+                (need <= gdn::kScratchBytes ? lo : hi) = mid;
+            }
+            window = lo;
+            lay = gdn::prefill_layout(total_tokens, num_seqs, H, dk, dv, chunk, bf16, window);
+        }
+        if (gdn::scratch_device_ptr(&workspace) != hipSuccess || !workspace) return GDN_ERR_LAUNCH;
+        workspace_bytes = gdn::kScratchBytes;
+    }
     if (workspace_bytes < lay.total) return GDN_ERR_WORKSPACE;
     if (init_state && final_state && init_state != final_state) {
         // partial overlap would make the in-place carry order-dependent
@@ -206,6 +230,7 @@ gdn_status prefill_impl(const void* q, const void* k, const void* v, const float
     a.stages = stages;
     a.norm = norm;
     a.ctx = ctx;
+    a.window = window;
     a.stream = stream;
     return finish(gdn::launch_prefill(a), stream);
 }
@@ -262,6 +287,17 @@ gdn_status gdn_chunk_prefill(const void* q, const void* k, const void* v, const 
     return prefill_impl(q, k, v, g, beta, init_state, cu_seqlens, cu_seqlens_host, num_seqs, total_tokens, H, dk, dv,
                         chunk, dt, scale, qk_l2norm, o, final_state, workspace, workspace_bytes, GDN_STAGE_ALL,
                         gdn::GatedNorm{}, nullptr, stream);
+}
+
+gdn_status gdn_chunk_prefill_noalloc(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                                     const float* init_state, const int32_t* cu_seqlens,
+                                     const int32_t* cu_seqlens_host, int32_t num_seqs, int64_t total_tokens,
+                                     int32_t H, int32_t dk, int32_t dv, int32_t chunk, gdn_dtype dt, float scale,
+                                     int32_t qk_l2norm, void* o, float* final_state, hipStream_t stream)
+{
+    return prefill_impl(q, k, v, g, beta, init_state, cu_seqlens, cu_seqlens_host, num_seqs, total_tokens, H, dk, dv,
+                        chunk, dt, scale, qk_l2norm, o, final_state, nullptr, 0, GDN_STAGE_ALL, gdn::GatedNorm{},
+                        nullptr, stream, true);
 }
 
 gdn_status gdn_chunk_prefill_ctx(gdn_context_t ctx, const void* q, const void* k, const void* v, const float* g,

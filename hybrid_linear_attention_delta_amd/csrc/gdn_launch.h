@@ -59,8 +59,10 @@ struct PrefillLayout {
 };
 
 bool prefill_supported(bool bf16, int32_t dk, int32_t dv, int32_t chunk);
+// window_chunks > 0: the per-chunk regions (records, states, deltas) hold that
+// many chunks instead of every chunk of the call
 PrefillLayout prefill_layout(int64_t total_tokens, int32_t num_seqs, int32_t H, int32_t dk, int32_t dv,
-                             int32_t chunk, bool bf16);
+                             int32_t chunk, bool bf16, int64_t window_chunks = 0);
 
 struct PrefillArgs {
     const void *q, *k, *v;
@@ -81,10 +83,17 @@ struct PrefillArgs {
     int32_t stages;  // bit 0: prepare (chunk table + intra-chunk), bit 1: propagate (state chain), bit 2: outputs
     GatedNorm norm;  // epilogue of the output stage
     gdn_context* ctx;  // NULL: every kernel on `stream`
+    int64_t window;    // > 0: the workspace holds `window` chunks of per-chunk data (stage by stage per window)
     hipStream_t stream;
 };
 
 hipError_t launch_prefill(const PrefillArgs& a);
+
+// The no-allocation prefill's workspace: a device array of kScratchBytes per
+// GPU inside the library.  scratch_device_ptr returns its address on the
+// current device (looked up once per device with hipGetSymbolAddress).
+constexpr size_t kScratchBytes = (size_t)256 << 20;
+hipError_t scratch_device_ptr(void** out);
 
 // Front end: short causal conv + SiLU on the q, k, v projections and the gate
 // math.  Channels of q, k, v form one axis of 2 H dk + H dv (q, k, v in order)

@@ -420,7 +420,7 @@ __device__ __forceinline__ void intra_chunk(const TIn* __restrict__ q, const TIn
                                                     const ChunkInfo* __restrict__ tab, int32_t varlen, int64_t T,
                                                     int32_t H, int32_t l2norm,
                                                     unsigned char* __restrict__ records, size_t record_bytes,
-                                                    int64_t c)
+                                                    int64_t c, int64_t slot)
 {
     using M = Mma<TIn>;
     using F = Mma<float>;
@@ -444,7 +444,7 @@ __device__ __forceinline__ void intra_chunk(const TIn* __restrict__ q, const TIn
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave: scalar branches
     const int g16 = lane >> 4, l16 = lane & 15;
 
-    unsigned char* recb = records + ((size_t)c * H + h) * record_bytes;
+    unsigned char* recb = records + ((size_t)slot * H + h) * record_bytes;
     TIn* rec = reinterpret_cast<TIn*>(recb);
     float* recU = reinterpret_cast<float*>(recb + R::U_BYTE_OFF);
 
@@ -774,7 +774,7 @@ __device__ __forceinline__ void intra_chunk_bf16(const uint16_t* __restrict__ q,
                                                  const float* __restrict__ beta, const int32_t* __restrict__ header,
                                                  const ChunkInfo* __restrict__ tab, int32_t varlen, int64_t T,
                                                  int32_t H, int32_t l2norm, unsigned char* __restrict__ records,
-                                                 size_t record_bytes, int64_t c)
+                                                 size_t record_bytes, int64_t c, int64_t slot)
 {
     using M = Mma<uint16_t>;
     using F = Mma<float>;
@@ -798,7 +798,7 @@ __device__ __forceinline__ void intra_chunk_bf16(const uint16_t* __restrict__ q,
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // = the row tile this wave owns
     const int g16 = lane >> 4, l16 = lane & 15;
 
-    unsigned char* recb = records + ((size_t)c * H + h) * record_bytes;
+    unsigned char* recb = records + ((size_t)slot * H + h) * record_bytes;
     uint16_t* rec = reinterpret_cast<uint16_t*>(recb);
     float* recU = reinterpret_cast<float*>(recb + R::U_BYTE_OFF);
     const int64_t row0 = (int64_t)ci.tok0 * H + h;  // row index of token tok0 in [tokens*H]
@@ -1112,14 +1112,18 @@ __global__ __launch_bounds__(256) void intra_kernel(const TIn* __restrict__ q, c
                                                     const ChunkInfo* __restrict__ tab, int32_t varlen, int64_t T,
                                                     int32_t H, int32_t l2norm,
                                                     unsigned char* __restrict__ records, size_t record_bytes,
-                                                    int64_t c_base, int64_t c_end)
+                                                    int64_t c_base, int64_t c_end, int64_t slot0)
 {
+    // chunk c's record is slot c - slot0 of `records` (slot0 = 0 unless the
+    // workspace holds a window of the chunks)
     const int64_t c = c_base + blockIdx.x;
     if (c >= c_end) return;
     if constexpr (sizeof(TIn) == 2 && C == 64)
-        intra_chunk_bf16<DK, DV>(q, k, v, g, beta, header, tab, varlen, T, H, l2norm, records, record_bytes, c);
+        intra_chunk_bf16<DK, DV>(q, k, v, g, beta, header, tab, varlen, T, H, l2norm, records, record_bytes, c,
+                                 c - slot0);
     else
-        intra_chunk<TIn, C, DK, DV>(q, k, v, g, beta, header, tab, varlen, T, H, l2norm, records, record_bytes, c);
+        intra_chunk<TIn, C, DK, DV>(q, k, v, g, beta, header, tab, varlen, T, H, l2norm, records, record_bytes, c,
+                                    c - slot0);
 }
 
 // ------------------------------------------------------------------ chain kernel
@@ -1250,7 +1254,7 @@ __global__ __launch_bounds__((NW + chain_loaders<TIn, C>()) * 64) void chain_ker
     const int32_t* __restrict__ header, const int32_t* __restrict__ seq_first,
     const int32_t* __restrict__ seq_order, int32_t varlen, int64_t T, int32_t H, int32_t pairs, const unsigned char* records, size_t record_bytes, const float* init_state,
     float* final_state, TIn* __restrict__ states, TIn* __restrict__ deltas, int64_t seg_begin, int64_t seg_end,
-    float* carry)
+    float* carry, int64_t slot0)
 // (records is deliberately not __restrict__: a restrict read-only argument lets
 // the compiler treat its loads as invariant and sink them across the barriers
 // to their use, which would turn the loaders' early loads into late ones)
@@ -1311,13 +1315,16 @@ __global__ __launch_bounds__((NW + chain_loaders<TIn, C>()) * 64) void chain_ker
 
     // ---------------------------------------------------------------- operands
     const uint32_t lane_b = (uint32_t)lane * 16;
-    auto rec_ptr = [&](int64_t c) { return records + ((size_t)c * H + h) * record_bytes; };
+    // chunk c's record, state and Delta are slot c - slot0 of their regions
+    auto rec_ptr = [&](int64_t c) { return records + ((size_t)(c - slot0) * H + h) * record_bytes; };
     auto w_src = [&](int r, int ks) { return R::WH_OFF * EB + (uint32_t)(r * R::DKS + ks) * FB; };
     auto k_src = [&](int mt, int ks) { return R::K_OFF * EB + (uint32_t)(mt * R::CKS + ks) * FB; };
     auto u_src = [&](int r) { return (uint32_t)R::U_BYTE_OFF + (uint32_t)(r * R::VT + tile) * FB; };
-    auto state_out = [&](int64_t c) { return states + ((size_t)c * H + h) * CO::STATE_ELEMS + (size_t)row0 * DK; };
+    auto state_out = [&](int64_t c) {
+        return states + ((size_t)(c - slot0) * H + h) * CO::STATE_ELEMS + (size_t)row0 * DK;
+    };
     auto delta_out = [&](int64_t c, int part) {
-        return deltas + ((size_t)c * H + h) * CO::DELTA_ELEMS + ((size_t)part * DV + row0) * C;
+        return deltas + ((size_t)(c - slot0) * H + h) * CO::DELTA_ELEMS + ((size_t)part * DV + row0) * C;
     };
 
     // ------------------------------------------------- loader waves (staged form)
@@ -1640,7 +1647,7 @@ __device__ __forceinline__ void output_chunk(const int32_t* __restrict__ header,
                                                      size_t record_bytes, const TIn* __restrict__ states,
                                                      const TIn* __restrict__ deltas, TIn* __restrict__ o, float scale,
                                                      const TIn* __restrict__ gz, const float* __restrict__ gw,
-                                                     float geps, int64_t c)
+                                                     float geps, int64_t c, int64_t slot)
 {
     using M = Mma<TIn>;
     using R = Rec<TIn, C, DK, DV>;
@@ -1664,12 +1671,12 @@ __device__ __forceinline__ void output_chunk(const int32_t* __restrict__ header,
     const int g16 = lane >> 4, l16 = lane & 15;
     const uint32_t lane_b = (uint32_t)lane * 16;
 
-    const unsigned char* recb = records + ((size_t)c * H + h) * record_bytes;
+    const unsigned char* recb = records + ((size_t)slot * H + h) * record_bytes;
     const __amdgpu_buffer_rsrc_t rr = make_rsrc(recb, (uint32_t)R::BYTES);
     const __amdgpu_buffer_rsrc_t rs =
-        make_rsrc(states + ((size_t)c * H + h) * CO::STATE_ELEMS, (uint32_t)(CO::STATE_ELEMS * EB));
+        make_rsrc(states + ((size_t)slot * H + h) * CO::STATE_ELEMS, (uint32_t)(CO::STATE_ELEMS * EB));
     const __amdgpu_buffer_rsrc_t rd =
-        make_rsrc(deltas + ((size_t)c * H + h) * CO::DELTA_ELEMS, (uint32_t)(CO::DELTA_ELEMS * EB));
+        make_rsrc(deltas + ((size_t)slot * H + h) * CO::DELTA_ELEMS, (uint32_t)(CO::DELTA_ELEMS * EB));
 
     f32x4 qs[RT];
 #pragma unroll
@@ -1799,12 +1806,12 @@ __global__ __launch_bounds__(256) void output_kernel(const int32_t* __restrict__
                                                      size_t record_bytes, const TIn* __restrict__ states,
                                                      const TIn* __restrict__ deltas, TIn* __restrict__ o, float scale,
                                                      const TIn* __restrict__ gz, const float* __restrict__ gw,
-                                                     float geps, int64_t c_base, int64_t c_end)
+                                                     float geps, int64_t c_base, int64_t c_end, int64_t slot0)
 {
     const int64_t c = c_base + blockIdx.x;
     if (c >= c_end) return;
     output_chunk<TIn, C, DK, DV, GATED>(header, tab, varlen, T, H, records, record_bytes, states, deltas, o, scale,
-                                        gz, gw, geps, c);
+                                        gz, gw, geps, c, c - slot0);
 }
 
 // ------------------------------------------------------------------ dispatch
@@ -1900,6 +1907,41 @@ hipError_t context_create(int32_t chain_cus_per_xcd, gdn_context** out)
 
 hipError_t context_destroy(gdn_context* ctx) { return context_release(ctx); }
 
+}  // namespace gdn
+
+// Workspace of the no-allocation prefill (gdn_chunk_prefill_noalloc): every GPU
+// the library runs on holds one copy of this array from the first use of the
+// library's code on that device until the process ends.  In host code the name
+// stands for a host-side shadow, not a device address: only the address that
+// hipGetSymbolAddress returns for the current device may be handed to kernels.
+static __device__ __align__(256) unsigned char scratch[gdn::kScratchBytes];
+
+namespace gdn {
+
+// The device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+hipError_t scratch_device_ptr(void** out)
+{
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* ptr[kMaxDevices] = {};
+    *out = nullptr;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        ptr[dev] = p;
+    }
+    *out = ptr[dev];
+    return hipSuccess;
+}
+
 int context_device(const gdn_context* ctx) { return ctx->dev; }
 
 // Raises a kernel's dynamic-LDS limit to what this launch uses.  Set on every
@@ -1932,7 +1974,9 @@ static hipError_t run_prefill(const PrefillArgs& a)
     if (pairs > 0x7fffffff || chain_blocks > 0x7fffffff || grid_chunks > 0x7fffffff) return hipErrorInvalidConfiguration;
     constexpr int64_t ALL = INT64_MAX;
 
-    auto launch_intra = [&](int64_t c0, int64_t c1, hipStream_t st) -> hipError_t {
+    // slot0: the chunk whose per-chunk data sits at slot 0 of the records,
+    // states and deltas (0 unless the workspace holds a window of the chunks)
+    auto launch_intra = [&](int64_t c0, int64_t c1, hipStream_t st, int64_t slot0 = 0) -> hipError_t {
         if (c1 <= c0) return hipSuccess;
         size_t smem = sizeof(IntraSmem<TIn, C, DK, DV>);
         if constexpr (sizeof(TIn) == 2 && C == 64) smem = sizeof(IntraBfSmem<DK, DV>);
@@ -1940,10 +1984,10 @@ static hipError_t run_prefill(const PrefillArgs& a)
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL((intra_kernel<TIn, C, DK, DV>), dim3((uint32_t)(c1 - c0), a.H), dim3(256), smem,
                            st, (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, a.g, a.beta, header, tab, varlen,
-                           a.T, a.H, a.l2norm, records, a.lay.record_bytes, c0, c1);
+                           a.T, a.H, a.l2norm, records, a.lay.record_bytes, c0, c1, slot0);
         return hipGetLastError();
     };
-    auto launch_chain = [&](int64_t c0, int64_t c1, hipStream_t st) -> hipError_t {
+    auto launch_chain = [&](int64_t c0, int64_t c1, hipStream_t st, int64_t slot0 = 0) -> hipError_t {
         constexpr int NW = 8;
         using Lds = ChainLds<TIn, C, DK, DV, NW, chain_staged<TIn, C>()>;
         static_assert(sizeof(Lds) <= 160 * 1024, "chain kernel LDS");
@@ -1956,14 +2000,14 @@ static hipError_t run_prefill(const PrefillArgs& a)
         if (seg)
             hipLaunchKernelGGL((chain_kernel<TIn, C, DK, DV, NW, true>), grid, block, sizeof(Lds), st, header, first,
                                order, varlen, a.T, a.H, (int32_t)pairs, records, a.lay.record_bytes, a.init_state,
-                               a.final_state, states, deltas, c0, c1, carry);
+                               a.final_state, states, deltas, c0, c1, carry, slot0);
         else
             hipLaunchKernelGGL((chain_kernel<TIn, C, DK, DV, NW, false>), grid, block, sizeof(Lds), st, header, first,
                                order, varlen, a.T, a.H, (int32_t)pairs, records, a.lay.record_bytes, a.init_state,
-                               a.final_state, states, deltas, c0, c1, carry);
+                               a.final_state, states, deltas, c0, c1, carry, slot0);
         return hipGetLastError();
     };
-    auto launch_output = [&](int64_t c0, int64_t c1, hipStream_t st) -> hipError_t {
+    auto launch_output = [&](int64_t c0, int64_t c1, hipStream_t st, int64_t slot0 = 0) -> hipError_t {
         if (c1 <= c0) return hipSuccess;
         const bool gated = a.norm.z != nullptr;
         const size_t smem = OutCfg<TIn, C, DK, DV>::lds_bytes(gated);
@@ -1975,11 +2019,11 @@ static hipError_t run_prefill(const PrefillArgs& a)
         if (gated)
             hipLaunchKernelGGL((output_kernel<TIn, C, DK, DV, true>), grid, dim3(256), smem, st, header, tab, varlen,
                                a.T, a.H, records, a.lay.record_bytes, states, deltas, (TIn*)a.o, a.scale,
-                               (const TIn*)a.norm.z, a.norm.w, a.norm.eps, c0, c1);
+                               (const TIn*)a.norm.z, a.norm.w, a.norm.eps, c0, c1, slot0);
         else
             hipLaunchKernelGGL((output_kernel<TIn, C, DK, DV, false>), grid, dim3(256), smem, st, header, tab, varlen,
                                a.T, a.H, records, a.lay.record_bytes, states, deltas, (TIn*)a.o, a.scale,
-                               (const TIn*)nullptr, (const float*)nullptr, 0.f, c0, c1);
+                               (const TIn*)nullptr, (const float*)nullptr, 0.f, c0, c1, slot0);
         return hipGetLastError();
     };
 #define GDN_TRY(x)                       \
@@ -2007,6 +2051,23 @@ static hipError_t run_prefill(const PrefillArgs& a)
     // (measured: 8K tokens 0.38 ms pipelined against 0.24 ms stage by stage),
     // which the overlap repays only past about 36K tokens of one sequence
     // (32K: 1.07 against 1.04 ms; 40K: 1.26 against 1.30 ms).
+    // A workspace that holds a window of a.window chunks (the no-allocation
+    // entry point): the chunks are processed stage by stage, one window at a
+    // time, on the caller's stream; each window's chain launch carries the
+    // states of the sequences that continue past it through `carry`, exactly as
+    // the pipeline's segments do.  The last window is open-ended so that empty
+    // sequences after the last chunk still copy their initial state.
+    if (a.window > 0) {
+        if (a.stages != 7) return hipErrorInvalidValue;
+        for (int64_t c0 = 0; c0 == 0 || c0 < grid_chunks; c0 += a.window) {
+            const int64_t c1 = std::min(c0 + a.window, grid_chunks);
+            GDN_TRY(launch_intra(c0, c1, a.stream, c0));
+            GDN_TRY(launch_chain(c0, c1 >= grid_chunks ? ALL : c1, a.stream, c0));
+            GDN_TRY(launch_output(c0, c1, a.stream, c0));
+        }
+        return hipSuccess;
+    }
+
     constexpr int64_t PIPE_MIN_CHUNKS = 576, GEOM_MIN_CHUNKS = 768;
     const int64_t chain_per_xcd = ((pairs + 7) / 8) * (DV / 16);
     gdn_context* pr = a.ctx;

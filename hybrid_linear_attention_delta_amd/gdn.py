@@ -62,6 +62,9 @@ def load_library(path: str | None = None):
             lib.gdn_context_create.restype = ctypes.c_int
             lib.gdn_context_destroy.argtypes = [vp]
             lib.gdn_context_destroy.restype = ctypes.c_int
+            lib.gdn_chunk_prefill_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32,
+                                                      ctypes.c_int, f32, i32, vp, vp, vp]
+            lib.gdn_chunk_prefill_noalloc.restype = ctypes.c_int
             lib.gdn_chunk_prefill_ctx.argtypes = [vp] + lib.gdn_chunk_prefill.argtypes
             lib.gdn_chunk_prefill_ctx.restype = ctypes.c_int
             lib.gdn_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int, f32, i32,

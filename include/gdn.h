@@ -195,6 +195,32 @@ gdn_status gdn_chunk_prefill_ctx(gdn_context_t ctx, const void* q, const void* k
                                  size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * For callers that cannot allocate device memory -- code being captured into
+ * a HIP graph, serving loops that must not call hipMalloc, harnesses that
+ * forbid it: gdn_chunk_prefill without a workspace argument.  The workspace is
+ * a device array inside the library, GDN_NOALLOC_SCRATCH_BYTES (256 MiB) on
+ * every GPU the library is used on, held from the library's first use on that
+ * device until the process ends; the call itself allocates nothing.  When the
+ * call's workspace (gdn_prefill_workspace_size) is larger, the chunks are
+ * processed in windows that fit, one after another on `stream`, each
+ * sequence's state carried from window to window in fp32; the results are
+ * bit-identical to gdn_chunk_prefill's.  Sizes whose fixed part (chunk table
+ * and the num_seqs x H x dv x dk fp32 carry) leaves no room for even one chunk
+ * are rejected with GDN_ERR_WORKSPACE before anything is launched.
+ * Every call on one GPU uses the same array and leaves its contents behind
+ * (nothing in it needs to start at zero): calls that can overlap on one GPU --
+ * on different streams, or from several threads without ordering -- race on
+ * it and must be serialised by the caller.  Arguments and every other rule as
+ * for gdn_chunk_prefill.
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+gdn_status gdn_chunk_prefill_noalloc(const void* q, const void* k, const void* v, const float* g,
+                                     const float* beta, const float* init_state, const int32_t* cu_seqlens,
+                                     const int32_t* cu_seqlens_host, int32_t num_seqs, int64_t total_tokens,
+                                     int32_t H, int32_t dk, int32_t dv, int32_t chunk, gdn_dtype dt, float scale,
+                                     int32_t qk_l2norm, void* o, float* final_state, hipStream_t stream);
+
+/*
  * One recurrent decode step for N independent sequences (the token-level
  * recurrence above with one token per sequence; the serving form of the
  * fixed-size state described in App. A.3 and the HyLo-Qwen GDN model card).
