@@ -370,10 +370,13 @@ def bench_frontend(torch, gdn, synth, steps, warmup, ctx):
         q, k, v, g, beta, _ = front()
         gdn.chunk_prefill(q, k, v, g, beta, chunk=C, out=o, final_state=fs, workspace=ws, ctx=ctx)
 
+    fused = lambda: gdn.chunk_prefill_frontend(xq, xk, xv, w, a_, b_, al, db, return_conv_state=False, out=o,
+                                               final_state=fs, workspace=ws, ctx=ctx)
+
     res = {}
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    for name, fn in (("frontend", front), ("frontend_then_prefill", both)):
+    for name, fn in (("frontend", front), ("frontend_then_prefill", both), ("fused", fused)):
         for _ in range(max(1, warmup)):
             fn()
         torch.cuda.synchronize()
@@ -383,7 +386,8 @@ def bench_frontend(torch, gdn, synth, steps, warmup, ctx):
         t1.record()
         torch.cuda.synchronize()
         res[name] = t0.elapsed_time(t1) / steps
-    log(f"[bench] front end {res['frontend'] * 1e3:.1f} us; front end + prefill {res['frontend_then_prefill']:.3f} ms")
+    log(f"[bench] front end {res['frontend'] * 1e3:.1f} us; front end + prefill {res['frontend_then_prefill']:.3f} ms; "
+        f"front end folded into the prefill {res['fused']:.3f} ms")
 
     fd = synth.frontend_inputs(DEC_N, H, DK, DV, "bf16", seed=synth.seed_for("decode"), with_state=True,
                                N=DEC_N)
@@ -610,6 +614,9 @@ def main():
         "ms_per_step": fe["frontend"],
         "frontend_then_prefill_ms": fe["frontend_then_prefill"],
         "frontend_then_prefill_tokens_per_s": T / (fe["frontend_then_prefill"] / 1e3),
+        "fused_frontend_prefill_ms": fe["fused"],
+        "fused_frontend_prefill_tokens_per_s": T / (fe["fused"] / 1e3),
+        "fused_overhead_over_prefill_ms": fe["fused"] - pre["ms_per_step"],
         "roofline": {"kernel": "conv_silu_kernel", "bound": "hbm", "achieved": fb / (fe["frontend"] / 1e3) / 1e9,
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": fb / (fe["frontend"] / 1e3) / 1e9 / PEAK_HBM_GBPS,

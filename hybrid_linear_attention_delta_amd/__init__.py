@@ -10,6 +10,7 @@ from .gdn import (  # noqa: F401
     GdnError,
     chunk_prefill,
     chunk_prefill_backward,
+    chunk_prefill_frontend,
     decode_step,
     frontend_decode,
     frontend_prefill,
@@ -18,5 +19,5 @@ from .gdn import (  # noqa: F401
     prefill_workspace_size,
 )
 
-__all__ = ["chunk_prefill", "chunk_prefill_backward", "decode_step", "frontend_prefill", "frontend_decode",
+__all__ = ["chunk_prefill", "chunk_prefill_frontend", "chunk_prefill_backward", "decode_step", "frontend_prefill", "frontend_decode",
            "prefill_workspace_size", "prefill_backward_workspace_size", "load_library", "GdnError", "Context"]

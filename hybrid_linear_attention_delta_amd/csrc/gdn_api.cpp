@@ -161,7 +161,8 @@ gdn_status prefill_impl(const void* q, const void* k, const void* v, const float
                         int32_t num_seqs, int64_t total_tokens, int32_t H, int32_t dk, int32_t dv, int32_t chunk,
                         gdn_dtype dt, float scale, int32_t qk_l2norm, void* o, float* final_state, void* workspace,
                         size_t workspace_bytes, int32_t stages, const gdn::GatedNorm& norm, gdn_context* ctx,
-                        hipStream_t stream, bool use_scratch = false)
+                        hipStream_t stream, bool use_scratch = false, const gdn::FrontIn* fe = nullptr,
+                        void* conv_state_out = nullptr)
 {
     if (stages < 1 || stages > GDN_STAGE_ALL) return GDN_ERR_BAD_SHAPE;
     if (dt != GDN_F32 && dt != GDN_BF16) return GDN_ERR_UNSUPPORTED;
@@ -216,6 +217,12 @@ gdn_status prefill_impl(const void* q, const void* k, const void* v, const float
     }
 
     gdn::PrefillArgs a;
+    a.fused = fe != nullptr;
+    if (fe) {
+        a.fe = *fe;
+        a.fe.cu = cu_seqlens;
+    }
+    a.conv_state_out = conv_state_out;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
     a.init_state = init_state;
     a.cu_seqlens = cu_seqlens;
@@ -298,6 +305,42 @@ gdn_status gdn_chunk_prefill_noalloc(const void* q, const void* k, const void* v
     return prefill_impl(q, k, v, g, beta, init_state, cu_seqlens, cu_seqlens_host, num_seqs, total_tokens, H, dk, dv,
                         chunk, dt, scale, qk_l2norm, o, final_state, nullptr, 0, GDN_STAGE_ALL, gdn::GatedNorm{},
                         nullptr, stream, true);
+}
+
+gdn_status gdn_chunk_prefill_frontend(gdn_context_t ctx, const void* xq, const void* xk, const void* xv,
+                                      const float* conv_weight, const float* a, const float* b, const float* A_log,
+                                      const float* dt_bias, const void* conv_state_in, const float* init_state,
+                                      const int32_t* cu_seqlens, const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                      int64_t total_tokens, int32_t H, int32_t dk, int32_t dv, int32_t chunk,
+                                      gdn_dtype dt, float scale, int32_t qk_l2norm, void* o, float* final_state,
+                                      void* conv_state_out, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream)
+{
+    if (dt != GDN_BF16 && dt != GDN_F32) return GDN_ERR_UNSUPPORTED;
+    if (dt != GDN_BF16 || chunk != 64) return GDN_ERR_UNSUPPORTED;  // the folded front end is built for bf16
+    if (H < 1 || dk < 1 || dv < 1 || num_seqs < 1 || total_tokens < 0) return GDN_ERR_BAD_SHAPE;
+    if (total_tokens > 0 && (!conv_weight || !A_log || !dt_bias)) return GDN_ERR_NULL_ARG;
+    const void* p16[] = {conv_weight, conv_state_in, conv_state_out};
+    for (const void* p : p16)
+        if (p && !aligned16(p)) return GDN_ERR_ALIGNMENT;
+    const void* p4[] = {A_log, dt_bias};
+    for (const void* p : p4)
+        if (!aligned4(p)) return GDN_ERR_ALIGNMENT;
+    if (conv_state_in && conv_state_out && conv_state_in != conv_state_out) {
+        const size_t bytes = (size_t)num_seqs * 3 * (size_t)H * (2 * (size_t)dk + dv) * 2;
+        const char* a0 = (const char*)conv_state_in;
+        const char* b0 = (const char*)conv_state_out;
+        if (a0 < b0 + bytes && b0 < a0 + bytes) return GDN_ERR_BAD_SHAPE;  // partial overlap
+    }
+    gdn::FrontIn fe;
+    fe.xq = xq; fe.xk = xk; fe.xv = xv; fe.w = conv_weight;
+    fe.a = a; fe.b = b; fe.A_log = A_log; fe.dt_bias = dt_bias;
+    fe.state_in = conv_state_in;
+    // the projections and gate inputs take the places of q, k, v, g and beta in
+    // the shared checks (shapes, alignment, null pointers)
+    return prefill_impl(xq, xk, xv, a, b, init_state, cu_seqlens, cu_seqlens_host, num_seqs, total_tokens, H, dk, dv,
+                        chunk, dt, scale, qk_l2norm, o, final_state, workspace, workspace_bytes, GDN_STAGE_ALL,
+                        gdn::GatedNorm{}, ctx, stream, false, &fe, conv_state_out);
 }
 
 gdn_status gdn_chunk_prefill_ctx(gdn_context_t ctx, const void* q, const void* k, const void* v, const float* g,

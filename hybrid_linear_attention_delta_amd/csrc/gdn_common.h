@@ -108,4 +108,26 @@ __device__ __forceinline__ float fast_silu(float u)
     return u * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * u));
 }
 
+// ---- front end (App. A.3: the short convolution before the recurrence and the
+//      gates of the paragraph after Eq. 21).  Shared by the standalone front-end
+//      kernels and the prefill that folds the front end into its row loads, so
+//      that both round every value identically.
+
+// silu of the 4-tap causal convolution of one channel: taps oldest first,
+// x0 .. x3 the inputs of tokens t-3 .. t (explicit FMA order).
+__device__ __forceinline__ float conv4_silu(const float (&w)[4], float x0, float x1, float x2, float x3)
+{
+    return fast_silu(fmaf(w[3], x3, fmaf(w[2], x2, fmaf(w[1], x1, w[0] * x0))));
+}
+
+// log(1 + e^u) without overflow: max(u, 0) + log1p(e^{-|u|})
+__device__ __forceinline__ float softplus(float u) { return fmaxf(u, 0.f) + log1pf(expf(-fabsf(u))); }
+
+// g = -exp(A_log) softplus(a + dt_bias), beta = sigmoid(b)
+__device__ __forceinline__ float gate_g(float a, float A_log, float dt_bias)
+{
+    return -expf(A_log) * softplus(a + dt_bias);
+}
+__device__ __forceinline__ float gate_beta(float b) { return 1.0f / (1.0f + expf(-b)); }
+
 }  // namespace gdn

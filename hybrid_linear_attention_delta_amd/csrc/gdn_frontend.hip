@@ -80,19 +80,15 @@ __device__ __forceinline__ void st_vec(TIn* p, typename FVec<TIn>::Raw r)
     __builtin_nontemporal_store(r, reinterpret_cast<typename FVec<TIn>::Raw*>(p));
 }
 
-// SiLU on the hardware exp2 and reciprocal: the IEEE expf and divide made this
-// streaming kernel ALU-bound (0.42 against 0.25 ms at 64K tokens).
-__device__ __forceinline__ float silu(float u) { return fast_silu(u); }
-
-// log(1 + e^u) without overflow: max(u, 0) + log1p(e^{-|u|})
-__device__ __forceinline__ float softplus(float u) { return fmaxf(u, 0.f) + log1pf(expf(-fabsf(u))); }
+// SiLU runs on the hardware exp2 and reciprocal (conv4_silu): the IEEE expf and
+// divide made this streaming kernel ALU-bound (0.42 against 0.25 ms at 64K tokens).
 
 __device__ __forceinline__ void gate_one(const float* __restrict__ a, const float* __restrict__ b,
                                          const float* __restrict__ A_log, const float* __restrict__ dt_bias,
                                          float* __restrict__ g, float* __restrict__ beta, int64_t e, int h)
 {
-    g[e] = -expf(A_log[h]) * softplus(a[e] + dt_bias[h]);
-    beta[e] = 1.0f / (1.0f + expf(-b[e]));
+    g[e] = gate_g(a[e], A_log[h], dt_bias[h]);
+    beta[e] = gate_beta(b[e]);
 }
 
 // Which of q, k, v a channel vector belongs to, and its offset inside that tensor.
@@ -227,8 +223,7 @@ __global__ __launch_bounds__(256) void conv_silu_kernel(const TIn* __restrict__ 
         V::widen(rows[i], x);
 #pragma unroll
         for (int e = 0; e < NV; ++e) {
-            const float acc = wt[e][0] * h[0][e] + wt[e][1] * h[1][e] + wt[e][2] * h[2][e] + wt[e][3] * x[e];
-            y[e] = silu(acc);
+            y[e] = conv4_silu(wt[e], h[0][e], h[1][e], h[2][e], x[e]);
             h[0][e] = h[1][e];
             h[1][e] = h[2][e];
             h[2][e] = x[e];
@@ -309,7 +304,8 @@ __global__ __launch_bounds__(256) void conv_decode_kernel(const TIn* __restrict_
 #pragma unroll
         for (int e = 0; e < NV; ++e) {
             const f32x4 t = *reinterpret_cast<const f32x4*>(w + (int64_t)(c + e) * 4);
-            y[e] = silu(t[0] * h0[e] + t[1] * h1[e] + t[2] * h2[e] + t[3] * x[e]);
+            const float wt[4] = {t[0], t[1], t[2], t[3]};
+            y[e] = conv4_silu(wt, h0[e], h1[e], h2[e], x[e]);
         }
         st_vec(sel.y + (int64_t)n * sel.ld + sel.col, V::narrow(y));
         st_vec(sp, r1);
@@ -317,6 +313,9 @@ __global__ __launch_bounds__(256) void conv_decode_kernel(const TIn* __restrict_
         st_vec(sp + 2 * ctot, rx);
     }
 }
+
+template <typename TIn>
+hipError_t launch_conv_state_t(const FrontendArgs& a);
 
 template <typename TIn>
 hipError_t launch_frontend_t(const FrontendArgs& a)
@@ -345,6 +344,17 @@ hipError_t launch_frontend_t(const FrontendArgs& a)
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
+    return launch_conv_state_t<TIn>(a);
+}
+
+template <typename TIn>
+hipError_t launch_conv_state_t(const FrontendArgs& a)
+{
+    constexpr int NV = FVec<TIn>::N;
+    const int32_t cq = a.H * a.dk, cv = a.H * a.dv;
+    const int32_t groups = (2 * cq + cv) / NV;
+    const uint32_t gx = (uint32_t)((groups + 255) / 256);
+    const int32_t T = (int32_t)a.T;
     if (!a.state_out) return hipSuccess;
     const uint32_t gy = (uint32_t)min(a.N, 65535);
     hipLaunchKernelGGL((conv_state_kernel<TIn>), dim3(gx, gy), dim3(256), 0, a.stream, (const TIn*)a.xq,
@@ -358,6 +368,11 @@ hipError_t launch_frontend_t(const FrontendArgs& a)
 hipError_t launch_frontend(const FrontendArgs& a)
 {
     return a.bf16 ? launch_frontend_t<uint16_t>(a) : launch_frontend_t<float>(a);
+}
+
+hipError_t launch_conv_state(const FrontendArgs& a)
+{
+    return a.bf16 ? launch_conv_state_t<uint16_t>(a) : launch_conv_state_t<float>(a);
 }
 
 }  // namespace gdn

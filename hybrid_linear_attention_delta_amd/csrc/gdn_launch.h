@@ -64,6 +64,18 @@ bool prefill_supported(bool bf16, int32_t dk, int32_t dv, int32_t chunk);
 PrefillLayout prefill_layout(int64_t total_tokens, int32_t num_seqs, int32_t H, int32_t dk, int32_t dv,
                              int32_t chunk, bool bf16, int64_t window_chunks = 0);
 
+// The front end folded into the prefill's row loads (gdn_chunk_prefill_frontend):
+// the projections xq, xk, xv [T][H][dk|dv] and the gate inputs a, b [T][H]
+// replace q, k, v, g and beta; taps w [ctot][4] fp32 and the conv state
+// [N][3][ctot] as in FrontendArgs.  cu: the device cu_seqlens (or NULL).
+struct FrontIn {
+    const void *xq = nullptr, *xk = nullptr, *xv = nullptr;
+    const float* w = nullptr;
+    const float *a = nullptr, *b = nullptr, *A_log = nullptr, *dt_bias = nullptr;
+    const void* state_in = nullptr;
+    const int32_t* cu = nullptr;
+};
+
 struct PrefillArgs {
     const void *q, *k, *v;
     const float *g, *beta;
@@ -84,6 +96,9 @@ struct PrefillArgs {
     GatedNorm norm;  // epilogue of the output stage
     gdn_context* ctx;  // NULL: every kernel on `stream`
     int64_t window;    // > 0: the workspace holds `window` chunks of per-chunk data (stage by stage per window)
+    bool fused;        // the front end is folded into the preparation (fe replaces q, k, v, g, beta)
+    FrontIn fe;
+    void* conv_state_out;  // fused: [N][3][ctot] or NULL (may alias fe.state_in)
     hipStream_t stream;
 };
 
@@ -116,6 +131,9 @@ struct FrontendArgs {
 };
 
 hipError_t launch_frontend(const FrontendArgs& a);
+// Only the conv-state update of a prefill front end (state_in -> state_out from
+// the last three inputs of every sequence); the q, k, v and gate outputs are not made.
+hipError_t launch_conv_state(const FrontendArgs& a);
 
 // Backward of the chunked prefill (fp32 workspace, chunk 64).  Offsets are
 // bytes into the workspace; per chunk-head arrays hold max_chunks * H slices.

@@ -768,13 +768,78 @@ struct IntraBfSmem {
     float gam[Cf::C], beta[Cf::C], sw[Cf::C];
 };
 
-template <int DK, int DV>
+// The front end folded into the row loads: chunk rows j0 .. j0 + NR - 1 of one
+// 8-channel group, each y_t = silu(4-tap causal convolution) of the bf16
+// projection x ([tokens][ld], columns col .. col + 7; channels chan .. chan + 7
+// of the concatenated conv axis for the taps and the conv state), rounded to
+// bf16 exactly as the standalone front end rounds it.  The three inputs before
+// a sequence come from its conv state (zeros without one); rows at or past
+// len are zero (and nothing past them is read).  The NR + 3 rows are read once
+// and the window slides down them in registers.
+template <int NR>
+__device__ __forceinline__ void conv_strip(const uint16_t* __restrict__ x, int64_t ld, int col, const FrontIn& fe,
+                                           int32_t ctot, int32_t chan, int32_t seq, int64_t seq_start, int64_t tok0,
+                                           int j0, int len, uint4 (&out)[NR])
+{
+    float wt[8][4];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const f32x4 t = *reinterpret_cast<const f32x4*>(fe.w + (int64_t)(chan + e) * 4);
+        wt[e][0] = t[0]; wt[e][1] = t[1]; wt[e][2] = t[2]; wt[e][3] = t[3];
+    }
+    uint4 raw[NR + 3];
+#pragma unroll
+    for (int m = 0; m < NR + 3; ++m) {
+        const int j = j0 - 3 + m;  // chunk row (negative: before the chunk)
+        const int64_t p = tok0 + j;
+        uint4 r = {0u, 0u, 0u, 0u};
+        if (j < len) {
+            if (p >= seq_start) {
+                r = *reinterpret_cast<const uint4*>(x + p * ld + col);
+            } else if (fe.state_in) {
+                const int sl = 3 - (int)(seq_start - p);  // slot of the conv state, oldest first
+                if (sl >= 0)
+                    r = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(fe.state_in) +
+                                                         ((int64_t)seq * 3 + sl) * ctot + chan);
+            }
+        }
+        raw[m] = r;
+    }
+    auto widen = [](uint4 r, float (&y)[8]) {
+        const uint32_t u[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            y[2 * i] = __uint_as_float(u[i] << 16);
+            y[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+        }
+    };
+    float h0[8], h1[8], h2[8];
+    widen(raw[0], h0);
+    widen(raw[1], h1);
+    widen(raw[2], h2);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        float xr[8], y[8];
+        widen(raw[r + 3], xr);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            y[e] = conv4_silu(wt[e], h0[e], h1[e], h2[e], xr[e]);
+            h0[e] = h1[e];
+            h1[e] = h2[e];
+            h2[e] = xr[e];
+        }
+        uint4 o = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7])};
+        out[r] = j0 + r < len ? o : uint4{0u, 0u, 0u, 0u};
+    }
+}
+
+template <int DK, int DV, bool FE>
 __device__ __forceinline__ void intra_chunk_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                  const uint16_t* __restrict__ v, const float* __restrict__ g,
                                                  const float* __restrict__ beta, const int32_t* __restrict__ header,
                                                  const ChunkInfo* __restrict__ tab, int32_t varlen, int64_t T,
                                                  int32_t H, int32_t l2norm, unsigned char* __restrict__ records,
-                                                 size_t record_bytes, int64_t c, int64_t slot)
+                                                 size_t record_bytes, int64_t c, int64_t slot, const FrontIn& fe)
 {
     using M = Mma<uint16_t>;
     using F = Mma<float>;
@@ -803,32 +868,98 @@ __device__ __forceinline__ void intra_chunk_bf16(const uint16_t* __restrict__ q,
     float* recU = reinterpret_cast<float*>(recb + R::U_BYTE_OFF);
     const int64_t row0 = (int64_t)ci.tok0 * H + h;  // row index of token tok0 in [tokens*H]
 
-    // ---- phase 1: every global read of the chunk, issued up front
+    // ---- phase 1: every global read of the chunk, issued up front.  Thread
+    // tid owns the 16-byte row pieces (j, ch) of K and V given by kmap / vmap:
+    // strided over rows when q, k, v are inputs; with the front end folded in
+    // (FE), KLD (VLD) consecutive rows of one 8-channel group, so that the
+    // 4-token window slides down them and each projection row is read once,
+    // plus three halo rows per strip.
+    auto kmap = [&](int s, int& j, int& ch) {
+        if constexpr (FE) {
+            ch = tid % KCPR;
+            j = (tid / KCPR) * Cf::KLD + s;
+        } else {
+            const int qi = s * 256 + tid;
+            j = qi / KCPR;
+            ch = qi % KCPR;
+        }
+    };
+    auto vmap = [&](int s, int& j, int& ch) {
+        if constexpr (FE) {
+            ch = tid % VCPR;
+            j = (tid / VCPR) * Cf::VLD + s;
+        } else {
+            const int qi = s * 256 + tid;
+            j = qi / VCPR;
+            ch = qi % VCPR;
+        }
+    };
+    const int32_t ctot = H * (2 * DK + DV);                    // FE: channels of the conv axis
+    const int64_t seq_start = FE && varlen ? fe.cu[ci.seq] : 0;  // FE: first token of the chunk's sequence
     float gv = 0.f, bv = 0.f;
     if (wave == 0 && lane < len) {
-        gv = g[row0 + (int64_t)lane * H];
-        bv = beta[row0 + (int64_t)lane * H];
+        if constexpr (FE) {
+            const int64_t e = row0 + (int64_t)lane * H;
+            gv = gate_g(fe.a[e], fe.A_log[h], fe.dt_bias[h]);
+            bv = gate_beta(fe.b[e]);
+        } else {
+            gv = g[row0 + (int64_t)lane * H];
+            bv = beta[row0 + (int64_t)lane * H];
+        }
     }
     uint4 kr[Cf::KLD];
+    if constexpr (FE) {
+        int j0, ch;
+        kmap(0, j0, ch);
+        conv_strip<Cf::KLD>(reinterpret_cast<const uint16_t*>(fe.xk), (int64_t)H * DK, h * DK + ch * 8, fe, ctot,
+                            H * DK + h * DK + ch * 8, ci.seq, seq_start, ci.tok0, j0, len, kr);
+    } else {
 #pragma unroll
-    for (int s = 0; s < Cf::KLD; ++s) {
-        const int qi = s * 256 + tid, j = qi / KCPR, ch = qi % KCPR;
-        kr[s] = j < len ? *reinterpret_cast<const uint4*>(k + (row0 + (int64_t)j * H) * DK + ch * 8)
-                        : uint4{0u, 0u, 0u, 0u};
+        for (int s = 0; s < Cf::KLD; ++s) {
+            int j, ch;
+            kmap(s, j, ch);
+            kr[s] = j < len ? *reinterpret_cast<const uint4*>(k + (row0 + (int64_t)j * H) * DK + ch * 8)
+                            : uint4{0u, 0u, 0u, 0u};
+        }
     }
     const int r_own = wave * 16 + l16;  // the chunk row (column of the products) this lane owns
     const bool live = r_own < len;
     Frag qf[DKS];  // Q row r_own in sigma order over d_k: operand of R and the stored Q fragments
+    if constexpr (FE) {
+        // the convolved Q rows pass through the A / T region of LDS (free until phase 2)
+        // as a row tile, from which the sigma fragments are read below
+        uint4 qr[Cf::KLD];
+        int j0, ch;
+        kmap(0, j0, ch);
+        conv_strip<Cf::KLD>(reinterpret_cast<const uint16_t*>(fe.xq), (int64_t)H * DK, h * DK + ch * 8, fe, ctot,
+                            h * DK + ch * 8, ci.seq, seq_start, ci.tok0, j0, len, qr);
+        static_assert(sizeof(sm.at) + sizeof(sm.tt) >= sizeof(uint16_t) * C * DK, "Q tile fits the A and T region");
+        uint16_t* qt = reinterpret_cast<uint16_t*>(sm.at);
 #pragma unroll
-    for (int ks = 0; ks < DKS; ++ks)
-        qf[ks] = live ? M::ld_sigma(q + (row0 + (int64_t)r_own * H) * DK + ks * 32, g16) : zero_frag<uint16_t>();
+        for (int s = 0; s < Cf::KLD; ++s)
+            *reinterpret_cast<uint4*>(qt + (j0 + s) * DK + (KX::chunk(j0 + s, ch) << 3)) = qr[s];
+    } else {
+#pragma unroll
+        for (int ks = 0; ks < DKS; ++ks)
+            qf[ks] = live ? M::ld_sigma(q + (row0 + (int64_t)r_own * H) * DK + ks * 32, g16) : zero_frag<uint16_t>();
+    }
     uint4 vr[Cf::VLD];
     auto load_v = [&](int pass) {
+        if constexpr (FE) {
+            int j0, ch;
+            vmap(0, j0, ch);
+            conv_strip<Cf::VLD>(reinterpret_cast<const uint16_t*>(fe.xv), (int64_t)H * DV, h * DV + pass * Cf::VP + ch * 8,
+                                fe, ctot, 2 * H * DK + h * DV + pass * Cf::VP + ch * 8, ci.seq, seq_start, ci.tok0,
+                                j0, len, vr);
+        } else {
 #pragma unroll
-        for (int s = 0; s < Cf::VLD; ++s) {
-            const int qi = s * 256 + tid, j = qi / VCPR, ch = qi % VCPR;
-            vr[s] = j < len ? *reinterpret_cast<const uint4*>(v + (row0 + (int64_t)j * H) * DV + pass * Cf::VP + ch * 8)
-                            : uint4{0u, 0u, 0u, 0u};
+            for (int s = 0; s < Cf::VLD; ++s) {
+                int j, ch;
+                vmap(s, j, ch);
+                vr[s] = j < len ? *reinterpret_cast<const uint4*>(v + (row0 + (int64_t)j * H) * DV + pass * Cf::VP +
+                                                                  ch * 8)
+                                : uint4{0u, 0u, 0u, 0u};
+            }
         }
     };
     load_v(0);
@@ -845,20 +976,27 @@ __device__ __forceinline__ void intra_chunk_bf16(const uint16_t* __restrict__ q,
     }
 #pragma unroll
     for (int s = 0; s < Cf::KLD; ++s) {
-        const int qi = s * 256 + tid, j = qi / KCPR, ch = qi % KCPR;
+        int j, ch;
+        kmap(s, j, ch);
         *reinterpret_cast<uint4*>(sm.x + j * DK + (KX::chunk(j, ch) << 3)) = kr[s];
     }
     __syncthreads();
 
     // ---- phase 2: G, R against K row tiles 0..wave; A rows, P, Q fragments, row scales
-    auto lds_sigma = [&](int r, int ks) -> Frag {
-        const u16x4 lo = *reinterpret_cast<const u16x4*>(sm.x + KX::at(r, ks * 32 + 4 * g16));
-        const u16x4 hi = *reinterpret_cast<const u16x4*>(sm.x + KX::at(r, ks * 32 + 16 + 4 * g16));
+    auto tile_sigma = [&](const uint16_t* tl, int r, int ks) -> Frag {
+        const u16x4 lo = *reinterpret_cast<const u16x4*>(tl + KX::at(r, ks * 32 + 4 * g16));
+        const u16x4 hi = *reinterpret_cast<const u16x4*>(tl + KX::at(r, ks * 32 + 16 + 4 * g16));
         Frag f;
         f[0] = lo.x; f[1] = lo.y; f[2] = lo.z; f[3] = lo.w;
         f[4] = hi.x; f[5] = hi.y; f[6] = hi.z; f[7] = hi.w;
         return f;
     };
+    auto lds_sigma = [&](int r, int ks) -> Frag { return tile_sigma(sm.x, r, ks); };
+    if constexpr (FE) {
+#pragma unroll
+        for (int ks = 0; ks < DKS; ++ks) qf[ks] = tile_sigma(reinterpret_cast<const uint16_t*>(sm.at), r_own, ks);
+        __syncthreads();  // the Q tile is read; A may be written
+    }
     // 1/||x|| of the row whose sigma fragments this lane and its three partner lanes hold
     auto inv_norm = [&](const Frag* f, bool row_live) -> float {
         float ss = 0.f;
@@ -952,7 +1090,8 @@ __device__ __forceinline__ void intra_chunk_bf16(const uint16_t* __restrict__ q,
     auto store_v = [&]() {
 #pragma unroll
         for (int s = 0; s < Cf::VLD; ++s) {
-            const int qi = s * 256 + tid, j = qi / VCPR, ch = qi % VCPR;
+            int j, ch;
+            vmap(s, j, ch);
             *reinterpret_cast<uint4*>(sm.x + j * Cf::VP + (VX::chunk(j, ch) << 3)) = vr[s];
         }
     };
@@ -1104,24 +1243,26 @@ __device__ __forceinline__ void intra_chunk_bf16(const uint16_t* __restrict__ q,
     }
 }
 
-// One workgroup per (chunk, head), for the chunks [c_base, c_end).
-template <typename TIn, int C, int DK, int DV>
+// One workgroup per (chunk, head), for the chunks [c_base, c_end).  With FE
+// (bf16, chunk 64 only) the front end is folded into the row loads: fe holds
+// the projections and gate inputs, and q, k, v, g, beta are unused.
+template <typename TIn, int C, int DK, int DV, bool FE>
 __global__ __launch_bounds__(256) void intra_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
                                                     const TIn* __restrict__ v, const float* __restrict__ g,
                                                     const float* __restrict__ beta, const int32_t* __restrict__ header,
                                                     const ChunkInfo* __restrict__ tab, int32_t varlen, int64_t T,
                                                     int32_t H, int32_t l2norm,
                                                     unsigned char* __restrict__ records, size_t record_bytes,
-                                                    int64_t c_base, int64_t c_end, int64_t slot0)
+                                                    int64_t c_base, int64_t c_end, int64_t slot0, FrontIn fe)
 {
     // chunk c's record is slot c - slot0 of `records` (slot0 = 0 unless the
     // workspace holds a window of the chunks)
     const int64_t c = c_base + blockIdx.x;
     if (c >= c_end) return;
     if constexpr (sizeof(TIn) == 2 && C == 64)
-        intra_chunk_bf16<DK, DV>(q, k, v, g, beta, header, tab, varlen, T, H, l2norm, records, record_bytes, c,
-                                 c - slot0);
-    else
+        intra_chunk_bf16<DK, DV, FE>(q, k, v, g, beta, header, tab, varlen, T, H, l2norm, records, record_bytes, c,
+                                     c - slot0, fe);
+    else if constexpr (!FE)
         intra_chunk<TIn, C, DK, DV>(q, k, v, g, beta, header, tab, varlen, T, H, l2norm, records, record_bytes, c,
                                     c - slot0);
 }
@@ -1980,11 +2121,24 @@ static hipError_t run_prefill(const PrefillArgs& a)
         if (c1 <= c0) return hipSuccess;
         size_t smem = sizeof(IntraSmem<TIn, C, DK, DV>);
         if constexpr (sizeof(TIn) == 2 && C == 64) smem = sizeof(IntraBfSmem<DK, DV>);
-        const hipError_t e = lds_limit((const void*)intra_kernel<TIn, C, DK, DV>, smem);
+        const dim3 grid((uint32_t)(c1 - c0), a.H);
+        if constexpr (sizeof(TIn) == 2 && C == 64) {
+            if (a.fused) {
+                const hipError_t e = lds_limit((const void*)intra_kernel<TIn, C, DK, DV, true>, smem);
+                if (e != hipSuccess) return e;
+                hipLaunchKernelGGL((intra_kernel<TIn, C, DK, DV, true>), grid, dim3(256), smem, st, (const TIn*)nullptr,
+                                   (const TIn*)nullptr, (const TIn*)nullptr, (const float*)nullptr,
+                                   (const float*)nullptr, header, tab, varlen, a.T, a.H, a.l2norm, records,
+                                   a.lay.record_bytes, c0, c1, slot0, a.fe);
+                return hipGetLastError();
+            }
+        }
+        if (a.fused) return hipErrorInvalidValue;
+        const hipError_t e = lds_limit((const void*)intra_kernel<TIn, C, DK, DV, false>, smem);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((intra_kernel<TIn, C, DK, DV>), dim3((uint32_t)(c1 - c0), a.H), dim3(256), smem,
-                           st, (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, a.g, a.beta, header, tab, varlen,
-                           a.T, a.H, a.l2norm, records, a.lay.record_bytes, c0, c1, slot0);
+        hipLaunchKernelGGL((intra_kernel<TIn, C, DK, DV, false>), grid, dim3(256), smem, st, (const TIn*)a.q,
+                           (const TIn*)a.k, (const TIn*)a.v, a.g, a.beta, header, tab, varlen, a.T, a.H, a.l2norm,
+                           records, a.lay.record_bytes, c0, c1, slot0, FrontIn{});
         return hipGetLastError();
     };
     auto launch_chain = [&](int64_t c0, int64_t c1, hipStream_t st, int64_t slot0 = 0) -> hipError_t {
@@ -2161,7 +2315,29 @@ static hipError_t dispatch_f32_dk(const PrefillArgs& a)
     return hipErrorInvalidValue;
 }
 
+static hipError_t launch_prefill_stages(const PrefillArgs& a);
+
+// With the front end folded in, the conv state after the call (the last three
+// inputs of every sequence) is written once every preparation kernel has read
+// the state it was given (it may be overwritten in place): on `stream`, after
+// the prefill's last kernel, which every schedule orders after all the others.
 hipError_t launch_prefill(const PrefillArgs& a)
+{
+    const hipError_t e = launch_prefill_stages(a);
+    if (e != hipSuccess || !a.fused || !a.conv_state_out) return e;
+    FrontendArgs fa;
+    memset(&fa, 0, sizeof fa);
+    fa.xq = a.fe.xq; fa.xk = a.fe.xk; fa.xv = a.fe.xv;
+    fa.state_in = a.fe.state_in;
+    fa.state_out = a.conv_state_out;
+    fa.cu = a.cu_seqlens;
+    fa.N = a.N; fa.T = a.T; fa.H = a.H; fa.dk = a.dk; fa.dv = a.dv;
+    fa.bf16 = a.bf16;
+    fa.stream = a.stream;
+    return launch_conv_state(fa);
+}
+
+static hipError_t launch_prefill_stages(const PrefillArgs& a)
 {
     if (a.bf16) {
         if (a.chunk != 64) return hipErrorInvalidValue;

@@ -81,6 +81,10 @@ def load_library(path: str | None = None):
             lib.gdn_frontend_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
                                                  ctypes.c_int, vp, vp, vp, vp, vp, vp, vp]
             lib.gdn_frontend_prefill.restype = ctypes.c_int
+            lib.gdn_chunk_prefill_frontend.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i64,
+                                                       i32, i32, i32, i32, ctypes.c_int, f32, i32, vp, vp, vp, vp,
+                                                       sz, vp]
+            lib.gdn_chunk_prefill_frontend.restype = ctypes.c_int
             lib.gdn_frontend_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int,
                                                 vp, vp, vp, vp, vp, vp]
             lib.gdn_frontend_decode.restype = ctypes.c_int
@@ -479,6 +483,57 @@ def frontend_prefill(xq, xk, xv, conv_weight, a, b, A_log, dt_bias, conv_state=N
     if st != 0:
         raise GdnError(st, "gdn_frontend_prefill")
     return q, k, v, g, beta, conv_state_out
+
+
+def chunk_prefill_frontend(xq, xk, xv, conv_weight, a, b, A_log, dt_bias, conv_state=None, init_state=None,
+                           cu_seqlens=None, scale=None, qk_l2norm=True, chunk=64, out=None, final_state=None,
+                           return_conv_state=True, conv_state_out=None, workspace=None, ctx=None):
+    """The front end folded into the chunked prefill (bf16): the result of
+    ``frontend_prefill`` followed by ``chunk_prefill``, bit for bit, without the
+    q, k, v, g, beta round trip.  Arguments as for those two calls.  Returns
+    (o [T, H, dv], final_state [N, H, dv, dk], conv_state_out or None)."""
+    torch = _torch()
+    lib = load_library()
+    dev, dt, T, H, dk, dv, ctot = _frontend_args(xq, xk, xv, conv_weight, a, b, A_log, dt_bias)
+    cu_dev, cu_host, N = _seqlens(cu_seqlens, dev)
+    if conv_state is not None:
+        _check(conv_state, "conv_state", dtype=dt, device=dev)
+        if conv_state.shape != (N, 3, ctot):
+            raise ValueError(f"conv_state must be [{N}, 3, {ctot}]")
+    if conv_state_out is None and return_conv_state:
+        conv_state_out = torch.empty((N, 3, ctot), dtype=dt, device=dev)
+    elif conv_state_out is not None:
+        _check(conv_state_out, "conv_state_out", dtype=dt, device=dev)
+        if conv_state_out.shape != (N, 3, ctot):
+            raise ValueError(f"conv_state_out must be [{N}, 3, {ctot}]")
+    if init_state is not None:
+        _check(init_state, "init_state", dtype=torch.float32, device=dev)
+        if init_state.shape != (N, H, dv, dk):
+            raise ValueError(f"init_state must be [{N}, {H}, {dv}, {dk}]")
+    if out is None:
+        out = torch.empty((T, H, dv), dtype=dt, device=dev)
+    else:
+        _check(out, "out", dtype=dt, device=dev)
+    if final_state is None:
+        final_state = torch.empty((N, H, dv, dk), dtype=torch.float32, device=dev)
+    else:
+        _check(final_state, "final_state", dtype=torch.float32, device=dev)
+    code = _dtype_code(xq)
+    need = int(lib.gdn_prefill_workspace_size(T, N, H, dk, dv, chunk, code))
+    if need == 0:
+        raise GdnError(3, "gdn_prefill_workspace_size")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    s = -1.0 if scale is None else float(scale)
+    cu_host_ptr = None if cu_host is None else ctypes.c_void_p(cu_host.data_ptr())
+    st = lib.gdn_chunk_prefill_frontend(None if ctx is None else ctx.handle, _ptr(xq), _ptr(xk), _ptr(xv),
+                                        _ptr(conv_weight), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias),
+                                        _ptr(conv_state), _ptr(init_state), _ptr(cu_dev), cu_host_ptr, N, T, H, dk,
+                                        dv, chunk, code, s, int(bool(qk_l2norm)), _ptr(out), _ptr(final_state),
+                                        _ptr(conv_state_out), _ptr(workspace), workspace.numel(), _stream(dev))
+    if st != 0:
+        raise GdnError(st, "gdn_chunk_prefill_frontend")
+    return out, final_state, conv_state_out
 
 
 def frontend_decode(xq, xk, xv, conv_weight, a, b, A_log, dt_bias, conv_state, out=None):

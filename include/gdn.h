@@ -328,6 +328,34 @@ gdn_status gdn_frontend_decode(const void* xq, const void* xk, const void* xv, c
                                void* k, void* v, float* g, float* beta, hipStream_t stream);
 
 /*
+ * The front end folded into the chunked prefill: the same result as
+ * gdn_frontend_prefill followed by gdn_chunk_prefill_ctx, bit for bit, without
+ * the round trip of q, k, v, g and beta through device memory.  The paragraph
+ * under Table 8 of App. A.3 puts the short convolution with SiLU directly
+ * before the recurrence; here it runs inside the per-chunk preparation: each
+ * chunk's preparation reads the projections of its tokens plus the three
+ * before them (or the sequence's conv state), convolves, applies SiLU, rounds
+ * to bf16 as the front end does, and computes g and beta from a and b.
+ *
+ *   ctx, init_state, cu_seqlens, cu_seqlens_host, num_seqs, total_tokens, H,
+ *   dk, dv, chunk, scale, qk_l2norm, o, final_state, workspace,
+ *   workspace_bytes, stream      as for gdn_chunk_prefill_ctx (ctx may be NULL)
+ *   xq, xk, xv, conv_weight, a, b, A_log, dt_bias, conv_state_in,
+ *   conv_state_out               as for gdn_frontend_prefill
+ * Supported: dt = GDN_BF16, chunk 64 (the combinations of gdn_chunk_prefill
+ * for bf16); anything else returns GDN_ERR_UNSUPPORTED.  conv_state_out may
+ * alias conv_state_in exactly; it is written after every read of it.
+ */
+gdn_status gdn_chunk_prefill_frontend(gdn_context_t ctx, const void* xq, const void* xk, const void* xv,
+                                      const float* conv_weight, const float* a, const float* b, const float* A_log,
+                                      const float* dt_bias, const void* conv_state_in, const float* init_state,
+                                      const int32_t* cu_seqlens, const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                      int64_t total_tokens, int32_t H, int32_t dk, int32_t dv, int32_t chunk,
+                                      gdn_dtype dt, float scale, int32_t qk_l2norm, void* o, float* final_state,
+                                      void* conv_state_out, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream);
+
+/*
  * Bytes of device workspace gdn_chunk_prefill_backward needs for these sizes
  * (0 for an unsupported or invalid combination).  It holds fp32 per-chunk
  * intermediates, among them the state entering every chunk and the state
