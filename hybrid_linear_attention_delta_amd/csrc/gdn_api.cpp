@@ -97,6 +97,62 @@ PrefillLayout prefill_layout(int64_t T, int32_t N, int32_t H, int32_t dk, int32_
     return L;
 }
 
+// Workspace of the backward (fp32 per-chunk intermediates, chunk kBwdChunk).
+bool backward_supported(int32_t dk, int32_t dv)
+{
+    return (dk == 64 || dk == 128 || dk == 256) && (dv == 64 || dv == 128 || dv == 256);
+}
+
+BwdLayout backward_layout(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv)
+{
+    BwdLayout L;
+    memset(&L, 0, sizeof L);
+    L.max_chunks = T / kBwdChunk + N;
+    const size_t chs = (size_t)L.max_chunks * H;
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = up(off + bytes);
+        return o;
+    };
+    L.off_header = take(64);
+    L.off_tab = take((size_t)L.max_chunks * 16);
+    L.off_seq_first = take(((size_t)N + 1) * 4);
+    const size_t cdk = chs * kBwdChunk * dk * 4, cdv = chs * kBwdChunk * dv * 4;
+    const size_t cc = chs * kBwdChunk * kBwdChunk * 4, c1 = chs * kBwdChunk * 4;
+    const size_t st = chs * (size_t)dv * dk * 4;
+    L.off_Q = take(cdk);
+    L.off_K = take(cdk);
+    L.off_V = take(cdv);
+    L.off_dO = take(cdv);
+    L.off_rq = take(c1);
+    L.off_rk = take(c1);
+    L.off_gam = take(c1);
+    L.off_bet = take(c1);
+    L.off_T = take(cc);
+    L.off_P = take(cc);
+    L.off_KKG = take(cc);
+    L.off_W = take(cdk);
+    L.off_U = take(cdv);
+    L.off_DK = take(cdk);
+    L.off_E = take(cdv);
+    L.off_dDl = take(cdv);
+    L.off_S = take(st);
+    L.off_Dl = take(cdv);
+    L.off_dS = take(st);
+    L.off_dD = take(cdv);
+    L.off_dQ = take(cdk);
+    L.off_dK = take(cdk);
+    L.off_dW = take(cdk);
+    L.off_dPG = take(cc);
+    L.off_dT = take(cc);
+    L.off_X1 = take(cc);
+    L.off_Bd = take(cc);
+    L.total = off;
+    return L;
+}
+
 }  // namespace gdn
 
 extern "C" {

@@ -147,6 +147,7 @@ struct BwdLayout {
     size_t total;
 };
 
+constexpr int kBwdChunk = 64;  // chunk length of the backward
 bool backward_supported(int32_t dk, int32_t dv);
 BwdLayout backward_layout(int64_t total_tokens, int32_t num_seqs, int32_t H, int32_t dk, int32_t dv);
 
