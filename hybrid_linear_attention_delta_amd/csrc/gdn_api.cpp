@@ -68,12 +68,15 @@ PrefillLayout prefill_layout(int64_t T, int32_t N, int32_t H, int32_t dk, int32_
     // chunks whose per-chunk data the workspace holds at once
     const int64_t held = window_chunks > 0 && window_chunks < L.max_chunks ? window_chunks : L.max_chunks;
     const size_t el = bf16 ? 2 : 4;
-    // record: W fragments (C x dk), raw K^T fragments (dk x C), raw Q fragments
-    // (C x dk), P fragments (C x C, hi+lo for bf16) in the operand element type;
-    // then U tiles (C x dv), two per-row scale vectors (C each) and the chunk
-    // decay with the chunk's token range in fp32/int32.
+    // record, operand element type: fp32, W fragments (C x dk), raw K^T
+    // fragments (dk x C), raw Q fragments (C x dk), P fragments (C x C); bf16,
+    // the raw K rows (C x dk), T' = T diag(beta e^gamma r_k) (C x C), raw Q
+    // fragments (C x dk), P fragments (C x C, hi and lo).  Then U tiles (C x dv),
+    // two per-row scale vectors (C each) and the chunk decay with the chunk's
+    // token range in fp32/int32.
     const size_t split = bf16 ? 2 : 1;
-    const size_t oper = align_up(((size_t)C * dk * 3 + (size_t)C * C * split) * el, 16);
+    const size_t oper = bf16 ? align_up(((size_t)C * dk * 2 + (size_t)C * C * 3) * el, 16)
+                             : align_up(((size_t)C * dk * 3 + (size_t)C * C) * el, 16);
     L.record_bytes = align_up(oper + (size_t)C * dv * 4 + (size_t)C * 8 + 16, 256);
     size_t off = 0;
     L.off_header = off;

@@ -23,20 +23,26 @@
 //   chunk_table_kernel  varlen only: chunk table from cu_seqlens, on device.
 //   intra_kernel        one workgroup per (chunk, head), fully parallel:
 //                       norms, gamma, A and P on MFMA, T by forward
-//                       substitution in LDS, W and U on MFMA.  Writes an
-//                       operand record per chunk-head whose fragments are laid
-//                       out exactly in the per-lane order of the MFMA operands
-//                       of the chain kernel (one 16-byte load per operand).
-//   chain_kernel        one workgroup per (sequence, head, 16 state rows):
-//                       sequential over the sequence's chunks; state tile in
-//                       fp32 MFMA accumulators, a rounded copy in LDS as the
-//                       MFMA operand; computes Delta and the state update;
-//                       writes the state entering every chunk, every chunk's
-//                       Delta and the final state.  Eight compute waves run
-//                       only LDS and MFMA work between three barriers per
-//                       chunk; in the bf16 form, seven loader waves stage the
-//                       operands through registers into LDS and one wave
-//                       prefetches chunks ahead into L2.
+//                       substitution in LDS, U (and for fp32 W) on MFMA.
+//                       Writes an operand record per chunk-head whose
+//                       fragments are laid out exactly in the per-lane order
+//                       of the MFMA operands of the later kernels (one
+//                       16-byte load per operand); for bf16 it holds the raw
+//                       K rows and T' = T diag(beta e^{gamma} r_k) in place
+//                       of W = T' K.
+//   chain_kr_kernel     bf16: one workgroup of 16 waves per (sequence, head,
+//                       16 state rows), sequential over the sequence's chunks;
+//                       state tile in fp32 MFMA accumulators, a rounded copy in
+//                       LDS as the MFMA operand; Delta = U - T' (K S^T) and the
+//                       state update from the chunk's K tile in LDS (row reads
+//                       and transposing reads); writes the state entering
+//                       every chunk, every chunk's Delta and the final state.
+//                       Eight compute waves run only LDS and MFMA work between
+//                       three barriers per chunk; loader waves bring the
+//                       operands two chunks ahead by LDS-DMA and write the
+//                       per-chunk outputs.
+//   chain_kernel        fp32: the same recurrence as Delta = U - W S^T with W
+//                       and K^T fragments read from the record.
 //   output_kernel       one workgroup per (chunk, head), fully parallel: the
 //                       outputs O of the chunk from Q, P, the state entering
 //                       the chunk and Delta.
@@ -190,7 +196,8 @@ template <> struct Quad<float> {
 // stored as hi = bf16(x), lo = bf16(x - hi), so hi + lo carries ~16 bits and a
 // product takes two MFMAs.  K enters as the exact stored input (its per-row
 // scale moves to the other operand in fp32); so does Q (read from the input,
-// its row scale applied to the fp32 result).
+// its row scale applied to the fp32 result).  This general layout serves the
+// fp32 operands; the bf16 record (chunk 64) is the specialisation below.
 template <typename TIn, int C, int DK, int DV>
 struct Rec {
     static constexpr bool SPLIT = sizeof(TIn) == 2;
@@ -214,6 +221,37 @@ struct Rec {
     static constexpr size_t DEC_BYTE_OFF = KSC_BYTE_OFF + (size_t)C * 4;    // {e^{gamma_L}, tok0, len, 0} (f32, i32, i32)
     static constexpr size_t BYTES = DEC_BYTE_OFF + 16;
     static_assert(C % KS == 0 && DK % KS == 0, "tile shape");
+};
+
+// bf16 (chunk 64): the state chain forms X = W S^T as T' (K^ S^T), with
+// T' = T diag(beta e^{gamma} r_k) the 64 x 64 factor of W = T' K^.  The record
+// therefore carries the chunk's raw K rows (once, in the LDS tile order of the
+// chain, from which the chain reads both K^ and K^T fragments) and T', instead
+// of the W and K^T fragments: 40 KB instead of 64 KB of the chain's operands
+// per chunk-head at d_k = 256.  The chain's per-chunk operand volume is what
+// bounds it (each workgroup streams the chunk's operands from L2 every step).
+template <int C, int DK, int DV>
+struct Rec<uint16_t, C, DK, DV> {
+    static constexpr bool SPLIT = true;
+    static constexpr int KS = 32, E = 8;
+    static constexpr int RT = C / 16;               // chunk row tiles
+    static constexpr int DKS = DK / KS;             // k-steps over d_k
+    static constexpr int CKS = C / KS;              // k-steps over the chunk
+    static constexpr int MT = DK / 16;              // d_k tiles
+    static constexpr int VT = DV / 16;              // d_v tiles
+    static constexpr int KR_OFF = 0;                // [C][DK] raw K rows, KTile<DK> layout; rows >= len zero
+    static constexpr int TP_OFF = KR_OFF + C * DK;  // [RT][CKS][64][E] T' (bf16), sigma over the chunk
+    static constexpr int Q_OFF = TP_OFF + C * C;    // [RT][DKS][64][E] raw Q, sigma over d_k
+    static constexpr int PH_OFF = Q_OFF + C * DK;   // [RT][CKS][64][E] P hi
+    static constexpr int PL_OFF = PH_OFF + C * C;   // [RT][CKS][64][E] P lo
+    static constexpr int CHAIN_ELEMS = Q_OFF;       // the state chain's shared operands: K rows, T'
+    static constexpr int OPER_ELEMS = PL_OFF + C * C;
+    static constexpr size_t U_BYTE_OFF = ((size_t)OPER_ELEMS * 2 + 15) / 16 * 16;  // f32 [RT][VT][64][4]
+    static constexpr size_t QS_BYTE_OFF = U_BYTE_OFF + (size_t)C * DV * 4;
+    static constexpr size_t KSC_BYTE_OFF = QS_BYTE_OFF + (size_t)C * 4;
+    static constexpr size_t DEC_BYTE_OFF = KSC_BYTE_OFF + (size_t)C * 4;
+    static constexpr size_t BYTES = DEC_BYTE_OFF + 16;
+    static_assert(C == 64 && DK % KS == 0, "tile shape");
 };
 
 // Position of the four consecutive columns 16*tile + 4*g .. +3 inside an LDS
@@ -743,6 +781,33 @@ struct RowTile {
     static __device__ __forceinline__ int at(int j, int col) { return j * W + (chunk(j, col >> 3) << 3) + (col & 7); }
 };
 
+// The state chain's K tile (bf16, chunk 64 x DK, in the record and in the
+// chain's LDS): row j holds the chunk's raw K row j in 8-byte units of four
+// columns; logical unit 8 kb + 2 g + u holds columns 32 kb + 16 u + 4 g .. + 3
+// (so units 2 (4 kb + g) and 2 (4 kb + g) + 1 are the sigma-ordered operand
+// slots of lane group g for k-step kb), stored at unit (8 kb + 2 g + u) ^ s(j).
+// s(j) places row bits 0, 2, 1, 3 at unit bits 0, 2, 3, 4.  A row fragment
+// is two 8-byte reads, and four consecutive columns of a 16-column tile are
+// one 8-byte unit, as the transposing read needs.  Both are free of LDS bank
+// conflicts: the 32 lanes of one pass touch 32 distinct bank pairs, for a
+// row-fragment half (16 consecutive rows x 2 lane groups) as for a
+// transposing read (rows 8 g + 4 h + i of 2 lane groups x 4 units).  (A
+// 16-byte row read with the halves swapped on odd rows, which the same
+// conditions allow, measured slower.)
+template <int DK>
+struct KTile {
+    static constexpr int UPR = DK / 4;  // 8-byte units per row
+    static __device__ __forceinline__ int swz(int j)
+    {
+        return ((j & 1) | (j & 4) | ((j & 2) << 2) | ((j & 8) << 1)) & (UPR - 1);
+    }
+    // element offset of unit (block kb, lane group g, half u) of row j
+    static __device__ __forceinline__ int at(int j, int kb, int g, int u)
+    {
+        return j * DK + (((8 * kb + 2 * g + u) ^ swz(j)) << 2);
+    }
+};
+
 template <int DK, int DV>
 struct IntraBf {
     static constexpr int C = 64;
@@ -1065,24 +1130,19 @@ __device__ __forceinline__ void intra_chunk_bf16(const uint16_t* __restrict__ q,
         reinterpret_cast<float*>(recb + R::QS_BYTE_OFF)[r_own] = rq * eg;
         reinterpret_cast<float*>(recb + R::KSC_BYTE_OFF)[r_own] = rk * expf(gL - gam_r);
     }
-    // raw K^T fragments (identity over the chunk) of this wave's d_k blocks: stored,
-    // and kept as the W operand
-    Frag kT[Cf::DBW][2][2];
+    // the raw K rows for the state chain in its tile layout (rows >= len zero):
+    // stored units 2 p, 2 p + 1 of row j hold logical units (2 p) ^ s(j) and
+    // (2 p + 1) ^ s(j), the two halves of piece (block, lane group) = p ^ (s(j) / 2),
+    // swapped when s(j) is odd
 #pragma unroll
-    for (int b = 0; b < Cf::DBW; ++b) {
-        const int dks = wave + 4 * b;
-        if (dks >= DKS) break;
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-            for (int jk = 0; jk < 2; ++jk) {
-                const int col = (2 * dks + u) * 16 + l16;
-                Frag f;
-#pragma unroll
-                for (int e = 0; e < E; ++e) f[e] = sm.x[KX::at(jk * 32 + g16 * 8 + e, col)];
-                kT[b][u][jk] = f;
-                st_frag<uint16_t>(rec + R::K_OFF + ((size_t)((2 * dks + u) * R::CKS + jk) * 64 + lane) * E, f);
-            }
+    for (int s = 0; s < Cf::KLD; ++s) {
+        const int pc = s * 256 + tid;  // stored 16-byte chunk
+        const int j = pc / KCPR, sw = KTile<DK>::swz(j), lp = (pc % KCPR) ^ (sw >> 1), kb = lp >> 2, gp = lp & 3;
+        const u16x4 lo = *reinterpret_cast<const u16x4*>(sm.x + KX::at(j, kb * 32 + 4 * gp));
+        const u16x4 hi = *reinterpret_cast<const u16x4*>(sm.x + KX::at(j, kb * 32 + 16 + 4 * gp));
+        const u16x8 v = (sw & 1) ? u16x8{hi.x, hi.y, hi.z, hi.w, lo.x, lo.y, lo.z, lo.w}
+                                 : u16x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        __builtin_nontemporal_store(v, reinterpret_cast<u16x8*>(rec + R::KR_OFF + pc * 8));
     }
     __syncthreads();  // K rows no longer read; A complete
 
@@ -1140,10 +1200,10 @@ __device__ __forceinline__ void intra_chunk_bf16(const uint16_t* __restrict__ q,
         __syncthreads();
     }
 
-    // ---- phase 4: W^T = K^T (T diag(sw))^T and U = (T diag(beta)) V, T split hi/lo.
-    // Row r = 16 rt + l16 of T diag(x) over k-step jk is both the B operand of W^T
-    // and the A operand of U; entries above the diagonal are zero (masked here,
-    // the blocks above the diagonal are never written).
+    // ---- phase 4: T' = T diag(sw) for the state chain, and U = (T diag(beta)) V with
+    // T diag(beta) split hi/lo.  Row r = 16 rt + l16 of T diag(beta) over k-step jk
+    // is the A operand of U; entries above the diagonal are zero (masked here, the
+    // blocks above the diagonal are never written).
     auto t_frags = [&](int rt, int jk, bool want_w, Frag& swh, Frag& swl, Frag& sbh, Frag& sbl) {
         const int r = rt * 16 + l16, j0 = jk * 32 + g16 * 8;
         const f32x4 t0 = *reinterpret_cast<const f32x4*>(sm.tt + r * AP + j0);
@@ -1188,6 +1248,23 @@ __device__ __forceinline__ void intra_chunk_bf16(const uint16_t* __restrict__ q,
             __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(recU + ((size_t)(rt * R::VT + vg) * 64 + lane) * 4));
         }
     };
+    // T' = T diag(sw): row tile `wave`, both k-steps, sigma order over the chunk
+    // (lane group g, element e holds column 32 ks + 16 (e / 4) + 4 g + e % 4);
+    // zero above the diagonal
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        const int r = wave * 16 + l16, j0 = ks * 32 + 4 * g16;
+        const f32x4 t0 = *reinterpret_cast<const f32x4*>(sm.tt + r * AP + j0);
+        const f32x4 t1 = *reinterpret_cast<const f32x4*>(sm.tt + r * AP + j0 + 16);
+        float x[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int j = j0 + 16 * (e >> 2) + (e & 3);
+            const float tv = e < 4 ? t0[e & 3] : t1[e & 3];
+            x[e] = j <= r ? tv * sm.sw[j] : 0.f;
+        }
+        st_frag<uint16_t>(rec + R::TP_OFF + ((size_t)(wave * R::CKS + ks) * 64 + lane) * E, frag_from<uint16_t>(x));
+    }
     {
         Frag vf[Cf::VTW][2];
         v_frags(vf);
@@ -1197,29 +1274,7 @@ __device__ __forceinline__ void intra_chunk_bf16(const uint16_t* __restrict__ q,
             Frag swh[2], swl[2], sbh[2], sbl[2];
 #pragma unroll
             for (int jk = 0; jk < 2; ++jk)
-                if (jk < nks) t_frags(rt, jk, true, swh[jk], swl[jk], sbh[jk], sbl[jk]);
-#pragma unroll
-            for (int b = 0; b < Cf::DBW; ++b) {
-                const int dks = wave + 4 * b;
-                if (dks >= DKS) break;
-                f32x4 acc[2];
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int jk = 0; jk < 2; ++jk) {
-                        if (jk >= nks) break;
-                        acc[u] = M::mma(kT[b][u][jk], swh[jk], acc[u]);
-                        acc[u] = M::mma(kT[b][u][jk], swl[jk], acc[u]);
-                    }
-                }
-                float x[E];
-#pragma unroll
-                for (int u = 0; u < 2; ++u)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) x[u * 4 + i] = acc[u][i];
-                st_frag<uint16_t>(rec + R::WH_OFF + ((size_t)(rt * DKS + dks) * 64 + lane) * E, frag_from<uint16_t>(x));
-            }
+                if (jk < nks) t_frags(rt, jk, false, swh[jk], swl[jk], sbh[jk], sbl[jk]);
             u_tiles(0, rt, nks, vf, sbh, sbl);
         }
     }
@@ -1312,16 +1367,7 @@ __device__ __forceinline__ void lds_barrier()
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// The chain kernel stages its operands in LDS for bf16 operands (chunk 64);
-// fp32 operands of the production shape are read from the records directly.
-template <typename TIn, int C>
-constexpr bool chain_staged() { return sizeof(TIn) == 2 && C == 64; }
-// Loader waves of the staged form (they bring in every operand and write the
-// per-chunk states and Delta out).
-template <typename TIn, int C>
-constexpr int chain_loaders() { return chain_staged<TIn, C>() ? 8 : 0; }
-
-// Work split of the chain kernel over NW compute waves (NW a multiple of 4).
+// Work split of the fp32 chain kernel over NW compute waves (NW a multiple of 4).
 template <typename TIn, int C, int DK, int DV, int NW>
 struct ChainSplit {
     using R = Rec<TIn, C, DK, DV>;
@@ -1335,7 +1381,7 @@ struct ChainSplit {
 //   states: [chunk][H][DV][DK] operand type, the state entering the chunk; bf16
 //           rows are in sigma order within each 32-column block
 //   deltas: [chunk][H][NS][DV][C] operand type, Delta^T (hi, lo for bf16), sigma
-//           order over the chunk positions
+//           order over the chunk positions (natural order for fp32)
 template <typename TIn, int C, int DK, int DV>
 struct ChainOut {
     static constexpr int NS = sizeof(TIn) == 2 ? 2 : 1;
@@ -1343,30 +1389,16 @@ struct ChainOut {
     static constexpr size_t DELTA_ELEMS = (size_t)NS * DV * C;
 };
 
-// LDS of the chain kernel.  In the staged form every per-chunk operand is
-// written here by dedicated loader waves; each operand region is
-// single-buffered and refilled as soon as its last reader has passed a
-// barrier.  Without STAGE (fp32 operands) the operands are read from the
-// records directly.
-template <typename TIn, int C, int DK, int DV, int NW, bool STAGE>
+// LDS of the fp32 chain kernel (its operands are read from the records directly).
+template <int C, int DK, int DV, int NW>
 struct ChainLds {
-    using R = Rec<TIn, C, DK, DV>;
-    using P = ChainSplit<TIn, C, DK, DV, NW>;
-    static constexpr int SP = DK + 16 / (int)sizeof(TIn);  // state copy pitch (dwords = 4 mod 32)
-    static constexpr int DP = C + 16 / (int)sizeof(TIn);   // Delta^T pitch
-    static constexpr int NS = R::SPLIT ? 2 : 1;
+    using P = ChainSplit<float, C, DK, DV, NW>;
+    static constexpr int SP = DK + 4;  // state copy pitch (dwords = 4 mod 32)
+    static constexpr int DP = C + 4;   // (kscale o Delta)^T pitch
     static constexpr int RT = C / 16;
-    // operand fragment slots (1 KB each: 64 lanes x 16 B, lane order)
-    static constexpr int F_U = 0;                          // [RT] U (this workgroup's 16 value columns)
-    static constexpr int F_SINK = F_U + RT;                // landing slot of prefetch transfers
-    static constexpr int NFRAG = STAGE ? F_SINK + 1 : 1;
-    unsigned char frag[NFRAG][1024];
-    float ksc[C];                     // k row scales
-    f32x4 meta[16];                   // [0] = e^{gamma_L}, tok0, len (a 256-byte landing area)
-    TIn sr[16 * SP];                  // state rows S[r][col] rounded to operands, sigma order
-    TIn dt[NS][16 * DP];              // Delta^T[r][j], sigma order (hi, lo)
-    TIn ds[NS][16 * DP];              // (kscale o Delta)^T[r][j], natural order (hi, lo)
-    f32x4 xp[P::KQ][RT][64];          // partial W S^T per d_k part
+    float sr[16 * SP];                 // state rows S[r][col]
+    float ds[16 * DP];                 // (kscale o Delta)^T[r][j]
+    f32x4 xp[P::KQ][RT][64];           // partial W S^T per d_k part
 };
 
 template <int N>
@@ -1376,55 +1408,46 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// State chain: one workgroup per (sequence, head, 16 state rows), sequential
-// over the sequence's chunks.  Per chunk c, the NW compute waves
+// State chain, fp32 operands: one workgroup of NW waves per (sequence, head,
+// 16 state rows), sequential over the sequence's chunks, operands read from the
+// record.  Per chunk c:
 //   phase 1  wave (rt, kq) = (w % 4, w / 4): partial X = W S^T of chunk row
 //            tile rt over d_k part kq (partials to LDS)
-//   phase 2  wave (rt, 0): Delta = U - X -> LDS (sigma and natural order, hi/lo)
+//   phase 2  wave (rt, 0): Delta = U - X (k-scaled copy to LDS, Delta^T to `deltas`)
 //   phase 3  every wave, its state d_k tiles: S^T = e^{gamma_L} S^T + K^T (kscale o Delta)
-// separated by the barriers A, B, C.  The state entering chunk c and Delta of
-// chunk c go to `states` and `deltas` for the output kernel (by the loader
-// waves in the staged form, else by the compute waves).
-// Workgroups are mapped so that all row tiles of one (sequence, head) pair run
-// on one XCD (workgroups are dealt to the 8 XCDs round-robin): they read the
-// same per-chunk records, which then come from that XCD's L2.  Pair indices
-// follow seq_order (longest sequence first) in a packed batch, so when there
-// are more workgroups than CUs the longest chains are dispatched first.
-template <typename TIn, int C, int DK, int DV, int NW, bool SEG>
-__global__ __launch_bounds__((NW + chain_loaders<TIn, C>()) * 64) void chain_kernel(
+// separated by the barriers A, B, C; the state entering chunk c goes to
+// `states`.  Workgroups are mapped so that all row tiles of one (sequence,
+// head) pair run on one XCD (workgroups are dealt to the 8 XCDs
+// round-robin): they read the same per-chunk records, which then come from
+// that XCD's L2.  Pair indices follow seq_order (longest sequence first) in a
+// packed batch, so when there are more workgroups than CUs the longest chains
+// are dispatched first.
+template <int C, int DK, int DV, int NW, bool SEG>
+__global__ __launch_bounds__(NW * 64) void chain_kernel(
     const int32_t* __restrict__ header, const int32_t* __restrict__ seq_first,
-    const int32_t* __restrict__ seq_order, int32_t varlen, int64_t T, int32_t H, int32_t pairs, const unsigned char* records, size_t record_bytes, const float* init_state,
-    float* final_state, TIn* __restrict__ states, TIn* __restrict__ deltas, int64_t seg_begin, int64_t seg_end,
-    float* carry, int64_t slot0)
-// (records is deliberately not __restrict__: a restrict read-only argument lets
-// the compiler treat its loads as invariant and sink them across the barriers
-// to their use, which would turn the loaders' early loads into late ones)
+    const int32_t* __restrict__ seq_order, int32_t varlen, int64_t T, int32_t H, int32_t pairs,
+    const unsigned char* records, size_t record_bytes, const float* init_state, float* final_state,
+    float* __restrict__ states, float* __restrict__ deltas, int64_t seg_begin, int64_t seg_end, float* carry,
+    int64_t slot0)
 {
+    using TIn = float;
     using M = Mma<TIn>;
     using R = Rec<TIn, C, DK, DV>;
     using P = ChainSplit<TIn, C, DK, DV, NW>;
     using CO = ChainOut<TIn, C, DK, DV>;
-    constexpr bool SPL = R::SPLIT;
-    constexpr bool STAGE = chain_staged<TIn, C>();
-    constexpr int NL = chain_loaders<TIn, C>();
-    using L = ChainLds<TIn, C, DK, DV, NW, STAGE>;
+    using L = ChainLds<C, DK, DV, NW>;
     typedef typename M::Frag Frag;
     constexpr int KS = M::KS, E = M::E;
-    constexpr int SP = L::SP, DP = L::DP, NS = L::NS;
-    constexpr int RT = R::RT;
+    constexpr int SP = L::SP, DP = L::DP;
     constexpr int TILES = DV / 16;
     constexpr uint32_t FB = 64 * 16;  // bytes of one operand fragment (64 lanes x 16 B)
     constexpr uint32_t EB = sizeof(TIn);
-    constexpr int SINK = STAGE ? L::F_SINK : 0;
-    static_assert(!STAGE || (C == 64 && NL == 8), "staged form: chunk 64, 8 loader waves");
 
     extern __shared__ __align__(16) unsigned char lds_raw[];
     L& sm = *reinterpret_cast<L*>(lds_raw);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave: scalar branches
-    const bool loader = wave >= NW;
-    const int lw = wave - NW;                                    // loader index
     const int g16 = lane >> 4, l16 = lane & 15;
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
     const int pair = xcd + 8 * (slot / TILES);
@@ -1454,7 +1477,6 @@ __global__ __launch_bounds__((NW + chain_loaders<TIn, C>()) * 64) void chain_ker
     const float* state_in = c_begin == s_first ? init_state : carry;
     float* state_out_ptr = c_end == s_last ? final_state : carry;
 
-    // ---------------------------------------------------------------- operands
     const uint32_t lane_b = (uint32_t)lane * 16;
     // chunk c's record, state and Delta are slot c - slot0 of their regions
     auto rec_ptr = [&](int64_t c) { return records + ((size_t)(c - slot0) * H + h) * record_bytes; };
@@ -1464,164 +1486,16 @@ __global__ __launch_bounds__((NW + chain_loaders<TIn, C>()) * 64) void chain_ker
     auto state_out = [&](int64_t c) {
         return states + ((size_t)(c - slot0) * H + h) * CO::STATE_ELEMS + (size_t)row0 * DK;
     };
-    auto delta_out = [&](int64_t c, int part) {
-        return deltas + ((size_t)(c - slot0) * H + h) * CO::DELTA_ELEMS + ((size_t)part * DV + row0) * C;
+    auto delta_out = [&](int64_t c) {
+        return deltas + ((size_t)(c - slot0) * H + h) * CO::DELTA_ELEMS + (size_t)row0 * C;
     };
 
-    // ------------------------------------------------- loader waves (staged form)
-    // The compute waves read, in the three phases of chunk c: W(c) (phase 1),
-    // U(c) and the k scales (phase 2), K^T(c) and the decay (phase 3).  Each LDS
-    // region is refilled in the phase after its last read, from registers that
-    // the operand loaders (waves 0 .. NOP-1) loaded about one and a half phases
-    // earlier, so no barrier waits for a load that was just issued:
-    //   phase 1 of c:  write K^T(c), meta(c);  load U(c+1), k scales(c+1)
-    //   phase 2 of c:  write W(c+1);           load K^T(c+1), meta(c+1)
-    //   phase 3 of c:  write U(c+1), k scales; load W(c+2)
-    // Chunk indices past the sequence are clamped to its last chunk (harmless
-    // reloads).  Loaders 0..3 copy the state rows entering chunk c to `states`
-    // (phase 1 of c, before phase 3 rewrites them) and loaders 3..6 copy Delta
-    // of chunk c to `deltas` (phase 3 of c).  Every loader issues the same loads
-    // on every path (fragment indices past the end are clamped), so the
-    // compiler's vmcnt waits stay exact.  The last loader wave only prefetches:
-    // each phase 1 it brings its share of chunk c+2's W and K^T and this
-    // workgroup's U tiles into L2 by fire-and-forget LDS-DMA transfers into a
-    // sink slot; it waits for nothing in the loop, so the in-order vmcnt of the
-    // other waves never includes them.
-    if (loader) {
-        if constexpr (STAGE) {
-            constexpr int NOP = NL - 1;  // operand loaders
-            constexpr int L_KSC = RT % NOP, L_META = (RT + 1) % NOP;
-            static_assert(RT + 2 <= NOP && NOP >= 7, "one loader per U tile, distinct row-vector loaders");
-            struct GroupU { u32x4 u; uint32_t x, m; };
-            // Every loader issues the same loads and stores; a wave without the role
-            // reads a duplicate or stores through an empty view (dropped).
-            auto load_u = [&](int64_t c, GroupU& g) {
-                const unsigned char* rb = rec_ptr(c);
-                g.u = buf_load16(make_rsrc(rb, (uint32_t)R::BYTES), lane_b, u_src(lw % RT));
-                g.x = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(rb + R::KSC_BYTE_OFF, C * 4), lane * 4, 0, 0);
-                g.m = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(rb + R::DEC_BYTE_OFF, 16), lane * 4, 0, 0);
-            };
-            auto write_u = [&](const GroupU& g) {
-                if (lw < RT) *reinterpret_cast<u32x4*>(sm.frag[L::F_U + lw] + lane_b) = g.u;
-                if (lw == L_KSC) reinterpret_cast<uint32_t*>(sm.ksc)[lane] = g.x;
-                if (lw == L_META) reinterpret_cast<uint32_t*>(sm.meta)[lane] = g.m;  // lanes >= 4 write 0
-            };
-            // LDS rows -> global rows, 16 bytes per lane
-            constexpr int SROW = DK * (int)EB / 16;          // 16-byte units per state row
-            constexpr int SU = (16 * SROW + 255) / 256;      // units per lane of loaders 0..3
-            auto store_state = [&](int64_t c) {
-                const __amdgpu_buffer_rsrc_t r = make_rsrc(state_out(c), lw < 4 ? 16u * DK * EB : 0u);
-#pragma unroll
-                for (int i = 0; i < SU; ++i) {
-                    int u = ((lw & 3) * 64 + lane) + 256 * i;
-                    u = u < 16 * SROW ? u : 16 * SROW;  // past the rows: offset past the view, dropped
-                    const int row = min(u / SROW, 15), part = u % SROW;
-                    const u32x4 v = *reinterpret_cast<const u32x4*>(sm.sr + row * SP + part * 8);
-                    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)((uint32_t)u * 16), 0, kNtAux);
-                }
-            };
-            constexpr int DROW = C * (int)EB / 16;           // 16-byte units per Delta row (8)
-            static_assert(NS == 2 && 16 * DROW == 128, "one Delta unit per lane of loaders 3..6, two per part");
-            auto store_delta = [&](int64_t c) {
-                const bool live = lw >= 3 && lw < 7;
-                const int part = ((lw + 1) >> 1) & 1;  // loaders 3, 4 -> hi; 5, 6 -> lo (wave-uniform)
-                const int u = ((lw + 1) & 1) * 64 + lane, row = u / DROW, q = u % DROW;
-                const u32x4 v = *reinterpret_cast<const u32x4*>(sm.dt[part] + row * DP + q * 8);
-                const __amdgpu_buffer_rsrc_t r = make_rsrc(delta_out(c, part), live ? 16u * C * EB : 0u);
-                __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)((uint32_t)row * C * EB + q * 16), 0, kNtAux);
-            };
-            // prefetch wave: a 1/TILES share of chunk cp's W and K^T (identical for
-            // all row tiles) and this workgroup's U tiles
-            constexpr uint32_t SHARED_KB = (uint32_t)((size_t)R::CHAIN_ELEMS * EB / 1024);
-            constexpr int PF = (int)((SHARED_KB + TILES - 1) / TILES);
-            auto prefetch = [&](int64_t cp) {
-                const __amdgpu_buffer_rsrc_t r = make_rsrc(rec_ptr(cp), (uint32_t)R::BYTES);
-#pragma unroll
-                for (int i = 0; i < PF; ++i) {
-                    uint32_t blk = (uint32_t)(i * TILES + tile);
-                    blk = blk < SHARED_KB ? blk : SHARED_KB - 1;
-                    const uint32_t src = blk * 1024;
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)sm.frag[SINK], 16, lane_b, src, 0, 0);
-                }
-#pragma unroll
-                for (int i = 0; i < RT; ++i) {
-                    const uint32_t src = u_src(i);  // (a lambda call inside the builtin's argument list
-                                                    // drops the host-side kernel stub)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)sm.frag[SINK], 16, lane_b, src, 0, 0);
-                }
-            };
-
-            if (lw == NOP) {
-                __syncthreads();
-                for (int64_t c = c_begin; c < c_end; ++c) {
-                    if (c + 2 < c_end) prefetch(c + 2);
-                    lds_barrier();  // ---- B
-                    lds_barrier();  // ---- C
-                }
-                wait_vmcnt<0>();  // no transfer may still target LDS when the workgroup ends
-                return;
-            }
-            const int64_t last = c_end - 1;
-            if (c_begin < c_end) {
-                GroupU gu;
-                load_u(c_begin, gu);
-                write_u(gu);
-            }
-            __syncthreads();  // the compute waves have written the initial state rows
-            for (int64_t c = c_begin; c < c_end; ++c) {
-                GroupU gu;
-                // ---- phase 1 of c
-                store_state(c);
-                load_u(min(c + 1, last), gu);
-                lds_barrier();  // ---- B
-                // ---- phase 2 of c (U, the scales and the decay of c were read in phase 1)
-                write_u(gu);
-                store_delta(c);
-                lds_barrier();  // ---- C
-            }
-            wait_vmcnt<0>();
-        }
-        return;
-    }
-
-    // ---------------------------------------------------------------- compute waves
-    // general form: fragment of the current chunk at record byte offset `src`
+    // fragment of the current chunk at record byte offset `src`
     __amdgpu_buffer_rsrc_t rcur = make_rsrc(records, 0u);
-    auto frag = [&](int, uint32_t src) -> Frag { return __builtin_bit_cast(Frag, buf_load16(rcur, lane_b, src)); };
+    auto frag = [&](uint32_t src) -> Frag { return __builtin_bit_cast(Frag, buf_load16(rcur, lane_b, src)); };
     const int rt = wave & 3, kq = wave >> 2;
-    const bool p1 = rt < RT && kq < P::KQ;   // phase-1 partial products
-    const bool fin_d = rt < RT && kq == 0;   // Delta finaliser of row tile rt
-    // Staged form: every compute wave reads its own W and K^T fragments (each is
-    // used by exactly one wave) straight into registers, one chunk ahead of use;
-    // the loads are the same on every compute wave (tile indices past the end are
-    // clamped), so the compiler's vmcnt waits stay exact.  The prefetch wave has
-    // brought them into L2 two chunks earlier.
-    Frag wreg[STAGE ? R::DKS : 1], kreg[STAGE ? P::MTW : 1][STAGE ? R::CKS : 1];
-    auto load_wk_w = [&](int64_t cc) {  // the W row tile of waves 0 .. RT-1
-        if constexpr (STAGE) {
-            if (wave < RT) {
-                const __amdgpu_buffer_rsrc_t r = make_rsrc(rec_ptr(cc), (uint32_t)R::BYTES);
-#pragma unroll
-                for (int ks = 0; ks < R::DKS; ++ks) {
-                    const uint32_t src = w_src(wave, ks);
-                    wreg[ks] = __builtin_bit_cast(Frag, buf_load16(r, lane_b, src));
-                }
-            }
-        }
-    };
-    auto load_wk_k = [&](int64_t cc) {
-        if constexpr (STAGE) {
-            const __amdgpu_buffer_rsrc_t r = make_rsrc(rec_ptr(cc), (uint32_t)R::BYTES);
-#pragma unroll
-            for (int a = 0; a < P::MTW; ++a)
-#pragma unroll
-                for (int ks = 0; ks < R::CKS; ++ks) {
-                    const uint32_t src = k_src(min(wave + NW * a, R::MT - 1), ks);
-                    kreg[a][ks] = __builtin_bit_cast(Frag, buf_load16(r, lane_b, src));
-                }
-        }
-    };
-    const int64_t last_c = c_end - 1;
+    const bool p1 = rt < R::RT && kq < P::KQ;  // phase-1 partial products
+    const bool fin_d = rt < R::RT && kq == 0;  // Delta finaliser of row tile rt
 
     // state tiles S^T[mt] in result layout: lane holds S[row0 + l16][mt*16 + 4*g16 + i]
     f32x4 S[P::MTW];
@@ -1634,118 +1508,60 @@ __global__ __launch_bounds__((NW + chain_loaders<TIn, C>()) * 64) void chain_ker
             if (state_in)
                 S[a] = *reinterpret_cast<const f32x4*>(state_in + st_base + (size_t)(row0 + l16) * DK + mt * 16 +
                                                        4 * g16);
-            store_quad<TIn, false>(sm.sr + l16 * SP + quad_pos<TIn>(mt, g16), nullptr, S[a]);
+            *reinterpret_cast<f32x4*>(sm.sr + l16 * SP + mt * 16 + 4 * g16) = S[a];
         }
-    }
-    if (c_begin < c_end) {
-        load_wk_w(c_begin);
-        load_wk_k(c_begin);
     }
     __syncthreads();
 
-    if constexpr (STAGE) {
-        // Two phases per chunk: waves 0 .. RT-1 form X = W S^T of their row tile
-        // over all of d_k (two accumulators) and Delta = U - X at once; then
-        // every wave updates its state tiles.
-        for (int64_t c = c_begin; c < c_end; ++c) {
-            if (wave < RT) {
-                // ---- phase 1: Delta of row tile `wave` (sigma-ordered dt, natural-order ds)
-                f32x4 X0 = {0.f, 0.f, 0.f, 0.f}, X1 = {0.f, 0.f, 0.f, 0.f};
+    for (int64_t c = c_begin; c < c_end; ++c) {
+        rcur = make_rsrc(rec_ptr(c), (uint32_t)R::BYTES);
+        // the state entering chunk c
 #pragma unroll
-                for (int ks = 0; ks < R::DKS; ks += 2) {
-                    X0 = M::mma(wreg[ks], *reinterpret_cast<const Frag*>(sm.sr + l16 * SP + ks * KS + g16 * E), X0);
-                    if (ks + 1 < R::DKS)
-                        X1 = M::mma(wreg[ks + 1],
-                                    *reinterpret_cast<const Frag*>(sm.sr + l16 * SP + (ks + 1) * KS + g16 * E), X1);
-                }
-                const f32x4 ks4 = *reinterpret_cast<const f32x4*>(sm.ksc + wave * 16 + 4 * g16);
-                const f32x4 d = __builtin_bit_cast(f32x4, *reinterpret_cast<const u32x4*>(sm.frag[L::F_U + wave] + lane_b)) -
-                                (X0 + X1);
-                const int pd = l16 * DP + quad_pos<TIn>(wave, g16);
-                const int pn = l16 * DP + wave * 16 + 4 * g16;
-                store_quad<TIn, SPL>(sm.dt[0] + pd, sm.dt[NS - 1] + pd, d);
-                store_quad<TIn, SPL>(sm.ds[0] + pn, sm.ds[NS - 1] + pn, d * ks4);
-            }
-            load_wk_w(min(c + 1, last_c));
-            const float decay = sm.meta[0].x;  // read before the loaders refill its slot
-            lds_barrier();  // ---- B: Delta visible; U, scales and decay free
-
-            // ---- phase 2: state update on this wave's d_k tiles
-#pragma unroll
-            for (int a = 0; a < P::MTW; ++a) {
-                const int mt = wave + NW * a;
-                if (mt >= R::MT) continue;
-                f32x4 acc0 = S[a] * decay, acc1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < R::CKS; ++ks) {
-                    const int doff = l16 * DP + ks * KS + g16 * E;
-                    acc0 = M::mma(kreg[a][ks], *reinterpret_cast<const Frag*>(sm.ds[0] + doff), acc0);
-                    acc1 = M::mma(kreg[a][ks], *reinterpret_cast<const Frag*>(sm.ds[1] + doff), acc1);
-                }
-                S[a] = acc0 + acc1;
-                store_quad<TIn, false>(sm.sr + l16 * SP + quad_pos<TIn>(mt, g16), nullptr, S[a]);
-            }
-            load_wk_k(min(c + 1, last_c));
-            lds_barrier();  // ---- C: state copy visible
+        for (int a = 0; a < P::MTW; ++a) {
+            const int mt = wave + NW * a;
+            if (mt < R::MT) *reinterpret_cast<f32x4*>(state_out(c) + (size_t)l16 * DK + mt * 16 + 4 * g16) = S[a];
         }
-    }
-    if constexpr (!STAGE) {
-        // General form (fp32 operands): three phases per chunk, operands read
-        // from the record directly.
-        for (int64_t c = c_begin; c < c_end; ++c) {
-            rcur = make_rsrc(rec_ptr(c), (uint32_t)R::BYTES);
-            // the state entering chunk c (fp32, natural order)
+        if (p1) {
+            // ---- phase 1: partial X = W S^T over this wave's d_k part
+            f32x4 X = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int a = 0; a < P::MTW; ++a) {
-                const int mt = wave + NW * a;
-                if (mt < R::MT)
-                    *reinterpret_cast<f32x4*>(state_out(c) + (size_t)l16 * DK + mt * 16 + 4 * g16) = S[a];
+            for (int i = 0; i < P::KPW; ++i) {
+                const int ks = kq * P::KPW + i;
+                X = M::mma(frag(w_src(rt, ks)), *reinterpret_cast<const Frag*>(sm.sr + l16 * SP + ks * KS + g16 * E), X);
             }
-            if (p1) {
-                // ---- phase 1: partial X = W S^T over this wave's d_k part
-                f32x4 X = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int i = 0; i < P::KPW; ++i) {
-                    const int ks = kq * P::KPW + i;
-                    X = M::mma(frag(0, w_src(rt, ks)), *reinterpret_cast<const Frag*>(sm.sr + l16 * SP + ks * KS + g16 * E),
-                               X);
-                }
-                sm.xp[kq][rt][lane] = X;
-            }
-            lds_barrier();  // ---- A: partials visible
-
-            if (fin_d) {
-                // ---- phase 2: Delta = U - X for row tile rt (natural order, k-scaled in ds)
-                const f32x4 ks4 = __builtin_bit_cast(
-                    f32x4, buf_load16(rcur, (uint32_t)(rt * 16 + 4 * g16) * 4, (uint32_t)R::KSC_BYTE_OFF));
-                f32x4 X = sm.xp[0][rt][lane];
-#pragma unroll
-                for (int qq = 1; qq < P::KQ; ++qq) X += sm.xp[qq][rt][lane];
-                const f32x4 d = __builtin_bit_cast(f32x4, frag(0, u_src(rt))) - X;
-                const int pn = l16 * DP + rt * 16 + 4 * g16;
-                store_quad<TIn, SPL>(sm.ds[0] + pn, sm.ds[NS - 1] + pn, d * ks4);
-                // Delta^T rows (fp32, natural order over the chunk)
-                *reinterpret_cast<f32x4*>(delta_out(c, 0) + (size_t)l16 * C + rt * 16 + 4 * g16) = d;
-            }
-            const float decay = __builtin_bit_cast(f32x4, buf_load16(rcur, 0, (uint32_t)R::DEC_BYTE_OFF)).x;
-            lds_barrier();  // ---- B: Delta visible
-
-            // ---- phase 3: state update on this wave's d_k tiles
-#pragma unroll
-            for (int a = 0; a < P::MTW; ++a) {
-                const int mt = wave + NW * a;
-                if (mt >= R::MT) continue;
-                f32x4 acc = S[a] * decay;
-#pragma unroll
-                for (int ks = 0; ks < R::CKS; ++ks) {
-                    const int doff = l16 * DP + ks * KS + g16 * E;
-                    acc = M::mma(frag(0, k_src(mt, ks)), *reinterpret_cast<const Frag*>(sm.ds[0] + doff), acc);
-                }
-                S[a] = acc;
-                store_quad<TIn, false>(sm.sr + l16 * SP + quad_pos<TIn>(mt, g16), nullptr, acc);
-            }
-            lds_barrier();  // ---- C: state copy visible
+            sm.xp[kq][rt][lane] = X;
         }
+        lds_barrier();  // ---- A: partials visible
+
+        if (fin_d) {
+            // ---- phase 2: Delta = U - X for row tile rt (natural order, k-scaled in ds)
+            const f32x4 ks4 = __builtin_bit_cast(
+                f32x4, buf_load16(rcur, (uint32_t)(rt * 16 + 4 * g16) * 4, (uint32_t)R::KSC_BYTE_OFF));
+            f32x4 X = sm.xp[0][rt][lane];
+#pragma unroll
+            for (int qq = 1; qq < P::KQ; ++qq) X += sm.xp[qq][rt][lane];
+            const f32x4 d = __builtin_bit_cast(f32x4, frag(u_src(rt))) - X;
+            *reinterpret_cast<f32x4*>(sm.ds + l16 * DP + rt * 16 + 4 * g16) = d * ks4;
+            *reinterpret_cast<f32x4*>(delta_out(c) + (size_t)l16 * C + rt * 16 + 4 * g16) = d;  // Delta^T rows
+        }
+        const float decay = __builtin_bit_cast(f32x4, buf_load16(rcur, 0, (uint32_t)R::DEC_BYTE_OFF)).x;
+        lds_barrier();  // ---- B: Delta visible
+
+        // ---- phase 3: state update on this wave's d_k tiles
+#pragma unroll
+        for (int a = 0; a < P::MTW; ++a) {
+            const int mt = wave + NW * a;
+            if (mt >= R::MT) continue;
+            f32x4 acc = S[a] * decay;
+#pragma unroll
+            for (int ks = 0; ks < R::CKS; ++ks) {
+                const int doff = l16 * DP + ks * KS + g16 * E;
+                acc = M::mma(frag(k_src(mt, ks)), *reinterpret_cast<const Frag*>(sm.ds + doff), acc);
+            }
+            S[a] = acc;
+            *reinterpret_cast<f32x4*>(sm.sr + l16 * SP + mt * 16 + 4 * g16) = acc;
+        }
+        lds_barrier();  // ---- C: state copy visible
     }
 
     if (state_out_ptr) {
@@ -1753,6 +1569,351 @@ __global__ __launch_bounds__((NW + chain_loaders<TIn, C>()) * 64) void chain_ker
         for (int a = 0; a < P::MTW; ++a) {
             const int mt = wave + NW * a;
             if (mt < R::MT)
+                *reinterpret_cast<f32x4*>(state_out_ptr + st_base + (size_t)(row0 + l16) * DK + mt * 16 + 4 * g16) =
+                    S[a];
+        }
+    }
+}
+
+// ---------------------------------------------------------------- bf16 state chain
+// LDS transposing read of gfx950 (ds_read_b64_tr_b16): within each group of 16
+// lanes, lane j supplies the address of four consecutive 16-bit values, and
+// lane i receives value i % 4 of lanes i / 4, 4 + i / 4, 8 + i / 4 and
+// 12 + i / 4.  When lane j points at row r0 + j / 4, columns c0 + 4 (j % 4)
+// .. + 3 of a row-major tile, lane i therefore receives column c0 + i of the
+// rows r0 .. r0 + 3: four consecutive elements down one column.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p)
+{
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4i16* lds_v4i16_t;
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t)p));
+}
+
+// LDS of the bf16 chain kernel.  The per-chunk operands are triple-buffered:
+// chunk c's sit in buffer c % 3, written by LDS-DMA two chunks ahead.
+template <int DK, int DV>
+struct ChainKrLds {
+    using R = Rec<uint16_t, 64, DK, DV>;
+    static constexpr int C = 64, RT = 4, NB = 3;
+    static constexpr int SP = DK + 8;              // state copy pitch (dwords = 4 mod 32)
+    static constexpr int DP = C + 8;               // Delta^T pitch
+    static constexpr int KB = C * DK * 2;          // bytes of the K tile
+    static constexpr int NKP = KB / 1024;          // 1 KB transfers of the K tile
+    static constexpr int NTP = RT * R::CKS;        // T' fragments
+    static constexpr int NDMA = NKP + NTP + RT + 1;  // transfers per chunk: K, T', U tiles, row vectors
+    unsigned char kt[NB][KB];                      // K tile, KTile<DK> layout
+    unsigned char tp[NB][NTP][1024];               // T' fragments [row tile][k-step], lane order
+    unsigned char uf[NB][RT][1024];                // U tiles of this workgroup's 16 value columns
+    unsigned char vec[NB][1024];                   // k scales (bytes 0..255), decay and token range (256..271)
+    uint16_t sr[16 * SP];                          // state rows S[r][col] rounded to bf16, sigma order
+    u32x2 yb[2][2][2][64];                         // Y = K S^T, B operand of T' Y: [k-step][hi, lo][half][lane]
+    uint16_t dt[2][16 * DP];                       // Delta^T[r][j], sigma order (hi, lo)
+    uint16_t ds[2][16 * DP];                       // (kscale o Delta)^T[r][j], natural order (hi, lo)
+};
+
+// State chain, bf16 operands: one workgroup of 16 waves per (sequence, head,
+// 16 state rows), sequential over the sequence's chunks.  With the chunk's raw
+// K rows in LDS, the corrected values come as Delta = U - T' (K S^T) and the
+// state update as S^T = e^{gamma_L} S^T + K^T (kscale o Delta): K is read as
+// row fragments for K S^T and, through the transposing read, as column
+// fragments for K^T, so each chunk's K crosses from L2 once.  Per chunk c the
+// 8 compute waves run
+//   phase 1  waves 0..3, row tile w: Y = K S^T (fp32), split hi/lo into LDS
+//   phase 2  waves 0..3, row tile w: X = T' (Y_hi + Y_lo), Delta = U - X
+//            (sigma-ordered Delta^T and the k-scaled natural-order copy, hi/lo)
+//   phase 3  waves 0..7, their state d_k tiles: the state update
+// separated by the barriers A, B and C, every operand read from LDS (no global
+// memory instruction inside the loop), each phase's reads issued together.
+// Loader waves 0..5 (waves 8..13) move chunk c+2's K tile, T', U tiles and row
+// vectors into buffer (c+2) % 3 during chunk c (transfer i by loader i mod 6,
+// in three bursts, one per phase; the buffer was released by barrier C of
+// chunk c-1) and wait before barrier C for chunk c+1's transfers, issued a
+// chunk earlier.  Loaders 6 and 7 copy the state rows entering chunk c to
+// `states` (before barrier A) and Delta of chunk c to `deltas` (after B); they
+// issue no transfer into LDS, so no read of theirs waits for one.  The
+// workgroup -> (pair, row tile) mapping and the segment logic are those of
+// chain_kernel.
+template <int DK, int DV, bool SEG>
+__global__ __launch_bounds__(1024) void chain_kr_kernel(
+    const int32_t* __restrict__ header, const int32_t* __restrict__ seq_first,
+    const int32_t* __restrict__ seq_order, int32_t varlen, int64_t T, int32_t H, int32_t pairs,
+    const unsigned char* records, size_t record_bytes, const float* init_state, float* final_state,
+    uint16_t* __restrict__ states, uint16_t* __restrict__ deltas, int64_t seg_begin, int64_t seg_end, float* carry,
+    int64_t slot0)
+{
+    using M = Mma<uint16_t>;
+    using R = Rec<uint16_t, 64, DK, DV>;
+    using CO = ChainOut<uint16_t, 64, DK, DV>;
+    using L = ChainKrLds<DK, DV>;
+    using KT = KTile<DK>;
+    typedef M::Frag Frag;
+    constexpr int C = 64, RT = 4, KS = 32, E = 8, NW = 8;
+    constexpr int SP = L::SP, DP = L::DP, NKP = L::NKP, NTP = L::NTP, NDMA = L::NDMA;
+    constexpr int DKS = R::DKS, CKS = R::CKS, MT = R::MT;
+    constexpr int MTW = (MT + NW - 1) / NW;      // state d_k tiles per compute wave
+    constexpr int TILES = DV / 16;
+    constexpr uint32_t FB = 64 * 16;             // bytes of one fragment
+    constexpr int ND = 6;                        // transfer loaders
+    constexpr int NJ = (NDMA + ND - 1) / ND;     // transfers of the busiest loader
+    constexpr int J1 = (NJ + 2) / 3, J2 = (2 * NJ + 2) / 3;  // burst bounds (phase 1 | 2 | 3)
+    static_assert(KS == M::KS && E == M::E && CKS == 2 && RT == R::RT, "chunk 64");
+    static_assert(sizeof(L) <= 160 * 1024, "chain LDS");
+
+    extern __shared__ __align__(16) unsigned char lds_raw[];
+    L& sm = *reinterpret_cast<L*>(lds_raw);
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave: scalar branches
+    const int g16 = lane >> 4, l16 = lane & 15;
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int pair = xcd + 8 * (slot / TILES);
+    if (pair >= pairs) return;
+    const int n = varlen ? seq_order[pair / H] : pair / H, h = pair % H;  // longest sequences first
+    const int tile = slot % TILES;
+    const int row0 = tile * 16;  // first state row (value index) of this workgroup
+
+    int64_t s_first, s_last;  // the sequence's chunk range
+    if (varlen) {
+        if (header[0] != 0) return;
+        s_first = seq_first[n];
+        s_last = seq_first[n + 1];
+    } else {
+        s_first = 0;
+        s_last = (T + C - 1) / C;
+    }
+    const int64_t c_begin = SEG && s_first < seg_begin ? seg_begin : s_first;
+    const int64_t c_end = SEG && s_last > seg_end ? seg_end : s_last;
+    if (c_begin >= c_end && !(s_first == s_last && s_first >= seg_begin && s_first < seg_end)) return;
+    const float* state_in = c_begin == s_first ? init_state : carry;
+    float* state_out_ptr = c_end == s_last ? final_state : carry;
+    const int64_t last = c_end - 1;
+
+    const uint32_t lane_b = (uint32_t)lane * 16;
+    auto rec_ptr = [&](int64_t c) { return records + ((size_t)(c - slot0) * H + h) * record_bytes; };
+    auto state_out = [&](int64_t c) {
+        return states + ((size_t)(c - slot0) * H + h) * CO::STATE_ELEMS + (size_t)row0 * DK;
+    };
+    auto delta_out = [&](int64_t c, int part) {
+        return deltas + ((size_t)(c - slot0) * H + h) * CO::DELTA_ELEMS + ((size_t)part * DV + row0) * C;
+    };
+
+    // ------------------------------------------------------------ loader waves
+    if (wave >= NW) {
+        const int lw = wave - NW;
+        if (lw < ND) {
+            // transfers j0 .. j1-1 of this loader for chunk cc (transfer i = lw + ND j)
+            auto transfers = [&](int64_t cc, int j0, int j1) {
+                const unsigned char* rb = rec_ptr(cc);
+                const __amdgpu_buffer_rsrc_t r = make_rsrc(rb, (uint32_t)R::BYTES);
+                const __amdgpu_buffer_rsrc_t rv = make_rsrc(rb + R::KSC_BYTE_OFF, C * 4 + 16);  // lanes past: zeros
+                const int b = (int)(cc % 3);
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    const int i = lw + ND * j;
+                    if (j < j0 || j >= j1 || i >= NDMA) continue;
+                    if (i < NKP) {
+                        const uint32_t src = (uint32_t)(R::KR_OFF * 2) + (uint32_t)i * FB;
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(sm.kt[b] + i * FB), 16, lane_b, src, 0, 0);
+                    } else if (i < NKP + NTP) {
+                        const uint32_t src = (uint32_t)(R::TP_OFF * 2) + (uint32_t)(i - NKP) * FB;
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)sm.tp[b][i - NKP], 16, lane_b, src, 0, 0);
+                    } else if (i < NKP + NTP + RT) {
+                        const int u = i - NKP - NTP;
+                        const uint32_t src = (uint32_t)R::U_BYTE_OFF + (uint32_t)(u * R::VT + tile) * FB;
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)sm.uf[b][u], 16, lane_b, src, 0, 0);
+                    } else {
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)sm.vec[b], 16, lane_b, 0, 0, 0);
+                    }
+                }
+            };
+            const bool busiest = lw + ND * (NJ - 1) < NDMA;  // issues NJ transfers per chunk, else NJ - 1
+            if (c_begin < c_end) transfers(c_begin, 0, NJ);
+            if (c_begin + 1 < c_end) transfers(c_begin + 1, 0, NJ);
+            wait_vmcnt<0>();
+            __syncthreads();  // the first chunk's operands and the initial state rows are in LDS
+            for (int64_t c = c_begin; c < c_end; ++c) {
+                const bool more = c + 2 <= last;
+                if (more) transfers(c + 2, 0, J1);
+                lds_barrier();  // ---- A
+                if (more) transfers(c + 2, J1, J2);
+                lds_barrier();  // ---- B
+                if (more) {
+                    transfers(c + 2, J2, NJ);
+                    // chunk c+1's transfers (a chunk older than this chunk's) have landed
+                    if (busiest)
+                        wait_vmcnt<NJ>();
+                    else
+                        wait_vmcnt<NJ - 1>();
+                } else {
+                    wait_vmcnt<0>();
+                }
+                lds_barrier();  // ---- C
+            }
+            wait_vmcnt<0>();
+            return;
+        }
+        // store loaders 6 and 7: LDS rows -> global rows, 16 bytes per lane
+        const int sl = lw - ND;                      // 0 or 1
+        constexpr int SROW = DK * 2 / 16;            // 16-byte units per state row
+        constexpr int SU = (16 * SROW + 127) / 128;  // units per lane
+        auto store_state = [&](int64_t c) {
+            const __amdgpu_buffer_rsrc_t r = make_rsrc(state_out(c), 16u * DK * 2);
+#pragma unroll
+            for (int i = 0; i < SU; ++i) {
+                int u = (sl * 64 + lane) + 128 * i;
+                u = u < 16 * SROW ? u : 16 * SROW;  // past the rows: offset past the view, dropped
+                const int row = min(u / SROW, 15), part = u % SROW;
+                const u32x4 v = *reinterpret_cast<const u32x4*>(sm.sr + row * SP + part * 8);
+                __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)((uint32_t)u * 16), 0, kNtAux);
+            }
+        };
+        constexpr int DROW = C * 2 / 16;  // 16-byte units per Delta row (8)
+        static_assert(16 * DROW == 128, "one Delta row-part unit per lane and part");
+        auto store_delta = [&](int64_t c) {
+#pragma unroll
+            for (int part = 0; part < 2; ++part) {
+                const int u = sl * 64 + lane, row = u / DROW, q = u % DROW;
+                const u32x4 v = *reinterpret_cast<const u32x4*>(sm.dt[part] + row * DP + q * 8);
+                const __amdgpu_buffer_rsrc_t r = make_rsrc(delta_out(c, part), 16u * C * 2);
+                __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)((uint32_t)row * C * 2 + q * 16), 0, kNtAux);
+            }
+        };
+        __syncthreads();
+        for (int64_t c = c_begin; c < c_end; ++c) {
+            store_state(c);  // before phase 3 rewrites the rows
+            lds_barrier();  // ---- A
+            lds_barrier();  // ---- B
+            store_delta(c);  // before phase 2 of c+1 rewrites it
+            lds_barrier();  // ---- C
+        }
+        wait_vmcnt<0>();
+        return;
+    }
+
+    // ------------------------------------------------------------ compute waves
+    // K^T fragment of d_k tile mt, k-step ks (identity order over the chunk):
+    // lane (l16, g16) element e = K[32 ks + 8 g16 + e][16 mt + l16], two transposing reads
+    auto kt_frag = [&](const uint16_t* kc, int mt, int ks) -> Frag {
+        const int r = ks * KS + 8 * g16 + (l16 >> 2);
+        const u32x2 a = lds_read_tr16(kc + KT::at(r, mt >> 1, l16 & 3, mt & 1));
+        const u32x2 b = lds_read_tr16(kc + KT::at(r + 4, mt >> 1, l16 & 3, mt & 1));
+        return __builtin_bit_cast(Frag, u32x4{a.x, a.y, b.x, b.y});
+    };
+    auto frag_at = [&](const unsigned char* p) -> Frag { return *reinterpret_cast<const Frag*>(p + lane_b); };
+
+    // state tiles S^T[mt] in result layout: lane holds S[row0 + l16][mt*16 + 4*g16 + i]
+    f32x4 S[MTW];
+    const size_t st_base = ((size_t)n * H + h) * DV * DK;
+#pragma unroll
+    for (int a = 0; a < MTW; ++a) {
+        const int mt = wave + NW * a;
+        S[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (mt < MT) {
+            if (state_in)
+                S[a] = *reinterpret_cast<const f32x4*>(state_in + st_base + (size_t)(row0 + l16) * DK + mt * 16 +
+                                                       4 * g16);
+            store_quad<uint16_t, false>(sm.sr + l16 * SP + quad_pos<uint16_t>(mt, g16), nullptr, S[a]);
+        }
+    }
+    __syncthreads();
+
+    for (int64_t c = c_begin; c < c_end; ++c) {
+        const int b = (int)(c % 3);
+        const uint16_t* kc = reinterpret_cast<const uint16_t*>(sm.kt[b]);
+        if (wave < RT) {
+            // ---- phase 1: Y = K S^T for chunk rows 16 wave .. +15, split hi/lo
+            Frag kf[DKS], sf[DKS];
+#pragma unroll
+            for (int ks = 0; ks < DKS; ++ks) {
+                const u32x2 lo = *reinterpret_cast<const u32x2*>(kc + KT::at(wave * 16 + l16, ks, g16, 0));
+                const u32x2 hi = *reinterpret_cast<const u32x2*>(kc + KT::at(wave * 16 + l16, ks, g16, 1));
+                kf[ks] = __builtin_bit_cast(Frag, u32x4{lo.x, lo.y, hi.x, hi.y});
+                sf[ks] = *reinterpret_cast<const Frag*>(sm.sr + l16 * SP + ks * KS + g16 * E);
+            }
+            f32x4 y0 = {0.f, 0.f, 0.f, 0.f}, y1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < DKS; ks += 2) {
+                y0 = M::mma(kf[ks], sf[ks], y0);
+                if (ks + 1 < DKS) y1 = M::mma(kf[ks + 1], sf[ks + 1], y1);
+            }
+            const f32x4 y = y0 + y1;
+            // lane holds Y[16 wave + 4 g16 + i][row l16]: elements 4 (wave % 2) + i of the
+            // sigma-ordered B operand of k-step wave / 2
+            uint32_t h0, l0, h1, l1;
+            split_bf16x2(y.x, y.y, h0, l0);
+            split_bf16x2(y.z, y.w, h1, l1);
+            sm.yb[wave >> 1][0][wave & 1][lane] = u32x2{h0, h1};
+            sm.yb[wave >> 1][1][wave & 1][lane] = u32x2{l0, l1};
+        }
+        lds_barrier();  // ---- A: Y visible
+
+        if (wave < RT) {
+            // ---- phase 2: Delta = U - T' Y of row tile `wave` (T' is zero above the diagonal)
+            const int nks = wave / 2 + 1;
+            Frag tf[CKS], yh[CKS], yl[CKS];
+#pragma unroll
+            for (int ks = 0; ks < CKS; ++ks) {
+                if (ks >= nks) break;
+                tf[ks] = frag_at(sm.tp[b][wave * CKS + ks]);
+                const u32x2 h0 = sm.yb[ks][0][0][lane], h1 = sm.yb[ks][0][1][lane];
+                const u32x2 l0 = sm.yb[ks][1][0][lane], l1 = sm.yb[ks][1][1][lane];
+                yh[ks] = __builtin_bit_cast(Frag, u32x4{h0.x, h0.y, h1.x, h1.y});
+                yl[ks] = __builtin_bit_cast(Frag, u32x4{l0.x, l0.y, l1.x, l1.y});
+            }
+            const f32x4 ks4 = *reinterpret_cast<const f32x4*>(sm.vec[b] + wave * 64 + 16 * g16);
+            const f32x4 u4 = *reinterpret_cast<const f32x4*>(sm.uf[b][wave] + lane_b);
+            f32x4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < CKS; ++ks) {
+                if (ks >= nks) break;
+                x = M::mma(tf[ks], yh[ks], x);
+                x = M::mma(tf[ks], yl[ks], x);
+            }
+            const f32x4 d = u4 - x;
+            const int pd = l16 * DP + quad_pos<uint16_t>(wave, g16);
+            const int pn = l16 * DP + wave * 16 + 4 * g16;
+            store_quad<uint16_t, true>(sm.dt[0] + pd, sm.dt[1] + pd, d);
+            store_quad<uint16_t, true>(sm.ds[0] + pn, sm.ds[1] + pn, d * ks4);
+        }
+        lds_barrier();  // ---- B: Delta visible
+
+        // ---- phase 3: state update on this wave's d_k tiles
+        {
+            const float decay = *reinterpret_cast<const float*>(sm.vec[b] + C * 4);
+            Frag kf[MTW][CKS], dh[CKS], dl[CKS];
+#pragma unroll
+            for (int ks = 0; ks < CKS; ++ks) {
+                const int doff = l16 * DP + ks * KS + g16 * E;
+                dh[ks] = *reinterpret_cast<const Frag*>(sm.ds[0] + doff);
+                dl[ks] = *reinterpret_cast<const Frag*>(sm.ds[1] + doff);
+#pragma unroll
+                for (int a = 0; a < MTW; ++a) {
+                    const int mt = wave + NW * a;
+                    if (mt < MT) kf[a][ks] = kt_frag(kc, mt, ks);
+                }
+            }
+#pragma unroll
+            for (int a = 0; a < MTW; ++a) {
+                const int mt = wave + NW * a;
+                if (mt >= MT) continue;
+                f32x4 acc0 = S[a] * decay, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < CKS; ++ks) {
+                    acc0 = M::mma(kf[a][ks], dh[ks], acc0);
+                    acc1 = M::mma(kf[a][ks], dl[ks], acc1);
+                }
+                S[a] = acc0 + acc1;
+                store_quad<uint16_t, false>(sm.sr + l16 * SP + quad_pos<uint16_t>(mt, g16), nullptr, S[a]);
+            }
+        }
+        lds_barrier();  // ---- C: state copy visible; buffer c % 3 free
+    }
+
+    if (state_out_ptr) {
+#pragma unroll
+        for (int a = 0; a < MTW; ++a) {
+            const int mt = wave + NW * a;
+            if (mt < MT)
                 *reinterpret_cast<f32x4*>(state_out_ptr + st_base + (size_t)(row0 + l16) * DK + mt * 16 + 4 * g16) =
                     S[a];
         }
@@ -2142,24 +2303,41 @@ static hipError_t run_prefill(const PrefillArgs& a)
         return hipGetLastError();
     };
     auto launch_chain = [&](int64_t c0, int64_t c1, hipStream_t st, int64_t slot0 = 0) -> hipError_t {
-        constexpr int NW = 8;
-        using Lds = ChainLds<TIn, C, DK, DV, NW, chain_staged<TIn, C>()>;
-        static_assert(sizeof(Lds) <= 160 * 1024, "chain kernel LDS");
         const bool seg = !(c0 == 0 && c1 == ALL);
-        const void* fn = seg ? (const void*)chain_kernel<TIn, C, DK, DV, NW, true>
-                             : (const void*)chain_kernel<TIn, C, DK, DV, NW, false>;
-        const hipError_t e = lds_limit(fn, sizeof(Lds));
-        if (e != hipSuccess) return e;
-        const dim3 grid((uint32_t)chain_blocks), block((NW + chain_loaders<TIn, C>()) * 64);
-        if (seg)
-            hipLaunchKernelGGL((chain_kernel<TIn, C, DK, DV, NW, true>), grid, block, sizeof(Lds), st, header, first,
-                               order, varlen, a.T, a.H, (int32_t)pairs, records, a.lay.record_bytes, a.init_state,
-                               a.final_state, states, deltas, c0, c1, carry, slot0);
-        else
-            hipLaunchKernelGGL((chain_kernel<TIn, C, DK, DV, NW, false>), grid, block, sizeof(Lds), st, header, first,
-                               order, varlen, a.T, a.H, (int32_t)pairs, records, a.lay.record_bytes, a.init_state,
-                               a.final_state, states, deltas, c0, c1, carry, slot0);
-        return hipGetLastError();
+        if constexpr (sizeof(TIn) == 2) {
+            using Lds = ChainKrLds<DK, DV>;
+            const void* fn = seg ? (const void*)chain_kr_kernel<DK, DV, true> : (const void*)chain_kr_kernel<DK, DV, false>;
+            const hipError_t e = lds_limit(fn, sizeof(Lds));
+            if (e != hipSuccess) return e;
+            const dim3 grid((uint32_t)chain_blocks), block(1024);
+            if (seg)
+                hipLaunchKernelGGL((chain_kr_kernel<DK, DV, true>), grid, block, sizeof(Lds), st, header, first, order,
+                                   varlen, a.T, a.H, (int32_t)pairs, records, a.lay.record_bytes, a.init_state,
+                                   a.final_state, states, deltas, c0, c1, carry, slot0);
+            else
+                hipLaunchKernelGGL((chain_kr_kernel<DK, DV, false>), grid, block, sizeof(Lds), st, header, first, order,
+                                   varlen, a.T, a.H, (int32_t)pairs, records, a.lay.record_bytes, a.init_state,
+                                   a.final_state, states, deltas, c0, c1, carry, slot0);
+            return hipGetLastError();
+        } else {
+            constexpr int NW = 8;
+            using Lds = ChainLds<C, DK, DV, NW>;
+            static_assert(sizeof(Lds) <= 160 * 1024, "chain kernel LDS");
+            const void* fn = seg ? (const void*)chain_kernel<C, DK, DV, NW, true>
+                                 : (const void*)chain_kernel<C, DK, DV, NW, false>;
+            const hipError_t e = lds_limit(fn, sizeof(Lds));
+            if (e != hipSuccess) return e;
+            const dim3 grid((uint32_t)chain_blocks), block(NW * 64);
+            if (seg)
+                hipLaunchKernelGGL((chain_kernel<C, DK, DV, NW, true>), grid, block, sizeof(Lds), st, header, first,
+                                   order, varlen, a.T, a.H, (int32_t)pairs, records, a.lay.record_bytes, a.init_state,
+                                   a.final_state, states, deltas, c0, c1, carry, slot0);
+            else
+                hipLaunchKernelGGL((chain_kernel<C, DK, DV, NW, false>), grid, block, sizeof(Lds), st, header, first,
+                                   order, varlen, a.T, a.H, (int32_t)pairs, records, a.lay.record_bytes, a.init_state,
+                                   a.final_state, states, deltas, c0, c1, carry, slot0);
+            return hipGetLastError();
+        }
     };
     auto launch_output = [&](int64_t c0, int64_t c1, hipStream_t st, int64_t slot0 = 0) -> hipError_t {
         if (c1 <= c0) return hipSuccess;
