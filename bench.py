@@ -19,9 +19,9 @@ reported under "decode" (state GB/s).
 Roofline: the dominant kernel of the step is the state chain.  Its achieved
 rate is its algorithmic flops per launch over its average launch duration
 (the one-launch form of the stage-by-stage run):
-4 d_k d_v flops per token and head (Delta = U - W S^T and the rank-C state
-update, 2 d_k d_v each), the dense contraction it performs; peak is dense
-bf16 MFMA.  Whole-path figures use F_tok = H [6 d_k d_v + C (3 d_k + 2 d_v)
+4 d_k d_v flops per token and head (Delta = U - W S^T, which the bf16 chain
+forms as U - T' (K S^T), and the rank-C state update, 2 d_k d_v each), the
+dense contraction it performs; peak is dense bf16 MFMA.  Whole-path figures use F_tok = H [6 d_k d_v + C (3 d_k + 2 d_v)
 + C^2 / 3] flops per token and the minimum HBM traffic (q, k, v, o in bf16,
 g and beta in fp32).
 
@@ -554,13 +554,13 @@ def main():
                    "global_batch": 1, "seq_len": T, "heads": H, "d_k": DK, "d_v": DV, "chunk": C,
                    "parallelism": "single-gpu"},
         "roofline": {
-            "kernel": "chain_kernel (sequential state chain, one launch over all chunks)",
+            "kernel": "chain_kr_kernel (sequential state chain, one launch over all chunks)",
             "bound": "mfma",
             "achieved": chain_tflops,
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": chain_tflops / PEAK_BF16_TFLOPS,
-            "traffic": traffic_from_profiles("chain_kernel"),
+            "traffic": traffic_from_profiles("chain_kr_kernel"),
             "avg_launch_ms": pre["chain_ms"],
             "algorithmic_flops_per_launch": chain_flops,
         },

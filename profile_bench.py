@@ -47,7 +47,7 @@ OUT = os.path.join(ROOT, "profile_out")  # raw profiler output; set by --out
 PROFILES = os.path.join(ROOT, "profiles")
 # more specific names first: a kernel is keyed by the first entry its name contains
 KERNELS = ("bwd_chain_kernel", "bwd_local_kernel", "bwd_grad_kernel", "bwd_table_kernel", "conv_silu_kernel",
-           "conv_decode_kernel", "chain_kernel", "intra_kernel", "output_kernel", "decode_kernel", "chunk_table_kernel")
+           "conv_decode_kernel", "chain_kr_kernel", "chain_kernel", "intra_kernel", "output_kernel", "decode_kernel", "chunk_table_kernel")
 COPY_BYTES = 1 << 30
 BENCH_TRACE = ["bench.py", "--steps", "5", "--warmup", "2", "--decode-steps", "32", "--no-cpu-baseline", "--no-other"]
 BENCH_PMC = ["bench.py", "--steps", "1", "--warmup", "1", "--decode-steps", "4", "--no-cpu-baseline", "--no-other",
@@ -150,7 +150,7 @@ def full_launch(name, grid, groups):
     else the largest grid of the kernel."""
     if kernel_key(name).startswith("bwd_"):
         return True  # the backward has no segmented launches
-    if "chain_kernel" in name:
+    if kernel_key(name) in ("chain_kr_kernel", "chain_kernel"):
         return ", false>" in name
     grids = [g for (nm, g) in groups if kernel_key(nm) == kernel_key(name)]
     if kernel_key(name) == "decode_kernel":
@@ -198,7 +198,7 @@ def mode_traffic():
         if not profiler_ok(rc, d, "counter_collection.csv") or counter_sums(d).get("copy") is None:
             raise SystemExit(f"copy calibration for {counter} failed (exit {rc})")
         rc, d, cmd = launch(BENCH_PMC, ["--pmc", counter, "--kernel-include-regex",
-                                        "chain_kernel|intra_kernel|output_kernel|decode_kernel|conv_silu_kernel"],
+                                        "chain_kr_kernel|intra_kernel|output_kernel|decode_kernel|conv_silu_kernel"],
                             f"bench_{counter}", 600)
         cmds.append(cmd)
         if not profiler_ok(rc, d, "counter_collection.csv"):
@@ -263,7 +263,7 @@ def render_traffic():
 
 
 MFMA_COUNTERS = ("MfmaUtil", "MfmaFlops", "MfmaFlopsBF16", "MfmaFlopsF32")
-MFMA_KERNELS = "chain_kernel|intra_kernel|output_kernel"
+MFMA_KERNELS = "chain_kr_kernel|intra_kernel|output_kernel"
 BENCH_PMC_BWD = ["bench.py", "--steps", "1", "--warmup", "1", "--no-decode", "--no-other", "--no-cpu-baseline"]
 
 
@@ -331,16 +331,16 @@ def render_mfma():
              "workgroups return at once, so 6 heads x 16 row blocks = 96 work).", "",
              "| kernel | dispatches | workgroups | us (counter run) | executed GFLOP | of which bf16"
              " | executed TFLOP/s | MfmaUtil % | % per occupied CU |", "|---|---|---|---|---|---|---|---|---|"]
-    for key in ("intra_kernel", "chain_kernel", "output_kernel"):
+    for key in ("intra_kernel", "chain_kr_kernel", "output_kernel"):
         e = table.get(key)
         if e is None:
             continue
         tf = e["MfmaFlops"] / (e["ns"] * 1e-9) / 1e12 if e["ns"] > 0 else float("nan")
-        working = bench.H * (bench.DV // 16) if key == "chain_kernel" else e["wg"]
+        working = bench.H * (bench.DV // 16) if key == "chain_kr_kernel" else e["wg"]
         occ = e["MfmaUtil"] * 256 / min(256.0, max(1.0, working))
         lines.append(f"| `{key}` | {e['n']} | {e['wg']:.0f} | {e['ns'] / 1e3:.0f} | {e['MfmaFlops'] / 1e9:.1f}"
                      f" | {e['MfmaFlopsBF16'] / 1e9:.1f} | {tf:.1f} | {e['MfmaUtil']:.2f} | {occ:.2f} |")
-    ch = table.get("chain_kernel")
+    ch = table.get("chain_kr_kernel")
     if ch is not None:
         lines += ["", f"State chain: algorithmic {chain_alg / 1e9:.1f} GFLOP per launch (4 d_k d_v per token and head);",
                   f"executed / algorithmic = {ch['MfmaFlops'] / chain_alg:.2f}.", ""]
