@@ -289,32 +289,36 @@ def bench_decode(torch, gdn, synth, n_steps, warmup=3):
 
 
 def bench_prefill_other(torch, gdn, synth, steps, warmup, ctx):
-    """The two other prefill workloads, timed as whole-prefill calls: 8K tokens
-    (B=1, H=6, d=256, bf16) and the packed 2M-token batch (16 sequences,
-    log-uniform lengths in [4K, 512K])."""
+    """The other prefill workloads, timed as whole-prefill calls: 8K tokens
+    (B=1, H=6, d=256, bf16), 64K tokens at d_v = 512, and the packed 2M-token
+    batch (16 sequences, log-uniform lengths in [4K, 512K]) with a full-size
+    workspace and with one bounded to 8 GiB (the chunks then run in windows)."""
     dev = torch.device("cuda:0")
     res = {}
     inp = synth.prefill_inputs(8192, H, DK, DV, "bf16", seed=synth.seed_for("prefill8k"))
     q, k, v = (synth.to_torch(x, dev, bf16=True) for x in (inp.q, inp.k, inp.v))
     g, beta = synth.to_torch(inp.g, dev), synth.to_torch(inp.beta, dev)
-    cases = [("prefill_8k", (q, k, v, g, beta), None, None)]
+    cases = [("prefill_8k", (q, k, v, g, beta), None, None, None)]
     # d_v = 2 d_k = 512, the value width of the pages' GDN layer (64K tokens)
     inp5 = synth.prefill_inputs(T, H, DK, 2 * DV, "bf16", seed=synth.seed_for("prefill64k"))
     cases.append(("prefill_64k_dv512", tuple(synth.to_torch(x, dev, bf16=True) for x in (inp5.q, inp5.k, inp5.v))
-                  + (synth.to_torch(inp5.g, dev), synth.to_torch(inp5.beta, dev)), None, None))
+                  + (synth.to_torch(inp5.g, dev), synth.to_torch(inp5.beta, dev)), None, None, None))
     del inp5
     lengths = synth.varlen_lengths(synth.seed_for("varlen2m"))
     log(f"[bench] generating the 2M-token packed batch (lengths {list(map(int, lengths))})")
     vq, vk, vv, vg, vb, cu = synth.varlen_torch_inputs(lengths, H, DK, DV, synth.seed_for("varlen2m"), dev)
     cu_host = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
-    cases.append(("varlen_2m", (vq, vk, vv, vg, vb), cu_host, lengths))
+    cases.append(("varlen_2m", (vq, vk, vv, vg, vb), cu_host, lengths, None))
+    cases.append(("varlen_2m_workspace_8GiB", (vq, vk, vv, vg, vb), cu_host, lengths, 8 << 30))
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    for name, (a, b, c, d, e), cuh, lens in cases:
+    for name, (a, b, c, d, e), cuh, lens, ws_cap in cases:
         Tn, N, dvn = a.shape[0], (1 if cuh is None else len(lens)), c.shape[2]
         o = torch.empty((Tn, H, dvn), dtype=torch.bfloat16, device=dev)
         fs = torch.empty((N, H, dvn, DK), dtype=torch.float32, device=dev)
-        ws = torch.empty(gdn.prefill_workspace_size(Tn, N, H, DK, dvn, C), dtype=torch.uint8, device=dev)
+        need = gdn.prefill_workspace_size(Tn, N, H, DK, dvn, C)
+        ws_bytes = need if ws_cap is None else min(need, ws_cap)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
         cu_arg = None if cuh is None else torch.from_numpy(cuh)
         run = lambda: gdn.chunk_prefill(a, b, c, d, e, cu_seqlens=cu_arg, chunk=C, out=o, final_state=fs,
                                         workspace=ws, ctx=ctx)
@@ -330,6 +334,7 @@ def bench_prefill_other(torch, gdn, synth, steps, warmup, ctx):
         ms = t0.elapsed_time(t1) / n_steps
         f_tok = H * (6 * DK * dvn + C * (3 * DK + 2 * dvn) + C * C / 3.0)
         ent = {"tokens": int(Tn), "d_v": int(dvn), "ms_per_step": ms, "tokens_per_s": Tn / (ms / 1e3),
+               "workspace_GiB": ws_bytes / 2**30, "full_workspace_GiB": need / 2**30,
                "mfma_frac": f_tok * Tn / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
                "min_traffic_hbm_frac": Tn * H * ((2 * DK + 2 * dvn) * 2 + 8) / (ms / 1e3) / 1e9 / PEAK_HBM_GBPS}
         if lens is not None:

@@ -187,6 +187,17 @@ size_t gdn_prefill_workspace_size(int64_t total_tokens, int32_t num_seqs, int32_
     return gdn::prefill_layout(total_tokens, num_seqs, H, dk, dv, chunk, dt == GDN_BF16).total;
 }
 
+size_t gdn_prefill_workspace_min_size(int64_t total_tokens, int32_t num_seqs, int32_t H, int32_t dk, int32_t dv,
+                                      int32_t chunk, gdn_dtype dt)
+{
+    if (total_tokens < 0 || num_seqs < 1 || H < 1) return 0;
+    if (dt != GDN_F32 && dt != GDN_BF16) return 0;
+    if (!gdn::prefill_supported(dt == GDN_BF16, dk, dv, chunk)) return 0;
+    const size_t full = gdn::prefill_layout(total_tokens, num_seqs, H, dk, dv, chunk, dt == GDN_BF16).total;
+    const size_t one = gdn::prefill_layout(total_tokens, num_seqs, H, dk, dv, chunk, dt == GDN_BF16, 1).total;
+    return one < full ? one : full;
+}
+
 gdn_status gdn_context_create(int32_t chain_cus_per_xcd, gdn_context_t* ctx)
 {
     if (!ctx) return GDN_ERR_NULL_ARG;
@@ -213,6 +224,22 @@ gdn_status check_norm(const gdn::GatedNorm& nm, bool need_z)
     if (nm.w && !aligned4(nm.w)) return GDN_ERR_ALIGNMENT;
     if (!(nm.eps >= 0.f) || !(nm.eps < INFINITY)) return GDN_ERR_BAD_SHAPE;
     return GDN_OK;
+}
+
+// Chunks per window of a workspace of `capacity` bytes: 0 when the whole
+// layout fits, else the largest window (>= 1 chunk) whose layout fits, or -1
+// when not even one chunk does.
+int64_t fit_window(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv, int32_t chunk, bool bf16, size_t capacity)
+{
+    const gdn::PrefillLayout full = gdn::prefill_layout(T, N, H, dk, dv, chunk, bf16);
+    if (full.total <= capacity) return 0;
+    if (gdn::prefill_layout(T, N, H, dk, dv, chunk, bf16, 1).total > capacity) return -1;
+    int64_t lo = 1, hi = full.max_chunks;  // layout(lo) fits, layout(hi) does not
+    while (hi - lo > 1) {
+        const int64_t mid = lo + (hi - lo) / 2;
+        (gdn::prefill_layout(T, N, H, dk, dv, chunk, bf16, mid).total <= capacity ? lo : hi) = mid;
+    }
+    return lo;
 }
 
 gdn_status prefill_impl(const void* q, const void* k, const void* v, const float* g, const float* beta,
@@ -242,23 +269,15 @@ gdn_status prefill_impl(const void* q, const void* k, const void* v, const float
         for (int32_t n = 0; n < num_seqs; ++n)
             if (cu_seqlens_host[n + 1] < cu_seqlens_host[n]) return GDN_ERR_BAD_SEQLENS;
     }
-    gdn::PrefillLayout lay = gdn::prefill_layout(total_tokens, num_seqs, H, dk, dv, chunk, bf16);
-    int64_t window = 0;
+    // The workspace (the caller's, or the library's scratch array) holds every
+    // chunk's intermediates when it is large enough; else, for a call that runs
+    // every stage, the largest window of chunks that fits, processed window by
+    // window with the state carried in between (bit-identical results).
+    const size_t capacity = use_scratch ? gdn::kScratchBytes : workspace_bytes;
+    const int64_t window = fit_window(total_tokens, num_seqs, H, dk, dv, chunk, bf16, capacity);
+    if (window < 0 || (window > 0 && stages != GDN_STAGE_ALL)) return GDN_ERR_WORKSPACE;
+    const gdn::PrefillLayout lay = gdn::prefill_layout(total_tokens, num_seqs, H, dk, dv, chunk, bf16, window);
     if (use_scratch) {
-        // The library's scratch array: the whole workspace if it fits, else the
-        // largest window of chunks that does (binary search; at least one chunk).
-        if (lay.total > gdn::kScratchBytes) {
-            if (gdn::prefill_layout(total_tokens, num_seqs, H, dk, dv, chunk, bf16, 1).total > gdn::kScratchBytes)
-                return GDN_ERR_WORKSPACE;
-            int64_t lo = 1, hi = lay.max_chunks;  // layout(lo) fits, layout(hi) does not
-            while (hi - lo > 1) {
-                const int64_t mid = lo + (hi - lo) / 2;
-                const size_t need = gdn::prefill_layout(total_tokens, num_seqs, H, dk, dv, chunk, bf16, mid).total;
-                (need <= gdn::kScratchBytes ? lo : hi) = mid;
-            }
-            window = lo;
-            lay = gdn::prefill_layout(total_tokens, num_seqs, H, dk, dv, chunk, bf16, window);
-        }
         if (gdn::scratch_device_ptr(&workspace) != hipSuccess || !workspace) return GDN_ERR_LAUNCH;
         workspace_bytes = gdn::kScratchBytes;
     }

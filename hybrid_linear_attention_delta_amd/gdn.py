@@ -52,6 +52,8 @@ def load_library(path: str | None = None):
             vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
             lib.gdn_prefill_workspace_size.argtypes = [i64, i32, i32, i32, i32, i32, ctypes.c_int]
             lib.gdn_prefill_workspace_size.restype = sz
+            lib.gdn_prefill_workspace_min_size.argtypes = [i64, i32, i32, i32, i32, i32, ctypes.c_int]
+            lib.gdn_prefill_workspace_min_size.restype = sz
             lib.gdn_chunk_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32,
                                               ctypes.c_int, f32, i32, vp, vp, vp, sz, vp]
             lib.gdn_chunk_prefill.restype = ctypes.c_int
@@ -188,6 +190,15 @@ def prefill_workspace_size(total_tokens: int, num_seqs: int, H: int, dk: int, dv
     return int(load_library().gdn_prefill_workspace_size(total_tokens, num_seqs, H, dk, dv, chunk, code))
 
 
+def prefill_workspace_min_size(total_tokens: int, num_seqs: int, H: int, dk: int, dv: int, chunk: int = 64,
+                               dtype=None) -> int:
+    """Smallest workspace a whole-prefill call accepts (gdn_prefill_workspace_min_size):
+    below prefill_workspace_size the chunks run in windows that fit, bit-identically."""
+    torch = _torch()
+    code = GDN_BF16 if (dtype is None or dtype == torch.bfloat16) else GDN_F32
+    return int(load_library().gdn_prefill_workspace_min_size(total_tokens, num_seqs, H, dk, dv, chunk, code))
+
+
 def _norm_args(gate, norm_weight, shape, dt, dev):
     torch = _torch()
     _check(gate, "gate", dtype=dt, device=dev)
@@ -257,8 +268,10 @@ def chunk_prefill(q, k, v, g, beta, init_state=None, cu_seqlens=None, scale=None
     need = int(lib.gdn_prefill_workspace_size(T, N, H, dk, dv, chunk, code))
     if need == 0:
         raise GdnError(3, "gdn_prefill_workspace_size")
-    if workspace is None or workspace.numel() < need:
+    if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    else:  # a smaller buffer (down to prefill_workspace_min_size) runs the chunks in windows
+        _check(workspace, "workspace", dtype=torch.uint8, device=dev)
     s = -1.0 if scale is None else float(scale)
     cu_host_ptr = None if cu_host is None else ctypes.c_void_p(cu_host.data_ptr())
     if gate is not None:
@@ -522,8 +535,10 @@ def chunk_prefill_frontend(xq, xk, xv, conv_weight, a, b, A_log, dt_bias, conv_s
     need = int(lib.gdn_prefill_workspace_size(T, N, H, dk, dv, chunk, code))
     if need == 0:
         raise GdnError(3, "gdn_prefill_workspace_size")
-    if workspace is None or workspace.numel() < need:
+    if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    else:  # a smaller buffer (down to prefill_workspace_min_size) runs the chunks in windows
+        _check(workspace, "workspace", dtype=torch.uint8, device=dev)
     s = -1.0 if scale is None else float(scale)
     cu_host_ptr = None if cu_host is None else ctypes.c_void_p(cu_host.data_ptr())
     st = lib.gdn_chunk_prefill_frontend(None if ctx is None else ctx.handle, _ptr(xq), _ptr(xk), _ptr(xv),

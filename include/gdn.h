@@ -57,7 +57,7 @@ typedef enum {
     GDN_ERR_UNSUPPORTED = 3,  /* (dtype, d_k, d_v, chunk) combination not built             */
     GDN_ERR_BAD_SEQLENS = 4,  /* cu_seqlens not 0 = c_0 <= c_1 <= ... <= c_N = total_tokens  */
     GDN_ERR_ALIGNMENT = 5,    /* q/k/v/o/state not 16-byte, g/beta not 4-byte aligned       */
-    GDN_ERR_WORKSPACE = 6,    /* workspace NULL or smaller than gdn_prefill_workspace_size */
+    GDN_ERR_WORKSPACE = 6,    /* workspace NULL or too small (see gdn_prefill_workspace_size)  */
     GDN_ERR_LAUNCH = 7,       /* a kernel launch failed (or, under GDN_DEBUG_SYNC, faulted) */
     GDN_ERR_CONTEXT = 8       /* context creation failed, or the context belongs to another device */
 } gdn_status;
@@ -80,6 +80,21 @@ typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
  */
 size_t gdn_prefill_workspace_size(int64_t total_tokens, int32_t num_seqs, int32_t H, int32_t dk,
                                   int32_t dv, int32_t chunk, gdn_dtype dt);
+
+/*
+ * Smallest workspace gdn_chunk_prefill (and the _ctx, _gated and _frontend
+ * forms) accept for these sizes: room for the chunk table, the per-sequence
+ * fp32 state carry (num_seqs x H x dv x dk) and one chunk's intermediates.
+ * Between this and gdn_prefill_workspace_size, the call processes the chunks
+ * in the largest windows that fit, one window after another on its stream
+ * (each stage over the window, each sequence's state carried from window to
+ * window in fp32); results are bit-identical to a full-size workspace's, the
+ * overlap of the stages is given up, and a sequence cut by window boundaries
+ * runs its chain in pieces.  (gdn_chunk_prefill_staged with a subset of the
+ * stages needs the full size.)  Returns 0 for an unsupported combination.
+ */
+size_t gdn_prefill_workspace_min_size(int64_t total_tokens, int32_t num_seqs, int32_t H, int32_t dk,
+                                      int32_t dv, int32_t chunk, gdn_dtype dt);
 
 /*
  * Chunked prefill over packed variable-length sequences (App. A.3, last
@@ -106,8 +121,9 @@ size_t gdn_prefill_workspace_size(int64_t total_tokens, int32_t num_seqs, int32_
  *   o           [total_tokens, H, dv]   dt (written)
  *   final_state [num_seqs, H, dv, dk]   fp32 (written), may be NULL, may
  *               alias init_state exactly (in-place carry)
- *   workspace   device buffer of at least gdn_prefill_workspace_size(...)
- *               bytes, 256-byte aligned
+ *   workspace   device buffer, 256-byte aligned, of gdn_prefill_workspace_size(...)
+ *               bytes, or of fewer but at least gdn_prefill_workspace_min_size(...)
+ *               (then processed in windows of chunks, see there)
  * Sequences of length 0 are allowed: their final state equals the initial.
  */
 gdn_status gdn_chunk_prefill(const void* q, const void* k, const void* v, const float* g, const float* beta,

@@ -34,6 +34,7 @@ struct gdn_context {
 };
 
 static int g_launches = 0;
+static int64_t g_last_window = -1;  // window of the last prefill launch (0: the whole workspace)
 static volatile unsigned char g_sink = 0;
 
 static void touch(const void* base, size_t off, size_t bytes)
@@ -80,7 +81,8 @@ hipError_t launch_prefill(const PrefillArgs& a)
     touch(a.ws, 0, L.total);  // the whole workspace belongs to the caller's buffer
     touch(a.ws, L.off_carry, (size_t)a.N * a.H * a.dv * a.dk * 4);
     assert(a.window >= 0);
-    if (a.window > 0) assert(L.total <= kScratchBytes);
+    if (a.window > 0) assert(a.stages == 7);  // windows only for calls that run every stage
+    g_last_window = a.window;
     return hipSuccess;
 }
 hipError_t launch_decode(const DecodeArgs&)
@@ -169,7 +171,13 @@ int main()
         const int32_t cu[] = {0, 70, 70, 200, 201};
         const size_t ws = gdn_prefill_workspace_size(201, 4, 2, 64, 64, 64, GDN_BF16);
         CHECK(prefill(201, 4, 2, 64, 64, 64, GDN_BF16, cu, ws) == GDN_OK);
-        CHECK(prefill(201, 4, 2, 64, 64, 64, GDN_BF16, cu, ws - 1) == GDN_ERR_WORKSPACE);
+        // below the full size: windows of chunks (the whole buffer still in bounds), down to the minimum
+        CHECK(prefill(201, 4, 2, 64, 64, 64, GDN_BF16, cu, ws - 1) == GDN_OK && g_last_window > 0);
+        const size_t mn = gdn_prefill_workspace_min_size(201, 4, 2, 64, 64, 64, GDN_BF16);
+        CHECK(mn > 0 && mn < ws);
+        CHECK(prefill(201, 4, 2, 64, 64, 64, GDN_BF16, cu, mn) == GDN_OK && g_last_window == 1);
+        CHECK(prefill(201, 4, 2, 64, 64, 64, GDN_BF16, cu, mn - 1) == GDN_ERR_WORKSPACE);
+        CHECK(prefill(201, 4, 2, 64, 64, 64, GDN_BF16, cu, ws) == GDN_OK && g_last_window == 0);
         const int32_t bad[] = {0, 70, 60, 200, 201};
         CHECK(prefill(201, 4, 2, 64, 64, 64, GDN_BF16, bad, ws) == GDN_ERR_BAD_SEQLENS);
     }
@@ -194,7 +202,14 @@ int main()
     const size_t ws = gdn_prefill_workspace_size(128, 1, 2, 64, 64, 64, GDN_BF16);
     CHECK(prefill(128, 1, 2, 48, 64, 64, GDN_BF16, nullptr, ws) == GDN_ERR_UNSUPPORTED);
     CHECK(prefill(128, 1, 2, 64, 64, 32, GDN_BF16, nullptr, ws) == GDN_ERR_UNSUPPORTED);
-    CHECK(prefill(128, 1, 2, 64, 64, 64, GDN_BF16, nullptr, ws - 1) == GDN_ERR_WORKSPACE);
+    CHECK(prefill(128, 1, 2, 64, 64, 64, GDN_BF16, nullptr,
+                  gdn_prefill_workspace_min_size(128, 1, 2, 64, 64, 64, GDN_BF16) - 1) == GDN_ERR_WORKSPACE);
+    {  // a stage subset needs the full size
+        Buf x(1 << 16), w(ws);
+        CHECK(gdn_chunk_prefill_staged(x.p(), x.p(), x.p(), (float*)x.p(), (float*)x.p(), nullptr, nullptr, nullptr, 1,
+                                       128, 2, 64, 64, 64, GDN_BF16, -1.f, 1, x.p(), nullptr, w.p(), ws - 1,
+                                       GDN_STAGE_PREPARE, nullptr) == GDN_ERR_WORKSPACE);
+    }
     CHECK(prefill(128, 2, 2, 64, 64, 64, GDN_BF16, nullptr, ws) == GDN_ERR_BAD_SHAPE);
     CHECK(prefill(-1, 1, 2, 64, 64, 64, GDN_BF16, nullptr, ws) == GDN_ERR_BAD_SHAPE);
 

@@ -250,3 +250,28 @@ def test_backward_host_validation(lib):
     assert bwd_states(_fake(0x40000), None, _fake(0x40000)) == 2   # the initial-state gradient over init_state
     assert bwd_states(None, _fake(0x40000), _fake(0x44000)) == 2   # partly over d_final_state
     assert bwd_states(None, _fake(0x40000), _fake(0x40000)) == 2   # or exactly
+
+
+def test_workspace_min_size_and_windowed_workspace_checks(lib):
+    """gdn_prefill_workspace_min_size: between it and the full size a whole-prefill
+    call runs in windows of chunks; below it, or for a subset of the stages with
+    less than the full size, the call is refused before any launch."""
+    args = (65536, 1, 6, 256, 256, 64, gdn.GDN_BF16)
+    full = lib.gdn_prefill_workspace_size(*args)
+    mn = lib.gdn_prefill_workspace_min_size(*args)
+    assert 0 < mn < full
+    assert mn >= 6 * 256 * 256 * 4  # at least the fp32 state carry of the six (sequence, head) pairs
+    assert lib.gdn_prefill_workspace_min_size(1024, 1, 6, 256, 256, 32, gdn.GDN_BF16) == 0  # unsupported
+    assert lib.gdn_prefill_workspace_min_size(-1, 1, 2, 16, 16, 16, gdn.GDN_F32) == 0
+    # the minimum grows with the carried state (sequences), not with the tokens
+    assert lib.gdn_prefill_workspace_min_size(8 * 65536, 1, 6, 256, 256, 64, gdn.GDN_BF16) < full
+    T = 4096
+    mn = lib.gdn_prefill_workspace_min_size(T, 1, 2, 64, 64, 64, gdn.GDN_BF16)
+    full = lib.gdn_prefill_workspace_size(T, 1, 2, 64, 64, 64, gdn.GDN_BF16)
+    assert _prefill(lib, T=T, wsb=mn - 256) == 6
+    f = _fake()
+    staged = lambda wsb, stages: lib.gdn_chunk_prefill_staged(f, f, f, f, f, None, None, None, 1, T, 2, 64, 64, 64,
+                                                               gdn.GDN_BF16, -1.0, 1, f, None, _fake(0x100000), wsb,
+                                                               stages, None)
+    assert staged(full - 256, gdn.STAGE_PREPARE) == 6
+    assert staged(mn, gdn.STAGE_ALL ^ gdn.STAGE_OUTPUT) == 6
