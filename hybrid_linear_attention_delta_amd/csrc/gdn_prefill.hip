@@ -1408,6 +1408,64 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Hand-offs of the pipelined prefill through device memory.  The bf16 state
+// chain runs as one launch over every chunk while the intra-chunk kernel
+// prepares the chunks segment by segment and the output kernel finishes them
+// on other CUs.  flags[s] (s < kPipeMaxSeg) is raised by a one-wave kernel that
+// follows segment s's intra-chunk kernel on its stream, so the kernel boundary
+// has already made the records visible to the whole device; the chain's
+// loader waves wait for it before the first transfer of a chunk of segment s.
+// flags[kPipeMaxSeg + s] counts the chain's store waves (kPipePublishers per
+// workgroup) that have written their part of every state and Delta of segment
+// s, each after releasing its stores at agent scope; a one-wave kernel waits
+// for all of them in front of segment s's output kernel.  flags[2 kPipeMaxSeg] counts waits that gave up.  Every wait
+// is bounded by the device's constant 100 MHz clock (kPipeWaitTicks, about
+// 1.3 s), so no wave can spin forever; one that gives up counts itself in
+// flags[2 kPipeMaxSeg] and goes on.
+constexpr int kPipeMaxSeg = 16;
+constexpr int kPipeFlags = 2 * kPipeMaxSeg + 1;
+constexpr uint64_t kPipeWaitTicks = (uint64_t)1 << 27;
+constexpr uint32_t kPipePublishers = 2;  // store waves of a bf16 chain workgroup
+struct PipeSync {
+    uint32_t* flags;              // kPipeFlags words in the workspace header; null: no pipeline
+    int32_t nseg;                 // segments
+    int64_t end[kPipeMaxSeg];     // first chunk after segment s (end[nseg - 1] = every chunk)
+};
+
+// Waits until *p >= target (agent-scope loads), then acquires at agent scope.
+__device__ __forceinline__ void pipe_wait(const uint32_t* p, uint32_t target, uint32_t* gave_up)
+{
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    while (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+        if (__builtin_amdgcn_s_memrealtime() - t0 > kPipeWaitTicks) {
+            if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_add(gave_up, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(8);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
+// Zeroes the hand-off words (a kernel, not a memset, so that the call may be
+// captured into a graph).
+__global__ __launch_bounds__(64) void pipe_reset_kernel(uint32_t* flags)
+{
+    for (int i = threadIdx.x; i < kPipeFlags; i += 64) flags[i] = 0u;
+}
+
+// Raises flags[s]: every record of segment s, written by the kernels before
+// this one on its stream, is visible to the device.
+__global__ __launch_bounds__(64) void pipe_signal_kernel(uint32_t* flags, int32_t s)
+{
+    if (threadIdx.x == 0) __hip_atomic_store(flags + s, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Returns once `target` chain workgroups have finished segment s.
+__global__ __launch_bounds__(64) void pipe_wait_kernel(uint32_t* flags, int32_t s, uint32_t target)
+{
+    pipe_wait(flags + kPipeMaxSeg + s, target, flags + 2 * kPipeMaxSeg);
+}
+
 // State chain, fp32 operands: one workgroup of NW waves per (sequence, head,
 // 16 state rows), sequential over the sequence's chunks, operands read from the
 // record.  Per chunk c:
@@ -1639,7 +1697,7 @@ __global__ __launch_bounds__(1024) void chain_kr_kernel(
     const int32_t* __restrict__ seq_order, int32_t varlen, int64_t T, int32_t H, int32_t pairs,
     const unsigned char* records, size_t record_bytes, const float* init_state, float* final_state,
     uint16_t* __restrict__ states, uint16_t* __restrict__ deltas, int64_t seg_begin, int64_t seg_end, float* carry,
-    int64_t slot0)
+    int64_t slot0, PipeSync ps)
 {
     using M = Mma<uint16_t>;
     using R = Rec<uint16_t, 64, DK, DV>;
@@ -1654,6 +1712,7 @@ __global__ __launch_bounds__(1024) void chain_kr_kernel(
     constexpr int TILES = DV / 16;
     constexpr uint32_t FB = 64 * 16;             // bytes of one fragment
     constexpr int ND = 6;                        // transfer loaders
+    static_assert(16 - NW - ND == (int)kPipePublishers, "the other loader waves store");
     constexpr int NJ = (NDMA + ND - 1) / ND;     // transfers of the busiest loader
     constexpr int J1 = (NJ + 2) / 3, J2 = (2 * NJ + 2) / 3;  // burst bounds (phase 1 | 2 | 3)
     static_assert(KS == M::KS && E == M::E && CKS == 2 && RT == R::RT, "chunk 64");
@@ -1672,9 +1731,19 @@ __global__ __launch_bounds__(1024) void chain_kr_kernel(
     const int tile = slot % TILES;
     const int row0 = tile * 16;  // first state row (value index) of this workgroup
 
+    // this workgroup is done with every segment: nothing of it waits for it
+    auto pipe_release_all = [&]() {
+        if (ps.flags && threadIdx.x == 0)
+            for (int q = 0; q < ps.nseg; ++q)
+                __hip_atomic_fetch_add(ps.flags + kPipeMaxSeg + q, kPipePublishers, __ATOMIC_RELEASE,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+    };
     int64_t s_first, s_last;  // the sequence's chunk range
     if (varlen) {
-        if (header[0] != 0) return;
+        if (header[0] != 0) {
+            pipe_release_all();
+            return;
+        }
         s_first = seq_first[n];
         s_last = seq_first[n + 1];
     } else {
@@ -1683,7 +1752,10 @@ __global__ __launch_bounds__(1024) void chain_kr_kernel(
     }
     const int64_t c_begin = SEG && s_first < seg_begin ? seg_begin : s_first;
     const int64_t c_end = SEG && s_last > seg_end ? seg_end : s_last;
-    if (c_begin >= c_end && !(s_first == s_last && s_first >= seg_begin && s_first < seg_end)) return;
+    if (c_begin >= c_end && !(s_first == s_last && s_first >= seg_begin && s_first < seg_end)) {
+        pipe_release_all();
+        return;
+    }
     const float* state_in = c_begin == s_first ? init_state : carry;
     float* state_out_ptr = c_end == s_last ? final_state : carry;
     const int64_t last = c_end - 1;
@@ -1702,7 +1774,14 @@ __global__ __launch_bounds__(1024) void chain_kr_kernel(
         const int lw = wave - NW;
         if (lw < ND) {
             // transfers j0 .. j1-1 of this loader for chunk cc (transfer i = lw + ND j)
+            int64_t ready_below = ps.flags ? 0 : INT64_MAX;  // chunks below this are known to be prepared
+            int seg = 0;
             auto transfers = [&](int64_t cc, int j0, int j1) {
+                while (cc >= ready_below) {  // the first chunk of a later segment
+                    while (seg + 1 < ps.nseg && ps.end[seg] <= cc) ++seg;
+                    pipe_wait(ps.flags + seg, 1u, ps.flags + 2 * kPipeMaxSeg);
+                    ready_below = seg + 1 < ps.nseg ? ps.end[seg] : INT64_MAX;
+                }
                 const unsigned char* rb = rec_ptr(cc);
                 const __amdgpu_buffer_rsrc_t r = make_rsrc(rb, (uint32_t)R::BYTES);
                 const __amdgpu_buffer_rsrc_t rv = make_rsrc(rb + R::KSC_BYTE_OFF, C * 4 + 16);  // lanes past: zeros
@@ -1778,15 +1857,36 @@ __global__ __launch_bounds__(1024) void chain_kr_kernel(
                 __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)((uint32_t)row * C * 2 + q * 16), 0, kNtAux);
             }
         };
+        // segments whose states and Delta this store wave has written its part
+        // of: release the stores at agent scope, then count the wave in
+        // (the segment index and the next segment end stay wave-uniform, so the
+        // loop keeps its addresses and descriptors in scalar registers)
+        int sig = ps.flags ? 0 : ps.nseg;
+        int64_t next_end = sig < ps.nseg ? ps.end[0] : INT64_MAX;
+        auto publish = [&](int64_t done_below) {
+            int n = sig;
+            while (n < ps.nseg && ps.end[n] <= done_below) ++n;
+            n = __builtin_amdgcn_readfirstlane(n);
+            if (n == sig) return;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            if (lane == 0)
+                for (int q = sig; q < n; ++q)
+                    __hip_atomic_fetch_add(ps.flags + kPipeMaxSeg + q, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            sig = n;
+            next_end = n < ps.nseg ? ps.end[n] : INT64_MAX;
+        };
+        publish(c_begin);
         __syncthreads();
         for (int64_t c = c_begin; c < c_end; ++c) {
             store_state(c);  // before phase 3 rewrites the rows
             lds_barrier();  // ---- A
             lds_barrier();  // ---- B
             store_delta(c);  // before phase 2 of c+1 rewrites it
+            if (c + 1 >= next_end) publish(c + 1);
             lds_barrier();  // ---- C
         }
         wait_vmcnt<0>();
+        publish(INT64_MAX);
         return;
     }
 
@@ -2121,8 +2221,9 @@ __global__ __launch_bounds__(256) void output_kernel(const int32_t* __restrict__
 }  // namespace gdn
 
 // Streams and events of the pipelined prefill, owned by the caller through
-// gdn_context_create / gdn_context_destroy (default priority, non-blocking
-// with respect to the legacy default stream).  The state chain gets a stream
+// gdn_context_create / gdn_context_destroy (default priority; the CU-masked
+// streams synchronise with the legacy default stream, the unmasked fallback
+// streams do not).  The state chain gets a stream
 // of its own, CU-masked to the same number of CUs on every XCD, and the
 // per-segment intra-chunk and output kernels two more streams on all other
 // CUs: the chain's workgroups then never share a CU with the parallel kernels
@@ -2133,6 +2234,7 @@ struct gdn_context {
     std::mutex use;  // held while one call enqueues its pipeline: the events are reused by every call
     int dev = -1;
     int32_t chain_cus = 0;  // CUs of each XCD reserved for the chain
+    bool masked = false;    // the streams are CU-masked, so each has a hardware queue of its own
     hipStream_t chain_s = nullptr, intra_s = nullptr, out_s = nullptr;
     hipEvent_t start = nullptr, intra_end = nullptr, out_end = nullptr;
     hipEvent_t intra_done[MAX_SEG] = {}, chain_done[MAX_SEG] = {};
@@ -2191,6 +2293,7 @@ hipError_t context_create(int32_t chain_cus_per_xcd, gdn_context** out)
         if ((e = hipExtStreamCreateWithCUMask(&r->chain_s, 8, mine)) != hipSuccess) return fail(e);
         if ((e = hipExtStreamCreateWithCUMask(&r->intra_s, 8, rest)) != hipSuccess) return fail(e);
         if ((e = hipExtStreamCreateWithCUMask(&r->out_s, 8, rest)) != hipSuccess) return fail(e);
+        r->masked = true;
     } else {
         if ((e = hipStreamCreateWithFlags(&r->chain_s, hipStreamNonBlocking)) != hipSuccess) return fail(e);
         if ((e = hipStreamCreateWithFlags(&r->intra_s, hipStreamNonBlocking)) != hipSuccess) return fail(e);
@@ -2302,7 +2405,8 @@ static hipError_t run_prefill(const PrefillArgs& a)
                            records, a.lay.record_bytes, c0, c1, slot0, FrontIn{});
         return hipGetLastError();
     };
-    auto launch_chain = [&](int64_t c0, int64_t c1, hipStream_t st, int64_t slot0 = 0) -> hipError_t {
+    auto launch_chain = [&](int64_t c0, int64_t c1, hipStream_t st, int64_t slot0 = 0,
+                            PipeSync pipe = PipeSync{}) -> hipError_t {
         const bool seg = !(c0 == 0 && c1 == ALL);
         if constexpr (sizeof(TIn) == 2) {
             using Lds = ChainKrLds<DK, DV>;
@@ -2313,11 +2417,11 @@ static hipError_t run_prefill(const PrefillArgs& a)
             if (seg)
                 hipLaunchKernelGGL((chain_kr_kernel<DK, DV, true>), grid, block, sizeof(Lds), st, header, first, order,
                                    varlen, a.T, a.H, (int32_t)pairs, records, a.lay.record_bytes, a.init_state,
-                                   a.final_state, states, deltas, c0, c1, carry, slot0);
+                                   a.final_state, states, deltas, c0, c1, carry, slot0, pipe);
             else
                 hipLaunchKernelGGL((chain_kr_kernel<DK, DV, false>), grid, block, sizeof(Lds), st, header, first, order,
                                    varlen, a.T, a.H, (int32_t)pairs, records, a.lay.record_bytes, a.init_state,
-                                   a.final_state, states, deltas, c0, c1, carry, slot0);
+                                   a.final_state, states, deltas, c0, c1, carry, slot0, pipe);
             return hipGetLastError();
         } else {
             constexpr int NW = 8;
@@ -2434,9 +2538,63 @@ static hipError_t run_prefill(const PrefillArgs& a)
         }
     }
     auto seg_lo = [&](int s) { return bounds[std::min(s, nseg)]; };
-    // The first segment's preparation and the last segment's outputs run on the
-    // caller's stream over the whole GPU (nothing else runs then); everything in
-    // between overlaps on the three pipeline streams.
+    // bf16 on CU-masked streams, outside stream capture: the chain runs as one
+    // launch over every chunk and the hand-offs go through device memory
+    // (PipeSync), so the chain never stops between segments.  The caller's
+    // stream zeroes the hand-off words, prepares the first segment over the
+    // whole GPU and, at the end, finishes the last segment's outputs over the
+    // whole GPU; in between the intra-chunk kernel prepares segments 1.. and
+    // the output kernel finishes segments 0..nseg-2 on the two side streams.
+    // A wait in device memory needs its producer to run beside it: masked
+    // streams each own a hardware queue, while a graph's executor, or streams
+    // that share a queue, may run the two in sequence.  Those cases keep the
+    // event-ordered schedule below.
+    hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+    GDN_TRY(hipStreamIsCapturing(a.stream, &capture));
+    if (sizeof(TIn) == 2 && pr->masked && capture == hipStreamCaptureStatusNone) {
+        PipeSync ps{};
+        ps.flags = reinterpret_cast<uint32_t*>(header) + 16;
+        ps.nseg = nseg;
+        for (int s = 0; s < nseg; ++s) ps.end[s] = s + 1 < nseg ? seg_lo(s + 1) : ALL;
+        const uint32_t chain_wgs = (uint32_t)(pairs * (DV / 16)) * kPipePublishers;
+        // The caller's stream only forks the three streams and joins them at the
+        // end: when it is the legacy default stream, every command on it waits
+        // for all work enqueued before on the (blocking) masked streams, and
+        // theirs for all enqueued before on it.  The chain stream zeroes the
+        // hand-off words and starts the chain, whose loaders then wait for the
+        // intra-chunk stream's signals; that stream prepares segment 0 and
+        // waits for the zeroing before its first signal.
+        GDN_TRY(hipEventRecord(pr->start, a.stream));
+        GDN_TRY(hipStreamWaitEvent(pr->chain_s, pr->start, 0));
+        GDN_TRY(hipStreamWaitEvent(pr->intra_s, pr->start, 0));
+        hipLaunchKernelGGL(pipe_reset_kernel, dim3(1), dim3(64), 0, pr->chain_s, ps.flags);
+        GDN_TRY(hipGetLastError());
+        GDN_TRY(hipEventRecord(pr->intra_done[0], pr->chain_s));  // the hand-off words are zero
+        GDN_TRY(launch_chain(0, ALL, pr->chain_s, 0, ps));
+        GDN_TRY(hipEventRecord(pr->chain_done[0], pr->chain_s));
+        for (int s = 0; s < nseg; ++s) {
+            GDN_TRY(launch_intra(seg_lo(s), seg_lo(s + 1), pr->intra_s));
+            if (s == 0) GDN_TRY(hipStreamWaitEvent(pr->intra_s, pr->intra_done[0], 0));
+            hipLaunchKernelGGL(pipe_signal_kernel, dim3(1), dim3(64), 0, pr->intra_s, ps.flags, s);
+            GDN_TRY(hipGetLastError());
+        }
+        GDN_TRY(hipEventRecord(pr->intra_end, pr->intra_s));
+        GDN_TRY(hipStreamWaitEvent(pr->out_s, pr->intra_done[0], 0));
+        for (int s = 0; s < nseg; ++s) {
+            hipLaunchKernelGGL(pipe_wait_kernel, dim3(1), dim3(64), 0, pr->out_s, ps.flags, s, chain_wgs);
+            GDN_TRY(hipGetLastError());
+            GDN_TRY(launch_output(seg_lo(s), seg_lo(s + 1), pr->out_s));
+        }
+        GDN_TRY(hipEventRecord(pr->out_end, pr->out_s));
+        GDN_TRY(hipStreamWaitEvent(a.stream, pr->intra_end, 0));
+        GDN_TRY(hipStreamWaitEvent(a.stream, pr->chain_done[0], 0));
+        GDN_TRY(hipStreamWaitEvent(a.stream, pr->out_end, 0));
+        return hipSuccess;
+    }
+    // One chain launch per segment, ordered by events.  The first
+    // segment's preparation and the last segment's outputs run on the caller's
+    // stream over the whole GPU (nothing else runs then); everything in between
+    // overlaps on the three pipeline streams.
     GDN_TRY(launch_intra(0, seg_lo(1), a.stream));
     GDN_TRY(hipEventRecord(pr->start, a.stream));
     GDN_TRY(hipStreamWaitEvent(pr->chain_s, pr->start, 0));
