@@ -152,6 +152,12 @@ BwdLayout backward_layout(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t d
     L.off_dT = take(cc);
     L.off_X1 = take(cc);
     L.off_Bd = take(cc);
+    L.off_Wf = take(cdk);
+    L.off_DKf = take(cdk);
+    L.off_Qf = take(cdk);
+    L.off_Ef = take(cdv);
+    L.off_Wr = take(cdk);
+    L.off_DKr = take(cdk);
     L.total = off;
     return L;
 }

@@ -156,6 +156,78 @@ __device__ Slices slices(const BwdArgs& a, int64_t b)
     return s;
 }
 
+// B-operand fragments of a row-major fp32 [BC][d] matrix X for a product
+// contracting over the chunk rows, on the bf16 matrix cores with hi/lo
+// splits: fragment (ct, ks) gives lane (l16, g) the elements
+// X[32 ks + 8 g + e][16 ct + l16], e = 0..7, as bf16 hi and lo parts at
+// out + (((ct * 2 + ks) * 2 + part) * 64 + lane) * 8.
+__device__ void col_frags(const float* __restrict__ X, int d, uint16_t* __restrict__ out)
+{
+    for (int task = threadIdx.x; task < (d / 16) * 128; task += 256) {
+        const int lane = task & 63, ks = (task >> 6) & 1, ct = task >> 7;
+        const int l16 = lane & 15, g = lane >> 4;
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = X[(32 * ks + 8 * g + e) * d + 16 * ct + l16];
+        uint32_t hi[4], lo[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) split_bf16x2(x[2 * w], x[2 * w + 1], hi[w], lo[w]);
+        uint16_t* p = out + ((size_t)((ct * 2 + ks) * 2) * 64 + lane) * 8;
+        *reinterpret_cast<u32x4*>(p) = u32x4{hi[0], hi[1], hi[2], hi[3]};
+        *reinterpret_cast<u32x4*>(p + 512) = u32x4{lo[0], lo[1], lo[2], lo[3]};
+    }
+}
+
+// Operand fragments of a row-major fp32 [BC][d] matrix X for a product
+// contracting over its columns: fragment (rt, ks) gives lane (l16, g) the
+// elements X[16 rt + l16][32 ks + 8 g + e], e = 0..7, as bf16 hi and lo parts
+// at out + (((rt * (d / 32) + ks) * 2 + part) * 64 + lane) * 8.
+__device__ void row_frags(const float* __restrict__ X, int d, uint16_t* __restrict__ out)
+{
+    const int ksn = d / 32;
+    for (int task = threadIdx.x; task < (BC / 16) * ksn * 64; task += 256) {
+        const int lane = task & 63, ks = (task >> 6) % ksn, rt = (task >> 6) / ksn;
+        const int l16 = lane & 15, g = lane >> 4;
+        const float* src = X + (16 * rt + l16) * d + 32 * ks + 8 * g;
+        const f32x4 a = *reinterpret_cast<const f32x4*>(src), b = *reinterpret_cast<const f32x4*>(src + 4);
+        uint32_t hi[4], lo[4];
+        split_bf16x2(a.x, a.y, hi[0], lo[0]);
+        split_bf16x2(a.z, a.w, hi[1], lo[1]);
+        split_bf16x2(b.x, b.y, hi[2], lo[2]);
+        split_bf16x2(b.z, b.w, hi[3], lo[3]);
+        uint16_t* p = out + ((size_t)((rt * ksn + ks) * 2) * 64 + lane) * 8;
+        *reinterpret_cast<u32x4*>(p) = u32x4{hi[0], hi[1], hi[2], hi[3]};
+        *reinterpret_cast<u32x4*>(p + 512) = u32x4{lo[0], lo[1], lo[2], lo[3]};
+    }
+}
+
+__device__ __forceinline__ f32x4 mma_bf16(u32x4 a, u32x4 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0,
+                                                   0);
+}
+
+// A B with both operands split into bf16 hi + lo: A_hi B_hi + A_lo B_hi + A_hi B_lo
+// (the dropped A_lo B_lo is below 2^-16 of the product)
+__device__ __forceinline__ f32x4 mma3(u32x4 ah, u32x4 al, u32x4 bh, u32x4 bl, f32x4 c)
+{
+    c = mma_bf16(ah, bh, c);
+    c = mma_bf16(al, bh, c);
+    return mma_bf16(ah, bl, c);
+}
+
+// eight fp32 values -> bf16 hi and lo operand fragments
+__device__ __forceinline__ void split8(f32x4 a, f32x4 b, u32x4& hi, u32x4& lo)
+{
+    uint32_t h[4], l[4];
+    split_bf16x2(a.x, a.y, h[0], l[0]);
+    split_bf16x2(a.z, a.w, h[1], l[1]);
+    split_bf16x2(b.x, b.y, h[2], l[2]);
+    split_bf16x2(b.z, b.w, h[3], l[3]);
+    hi = u32x4{h[0], h[1], h[2], h[3]};
+    lo = u32x4{l[0], l[1], l[2], l[3]};
+}
+
 // Chunk table: header[0] = 1 if cu_seqlens is invalid (then no chunk is
 // processed), header[1] = number of chunks; tab[c] = {first token, length,
 // sequence, 0}; seq_first[n] = first chunk of sequence n.
@@ -342,27 +414,39 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a)
                 s.dDl[r * dv + n] = a.scale * acc2[i][j];
             }
     }
+    // the chains' operands contracted over the chunk rows, as bf16 hi/lo fragments
+    __syncthreads();
+    const int64_t fper = (int64_t)BC * dk * 2;
+    col_frags(s.W, dk, reinterpret_cast<uint16_t*>(a.ws + a.lay.off_Wf) + b * fper);
+    col_frags(s.DK, dk, reinterpret_cast<uint16_t*>(a.ws + a.lay.off_DKf) + b * fper);
+    col_frags(s.Q, dk, reinterpret_cast<uint16_t*>(a.ws + a.lay.off_Qf) + b * fper);
+    col_frags(s.E, dv, reinterpret_cast<uint16_t*>(a.ws + a.lay.off_Ef) + b * (int64_t)BC * dv * 2);
+    row_frags(s.W, dk, reinterpret_cast<uint16_t*>(a.ws + a.lay.off_Wr) + b * fper);
+    row_frags(s.DK, dk, reinterpret_cast<uint16_t*>(a.ws + a.lay.off_DKr) + b * fper);
 }
 
 // One row-split recurrence over the chunks of each sequence (see the header):
 //     Delta = X + ysign Y S^T                 (C x 16 rows of this workgroup)
 //     S    <- e^{gamma_L} S + zsign Delta^T Z + E^T F
 // storing S before each chunk (S_store) and Delta (D_store).  A workgroup owns
-// 16 rows of one (sequence, head) state.  Both products run on the fp32
-// matrix cores (v_mfma_f32_16x16x4_f32: exact fp32 products, fp32 sums):
-//   - S Y^T (16 x 64, K = DK): wave w computes the 16 chunk rows 16w..16w+15;
-//     A = S (from LDS), B = Y^T (from LDS);
+// 16 rows of one (sequence, head) state; its four waves run both products on
+// the bf16 matrix cores with hi/lo splits of both operands (three products
+// per fragment pair, relative error ~2^-16, the fp32 path's level):
+//   - S Y^T (16 x 64, K = DK): wave w computes chunk rows 16 w .. 16 w + 15,
+//     A = S (the state rows from LDS), B = Y^T (its 16 rows of Y, registers);
 //   - Delta^T Z + E^T F (16 x DK, K = 64): wave w owns the DK/4 state columns
-//     w DK/4 .. and keeps them in registers in the accumulator layout
-//     (lane l: rows 4 (l / 16) + i, column l % 16 of each 16-column tile);
-//     A = Delta^T (from LDS) and E^T (registers), B = Z and F (from LDS).
-// Operands pass through registers into two LDS buffers (row pitch DK + 4):
-// each thread loads its share of a whole 64 x DK operand at once, and the
-// next operand is in flight during the arithmetic on the current one.
+//     w DK/4 .. in registers in the accumulator layout (lane l: rows
+//     4 (l / 16) + i, column l % 16 of each 16-column tile); A = Delta^T (from
+//     LDS) and E^T (registers), B = Z and F as the local kernel's column
+//     fragments (registers).
+// Every wave loads only its quarter of each operand, straight into registers,
+// right after its last use: the next chunk's Y during the update, the next Z
+// and F during the following products.  Two barriers per chunk (the state
+// rows and Delta cross the waves through LDS).
 // The operands of one direction of the chain (workspace byte offsets; E and
-// F absent when their offset is 0).
+// F absent when their offset is 0; Zf and Ff are fragment arrays).
 struct ChainOps {
-    size_t off_X, off_Y, off_Z, off_E, off_F, off_Sst, off_Dst;
+    size_t off_X, off_Yr, off_Zf, off_Ef, off_Ff, off_Sst, off_Dst;
     const float* S_init;  // [N][H][dv][dk] or NULL (zeros)
     float* S_final;       // [N][H][dv][dk] or NULL
     float ysign, zsign;
@@ -370,64 +454,120 @@ struct ChainOps {
 };
 
 // The forward and the reverse recurrence need nothing from each other (only
-// the gradient kernel reads both), so one launch runs them side by side: the
-// first half of the grid is the reverse chain (the longer one), the second
-// half the forward chain.
+// the gradient kernel reads both), so one launch runs them side by side.
+// Workgroup -> (direction and pair, row block): the dv/16 row blocks of one
+// (direction, sequence, head) sit 8 workgroups apart, so they share one XCD
+// and its L2 copy of the chunk operands (the reverse chains first).
 template <int DK>
 __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs a, ChainOps rev_ops, ChainOps fwd_ops)
 {
-    constexpr int PER = BC * DK / 4 / 256;  // float4 of one operand per thread
-    constexpr int P = DK + 4;               // LDS row pitch (floats)
-    constexpr int NT = DK / 64;             // 16-column tiles per wave
+    constexpr int P = DK + 4;   // LDS pitch of the state rows (floats)
+    constexpr int DP = BC + 4;  // LDS pitch of Delta^T
+    constexpr int NT = DK / 64;  // 16-column state tiles per wave
+    constexpr int DKS = DK / 32;  // k-steps over d_k
+    static_assert(BC == 64, "two k-steps over the chunk");
     const int dv = a.dv, H = a.H;
-    const int rblocks = dv / 16;
-    const int64_t half = (int64_t)a.N * H * rblocks;
-    const bool is_rev = blockIdx.x < half;
+    const int RB = dv / 16;
+    const int64_t NP = (int64_t)a.N * H;
+    const int xcd = (int)(blockIdx.x & 7);
+    const int64_t slot = blockIdx.x >> 3;
+    const int64_t sidx = xcd + 8 * (slot / RB);
+    const int rb = (int)(slot % RB);
+    if (sidx >= 2 * NP) return;
+    const bool is_rev = sidx < NP;
     const ChainOps op = is_rev ? rev_ops : fwd_ops;
-    const int64_t bid = is_rev ? (int64_t)blockIdx.x : (int64_t)blockIdx.x - half;
+    const int64_t pair = is_rev ? sidx : sidx - NP;
     const float ysign = op.ysign, zsign = op.zsign;
     const float* __restrict__ S_init = op.S_init;
     float* __restrict__ S_final = op.S_final;
     const int reverse = op.reverse;
-    const int64_t pair = bid / rblocks;
-    const int rb = (int)(bid % rblocks);
     const int n = (int)(pair / H), h = (int)(pair % H);
-    const int t = threadIdx.x, w = t >> 6, l = t & 63, r16 = l & 15, g = l >> 4;
+    const int t = threadIdx.x, w = t >> 6, lane = t & 63, l16 = lane & 15, g = lane >> 4;
     const int32_t* seq_first = reinterpret_cast<const int32_t*>(a.ws + a.lay.off_seq_first);
     const float* gamv = reinterpret_cast<const float*>(a.ws + a.lay.off_gam);
     auto wsf = [&](size_t off) { return reinterpret_cast<float*>(a.ws + off); };
     const float* Xb = wsf(op.off_X);
-    const float* Yb = wsf(op.off_Y);
-    const float* Zb = wsf(op.off_Z);
-    const float* Eb = op.off_E ? wsf(op.off_E) : nullptr;
-    const float* Fb = op.off_F ? wsf(op.off_F) : nullptr;
+    const uint16_t* Yr = reinterpret_cast<const uint16_t*>(a.ws + op.off_Yr);
+    const uint16_t* Zf = reinterpret_cast<const uint16_t*>(a.ws + op.off_Zf);
+    const uint16_t* Ef = op.off_Ef ? reinterpret_cast<const uint16_t*>(a.ws + op.off_Ef) : nullptr;
+    const uint16_t* Ff = op.off_Ff ? reinterpret_cast<const uint16_t*>(a.ws + op.off_Ff) : nullptr;
+    const bool hasF = Ff != nullptr;
     float* Sst = wsf(op.off_Sst);
     float* Dst = wsf(op.off_Dst);
-    __shared__ __align__(16) float bufA[BC * P], bufB[BC * P];
-    __shared__ float Ssh[16 * P];
-    __shared__ float dsm[BC * 17];
+    constexpr int PB = DK + 8;  // LDS pitch of the bf16 state rows (elements)
+    __shared__ __align__(16) float Ssh[16 * P];   // state rows before the chunk
+    __shared__ __align__(16) uint16_t Sbh[16 * PB], Sbl[16 * PB];  // the same rows, bf16 hi and lo
+    __shared__ __align__(16) float dsm[16 * DP];  // Delta^T [state row][chunk row]
 
-    f32x4 reg[PER];
-    auto fetch = [&](const float* base, int64_t chx) {
-        const f32x4* p4 = reinterpret_cast<const f32x4*>(base + chx * BC * DK);
+    // this wave's operand quarters, one chunk ahead
+    u32x4 yr[DKS][2];     // Y fragments of chunk rows 16 w .., k-step ks, hi / lo
+    u32x4 zr[NT][2][2];   // Z fragments of column tiles w NT + tt, k-step ks, hi / lo
+    u32x4 fr[NT][2][2];   // F fragments, likewise
+    u32x4 er[2][2];       // E^T fragments of this row block, k-step ks, hi / lo
+    f32x4 xr;             // X[16 w + l16][16 rb + 4 g .. + 3]
+    float gl = 0.f;
+    const int64_t fper = (int64_t)BC * DK * 2;
+    auto load_y = [&](int64_t ch) {
+        const uint16_t* p = Yr + ch * fper + lane * 8;
 #pragma unroll
-        for (int i = 0; i < PER; ++i) reg[i] = p4[t + 256 * i];
+        for (int ks = 0; ks < DKS; ++ks)
+#pragma unroll
+            for (int part = 0; part < 2; ++part)
+                yr[ks][part] = *reinterpret_cast<const u32x4*>(p + ((w * DKS + ks) * 2 + part) * 512);
+        xr = *reinterpret_cast<const f32x4*>(Xb + (ch * BC + 16 * w + l16) * dv + rb * 16 + 4 * g);
+        gl = gamv[ch * BC + BC - 1];
     };
-    auto put = [&](float* dst) {
+    auto load_z = [&](int64_t ch) {
+        const uint16_t* p = Zf + ch * fper + lane * 8;
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int e = t + 256 * i;
-            *reinterpret_cast<f32x4*>(dst + (e / (DK / 4)) * P + 4 * (e % (DK / 4))) = reg[i];
+        for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int part = 0; part < 2; ++part)
+                    zr[tt][ks][part] = *reinterpret_cast<const u32x4*>(p + (((w * NT + tt) * 2 + ks) * 2 + part) * 512);
+    };
+    auto load_f = [&](int64_t ch) {
+        const uint16_t* p = Ff + ch * fper + lane * 8;
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int part = 0; part < 2; ++part)
+                    fr[tt][ks][part] = *reinterpret_cast<const u32x4*>(p + (((w * NT + tt) * 2 + ks) * 2 + part) * 512);
+        const uint16_t* pe = Ef + ch * (int64_t)BC * dv * 2 + lane * 8;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int part = 0; part < 2; ++part)
+                er[ks][part] = *reinterpret_cast<const u32x4*>(pe + ((rb * 2 + ks) * 2 + part) * 512);
+    };
+
+    // L2 prefetch two chunks ahead: the operands the chain reads for one chunk
+    // (Y, Z, E and F, 64 x DK / dv each), cut into 1 KB pieces, this
+    // workgroup's share of the pair's pieces, one 16-byte load per lane; the
+    // loaded words are folded into a register two chunks later (kept alive
+    // to the end), so no wait is added before they arrive
+    constexpr int OPB = BC * DK * 4 / 1024;  // 1 KB pieces of one d_k operand
+    const int eb = BC * dv * 4 / 1024;       // of E
+    const int npiece = 2 * OPB + (hasF ? OPB + eb : 0);
+    const int per_wg = (npiece + RB - 1) / RB, per_wave = (per_wg + 3) / 4;
+    uint32_t pf_acc = 0;
+    u32x4 pf[2][4];
+    auto prefetch = [&](int64_t ch, u32x4* dst) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int q = rb * per_wg + w * per_wave + i;
+            const unsigned char* src = nullptr;
+            if (i < per_wave && q < npiece && (w * per_wave + i) < per_wg) {
+                if (q < OPB) src = reinterpret_cast<const unsigned char*>(Yr + ch * fper) + q * 1024;
+                else if (q < 2 * OPB) src = reinterpret_cast<const unsigned char*>(Zf + ch * fper) + (q - OPB) * 1024;
+                else if (q < 3 * OPB) src = reinterpret_cast<const unsigned char*>(Ff + ch * fper) + (q - 2 * OPB) * 1024;
+                else src = reinterpret_cast<const unsigned char*>(Ef + ch * (int64_t)BC * dv * 2) + (q - 3 * OPB) * 1024;
+            }
+            dst[i] = src ? *reinterpret_cast<const u32x4*>(src + lane * 16) : u32x4{0u, 0u, 0u, 0u};
         }
-    };
-    // the chunk's X at this lane's Delta positions, E at its A-operand positions, and the decay
-    float xr[4], er[16], gl = 0.f;
-    auto fetch_small = [&](int64_t chx) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) xr[i] = Xb[(chx * BC + 16 * w + r16) * dv + rb * 16 + 4 * g + i];
-#pragma unroll
-        for (int s4 = 0; s4 < 16; ++s4) er[s4] = Eb ? Eb[(chx * BC + 4 * s4 + g) * dv + rb * 16 + r16] : 0.f;
-        gl = gamv[chx * BC + BC - 1];
     };
 
     // this wave's state columns, accumulator layout
@@ -437,85 +577,87 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs a, ChainOps rev_
     for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            sreg[tt][i] = S_init ? S_init[(sbase + 4 * g + i) * DK + w * (DK / 4) + 16 * tt + r16] : 0.f;
+            sreg[tt][i] = S_init ? S_init[(sbase + 4 * g + i) * DK + w * (DK / 4) + 16 * tt + l16] : 0.f;
     const int c0 = seq_first[n], c1 = seq_first[n + 1];
     const int steps = c1 - c0;
     auto chunk_of = [&](int it) -> int64_t { return (int64_t)(reverse ? c1 - 1 - it : c0 + it) * H + h; };
     if (steps > 0) {
-        fetch(Yb, chunk_of(0));
-        fetch_small(chunk_of(0));
+        load_y(chunk_of(0));
+        load_z(chunk_of(0));
+        if (hasF) load_f(chunk_of(0));
     }
     for (int it = 0; it < steps; ++it) {
         const int64_t ch = chunk_of(it);
-        const float decay = expf(gl);
-        float xc[4];
+        {
+            u32x4* slot = pf[it & 1];
+            if (it >= 2)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) xc[i] = xr[i];
-        float ec[16];
+                for (int i = 0; i < 4; ++i) pf_acc ^= slot[i].x ^ slot[i].w;
+            if (it + 2 < steps) prefetch(chunk_of(it + 2), slot);
+            else
 #pragma unroll
-        for (int s4 = 0; s4 < 16; ++s4) ec[s4] = er[s4];
-        // the state before the chunk: to the record and to LDS (A operand of S Y^T)
+                for (int i = 0; i < 4; ++i) slot[i] = u32x4{0u, 0u, 0u, 0u};
+        }
+        // the state before the chunk: to LDS in fp32 (for the record) and split
+        // into bf16 hi and lo (the A operand of S Y^T), then from its rows to the
+        // record, 16 bytes per lane
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int row = 4 * g + i, col = w * (DK / 4) + 16 * tt + r16;
-                Sst[(ch * dv + rb * 16 + row) * DK + col] = sreg[tt][i];
-                Ssh[row * P + col] = sreg[tt][i];
+                const int at = (4 * g + i), col = w * (DK / 4) + 16 * tt + l16;
+                const float x = sreg[tt][i];
+                const uint16_t hb = __builtin_bit_cast(uint16_t, (__bf16)x);
+                const float hf = __uint_as_float((uint32_t)hb << 16);
+                Ssh[at * P + col] = x;
+                Sbh[at * PB + col] = hb;
+                Sbl[at * PB + col] = __builtin_bit_cast(uint16_t, (__bf16)(x - hf));
             }
-        __syncthreads();  // Ssh written; the previous step's readers of bufA, bufB, dsm are done
-        put(bufA);        // Y
-        fetch(Zb, ch);
-        __syncthreads();
-        // (S Y^T)[row][16 w + n]: A(m, k) = S[m][k], B(k, n) = Y[16 w + n][k]
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-        for (int s4 = 0; s4 < DK / 4; ++s4)
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(Ssh[r16 * P + 4 * s4 + g], bufA[(16 * w + r16) * P + 4 * s4 + g],
-                                                       acc, 0, 0, 0);
-        // lane holds rows 4 g + i of chunk row 16 w + r16
+        __syncthreads();  // ---- the state rows in LDS; the previous chunk's Delta readers are done
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dsm[(16 * w + r16) * 17 + 4 * g + i] = xc[i] + ysign * acc[i];
-        put(bufB);  // Z
-        if (Fb) {
-            fetch(Fb, ch);
-        } else if (it + 1 < steps) {
-            fetch(Yb, chunk_of(it + 1));
-            fetch_small(chunk_of(it + 1));
+        for (int i = 0; i < 16 * DK / 4 / 256; ++i) {
+            const int u = t + 256 * i, row = u / (DK / 4), c4 = u % (DK / 4);
+            *reinterpret_cast<f32x4*>(Sst + (ch * dv + rb * 16 + row) * DK + 4 * c4) =
+                *reinterpret_cast<const f32x4*>(Ssh + row * P + 4 * c4);
         }
-        __syncthreads();  // dsm and bufB complete; bufA (Y) and Ssh no longer read
-        for (int e = t; e < BC * 16; e += 256) {
-            const int cc = e >> 4, rr = e & 15;
-            Dst[(ch * BC + cc) * dv + rb * 16 + rr] = dsm[cc * 17 + rr];
+        // (S Y^T)[state row][chunk row 16 w + l16], the three hi/lo products in
+        // three accumulators
+        f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0;
+#pragma unroll
+        for (int ks = 0; ks < DKS; ++ks) {
+            const u32x4 sh = *reinterpret_cast<const u32x4*>(Sbh + l16 * PB + 32 * ks + 8 * g);
+            const u32x4 sl = *reinterpret_cast<const u32x4*>(Sbl + l16 * PB + 32 * ks + 8 * g);
+            a0 = mma_bf16(sh, yr[ks][0], a0);
+            a1 = mma_bf16(sl, yr[ks][0], a1);
+            a2 = mma_bf16(sh, yr[ks][1], a2);
         }
-        // S <- decay S + zsign Delta^T Z: A(m, k) = Delta[k][m], B(k, n) = Z[k][col n]
+        const f32x4 acc = a0 + a1 + a2;
+        // lane holds state rows 4 g + i of chunk row 16 w + l16
+        const f32x4 d = xr + ysign * acc;
 #pragma unroll
-        for (int tt = 0; tt < NT; ++tt) {
-            f32x4 sacc = sreg[tt] * decay;
-            const int col = w * (DK / 4) + 16 * tt + r16;
+        for (int i = 0; i < 4; ++i) dsm[(4 * g + i) * DP + 16 * w + l16] = d[i];
+        *reinterpret_cast<f32x4*>(Dst + (ch * BC + 16 * w + l16) * dv + rb * 16 + 4 * g) = d;
+        const float decay = expf(gl);
+        if (it + 1 < steps) load_y(chunk_of(it + 1));
+        __syncthreads();  // ---- Delta^T in LDS; the state rows read
+        // S <- e^{gamma_L} S + zsign Delta^T Z (+ E^T F)
 #pragma unroll
-            for (int s4 = 0; s4 < 16; ++s4)
-                sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(zsign * dsm[(4 * s4 + g) * 17 + r16],
-                                                            bufB[(4 * s4 + g) * P + col], sacc, 0, 0, 0);
-            sreg[tt] = sacc;
+        for (int tt = 0; tt < NT; ++tt) sreg[tt] *= decay;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const float* dp = dsm + l16 * DP + 32 * ks + 8 * g;
+            u32x4 dh, dl;
+            split8(zsign * *reinterpret_cast<const f32x4*>(dp), zsign * *reinterpret_cast<const f32x4*>(dp + 4), dh, dl);
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) sreg[tt] = mma3(dh, dl, zr[tt][ks][0], zr[tt][ks][1], sreg[tt]);
         }
-        if (Fb) {
-            put(bufA);  // F
-            if (it + 1 < steps) {
-                fetch(Yb, chunk_of(it + 1));
-                fetch_small(chunk_of(it + 1));
-            }
-            __syncthreads();
-            // S += E^T F: A(m, k) = E[k][m], B(k, n) = F[k][col n]
+        if (it + 1 < steps) load_z(chunk_of(it + 1));
+        if (hasF) {
 #pragma unroll
-            for (int tt = 0; tt < NT; ++tt) {
-                f32x4 sacc = sreg[tt];
-                const int col = w * (DK / 4) + 16 * tt + r16;
+            for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-                for (int s4 = 0; s4 < 16; ++s4)
-                    sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(ec[s4], bufA[(4 * s4 + g) * P + col], sacc, 0, 0, 0);
-                sreg[tt] = sacc;
-            }
+                for (int tt = 0; tt < NT; ++tt) sreg[tt] = mma3(er[ks][0], er[ks][1], fr[tt][ks][0], fr[tt][ks][1], sreg[tt]);
+            if (it + 1 < steps) load_f(chunk_of(it + 1));
         }
     }
     if (S_final)
@@ -523,7 +665,12 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs a, ChainOps rev_
         for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                S_final[(sbase + 4 * g + i) * DK + w * (DK / 4) + 16 * tt + r16] = sreg[tt][i];
+                S_final[(sbase + 4 * g + i) * DK + w * (DK / 4) + 16 * tt + l16] = sreg[tt][i];
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pf_acc ^= pf[b2][i].x ^ pf[b2][i].w;
+    asm volatile("" ::"v"(pf_acc));  // the prefetched words stay live: the loads are kept
 }
 
 __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a)
@@ -844,7 +991,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a)
 template <int DK>
 hipError_t launch_chain(const BwdArgs& a, const ChainOps& rev, const ChainOps& fwd)
 {
-    const int64_t blocks = 2 * (int64_t)a.N * a.H * (a.dv / 16);
+    const int64_t blocks = (2 * (int64_t)a.N * a.H + 7) / 8 * 8 * (a.dv / 16);
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((bwd_chain_kernel<DK>), dim3((uint32_t)blocks), dim3(256), 0, a.stream, a, rev, fwd);
     return hipGetLastError();
@@ -880,13 +1027,13 @@ hipError_t launch_backward(const BwdArgs& a)
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // forward: Delta = U - W S^T,  S <- e^{gamma_L} S + Delta^T (D K); records S and Delta
     ChainOps fwd;
-    fwd.off_X = L.off_U; fwd.off_Y = L.off_W; fwd.off_Z = L.off_DK; fwd.off_E = 0; fwd.off_F = 0;
+    fwd.off_X = L.off_U; fwd.off_Yr = L.off_Wr; fwd.off_Zf = L.off_DKf; fwd.off_Ef = 0; fwd.off_Ff = 0;
     fwd.off_Sst = L.off_S; fwd.off_Dst = L.off_Dl;
     fwd.S_init = a.init_state; fwd.S_final = nullptr;
     fwd.ysign = -1.f; fwd.zsign = 1.f; fwd.reverse = 0;
     // reverse: dDelta = dDelta_local + (D K) dS^T,  dS <- e^{gamma_L} dS - dDelta^T W + E^T Q
     ChainOps rev;
-    rev.off_X = L.off_dDl; rev.off_Y = L.off_DK; rev.off_Z = L.off_W; rev.off_E = L.off_E; rev.off_F = L.off_Q;
+    rev.off_X = L.off_dDl; rev.off_Yr = L.off_DKr; rev.off_Zf = L.off_Wf; rev.off_Ef = L.off_Ef; rev.off_Ff = L.off_Qf;
     rev.off_Sst = L.off_dS; rev.off_Dst = L.off_dD;
     rev.S_init = a.dstate; rev.S_final = a.dinit;
     rev.ysign = 1.f; rev.zsign = -1.f; rev.reverse = 1;

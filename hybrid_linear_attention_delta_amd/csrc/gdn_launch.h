@@ -144,6 +144,8 @@ struct BwdLayout {
     size_t off_T, off_P, off_KKG, off_W, off_U, off_DK, off_E, off_dDl;
     size_t off_S, off_Dl, off_dS, off_dD;
     size_t off_dQ, off_dK, off_dW, off_dPG, off_dT, off_X1, off_Bd;
+    size_t off_Wf, off_DKf, off_Qf, off_Ef;  // W, D K, Q, E as bf16 hi/lo fragments over the chunk rows (state chains)
+    size_t off_Wr, off_DKr;                  // W, D K as bf16 hi/lo fragments over d_k (state chains)
     size_t total;
 };
 
