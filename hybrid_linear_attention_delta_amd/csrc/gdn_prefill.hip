@@ -1690,8 +1690,9 @@ struct ChainKrLds {
 // `states` (before barrier A) and Delta of chunk c to `deltas` (after B); they
 // issue no transfer into LDS, so no read of theirs waits for one.  The
 // workgroup -> (pair, row tile) mapping and the segment logic are those of
-// chain_kernel.
-template <int DK, int DV, bool SEG>
+// chain_kernel.  PIPE: the one launch of the pipelined prefill, whose loaders
+// and store waves also take the hand-offs of PipeSync.
+template <int DK, int DV, bool SEG, bool PIPE>
 __global__ __launch_bounds__(1024) void chain_kr_kernel(
     const int32_t* __restrict__ header, const int32_t* __restrict__ seq_first,
     const int32_t* __restrict__ seq_order, int32_t varlen, int64_t T, int32_t H, int32_t pairs,
@@ -1733,7 +1734,8 @@ __global__ __launch_bounds__(1024) void chain_kr_kernel(
 
     // this workgroup is done with every segment: nothing of it waits for it
     auto pipe_release_all = [&]() {
-        if (ps.flags && threadIdx.x == 0)
+        if constexpr (PIPE)
+            if (threadIdx.x == 0)
             for (int q = 0; q < ps.nseg; ++q)
                 __hip_atomic_fetch_add(ps.flags + kPipeMaxSeg + q, kPipePublishers, __ATOMIC_RELEASE,
                                        __HIP_MEMORY_SCOPE_AGENT);
@@ -1774,14 +1776,15 @@ __global__ __launch_bounds__(1024) void chain_kr_kernel(
         const int lw = wave - NW;
         if (lw < ND) {
             // transfers j0 .. j1-1 of this loader for chunk cc (transfer i = lw + ND j)
-            int64_t ready_below = ps.flags ? 0 : INT64_MAX;  // chunks below this are known to be prepared
+            int64_t ready_below = 0;  // (PIPE) chunks below this are known to be prepared
             int seg = 0;
             auto transfers = [&](int64_t cc, int j0, int j1) {
-                while (cc >= ready_below) {  // the first chunk of a later segment
-                    while (seg + 1 < ps.nseg && ps.end[seg] <= cc) ++seg;
-                    pipe_wait(ps.flags + seg, 1u, ps.flags + 2 * kPipeMaxSeg);
-                    ready_below = seg + 1 < ps.nseg ? ps.end[seg] : INT64_MAX;
-                }
+                if constexpr (PIPE)
+                    while (cc >= ready_below) {  // the first chunk of a later segment
+                        while (seg + 1 < ps.nseg && ps.end[seg] <= cc) ++seg;
+                        pipe_wait(ps.flags + seg, 1u, ps.flags + 2 * kPipeMaxSeg);
+                        ready_below = seg + 1 < ps.nseg ? ps.end[seg] : INT64_MAX;
+                    }
                 const unsigned char* rb = rec_ptr(cc);
                 const __amdgpu_buffer_rsrc_t r = make_rsrc(rb, (uint32_t)R::BYTES);
                 const __amdgpu_buffer_rsrc_t rv = make_rsrc(rb + R::KSC_BYTE_OFF, C * 4 + 16);  // lanes past: zeros
@@ -1861,8 +1864,8 @@ __global__ __launch_bounds__(1024) void chain_kr_kernel(
         // of: release the stores at agent scope, then count the wave in
         // (the segment index and the next segment end stay wave-uniform, so the
         // loop keeps its addresses and descriptors in scalar registers)
-        int sig = ps.flags ? 0 : ps.nseg;
-        int64_t next_end = sig < ps.nseg ? ps.end[0] : INT64_MAX;
+        int sig = 0;
+        int64_t next_end = PIPE && ps.nseg > 0 ? ps.end[0] : INT64_MAX;
         auto publish = [&](int64_t done_below) {
             int n = sig;
             while (n < ps.nseg && ps.end[n] <= done_below) ++n;
@@ -1875,18 +1878,19 @@ __global__ __launch_bounds__(1024) void chain_kr_kernel(
             sig = n;
             next_end = n < ps.nseg ? ps.end[n] : INT64_MAX;
         };
-        publish(c_begin);
+        if constexpr (PIPE) publish(c_begin);
         __syncthreads();
         for (int64_t c = c_begin; c < c_end; ++c) {
             store_state(c);  // before phase 3 rewrites the rows
             lds_barrier();  // ---- A
             lds_barrier();  // ---- B
             store_delta(c);  // before phase 2 of c+1 rewrites it
-            if (c + 1 >= next_end) publish(c + 1);
+            if constexpr (PIPE)
+                if (c + 1 >= next_end) publish(c + 1);
             lds_barrier();  // ---- C
         }
         wait_vmcnt<0>();
-        publish(INT64_MAX);
+        if constexpr (PIPE) publish(INT64_MAX);
         return;
     }
 
@@ -2410,17 +2414,24 @@ static hipError_t run_prefill(const PrefillArgs& a)
         const bool seg = !(c0 == 0 && c1 == ALL);
         if constexpr (sizeof(TIn) == 2) {
             using Lds = ChainKrLds<DK, DV>;
-            const void* fn = seg ? (const void*)chain_kr_kernel<DK, DV, true> : (const void*)chain_kr_kernel<DK, DV, false>;
+            const bool pipe_on = pipe.flags != nullptr;
+            const void* fn = seg ? (const void*)chain_kr_kernel<DK, DV, true, false>
+                                 : pipe_on ? (const void*)chain_kr_kernel<DK, DV, false, true>
+                                           : (const void*)chain_kr_kernel<DK, DV, false, false>;
             const hipError_t e = lds_limit(fn, sizeof(Lds));
             if (e != hipSuccess) return e;
             const dim3 grid((uint32_t)chain_blocks), block(1024);
             if (seg)
-                hipLaunchKernelGGL((chain_kr_kernel<DK, DV, true>), grid, block, sizeof(Lds), st, header, first, order,
-                                   varlen, a.T, a.H, (int32_t)pairs, records, a.lay.record_bytes, a.init_state,
+                hipLaunchKernelGGL((chain_kr_kernel<DK, DV, true, false>), grid, block, sizeof(Lds), st, header, first,
+                                   order, varlen, a.T, a.H, (int32_t)pairs, records, a.lay.record_bytes, a.init_state,
+                                   a.final_state, states, deltas, c0, c1, carry, slot0, pipe);
+            else if (pipe_on)
+                hipLaunchKernelGGL((chain_kr_kernel<DK, DV, false, true>), grid, block, sizeof(Lds), st, header, first,
+                                   order, varlen, a.T, a.H, (int32_t)pairs, records, a.lay.record_bytes, a.init_state,
                                    a.final_state, states, deltas, c0, c1, carry, slot0, pipe);
             else
-                hipLaunchKernelGGL((chain_kr_kernel<DK, DV, false>), grid, block, sizeof(Lds), st, header, first, order,
-                                   varlen, a.T, a.H, (int32_t)pairs, records, a.lay.record_bytes, a.init_state,
+                hipLaunchKernelGGL((chain_kr_kernel<DK, DV, false, false>), grid, block, sizeof(Lds), st, header, first,
+                                   order, varlen, a.T, a.H, (int32_t)pairs, records, a.lay.record_bytes, a.init_state,
                                    a.final_state, states, deltas, c0, c1, carry, slot0, pipe);
             return hipGetLastError();
         } else {

@@ -145,12 +145,15 @@ def render_trace():
 
 def full_launch(name, grid, groups):
     """True for the dispatch group that covers the whole workload: the
-    non-segmented chain instance; for the decode kernel the d_v = 256 batch
+    chain instance launched once over all chunks on its own (the stage-by-stage
+    run, as timed for the roofline); for the decode kernel the d_v = 256 batch
     (the smaller of its two grids: the bench also times a d_v = 512 batch);
     else the largest grid of the kernel."""
     if kernel_key(name).startswith("bwd_"):
         return True  # the backward has no segmented launches
-    if kernel_key(name) in ("chain_kr_kernel", "chain_kernel"):
+    if kernel_key(name) == "chain_kr_kernel":
+        return ", false, false>" in name  # neither a window/segment launch nor the pipelined one
+    if kernel_key(name) == "chain_kernel":
         return ", false>" in name
     grids = [g for (nm, g) in groups if kernel_key(nm) == kernel_key(name)]
     if kernel_key(name) == "decode_kernel":
