@@ -52,44 +52,79 @@ constexpr int KTG = 32;  // and in the gradient kernel
 
 // acc[i][j] += sum_k A(r, k) B(k, n) for r = 4 tr + i in [0, 64), n = n0 + 16 j + tc
 // (tr = threadIdx / 16, tc = threadIdx % 16), with
-// A(r, k) = A[r * ars + k * acs] * (kscale ? kscale[k] : 1) and
-// B(k, n) = B[k * brs + n * bcs]; K a multiple of the k block KT, [n0, n0 + 64)
-// inside B.  All 256 threads take part (two barriers per KT-wide k block; as
-// and bs hold KT x LD floats each).  A wider block keeps more loads in flight
-// but needs more registers: 32 measured best for the gradient kernel, 16 for
-// the local one (64 left one workgroup per CU and was slower in both).  The products
-// run on the fp32 matrix cores (v_mfma_f32_16x16x4_f32, exact fp32 products
-// and fp32 sums): wave w computes rows 16 w .. 16 w + 15 as four 16 x 16
-// tiles, and its accumulator layout (lane l: rows 4 (l / 16) + i, column
-// l % 16 of each tile) is the (r, n) map above.
-template <int KT>
-__device__ void mm64(float acc[4][4], const float* __restrict__ A, int ars, int acs, const float* kscale,
-                     const float* __restrict__ B, int brs, int bcs, int K, int n0, float* as, float* bs)
+//   A(r, k) = A[r * lda + k] (AK: rows along k) or A[r + k * lda] (else),
+//             times kscale[k] if kscale is given;
+//   B(k, n) = B[k * ldb + n] (BN: rows along n) or B[k + n * ldb] (else);
+// K a multiple of the k block KT, [n0, n0 + 64) inside B, every operand row
+// and n0 a multiple of four floats from a 16-byte aligned base.  All 256 threads
+// take part: each k block arrives by 16-byte loads (KT / 16 per operand and
+// thread, all in flight together, issued while the previous block's products
+// run) into LDS, k-major with row pitch LD (as and bs hold KT x LD floats
+// each), two barriers per block.  The products run on
+// the fp32 matrix cores (v_mfma_f32_16x16x4_f32, exact fp32 products and fp32
+// sums): wave w computes rows 16 w .. 16 w + 15 as four 16 x 16 tiles, and its
+// accumulator layout (lane l: rows 4 (l / 16) + i, column l % 16 of each tile)
+// is the (r, n) map above.
+template <int KT, bool AK, bool BN>
+__device__ void mm64(float acc[4][4], const float* __restrict__ A, int lda, const float* kscale,
+                     const float* __restrict__ B, int ldb, int K, int n0, float* as, float* bs)
 {
-    const int t = threadIdx.x;
+    static_assert(KT % 16 == 0, "a k block is a whole number of 16-byte loads per thread");
+    constexpr int NV = KT / 16;  // 16-byte loads per operand and thread
+    int t = threadIdx.x;
+    asm volatile("" : "+v"(t));  // per-call lane offsets: recomputed here, not hoisted and held across calls
     const int w = t >> 6, l = t & 63, r16 = l & 15, g = l >> 4;
     f32x4 d[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) d[j] = f32x4{acc[0][j], acc[1][j], acc[2][j], acc[3][j]};
-    for (int k0 = 0; k0 < K; k0 += KT) {
-        // the 64 x KT block of A and the KT x 64 block of B: all loads in flight, then to LDS
-        float xa[KT / 4], xb[KT / 4];
+    f32x4 xa[NV], xb[NV];
+    auto fetch = [&](int k0) {  // the 64 x KT block of A and the KT x 64 block of B into registers
 #pragma unroll
-        for (int i = 0; i < KT / 4; ++i) {
+        for (int i = 0; i < NV; ++i) {
             const int e = t + 256 * i;
-            const int r = e / KT, kk = e % KT;
-            xa[i] = A[(int64_t)r * ars + (int64_t)(k0 + kk) * acs];
-            if (kscale) xa[i] *= kscale[k0 + kk];
-            const int kb = e >> 6, n = e & 63;
-            xb[i] = B[(int64_t)(k0 + kb) * brs + (int64_t)(n0 + n) * bcs];
+            if constexpr (AK) {  // KT / 4 lanes read one row's k block
+                const int r = e / (KT / 4), kq = e % (KT / 4);
+                xa[i] = *reinterpret_cast<const f32x4*>(A + (int64_t)r * lda + k0 + 4 * kq);
+                if (kscale) {
+                    const f32x4 s4 = *reinterpret_cast<const f32x4*>(kscale + k0 + 4 * kq);
+                    xa[i] *= s4;
+                }
+            } else {  // sixteen lanes read one k row of 64
+                const int kk = e >> 4, rq = e & 15;
+                xa[i] = *reinterpret_cast<const f32x4*>(A + (int64_t)(k0 + kk) * lda + 4 * rq);
+                if (kscale) xa[i] *= kscale[k0 + kk];
+            }
+            if constexpr (BN) {
+                const int kk = e >> 4, nq = e & 15;
+                xb[i] = *reinterpret_cast<const f32x4*>(B + (int64_t)(k0 + kk) * ldb + n0 + 4 * nq);
+            } else {
+                const int n = e / (KT / 4), kq = e % (KT / 4);
+                xb[i] = *reinterpret_cast<const f32x4*>(B + (int64_t)(n0 + n) * ldb + k0 + 4 * kq);
+            }
         }
+    };
+    fetch(0);
+    for (int k0 = 0; k0 < K; k0 += KT) {
 #pragma unroll
-        for (int i = 0; i < KT / 4; ++i) {
+        for (int i = 0; i < NV; ++i) {
             const int e = t + 256 * i;
-            as[(e % KT) * LD + e / KT] = xa[i];
-            bs[(e >> 6) * LD + (e & 63)] = xb[i];
+            if constexpr (AK) {
+                const int r = e / (KT / 4), kq = e % (KT / 4);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) as[(4 * kq + q) * LD + r] = xa[i][q];
+            } else {
+                *reinterpret_cast<f32x4*>(as + (e >> 4) * LD + 4 * (e & 15)) = xa[i];
+            }
+            if constexpr (BN) {
+                *reinterpret_cast<f32x4*>(bs + (e >> 4) * LD + 4 * (e & 15)) = xb[i];
+            } else {
+                const int n = e / (KT / 4), kq = e % (KT / 4);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) bs[(4 * kq + q) * LD + n] = xb[i][q];
+            }
         }
         __syncthreads();
+        if (k0 + KT < K) fetch(k0 + KT);  // the next block's loads fly during these products
 #pragma unroll
         for (int kq = 0; kq < KT / 4; ++kq) {
             const float av = as[(4 * kq + g) * LD + 16 * w + r16];
@@ -258,6 +293,19 @@ __global__ __launch_bounds__(64) void bwd_table_kernel(const int32_t* __restrict
     header[1] = (int32_t)count;
 }
 
+// eight consecutive stored elements p[i .. i + 7] (i a multiple of 8), widened
+__device__ __forceinline__ void load8(const float* p, int64_t i, f32x4& a, f32x4& b)
+{
+    a = *reinterpret_cast<const f32x4*>(p + i);
+    b = *reinterpret_cast<const f32x4*>(p + i + 4);
+}
+__device__ __forceinline__ void load8(const uint16_t* p, int64_t i, f32x4& a, f32x4& b)
+{
+    const u16x8 x = *reinterpret_cast<const u16x8*>(p + i);
+    a = f32x4{bf16_bits_to_f32(x[0]), bf16_bits_to_f32(x[1]), bf16_bits_to_f32(x[2]), bf16_bits_to_f32(x[3])};
+    b = f32x4{bf16_bits_to_f32(x[4]), bf16_bits_to_f32(x[5]), bf16_bits_to_f32(x[6]), bf16_bits_to_f32(x[7])};
+}
+
 template <typename TIn>
 __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a)
 {
@@ -271,7 +319,7 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a)
     const int dk = a.dk, dv = a.dv, H = a.H;
     Slices s = slices(a, b);
     __shared__ __align__(16) float as[KTL * LD], bs[KTL * LD];
-    __shared__ float gam[BC], bet[BC], bge[BC], dd[BC], eg[BC];
+    __shared__ float gam[BC], bet[BC], bge[BC], dd[BC], eg[BC], gin[BC];
     __shared__ float Am[BC][BC + 1], Ts[BC][BC + 1];
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
     const TIn* q = (const TIn*)a.q;
@@ -279,73 +327,111 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a)
     const TIn* v = (const TIn*)a.v;
     const TIn* dO = (const TIn*)a.dO;
 
-    // rows of the chunk, normalised and padded with zeros; each wave takes its
-    // 16 rows four at a time with all of their loads in flight (d <= 256: at
-    // most four values per lane and row)
-    for (int r0 = wv; r0 < BC; r0 += 16) {
-        float xq[4][4], xk[4][4], xv[4][4], xo[4][4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = r0 + 4 * i;
-            const bool live = r < len;
-            const int64_t row = (int64_t)(tok0 + (live ? r : 0)) * H + h;
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int col = lane + 64 * m;
-                xq[i][m] = (live && col < dk) ? Elem<TIn>::load(q, row * dk + col) : 0.f;
-                xk[i][m] = (live && col < dk) ? Elem<TIn>::load(k, row * dk + col) : 0.f;
-                xv[i][m] = (live && col < dv) ? Elem<TIn>::load(v, row * dv + col) : 0.f;
-                xo[i][m] = (live && col < dv) ? Elem<TIn>::load(dO, row * dv + col) : 0.f;
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = r0 + 4 * i;
-            float ssq = 0.f, ssk = 0.f;
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                ssq += xq[i][m] * xq[i][m];
-                ssk += xk[i][m] * xk[i][m];
-            }
-            ssq = group_sum<64>(ssq);
-            ssk = group_sum<64>(ssk);
-            const float rq = a.l2norm ? 1.0f / sqrtf(ssq + kNormEps) : 1.f;
-            const float rk = a.l2norm ? 1.0f / sqrtf(ssk + kNormEps) : 1.f;
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int col = lane + 64 * m;
-                if (col < dk) {
-                    s.Q[r * dk + col] = xq[i][m] * rq;
-                    s.K[r * dk + col] = xk[i][m] * rk;
-                }
-                if (col < dv) {
-                    s.V[r * dv + col] = xv[i][m];
-                    s.dO[r * dv + col] = xo[i][m];
-                }
-            }
-            if (lane == 0) {
-                s.rq[r] = rq;
-                s.rk[r] = rk;
-            }
-        }
-    }
-    if (t == 0) {
-        float acc = 0.f;
-        for (int r = 0; r < BC; ++r) {
-            const bool live = r < len;
-            const int64_t row = (int64_t)(tok0 + (live ? r : 0)) * H + h;
-            acc += live ? a.g[row] : 0.f;
-            gam[r] = acc;
-            bet[r] = live ? a.beta[row] : 0.f;
-        }
+    // chunk-local cumulative log-decay gamma and beta: one row per lane of
+    // wave 0 (padded rows add g = 0).  Lane r sums g_0 .. g_r in row order, the
+    // running sum's own rounding: a tree scan rounds each gamma_r - gamma_{r-1}
+    // differently and measurably loosened the decay gradient.
+    if (wv == 0) {
+        const bool live = lane < len;
+        const int64_t row = (int64_t)(tok0 + (live ? lane : 0)) * H + h;
+        gin[lane] = live ? a.g[row] : 0.f;
+        const float bt = live ? a.beta[row] : 0.f;
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        float x = 0.f;
+        for (int r = 0; r <= lane; ++r) x += gin[r];
+        const float gl = __shfl(x, BC - 1, kWave);
+        gam[lane] = x;
+        bet[lane] = bt;
+        eg[lane] = expf(x);
+        dd[lane] = expf(gl - x);
+        bge[lane] = bt * expf(x);
+        s.gam[lane] = x;
+        s.bet[lane] = bt;
     }
     __syncthreads();
-    if (t < BC) {
-        eg[t] = expf(gam[t]);
-        dd[t] = expf(gam[BC - 1] - gam[t]);
-        bge[t] = bet[t] * eg[t];
-        s.gam[t] = gam[t];
-        s.bet[t] = bet[t];
+
+    // rows of the chunk, normalised and padded with zeros, by 16-byte loads and
+    // stores: a row of d elements spreads over d / 8 lanes, eight elements
+    // each; wave w takes rows 16 w .. 16 w + 15, up to four rows per lane in
+    // flight.  D K and E = scale e^gamma dO are formed here as well.
+    const int r_end = 16 * wv + 16;
+    {
+        const int lpr = dk / 8, rpi = kWave / lpr, sub = lane / lpr, c8 = 8 * (lane % lpr);
+        for (int r0 = 16 * wv; r0 < r_end; r0 += 4 * rpi) {
+            f32x4 xq[4][2], xk[4][2];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = r0 + i * rpi + sub;
+                const bool live = r < len && r0 + i * rpi < r_end;
+                const int64_t row = (int64_t)(tok0 + (live ? r : 0)) * H + h;
+                if (r0 + i * rpi < r_end) {
+                    load8(q, row * dk + c8, xq[i][0], xq[i][1]);
+                    load8(k, row * dk + c8, xk[i][0], xk[i][1]);
+                }
+                if (!live) xq[i][0] = xq[i][1] = xk[i][0] = xk[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (r0 + i * rpi >= r_end) break;
+                const int r = r0 + i * rpi + sub;
+                float ssq = 0.f, ssk = 0.f;
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        ssq += xq[i][u][e] * xq[i][u][e];
+                        ssk += xk[i][u][e] * xk[i][u][e];
+                    }
+                for (int m = 1; m < lpr; m <<= 1) {
+                    ssq += __shfl_xor(ssq, m, kWave);
+                    ssk += __shfl_xor(ssk, m, kWave);
+                }
+                const float rq = a.l2norm ? 1.0f / sqrtf(ssq + kNormEps) : 1.f;
+                const float rk = a.l2norm ? 1.0f / sqrtf(ssk + kNormEps) : 1.f;
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int64_t o = (int64_t)r * dk + c8 + 4 * u;
+                    *reinterpret_cast<f32x4*>(s.Q + o) = xq[i][u] * rq;
+                    *reinterpret_cast<f32x4*>(s.K + o) = xk[i][u] * rk;
+                    *reinterpret_cast<f32x4*>(s.DK + o) = xk[i][u] * (rk * dd[r]);
+                }
+                if (c8 == 0) {
+                    s.rq[r] = rq;
+                    s.rk[r] = rk;
+                }
+            }
+        }
+    }
+    {
+        const int lpr = dv / 8, rpi = kWave / lpr, sub = lane / lpr, c8 = 8 * (lane % lpr);
+        for (int r0 = 16 * wv; r0 < r_end; r0 += 4 * rpi) {
+            f32x4 xv[4][2], xo[4][2];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = r0 + i * rpi + sub;
+                const bool live = r < len && r0 + i * rpi < r_end;
+                const int64_t row = (int64_t)(tok0 + (live ? r : 0)) * H + h;
+                if (r0 + i * rpi < r_end) {
+                    load8(v, row * dv + c8, xv[i][0], xv[i][1]);
+                    load8(dO, row * dv + c8, xo[i][0], xo[i][1]);
+                }
+                if (!live) xv[i][0] = xv[i][1] = xo[i][0] = xo[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (r0 + i * rpi >= r_end) break;
+                const int r = r0 + i * rpi + sub;
+                const float se = a.scale * eg[r];
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int64_t o = (int64_t)r * dv + c8 + 4 * u;
+                    *reinterpret_cast<f32x4*>(s.V + o) = xv[i][u];
+                    *reinterpret_cast<f32x4*>(s.dO + o) = xo[i][u];
+                    *reinterpret_cast<f32x4*>(s.E + o) = xo[i][u] * se;
+                }
+            }
+        }
     }
     __syncthreads();  // also publishes the rows written above to the whole workgroup
 
@@ -353,7 +439,7 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a)
     float acc[4][4];
     // K K^T -> KKG = strict_lower(K K^T o Gamma), A = diag(beta) KKG
     zero(acc);
-    mm64<KTL>(acc, s.K, dk, 1, nullptr, s.K, 1, dk, dk, 0, as, bs);
+    mm64<KTL, true, false>(acc, s.K, dk, nullptr, s.K, dk, dk, 0, as, bs);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -365,7 +451,7 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a)
         }
     // Q K^T -> P = lower(Q K^T o Gamma)
     zero(acc);
-    mm64<KTL>(acc, s.Q, dk, 1, nullptr, s.K, 1, dk, dk, 0, as, bs);
+    mm64<KTL, true, false>(acc, s.Q, dk, nullptr, s.K, dk, dk, 0, as, bs);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -385,32 +471,30 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a)
     }
     for (int e = t; e < BC * BC; e += 256) s.T[e] = Ts[e >> 6][e & 63];
     __syncthreads();
-    // W = T diag(beta e^gamma) K,  D K,  then U = T diag(beta) V,  E = scale e^gamma dO
+    // W = T diag(beta e^gamma) K, then U = T diag(beta) V
     for (int n0 = 0; n0 < dk; n0 += 64) {
         zero(acc);
-        mm64<KTL>(acc, s.T, BC, 1, bge, s.K, dk, 1, BC, n0, as, bs);
+        mm64<KTL, true, true>(acc, s.T, BC, bge, s.K, dk, BC, n0, as, bs);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = 4 * tr + i, n = n0 + 16 * j + tc;
                 s.W[r * dk + n] = acc[i][j];
-                s.DK[r * dk + n] = dd[r] * s.K[r * dk + n];
             }
     }
     for (int n0 = 0; n0 < dv; n0 += 64) {
         zero(acc);
-        mm64<KTL>(acc, s.T, BC, 1, bet, s.V, dv, 1, BC, n0, as, bs);
+        mm64<KTL, true, true>(acc, s.T, BC, bet, s.V, dv, BC, n0, as, bs);
         float acc2[4][4];
         zero(acc2);
-        mm64<KTL>(acc2, s.P, 1, BC, nullptr, s.dO, dv, 1, BC, n0, as, bs);  // P^T dO
+        mm64<KTL, false, true>(acc2, s.P, BC, nullptr, s.dO, dv, BC, n0, as, bs);  // P^T dO
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = 4 * tr + i, n = n0 + 16 * j + tc;
                 s.U[r * dv + n] = acc[i][j];
-                s.E[r * dv + n] = a.scale * eg[r] * s.dO[r * dv + n];
                 s.dDl[r * dv + n] = a.scale * acc2[i][j];
             }
     }
@@ -729,47 +813,9 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a)
         __syncthreads();
     };
 
-    // dQ = scale e^gamma (dO S);  dgamma_r += Q_r . dQ_r
-    rowp[0] = rowp[1] = rowp[2] = rowp[3] = 0.f;
-    for (int n0 = 0; n0 < dk; n0 += 64) {
-        zero(acc);
-        mm64<KTG>(acc, s.dO, dv, 1, nullptr, s.S, dk, 1, dv, n0, as, bs);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 4 * tr + i, n = n0 + 16 * j + tc;
-                const float x = scale * eg[r] * acc[i][j];
-                s.dQ[r * dk + n] = x;
-                rowp[i] += s.Q[r * dk + n] * x;
-            }
-    }
-    row_add(dgam, 1.f);
-    // dK = D (Delta dS);  d(dd)_r = K_r . (Delta dS)_r
-    rowp[0] = rowp[1] = rowp[2] = rowp[3] = 0.f;
-    for (int n0 = 0; n0 < dk; n0 += 64) {
-        zero(acc);
-        mm64<KTG>(acc, s.Dl, dv, 1, nullptr, s.dS, dk, 1, dv, n0, as, bs);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 4 * tr + i, n = n0 + 16 * j + tc;
-                s.dK[r * dk + n] = dd[r] * acc[i][j];
-                rowp[i] += s.K[r * dk + n] * acc[i][j];
-            }
-    }
-    float dgL = 0.f;  // gradient of gamma_L, reduced over the workgroup below
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float x = group_sum<16>(rowp[i]);
-        const int r = 4 * tr + i;
-        if (tc == 0) {
-            dgam[r] -= x * dd[r];
-            dgL += x * dd[r];
-        }
-    }
-    // + e^{gamma_L} <dS, S>
+    // e^{gamma_L} <dS, S>: part of the gradient of gamma_L, reduced over the
+    // workgroup after the column blocks below
+    float dgL = 0.f;
     {
         const int64_t n4 = (int64_t)dv * dk / 4;
         const f32x4* S4 = reinterpret_cast<const f32x4*>(s.S);
@@ -788,12 +834,9 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a)
         }
         dgL += expf(gam[BC - 1]) * x;
     }
-    dgL = group_sum<64>(dgL);
-    if (lane == 0) red[wv] = dgL;
-    __syncthreads();
     // dP = scale lower(dO Delta^T);  dgamma from P;  dPG = dP o Gamma
     zero(acc);
-    mm64<KTG>(acc, s.dO, dv, 1, nullptr, s.Dl, 1, dv, dv, 0, as, bs);
+    mm64<KTG, true, false>(acc, s.dO, dv, nullptr, s.Dl, dv, dv, 0, as, bs);
     {
         float colp[4] = {0.f, 0.f, 0.f, 0.f};
         rowp[0] = rowp[1] = rowp[2] = rowp[3] = 0.f;
@@ -811,26 +854,10 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a)
         row_add(dgam, 1.f);
         col_sub(dgam, colp);  // its barriers also complete dPG
     }
-    // dQ += dPG K;  dK += dPG^T Q
-    for (int n0 = 0; n0 < dk; n0 += 64) {
-        zero(acc);
-        mm64<KTG>(acc, s.dPG, BC, 1, nullptr, s.K, dk, 1, BC, n0, as, bs);
-        float acc2[4][4];
-        zero(acc2);
-        mm64<KTG>(acc2, s.dPG, 1, BC, nullptr, s.Q, dk, 1, BC, n0, as, bs);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 4 * tr + i, n = n0 + 16 * j + tc;
-                s.dQ[r * dk + n] += acc[i][j];
-                s.dK[r * dk + n] += acc2[i][j];
-            }
-    }
     // dW = -(dDelta S)
     for (int n0 = 0; n0 < dk; n0 += 64) {
         zero(acc);
-        mm64<KTG>(acc, s.dD, dv, 1, nullptr, s.S, dk, 1, dv, n0, as, bs);
+        mm64<KTG, true, true>(acc, s.dD, dv, nullptr, s.S, dk, dv, n0, as, bs);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -840,10 +867,10 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a)
     // dT = (dDelta V^T) diag(beta) + (dW K^T) diag(beta e^gamma)
     {
         zero(acc);
-        mm64<KTG>(acc, s.dD, dv, 1, nullptr, s.V, 1, dv, dv, 0, as, bs);
+        mm64<KTG, true, false>(acc, s.dD, dv, nullptr, s.V, dv, dv, 0, as, bs);
         float acc2[4][4];
         zero(acc2);
-        mm64<KTG>(acc2, s.dW, dk, 1, nullptr, s.K, 1, dk, dk, 0, as, bs);
+        mm64<KTG, true, false>(acc2, s.dW, dk, nullptr, s.K, dk, dk, 0, as, bs);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -856,7 +883,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a)
     rowp[0] = rowp[1] = rowp[2] = rowp[3] = 0.f;
     for (int n0 = 0; n0 < dv; n0 += 64) {
         zero(acc);
-        mm64<KTG>(acc, s.T, 1, BC, nullptr, s.dD, dv, 1, BC, n0, as, bs);
+        mm64<KTG, false, true>(acc, s.T, BC, nullptr, s.dD, dv, BC, n0, as, bs);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -867,33 +894,10 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a)
             }
     }
     row_add(dbet, 1.f);
-    // dK += diag(beta e^gamma) T^T dW;  (T^T dW)_r . K_r feeds dbeta and dgamma
-    rowp[0] = rowp[1] = rowp[2] = rowp[3] = 0.f;
-    for (int n0 = 0; n0 < dk; n0 += 64) {
-        zero(acc);
-        mm64<KTG>(acc, s.T, 1, BC, nullptr, s.dW, dk, 1, BC, n0, as, bs);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 4 * tr + i, n = n0 + 16 * j + tc;
-                s.dK[r * dk + n] += bge[r] * acc[i][j];
-                rowp[i] += acc[i][j] * s.K[r * dk + n];
-            }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float x = group_sum<16>(rowp[i]);
-        const int r = 4 * tr + i;
-        if (tc == 0) {
-            dbet[r] += eg[r] * x;
-            dgam[r] += bge[r] * x;
-        }
-    }
     __syncthreads();  // dT complete
     // X1 = dT T^T
     zero(acc);
-    mm64<KTG>(acc, s.dT, BC, 1, nullptr, s.T, 1, BC, BC, 0, as, bs);
+    mm64<KTG, true, false>(acc, s.dT, BC, nullptr, s.T, BC, BC, 0, as, bs);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -901,7 +905,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a)
     __syncthreads();
     // dA = -strict_lower(T^T X1);  Bd = diag(beta) (dA o Gamma);  dbeta, dgamma from A
     zero(acc);
-    mm64<KTG>(acc, s.T, 1, BC, nullptr, s.X1, BC, 1, BC, 0, as, bs);
+    mm64<KTG, false, true>(acc, s.T, BC, nullptr, s.X1, BC, BC, 0, as, bs);
     {
         float colp[4] = {0.f, 0.f, 0.f, 0.f};
         float rowb[4] = {0.f, 0.f, 0.f, 0.f};
@@ -925,16 +929,65 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a)
         row_add(dbet, 1.f);
         col_sub(dgam, colp);  // its barriers also complete Bd
     }
-    // dK += Bd K + Bd^T K
+    // dQ and dK (before the norms), one 64-column block at a time, every term
+    // accumulated in registers and stored once:
+    //   dQ = scale e^gamma (dO S) + dPG K
+    //   dK = D (Delta dS) + dPG^T Q + diag(beta e^gamma) T^T dW + Bd K + Bd^T K
+    // with the row sums  Q_r . (scale e^gamma dO S)_r -> dgamma_r,
+    // K_r . (Delta dS)_r -> -D_r dgamma_r and gamma_L, (T^T dW)_r . K_r -> dbeta, dgamma.
+    float rq[4] = {0.f, 0.f, 0.f, 0.f}, rk[4] = {0.f, 0.f, 0.f, 0.f}, rt[4] = {0.f, 0.f, 0.f, 0.f};
     for (int n0 = 0; n0 < dk; n0 += 64) {
         zero(acc);
-        mm64<KTG>(acc, s.Bd, BC, 1, nullptr, s.K, dk, 1, BC, n0, as, bs);
-        mm64<KTG>(acc, s.Bd, 1, BC, nullptr, s.K, dk, 1, BC, n0, as, bs);
+        mm64<KTG, true, true>(acc, s.dO, dv, nullptr, s.S, dk, dv, n0, as, bs);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) s.dK[(4 * tr + i) * dk + n0 + 16 * j + tc] += acc[i][j];
+            for (int j = 0; j < 4; ++j) {
+                const int r = 4 * tr + i, n = n0 + 16 * j + tc;
+                acc[i][j] *= scale * eg[r];
+                rq[i] += s.Q[r * dk + n] * acc[i][j];
+            }
+        mm64<KTG, true, true>(acc, s.dPG, BC, nullptr, s.K, dk, BC, n0, as, bs);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) s.dQ[(4 * tr + i) * dk + n0 + 16 * j + tc] = acc[i][j];
+
+        float acc2[4][4];
+        zero(acc2);
+        mm64<KTG, false, true>(acc2, s.T, BC, nullptr, s.dW, dk, BC, n0, as, bs);
+        zero(acc);
+        mm64<KTG, true, true>(acc, s.Dl, dv, nullptr, s.dS, dk, dv, n0, as, bs);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 4 * tr + i;
+                const float kx = s.K[r * dk + n0 + 16 * j + tc];
+                rk[i] += kx * acc[i][j];
+                rt[i] += kx * acc2[i][j];
+                acc[i][j] = acc[i][j] * dd[r] + bge[r] * acc2[i][j];
+            }
+        mm64<KTG, false, true>(acc, s.dPG, BC, nullptr, s.Q, dk, BC, n0, as, bs);
+        mm64<KTG, true, true>(acc, s.Bd, BC, nullptr, s.K, dk, BC, n0, as, bs);
+        mm64<KTG, false, true>(acc, s.Bd, BC, nullptr, s.K, dk, BC, n0, as, bs);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) s.dK[(4 * tr + i) * dk + n0 + 16 * j + tc] = acc[i][j];
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float xq = group_sum<16>(rq[i]), xk = group_sum<16>(rk[i]), xt = group_sum<16>(rt[i]);
+        const int r = 4 * tr + i;
+        if (tc == 0) {
+            dgam[r] += xq - xk * dd[r] + bge[r] * xt;
+            dbet[r] += eg[r] * xt;
+            dgL += xk * dd[r];
+        }
+    }
+    dgL = group_sum<64>(dgL);
+    if (lane == 0) red[wv] = dgL;
     __syncthreads();  // dQ, dK, dgam, dbet complete
     // dg: reverse cumulative sum of dgamma (gamma_L is the last, padded-constant, entry)
     if (t == 0) {
