@@ -39,6 +39,8 @@
 // depend on scheduling: no atomics, fixed reduction orders.
 #include <string.h>
 
+#include <type_traits>
+
 #include "gdn_common.h"
 #include "gdn_launch.h"
 
@@ -639,18 +641,19 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs a, ChainOps rev_
     const int per_wg = (npiece + RB - 1) / RB, per_wave = (per_wg + 3) / 4;
     uint32_t pf_acc = 0;
     u32x4 pf[2][4];
+    // (a piece beyond this workgroup's share reloads the chunk's first Y piece:
+    // every lane loads on every step, with no branch around the loads)
     auto prefetch = [&](int64_t ch, u32x4* dst) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int q = rb * per_wg + w * per_wave + i;
-            const unsigned char* src = nullptr;
-            if (i < per_wave && q < npiece && (w * per_wave + i) < per_wg) {
-                if (q < OPB) src = reinterpret_cast<const unsigned char*>(Yr + ch * fper) + q * 1024;
-                else if (q < 2 * OPB) src = reinterpret_cast<const unsigned char*>(Zf + ch * fper) + (q - OPB) * 1024;
-                else if (q < 3 * OPB) src = reinterpret_cast<const unsigned char*>(Ff + ch * fper) + (q - 2 * OPB) * 1024;
-                else src = reinterpret_cast<const unsigned char*>(Ef + ch * (int64_t)BC * dv * 2) + (q - 3 * OPB) * 1024;
-            }
-            dst[i] = src ? *reinterpret_cast<const u32x4*>(src + lane * 16) : u32x4{0u, 0u, 0u, 0u};
+            const int q0 = rb * per_wg + w * per_wave + i;
+            const bool mine = i < per_wave && q0 < npiece && (w * per_wave + i) < per_wg;
+            const int q = mine ? q0 : 0;
+            const uint16_t* base = q < OPB ? Yr : q < 2 * OPB ? Zf : q < 3 * OPB ? Ff : Ef;
+            const int64_t per = q < 3 * OPB ? fper : (int64_t)BC * dv * 2;
+            const int qq = q < OPB ? q : q < 2 * OPB ? q - OPB : q < 3 * OPB ? q - 2 * OPB : q - 3 * OPB;
+            const unsigned char* src = reinterpret_cast<const unsigned char*>(base + ch * per) + qq * 1024;
+            dst[i] = *reinterpret_cast<const u32x4*>(src + lane * 16);
         }
     };
 
@@ -670,17 +673,15 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs a, ChainOps rev_
         load_z(chunk_of(0));
         if (hasF) load_f(chunk_of(0));
     }
-    for (int it = 0; it < steps; ++it) {
+    // one chunk; the loop below runs two per iteration, so that each uses a
+    // fixed prefetch slot (a slot picked by it & 1 is a dynamic register index,
+    // which the compiler serves with a wait for every load in flight)
+    auto chunk_step = [&](int it, u32x4* slot, auto hasF_c) __attribute__((always_inline)) {
         const int64_t ch = chunk_of(it);
         {
-            u32x4* slot = pf[it & 1];
-            if (it >= 2)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) pf_acc ^= slot[i].x ^ slot[i].w;
-            if (it + 2 < steps) prefetch(chunk_of(it + 2), slot);
-            else
-#pragma unroll
-                for (int i = 0; i < 4; ++i) slot[i] = u32x4{0u, 0u, 0u, 0u};
+            for (int i = 0; i < 4; ++i) pf_acc ^= slot[i].x ^ slot[i].w;
+            prefetch(chunk_of(min(it + 2, steps - 1)), slot);
         }
         // the state before the chunk: to LDS in fp32 (for the record) and split
         // into bf16 hi and lo (the A operand of S Y^T), then from its rows to the
@@ -722,7 +723,7 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs a, ChainOps rev_
         for (int i = 0; i < 4; ++i) dsm[(4 * g + i) * DP + 16 * w + l16] = d[i];
         *reinterpret_cast<f32x4*>(Dst + (ch * BC + 16 * w + l16) * dv + rb * 16 + 4 * g) = d;
         const float decay = expf(gl);
-        if (it + 1 < steps) load_y(chunk_of(it + 1));
+        load_y(chunk_of(min(it + 1, steps - 1)));
         __syncthreads();  // ---- Delta^T in LDS; the state rows read
         // S <- e^{gamma_L} S + zsign Delta^T Z (+ E^T F)
 #pragma unroll
@@ -735,15 +736,31 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs a, ChainOps rev_
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt) sreg[tt] = mma3(dh, dl, zr[tt][ks][0], zr[tt][ks][1], sreg[tt]);
         }
-        if (it + 1 < steps) load_z(chunk_of(it + 1));
-        if (hasF) {
+        load_z(chunk_of(min(it + 1, steps - 1)));
+        if constexpr (decltype(hasF_c)::value) {
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
                 for (int tt = 0; tt < NT; ++tt) sreg[tt] = mma3(er[ks][0], er[ks][1], fr[tt][ks][0], fr[tt][ks][1], sreg[tt]);
-            if (it + 1 < steps) load_f(chunk_of(it + 1));
+            load_f(chunk_of(min(it + 1, steps - 1)));
         }
-    }
+    };
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pf[b2][i] = u32x4{0u, 0u, 0u, 0u};
+    // the two directions as separate loops: the E^T F term and its loads are
+    // compiled in or out, never branched around
+    auto run = [&](auto hasF_c) __attribute__((always_inline)) {
+        for (int it = 0; it < steps; it += 2) {
+            chunk_step(it, pf[0], hasF_c);
+            if (it + 1 < steps) chunk_step(it + 1, pf[1], hasF_c);
+        }
+    };
+    if (hasF)
+        run(std::true_type{});
+    else
+        run(std::false_type{});
     if (S_final)
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt)
