@@ -462,15 +462,31 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a)
             s.P[r * BC + n] = n <= r ? acc[i][j] * expf(gam[r] - gam[n]) : 0.f;
         }
     __syncthreads();
-    // T = (I + A)^{-1} by forward substitution, one row per step
-    for (int r = 0; r < BC; ++r) {
-        if (t < BC) {
-            float x = (t == r) ? 1.f : 0.f;
-            for (int j = 0; j < r; ++j) x -= Am[r][j] * Ts[j][t];
-            Ts[r][t] = x;
+    // T = (I + A)^{-1} by forward substitution.  Column c of T depends only on
+    // its own earlier rows, T[r][c] = [r == c] - sum_{j < r} A[r][j] T[j][c],
+    // so four lanes of one wave own a column with no barrier: lane q keeps
+    // T[4 m + q][c] (m < 16) in registers and sums the terms j = q mod 4; a
+    // swap within the quad adds the four sums (the same bits in every lane).
+    {
+        const int tcol = 16 * wv + (lane >> 2), q = lane & 3;
+        float Tq[BC / 4];
+#pragma unroll
+        for (int m = 0; m < BC / 4; ++m) Tq[m] = 0.f;
+#pragma unroll
+        for (int r = 0; r < BC; ++r) {
+            float part = 0.f;
+#pragma unroll
+            for (int m = 0; 4 * m < r; ++m)
+                if (4 * m + q < r) part += Am[r][4 * m + q] * Tq[m];
+            part += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(part), 0xB1, 0xF, 0xF, false));
+            part += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(part), 0x4E, 0xF, 0xF, false));
+            const float x = (r == tcol ? 1.f : 0.f) - part;
+            if (q == (r & 3)) Tq[r >> 2] = x;
         }
-        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < BC / 4; ++m) Ts[4 * m + q][tcol] = Tq[m];
     }
+    __syncthreads();
     for (int e = t; e < BC * BC; e += 256) s.T[e] = Ts[e >> 6][e & 63];
     __syncthreads();
     // W = T diag(beta e^gamma) K, then U = T diag(beta) V
