@@ -790,7 +790,7 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs a, ChainOps rev_
     asm volatile("" ::"v"(pf_acc));  // the prefetched words stay live: the loads are kept
 }
 
-__global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a)
+__global__ __launch_bounds__(256, 3) void bwd_grad_kernel(BwdArgs a)
 {
     const int64_t b = blockIdx.x;
     const int32_t* header = reinterpret_cast<const int32_t*>(a.ws + a.lay.off_header);
@@ -1023,51 +1023,62 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a)
     if (lane == 0) red[wv] = dgL;
     __syncthreads();  // dQ, dK, dgam, dbet complete
     // dg: reverse cumulative sum of dgamma (gamma_L is the last, padded-constant, entry)
-    if (t == 0) {
+    // (lane r of wave 0 adds dgamma_63 .. dgamma_r in that order: the serial
+    // sum's own rounding, every row at once)
+    if (wv == 0) {
         float run = red[0] + red[1] + red[2] + red[3];
-        for (int r = BC - 1; r >= 0; --r) {
-            run += dgam[r];
-            if (r < len) {
-                const int64_t row = (int64_t)(tok0 + r) * H + h;
-                a.dg[row] = run;
-                a.dbeta[row] = dbet[r];
-            }
+        for (int j = BC - 1; j >= lane; --j) run += dgam[j];
+        if (lane < len) {
+            const int64_t row = (int64_t)(tok0 + lane) * H + h;
+            a.dg[row] = run;
+            a.dbeta[row] = dbet[lane];
         }
     }
-    // through the L2 norms: dx = r (dx^ - x^ (x^ . dx^)); four rows per wave in flight
-    for (int r0 = wv; r0 < BC; r0 += 16) {
-        float xq[4][4], gq[4][4], xk[4][4], gk[4][4];
+    // through the L2 norms: dx = r (dx^ - x^ (x^ . dx^)).  A row of d_k values
+    // spreads over d_k / 8 lanes, eight each, by 16-byte loads and stores;
+    // wave w takes rows 16 w .. 16 w + 15, two rows per lane in flight.
+    {
+        const int lpr = dk / 8, rpi = kWave / lpr, sub = lane / lpr, c8 = 8 * (lane % lpr);
+        const int r_end = 16 * wv + 16;
+        for (int r0 = 16 * wv; r0 < r_end; r0 += 2 * rpi) {
+            f32x4 xq[2][2], gq[2][2], xk[2][2], gk[2][2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 2; ++i) {
+                const int r = min(r0 + i * rpi, r_end - rpi) + sub;
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int r = r0 + 4 * i, col = lane + 64 * m;
-                const bool in = col < dk;
-                xq[i][m] = in ? s.Q[r * dk + col] : 0.f;
-                gq[i][m] = in ? s.dQ[r * dk + col] : 0.f;
-                xk[i][m] = in ? s.K[r * dk + col] : 0.f;
-                gk[i][m] = in ? s.dK[r * dk + col] : 0.f;
+                for (int u = 0; u < 2; ++u) {
+                    const int o = r * dk + c8 + 4 * u;
+                    xq[i][u] = *reinterpret_cast<const f32x4*>(s.Q + o);
+                    gq[i][u] = *reinterpret_cast<const f32x4*>(s.dQ + o);
+                    xk[i][u] = *reinterpret_cast<const f32x4*>(s.K + o);
+                    gk[i][u] = *reinterpret_cast<const f32x4*>(s.dK + o);
+                }
             }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = r0 + 4 * i;
-            float pq = 0.f, pk = 0.f;
+            for (int i = 0; i < 2; ++i) {
+                if (r0 + i * rpi >= r_end) break;  // wave-uniform
+                const int r = r0 + i * rpi + sub;
+                float pq = 0.f, pk = 0.f;
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                pq += xq[i][m] * gq[i][m];
-                pk += xk[i][m] * gk[i][m];
-            }
-            pq = a.l2norm ? group_sum<64>(pq) : 0.f;
-            pk = a.l2norm ? group_sum<64>(pk) : 0.f;
-            if (r >= len) continue;  // wave-uniform
-            const int64_t row = (int64_t)(tok0 + r) * H + h;
-            const float rq = s.rq[r], rk = s.rk[r];
+                for (int u = 0; u < 2; ++u)
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int col = lane + 64 * m;
-                if (col < dk) {
-                    a.dq[row * dk + col] = rq * (gq[i][m] - xq[i][m] * pq);
-                    a.dk_out[row * dk + col] = rk * (gk[i][m] - xk[i][m] * pk);
+                    for (int e = 0; e < 4; ++e) {
+                        pq += xq[i][u][e] * gq[i][u][e];
+                        pk += xk[i][u][e] * gk[i][u][e];
+                    }
+                for (int m = 1; m < lpr; m <<= 1) {
+                    pq += __shfl_xor(pq, m, kWave);
+                    pk += __shfl_xor(pk, m, kWave);
+                }
+                if (!a.l2norm) pq = pk = 0.f;
+                if (r >= len) continue;
+                const int64_t row = (int64_t)(tok0 + r) * H + h;
+                const float rq = s.rq[r], rk = s.rk[r];
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int64_t o = row * dk + c8 + 4 * u;
+                    *reinterpret_cast<f32x4*>(a.dq + o) = rq * (gq[i][u] - xq[i][u] * pq);
+                    *reinterpret_cast<f32x4*>(a.dk_out + o) = rk * (gk[i][u] - xk[i][u] * pk);
                 }
             }
         }
