@@ -2551,11 +2551,10 @@ static hipError_t run_prefill(const PrefillArgs& a)
     auto seg_lo = [&](int s) { return bounds[std::min(s, nseg)]; };
     // bf16 on CU-masked streams, outside stream capture: the chain runs as one
     // launch over every chunk and the hand-offs go through device memory
-    // (PipeSync), so the chain never stops between segments.  The caller's
-    // stream zeroes the hand-off words, prepares the first segment over the
-    // whole GPU and, at the end, finishes the last segment's outputs over the
-    // whole GPU; in between the intra-chunk kernel prepares segments 1.. and
-    // the output kernel finishes segments 0..nseg-2 on the two side streams.
+    // (PipeSync), so the chain never stops between segments.  The intra-chunk
+    // kernel prepares every segment, in order, on one side stream and raises
+    // each segment's flag; the output kernel finishes every segment, in order,
+    // on the other, each behind a wait for the chain's store waves.
     // A wait in device memory needs its producer to run beside it: masked
     // streams each own a hardware queue, while a graph's executor, or streams
     // that share a queue, may run the two in sequence.  Those cases keep the
