@@ -49,7 +49,7 @@ namespace {
 
 constexpr int BC = kBwdChunk;  // chunk length of the backward
 constexpr int LD = 68;   // LDS row pitch of the tile routine (floats)
-constexpr int KTL = 16;  // its k block in the local kernel
+constexpr int KTL = 32;  // its k block in the local kernel
 constexpr int KTG = 32;  // and in the gradient kernel
 
 // acc[i][j] += sum_k A(r, k) B(k, n) for r = 4 tr + i in [0, 64), n = n0 + 16 j + tc
