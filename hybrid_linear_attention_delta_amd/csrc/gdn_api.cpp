@@ -138,9 +138,11 @@ BwdLayout backward_layout(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t d
     L.off_KKG = take(cc);
     L.off_W = take(cdk);
     L.off_U = take(cdv);
-    L.off_DK = take(cdk);
+    L.off_Kraw = take(cdk);
+    L.off_Qraw = take(cdk);
     L.off_E = take(cdv);
     L.off_dDl = take(cdv);
+    L.off_sck = take(c1);
     L.off_S = take(st);
     L.off_Dl = take(cdv);
     L.off_dS = take(st);
@@ -153,11 +155,11 @@ BwdLayout backward_layout(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t d
     L.off_X1 = take(cc);
     L.off_Bd = take(cc);
     L.off_Wf = take(cdk);
-    L.off_DKf = take(cdk);
+    L.off_Kf = take(cdk);
     L.off_Qf = take(cdk);
     L.off_Ef = take(cdv);
     L.off_Wr = take(cdk);
-    L.off_DKr = take(cdk);
+    L.off_Kr = take(cdk);
     L.total = off;
     return L;
 }

@@ -152,7 +152,7 @@ __device__ __forceinline__ void zero(float acc[4][4])
 
 // Per chunk-head slices of the workspace.
 struct Slices {
-    float *Q, *K, *V, *dO, *rq, *rk, *gam, *bet, *T, *P, *KKG, *W, *U, *DK, *E, *dDl;
+    float *Q, *K, *V, *dO, *rq, *rk, *gam, *bet, *T, *P, *KKG, *W, *U, *Kraw, *Qraw, *E, *dDl, *sck;
     float *S, *Dl, *dS, *dD, *dQ, *dK, *dW, *dPG, *dT, *X1, *Bd;
 };
 
@@ -176,8 +176,10 @@ __device__ Slices slices(const BwdArgs& a, int64_t b)
     s.KKG = f(L.off_KKG, cc);
     s.W = f(L.off_W, cdk);
     s.U = f(L.off_U, cdv);
-    s.DK = f(L.off_DK, cdk);
+    s.Kraw = f(L.off_Kraw, cdk);
+    s.Qraw = f(L.off_Qraw, cdk);
     s.E = f(L.off_E, cdv);
+    s.sck = f(L.off_sck, BC);
     s.dDl = f(L.off_dDl, cdv);
     s.S = f(L.off_S, dvdk);
     s.Dl = f(L.off_Dl, cdv);
@@ -197,7 +199,9 @@ __device__ Slices slices(const BwdArgs& a, int64_t b)
 // contracting over the chunk rows, on the bf16 matrix cores with hi/lo
 // splits: fragment (ct, ks) gives lane (l16, g) the elements
 // X[32 ks + 8 g + e][16 ct + l16], e = 0..7, as bf16 hi and lo parts at
-// out + (((ct * 2 + ks) * 2 + part) * 64 + lane) * 8.
+// out + (((ct * 2 + ks) * 2 + part) * 64 + lane) * 8 (HI: the hi parts only,
+// for values that bf16 holds exactly).
+template <bool HI>
 __device__ void col_frags(const float* __restrict__ X, int d, uint16_t* __restrict__ out)
 {
     for (int task = threadIdx.x; task < (d / 16) * 128; task += 256) {
@@ -211,14 +215,16 @@ __device__ void col_frags(const float* __restrict__ X, int d, uint16_t* __restri
         for (int w = 0; w < 4; ++w) split_bf16x2(x[2 * w], x[2 * w + 1], hi[w], lo[w]);
         uint16_t* p = out + ((size_t)((ct * 2 + ks) * 2) * 64 + lane) * 8;
         *reinterpret_cast<u32x4*>(p) = u32x4{hi[0], hi[1], hi[2], hi[3]};
-        *reinterpret_cast<u32x4*>(p + 512) = u32x4{lo[0], lo[1], lo[2], lo[3]};
+        if constexpr (!HI) *reinterpret_cast<u32x4*>(p + 512) = u32x4{lo[0], lo[1], lo[2], lo[3]};
     }
 }
 
 // Operand fragments of a row-major fp32 [BC][d] matrix X for a product
 // contracting over its columns: fragment (rt, ks) gives lane (l16, g) the
 // elements X[16 rt + l16][32 ks + 8 g + e], e = 0..7, as bf16 hi and lo parts
-// at out + (((rt * (d / 32) + ks) * 2 + part) * 64 + lane) * 8.
+// at out + (((rt * (d / 32) + ks) * 2 + part) * 64 + lane) * 8 (HI: the hi
+// parts only).
+template <bool HI>
 __device__ void row_frags(const float* __restrict__ X, int d, uint16_t* __restrict__ out)
 {
     const int ksn = d / 32;
@@ -234,7 +240,7 @@ __device__ void row_frags(const float* __restrict__ X, int d, uint16_t* __restri
         split_bf16x2(b.z, b.w, hi[3], lo[3]);
         uint16_t* p = out + ((size_t)((rt * ksn + ks) * 2) * 64 + lane) * 8;
         *reinterpret_cast<u32x4*>(p) = u32x4{hi[0], hi[1], hi[2], hi[3]};
-        *reinterpret_cast<u32x4*>(p + 512) = u32x4{lo[0], lo[1], lo[2], lo[3]};
+        if constexpr (!HI) *reinterpret_cast<u32x4*>(p + 512) = u32x4{lo[0], lo[1], lo[2], lo[3]};
     }
 }
 
@@ -251,6 +257,13 @@ __device__ __forceinline__ f32x4 mma3(u32x4 ah, u32x4 al, u32x4 bh, u32x4 bl, f3
     c = mma_bf16(ah, bh, c);
     c = mma_bf16(al, bh, c);
     return mma_bf16(ah, bl, c);
+}
+
+// A B with A split into bf16 hi + lo and B exact in bf16: A_hi B + A_lo B
+__device__ __forceinline__ f32x4 mma2(u32x4 ah, u32x4 al, u32x4 b, f32x4 c)
+{
+    c = mma_bf16(ah, b, c);
+    return mma_bf16(al, b, c);
 }
 
 // eight fp32 values -> bf16 hi and lo operand fragments
@@ -321,7 +334,7 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a)
     const int dk = a.dk, dv = a.dv, H = a.H;
     Slices s = slices(a, b);
     __shared__ __align__(16) float as[KTL * LD], bs[KTL * LD];
-    __shared__ float gam[BC], bet[BC], bge[BC], dd[BC], eg[BC], gin[BC];
+    __shared__ float gam[BC], bet[BC], bge[BC], dd[BC], eg[BC], gin[BC], rqs[BC];
     __shared__ float Am[BC][BC + 1], Ts[BC][BC + 1];
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
     const TIn* q = (const TIn*)a.q;
@@ -356,7 +369,9 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a)
     // rows of the chunk, normalised and padded with zeros, by 16-byte loads and
     // stores: a row of d elements spreads over d / 8 lanes, eight elements
     // each; wave w takes rows 16 w .. 16 w + 15, up to four rows per lane in
-    // flight.  D K and E = scale e^gamma dO are formed here as well.
+    // flight.  The raw (widened) k and q rows, the row scales D r_k and
+    // E = r_q scale e^gamma dO are formed here as well: the state chains
+    // take K^ and Q^ as raw rows with their scales applied in fp32.
     const int r_end = 16 * wv + 16;
     {
         const int lpr = dk / 8, rpi = kWave / lpr, sub = lane / lpr, c8 = 8 * (lane % lpr);
@@ -396,15 +411,19 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a)
                     const int64_t o = (int64_t)r * dk + c8 + 4 * u;
                     *reinterpret_cast<f32x4*>(s.Q + o) = xq[i][u] * rq;
                     *reinterpret_cast<f32x4*>(s.K + o) = xk[i][u] * rk;
-                    *reinterpret_cast<f32x4*>(s.DK + o) = xk[i][u] * (rk * dd[r]);
+                    *reinterpret_cast<f32x4*>(s.Qraw + o) = xq[i][u];
+                    *reinterpret_cast<f32x4*>(s.Kraw + o) = xk[i][u];
                 }
                 if (c8 == 0) {
                     s.rq[r] = rq;
                     s.rk[r] = rk;
+                    s.sck[r] = rk * dd[r];
+                    rqs[r] = rq;
                 }
             }
         }
     }
+    __syncthreads();  // rqs
     {
         const int lpr = dv / 8, rpi = kWave / lpr, sub = lane / lpr, c8 = 8 * (lane % lpr);
         for (int r0 = 16 * wv; r0 < r_end; r0 += 4 * rpi) {
@@ -424,7 +443,7 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a)
             for (int i = 0; i < 4; ++i) {
                 if (r0 + i * rpi >= r_end) break;
                 const int r = r0 + i * rpi + sub;
-                const float se = a.scale * eg[r];
+                const float se = a.scale * eg[r] * rqs[r];
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
                     const int64_t o = (int64_t)r * dv + c8 + 4 * u;
@@ -519,12 +538,13 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a)
     // the chains' operands contracted over the chunk rows, as bf16 hi/lo fragments
     __syncthreads();
     const int64_t fper = (int64_t)BC * dk * 2;
-    col_frags(s.W, dk, reinterpret_cast<uint16_t*>(a.ws + a.lay.off_Wf) + b * fper);
-    col_frags(s.DK, dk, reinterpret_cast<uint16_t*>(a.ws + a.lay.off_DKf) + b * fper);
-    col_frags(s.Q, dk, reinterpret_cast<uint16_t*>(a.ws + a.lay.off_Qf) + b * fper);
-    col_frags(s.E, dv, reinterpret_cast<uint16_t*>(a.ws + a.lay.off_Ef) + b * (int64_t)BC * dv * 2);
-    row_frags(s.W, dk, reinterpret_cast<uint16_t*>(a.ws + a.lay.off_Wr) + b * fper);
-    row_frags(s.DK, dk, reinterpret_cast<uint16_t*>(a.ws + a.lay.off_DKr) + b * fper);
+    constexpr bool RAW_EXACT = sizeof(TIn) == 2;  // bf16 inputs: raw k and q are exact in bf16
+    col_frags<false>(s.W, dk, reinterpret_cast<uint16_t*>(a.ws + a.lay.off_Wf) + b * fper);
+    col_frags<RAW_EXACT>(s.Kraw, dk, reinterpret_cast<uint16_t*>(a.ws + a.lay.off_Kf) + b * fper);
+    col_frags<RAW_EXACT>(s.Qraw, dk, reinterpret_cast<uint16_t*>(a.ws + a.lay.off_Qf) + b * fper);
+    col_frags<false>(s.E, dv, reinterpret_cast<uint16_t*>(a.ws + a.lay.off_Ef) + b * (int64_t)BC * dv * 2);
+    row_frags<false>(s.W, dk, reinterpret_cast<uint16_t*>(a.ws + a.lay.off_Wr) + b * fper);
+    row_frags<RAW_EXACT>(s.Kraw, dk, reinterpret_cast<uint16_t*>(a.ws + a.lay.off_Kr) + b * fper);
 }
 
 // One row-split recurrence over the chunks of each sequence (see the header):
@@ -560,7 +580,7 @@ struct ChainOps {
 // Workgroup -> (direction and pair, row block): the dv/16 row blocks of one
 // (direction, sequence, head) sit 8 workgroups apart, so they share one XCD
 // and its L2 copy of the chunk operands (the reverse chains first).
-template <int DK>
+template <int DK, bool EXACT>
 __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs a, ChainOps rev_ops, ChainOps fwd_ops)
 {
     constexpr int P = DK + 4;   // LDS pitch of the state rows (floats)
@@ -593,7 +613,6 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs a, ChainOps rev_
     const uint16_t* Zf = reinterpret_cast<const uint16_t*>(a.ws + op.off_Zf);
     const uint16_t* Ef = op.off_Ef ? reinterpret_cast<const uint16_t*>(a.ws + op.off_Ef) : nullptr;
     const uint16_t* Ff = op.off_Ff ? reinterpret_cast<const uint16_t*>(a.ws + op.off_Ff) : nullptr;
-    const bool hasF = Ff != nullptr;
     float* Sst = wsf(op.off_Sst);
     float* Dst = wsf(op.off_Dst);
     constexpr int PB = DK + 8;  // LDS pitch of the bf16 state rows (elements)
@@ -601,42 +620,55 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs a, ChainOps rev_
     __shared__ __align__(16) uint16_t Sbh[16 * PB], Sbl[16 * PB];  // the same rows, bf16 hi and lo
     __shared__ __align__(16) float dsm[16 * DP];  // Delta^T [state row][chunk row]
 
-    // this wave's operand quarters, one chunk ahead
+    // this wave's operand quarters, one chunk ahead.  K^ and Q^ enter as raw
+    // rows (Y of the reverse direction, Z of the forward one, F): their row
+    // scales D r_k are applied in fp32, to the product S Y^T in reverse and to
+    // Delta^T forward, and r_q is folded into E.  With bf16 inputs (EXACT) the
+    // raw rows are exact in bf16, so only their hi parts are loaded and
+    // multiplied: two products per fragment pair instead of three.
     u32x4 yr[DKS][2];     // Y fragments of chunk rows 16 w .., k-step ks, hi / lo
     u32x4 zr[NT][2][2];   // Z fragments of column tiles w NT + tt, k-step ks, hi / lo
     u32x4 fr[NT][2][2];   // F fragments, likewise
     u32x4 er[2][2];       // E^T fragments of this row block, k-step ks, hi / lo
     f32x4 xr;             // X[16 w + l16][16 rb + 4 g .. + 3]
-    float gl = 0.f;
+    float gl = 0.f;       // gamma_L of the chunk
+    float scv = 1.f;      // D r_k of chunk row 16 w + l16
+    const float* scb = wsf(a.lay.off_sck);
     const int64_t fper = (int64_t)BC * DK * 2;
-    auto load_y = [&](int64_t ch) {
+    // (REV: the reverse direction, whose Y and F are raw rows; the forward
+    // direction's Z is)
+    auto load_y = [&](int64_t ch, auto rev_c) {
+        constexpr int NPART = decltype(rev_c)::value && EXACT ? 1 : 2;
         const uint16_t* p = Yr + ch * fper + lane * 8;
 #pragma unroll
         for (int ks = 0; ks < DKS; ++ks)
 #pragma unroll
-            for (int part = 0; part < 2; ++part)
+            for (int part = 0; part < NPART; ++part)
                 yr[ks][part] = *reinterpret_cast<const u32x4*>(p + ((w * DKS + ks) * 2 + part) * 512);
         xr = *reinterpret_cast<const f32x4*>(Xb + (ch * BC + 16 * w + l16) * dv + rb * 16 + 4 * g);
         gl = gamv[ch * BC + BC - 1];
+        scv = scb[ch * BC + 16 * w + l16];
     };
-    auto load_z = [&](int64_t ch) {
+    auto load_z = [&](int64_t ch, auto rev_c) {
+        constexpr int NPART = !decltype(rev_c)::value && EXACT ? 1 : 2;
         const uint16_t* p = Zf + ch * fper + lane * 8;
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-                for (int part = 0; part < 2; ++part)
+                for (int part = 0; part < NPART; ++part)
                     zr[tt][ks][part] = *reinterpret_cast<const u32x4*>(p + (((w * NT + tt) * 2 + ks) * 2 + part) * 512);
     };
     auto load_f = [&](int64_t ch) {
+        constexpr int NPART = EXACT ? 1 : 2;
         const uint16_t* p = Ff + ch * fper + lane * 8;
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-                for (int part = 0; part < 2; ++part)
+                for (int part = 0; part < NPART; ++part)
                     fr[tt][ks][part] = *reinterpret_cast<const u32x4*>(p + (((w * NT + tt) * 2 + ks) * 2 + part) * 512);
         const uint16_t* pe = Ef + ch * (int64_t)BC * dv * 2 + lane * 8;
 #pragma unroll
@@ -646,29 +678,34 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs a, ChainOps rev_
                 er[ks][part] = *reinterpret_cast<const u32x4*>(pe + ((rb * 2 + ks) * 2 + part) * 512);
     };
 
-    // L2 prefetch two chunks ahead: the operands the chain reads for one chunk
-    // (Y, Z, E and F, 64 x DK / dv each), cut into 1 KB pieces, this
-    // workgroup's share of the pair's pieces, one 16-byte load per lane; the
-    // loaded words are folded into a register two chunks later (kept alive
-    // to the end), so no wait is added before they arrive
-    constexpr int OPB = BC * DK * 4 / 1024;  // 1 KB pieces of one d_k operand
+    // L2 prefetch two chunks ahead: the operand bytes the chain reads for one
+    // chunk (Y, Z, F and E; of a hi-only operand its hi parts, every other
+    // 1 KB block), cut into 1 KB pieces, this workgroup's share of the pair's
+    // pieces, one 16-byte load per lane; the loaded words are folded into a
+    // register two chunks later (kept alive to the end), so no wait is added
+    // before they arrive.  A piece beyond this workgroup's share reloads the
+    // chunk's first Y piece: every lane loads on every step, with no branch
+    // around the loads.
+    constexpr int OPB = BC * DK * 4 / 1024;  // 1 KB blocks of one d_k operand (hi and lo)
     const int eb = BC * dv * 4 / 1024;       // of E
-    const int npiece = 2 * OPB + (hasF ? OPB + eb : 0);
-    const int per_wg = (npiece + RB - 1) / RB, per_wave = (per_wg + 3) / 4;
     uint32_t pf_acc = 0;
     u32x4 pf[2][4];
-    // (a piece beyond this workgroup's share reloads the chunk's first Y piece:
-    // every lane loads on every step, with no branch around the loads)
-    auto prefetch = [&](int64_t ch, u32x4* dst) {
+    auto prefetch = [&](int64_t ch, u32x4* dst, auto rev_c) {
+        constexpr bool REV = decltype(rev_c)::value;
+        constexpr int SY = REV && EXACT ? 2 : 1, SZ = !REV && EXACT ? 2 : 1, SF = EXACT ? 2 : 1;
+        constexpr int NY = OPB / SY, NZ = OPB / SZ, NF = REV ? OPB / SF : 0;
+        const int npiece = NY + NZ + NF + (REV ? eb : 0);
+        const int per_wg = (npiece + RB - 1) / RB, per_wave = (per_wg + 3) / 4;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int q0 = rb * per_wg + w * per_wave + i;
             const bool mine = i < per_wave && q0 < npiece && (w * per_wave + i) < per_wg;
             const int q = mine ? q0 : 0;
-            const uint16_t* base = q < OPB ? Yr : q < 2 * OPB ? Zf : q < 3 * OPB ? Ff : Ef;
-            const int64_t per = q < 3 * OPB ? fper : (int64_t)BC * dv * 2;
-            const int qq = q < OPB ? q : q < 2 * OPB ? q - OPB : q < 3 * OPB ? q - 2 * OPB : q - 3 * OPB;
-            const unsigned char* src = reinterpret_cast<const unsigned char*>(base + ch * per) + qq * 1024;
+            const uint16_t* base = q < NY ? Yr : q < NY + NZ ? Zf : q < NY + NZ + NF ? Ff : Ef;
+            const int64_t per = q < NY + NZ + NF ? fper : (int64_t)BC * dv * 2;
+            const int blk = q < NY ? q * SY : q < NY + NZ ? (q - NY) * SZ : q < NY + NZ + NF ? (q - NY - NZ) * SF
+                                                                                           : q - NY - NZ - NF;
+            const unsigned char* src = reinterpret_cast<const unsigned char*>(base + ch * per) + blk * 1024;
             dst[i] = *reinterpret_cast<const u32x4*>(src + lane * 16);
         }
     };
@@ -684,20 +721,16 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs a, ChainOps rev_
     const int c0 = seq_first[n], c1 = seq_first[n + 1];
     const int steps = c1 - c0;
     auto chunk_of = [&](int it) -> int64_t { return (int64_t)(reverse ? c1 - 1 - it : c0 + it) * H + h; };
-    if (steps > 0) {
-        load_y(chunk_of(0));
-        load_z(chunk_of(0));
-        if (hasF) load_f(chunk_of(0));
-    }
     // one chunk; the loop below runs two per iteration, so that each uses a
     // fixed prefetch slot (a slot picked by it & 1 is a dynamic register index,
     // which the compiler serves with a wait for every load in flight)
-    auto chunk_step = [&](int it, u32x4* slot, auto hasF_c) __attribute__((always_inline)) {
+    auto chunk_step = [&](int it, u32x4* slot, auto rev_c) __attribute__((always_inline)) {
+        constexpr bool REV = decltype(rev_c)::value;
         const int64_t ch = chunk_of(it);
         {
 #pragma unroll
             for (int i = 0; i < 4; ++i) pf_acc ^= slot[i].x ^ slot[i].w;
-            prefetch(chunk_of(min(it + 2, steps - 1)), slot);
+            prefetch(chunk_of(min(it + 2, steps - 1)), slot, rev_c);
         }
         // the state before the chunk: to LDS in fp32 (for the record) and split
         // into bf16 hi and lo (the A operand of S Y^T), then from its rows to the
@@ -730,16 +763,18 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs a, ChainOps rev_
             const u32x4 sl = *reinterpret_cast<const u32x4*>(Sbl + l16 * PB + 32 * ks + 8 * g);
             a0 = mma_bf16(sh, yr[ks][0], a0);
             a1 = mma_bf16(sl, yr[ks][0], a1);
-            a2 = mma_bf16(sh, yr[ks][1], a2);
+            if constexpr (!(REV && EXACT)) a2 = mma_bf16(sh, yr[ks][1], a2);
         }
         const f32x4 acc = a0 + a1 + a2;
-        // lane holds state rows 4 g + i of chunk row 16 w + l16
-        const f32x4 d = xr + ysign * acc;
+        // lane holds state rows 4 g + i of chunk row 16 w + l16; in reverse Y is
+        // the raw k rows (the product takes their scale D r_k here), forward
+        // Delta^T takes it for the raw k rows of Z
+        const f32x4 d = REV ? xr + ysign * (acc * scv) : xr + ysign * acc;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dsm[(4 * g + i) * DP + 16 * w + l16] = d[i];
+        for (int i = 0; i < 4; ++i) dsm[(4 * g + i) * DP + 16 * w + l16] = REV ? d[i] : d[i] * scv;
         *reinterpret_cast<f32x4*>(Dst + (ch * BC + 16 * w + l16) * dv + rb * 16 + 4 * g) = d;
         const float decay = expf(gl);
-        load_y(chunk_of(min(it + 1, steps - 1)));
+        load_y(chunk_of(min(it + 1, steps - 1)), rev_c);
         __syncthreads();  // ---- Delta^T in LDS; the state rows read
         // S <- e^{gamma_L} S + zsign Delta^T Z (+ E^T F)
 #pragma unroll
@@ -750,14 +785,18 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs a, ChainOps rev_
             u32x4 dh, dl;
             split8(zsign * *reinterpret_cast<const f32x4*>(dp), zsign * *reinterpret_cast<const f32x4*>(dp + 4), dh, dl);
 #pragma unroll
-            for (int tt = 0; tt < NT; ++tt) sreg[tt] = mma3(dh, dl, zr[tt][ks][0], zr[tt][ks][1], sreg[tt]);
+            for (int tt = 0; tt < NT; ++tt)
+                sreg[tt] = !REV && EXACT ? mma2(dh, dl, zr[tt][ks][0], sreg[tt])
+                                         : mma3(dh, dl, zr[tt][ks][0], zr[tt][ks][1], sreg[tt]);
         }
-        load_z(chunk_of(min(it + 1, steps - 1)));
-        if constexpr (decltype(hasF_c)::value) {
+        load_z(chunk_of(min(it + 1, steps - 1)), rev_c);
+        if constexpr (REV) {
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-                for (int tt = 0; tt < NT; ++tt) sreg[tt] = mma3(er[ks][0], er[ks][1], fr[tt][ks][0], fr[tt][ks][1], sreg[tt]);
+                for (int tt = 0; tt < NT; ++tt)
+                    sreg[tt] = EXACT ? mma2(er[ks][0], er[ks][1], fr[tt][ks][0], sreg[tt])
+                                     : mma3(er[ks][0], er[ks][1], fr[tt][ks][0], fr[tt][ks][1], sreg[tt]);
             load_f(chunk_of(min(it + 1, steps - 1)));
         }
     };
@@ -765,15 +804,20 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs a, ChainOps rev_
     for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
         for (int i = 0; i < 4; ++i) pf[b2][i] = u32x4{0u, 0u, 0u, 0u};
-    // the two directions as separate loops: the E^T F term and its loads are
-    // compiled in or out, never branched around
-    auto run = [&](auto hasF_c) __attribute__((always_inline)) {
+    // the two directions as separate loops: the E^T F term, the raw-row
+    // operands and their loads are compiled in or out, never branched around
+    auto run = [&](auto rev_c) __attribute__((always_inline)) {
+        if (steps > 0) {
+            load_y(chunk_of(0), rev_c);
+            load_z(chunk_of(0), rev_c);
+            if constexpr (decltype(rev_c)::value) load_f(chunk_of(0));
+        }
         for (int it = 0; it < steps; it += 2) {
-            chunk_step(it, pf[0], hasF_c);
-            if (it + 1 < steps) chunk_step(it + 1, pf[1], hasF_c);
+            chunk_step(it, pf[0], rev_c);
+            if (it + 1 < steps) chunk_step(it + 1, pf[1], rev_c);
         }
     };
-    if (hasF)
+    if (is_rev)
         run(std::true_type{});
     else
         run(std::false_type{});
@@ -1090,7 +1134,10 @@ hipError_t launch_chain(const BwdArgs& a, const ChainOps& rev, const ChainOps& f
 {
     const int64_t blocks = (2 * (int64_t)a.N * a.H + 7) / 8 * 8 * (a.dv / 16);
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((bwd_chain_kernel<DK>), dim3((uint32_t)blocks), dim3(256), 0, a.stream, a, rev, fwd);
+    if (a.bf16)
+        hipLaunchKernelGGL((bwd_chain_kernel<DK, true>), dim3((uint32_t)blocks), dim3(256), 0, a.stream, a, rev, fwd);
+    else
+        hipLaunchKernelGGL((bwd_chain_kernel<DK, false>), dim3((uint32_t)blocks), dim3(256), 0, a.stream, a, rev, fwd);
     return hipGetLastError();
 }
 
@@ -1124,13 +1171,13 @@ hipError_t launch_backward(const BwdArgs& a)
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // forward: Delta = U - W S^T,  S <- e^{gamma_L} S + Delta^T (D K); records S and Delta
     ChainOps fwd;
-    fwd.off_X = L.off_U; fwd.off_Yr = L.off_Wr; fwd.off_Zf = L.off_DKf; fwd.off_Ef = 0; fwd.off_Ff = 0;
+    fwd.off_X = L.off_U; fwd.off_Yr = L.off_Wr; fwd.off_Zf = L.off_Kf; fwd.off_Ef = 0; fwd.off_Ff = 0;
     fwd.off_Sst = L.off_S; fwd.off_Dst = L.off_Dl;
     fwd.S_init = a.init_state; fwd.S_final = nullptr;
     fwd.ysign = -1.f; fwd.zsign = 1.f; fwd.reverse = 0;
     // reverse: dDelta = dDelta_local + (D K) dS^T,  dS <- e^{gamma_L} dS - dDelta^T W + E^T Q
     ChainOps rev;
-    rev.off_X = L.off_dDl; rev.off_Yr = L.off_DKr; rev.off_Zf = L.off_Wf; rev.off_Ef = L.off_Ef; rev.off_Ff = L.off_Qf;
+    rev.off_X = L.off_dDl; rev.off_Yr = L.off_Kr; rev.off_Zf = L.off_Wf; rev.off_Ef = L.off_Ef; rev.off_Ff = L.off_Qf;
     rev.off_Sst = L.off_dS; rev.off_Dst = L.off_dD;
     rev.S_init = a.dstate; rev.S_final = a.dinit;
     rev.ysign = 1.f; rev.zsign = -1.f; rev.reverse = 1;
