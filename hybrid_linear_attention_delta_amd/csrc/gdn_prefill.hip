@@ -1692,8 +1692,13 @@ struct ChainKrLds {
 // workgroup -> (pair, row tile) mapping and the segment logic are those of
 // chain_kernel.  PIPE: the one launch of the pipelined prefill, whose loaders
 // and store waves also take the hand-offs of PipeSync.
+// At most 120 VGPRs per lane: the 16 waves of a workgroup take 4 x 120 of a
+// SIMD's 512, so a chain workgroup still fits on a CU where a one-wave
+// hand-off kernel (pipe_wait_kernel, 5 VGPRs) runs.  That wave waits for the
+// chain, so a chain workgroup that could not start beside it would never let
+// it finish.
 template <int DK, int DV, bool SEG, bool PIPE>
-__global__ __launch_bounds__(1024) void chain_kr_kernel(
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_num_vgpr(120))) void chain_kr_kernel(
     const int32_t* __restrict__ header, const int32_t* __restrict__ seq_first,
     const int32_t* __restrict__ seq_order, int32_t varlen, int64_t T, int32_t H, int32_t pairs,
     const unsigned char* records, size_t record_bytes, const float* init_state, float* final_state,
@@ -2227,12 +2232,16 @@ __global__ __launch_bounds__(256) void output_kernel(const int32_t* __restrict__
 // Streams and events of the pipelined prefill, owned by the caller through
 // gdn_context_create / gdn_context_destroy (default priority; the CU-masked
 // streams synchronise with the legacy default stream, the unmasked fallback
-// streams do not).  The state chain gets a stream
-// of its own, CU-masked to the same number of CUs on every XCD, and the
-// per-segment intra-chunk and output kernels two more streams on all other
-// CUs: the chain's workgroups then never share a CU with the parallel kernels
-// and never wait for one to drain.  CU mask bit i is CU i / 8 of XCD i % 8
-// (CU masks number the CUs round-robin over the XCDs).
+// streams do not).  The state chain gets a stream of its own, CU-masked to the
+// same number of CUs on every XCD (CU mask bit i is CU i / 8 of XCD i % 8: the
+// masks number the CUs round-robin over the XCDs), and the per-segment
+// intra-chunk and output kernels two more streams, masked to every CU: so each
+// stream owns a hardware queue, and the side kernels also use the reserved
+// CUs that hold no chain workgroup (at six (sequence, head) pairs, those of
+// two XCDs) and every CU before the chain's launch and after its end.  The one
+// chain launch of the pipeline holds its CUs from start to end, and nothing
+// on the side streams waits while holding a CU except one-wave hand-off
+// kernels, beside which a chain workgroup still fits (its VGPR cap).
 struct gdn_context {
     static constexpr int MAX_SEG = 16;
     std::mutex use;  // held while one call enqueues its pipeline: the events are reused by every call
@@ -2287,16 +2296,16 @@ hipError_t context_create(int32_t chain_cus_per_xcd, gdn_context** out)
         return err;
     };
     if (cus == 256) {
-        uint32_t mine[8] = {0, 0, 0, 0, 0, 0, 0, 0}, rest[8];
+        uint32_t mine[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        const uint32_t all[8] = {~0u, ~0u, ~0u, ~0u, ~0u, ~0u, ~0u, ~0u};
         for (int x = 0; x < 8; ++x)
             for (int c = 0; c < per_xcd; ++c) {
                 const int bit = x + 8 * c;
                 mine[bit >> 5] |= 1u << (bit & 31);
             }
-        for (int w = 0; w < 8; ++w) rest[w] = ~mine[w];
         if ((e = hipExtStreamCreateWithCUMask(&r->chain_s, 8, mine)) != hipSuccess) return fail(e);
-        if ((e = hipExtStreamCreateWithCUMask(&r->intra_s, 8, rest)) != hipSuccess) return fail(e);
-        if ((e = hipExtStreamCreateWithCUMask(&r->out_s, 8, rest)) != hipSuccess) return fail(e);
+        if ((e = hipExtStreamCreateWithCUMask(&r->intra_s, 8, all)) != hipSuccess) return fail(e);
+        if ((e = hipExtStreamCreateWithCUMask(&r->out_s, 8, all)) != hipSuccess) return fail(e);
         r->masked = true;
     } else {
         if ((e = hipStreamCreateWithFlags(&r->chain_s, hipStreamNonBlocking)) != hipSuccess) return fail(e);
@@ -2519,7 +2528,14 @@ static hipError_t run_prefill(const PrefillArgs& a)
     const int64_t chain_per_xcd = ((pairs + 7) / 8) * (DV / 16);
     gdn_context* pr = a.ctx;
     int nseg = 1;
-    if (pr && a.stages == 7 && chain_per_xcd <= pr->chain_cus && grid_chunks >= PIPE_MIN_CHUNKS)
+    // Under stream capture the call runs stage by stage: a graph's executor may
+    // run the pipeline's branches in sequence, so the device-memory hand-offs
+    // are out, and the event-ordered schedule measured no faster than stage by
+    // stage when replayed (1.92 against 1.92 ms at 64K tokens).
+    hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+    GDN_TRY(hipStreamIsCapturing(a.stream, &capture));
+    if (pr && a.stages == 7 && chain_per_xcd <= pr->chain_cus && grid_chunks >= PIPE_MIN_CHUNKS &&
+        capture == hipStreamCaptureStatusNone)
         nseg = (grid_chunks >= GEOM_MIN_CHUNKS && !a.norm.z) ? 6 : 4;
     if (nseg == 1) {
         if (a.stages & 1) GDN_TRY(launch_intra(0, grid_chunks, a.stream));
@@ -2556,14 +2572,10 @@ static hipError_t run_prefill(const PrefillArgs& a)
     // each segment's flag; the output kernel finishes every segment, in order,
     // on the other, each behind a wait for the chain's store waves.
     // A wait in device memory needs its producer to run beside it: masked
-    // streams each own a hardware queue, while a graph's executor, or streams
-    // that share a queue, may run the two in sequence.  Those cases keep the
-    // event-ordered schedule below, and so does the gated read-out, whose
-    // heavier output kernel measured faster there (1.83 against 1.89 ms at
-    // 64K tokens; the plain read-out 1.733 against 1.744 ms the other way).
-    hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
-    GDN_TRY(hipStreamIsCapturing(a.stream, &capture));
-    if (sizeof(TIn) == 2 && pr->masked && capture == hipStreamCaptureStatusNone && !a.norm.z) {
+    // streams each own a hardware queue, while streams that share a queue may
+    // run the two in sequence.  Unmasked contexts (and the fp32 chain) keep the
+    // event-ordered schedule below.
+    if (sizeof(TIn) == 2 && pr->masked) {
         PipeSync ps{};
         ps.flags = reinterpret_cast<uint32_t*>(header) + 16;
         ps.nseg = nseg;
