@@ -150,6 +150,91 @@ __device__ __forceinline__ void zero(float acc[4][4])
         for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
 }
 
+// Three products that share their B operands, in one pass over k:
+//   p1 = A1 B1,  p2 = A2 B1,  p3 = A3 B2   (64 x 64 blocks, [n0, n0 + 64) of B),
+// A_i[r][k] rows along k (pitch lda), B_i[k][n] rows along n (pitch ldb), and
+// dot += sum over the block of B1 o B2, each element counted once over the
+// calls for all n0.  The same tiling and 16-byte loads as mm64 (KT = 32),
+// with the next k block's loads in flight during the current products; every
+// B1 and B2 element crosses from memory once instead of once per product.
+// ls holds 5 KT x LD floats (A1, A2, A3, B1, B2).
+__device__ void mm64x3(float p1[4][4], float p2[4][4], float p3[4][4], float& dot, const float* __restrict__ A1,
+                       const float* __restrict__ A2, const float* __restrict__ A3, int lda,
+                       const float* __restrict__ B1, const float* __restrict__ B2, int ldb, int K, int n0, float* ls)
+{
+    constexpr int KT = 32, NV = KT / 16;
+    int t = threadIdx.x;
+    asm volatile("" : "+v"(t));  // per-call lane offsets: recomputed here, not hoisted and held across calls
+    const int w = t >> 6, l = t & 63, r16 = l & 15, g = l >> 4;
+    float* const la[3] = {ls, ls + KT * LD, ls + 2 * KT * LD};
+    float* const lb[2] = {ls + 3 * KT * LD, ls + 4 * KT * LD};
+    f32x4 d[3][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        d[0][j] = f32x4{p1[0][j], p1[1][j], p1[2][j], p1[3][j]};
+        d[1][j] = f32x4{p2[0][j], p2[1][j], p2[2][j], p2[3][j]};
+        d[2][j] = f32x4{p3[0][j], p3[1][j], p3[2][j], p3[3][j]};
+    }
+    const float* const A[3] = {A1, A2, A3};
+    const float* const B[2] = {B1, B2};
+    f32x4 xa[3][NV], xb[2][NV];
+    auto fetch = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int e = t + 256 * i;
+            const int r = e / (KT / 4), kq = e % (KT / 4);
+#pragma unroll
+            for (int m = 0; m < 3; ++m)
+                xa[m][i] = *reinterpret_cast<const f32x4*>(A[m] + (int64_t)r * lda + k0 + 4 * kq);
+            const int kk = e >> 4, nq = e & 15;
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+                xb[m][i] = *reinterpret_cast<const f32x4*>(B[m] + (int64_t)(k0 + kk) * ldb + n0 + 4 * nq);
+        }
+    };
+    float acc_dot = 0.f;
+    fetch(0);
+    for (int k0 = 0; k0 < K; k0 += KT) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int e = t + 256 * i;
+            const int r = e / (KT / 4), kq = e % (KT / 4);
+#pragma unroll
+            for (int m = 0; m < 3; ++m)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) la[m][(4 * kq + q) * LD + r] = xa[m][i][q];
+#pragma unroll
+            for (int m = 0; m < 2; ++m) *reinterpret_cast<f32x4*>(lb[m] + (e >> 4) * LD + 4 * (e & 15)) = xb[m][i];
+            acc_dot += xb[0][i].x * xb[1][i].x + xb[0][i].y * xb[1][i].y + xb[0][i].z * xb[1][i].z +
+                       xb[0][i].w * xb[1][i].w;
+        }
+        __syncthreads();
+        if (k0 + KT < K) fetch(k0 + KT);  // the next block's loads fly during these products
+#pragma unroll
+        for (int kq = 0; kq < KT / 4; ++kq) {
+            const int kr = (4 * kq + g) * LD;
+            const float a0 = la[0][kr + 16 * w + r16], a1 = la[1][kr + 16 * w + r16], a2 = la[2][kr + 16 * w + r16];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float b1 = lb[0][kr + 16 * j + r16], b2 = lb[1][kr + 16 * j + r16];
+                d[0][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b1, d[0][j], 0, 0, 0);
+                d[1][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b1, d[1][j], 0, 0, 0);
+                d[2][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a2, b2, d[2][j], 0, 0, 0);
+            }
+        }
+        __syncthreads();
+    }
+    dot += acc_dot;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            p1[i][j] = d[0][j][i];
+            p2[i][j] = d[1][j][i];
+            p3[i][j] = d[2][j][i];
+        }
+}
+
 // Per chunk-head slices of the workspace.
 struct Slices {
     float *Q, *K, *V, *dO, *rq, *rk, *gam, *bet, *T, *P, *KKG, *W, *U, *Kraw, *Qraw, *E, *dDl, *sck;
@@ -847,6 +932,7 @@ __global__ __launch_bounds__(256, 3) void bwd_grad_kernel(BwdArgs a)
     const float scale = a.scale;
     Slices s = slices(a, b);
     __shared__ __align__(16) float as[KTG * LD], bs[KTG * LD];
+    __shared__ __align__(16) float ls3[5 * 32 * LD];  // the fused pass over S and dS
     __shared__ float gam[BC], bet[BC], eg[BC], dd[BC], bge[BC], dgam[BC], dbet[BC];
     __shared__ float red[4];
     __shared__ float cs[16][BC];
@@ -890,26 +976,37 @@ __global__ __launch_bounds__(256, 3) void bwd_grad_kernel(BwdArgs a)
         __syncthreads();
     };
 
-    // e^{gamma_L} <dS, S>: part of the gradient of gamma_L, reduced over the
-    // workgroup after the column blocks below
+    // One pass over the 64-column blocks of S and dS: each block crosses from
+    // memory once for the three products that read it,
+    //   dO S -> the first term of dQ,  -dDelta S -> dW,  Delta dS -> the first term of dK,
+    // and e^{gamma_L} <dS, S> (part of the gradient of gamma_L) from the same
+    // registers.  dQ and dK are stored partial here and completed below; the
+    // row sums Q_r . (scale e^gamma dO S)_r -> dgamma_r and K_r . (Delta dS)_r ->
+    // -D_r dgamma_r and gamma_L are taken now.
     float dgL = 0.f;
+    float rq[4] = {0.f, 0.f, 0.f, 0.f}, rk[4] = {0.f, 0.f, 0.f, 0.f}, rt[4] = {0.f, 0.f, 0.f, 0.f};
     {
-        const int64_t n4 = (int64_t)dv * dk / 4;
-        const f32x4* S4 = reinterpret_cast<const f32x4*>(s.S);
-        const f32x4* dS4 = reinterpret_cast<const f32x4*>(s.dS);
-        float x = 0.f;
-        for (int64_t e0 = t; e0 < n4; e0 += 256 * 8) {  // eight vector pairs in flight per thread
-            f32x4 u[8], w[8];
+        float dot = 0.f;
+        for (int n0 = 0; n0 < dk; n0 += 64) {
+            float pq[4][4], pw[4][4];
+            zero(acc);
+            zero(pq);
+            zero(pw);
+            mm64x3(pq, pw, acc, dot, s.dO, s.dD, s.Dl, dv, s.S, s.dS, dk, dv, n0, ls3);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int64_t e = e0 + 256 * j;
-                u[j] = e < n4 ? S4[e] : f32x4{0.f, 0.f, 0.f, 0.f};
-                w[j] = e < n4 ? dS4[e] : f32x4{0.f, 0.f, 0.f, 0.f};
-            }
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) x += u[j].x * w[j].x + u[j].y * w[j].y + u[j].z * w[j].z + u[j].w * w[j].w;
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 4 * tr + i, n = n0 + 16 * j + tc;
+                    const float x = scale * eg[r] * pq[i][j];
+                    rq[i] += s.Q[r * dk + n] * x;
+                    s.dQ[r * dk + n] = x;
+                    s.dW[r * dk + n] = -pw[i][j];
+                    rk[i] += s.K[r * dk + n] * acc[i][j];
+                    s.dK[r * dk + n] = dd[r] * acc[i][j];
+                }
         }
-        dgL += expf(gam[BC - 1]) * x;
+        dgL += expf(gam[BC - 1]) * dot;
     }
     // dP = scale lower(dO Delta^T);  dgamma from P;  dPG = dP o Gamma
     zero(acc);
@@ -930,15 +1027,6 @@ __global__ __launch_bounds__(256, 3) void bwd_grad_kernel(BwdArgs a)
             }
         row_add(dgam, 1.f);
         col_sub(dgam, colp);  // its barriers also complete dPG
-    }
-    // dW = -(dDelta S)
-    for (int n0 = 0; n0 < dk; n0 += 64) {
-        zero(acc);
-        mm64<KTG, true, true>(acc, s.dD, dv, nullptr, s.S, dk, dv, n0, as, bs);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) s.dW[(4 * tr + i) * dk + n0 + 16 * j + tc] = -acc[i][j];
     }
     __syncthreads();  // dW complete
     // dT = (dDelta V^T) diag(beta) + (dW K^T) diag(beta e^gamma)
@@ -1006,24 +1094,16 @@ __global__ __launch_bounds__(256, 3) void bwd_grad_kernel(BwdArgs a)
         row_add(dbet, 1.f);
         col_sub(dgam, colp);  // its barriers also complete Bd
     }
-    // dQ and dK (before the norms), one 64-column block at a time, every term
-    // accumulated in registers and stored once:
-    //   dQ = scale e^gamma (dO S) + dPG K
-    //   dK = D (Delta dS) + dPG^T Q + diag(beta e^gamma) T^T dW + Bd K + Bd^T K
-    // with the row sums  Q_r . (scale e^gamma dO S)_r -> dgamma_r,
-    // K_r . (Delta dS)_r -> -D_r dgamma_r and gamma_L, (T^T dW)_r . K_r -> dbeta, dgamma.
-    float rq[4] = {0.f, 0.f, 0.f, 0.f}, rk[4] = {0.f, 0.f, 0.f, 0.f}, rt[4] = {0.f, 0.f, 0.f, 0.f};
+    // dQ and dK (before the norms) completed one 64-column block at a time,
+    // onto the partial blocks of the pass above:
+    //   dQ += dPG K
+    //   dK += diag(beta e^gamma) T^T dW + dPG^T Q + Bd K + Bd^T K
+    // with the row sums (T^T dW)_r . K_r -> dbeta, dgamma.
     for (int n0 = 0; n0 < dk; n0 += 64) {
-        zero(acc);
-        mm64<KTG, true, true>(acc, s.dO, dv, nullptr, s.S, dk, dv, n0, as, bs);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 4 * tr + i, n = n0 + 16 * j + tc;
-                acc[i][j] *= scale * eg[r];
-                rq[i] += s.Q[r * dk + n] * acc[i][j];
-            }
+            for (int j = 0; j < 4; ++j) acc[i][j] = s.dQ[(4 * tr + i) * dk + n0 + 16 * j + tc];
         mm64<KTG, true, true>(acc, s.dPG, BC, nullptr, s.K, dk, BC, n0, as, bs);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -1033,17 +1113,13 @@ __global__ __launch_bounds__(256, 3) void bwd_grad_kernel(BwdArgs a)
         float acc2[4][4];
         zero(acc2);
         mm64<KTG, false, true>(acc2, s.T, BC, nullptr, s.dW, dk, BC, n0, as, bs);
-        zero(acc);
-        mm64<KTG, true, true>(acc, s.Dl, dv, nullptr, s.dS, dk, dv, n0, as, bs);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int r = 4 * tr + i;
-                const float kx = s.K[r * dk + n0 + 16 * j + tc];
-                rk[i] += kx * acc[i][j];
-                rt[i] += kx * acc2[i][j];
-                acc[i][j] = acc[i][j] * dd[r] + bge[r] * acc2[i][j];
+                const int r = 4 * tr + i, n = n0 + 16 * j + tc;
+                rt[i] += s.K[r * dk + n] * acc2[i][j];
+                acc[i][j] = s.dK[r * dk + n] + bge[r] * acc2[i][j];
             }
         mm64<KTG, false, true>(acc, s.dPG, BC, nullptr, s.Q, dk, BC, n0, as, bs);
         mm64<KTG, true, true>(acc, s.Bd, BC, nullptr, s.K, dk, BC, n0, as, bs);
