@@ -67,12 +67,22 @@ constexpr int KTG = 32;  // and in the gradient kernel
 // sums): wave w computes rows 16 w .. 16 w + 15 as four 16 x 16 tiles, and its
 // accumulator layout (lane l: rows 4 (l / 16) + i, column l % 16 of each tile)
 // is the (r, n) map above.
-template <int KT, bool AK, bool BN>
-__device__ void mm64(float acc[4][4], const float* __restrict__ A, int lda, const float* kscale,
-                     const float* __restrict__ B, int ldb, int K, int n0, float* as, float* bs)
+// bf16 bits of eight consecutive values -> widened into LDS at dst[q * stride], q = 0..7
+__device__ __forceinline__ void put8_col(float* dst, int stride, u16x8 x)
 {
-    static_assert(KT % 16 == 0, "a k block is a whole number of 16-byte loads per thread");
-    constexpr int NV = KT / 16;  // 16-byte loads per operand and thread
+#pragma unroll
+    for (int q = 0; q < 8; ++q) dst[q * stride] = bf16_bits_to_f32(x[q]);
+}
+
+template <int KT, bool AK, bool BN, typename TA = float, typename TB = float>
+__device__ void mm64(float acc[4][4], const TA* __restrict__ A, int lda, const float* kscale,
+                     const TB* __restrict__ B, int ldb, int K, int n0, float* as, float* bs)
+{
+    static_assert(KT % 32 == 0, "a k block is a whole number of 16-byte loads per thread");
+    static_assert(sizeof(TA) == 4 || AK, "bf16 A operands have rows along k");
+    constexpr int NV = KT / 16;   // 16-byte loads per fp32 operand and thread
+    constexpr int NB = KT / 32;   // 16-byte loads per bf16 operand and thread (eight values)
+    constexpr bool A16 = sizeof(TA) == 2, B16 = sizeof(TB) == 2;
     int t = threadIdx.x;
     asm volatile("" : "+v"(t));  // per-call lane offsets: recomputed here, not hoisted and held across calls
     const int w = t >> 6, l = t & 63, r16 = l & 15, g = l >> 4;
@@ -80,49 +90,114 @@ __device__ void mm64(float acc[4][4], const float* __restrict__ A, int lda, cons
 #pragma unroll
     for (int j = 0; j < 4; ++j) d[j] = f32x4{acc[0][j], acc[1][j], acc[2][j], acc[3][j]};
     f32x4 xa[NV], xb[NV];
+    u16x8 ya[NB], yb[NB];
     auto fetch = [&](int k0) {  // the 64 x KT block of A and the KT x 64 block of B into registers
+        if constexpr (A16) {
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int e = t + 256 * i;
-            if constexpr (AK) {  // KT / 4 lanes read one row's k block
-                const int r = e / (KT / 4), kq = e % (KT / 4);
-                xa[i] = *reinterpret_cast<const f32x4*>(A + (int64_t)r * lda + k0 + 4 * kq);
-                if (kscale) {
-                    const f32x4 s4 = *reinterpret_cast<const f32x4*>(kscale + k0 + 4 * kq);
-                    xa[i] *= s4;
-                }
-            } else {  // sixteen lanes read one k row of 64
-                const int kk = e >> 4, rq = e & 15;
-                xa[i] = *reinterpret_cast<const f32x4*>(A + (int64_t)(k0 + kk) * lda + 4 * rq);
-                if (kscale) xa[i] *= kscale[k0 + kk];
+            for (int i = 0; i < NB; ++i) {  // KT / 8 lanes read one row's k block
+                const int e = t + 256 * i, r = e / (KT / 8), k8 = e % (KT / 8);
+                ya[i] = *reinterpret_cast<const u16x8*>(A + (int64_t)r * lda + k0 + 8 * k8);
             }
-            if constexpr (BN) {
-                const int kk = e >> 4, nq = e & 15;
-                xb[i] = *reinterpret_cast<const f32x4*>(B + (int64_t)(k0 + kk) * ldb + n0 + 4 * nq);
-            } else {
-                const int n = e / (KT / 4), kq = e % (KT / 4);
-                xb[i] = *reinterpret_cast<const f32x4*>(B + (int64_t)(n0 + n) * ldb + k0 + 4 * kq);
+        } else {
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                const int e = t + 256 * i;
+                if constexpr (AK) {  // KT / 4 lanes read one row's k block
+                    const int r = e / (KT / 4), kq = e % (KT / 4);
+                    xa[i] = *reinterpret_cast<const f32x4*>(A + (int64_t)r * lda + k0 + 4 * kq);
+                    if (kscale) {
+                        const f32x4 s4 = *reinterpret_cast<const f32x4*>(kscale + k0 + 4 * kq);
+                        xa[i] *= s4;
+                    }
+                } else {  // sixteen lanes read one k row of 64
+                    const int kk = e >> 4, rq = e & 15;
+                    xa[i] = *reinterpret_cast<const f32x4*>(A + (int64_t)(k0 + kk) * lda + 4 * rq);
+                    if (kscale) xa[i] *= kscale[k0 + kk];
+                }
+            }
+        }
+        if constexpr (B16) {
+#pragma unroll
+            for (int i = 0; i < NB; ++i) {
+                const int e = t + 256 * i;
+                if constexpr (BN) {  // eight lanes read one k row of 64
+                    const int kk = e >> 3, n8 = e & 7;
+                    yb[i] = *reinterpret_cast<const u16x8*>(B + (int64_t)(k0 + kk) * ldb + n0 + 8 * n8);
+                } else {
+                    const int n = e / (KT / 8), k8 = e % (KT / 8);
+                    yb[i] = *reinterpret_cast<const u16x8*>(B + (int64_t)(n0 + n) * ldb + k0 + 8 * k8);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                const int e = t + 256 * i;
+                if constexpr (BN) {
+                    const int kk = e >> 4, nq = e & 15;
+                    xb[i] = *reinterpret_cast<const f32x4*>(B + (int64_t)(k0 + kk) * ldb + n0 + 4 * nq);
+                } else {
+                    const int n = e / (KT / 4), kq = e % (KT / 4);
+                    xb[i] = *reinterpret_cast<const f32x4*>(B + (int64_t)(n0 + n) * ldb + k0 + 4 * kq);
+                }
             }
         }
     };
     fetch(0);
     for (int k0 = 0; k0 < K; k0 += KT) {
+        if constexpr (A16) {
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int e = t + 256 * i;
-            if constexpr (AK) {
-                const int r = e / (KT / 4), kq = e % (KT / 4);
+            for (int i = 0; i < NB; ++i) {
+                const int e = t + 256 * i, r = e / (KT / 8), k8 = e % (KT / 8);
+                if (kscale) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) as[(4 * kq + q) * LD + r] = xa[i][q];
-            } else {
-                *reinterpret_cast<f32x4*>(as + (e >> 4) * LD + 4 * (e & 15)) = xa[i];
+                    for (int q = 0; q < 8; ++q) as[(8 * k8 + q) * LD + r] = bf16_bits_to_f32(ya[i][q]) * kscale[k0 + 8 * k8 + q];
+                } else {
+                    put8_col(as + (8 * k8) * LD + r, LD, ya[i]);
+                }
             }
-            if constexpr (BN) {
-                *reinterpret_cast<f32x4*>(bs + (e >> 4) * LD + 4 * (e & 15)) = xb[i];
-            } else {
-                const int n = e / (KT / 4), kq = e % (KT / 4);
+        } else {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) bs[(4 * kq + q) * LD + n] = xb[i][q];
+            for (int i = 0; i < NV; ++i) {
+                const int e = t + 256 * i;
+                if constexpr (AK) {
+                    const int r = e / (KT / 4), kq = e % (KT / 4);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) as[(4 * kq + q) * LD + r] = xa[i][q];
+                } else {
+                    *reinterpret_cast<f32x4*>(as + (e >> 4) * LD + 4 * (e & 15)) = xa[i];
+                }
+            }
+        }
+        if constexpr (B16) {
+#pragma unroll
+            for (int i = 0; i < NB; ++i) {
+                const int e = t + 256 * i;
+                if constexpr (BN) {
+                    const int kk = e >> 3, n8 = e & 7;
+                    f32x4 lo, hi;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        lo[q] = bf16_bits_to_f32(yb[i][q]);
+                        hi[q] = bf16_bits_to_f32(yb[i][4 + q]);
+                    }
+                    *reinterpret_cast<f32x4*>(bs + kk * LD + 8 * n8) = lo;
+                    *reinterpret_cast<f32x4*>(bs + kk * LD + 8 * n8 + 4) = hi;
+                } else {
+                    const int n = e / (KT / 8), k8 = e % (KT / 8);
+                    put8_col(bs + (8 * k8) * LD + n, LD, yb[i]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                const int e = t + 256 * i;
+                if constexpr (BN) {
+                    *reinterpret_cast<f32x4*>(bs + (e >> 4) * LD + 4 * (e & 15)) = xb[i];
+                } else {
+                    const int n = e / (KT / 4), kq = e % (KT / 4);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) bs[(4 * kq + q) * LD + n] = xb[i][q];
+                }
             }
         }
         __syncthreads();
@@ -157,8 +232,10 @@ __device__ __forceinline__ void zero(float acc[4][4])
 // calls for all n0.  The same tiling and 16-byte loads as mm64 (KT = 32),
 // with the next k block's loads in flight during the current products; every
 // B1 and B2 element crosses from memory once instead of once per product.
-// ls holds 5 KT x LD floats (A1, A2, A3, B1, B2).
-__device__ void mm64x3(float p1[4][4], float p2[4][4], float p3[4][4], float& dot, const float* __restrict__ A1,
+// ls holds 5 KT x LD floats (A1, A2, A3, B1, B2).  A1 may be bf16 (eight
+// values per 16-byte load).
+template <typename TA1>
+__device__ void mm64x3(float p1[4][4], float p2[4][4], float p3[4][4], float& dot, const TA1* __restrict__ A1,
                        const float* __restrict__ A2, const float* __restrict__ A3, int lda,
                        const float* __restrict__ B1, const float* __restrict__ B2, int ldb, int K, int n0, float* ls)
 {
@@ -175,16 +252,19 @@ __device__ void mm64x3(float p1[4][4], float p2[4][4], float p3[4][4], float& do
         d[1][j] = f32x4{p2[0][j], p2[1][j], p2[2][j], p2[3][j]};
         d[2][j] = f32x4{p3[0][j], p3[1][j], p3[2][j], p3[3][j]};
     }
-    const float* const A[3] = {A1, A2, A3};
+    constexpr bool A16 = sizeof(TA1) == 2;
+    const float* const A[3] = {reinterpret_cast<const float*>(A1), A2, A3};
     const float* const B[2] = {B1, B2};
     f32x4 xa[3][NV], xb[2][NV];
+    u16x8 ya;
     auto fetch = [&](int k0) {
+        if constexpr (A16) ya = *reinterpret_cast<const u16x8*>(A1 + (int64_t)(t / (KT / 8)) * lda + k0 + 8 * (t % (KT / 8)));
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const int e = t + 256 * i;
             const int r = e / (KT / 4), kq = e % (KT / 4);
 #pragma unroll
-            for (int m = 0; m < 3; ++m)
+            for (int m = A16 ? 1 : 0; m < 3; ++m)
                 xa[m][i] = *reinterpret_cast<const f32x4*>(A[m] + (int64_t)r * lda + k0 + 4 * kq);
             const int kk = e >> 4, nq = e & 15;
 #pragma unroll
@@ -200,7 +280,7 @@ __device__ void mm64x3(float p1[4][4], float p2[4][4], float p3[4][4], float& do
             const int e = t + 256 * i;
             const int r = e / (KT / 4), kq = e % (KT / 4);
 #pragma unroll
-            for (int m = 0; m < 3; ++m)
+            for (int m = A16 ? 1 : 0; m < 3; ++m)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) la[m][(4 * kq + q) * LD + r] = xa[m][i][q];
 #pragma unroll
@@ -208,6 +288,7 @@ __device__ void mm64x3(float p1[4][4], float p2[4][4], float p3[4][4], float& do
             acc_dot += xb[0][i].x * xb[1][i].x + xb[0][i].y * xb[1][i].y + xb[0][i].z * xb[1][i].z +
                        xb[0][i].w * xb[1][i].w;
         }
+        if constexpr (A16) put8_col(la[0] + (8 * (t % (KT / 8))) * LD + t / (KT / 8), LD, ya);
         __syncthreads();
         if (k0 + KT < K) fetch(k0 + KT);  // the next block's loads fly during these products
 #pragma unroll
@@ -529,11 +610,22 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a)
                 if (r0 + i * rpi >= r_end) break;
                 const int r = r0 + i * rpi + sub;
                 const float se = a.scale * eg[r] * rqs[r];
+                if constexpr (sizeof(TIn) == 2) {  // V and dO stored as bf16: the values are bf16 inputs, exact
+                    const int64_t o = (int64_t)r * dv + c8;
+                    *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(s.V) + o) =
+                        u32x4{pack_bf16x2(xv[i][0].x, xv[i][0].y), pack_bf16x2(xv[i][0].z, xv[i][0].w),
+                              pack_bf16x2(xv[i][1].x, xv[i][1].y), pack_bf16x2(xv[i][1].z, xv[i][1].w)};
+                    *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(s.dO) + o) =
+                        u32x4{pack_bf16x2(xo[i][0].x, xo[i][0].y), pack_bf16x2(xo[i][0].z, xo[i][0].w),
+                              pack_bf16x2(xo[i][1].x, xo[i][1].y), pack_bf16x2(xo[i][1].z, xo[i][1].w)};
+                }
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
                     const int64_t o = (int64_t)r * dv + c8 + 4 * u;
-                    *reinterpret_cast<f32x4*>(s.V + o) = xv[i][u];
-                    *reinterpret_cast<f32x4*>(s.dO + o) = xo[i][u];
+                    if constexpr (sizeof(TIn) != 2) {
+                        *reinterpret_cast<f32x4*>(s.V + o) = xv[i][u];
+                        *reinterpret_cast<f32x4*>(s.dO + o) = xo[i][u];
+                    }
                     *reinterpret_cast<f32x4*>(s.E + o) = xo[i][u] * se;
                 }
             }
@@ -607,10 +699,11 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a)
     }
     for (int n0 = 0; n0 < dv; n0 += 64) {
         zero(acc);
-        mm64<KTL, true, true>(acc, s.T, BC, bet, s.V, dv, BC, n0, as, bs);
+        mm64<KTL, true, true, float, TIn>(acc, s.T, BC, bet, reinterpret_cast<const TIn*>(s.V), dv, BC, n0, as, bs);
         float acc2[4][4];
         zero(acc2);
-        mm64<KTL, false, true>(acc2, s.P, BC, nullptr, s.dO, dv, BC, n0, as, bs);  // P^T dO
+        mm64<KTL, false, true, float, TIn>(acc2, s.P, BC, nullptr, reinterpret_cast<const TIn*>(s.dO), dv, BC, n0, as,
+                                           bs);  // P^T dO
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -919,6 +1012,7 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs a, ChainOps rev_
     asm volatile("" ::"v"(pf_acc));  // the prefetched words stay live: the loads are kept
 }
 
+template <typename TIn>
 __global__ __launch_bounds__(256, 3) void bwd_grad_kernel(BwdArgs a)
 {
     const int64_t b = blockIdx.x;
@@ -931,6 +1025,9 @@ __global__ __launch_bounds__(256, 3) void bwd_grad_kernel(BwdArgs a)
     const int dk = a.dk, dv = a.dv, H = a.H;
     const float scale = a.scale;
     Slices s = slices(a, b);
+    // V and dO as the local kernel stored them: the input type (bf16 exact)
+    const TIn* sV = reinterpret_cast<const TIn*>(s.V);
+    const TIn* sdO = reinterpret_cast<const TIn*>(s.dO);
     __shared__ __align__(16) float as[KTG * LD], bs[KTG * LD];
     __shared__ __align__(16) float ls3[5 * 32 * LD];  // the fused pass over S and dS
     __shared__ float gam[BC], bet[BC], eg[BC], dd[BC], bge[BC], dgam[BC], dbet[BC];
@@ -992,7 +1089,7 @@ __global__ __launch_bounds__(256, 3) void bwd_grad_kernel(BwdArgs a)
             zero(acc);
             zero(pq);
             zero(pw);
-            mm64x3(pq, pw, acc, dot, s.dO, s.dD, s.Dl, dv, s.S, s.dS, dk, dv, n0, ls3);
+            mm64x3(pq, pw, acc, dot, sdO, s.dD, s.Dl, dv, s.S, s.dS, dk, dv, n0, ls3);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -1010,7 +1107,7 @@ __global__ __launch_bounds__(256, 3) void bwd_grad_kernel(BwdArgs a)
     }
     // dP = scale lower(dO Delta^T);  dgamma from P;  dPG = dP o Gamma
     zero(acc);
-    mm64<KTG, true, false>(acc, s.dO, dv, nullptr, s.Dl, dv, dv, 0, as, bs);
+    mm64<KTG, true, false, TIn>(acc, sdO, dv, nullptr, s.Dl, dv, dv, 0, as, bs);
     {
         float colp[4] = {0.f, 0.f, 0.f, 0.f};
         rowp[0] = rowp[1] = rowp[2] = rowp[3] = 0.f;
@@ -1032,7 +1129,7 @@ __global__ __launch_bounds__(256, 3) void bwd_grad_kernel(BwdArgs a)
     // dT = (dDelta V^T) diag(beta) + (dW K^T) diag(beta e^gamma)
     {
         zero(acc);
-        mm64<KTG, true, false>(acc, s.dD, dv, nullptr, s.V, dv, dv, 0, as, bs);
+        mm64<KTG, true, false, float, TIn>(acc, s.dD, dv, nullptr, sV, dv, dv, 0, as, bs);
         float acc2[4][4];
         zero(acc2);
         mm64<KTG, true, false>(acc2, s.dW, dk, nullptr, s.K, dk, dk, 0, as, bs);
@@ -1054,7 +1151,7 @@ __global__ __launch_bounds__(256, 3) void bwd_grad_kernel(BwdArgs a)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = 4 * tr + i, n = n0 + 16 * j + tc;
-                rowp[i] += acc[i][j] * s.V[r * dv + n];
+                rowp[i] += acc[i][j] * Elem<TIn>::load(sV, r * dv + n);
                 if (r < len) a.dv_out[((int64_t)(tok0 + r) * H + h) * dv + n] = bet[r] * acc[i][j];
             }
     }
@@ -1259,7 +1356,10 @@ hipError_t launch_backward(const BwdArgs& a)
     rev.ysign = 1.f; rev.zsign = -1.f; rev.reverse = 1;
     e = chain_dispatch(a, rev, fwd);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_grad_kernel, dim3((uint32_t)chblocks), dim3(256), 0, a.stream, a);
+    if (a.bf16)
+        hipLaunchKernelGGL((bwd_grad_kernel<uint16_t>), dim3((uint32_t)chblocks), dim3(256), 0, a.stream, a);
+    else
+        hipLaunchKernelGGL((bwd_grad_kernel<float>), dim3((uint32_t)chblocks), dim3(256), 0, a.stream, a);
     return hipGetLastError();
 }
 
