@@ -138,8 +138,6 @@ BwdLayout backward_layout(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t d
     L.off_KKG = take(cc);
     L.off_W = take(cdk);
     L.off_U = take(cdv);
-    L.off_Kraw = take(cdk);
-    L.off_Qraw = take(cdk);
     L.off_E = take(cdv);
     L.off_dDl = take(cdv);
     L.off_sck = take(c1);

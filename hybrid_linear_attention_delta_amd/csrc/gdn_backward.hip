@@ -318,7 +318,7 @@ __device__ void mm64x3(float p1[4][4], float p2[4][4], float p3[4][4], float& do
 
 // Per chunk-head slices of the workspace.
 struct Slices {
-    float *Q, *K, *V, *dO, *rq, *rk, *gam, *bet, *T, *P, *KKG, *W, *U, *Kraw, *Qraw, *E, *dDl, *sck;
+    float *Q, *K, *V, *dO, *rq, *rk, *gam, *bet, *T, *P, *KKG, *W, *U, *E, *dDl, *sck;
     float *S, *Dl, *dS, *dD, *dQ, *dK, *dW, *dPG, *dT, *X1, *Bd;
 };
 
@@ -342,8 +342,6 @@ __device__ Slices slices(const BwdArgs& a, int64_t b)
     s.KKG = f(L.off_KKG, cc);
     s.W = f(L.off_W, cdk);
     s.U = f(L.off_U, cdv);
-    s.Kraw = f(L.off_Kraw, cdk);
-    s.Qraw = f(L.off_Qraw, cdk);
     s.E = f(L.off_E, cdv);
     s.sck = f(L.off_sck, BC);
     s.dDl = f(L.off_dDl, cdv);
@@ -361,21 +359,34 @@ __device__ Slices slices(const BwdArgs& a, int64_t b)
     return s;
 }
 
+// eight consecutive stored elements p[i .. i + 7] (i a multiple of 8), widened
+__device__ __forceinline__ void load8(const float* p, int64_t i, f32x4& a, f32x4& b)
+{
+    a = *reinterpret_cast<const f32x4*>(p + i);
+    b = *reinterpret_cast<const f32x4*>(p + i + 4);
+}
+__device__ __forceinline__ void load8(const uint16_t* p, int64_t i, f32x4& a, f32x4& b)
+{
+    const u16x8 x = *reinterpret_cast<const u16x8*>(p + i);
+    a = f32x4{bf16_bits_to_f32(x[0]), bf16_bits_to_f32(x[1]), bf16_bits_to_f32(x[2]), bf16_bits_to_f32(x[3])};
+    b = f32x4{bf16_bits_to_f32(x[4]), bf16_bits_to_f32(x[5]), bf16_bits_to_f32(x[6]), bf16_bits_to_f32(x[7])};
+}
+
 // B-operand fragments of a row-major fp32 [BC][d] matrix X for a product
 // contracting over the chunk rows, on the bf16 matrix cores with hi/lo
 // splits: fragment (ct, ks) gives lane (l16, g) the elements
 // X[32 ks + 8 g + e][16 ct + l16], e = 0..7, as bf16 hi and lo parts at
 // out + (((ct * 2 + ks) * 2 + part) * 64 + lane) * 8 (HI: the hi parts only,
 // for values that bf16 holds exactly).
-template <bool HI>
-__device__ void col_frags(const float* __restrict__ X, int d, uint16_t* __restrict__ out)
+template <bool HI, typename TX = float>
+__device__ void col_frags(const TX* __restrict__ X, int d, uint16_t* __restrict__ out)
 {
     for (int task = threadIdx.x; task < (d / 16) * 128; task += 256) {
         const int lane = task & 63, ks = (task >> 6) & 1, ct = task >> 7;
         const int l16 = lane & 15, g = lane >> 4;
         float x[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = X[(32 * ks + 8 * g + e) * d + 16 * ct + l16];
+        for (int e = 0; e < 8; ++e) x[e] = Elem<TX>::load(X, (32 * ks + 8 * g + e) * d + 16 * ct + l16);
         uint32_t hi[4], lo[4];
 #pragma unroll
         for (int w = 0; w < 4; ++w) split_bf16x2(x[2 * w], x[2 * w + 1], hi[w], lo[w]);
@@ -390,15 +401,15 @@ __device__ void col_frags(const float* __restrict__ X, int d, uint16_t* __restri
 // elements X[16 rt + l16][32 ks + 8 g + e], e = 0..7, as bf16 hi and lo parts
 // at out + (((rt * (d / 32) + ks) * 2 + part) * 64 + lane) * 8 (HI: the hi
 // parts only).
-template <bool HI>
-__device__ void row_frags(const float* __restrict__ X, int d, uint16_t* __restrict__ out)
+template <bool HI, typename TX = float>
+__device__ void row_frags(const TX* __restrict__ X, int d, uint16_t* __restrict__ out)
 {
     const int ksn = d / 32;
     for (int task = threadIdx.x; task < (BC / 16) * ksn * 64; task += 256) {
         const int lane = task & 63, ks = (task >> 6) % ksn, rt = (task >> 6) / ksn;
         const int l16 = lane & 15, g = lane >> 4;
-        const float* src = X + (16 * rt + l16) * d + 32 * ks + 8 * g;
-        const f32x4 a = *reinterpret_cast<const f32x4*>(src), b = *reinterpret_cast<const f32x4*>(src + 4);
+        f32x4 a, b;
+        load8(X, (16 * rt + l16) * d + 32 * ks + 8 * g, a, b);
         uint32_t hi[4], lo[4];
         split_bf16x2(a.x, a.y, hi[0], lo[0]);
         split_bf16x2(a.z, a.w, hi[1], lo[1]);
@@ -474,19 +485,6 @@ __global__ __launch_bounds__(64) void bwd_table_kernel(const int32_t* __restrict
     header[1] = (int32_t)count;
 }
 
-// eight consecutive stored elements p[i .. i + 7] (i a multiple of 8), widened
-__device__ __forceinline__ void load8(const float* p, int64_t i, f32x4& a, f32x4& b)
-{
-    a = *reinterpret_cast<const f32x4*>(p + i);
-    b = *reinterpret_cast<const f32x4*>(p + i + 4);
-}
-__device__ __forceinline__ void load8(const uint16_t* p, int64_t i, f32x4& a, f32x4& b)
-{
-    const u16x8 x = *reinterpret_cast<const u16x8*>(p + i);
-    a = f32x4{bf16_bits_to_f32(x[0]), bf16_bits_to_f32(x[1]), bf16_bits_to_f32(x[2]), bf16_bits_to_f32(x[3])};
-    b = f32x4{bf16_bits_to_f32(x[4]), bf16_bits_to_f32(x[5]), bf16_bits_to_f32(x[6]), bf16_bits_to_f32(x[7])};
-}
-
 template <typename TIn>
 __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a)
 {
@@ -500,7 +498,7 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a)
     const int dk = a.dk, dv = a.dv, H = a.H;
     Slices s = slices(a, b);
     __shared__ __align__(16) float as[KTL * LD], bs[KTL * LD];
-    __shared__ float gam[BC], bet[BC], bge[BC], dd[BC], eg[BC], gin[BC], rqs[BC];
+    __shared__ float gam[BC], bet[BC], bge[BC], dd[BC], eg[BC], gin[BC], rqs[BC], rks[BC], bgk[BC];
     __shared__ float Am[BC][BC + 1], Ts[BC][BC + 1];
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
     const TIn* q = (const TIn*)a.q;
@@ -575,21 +573,32 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a)
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
                     const int64_t o = (int64_t)r * dk + c8 + 4 * u;
-                    *reinterpret_cast<f32x4*>(s.Q + o) = xq[i][u] * rq;
-                    *reinterpret_cast<f32x4*>(s.K + o) = xk[i][u] * rk;
-                    *reinterpret_cast<f32x4*>(s.Qraw + o) = xq[i][u];
-                    *reinterpret_cast<f32x4*>(s.Kraw + o) = xk[i][u];
+                    if constexpr (sizeof(TIn) != 2) {
+                        *reinterpret_cast<f32x4*>(s.Q + o) = xq[i][u];
+                        *reinterpret_cast<f32x4*>(s.K + o) = xk[i][u];
+                    }
+                }
+                if constexpr (sizeof(TIn) == 2) {  // the raw rows, exact in bf16
+                    const int64_t o = (int64_t)r * dk + c8;
+                    *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(s.Q) + o) =
+                        u32x4{pack_bf16x2(xq[i][0].x, xq[i][0].y), pack_bf16x2(xq[i][0].z, xq[i][0].w),
+                              pack_bf16x2(xq[i][1].x, xq[i][1].y), pack_bf16x2(xq[i][1].z, xq[i][1].w)};
+                    *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(s.K) + o) =
+                        u32x4{pack_bf16x2(xk[i][0].x, xk[i][0].y), pack_bf16x2(xk[i][0].z, xk[i][0].w),
+                              pack_bf16x2(xk[i][1].x, xk[i][1].y), pack_bf16x2(xk[i][1].z, xk[i][1].w)};
                 }
                 if (c8 == 0) {
                     s.rq[r] = rq;
                     s.rk[r] = rk;
                     s.sck[r] = rk * dd[r];
                     rqs[r] = rq;
+                    rks[r] = rk;
                 }
             }
         }
     }
-    __syncthreads();  // rqs
+    __syncthreads();  // rqs, rks
+    if (t < BC) bgk[t] = bge[t] * rks[t];
     {
         const int lpr = dv / 8, rpi = kWave / lpr, sub = lane / lpr, c8 = 8 * (lane % lpr);
         for (int r0 = 16 * wv; r0 < r_end; r0 += 4 * rpi) {
@@ -635,27 +644,32 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a)
 
     const int tr = t >> 4, tc = t & 15;
     float acc[4][4];
+    // The Q and K slots hold the raw rows (the input type; bf16 exact): the
+    // normalised K^ = diag(r_k) k and Q^ = diag(r_q) q take their row scales
+    // in fp32, on the products' rows and columns or folded into the k scale.
+    const TIn* sQ = reinterpret_cast<const TIn*>(s.Q);
+    const TIn* sK = reinterpret_cast<const TIn*>(s.K);
     // K K^T -> KKG = strict_lower(K K^T o Gamma), A = diag(beta) KKG
     zero(acc);
-    mm64<KTL, true, false>(acc, s.K, dk, nullptr, s.K, dk, dk, 0, as, bs);
+    mm64<KTL, true, false, TIn, TIn>(acc, sK, dk, nullptr, sK, dk, dk, 0, as, bs);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int r = 4 * tr + i, n = 16 * j + tc;
-            const float x = n < r ? acc[i][j] * expf(gam[r] - gam[n]) : 0.f;
+            const float x = n < r ? acc[i][j] * (rks[r] * rks[n]) * expf(gam[r] - gam[n]) : 0.f;
             s.KKG[r * BC + n] = x;
             Am[r][n] = bet[r] * x;
         }
     // Q K^T -> P = lower(Q K^T o Gamma)
     zero(acc);
-    mm64<KTL, true, false>(acc, s.Q, dk, nullptr, s.K, dk, dk, 0, as, bs);
+    mm64<KTL, true, false, TIn, TIn>(acc, sQ, dk, nullptr, sK, dk, dk, 0, as, bs);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int r = 4 * tr + i, n = 16 * j + tc;
-            s.P[r * BC + n] = n <= r ? acc[i][j] * expf(gam[r] - gam[n]) : 0.f;
+            s.P[r * BC + n] = n <= r ? acc[i][j] * (rqs[r] * rks[n]) * expf(gam[r] - gam[n]) : 0.f;
         }
     __syncthreads();
     // T = (I + A)^{-1} by forward substitution.  Column c of T depends only on
@@ -688,7 +702,7 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a)
     // W = T diag(beta e^gamma) K, then U = T diag(beta) V
     for (int n0 = 0; n0 < dk; n0 += 64) {
         zero(acc);
-        mm64<KTL, true, true>(acc, s.T, BC, bge, s.K, dk, BC, n0, as, bs);
+        mm64<KTL, true, true, float, TIn>(acc, s.T, BC, bgk, sK, dk, BC, n0, as, bs);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -718,11 +732,11 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a)
     const int64_t fper = (int64_t)BC * dk * 2;
     constexpr bool RAW_EXACT = sizeof(TIn) == 2;  // bf16 inputs: raw k and q are exact in bf16
     col_frags<false>(s.W, dk, reinterpret_cast<uint16_t*>(a.ws + a.lay.off_Wf) + b * fper);
-    col_frags<RAW_EXACT>(s.Kraw, dk, reinterpret_cast<uint16_t*>(a.ws + a.lay.off_Kf) + b * fper);
-    col_frags<RAW_EXACT>(s.Qraw, dk, reinterpret_cast<uint16_t*>(a.ws + a.lay.off_Qf) + b * fper);
+    col_frags<RAW_EXACT>(sK, dk, reinterpret_cast<uint16_t*>(a.ws + a.lay.off_Kf) + b * fper);
+    col_frags<RAW_EXACT>(sQ, dk, reinterpret_cast<uint16_t*>(a.ws + a.lay.off_Qf) + b * fper);
     col_frags<false>(s.E, dv, reinterpret_cast<uint16_t*>(a.ws + a.lay.off_Ef) + b * (int64_t)BC * dv * 2);
     row_frags<false>(s.W, dk, reinterpret_cast<uint16_t*>(a.ws + a.lay.off_Wr) + b * fper);
-    row_frags<RAW_EXACT>(s.Kraw, dk, reinterpret_cast<uint16_t*>(a.ws + a.lay.off_Kr) + b * fper);
+    row_frags<RAW_EXACT>(sK, dk, reinterpret_cast<uint16_t*>(a.ws + a.lay.off_Kr) + b * fper);
 }
 
 // One row-split recurrence over the chunks of each sequence (see the header):
@@ -1028,15 +1042,22 @@ __global__ __launch_bounds__(256, 3) void bwd_grad_kernel(BwdArgs a)
     // V and dO as the local kernel stored them: the input type (bf16 exact)
     const TIn* sV = reinterpret_cast<const TIn*>(s.V);
     const TIn* sdO = reinterpret_cast<const TIn*>(s.dO);
+    // and Q, K as the raw rows: Q^ = diag(r_q) q, K^ = diag(r_k) k take their
+    // row scales (rqv, rkv) in fp32, folded into the k scale of the products
+    // that contract over the chunk rows, on output columns or row sums else
+    const TIn* sQ = reinterpret_cast<const TIn*>(s.Q);
+    const TIn* sK = reinterpret_cast<const TIn*>(s.K);
     __shared__ __align__(16) float as[KTG * LD], bs[KTG * LD];
     __shared__ __align__(16) float ls3[5 * 32 * LD];  // the fused pass over S and dS
-    __shared__ float gam[BC], bet[BC], eg[BC], dd[BC], bge[BC], dgam[BC], dbet[BC];
+    __shared__ float gam[BC], bet[BC], eg[BC], dd[BC], bge[BC], dgam[BC], dbet[BC], rqv[BC], rkv[BC];
     __shared__ float red[4];
     __shared__ float cs[16][BC];
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
     const int tr = t >> 4, tc = t & 15;
     if (t < BC) {
         gam[t] = s.gam[t];
+        rqv[t] = s.rq[t];
+        rkv[t] = s.rk[t];
         bet[t] = s.bet[t];
         dgam[t] = 0.f;
         dbet[t] = 0.f;
@@ -1096,10 +1117,10 @@ __global__ __launch_bounds__(256, 3) void bwd_grad_kernel(BwdArgs a)
                 for (int j = 0; j < 4; ++j) {
                     const int r = 4 * tr + i, n = n0 + 16 * j + tc;
                     const float x = scale * eg[r] * pq[i][j];
-                    rq[i] += s.Q[r * dk + n] * x;
+                    rq[i] += Elem<TIn>::load(sQ, r * dk + n) * x;
                     s.dQ[r * dk + n] = x;
                     s.dW[r * dk + n] = -pw[i][j];
-                    rk[i] += s.K[r * dk + n] * acc[i][j];
+                    rk[i] += Elem<TIn>::load(sK, r * dk + n) * acc[i][j];
                     s.dK[r * dk + n] = dd[r] * acc[i][j];
                 }
         }
@@ -1132,13 +1153,13 @@ __global__ __launch_bounds__(256, 3) void bwd_grad_kernel(BwdArgs a)
         mm64<KTG, true, false, float, TIn>(acc, s.dD, dv, nullptr, sV, dv, dv, 0, as, bs);
         float acc2[4][4];
         zero(acc2);
-        mm64<KTG, true, false>(acc2, s.dW, dk, nullptr, s.K, dk, dk, 0, as, bs);
+        mm64<KTG, true, false, float, TIn>(acc2, s.dW, dk, nullptr, sK, dk, dk, 0, as, bs);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = 4 * tr + i, n = 16 * j + tc;
-                s.dT[r * BC + n] = acc[i][j] * bet[n] + acc2[i][j] * bge[n];
+                s.dT[r * BC + n] = acc[i][j] * bet[n] + acc2[i][j] * (bge[n] * rkv[n]);
             }
     }
     // dV = diag(beta) T^T dDelta;  dbeta_r += (T^T dDelta)_r . V_r
@@ -1201,7 +1222,7 @@ __global__ __launch_bounds__(256, 3) void bwd_grad_kernel(BwdArgs a)
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] = s.dQ[(4 * tr + i) * dk + n0 + 16 * j + tc];
-        mm64<KTG, true, true>(acc, s.dPG, BC, nullptr, s.K, dk, BC, n0, as, bs);
+        mm64<KTG, true, true, float, TIn>(acc, s.dPG, BC, rkv, sK, dk, BC, n0, as, bs);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -1215,12 +1236,12 @@ __global__ __launch_bounds__(256, 3) void bwd_grad_kernel(BwdArgs a)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = 4 * tr + i, n = n0 + 16 * j + tc;
-                rt[i] += s.K[r * dk + n] * acc2[i][j];
+                rt[i] += Elem<TIn>::load(sK, r * dk + n) * acc2[i][j];
                 acc[i][j] = s.dK[r * dk + n] + bge[r] * acc2[i][j];
             }
-        mm64<KTG, false, true>(acc, s.dPG, BC, nullptr, s.Q, dk, BC, n0, as, bs);
-        mm64<KTG, true, true>(acc, s.Bd, BC, nullptr, s.K, dk, BC, n0, as, bs);
-        mm64<KTG, false, true>(acc, s.Bd, BC, nullptr, s.K, dk, BC, n0, as, bs);
+        mm64<KTG, false, true, float, TIn>(acc, s.dPG, BC, rqv, sQ, dk, BC, n0, as, bs);
+        mm64<KTG, true, true, float, TIn>(acc, s.Bd, BC, rkv, sK, dk, BC, n0, as, bs);
+        mm64<KTG, false, true, float, TIn>(acc, s.Bd, BC, rkv, sK, dk, BC, n0, as, bs);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -1228,8 +1249,9 @@ __global__ __launch_bounds__(256, 3) void bwd_grad_kernel(BwdArgs a)
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const float xq = group_sum<16>(rq[i]), xk = group_sum<16>(rk[i]), xt = group_sum<16>(rt[i]);
         const int r = 4 * tr + i;
+        const float xq = rqv[r] * group_sum<16>(rq[i]), xk = rkv[r] * group_sum<16>(rk[i]),
+                    xt = rkv[r] * group_sum<16>(rt[i]);
         if (tc == 0) {
             dgam[r] += xq - xk * dd[r] + bge[r] * xt;
             dbet[r] += eg[r] * xt;
@@ -1262,12 +1284,14 @@ __global__ __launch_bounds__(256, 3) void bwd_grad_kernel(BwdArgs a)
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const int r = min(r0 + i * rpi, r_end - rpi) + sub;
+                load8(sQ, r * dk + c8, xq[i][0], xq[i][1]);
+                load8(sK, r * dk + c8, xk[i][0], xk[i][1]);
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
                     const int o = r * dk + c8 + 4 * u;
-                    xq[i][u] = *reinterpret_cast<const f32x4*>(s.Q + o);
+                    xq[i][u] *= rqv[r];  // the normalised rows
+                    xk[i][u] *= rkv[r];
                     gq[i][u] = *reinterpret_cast<const f32x4*>(s.dQ + o);
-                    xk[i][u] = *reinterpret_cast<const f32x4*>(s.K + o);
                     gk[i][u] = *reinterpret_cast<const f32x4*>(s.dK + o);
                 }
             }
