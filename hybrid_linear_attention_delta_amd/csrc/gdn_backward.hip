@@ -396,6 +396,28 @@ __device__ void col_frags(const TX* __restrict__ X, int d, uint16_t* __restrict_
     }
 }
 
+// The hi parts of col_frags for bf16 values (exact, so no lo parts), by
+// 8 x 8 blocks: a thread loads eight rows of eight consecutive columns (16
+// bytes each) and writes the eight lanes' fragments those columns give.
+__device__ void col_frags_b16(const uint16_t* __restrict__ X, int d, uint16_t* __restrict__ out)
+{
+    const int ncg = d / 8;  // groups of eight columns
+    for (int task = threadIdx.x; task < 8 * ncg; task += 256) {
+        const int cg = task % ncg, rg = task / ncg, ks = rg >> 2, g = rg & 3;
+        u16x8 v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = *reinterpret_cast<const u16x8*>(X + (32 * ks + 8 * g + e) * d + 8 * cg);
+#pragma unroll
+        for (int h = 0; h < 8; ++h) {
+            const int c = 8 * cg + h, ct = c >> 4, lane = (c & 15) + 16 * g;
+            u32x4 f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) f[w] = (uint32_t)v[2 * w][h] | ((uint32_t)v[2 * w + 1][h] << 16);
+            *reinterpret_cast<u32x4*>(out + ((size_t)((ct * 2 + ks) * 2) * 64 + lane) * 8) = f;
+        }
+    }
+}
+
 // Operand fragments of a row-major fp32 [BC][d] matrix X for a product
 // contracting over its columns: fragment (rt, ks) gives lane (l16, g) the
 // elements X[16 rt + l16][32 ks + 8 g + e], e = 0..7, as bf16 hi and lo parts
@@ -732,8 +754,13 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a)
     const int64_t fper = (int64_t)BC * dk * 2;
     constexpr bool RAW_EXACT = sizeof(TIn) == 2;  // bf16 inputs: raw k and q are exact in bf16
     col_frags<false>(s.W, dk, reinterpret_cast<uint16_t*>(a.ws + a.lay.off_Wf) + b * fper);
-    col_frags<RAW_EXACT>(sK, dk, reinterpret_cast<uint16_t*>(a.ws + a.lay.off_Kf) + b * fper);
-    col_frags<RAW_EXACT>(sQ, dk, reinterpret_cast<uint16_t*>(a.ws + a.lay.off_Qf) + b * fper);
+    if constexpr (RAW_EXACT) {
+        col_frags_b16(reinterpret_cast<const uint16_t*>(sK), dk, reinterpret_cast<uint16_t*>(a.ws + a.lay.off_Kf) + b * fper);
+        col_frags_b16(reinterpret_cast<const uint16_t*>(sQ), dk, reinterpret_cast<uint16_t*>(a.ws + a.lay.off_Qf) + b * fper);
+    } else {
+        col_frags<false>(sK, dk, reinterpret_cast<uint16_t*>(a.ws + a.lay.off_Kf) + b * fper);
+        col_frags<false>(sQ, dk, reinterpret_cast<uint16_t*>(a.ws + a.lay.off_Qf) + b * fper);
+    }
     col_frags<false>(s.E, dv, reinterpret_cast<uint16_t*>(a.ws + a.lay.off_Ef) + b * (int64_t)BC * dv * 2);
     row_frags<false>(s.W, dk, reinterpret_cast<uint16_t*>(a.ws + a.lay.off_Wr) + b * fper);
     row_frags<RAW_EXACT>(sK, dk, reinterpret_cast<uint16_t*>(a.ws + a.lay.off_Kr) + b * fper);
