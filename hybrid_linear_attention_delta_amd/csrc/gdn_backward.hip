@@ -418,6 +418,35 @@ __device__ void col_frags_b16(const uint16_t* __restrict__ X, int d, uint16_t* _
     }
 }
 
+// col_frags of diag(rscale) X for bf16 X, hi and lo parts, by the same 8 x 8
+// blocks (the row scales applied in fp32 before the split).
+__device__ void col_frags_b16s(const uint16_t* __restrict__ X, int d, const float* rscale, uint16_t* __restrict__ out)
+{
+    const int ncg = d / 8;
+    for (int task = threadIdx.x; task < 8 * ncg; task += 256) {
+        const int cg = task % ncg, rg = task / ncg, ks = rg >> 2, g = rg & 3;
+        u16x8 v[8];
+        float sc[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            v[e] = *reinterpret_cast<const u16x8*>(X + (32 * ks + 8 * g + e) * d + 8 * cg);
+            sc[e] = rscale[32 * ks + 8 * g + e];
+        }
+#pragma unroll
+        for (int h = 0; h < 8; ++h) {
+            const int c = 8 * cg + h, ct = c >> 4, lane = (c & 15) + 16 * g;
+            uint32_t hi[4], lo[4];
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+                split_bf16x2(bf16_bits_to_f32(v[2 * w][h]) * sc[2 * w], bf16_bits_to_f32(v[2 * w + 1][h]) * sc[2 * w + 1],
+                             hi[w], lo[w]);
+            uint16_t* q = out + ((size_t)((ct * 2 + ks) * 2) * 64 + lane) * 8;
+            *reinterpret_cast<u32x4*>(q) = u32x4{hi[0], hi[1], hi[2], hi[3]};
+            *reinterpret_cast<u32x4*>(q + 512) = u32x4{lo[0], lo[1], lo[2], lo[3]};
+        }
+    }
+}
+
 // Operand fragments of a row-major fp32 [BC][d] matrix X for a product
 // contracting over its columns: fragment (rt, ks) gives lane (l16, g) the
 // elements X[16 rt + l16][32 ks + 8 g + e], e = 0..7, as bf16 hi and lo parts
@@ -508,7 +537,7 @@ __global__ __launch_bounds__(64) void bwd_table_kernel(const int32_t* __restrict
 }
 
 template <typename TIn>
-__global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void bwd_local_kernel(BwdArgs a)
 {
     const int64_t b = blockIdx.x;
     const int32_t* header = reinterpret_cast<const int32_t*>(a.ws + a.lay.off_header);
@@ -520,7 +549,7 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a)
     const int dk = a.dk, dv = a.dv, H = a.H;
     Slices s = slices(a, b);
     __shared__ __align__(16) float as[KTL * LD], bs[KTL * LD];
-    __shared__ float gam[BC], bet[BC], bge[BC], dd[BC], eg[BC], gin[BC], rqs[BC], rks[BC], bgk[BC];
+    __shared__ float gam[BC], bet[BC], bge[BC], dd[BC], eg[BC], gin[BC], rqs[BC], rks[BC], bgk[BC], esc[BC];
     __shared__ float Am[BC][BC + 1], Ts[BC][BC + 1];
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
     const TIn* q = (const TIn*)a.q;
@@ -620,7 +649,10 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a)
         }
     }
     __syncthreads();  // rqs, rks
-    if (t < BC) bgk[t] = bge[t] * rks[t];
+    if (t < BC) {
+        bgk[t] = bge[t] * rks[t];
+        esc[t] = a.scale * eg[t] * rqs[t];  // the row scale of E = r_q scale e^gamma dO
+    }
     {
         const int lpr = dv / 8, rpi = kWave / lpr, sub = lane / lpr, c8 = 8 * (lane % lpr);
         for (int r0 = 16 * wv; r0 < r_end; r0 += 4 * rpi) {
@@ -657,7 +689,7 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a)
                         *reinterpret_cast<f32x4*>(s.V + o) = xv[i][u];
                         *reinterpret_cast<f32x4*>(s.dO + o) = xo[i][u];
                     }
-                    *reinterpret_cast<f32x4*>(s.E + o) = xo[i][u] * se;
+                    if constexpr (sizeof(TIn) != 2) *reinterpret_cast<f32x4*>(s.E + o) = xo[i][u] * se;
                 }
             }
         }
@@ -761,7 +793,11 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a)
         col_frags<false>(sK, dk, reinterpret_cast<uint16_t*>(a.ws + a.lay.off_Kf) + b * fper);
         col_frags<false>(sQ, dk, reinterpret_cast<uint16_t*>(a.ws + a.lay.off_Qf) + b * fper);
     }
-    col_frags<false>(s.E, dv, reinterpret_cast<uint16_t*>(a.ws + a.lay.off_Ef) + b * (int64_t)BC * dv * 2);
+    if constexpr (RAW_EXACT)  // E from the bf16 dO copy, its row scale applied in fp32
+        col_frags_b16s(reinterpret_cast<const uint16_t*>(s.dO), dv, esc,
+                       reinterpret_cast<uint16_t*>(a.ws + a.lay.off_Ef) + b * (int64_t)BC * dv * 2);
+    else
+        col_frags<false>(s.E, dv, reinterpret_cast<uint16_t*>(a.ws + a.lay.off_Ef) + b * (int64_t)BC * dv * 2);
     row_frags<false>(s.W, dk, reinterpret_cast<uint16_t*>(a.ws + a.lay.off_Wr) + b * fper);
     row_frags<RAW_EXACT>(sK, dk, reinterpret_cast<uint16_t*>(a.ws + a.lay.off_Kr) + b * fper);
 }
