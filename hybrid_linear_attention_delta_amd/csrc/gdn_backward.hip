@@ -15,9 +15,11 @@
 // (Q, K the L2-normalised queries and keys).  The backward runs in four launches:
 //
 //   1. bwd_table_kernel   chunk table of the packed batch (one workgroup).
-//   2. bwd_local_kernel   per chunk-head: normalise and pad the chunk's rows,
+//   2. bwd_local_kernel   per chunk-head: gather and pad the chunk's rows (kept
+//                         in the input type, the L2 norms as fp32 row scales),
 //                         form Gamma, A, T, P, W, U, D K, scale e^gamma dO and
-//                         dDelta_local = scale P^T dO into a workspace.
+//                         dDelta_local = scale P^T dO into a workspace, with
+//                         the chains' operand fragments.
 //   3. bwd_chain_kernel   both directions in one launch.  Forward over the chunks
 //                         of each sequence: the state entering every chunk and
 //                         its Delta.  Reverse:
@@ -33,10 +35,13 @@
 // Ragged chunks are padded to C rows with q = k = v = dO = 0, beta = 0 and
 // g = 0, which leaves every product of the real rows unchanged.
 //
-// Everything is fp32.  The contractions run on the fp32 matrix cores
-// (v_mfma_f32_16x16x4_f32: exact fp32 products, fp32 sums); the per-chunk
-// products go through one LDS-tiled 64 x 64 block routine.  Results do not
-// depend on scheduling: no atomics, fixed reduction orders.
+// The arithmetic is fp32.  The per-chunk contractions run on the fp32 matrix
+// cores (v_mfma_f32_16x16x4_f32: exact fp32 products, fp32 sums) through one
+// LDS-tiled 64 x 64 block routine.  The two chains run on the bf16 matrix
+// cores with each fp32 operand split into bf16 hi and lo parts (three
+// products per fragment pair; a raw bf16 row is its own hi part, one product
+// less) and fp32 sums.  Results do not depend on scheduling: no atomics,
+// fixed reduction orders.
 #include <string.h>
 
 #include <type_traits>
@@ -581,12 +586,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
     }
     __syncthreads();
 
-    // rows of the chunk, normalised and padded with zeros, by 16-byte loads and
-    // stores: a row of d elements spreads over d / 8 lanes, eight elements
-    // each; wave w takes rows 16 w .. 16 w + 15, up to four rows per lane in
-    // flight.  The raw (widened) k and q rows, the row scales D r_k and
-    // E = r_q scale e^gamma dO are formed here as well: the state chains
-    // take K^ and Q^ as raw rows with their scales applied in fp32.
+    // rows of the chunk, padded with zeros, by 16-byte loads and stores: a row
+    // of d elements spreads over d / 8 lanes, eight elements each; wave w takes
+    // rows 16 w .. 16 w + 15, up to four rows per lane in flight.  The rows
+    // stay raw (in the input type); their L2 norms give the fp32 row scales
+    // r_q, r_k and D r_k, which every later product applies in fp32.  With
+    // fp32 inputs E = r_q scale e^gamma dO is stored here; with bf16 inputs
+    // its fragments come from the bf16 dO copy below.
     const int r_end = 16 * wv + 16;
     {
         const int lpr = dk / 8, rpi = kWave / lpr, sub = lane / lpr, c8 = 8 * (lane % lpr);
@@ -672,7 +678,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
             for (int i = 0; i < 4; ++i) {
                 if (r0 + i * rpi >= r_end) break;
                 const int r = r0 + i * rpi + sub;
-                const float se = a.scale * eg[r] * rqs[r];
                 if constexpr (sizeof(TIn) == 2) {  // V and dO stored as bf16: the values are bf16 inputs, exact
                     const int64_t o = (int64_t)r * dv + c8;
                     *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(s.V) + o) =
@@ -689,7 +694,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
                         *reinterpret_cast<f32x4*>(s.V + o) = xv[i][u];
                         *reinterpret_cast<f32x4*>(s.dO + o) = xo[i][u];
                     }
-                    if constexpr (sizeof(TIn) != 2) *reinterpret_cast<f32x4*>(s.E + o) = xo[i][u] * se;
+                    if constexpr (sizeof(TIn) != 2)
+                        *reinterpret_cast<f32x4*>(s.E + o) = xo[i][u] * (a.scale * eg[r] * rqs[r]);
                 }
             }
         }
