@@ -373,10 +373,11 @@ gdn_status gdn_chunk_prefill_frontend(gdn_context_t ctx, const void* xq, const v
 
 /*
  * Bytes of device workspace gdn_chunk_prefill_backward needs for these sizes
- * (0 for an unsupported or invalid combination).  It holds fp32 per-chunk
- * intermediates, among them the state entering every chunk and the state
- * gradient after it: about max_chunks * H * (2 dv dk + 14 * 64 (dk + dv))
- * * 4 bytes, max_chunks = total_tokens / 64 + num_seqs.
+ * (0 for an unsupported or invalid combination).  It holds per-chunk
+ * intermediates in 4-byte slots, among them the state entering every chunk
+ * and the state gradient after it: max_chunks * H * (2 dv dk + 64 (11 dk +
+ * 8 dv) + 7 * 64 * 64 + 5 * 64) * 4 bytes plus the chunk table and 256-byte
+ * alignment, max_chunks = total_tokens / 64 + num_seqs.
  */
 size_t gdn_prefill_backward_workspace_size(int64_t total_tokens, int32_t num_seqs, int32_t H, int32_t dk,
                                            int32_t dv);
@@ -402,8 +403,12 @@ size_t gdn_prefill_backward_workspace_size(int64_t total_tokens, int32_t num_seq
  *   grad_init_state [num_seqs, H, dv, dk] fp32 (written), or NULL
  *   workspace   at least gdn_prefill_backward_workspace_size(...) bytes,
  *               256-byte aligned
- * Supported: dt in {GDN_F32, GDN_BF16}, dk and dv in {64, 128, 256}; the
- * arithmetic is fp32 throughout.  Gradient buffers must not overlap the
+ * Supported: dt in {GDN_F32, GDN_BF16}, dk and dv in {64, 128, 256}.
+ * Intermediates and sums are fp32; the per-chunk products run on the fp32
+ * matrix cores, the two state recurrences on the bf16 ones with every fp32
+ * operand split into bf16 hi and lo parts (three products per pair; a bf16
+ * input row is exact in its hi part).  Every gradient stays within 1e-4 of
+ * the rms of an fp64 evaluation on the tested workloads.  Gradient buffers must not overlap the
  * inputs or each other; for grad_init_state against init_state and
  * d_final_state this is checked (GDN_ERR_BAD_SHAPE).  With an invalid device cu_seqlens (and no host
  * mirror) no chunk is processed and the gradients are unspecified.
