@@ -880,6 +880,7 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs a, ChainOps rev_
     __shared__ __align__(16) float Ssh[16 * P];   // state rows before the chunk
     __shared__ __align__(16) uint16_t Sbh[16 * PB], Sbl[16 * PB];  // the same rows, bf16 hi and lo
     __shared__ __align__(16) float dsm[16 * DP];  // Delta^T [state row][chunk row]
+    __shared__ __align__(16) uint16_t Esh[4 * 512];  // (reverse) E^T fragments of the chunk: (k-step, hi / lo) x 1 KB
 
     // this wave's operand quarters, one chunk ahead.  K^ and Q^ enter as raw
     // rows (Y of the reverse direction, Z of the forward one, F): their row
@@ -890,7 +891,7 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs a, ChainOps rev_
     u32x4 yr[DKS][2];     // Y fragments of chunk rows 16 w .., k-step ks, hi / lo
     u32x4 zr[NT][2][2];   // Z fragments of column tiles w NT + tt, k-step ks, hi / lo
     u32x4 fr[NT][2][2];   // F fragments, likewise
-    u32x4 er[2][2];       // E^T fragments of this row block, k-step ks, hi / lo
+    u32x4 eq;             // (reverse) this wave's quarter of the E^T fragments, staged in LDS for all four
     f32x4 xr;             // X[16 w + l16][16 rb + 4 g .. + 3]
     float gl = 0.f;       // gamma_L of the chunk
     float scv = 1.f;      // D r_k of chunk row 16 w + l16
@@ -931,12 +932,8 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs a, ChainOps rev_
 #pragma unroll
                 for (int part = 0; part < NPART; ++part)
                     fr[tt][ks][part] = *reinterpret_cast<const u32x4*>(p + (((w * NT + tt) * 2 + ks) * 2 + part) * 512);
-        const uint16_t* pe = Ef + ch * (int64_t)BC * dv * 2 + lane * 8;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int part = 0; part < 2; ++part)
-                er[ks][part] = *reinterpret_cast<const u32x4*>(pe + ((rb * 2 + ks) * 2 + part) * 512);
+        // fragment (k-step, part) = (w / 2, w % 2) of this row block
+        eq = *reinterpret_cast<const u32x4*>(Ef + ch * (int64_t)BC * dv * 2 + (rb * 4 + w) * 512 + lane * 8);
     };
 
     // L2 prefetch two chunks ahead: the operand bytes the chain reads for one
@@ -1035,8 +1032,16 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs a, ChainOps rev_
         for (int i = 0; i < 4; ++i) dsm[(4 * g + i) * DP + 16 * w + l16] = REV ? d[i] : d[i] * scv;
         *reinterpret_cast<f32x4*>(Dst + (ch * BC + 16 * w + l16) * dv + rb * 16 + 4 * g) = d;
         const float decay = expf(gl);
+        if constexpr (REV) *reinterpret_cast<u32x4*>(Esh + w * 512 + lane * 8) = eq;
         load_y(chunk_of(min(it + 1, steps - 1)), rev_c);
-        __syncthreads();  // ---- Delta^T in LDS; the state rows read
+        __syncthreads();  // ---- Delta^T and E^T in LDS; the state rows read
+        u32x4 er[2][2];
+        if constexpr (REV)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int part = 0; part < 2; ++part)
+                    er[ks][part] = *reinterpret_cast<const u32x4*>(Esh + (ks * 2 + part) * 512 + lane * 8);
         // S <- e^{gamma_L} S + zsign Delta^T Z (+ E^T F)
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) sreg[tt] *= decay;
