@@ -819,13 +819,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
 //     A = S (the state rows from LDS), B = Y^T (its 16 rows of Y, registers);
 //   - Delta^T Z + E^T F (16 x DK, K = 64): wave w owns the DK/4 state columns
 //     w DK/4 .. in registers in the accumulator layout (lane l: rows
-//     4 (l / 16) + i, column l % 16 of each 16-column tile); A = Delta^T (from
-//     LDS) and E^T (registers), B = Z and F as the local kernel's column
+//     4 (l / 16) + i, column l % 16 of each 16-column tile); A = Delta^T and
+//     E^T (both from LDS), B = Z and F as the local kernel's column
 //     fragments (registers).
 // Every wave loads only its quarter of each operand, straight into registers,
-// right after its last use: the next chunk's Y during the update, the next Z
-// and F during the following products.  Two barriers per chunk (the state
-// rows and Delta cross the waves through LDS).
+// right after its last use: the next chunk's Y during the update, the next Z,
+// F and E during the following products.  E^T is the same for all four waves,
+// so each loads a quarter of its fragments and stages it in LDS.  Two
+// barriers per chunk (the state rows, Delta and E^T cross the waves through
+// LDS).
 // The operands of one direction of the chain (workspace byte offsets; E and
 // F absent when their offset is 0; Zf and Ff are fragment arrays).
 struct ChainOps {
