@@ -759,18 +759,50 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
     __syncthreads();
     for (int e = t; e < BC * BC; e += 256) s.T[e] = Ts[e >> 6][e & 63];
     __syncthreads();
-    // W = T diag(beta e^gamma) K, then U = T diag(beta) V
-    for (int n0 = 0; n0 < dk; n0 += 64) {
-        zero(acc);
-        mm64<KTL, true, true, float, TIn>(acc, s.T, BC, bgk, sK, dk, BC, n0, as, bs);
+    // W = T diag(beta e^gamma) K by 64-column blocks, each staged in LDS (Ts is
+    // free now) and written out only as the chains' hi/lo fragments: the
+    // column fragments (Wf, the reverse chain's Z) and the row fragments (Wr,
+    // the forward chain's Y) of its columns, with no fp32 W in the workspace
+    const int64_t fper = (int64_t)BC * dk * 2;
+    {
+        uint16_t* const wf = reinterpret_cast<uint16_t*>(a.ws + a.lay.off_Wf) + b * fper;
+        uint16_t* const wr = reinterpret_cast<uint16_t*>(a.ws + a.lay.off_Wr) + b * fper;
+        const int ksn = dk / 32;
+        for (int n0 = 0; n0 < dk; n0 += 64) {
+            zero(acc);
+            mm64<KTL, true, true, float, TIn>(acc, s.T, BC, bgk, sK, dk, BC, n0, as, bs);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 4 * tr + i, n = n0 + 16 * j + tc;
-                s.W[r * dk + n] = acc[i][j];
+                for (int j = 0; j < 4; ++j) Ts[4 * tr + i][16 * j + tc] = acc[i][j];
+            __syncthreads();
+            // tasks 0..511: column fragment (tile n0/16 + task/128, k-step (task/64)%2);
+            // 512..1023: row fragment (row tile (task-512)/128, k-step n0/32 + (task/64)%2)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int task = t + 256 * q, fl = task & 63, kl = (task >> 6) & 1, tl = (task >> 7) & 3;
+                const int fl16 = fl & 15, fg = fl >> 4;
+                float x[8];
+                uint16_t* p;
+                if (q < 2) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) x[e] = Ts[32 * kl + 8 * fg + e][16 * tl + fl16];
+                    p = wf + ((size_t)(((n0 / 16 + tl) * 2 + kl) * 2) * 64 + fl) * 8;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) x[e] = Ts[16 * tl + fl16][32 * kl + 8 * fg + e];
+                    p = wr + ((size_t)((tl * ksn + n0 / 32 + kl) * 2) * 64 + fl) * 8;
+                }
+                uint32_t hi[4], lo[4];
+#pragma unroll
+                for (int w2 = 0; w2 < 4; ++w2) split_bf16x2(x[2 * w2], x[2 * w2 + 1], hi[w2], lo[w2]);
+                *reinterpret_cast<u32x4*>(p) = u32x4{hi[0], hi[1], hi[2], hi[3]};
+                *reinterpret_cast<u32x4*>(p + 512) = u32x4{lo[0], lo[1], lo[2], lo[3]};
             }
+            __syncthreads();  // Ts read: free for the next block
+        }
     }
+    // U = T diag(beta) V
     for (int n0 = 0; n0 < dv; n0 += 64) {
         zero(acc);
         mm64<KTL, true, true, float, TIn>(acc, s.T, BC, bet, reinterpret_cast<const TIn*>(s.V), dv, BC, n0, as, bs);
@@ -787,11 +819,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
                 s.dDl[r * dv + n] = a.scale * acc2[i][j];
             }
     }
-    // the chains' operands contracted over the chunk rows, as bf16 hi/lo fragments
+    // the other operands of the chains, as bf16 hi/lo fragments
     __syncthreads();
-    const int64_t fper = (int64_t)BC * dk * 2;
     constexpr bool RAW_EXACT = sizeof(TIn) == 2;  // bf16 inputs: raw k and q are exact in bf16
-    col_frags<false>(s.W, dk, reinterpret_cast<uint16_t*>(a.ws + a.lay.off_Wf) + b * fper);
     if constexpr (RAW_EXACT) {
         col_frags_b16(reinterpret_cast<const uint16_t*>(sK), dk, reinterpret_cast<uint16_t*>(a.ws + a.lay.off_Kf) + b * fper);
         col_frags_b16(reinterpret_cast<const uint16_t*>(sQ), dk, reinterpret_cast<uint16_t*>(a.ws + a.lay.off_Qf) + b * fper);
@@ -804,7 +834,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
                        reinterpret_cast<uint16_t*>(a.ws + a.lay.off_Ef) + b * (int64_t)BC * dv * 2);
     else
         col_frags<false>(s.E, dv, reinterpret_cast<uint16_t*>(a.ws + a.lay.off_Ef) + b * (int64_t)BC * dv * 2);
-    row_frags<false>(s.W, dk, reinterpret_cast<uint16_t*>(a.ws + a.lay.off_Wr) + b * fper);
     row_frags<RAW_EXACT>(sK, dk, reinterpret_cast<uint16_t*>(a.ws + a.lay.off_Kr) + b * fper);
 }
 
