@@ -136,7 +136,6 @@ BwdLayout backward_layout(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t d
     L.off_T = take(cc);
     L.off_P = take(cc);
     L.off_KKG = take(cc);
-    L.off_W = take(cdk);
     L.off_U = take(cdv);
     L.off_E = take(cdv);
     L.off_dDl = take(cdv);

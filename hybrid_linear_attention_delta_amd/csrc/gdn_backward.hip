@@ -323,7 +323,7 @@ __device__ void mm64x3(float p1[4][4], float p2[4][4], float p3[4][4], float& do
 
 // Per chunk-head slices of the workspace.
 struct Slices {
-    float *Q, *K, *V, *dO, *rq, *rk, *gam, *bet, *T, *P, *KKG, *W, *U, *E, *dDl, *sck;
+    float *Q, *K, *V, *dO, *rq, *rk, *gam, *bet, *T, *P, *KKG, *U, *E, *dDl, *sck;
     float *S, *Dl, *dS, *dD, *dQ, *dK, *dW, *dPG, *dT, *X1, *Bd;
 };
 
@@ -345,7 +345,6 @@ __device__ Slices slices(const BwdArgs& a, int64_t b)
     s.T = f(L.off_T, cc);
     s.P = f(L.off_P, cc);
     s.KKG = f(L.off_KKG, cc);
-    s.W = f(L.off_W, cdk);
     s.U = f(L.off_U, cdv);
     s.E = f(L.off_E, cdv);
     s.sck = f(L.off_sck, BC);

@@ -141,7 +141,7 @@ struct BwdLayout {
     int64_t max_chunks;  // upper bound on sum_n ceil(L_n / 64)
     size_t off_header, off_tab, off_seq_first;
     size_t off_Q, off_K, off_V, off_dO, off_rq, off_rk, off_gam, off_bet;
-    size_t off_T, off_P, off_KKG, off_W, off_U, off_E, off_dDl, off_sck;
+    size_t off_T, off_P, off_KKG, off_U, off_E, off_dDl, off_sck;
     size_t off_S, off_Dl, off_dS, off_dD;
     size_t off_dQ, off_dK, off_dW, off_dPG, off_dT, off_X1, off_Bd;
     // the state chains' operands as bf16 hi/lo fragments (hi parts only for the

@@ -375,7 +375,7 @@ gdn_status gdn_chunk_prefill_frontend(gdn_context_t ctx, const void* xq, const v
  * Bytes of device workspace gdn_chunk_prefill_backward needs for these sizes
  * (0 for an unsupported or invalid combination).  It holds per-chunk
  * intermediates in 4-byte slots, among them the state entering every chunk
- * and the state gradient after it: max_chunks * H * (2 dv dk + 64 (11 dk +
+ * and the state gradient after it: max_chunks * H * (2 dv dk + 64 (10 dk +
  * 8 dv) + 7 * 64 * 64 + 5 * 64) * 4 bytes plus the chunk table and 256-byte
  * alignment, max_chunks = total_tokens / 64 + num_seqs.
  */

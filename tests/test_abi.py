@@ -214,6 +214,20 @@ def test_frontend_host_validation(lib):
     assert dec(st=_fake(0x10008)) == 5
 
 
+@pytest.mark.parametrize("T,N,H,dk,dv", [(128, 1, 2, 64, 64), (1000, 3, 2, 64, 128), (65536, 1, 6, 256, 256),
+                                         (2_097_152, 16, 6, 256, 256)])
+def test_backward_workspace_size_matches_the_header_formula(lib, T, N, H, dk, dv):
+    """gdn_prefill_backward_workspace_size is the size the header documents:
+    max_chunks * H * (2 dv dk + 64 (10 dk + 8 dv) + 7 * 64 * 64 + 5 * 64) * 4
+    bytes for the per-chunk slots, plus the header words, the chunk table and
+    at most 256 bytes of alignment per slot."""
+    mc = T // 64 + N
+    formula = mc * H * (2 * dv * dk + 64 * (10 * dk + 8 * dv) + 7 * 64 * 64 + 5 * 64) * 4
+    size = lib.gdn_prefill_backward_workspace_size(T, N, H, dk, dv)
+    extra = size - formula
+    assert 0 <= extra - mc * 16 - (N + 1) * 4 - 64 < 40 * 256, (size, formula)
+
+
 def test_backward_host_validation(lib):
     """The backward entry point checks sizes, support, pointers, alignment,
     sequence bounds and the workspace on the host and returns before any launch."""
