@@ -1151,8 +1151,11 @@ __global__ __launch_bounds__(256, 3) void bwd_grad_kernel(BwdArgs a)
     // that contract over the chunk rows, on output columns or row sums else
     const TIn* sQ = reinterpret_cast<const TIn*>(s.Q);
     const TIn* sK = reinterpret_cast<const TIn*>(s.K);
-    __shared__ __align__(16) float as[KTG * LD], bs[KTG * LD];
-    __shared__ __align__(16) float ls3[5 * 32 * LD];  // the fused pass over S and dS
+    // the fused pass over S and dS stages five tiles; the 64 x 64 tile routine
+    // of the other products (never live at the same time) uses two of them
+    __shared__ __align__(16) float ls3[5 * 32 * LD];
+    float* const as = ls3;
+    float* const bs = ls3 + KTG * LD;
     __shared__ float gam[BC], bet[BC], eg[BC], dd[BC], bge[BC], dgam[BC], dbet[BC], rqv[BC], rkv[BC];
     __shared__ float red[4];
     __shared__ float cs[16][BC];
