@@ -541,7 +541,7 @@ __global__ __launch_bounds__(64) void bwd_table_kernel(const int32_t* __restrict
 }
 
 template <typename TIn>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void bwd_local_kernel(BwdArgs a)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void bwd_local_kernel(BwdArgs a)
 {
     const int64_t b = blockIdx.x;
     const int32_t* header = reinterpret_cast<const int32_t*>(a.ws + a.lay.off_header);
@@ -552,9 +552,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
     const int tok0 = tab[4 * c], len = tab[4 * c + 1];
     const int dk = a.dk, dv = a.dv, H = a.H;
     Slices s = slices(a, b);
-    __shared__ __align__(16) float as[KTL * LD], bs[KTL * LD];
+    // the tile routine's two k-block buffers; A = diag(beta) KKG, from the
+    // K K^T product (the last one before the inverse) to the inverse (the
+    // first one after it), in the same bytes
+    __shared__ __align__(16) float lds_ab[2 * KTL * LD];
+    static_assert(BC * (BC + 1) <= 2 * KTL * LD, "A fits the tile buffers");
+    float* const as = lds_ab;
+    float* const bs = lds_ab + KTL * LD;
+    float (*const Am)[BC + 1] = reinterpret_cast<float (*)[BC + 1]>(lds_ab);
     __shared__ float gam[BC], bet[BC], bge[BC], dd[BC], eg[BC], gin[BC], rqs[BC], rks[BC], bgk[BC], esc[BC];
-    __shared__ float Am[BC][BC + 1], Ts[BC][BC + 1];
+    __shared__ float Ts[BC][BC + 1];
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
     const TIn* q = (const TIn*)a.q;
     const TIn* k = (const TIn*)a.k;
@@ -708,6 +715,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
     // in fp32, on the products' rows and columns or folded into the k scale.
     const TIn* sQ = reinterpret_cast<const TIn*>(s.Q);
     const TIn* sK = reinterpret_cast<const TIn*>(s.K);
+    // Q K^T -> P = lower(Q K^T o Gamma)
+    zero(acc);
+    mm64<KTL, true, false, TIn, TIn>(acc, sQ, dk, nullptr, sK, dk, dk, 0, as, bs);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 4 * tr + i, n = 16 * j + tc;
+            s.P[r * BC + n] = n <= r ? acc[i][j] * (rqs[r] * rks[n]) * expf(gam[r] - gam[n]) : 0.f;
+        }
     // K K^T -> KKG = strict_lower(K K^T o Gamma), A = diag(beta) KKG
     zero(acc);
     mm64<KTL, true, false, TIn, TIn>(acc, sK, dk, nullptr, sK, dk, dk, 0, as, bs);
@@ -719,16 +736,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
             const float x = n < r ? acc[i][j] * (rks[r] * rks[n]) * expf(gam[r] - gam[n]) : 0.f;
             s.KKG[r * BC + n] = x;
             Am[r][n] = bet[r] * x;
-        }
-    // Q K^T -> P = lower(Q K^T o Gamma)
-    zero(acc);
-    mm64<KTL, true, false, TIn, TIn>(acc, sQ, dk, nullptr, sK, dk, dk, 0, as, bs);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = 4 * tr + i, n = 16 * j + tc;
-            s.P[r * BC + n] = n <= r ? acc[i][j] * (rqs[r] * rks[n]) * expf(gam[r] - gam[n]) : 0.f;
         }
     __syncthreads();
     // T = (I + A)^{-1} by forward substitution.  Column c of T depends only on
