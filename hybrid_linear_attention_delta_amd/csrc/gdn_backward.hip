@@ -984,8 +984,8 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs a, ChainOps rev_
     constexpr int OPB = BC * DK * 4 / 1024;  // 1 KB blocks of one d_k operand (hi and lo)
     const int eb = BC * dv * 4 / 1024;       // of E
     uint32_t pf_acc = 0;
-    u32x4 pf[2][4];
-    auto prefetch = [&](int64_t ch, u32x4* dst, auto rev_c) {
+    uint32_t pf[2][4];
+    auto prefetch = [&](int64_t ch, uint32_t* dst, auto rev_c) {
         constexpr bool REV = decltype(rev_c)::value;
         constexpr int SY = REV && EXACT ? 2 : 1, SZ = !REV && EXACT ? 2 : 1, SF = EXACT ? 2 : 1;
         constexpr int NY = OPB / SY, NZ = OPB / SZ, NF = REV ? OPB / SF : 0;
@@ -1001,7 +1001,7 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs a, ChainOps rev_
             const int blk = q < NY ? q * SY : q < NY + NZ ? (q - NY) * SZ : q < NY + NZ + NF ? (q - NY - NZ) * SF
                                                                                            : q - NY - NZ - NF;
             const unsigned char* src = reinterpret_cast<const unsigned char*>(base + ch * per) + blk * 1024;
-            dst[i] = *reinterpret_cast<const u32x4*>(src + lane * 16);
+            dst[i] = *reinterpret_cast<const uint32_t*>(src + lane * 16);
         }
     };
 
@@ -1019,12 +1019,12 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs a, ChainOps rev_
     // one chunk; the loop below runs two per iteration, so that each uses a
     // fixed prefetch slot (a slot picked by it & 1 is a dynamic register index,
     // which the compiler serves with a wait for every load in flight)
-    auto chunk_step = [&](int it, u32x4* slot, auto rev_c) __attribute__((always_inline)) {
+    auto chunk_step = [&](int it, uint32_t* slot, auto rev_c) __attribute__((always_inline)) {
         constexpr bool REV = decltype(rev_c)::value;
         const int64_t ch = chunk_of(it);
         {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) pf_acc ^= slot[i].x ^ slot[i].w;
+            for (int i = 0; i < 4; ++i) pf_acc ^= slot[i];
             prefetch(chunk_of(min(it + 2, steps - 1)), slot, rev_c);
         }
         // the state before the chunk: to LDS in fp32 (for the record) and split
@@ -1106,7 +1106,7 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs a, ChainOps rev_
 #pragma unroll
     for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pf[b2][i] = u32x4{0u, 0u, 0u, 0u};
+        for (int i = 0; i < 4; ++i) pf[b2][i] = 0u;
     // the two directions as separate loops: the E^T F term, the raw-row
     // operands and their loads are compiled in or out, never branched around
     auto run = [&](auto rev_c) __attribute__((always_inline)) {
@@ -1133,7 +1133,7 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs a, ChainOps rev_
 #pragma unroll
     for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pf_acc ^= pf[b2][i].x ^ pf[b2][i].w;
+        for (int i = 0; i < 4; ++i) pf_acc ^= pf[b2][i];
     asm volatile("" ::"v"(pf_acc));  // the prefetched words stay live: the loads are kept
 }
 
