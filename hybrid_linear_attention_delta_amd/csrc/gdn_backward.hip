@@ -976,11 +976,15 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs a, ChainOps rev_
     // L2 prefetch two chunks ahead: the operand bytes the chain reads for one
     // chunk (Y, Z, F and E; of a hi-only operand its hi parts, every other
     // 1 KB block), cut into 1 KB pieces, this workgroup's share of the pair's
-    // pieces, one 16-byte load per lane; the loaded words are folded into a
-    // register two chunks later (kept alive to the end), so no wait is added
-    // before they arrive.  A piece beyond this workgroup's share reloads the
-    // chunk's first Y piece: every lane loads on every step, with no branch
-    // around the loads.
+    // pieces, one 4-byte load per lane at a 16-byte stride (a word of each
+    // 16 bytes brings all of the piece's cache lines into L2); the loaded
+    // words are folded into a register two chunks later (kept alive to the
+    // end), so no wait is added before they arrive.  (16-byte loads of which
+    // only two words were folded left the other two registers free at once:
+    // the compiler reused them and waited for every load in flight, a full
+    // memory round trip on every step.)  A piece beyond this workgroup's
+    // share reloads the chunk's first Y piece: every lane loads on every
+    // step, with no branch around the loads.
     constexpr int OPB = BC * DK * 4 / 1024;  // 1 KB blocks of one d_k operand (hi and lo)
     const int eb = BC * dv * 4 / 1024;       // of E
     uint32_t pf_acc = 0;
