@@ -1479,11 +1479,7 @@ __global__ __launch_bounds__(64) void pipe_wait_kernel(uint32_t* flags, int32_t 
 // round-robin): they read the same per-chunk records, which then come from
 // that XCD's L2.  Pair indices follow seq_order (longest sequence first) in a
 // packed batch, so when there are more workgroups than CUs the longest chains
-// are dispatched first.  Each XCD dispatches its own workgroups in order, so
-// the pairs are dealt to the XCDs 8 at a time in alternating direction
-// (0..7, then 7..0): with longest-first pairs this evens out the XCDs' loads
-// (the packed 2M batch: 16.7 against 15.75 ms of chain work on its busiest
-// XCD in a list-scheduling model).
+// are dispatched first.
 template <int C, int DK, int DV, int NW, bool SEG>
 __global__ __launch_bounds__(NW * 64) void chain_kernel(
     const int32_t* __restrict__ header, const int32_t* __restrict__ seq_first,
@@ -1512,8 +1508,7 @@ __global__ __launch_bounds__(NW * 64) void chain_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave: scalar branches
     const int g16 = lane >> 4, l16 = lane & 15;
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-    const int round = slot / TILES;  // XCDs take pairs 8 at a time, in alternating direction
-    const int pair = 8 * round + ((round & 1) ? 7 - xcd : xcd);
+    const int pair = xcd + 8 * (slot / TILES);
     if (pair >= pairs) return;
     const int n = varlen ? seq_order[pair / H] : pair / H, h = pair % H;  // longest sequences first
     const int tile = slot % TILES;
@@ -1736,8 +1731,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_num_vgpr(120))) void ch
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave: scalar branches
     const int g16 = lane >> 4, l16 = lane & 15;
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-    const int round = slot / TILES;  // XCDs take pairs 8 at a time, in alternating direction
-    const int pair = 8 * round + ((round & 1) ? 7 - xcd : xcd);
+    const int pair = xcd + 8 * (slot / TILES);
     if (pair >= pairs) return;
     const int n = varlen ? seq_order[pair / H] : pair / H, h = pair % H;  // longest sequences first
     const int tile = slot % TILES;
