@@ -513,31 +513,67 @@ __device__ __forceinline__ void split8(f32x4 a, f32x4 b, u32x4& hi, u32x4& lo)
 // Chunk table: header[0] = 1 if cu_seqlens is invalid (then no chunk is
 // processed), header[1] = number of chunks; tab[c] = {first token, length,
 // sequence, 0}; seq_first[n] = first chunk of sequence n.
-__global__ __launch_bounds__(64) void bwd_table_kernel(const int32_t* __restrict__ cu, int32_t N, int64_t T,
-                                                       int64_t max_chunks, int32_t* __restrict__ header,
-                                                       int32_t* __restrict__ tab, int32_t* __restrict__ seq_first)
+__global__ __launch_bounds__(256) void bwd_table_kernel(const int32_t* __restrict__ cu, int32_t N, int64_t T,
+                                                        int64_t max_chunks, int32_t* __restrict__ header,
+                                                        int32_t* __restrict__ tab, int32_t* __restrict__ seq_first)
 {
-    if (threadIdx.x != 0) return;
-    bool ok = true;
-    if (cu) {
-        ok = cu[0] == 0 && (int64_t)cu[N] == T;
-        for (int32_t n = 0; ok && n < N; ++n) ok = cu[n + 1] >= cu[n];
+    // one workgroup: each thread counts the chunks of a run of sequences, a
+    // scan gives their first chunks, then every chunk finds its sequence by a
+    // binary search over them
+    __shared__ int64_t part[256];
+    __shared__ int bad;
+    __shared__ int64_t tot_s;
+    const int t = threadIdx.x;
+    if (t == 0) bad = cu && (cu[0] != 0 || (int64_t)cu[N] != T) ? 1 : 0;
+    __syncthreads();
+    const int32_t per = (N + 255) / 256, s0 = min(N, t * per), s1 = min(N, s0 + per);
+    auto len_of = [&](int32_t n) -> int64_t { return cu ? (int64_t)cu[n + 1] - cu[n] : T; };
+    int64_t cnt = 0;
+    bool mybad = false;
+    for (int32_t n = s0; n < s1; ++n) {
+        const int64_t L = len_of(n);
+        if (L < 0) mybad = true;
+        cnt += (max(L, (int64_t)0) + BC - 1) / BC;
     }
-    int64_t count = 0;
-    for (int32_t n = 0; n < N; ++n) {
-        seq_first[n] = (int32_t)count;
-        if (!ok) continue;
-        const int64_t s = cu ? cu[n] : 0, e = cu ? cu[n + 1] : T;
-        for (int64_t p = s; p < e && count < max_chunks; p += BC, ++count) {
-            tab[4 * count + 0] = (int32_t)p;
-            tab[4 * count + 1] = (int32_t)min((int64_t)BC, e - p);
-            tab[4 * count + 2] = n;
-            tab[4 * count + 3] = 0;
+    part[t] = cnt;
+    if (mybad) bad = 1;
+    __syncthreads();
+    if (t == 0) {
+        int64_t run = 0;
+        for (int i = 0; i < 256; ++i) {
+            const int64_t c = part[i];
+            part[i] = run;
+            run += c;
         }
+        if (run > max_chunks) bad = 1;  // not for valid input: the chunks number at most T / 64 + N
+        tot_s = run;
     }
-    seq_first[N] = (int32_t)count;
-    header[0] = ok ? 0 : 1;
-    header[1] = (int32_t)count;
+    __syncthreads();
+    const bool ok = !bad;
+    const int64_t tot = ok ? tot_s : 0;
+    int64_t off = part[t];
+    for (int32_t n = s0; n < s1; ++n) {
+        seq_first[n] = ok ? (int32_t)off : 0;
+        off += (max(len_of(n), (int64_t)0) + BC - 1) / BC;
+    }
+    if (t == 0) {
+        seq_first[N] = (int32_t)tot;
+        header[0] = ok ? 0 : 1;
+        header[1] = (int32_t)tot;
+    }
+    __syncthreads();  // seq_first complete
+    for (int64_t j = t; j < tot; j += 256) {
+        int32_t lo = 0, hi = N - 1;  // the last sequence whose first chunk is <= j (skips empty ones)
+        while (lo < hi) {
+            const int32_t mid = (lo + hi + 1) >> 1;
+            if (seq_first[mid] <= j) lo = mid; else hi = mid - 1;
+        }
+        const int64_t p = (cu ? cu[lo] : 0) + (j - seq_first[lo]) * BC, e = cu ? cu[lo + 1] : T;
+        tab[4 * j + 0] = (int32_t)p;
+        tab[4 * j + 1] = (int32_t)min((int64_t)BC, e - p);
+        tab[4 * j + 2] = lo;
+        tab[4 * j + 3] = 0;
+    }
 }
 
 template <typename TIn>
@@ -1473,7 +1509,7 @@ hipError_t launch_backward(const BwdArgs& a)
 {
     const BwdLayout& L = a.lay;
     int32_t* header = reinterpret_cast<int32_t*>(a.ws + L.off_header);
-    hipLaunchKernelGGL(bwd_table_kernel, dim3(1), dim3(64), 0, a.stream, a.cu_seqlens, a.N, a.T, L.max_chunks, header,
+    hipLaunchKernelGGL(bwd_table_kernel, dim3(1), dim3(256), 0, a.stream, a.cu_seqlens, a.N, a.T, L.max_chunks, header,
                        reinterpret_cast<int32_t*>(a.ws + L.off_tab), reinterpret_cast<int32_t*>(a.ws + L.off_seq_first));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
